@@ -1,0 +1,230 @@
+"""Thin ctypes binding of libdecoder.so (include/decoder.h, include/decoder_diag.h).
+
+Argument marshalling only: PyTorch supplies device memory and the stream;
+every step of the decoder runs in the library's HIP kernels.  The library
+must have been built (``decoder_only_transformer_step_amd.build``); there is
+no fallback path.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdecoder.so")
+_LIB = None
+
+DEC_OK, DEC_E_CONTEXT_OVERFLOW, DEC_E_INVALID, DEC_E_TOKEN, DEC_E_WORKSPACE, DEC_E_HIP = range(6)
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+
+
+class DecoderConfig(ctypes.Structure):
+    _fields_ = [(n, _I32) for n in (
+        "hidden", "n_layers", "n_heads", "n_kv_heads", "head_dim", "ffn_inter", "n_experts",
+        "top_k", "expert_inter", "shared_inter", "shared_gate", "norm_topk_prob", "vocab",
+        "qkv_bias")] + [("rope_base", ctypes.c_double), ("rms_eps", ctypes.c_double)] + [
+        (n, _I32) for n in ("max_seq", "max_chunk", "max_batch")]
+
+
+LAYER_FIELDS = ("attn_norm", "ffn_norm", "w_qkv", "b_qkv", "w_o", "w_gate_up", "w_down",
+                "w_router", "w_exp_gate_up", "w_exp_down", "w_sh_gate_up", "w_sh_down",
+                "w_sh_gate")
+
+
+class DecoderLayerWeights(ctypes.Structure):
+    _fields_ = [(n, _P) for n in LAYER_FIELDS]
+
+
+class DecoderWeights(ctypes.Structure):
+    _fields_ = [("embed", _P), ("final_norm", _P), ("lm_head", _P),
+                ("layers", ctypes.POINTER(DecoderLayerWeights))]
+
+
+# every symbol the headers declare, with its ctypes signature
+SIGNATURES = {
+    "decoder_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(DecoderConfig)]),
+    "decoder_init": (ctypes.c_int, [ctypes.POINTER(DecoderConfig), ctypes.POINTER(DecoderWeights), _P,
+                                    ctypes.c_size_t, _P, ctypes.POINTER(_P)]),
+    "prefill_chunk": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _I32, _P, _P]),
+    "decode_step": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P]),
+    "kv_reset": (ctypes.c_int, [_P, _I32]),
+    "kv_load": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _I32]),
+    "decoder_seq_len": (_I32, [_P, _I32]),
+    "decoder_set_stream": (ctypes.c_int, [_P, _P]),
+    "decoder_free": (None, [_P]),
+    "decoder_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "decoder_last_error": (ctypes.c_char_p, [_P]),
+    "dec_diag_gemm": (ctypes.c_int, [_P, _I32, _I32, _P, _I32, _P, _P]),
+    "dec_diag_rmsnorm": (ctypes.c_int, [_P, _P, _I32, _I32, ctypes.c_double, _P, _P]),
+    "decoder_debug_layer_limit": (ctypes.c_int, [_P, _I32]),
+    "decoder_debug_read_x": (ctypes.c_int, [_P, _P, _I32]),
+    "decoder_debug_read_routes": (ctypes.c_int, [_P, _P, _I32]),
+}
+
+
+def lib():
+    """Load libdecoder.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m decoder_only_transformer_step_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+class DecoderError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{msg} (code {code})")
+        self.code = code
+
+
+def _check(rc, handle=None, what=""):
+    if rc != DEC_OK:
+        L = lib()
+        detail = L.decoder_last_error(handle).decode() if handle else ""
+        raise DecoderError(rc, f"{what}: {L.decoder_strerror(rc).decode()}" + (f" [{detail}]" if detail else ""))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _i32_array(values):
+    vals = [int(v) for v in values]
+    return (ctypes.c_int32 * max(1, len(vals)))(*vals), len(vals)
+
+
+def make_config(shape):
+    """decoder_config_t from a synth.workloads.Shape-like object."""
+    s = shape
+    return DecoderConfig(
+        hidden=s.hidden, n_layers=s.n_layers, n_heads=s.n_heads, n_kv_heads=s.n_kv_heads,
+        head_dim=s.head_dim, ffn_inter=s.ffn_inter, n_experts=s.n_experts, top_k=s.top_k,
+        expert_inter=s.expert_inter, shared_inter=s.shared_inter, shared_gate=int(s.shared_gate),
+        norm_topk_prob=int(s.norm_topk_prob), vocab=s.vocab, qkv_bias=int(s.qkv_bias),
+        rope_base=float(s.rope_base), rms_eps=float(s.rms_eps), max_seq=s.max_seq,
+        max_chunk=s.max_chunk, max_batch=s.max_batch)
+
+
+# ---------------------------------------------------- same-named functions --
+
+def decoder_workspace_bytes(cfg):
+    return lib().decoder_workspace_bytes(ctypes.byref(cfg))
+
+
+def decoder_init(cfg, weights, workspace, stream):
+    """weights: dict with device tensors 'embed', 'final_norm', 'lm_head' and
+    'layers' (list of dicts keyed by LAYER_FIELDS).  Returns (handle, keepalive)."""
+    layers = (DecoderLayerWeights * cfg.n_layers)()
+    for l, lw in enumerate(weights["layers"]):
+        for f in LAYER_FIELDS:
+            t = lw.get(f)
+            if t is not None:
+                setattr(layers[l], f, t.data_ptr())
+    w = DecoderWeights(embed=weights["embed"].data_ptr(), final_norm=weights["final_norm"].data_ptr(),
+                       lm_head=weights["lm_head"].data_ptr(), layers=layers)
+    h = ctypes.c_void_p()
+    rc = lib().decoder_init(ctypes.byref(cfg), ctypes.byref(w), ctypes.c_void_p(workspace.data_ptr()),
+                            workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream),
+                            ctypes.byref(h))
+    _check(rc, None, "decoder_init")
+    return h, (layers, w)
+
+
+def prefill_chunk(handle, seq, ids, start_pos, logits_mode=1, logits=None, argmax=None):
+    arr, n = _i32_array(ids)
+    _check(lib().prefill_chunk(handle, seq, arr, n, start_pos, logits_mode, _ptr(logits), _ptr(argmax)),
+           handle, "prefill_chunk")
+
+
+def decode_step(handle, seqs, tokens=None, logits=None, argmax=None):
+    sarr, b = _i32_array(seqs)
+    tarr = _i32_array(tokens)[0] if tokens is not None else None
+    _check(lib().decode_step(handle, b, sarr, tarr, _ptr(logits), _ptr(argmax)), handle, "decode_step")
+
+
+def kv_reset(handle, seq=-1):
+    _check(lib().kv_reset(handle, seq), handle, "kv_reset")
+
+
+def kv_load(handle, seq, layer, k, v, length):
+    _check(lib().kv_load(handle, seq, layer, _ptr(k), _ptr(v), length), handle, "kv_load")
+
+
+def decoder_seq_len(handle, seq):
+    return lib().decoder_seq_len(handle, seq)
+
+
+def decoder_free(handle):
+    lib().decoder_free(handle)
+
+
+# ------------------------------------------------------------- convenience --
+
+class Decoder:
+    """Owns the workspace tensor and the handle; methods mirror the C ABI."""
+
+    def __init__(self, shape, weights, stream=None, device="cuda"):
+        import torch
+        self.shape = shape
+        self.cfg = make_config(shape)
+        nbytes = decoder_workspace_bytes(self.cfg)
+        if nbytes == 0:
+            raise DecoderError(DEC_E_INVALID, "invalid decoder config")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        self.weights = weights
+        self.handle, self._keep = decoder_init(self.cfg, weights, self.workspace, self.stream.cuda_stream)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            decoder_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def prefill_chunk(self, seq, ids, start_pos, logits_mode=1, logits=None, argmax=None):
+        prefill_chunk(self.handle, seq, ids, start_pos, logits_mode, logits, argmax)
+
+    def decode_step(self, seqs, tokens=None, logits=None, argmax=None):
+        decode_step(self.handle, seqs, tokens, logits, argmax)
+
+    def kv_reset(self, seq=-1):
+        kv_reset(self.handle, seq)
+
+    def kv_load(self, seq, layer, k, v, length):
+        kv_load(self.handle, seq, layer, k, v, length)
+
+    def seq_len(self, seq=0):
+        return decoder_seq_len(self.handle, seq)
+
+    def debug_layer_limit(self, layers):
+        _check(lib().decoder_debug_layer_limit(self.handle, layers), self.handle, "layer_limit")
+
+    def debug_read_x(self, out, rows):
+        _check(lib().decoder_debug_read_x(self.handle, _ptr(out), rows), self.handle, "read_x")
+
+    def debug_read_routes(self, out, rows):
+        _check(lib().decoder_debug_read_routes(self.handle, _ptr(out), rows), self.handle, "read_routes")
+
+
+def diag_gemm(A, W, C, stream):
+    M, K = A.shape
+    N = W.shape[0]
+    _check(lib().dec_diag_gemm(_ptr(A), M, K, _ptr(W), N, _ptr(C), ctypes.c_void_p(stream)), None, "dec_diag_gemm")
+
+
+def diag_rmsnorm(x, g, eps, out, stream):
+    rows, H = x.shape
+    _check(lib().dec_diag_rmsnorm(_ptr(x), _ptr(g), rows, H, float(eps), _ptr(out), ctypes.c_void_p(stream)),
+           None, "dec_diag_rmsnorm")

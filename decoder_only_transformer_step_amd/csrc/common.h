@@ -1,0 +1,109 @@
+// Shared device helpers for the gfx950 kernels: bf16 packing, MFMA fragment
+// types, wave reductions, and the launch-parameter structs the host side
+// fills in.  CDNA4 wavefronts are 64 lanes; every kernel here is written for
+// that width.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define WAVE 64
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+// ----------------------------------------------------------------- bf16 --
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t b = __float_as_uint(f);
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 16-byte global load that streams past the caches (weights are read once).
+__device__ __forceinline__ u32x4 load_stream16(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ u32x4 load16(const void *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ u32x2 load8(const void *p) {
+  return *reinterpret_cast<const u32x2 *>(p);
+}
+
+// D = A * B + C for a 16x16 tile with K = 32 (bf16 in, fp32 accumulate).
+// Lane l supplies A[m = l % 16][k = 8 (l / 16) + j] and B[k = 8 (l / 16) + j][n = l % 16]
+// for j < 8, and receives D[m = 4 (l / 16) + i][n = l % 16] for i < 4.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------- wave reductions --
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+// Block-wide sum for blockDim.x = 64 * nwaves; every thread gets the result.
+template <int NWAVES>
+__device__ __forceinline__ float block_sum(float v, float *lds) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / WAVE;
+  if ((threadIdx.x & (WAVE - 1)) == 0) lds[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) t += lds[i];
+  __syncthreads();
+  return t;
+}
+
+// ------------------------------------------------------ launch structs --
+
+// Epilogues of the projection kernel.
+enum {
+  EPI_STORE = 0,     // C[m][n] = acc (+ bias[n])                 fp32
+  EPI_ADD = 1,       // C[m][n] += acc                              fp32 (residual stream)
+  EPI_SWIGLU = 2,    // H[m][n] = bf16(silu(acc_gate) * acc_up)    gate rows n, up rows n + N
+};
+
+struct GemmArgs {
+  const uint16_t *A;      // bf16 activations, row m at A + row(m) * lda
+  const int32_t *a_rows;  // optional gather: A row of output row m (grouped mode: by pair)
+  int64_t lda;
+  const uint16_t *W;      // bf16 weights [N(+N)][K] row-major (per group: W + expert * w_group_stride)
+  int64_t w_group_stride;
+  int32_t M, N, K;
+  float *C;               // fp32 output / residual, row m at C + m * ldc
+  uint16_t *Hout;         // bf16 output for EPI_SWIGLU, row m at Hout + m * ldc
+  int64_t ldc;
+  const float *bias;      // optional, EPI_STORE only
+  // grouped (MoE) mode: blockIdx.y = group; rows of group g are
+  // group_start[g] .. group_start[g] + group_count[g]; weights of expert group_expert[g]
+  const int32_t *n_groups;
+  const int32_t *group_expert;
+  const int32_t *group_start;
+  const int32_t *group_count;
+  // split-K: blockIdx.z = split; partial sums go to Cpart[split][M][N]
+  float *Cpart;
+  int32_t ksplit;
+};

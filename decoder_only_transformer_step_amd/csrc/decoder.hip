@@ -1,0 +1,680 @@
+// Host runtime and C ABI of libdecoder.so (declared in include/decoder.h and
+// include/decoder_diag.h).
+//
+// The decoder owns no device memory: decoder_init carves the KV cache, the
+// RoPE table and every scratch buffer out of the caller's workspace once,
+// so a step never allocates (pipeline.rs ForwardScratch: steady-state decode
+// preallocates its buffers).  Per call the host validates everything, copies
+// the token ids / row positions / row sequences into the workspace from a
+// pinned staging ring, and enqueues the kernels of the step on the stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/decoder.h"
+#include "../../include/decoder_diag.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int STAGE_RING = 64;     // pinned staging slots (one per call in flight)
+constexpr int ATTN_TARGET_TASKS = 2048;
+constexpr int ATTN_MAX_TASKS = 8192;
+constexpr int GEMM_MAX_SPLIT = 8;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Layout {
+  size_t kcache, vcache, rope, x, act, attn, q, qkv, h, logits, stage, next_token;
+  size_t part_o, part_ml, gpart;
+  size_t rlogits, rids, rids_rec, rwts, rgate, groups, pair_row, pair_of, hexp, yexp, hsh, ysh;
+  size_t total;
+  int S, R, RL;
+  int64_t seq_stride;
+  size_t gpart_elems;
+};
+
+bool config_ok(const decoder_config_t *c) {
+  if (!c) return false;
+  if (c->hidden <= 0 || c->hidden % 8 || c->n_layers <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0)
+    return false;
+  if (c->n_heads % c->n_kv_heads || c->n_heads / c->n_kv_heads > 16) return false;
+  if (c->head_dim != 64 && c->head_dim != 128) return false;
+  if (c->vocab <= 0 || c->max_seq <= 0 || c->max_chunk <= 0 || c->max_chunk > 256 ||
+      c->max_batch <= 0 || c->max_batch > 256)
+    return false;
+  if (!(c->rope_base > 0.0) || !(c->rms_eps >= 0.0)) return false;
+  if (c->n_experts > 0) {
+    if (c->n_experts > 256 || c->top_k <= 0 || c->top_k > 8 || c->top_k > c->n_experts) return false;
+    if (c->expert_inter <= 0 || c->expert_inter % 8 || c->shared_inter < 0 || c->shared_inter % 8)
+      return false;
+  } else {
+    if (c->ffn_inter <= 0 || c->ffn_inter % 8) return false;
+  }
+  return true;
+}
+
+Layout make_layout(const decoder_config_t *c) {
+  Layout L{};
+  const size_t A = 256;
+  const int d = c->head_dim, H = c->hidden, Hq = c->n_heads, Hkv = c->n_kv_heads;
+  const int qd = Hq * d, qkvr = (Hq + 2 * Hkv) * d;
+  L.S = (int)align_up((size_t)c->max_seq, 32);
+  L.R = std::max(c->max_chunk, c->max_batch);
+  L.RL = std::max(c->max_chunk, c->max_batch);
+  L.seq_stride = (int64_t)c->n_layers * Hkv * (int64_t)L.S * d;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + std::max<size_t>(bytes, 1), A);
+    return o;
+  };
+  const size_t kv = (size_t)c->max_batch * L.seq_stride * 2;
+  L.kcache = take(kv);
+  L.vcache = take(kv);
+  L.rope = take((size_t)L.S * (d / 2) * sizeof(float2));
+  L.x = take((size_t)L.R * H * 4);
+  L.act = take((size_t)L.R * H * 2);
+  L.attn = take((size_t)L.R * qd * 2);
+  L.q = take((size_t)L.R * qd * 2);
+  L.qkv = take((size_t)L.R * qkvr * 4);
+  L.h = take((size_t)L.R * std::max(c->ffn_inter, 1) * 2);
+  L.logits = take((size_t)L.RL * c->vocab * 4);
+  L.stage = take((size_t)3 * L.R * 4);
+  L.next_token = take((size_t)c->max_batch * 4);
+  L.part_o = take((size_t)ATTN_MAX_TASKS * 16 * d * 4);
+  L.part_ml = take((size_t)ATTN_MAX_TASKS * 16 * 2 * 4);
+  int max_small_n = std::max(qkvr, H);
+  if (c->n_experts > 0) max_small_n = std::max(max_small_n, 2 * c->shared_inter);
+  L.gpart_elems = (size_t)GEMM_MAX_SPLIT * L.R * 2 * (size_t)max_small_n;
+  L.gpart = take(L.gpart_elems * 4);
+  if (c->n_experts > 0) {
+    const int E = c->n_experts, k = c->top_k, P = L.R * k;
+    L.rlogits = take((size_t)L.R * E * 4);
+    L.rids = take((size_t)P * 4);
+    L.rids_rec = take((size_t)c->n_layers * P * 4);
+    L.rwts = take((size_t)P * 4);
+    L.rgate = take((size_t)L.R * 4);
+    L.groups = take((size_t)(1 + 3 * E) * 4);
+    L.pair_row = take((size_t)P * 4);
+    L.pair_of = take((size_t)P * 4);
+    L.hexp = take((size_t)P * c->expert_inter * 2);
+    L.yexp = take((size_t)P * H * 4);
+    L.hsh = take((size_t)L.R * std::max(c->shared_inter, 1) * 2);
+    L.ysh = take((size_t)L.R * H * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+struct decoder {
+  decoder_config_t c;
+  Layout L;
+  std::vector<decoder_layer_weights_t> layers;
+  const uint16_t *embed = nullptr, *lm_head = nullptr;
+  const float *final_norm = nullptr;
+  hipStream_t stream = nullptr;
+  char *ws = nullptr;
+  // carved workspace
+  uint16_t *kcache, *vcache, *act, *attn, *q, *h, *hexp, *hsh;
+  float2 *rope;
+  float *x, *qkv, *logits, *part_o, *part_ml, *gpart, *rlogits, *rwts, *rgate, *yexp, *ysh;
+  int32_t *ids, *row_seq, *row_pos, *next_token, *rids, *rids_rec, *groups, *pair_row, *pair_of;
+  // host state
+  std::vector<int32_t> len;
+  std::vector<char> has_next;
+  std::vector<std::vector<int32_t>> kv_pending;  // per seq: layers loaded with the pending len
+  int layer_limit = -1;
+  int last_rows = 0;
+  int32_t *pinned = nullptr;
+  hipEvent_t ev[STAGE_RING];
+  bool ev_used[STAGE_RING];
+  int ring = 0;
+  std::string err;
+};
+
+namespace {
+
+int fail(decoder *D, int code, const std::string &msg) {
+  if (D) D->err = msg;
+  return code;
+}
+
+int hip_fail(decoder *D, hipError_t e, const char *where) {
+  return fail(D, DEC_E_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+#define HIP_TRY(D, expr, where)                    \
+  do {                                             \
+    hipError_t _e = (expr);                        \
+    if (_e != hipSuccess) return hip_fail(D, _e, where); \
+  } while (0)
+
+template <typename T>
+T *carve(decoder *D, size_t off) {
+  return reinterpret_cast<T *>(D->ws + off);
+}
+
+// Stage rows' ids / seqs / positions to the device through a pinned slot.
+int stage_rows(decoder *D, int rows, const int32_t *ids, const int32_t *seqs, const int32_t *pos) {
+  const int slot = D->ring;
+  D->ring = (D->ring + 1) % STAGE_RING;
+  if (D->ev_used[slot]) HIP_TRY(D, hipEventSynchronize(D->ev[slot]), "stage wait");
+  int32_t *h = D->pinned + (size_t)slot * 3 * D->L.R;
+  for (int r = 0; r < rows; ++r) {
+    h[r] = ids ? ids[r] : 0;
+    h[D->L.R + r] = seqs[r];
+    h[2 * D->L.R + r] = pos[r];
+  }
+  HIP_TRY(D, hipMemcpyAsync(D->ids, h, (size_t)3 * D->L.R * 4, hipMemcpyHostToDevice, D->stream),
+          "stage copy");
+  HIP_TRY(D, hipEventRecord(D->ev[slot], D->stream), "stage event");
+  D->ev_used[slot] = true;
+  return DEC_OK;
+}
+
+int gemm(decoder *D, int epi, const uint16_t *A, int64_t lda, const uint16_t *W, int M, int N, int K,
+         float *C, uint16_t *Hout, int64_t ldc, const float *bias) {
+  GemmArgs g{};
+  g.A = A;
+  g.lda = lda;
+  g.W = W;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.C = C;
+  g.Hout = Hout;
+  g.ldc = ldc;
+  g.bias = bias;
+  const int np = epi == EPI_SWIGLU ? 2 : 1;
+  const int ntiles = (N + 15) / 16;
+  const int steps = (K + 31) / 32;
+  int ks = 1;
+  if (ntiles < 192 && steps >= 16) {
+    ks = std::min(GEMM_MAX_SPLIT, std::max(1, 384 / ntiles));
+    ks = std::min(ks, steps / 8);
+    while (ks > 1 && (size_t)ks * M * np * N > D->L.gpart_elems) --ks;
+  }
+  g.ksplit = ks;
+  g.Cpart = D->gpart;
+  hipError_t e = launch_gemm(g, epi, M, 1, D->stream);
+  if (e != hipSuccess) return hip_fail(D, e, "gemm");
+  return DEC_OK;
+}
+
+int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos) {
+  const decoder_config_t &c = D->c;
+  AttnArgs a{};
+  a.q = D->q;
+  a.out = D->attn;
+  a.kcache = D->kcache;
+  a.vcache = D->vcache;
+  a.row_seq = D->row_seq;
+  a.row_pos = D->row_pos;
+  a.seq_stride = D->L.seq_stride;
+  a.layer_off = (int64_t)layer * c.n_kv_heads * (int64_t)D->L.S * c.head_dim;
+  a.S = D->L.S;
+  a.Hq = c.n_heads;
+  a.Hkv = c.n_kv_heads;
+  a.G = c.n_heads / c.n_kv_heads;
+  a.rows = rows;
+  a.rows_per_group = rows_per_group;
+  a.n_groups = (rows + rows_per_group - 1) / rows_per_group * c.n_kv_heads;
+  const int keys = max_pos + 1;
+  const int tiles = (keys + 31) / 32;
+  int ns = std::max(1, std::min((ATTN_TARGET_TASKS + a.n_groups - 1) / a.n_groups, tiles));
+  int kc = (int)align_up((size_t)((keys + ns - 1) / ns), 32);
+  ns = (keys + kc - 1) / kc;
+  while ((int64_t)a.n_groups * ns > ATTN_MAX_TASKS) {
+    kc *= 2;
+    ns = (keys + kc - 1) / kc;
+  }
+  a.kc = kc;
+  a.n_splits = ns;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+  a.part_o = D->part_o;
+  a.part_ml = D->part_ml;
+  hipError_t e = launch_attention(a, c.head_dim, D->stream);
+  if (e != hipSuccess) return hip_fail(D, e, "attention");
+  return DEC_OK;
+}
+
+int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos) {
+  const decoder_config_t &c = D->c;
+  const decoder_layer_weights_t &W = D->layers[l];
+  const int H = c.hidden, d = c.head_dim, qd = c.n_heads * d;
+  const int qkvr = (c.n_heads + 2 * c.n_kv_heads) * d;
+  const float eps = (float)c.rms_eps;
+  hipStream_t st = D->stream;
+  int rc;
+  hipError_t e;
+
+  e = launch_rmsnorm(D->x, H, W.attn_norm, rows, H, eps, D->act, H, st);
+  if (e != hipSuccess) return hip_fail(D, e, "rmsnorm");
+  if ((rc = gemm(D, EPI_STORE, D->act, H, W.w_qkv, rows, qkvr, H, D->qkv, nullptr, qkvr, nullptr))) return rc;
+  RopeArgs ra{};
+  ra.qkv = D->qkv;
+  ra.bias = c.qkv_bias ? W.b_qkv : nullptr;
+  ra.cs = D->rope;
+  ra.row_seq = D->row_seq;
+  ra.row_pos = D->row_pos;
+  ra.q = D->q;
+  ra.kcache = D->kcache;
+  ra.vcache = D->vcache;
+  ra.seq_stride = D->L.seq_stride;
+  ra.layer_off = (int64_t)l * c.n_kv_heads * (int64_t)D->L.S * d;
+  ra.S = D->L.S;
+  ra.Hq = c.n_heads;
+  ra.Hkv = c.n_kv_heads;
+  ra.d = d;
+  ra.rows = rows;
+  e = launch_rope_append(ra, st);
+  if (e != hipSuccess) return hip_fail(D, e, "rope_append");
+  if ((rc = attention(D, l, rows, rows_per_group, max_pos))) return rc;
+  if ((rc = gemm(D, EPI_ADD, D->attn, qd, W.w_o, rows, H, qd, D->x, nullptr, H, nullptr))) return rc;
+  e = launch_rmsnorm(D->x, H, W.ffn_norm, rows, H, eps, D->act, H, st);
+  if (e != hipSuccess) return hip_fail(D, e, "rmsnorm");
+
+  if (c.n_experts == 0) {
+    const int I = c.ffn_inter;
+    if ((rc = gemm(D, EPI_SWIGLU, D->act, H, W.w_gate_up, rows, I, H, nullptr, D->h, I, nullptr))) return rc;
+    if ((rc = gemm(D, EPI_ADD, D->h, I, W.w_down, rows, H, I, D->x, nullptr, H, nullptr))) return rc;
+    return DEC_OK;
+  }
+  // routed experts + shared expert
+  const int E = c.n_experts, k = c.top_k, Ie = c.expert_inter, Is = c.shared_inter;
+  if ((rc = gemm(D, EPI_STORE, D->act, H, W.w_router, rows, E, H, D->rlogits, nullptr, E, nullptr))) return rc;
+  MoeRouteArgs mr{};
+  mr.logits = D->rlogits;
+  mr.act = D->act;
+  mr.w_sh_gate = (Is > 0 && c.shared_gate) ? W.w_sh_gate : nullptr;
+  mr.rows = rows;
+  mr.E = E;
+  mr.k = k;
+  mr.H = H;
+  mr.renorm = c.norm_topk_prob;
+  mr.ids = D->rids;
+  mr.wts = D->rwts;
+  mr.gate = D->rgate;
+  mr.ids_record = D->rids_rec + (size_t)l * rows * k;
+  mr.n_groups = D->groups;
+  mr.group_expert = D->groups + 1;
+  mr.group_start = D->groups + 1 + E;
+  mr.group_count = D->groups + 1 + 2 * E;
+  mr.pair_row = D->pair_row;
+  mr.pair_of = D->pair_of;
+  e = launch_moe_route(mr, st);
+  if (e != hipSuccess) return hip_fail(D, e, "moe_route");
+  const int slots = std::min(E, rows * k);
+  const int grp_rows = std::min(rows, 32);
+  GemmArgs g{};
+  g.A = D->act;
+  g.a_rows = D->pair_row;
+  g.lda = H;
+  g.W = W.w_exp_gate_up;
+  g.w_group_stride = (int64_t)2 * Ie * H;
+  g.M = rows * k;
+  g.N = Ie;
+  g.K = H;
+  g.Hout = D->hexp;
+  g.ldc = Ie;
+  g.n_groups = mr.n_groups;
+  g.group_expert = mr.group_expert;
+  g.group_start = mr.group_start;
+  g.group_count = mr.group_count;
+  g.ksplit = 1;
+  e = launch_gemm(g, EPI_SWIGLU, grp_rows, slots, st);
+  if (e != hipSuccess) return hip_fail(D, e, "moe gate_up");
+  g.A = D->hexp;
+  g.a_rows = nullptr;
+  g.lda = Ie;
+  g.W = W.w_exp_down;
+  g.w_group_stride = (int64_t)H * Ie;
+  g.N = H;
+  g.K = Ie;
+  g.Hout = nullptr;
+  g.C = D->yexp;
+  g.ldc = H;
+  e = launch_gemm(g, EPI_STORE, grp_rows, slots, st);
+  if (e != hipSuccess) return hip_fail(D, e, "moe down");
+  if (Is > 0) {
+    if ((rc = gemm(D, EPI_SWIGLU, D->act, H, W.w_sh_gate_up, rows, Is, H, nullptr, D->hsh, Is, nullptr))) return rc;
+    if ((rc = gemm(D, EPI_STORE, D->hsh, Is, W.w_sh_down, rows, H, Is, D->ysh, nullptr, H, nullptr))) return rc;
+  }
+  e = launch_moe_combine(D->x, D->yexp, Is > 0 ? D->ysh : nullptr, D->rwts, D->rgate, D->pair_of, rows,
+                         k, H, st);
+  if (e != hipSuccess) return hip_fail(D, e, "moe combine");
+  return DEC_OK;
+}
+
+// Embedding, all layers, then (optionally) final norm + lm-head + argmax on
+// rows [first, first + nout).
+int run_step(decoder *D, int rows, int rows_per_group, int max_pos, int use_next, int first,
+             int nout, float *d_logits, int32_t *d_argmax, int argmax_rows) {
+  const decoder_config_t &c = D->c;
+  hipStream_t st = D->stream;
+  hipError_t e = launch_embed(D->embed, D->ids, D->next_token, D->row_seq, use_next, rows, c.hidden,
+                              D->x, st);
+  if (e != hipSuccess) return hip_fail(D, e, "embed");
+  const int nl = D->layer_limit >= 0 ? std::min(D->layer_limit, c.n_layers) : c.n_layers;
+  for (int l = 0; l < nl; ++l) {
+    int rc = run_layer(D, l, rows, rows_per_group, max_pos);
+    if (rc) return rc;
+  }
+  D->last_rows = rows;
+  if (nout <= 0) return DEC_OK;
+  const int H = c.hidden;
+  e = launch_rmsnorm(D->x + (size_t)first * H, H, D->final_norm, nout, H, (float)c.rms_eps, D->act, H, st);
+  if (e != hipSuccess) return hip_fail(D, e, "final rmsnorm");
+  float *out = d_logits ? d_logits : D->logits;
+  int rc = gemm(D, EPI_STORE, D->act, H, D->lm_head, nout, c.vocab, H, out, nullptr, c.vocab, nullptr);
+  if (rc) return rc;
+  // argmax over the last argmax_rows output rows; row r of the output belongs
+  // to input row first + r
+  const int a0 = nout - argmax_rows;
+  e = launch_argmax(out + (size_t)a0 * c.vocab, c.vocab, argmax_rows, c.vocab, d_argmax, D->next_token,
+                    D->row_seq + first + a0, st);
+  if (e != hipSuccess) return hip_fail(D, e, "argmax");
+  return DEC_OK;
+}
+
+int check_dec(const decoder *D) { return D ? DEC_OK : DEC_E_INVALID; }
+
+}  // namespace
+
+// ------------------------------------------------------------------ ABI --
+
+extern "C" {
+
+size_t decoder_workspace_bytes(const decoder_config_t *cfg) {
+  if (!config_ok(cfg)) return 0;
+  return make_layout(cfg).total;
+}
+
+const char *decoder_strerror(int code) {
+  switch (code) {
+    case DEC_OK: return "ok";
+    case DEC_E_CONTEXT_OVERFLOW: return "context overflow";
+    case DEC_E_INVALID: return "invalid argument";
+    case DEC_E_TOKEN: return "token id out of range";
+    case DEC_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case DEC_E_HIP: return "HIP runtime error";
+    default: return "unknown error";
+  }
+}
+
+const char *decoder_last_error(const decoder_t *dec) { return dec ? dec->err.c_str() : ""; }
+
+int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *d_workspace,
+                 size_t workspace_bytes, void *stream, decoder_t **out) {
+  if (!out) return DEC_E_INVALID;
+  *out = nullptr;
+  if (!config_ok(cfg) || !w || !w->layers || !w->embed || !w->lm_head || !w->final_norm)
+    return DEC_E_INVALID;
+  const Layout L = make_layout(cfg);
+  if (!d_workspace || workspace_bytes < L.total || ((uintptr_t)d_workspace & 255)) return DEC_E_WORKSPACE;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const decoder_layer_weights_t &lw = w->layers[l];
+    if (!lw.attn_norm || !lw.ffn_norm || !lw.w_qkv || !lw.w_o) return DEC_E_INVALID;
+    if (cfg->qkv_bias && !lw.b_qkv) return DEC_E_INVALID;
+    if (cfg->n_experts == 0 && (!lw.w_gate_up || !lw.w_down)) return DEC_E_INVALID;
+    if (cfg->n_experts > 0) {
+      if (!lw.w_router || !lw.w_exp_gate_up || !lw.w_exp_down) return DEC_E_INVALID;
+      if (cfg->shared_inter > 0 && (!lw.w_sh_gate_up || !lw.w_sh_down)) return DEC_E_INVALID;
+      if (cfg->shared_inter > 0 && cfg->shared_gate && !lw.w_sh_gate) return DEC_E_INVALID;
+    }
+  }
+  decoder *D = new decoder();
+  D->c = *cfg;
+  D->L = L;
+  D->layers.assign(w->layers, w->layers + cfg->n_layers);
+  D->embed = w->embed;
+  D->lm_head = w->lm_head;
+  D->final_norm = w->final_norm;
+  D->stream = (hipStream_t)stream;
+  D->ws = (char *)d_workspace;
+  D->kcache = carve<uint16_t>(D, L.kcache);
+  D->vcache = carve<uint16_t>(D, L.vcache);
+  D->rope = carve<float2>(D, L.rope);
+  D->x = carve<float>(D, L.x);
+  D->act = carve<uint16_t>(D, L.act);
+  D->attn = carve<uint16_t>(D, L.attn);
+  D->q = carve<uint16_t>(D, L.q);
+  D->qkv = carve<float>(D, L.qkv);
+  D->h = carve<uint16_t>(D, L.h);
+  D->logits = carve<float>(D, L.logits);
+  D->ids = carve<int32_t>(D, L.stage);
+  D->row_seq = D->ids + L.R;
+  D->row_pos = D->ids + 2 * L.R;
+  D->next_token = carve<int32_t>(D, L.next_token);
+  D->part_o = carve<float>(D, L.part_o);
+  D->part_ml = carve<float>(D, L.part_ml);
+  D->gpart = carve<float>(D, L.gpart);
+  if (cfg->n_experts > 0) {
+    D->rlogits = carve<float>(D, L.rlogits);
+    D->rids = carve<int32_t>(D, L.rids);
+    D->rids_rec = carve<int32_t>(D, L.rids_rec);
+    D->rwts = carve<float>(D, L.rwts);
+    D->rgate = carve<float>(D, L.rgate);
+    D->groups = carve<int32_t>(D, L.groups);
+    D->pair_row = carve<int32_t>(D, L.pair_row);
+    D->pair_of = carve<int32_t>(D, L.pair_of);
+    D->hexp = carve<uint16_t>(D, L.hexp);
+    D->yexp = carve<float>(D, L.yexp);
+    D->hsh = carve<uint16_t>(D, L.hsh);
+    D->ysh = carve<float>(D, L.ysh);
+  } else {
+    D->rlogits = D->rwts = D->rgate = D->yexp = D->ysh = nullptr;
+    D->rids = D->rids_rec = D->groups = D->pair_row = D->pair_of = nullptr;
+    D->hexp = D->hsh = nullptr;
+  }
+  D->len.assign(cfg->max_batch, 0);
+  D->has_next.assign(cfg->max_batch, 0);
+  D->kv_pending.assign(cfg->max_batch, std::vector<int32_t>(cfg->n_layers, -1));
+  for (int i = 0; i < STAGE_RING; ++i) D->ev_used[i] = false;
+
+  auto cleanup = [&](int code) {
+    if (D->pinned) (void)hipHostFree(D->pinned);
+    for (int i = 0; i < STAGE_RING; ++i) (void)hipEventDestroy(D->ev[i]);
+    delete D;
+    return code;
+  };
+  if (hipHostMalloc((void **)&D->pinned, (size_t)STAGE_RING * 3 * L.R * 4, hipHostMallocDefault) != hipSuccess) {
+    D->pinned = nullptr;
+    return cleanup(DEC_E_HIP);
+  }
+  for (int i = 0; i < STAGE_RING; ++i)
+    if (hipEventCreateWithFlags(&D->ev[i], hipEventDisableTiming) != hipSuccess) return cleanup(DEC_E_HIP);
+
+  // RoPE table: angle pos * base^(-2i/d) evaluated in fp64, stored as fp32
+  // (cos, sin) pairs (pipeline.rs Pipeline::new keeps a head_dim/2 table of
+  // inverse frequencies).
+  const int half = cfg->head_dim / 2;
+  std::vector<float2> tab((size_t)L.S * half);
+  for (int p = 0; p < L.S; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double ang = (double)p * std::pow(cfg->rope_base, -2.0 * i / cfg->head_dim);
+      tab[(size_t)p * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+    }
+  if (hipMemcpy(D->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess)
+    return cleanup(DEC_E_HIP);
+  const size_t kvb = (size_t)cfg->max_batch * L.seq_stride * 2;
+  if (hipMemsetAsync(D->kcache, 0, kvb, D->stream) != hipSuccess ||
+      hipMemsetAsync(D->vcache, 0, kvb, D->stream) != hipSuccess ||
+      hipMemsetAsync(D->next_token, 0, (size_t)cfg->max_batch * 4, D->stream) != hipSuccess ||
+      hipStreamSynchronize(D->stream) != hipSuccess)
+    return cleanup(DEC_E_HIP);
+  *out = D;
+  return DEC_OK;
+}
+
+void decoder_free(decoder_t *D) {
+  if (!D) return;
+  (void)hipStreamSynchronize(D->stream);
+  if (D->pinned) (void)hipHostFree(D->pinned);
+  for (int i = 0; i < STAGE_RING; ++i) (void)hipEventDestroy(D->ev[i]);
+  delete D;
+}
+
+int decoder_set_stream(decoder_t *D, void *stream) {
+  if (!D) return DEC_E_INVALID;
+  D->stream = (hipStream_t)stream;
+  return DEC_OK;
+}
+
+int32_t decoder_seq_len(const decoder_t *D, int32_t seq) {
+  if (!D || seq < 0 || seq >= D->c.max_batch) return -1;
+  return D->len[seq];
+}
+
+int prefill_chunk(decoder_t *D, int32_t seq, const int32_t *ids, int32_t n, int32_t start_pos,
+                  int32_t logits_mode, float *d_logits, int32_t *d_argmax) {
+  if (check_dec(D)) return DEC_E_INVALID;
+  const decoder_config_t &c = D->c;
+  if (seq < 0 || seq >= c.max_batch) return fail(D, DEC_E_INVALID, "seq out of range");
+  if (!ids || n <= 0 || n > c.max_chunk) return fail(D, DEC_E_INVALID, "chunk length outside [1, max_chunk]");
+  if (logits_mode < 0 || logits_mode > 2) return fail(D, DEC_E_INVALID, "logits_mode");
+  if (start_pos != D->len[seq]) return fail(D, DEC_E_INVALID, "start_pos differs from the sequence length");
+  if ((int64_t)start_pos + n > c.max_seq) return fail(D, DEC_E_CONTEXT_OVERFLOW, "prefill past max_seq");
+  for (int i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= c.vocab) return fail(D, DEC_E_TOKEN, "token id out of range");
+  std::vector<int32_t> seqs(n, seq), pos(n);
+  for (int i = 0; i < n; ++i) pos[i] = start_pos + i;
+  int rc = stage_rows(D, n, ids, seqs.data(), pos.data());
+  if (rc) return rc;
+  const int G = c.n_heads / c.n_kv_heads;
+  const int nout = logits_mode == 0 ? 0 : (logits_mode == 1 ? 1 : n);
+  const int first = logits_mode == 1 ? n - 1 : 0;
+  rc = run_step(D, n, 16 / G, start_pos + n - 1, 0, first, nout, d_logits, d_argmax, nout ? 1 : 0);
+  if (rc) return rc;
+  D->len[seq] = start_pos + n;
+  if (nout) D->has_next[seq] = 1;
+  return DEC_OK;
+}
+
+int decode_step(decoder_t *D, int32_t batch, const int32_t *seqs, const int32_t *tokens,
+                float *d_logits, int32_t *d_argmax) {
+  if (check_dec(D)) return DEC_E_INVALID;
+  const decoder_config_t &c = D->c;
+  if (batch <= 0 || batch > c.max_batch || !seqs) return fail(D, DEC_E_INVALID, "batch outside [1, max_batch]");
+  std::vector<int32_t> pos(batch);
+  int max_pos = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int s = seqs[b];
+    if (s < 0 || s >= c.max_batch) return fail(D, DEC_E_INVALID, "seq out of range");
+    for (int b2 = 0; b2 < b; ++b2)
+      if (seqs[b2] == s) return fail(D, DEC_E_INVALID, "duplicate seq in batch");
+    if (D->len[s] >= c.max_seq) return fail(D, DEC_E_CONTEXT_OVERFLOW, "sequence full");
+    if (tokens) {
+      if (tokens[b] < 0 || tokens[b] >= c.vocab) return fail(D, DEC_E_TOKEN, "token id out of range");
+    } else if (!D->has_next[s]) {
+      return fail(D, DEC_E_INVALID, "no previous greedy token for this sequence");
+    }
+    pos[b] = D->len[s];
+    max_pos = std::max(max_pos, pos[b]);
+  }
+  int rc = stage_rows(D, batch, tokens, seqs, pos.data());
+  if (rc) return rc;
+  rc = run_step(D, batch, 1, max_pos, tokens ? 0 : 1, 0, batch, d_logits, d_argmax, batch);
+  if (rc) return rc;
+  for (int b = 0; b < batch; ++b) {
+    D->len[seqs[b]] += 1;
+    D->has_next[seqs[b]] = 1;
+  }
+  return DEC_OK;
+}
+
+int kv_reset(decoder_t *D, int32_t seq) {
+  if (check_dec(D)) return DEC_E_INVALID;
+  const decoder_config_t &c = D->c;
+  if (seq < -1 || seq >= c.max_batch) return fail(D, DEC_E_INVALID, "seq out of range");
+  const int s0 = seq < 0 ? 0 : seq, s1 = seq < 0 ? c.max_batch : seq + 1;
+  const size_t bytes = (size_t)(s1 - s0) * D->L.seq_stride * 2;
+  HIP_TRY(D, hipMemsetAsync(D->kcache + (size_t)s0 * D->L.seq_stride, 0, bytes, D->stream), "kv_reset");
+  HIP_TRY(D, hipMemsetAsync(D->vcache + (size_t)s0 * D->L.seq_stride, 0, bytes, D->stream), "kv_reset");
+  for (int s = s0; s < s1; ++s) {
+    D->len[s] = 0;
+    D->has_next[s] = 0;
+    std::fill(D->kv_pending[s].begin(), D->kv_pending[s].end(), -1);
+  }
+  return DEC_OK;
+}
+
+int kv_load(decoder_t *D, int32_t seq, int32_t layer, const uint16_t *d_k, const uint16_t *d_v,
+            int32_t len) {
+  if (check_dec(D)) return DEC_E_INVALID;
+  const decoder_config_t &c = D->c;
+  if (seq < 0 || seq >= c.max_batch || layer < 0 || layer >= c.n_layers || !d_k || !d_v)
+    return fail(D, DEC_E_INVALID, "kv_load argument");
+  if (len < 0) return fail(D, DEC_E_INVALID, "kv_load length");
+  if (len > c.max_seq) return fail(D, DEC_E_CONTEXT_OVERFLOW, "kv_load past max_seq");
+  const int d = c.head_dim, S = D->L.S;
+  const int64_t loff = (int64_t)seq * D->L.seq_stride + (int64_t)layer * c.n_kv_heads * (int64_t)S * d;
+  for (int g = 0; g < c.n_kv_heads; ++g)
+    HIP_TRY(D, hipMemcpyAsync(D->kcache + loff + (int64_t)g * S * d, d_k + (int64_t)g * len * d,
+                              (size_t)len * d * 2, hipMemcpyDeviceToDevice, D->stream), "kv_load k");
+  if (len > 0) HIP_TRY(D, launch_kv_load_v(d_v, D->vcache + loff, c.n_kv_heads, len, d, S, D->stream), "kv_load v");
+  D->kv_pending[seq][layer] = len;
+  bool all = true;
+  for (int l = 0; l < c.n_layers; ++l) all = all && D->kv_pending[seq][l] == len;
+  if (all) {
+    D->len[seq] = len;
+    D->has_next[seq] = 0;
+    std::fill(D->kv_pending[seq].begin(), D->kv_pending[seq].end(), -1);
+  }
+  return DEC_OK;
+}
+
+// ----------------------------------------------------------------- diag --
+
+int dec_diag_gemm(const uint16_t *d_A, int32_t M, int32_t K, const uint16_t *d_W, int32_t N, float *d_C,
+                  void *stream) {
+  if (!d_A || !d_W || !d_C || M < 1 || M > 256 || N < 1 || K < 8 || K % 8) return DEC_E_INVALID;
+  GemmArgs g{};
+  g.A = d_A;
+  g.lda = K;
+  g.W = d_W;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.C = d_C;
+  g.ldc = N;
+  g.ksplit = 1;
+  return launch_gemm(g, EPI_STORE, M, 1, (hipStream_t)stream) == hipSuccess ? DEC_OK : DEC_E_HIP;
+}
+
+int dec_diag_rmsnorm(const float *d_x, const float *d_g, int32_t rows, int32_t H, double eps, uint16_t *d_out,
+                     void *stream) {
+  if (!d_x || !d_g || !d_out || rows < 1 || H < 4 || H % 4) return DEC_E_INVALID;
+  return launch_rmsnorm(d_x, H, d_g, rows, H, (float)eps, d_out, H, (hipStream_t)stream) == hipSuccess
+             ? DEC_OK
+             : DEC_E_HIP;
+}
+
+int decoder_debug_layer_limit(decoder_t *D, int32_t layers) {
+  if (check_dec(D)) return DEC_E_INVALID;
+  D->layer_limit = layers;
+  return DEC_OK;
+}
+
+int decoder_debug_read_x(decoder_t *D, float *d_out, int32_t rows) {
+  if (check_dec(D) || !d_out || rows < 1 || rows > D->L.R) return DEC_E_INVALID;
+  HIP_TRY(D, hipMemcpyAsync(d_out, D->x, (size_t)rows * D->c.hidden * 4, hipMemcpyDeviceToDevice, D->stream),
+          "read_x");
+  return DEC_OK;
+}
+
+int decoder_debug_read_routes(decoder_t *D, int32_t *d_out, int32_t rows) {
+  if (check_dec(D) || !d_out || rows < 1 || rows > D->L.R || D->c.n_experts == 0) return DEC_E_INVALID;
+  HIP_TRY(D, hipMemcpyAsync(d_out, D->rids_rec, (size_t)D->c.n_layers * rows * D->c.top_k * 4,
+                            hipMemcpyDeviceToDevice, D->stream), "read_routes");
+  return DEC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+/*
+ * decoder.h -- C ABI of libdecoder.so: one forward step of a decoder-only
+ * GQA transformer on an MI355X (gfx950), for single-token decode (batch of
+ * sequences) and chunked prefill, ending in the lm-head and a greedy argmax.
+ *
+ * The block (frink_models/decoder.rs, module doc; engine.zig, Engine.forward):
+ *   x = E[token]
+ *   per layer:  a = RMSNorm(x; g_attn)                 (engine.zig rmsnormColumn)
+ *               [q;k;v] = W_qkv a (+ b_qkv)            (decoder.rs AttnWeights: bias before RoPE)
+ *               q, k rotated at their position (RoPE),  (engine.zig ropeAndCache)
+ *               k, v appended to the layer's KV cache
+ *               o = causal GQA softmax attention        (engine.zig Engine.forward, attentionDecode;
+ *                                                        pipeline.rs Pipeline::new: scale 1/sqrt(d))
+ *               x += W_o o
+ *               b = RMSNorm(x; g_ffn)
+ *               x += W_down(silu(W_gate b) * W_up b)    dense SwiGLU, or
+ *               x += sum_top-k p_e FFN_e(b) + sigmoid(w_sg . b) FFN_shared(b)
+ *                                                       (pipeline.rs MoeFfn; engine.zig Engine.forward
+ *                                                        shared-expert gate; decoder.rs MoeWeights)
+ *   logits = W_head RMSNorm(x; g_final)                 (pipeline.rs lm_head_forward)
+ *   next token = argmax(logits), lowest id on ties.
+ * Prefill/decode contract (pipeline.rs module doc): every token is forwarded
+ * exactly once and enters the KV cache exactly once.
+ *
+ * Readings where the pages leave a step open: RoPE pairs element i with
+ * element i + d/2 and rotates it by pos * base^(-2i/d); q head h reads kv
+ * head floor(h * Hkv / Hq); top-k ties go to the lower expert index.
+ *
+ * Conventions
+ *  - All matrices are bf16 (uint16 bit patterns), row-major [out][in].
+ *    Norm gains and biases are fp32.  Logits are fp32.
+ *  - Weight pointers are DEVICE pointers, BORROWED: the caller keeps them
+ *    alive and unchanged until decoder_free (engine.zig module doc: the
+ *    engine borrows its weights, which must outlive it).
+ *  - The caller allocates one device workspace of decoder_workspace_bytes()
+ *    bytes and passes it in; the library lays out the KV cache, the RoPE
+ *    table and all scratch inside it and never allocates device memory.
+ *  - Token ids and sequence indices are HOST arrays (validated on the host
+ *    before anything is launched).  Output buffers are DEVICE pointers.
+ *  - Every call is asynchronous on the decoder's stream; only the returned
+ *    status is synchronous.  Outputs are valid once the stream has drained.
+ *  - A failing call returns a nonzero DEC_E_* code and launches nothing
+ *    (DEC_E_HIP excepted: the HIP error text is kept for decoder_last_error).
+ *    There is no silent fallback to another code path.
+ */
+#ifndef DECODER_H
+#define DECODER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DEC_OK = 0,
+  DEC_E_CONTEXT_OVERFLOW = 1, /* start_pos + n > max_seq, or a full sequence on decode */
+  DEC_E_INVALID = 2,          /* bad argument: n <= 0, n > max_chunk, batch > max_batch,
+                                 start_pos != current length, bad seq, bad config, ... */
+  DEC_E_TOKEN = 3,            /* token id outside [0, vocab) */
+  DEC_E_WORKSPACE = 4,        /* workspace NULL, too small or misaligned */
+  DEC_E_HIP = 5,              /* a HIP runtime call failed */
+};
+
+typedef struct decoder decoder_t; /* opaque */
+
+typedef struct {
+  int32_t hidden;          /* H */
+  int32_t n_layers;        /* L */
+  int32_t n_heads;         /* Hq */
+  int32_t n_kv_heads;      /* Hkv; Hq % Hkv == 0 and Hq / Hkv <= 16 */
+  int32_t head_dim;        /* d: 64 or 128 */
+  int32_t ffn_inter;       /* I: dense SwiGLU width; 0 for an MoE model */
+  int32_t n_experts;       /* E (0 for a dense model), <= 256 */
+  int32_t top_k;           /* k <= 8 */
+  int32_t expert_inter;    /* Ie */
+  int32_t shared_inter;    /* Is; 0 = no shared expert */
+  int32_t shared_gate;     /* 1: shared expert scaled by sigmoid(w_sg . b) */
+  int32_t norm_topk_prob;  /* 1: renormalise the top-k probabilities to sum to one */
+  int32_t vocab;           /* V */
+  int32_t qkv_bias;        /* 1: b_qkv is present */
+  double rope_base;        /* RoPE base */
+  double rms_eps;          /* RMSNorm epsilon */
+  int32_t max_seq;         /* KV capacity per sequence (positions) */
+  int32_t max_chunk;       /* largest prefill chunk (tokens per call), <= 256 */
+  int32_t max_batch;       /* number of sequences (KV slots); largest decode batch */
+} decoder_config_t;
+
+typedef struct {
+  const float *attn_norm;          /* [H] */
+  const float *ffn_norm;           /* [H] */
+  const uint16_t *w_qkv;           /* [(Hq + 2 Hkv) d][H]: q rows, then k rows, then v rows */
+  const float *b_qkv;              /* [(Hq + 2 Hkv) d], or NULL when qkv_bias == 0 */
+  const uint16_t *w_o;             /* [H][Hq d] */
+  const uint16_t *w_gate_up;       /* dense: [2 I][H], gate rows then up rows */
+  const uint16_t *w_down;          /* dense: [H][I] */
+  const uint16_t *w_router;        /* MoE: [E][H] */
+  const uint16_t *w_exp_gate_up;   /* MoE: [E][2 Ie][H] */
+  const uint16_t *w_exp_down;      /* MoE: [E][H][Ie] */
+  const uint16_t *w_sh_gate_up;    /* MoE shared expert: [2 Is][H] */
+  const uint16_t *w_sh_down;       /* MoE shared expert: [H][Is] */
+  const uint16_t *w_sh_gate;       /* MoE shared-expert gate vector: [H] (when shared_gate) */
+} decoder_layer_weights_t;
+
+typedef struct {
+  const uint16_t *embed;                  /* [V][H] */
+  const float *final_norm;                /* [H] */
+  const uint16_t *lm_head;                /* [V][H]; pass embed for tied embeddings */
+  const decoder_layer_weights_t *layers;  /* HOST array [n_layers]; copied by decoder_init */
+} decoder_weights_t;
+
+/* Bytes of device workspace decoder_init needs for this config (KV cache,
+ * RoPE table, activations and scratch), or 0 if the config is invalid. */
+size_t decoder_workspace_bytes(const decoder_config_t *cfg);
+
+/* Validate the config, record the borrowed weights, lay out the workspace
+ * (256-byte aligned; its contents are overwritten), upload the RoPE table
+ * and zero the KV cache.  stream is a hipStream_t (NULL = default stream).
+ * On success *out owns host-side state only; free it with decoder_free. */
+int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *weights,
+                 void *d_workspace, size_t workspace_bytes, void *stream, decoder_t **out);
+
+/* Forward n prompt tokens (host ids[n], 1 <= n <= max_chunk) of sequence
+ * seq at positions start_pos .. start_pos+n-1; start_pos must equal the
+ * sequence's current length (engine.zig Engine.prefill; pipeline.rs module
+ * doc).  start_pos + n == max_seq is allowed; more is DEC_E_CONTEXT_OVERFLOW.
+ * logits_mode: 0 no logits, 1 the last token's logits ([V] into d_logits),
+ * 2 every token's logits ([n][V]).  d_logits may be NULL (then logits go to
+ * internal scratch).  When logits are computed, the greedy next token of the
+ * last row is kept for decode_step(tokens = NULL) and, if d_argmax is not
+ * NULL, written to d_argmax[0] (int32). */
+int prefill_chunk(decoder_t *dec, int32_t seq, const int32_t *ids, int32_t n,
+                  int32_t start_pos, int32_t logits_mode, float *d_logits, int32_t *d_argmax);
+
+/* One decode step for batch sequences (host seqs[batch], distinct): each
+ * forwards one token at position len[seq] and appends it to its cache.
+ * tokens: host [batch] ids, or NULL to feed each sequence's own previous
+ * greedy token (kept on the device; no host round trip).  d_logits
+ * ([batch][V] fp32) and d_argmax ([batch] int32) may each be NULL. */
+int decode_step(decoder_t *dec, int32_t batch, const int32_t *seqs, const int32_t *tokens,
+                float *d_logits, int32_t *d_argmax);
+
+/* Forget sequence seq (-1: all sequences): its length becomes 0 and its KV
+ * rows are zeroed (engine.zig Engine.reset). */
+int kv_reset(decoder_t *dec, int32_t seq);
+
+/* Install a KV-cache prefix for one layer of one sequence from device
+ * buffers d_k, d_v, both bf16 [Hkv][len][d] (keys already rotated).  The
+ * sequence's length becomes len once every layer has been loaded with the
+ * same len (call in any layer order; the length is set on the last layer).
+ * decoder.rs: restoring a prefix into a resident device KV. */
+int kv_load(decoder_t *dec, int32_t seq, int32_t layer, const uint16_t *d_k,
+            const uint16_t *d_v, int32_t len);
+
+/* Current length (cached positions) of sequence seq, or -1 if seq is invalid. */
+int32_t decoder_seq_len(const decoder_t *dec, int32_t seq);
+
+/* Replace the stream all later calls launch on (hipStream_t). */
+int decoder_set_stream(decoder_t *dec, void *stream);
+
+void decoder_free(decoder_t *dec);
+const char *decoder_strerror(int code);
+/* Text of the last failure on this decoder (empty if none). */
+const char *decoder_last_error(const decoder_t *dec);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DECODER_H */

@@ -1,0 +1,234 @@
+"""GPU-vs-oracle parity on small shapes, through the C ABI.
+
+Inputs are seeded and synthetic (synth/): the same bf16 weights and token
+ids go to the oracle (host) and to the library (uploaded bit-identically).
+Decode is teacher-forced with the oracle's greedy tokens, so every step is
+compared on the same history.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth.weights import host_weights, prompt
+from synth.workloads import TINY, Shape
+from tests.gpu_util import assert_parity, compare_logits, decode, log, make_decoder, run_prefill
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def bits_of(x):
+    return synth.bf16_to_f32(x)
+
+
+# ------------------------------------------------------------ single kernels --
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 32), (1, 60, 2048), (5, 100, 688), (16, 64, 4096),
+                                   (37, 48, 576), (128, 32, 256), (200, 16, 64)])
+def test_projection_kernel_matches_numpy(M, N, K):
+    from decoder_only_transformer_step_amd.binding import diag_gemm
+    log("gemm", M, N, K)
+    A = synth.normal_bf16(M * K, 11 + M, 1.0)
+    W = synth.normal_bf16(N * K, 23 + N, 0.02)
+    dA = torch.from_numpy(A.view(np.int16)).cuda()
+    dW = torch.from_numpy(W.view(np.int16)).cuda()
+    dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    diag_gemm(dA.view(M, K), dW.view(N, K), dC, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = dC.cpu().numpy().astype(np.float64)
+    want = oracle.matmul(W, N, K, bits_of(A).astype(np.float64).reshape(M, K))
+    scale = np.abs(bits_of(A)).reshape(M, K).astype(np.float64) @ np.abs(bits_of(W)).reshape(N, K).T.astype(np.float64)
+    # fp32 accumulation of exact bf16 products: error bounded by ~K * 2^-24 * sum|a w|
+    assert np.all(np.abs(got - want) <= 1e-6 * K * scale + 1e-30)
+
+
+def test_rmsnorm_kernel_matches_oracle():
+    from decoder_only_transformer_step_amd.binding import diag_rmsnorm
+    rows, H = 7, 576
+    x = np.random.default_rng(1).normal(size=(rows, H)).astype(np.float32) * 3
+    g = (1 + 0.1 * np.random.default_rng(2).normal(size=H)).astype(np.float32)
+    out = torch.empty((rows, H), dtype=torch.int16, device="cuda")
+    diag_rmsnorm(torch.from_numpy(x).cuda(), torch.from_numpy(g).cuda(), 1e-5, out,
+                 torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = bits_of(out.cpu().numpy().view(np.uint16)).astype(np.float64)
+    for r in range(rows):
+        want = oracle.rmsnorm(x[r].astype(np.float64), g, 1e-5)
+        assert np.all(np.abs(got[r] - want) <= 2 ** -8 * np.abs(want) + 1e-30)
+
+
+# ------------------------------------------------------------- tiny model --
+
+def oracle_greedy(shape, W, ids, steps, chunk):
+    m = oracle.Model(shape, W)
+    out = m.prefill(ids, chunk)
+    logits = [out["logits"]]
+    toks = []
+    pos = len(ids)
+    for _ in range(steps):
+        t = oracle.argmax(logits[-1])
+        toks.append(t)
+        logits.append(m.forward([t], pos)["logits"])
+        pos += 1
+    return logits, toks
+
+
+@pytest.mark.parametrize("chunk", [16, 5])
+def test_tiny_prefill_then_teacher_forced_decode(chunk):
+    shape = TINY
+    W = host_weights(shape)
+    ids = prompt(shape, 16)
+    want, toks = oracle_greedy(shape, W, ids, 16, 16)
+    dec, _ = make_decoder(shape, W)
+    got = run_prefill(dec, ids, chunk)
+    st = compare_logits(got, want[0], "prefill")
+    log("prefill", st)
+    assert_parity(st, "prefill")
+    for i, t in enumerate(toks):
+        lg, am = decode(dec, [0], [t])
+        st = compare_logits(lg[0], want[i + 1], f"decode {i}")
+        assert_parity(st, f"decode {i}")
+        assert am[0] == int(np.argmax(lg[0]))
+    assert dec.seq_len(0) == 32
+
+
+def test_tiny_greedy_on_device_matches_oracle():
+    shape = TINY
+    W = host_weights(shape)
+    ids = prompt(shape, 16)
+    want, toks = oracle_greedy(shape, W, ids, 12, 16)
+    dec, _ = make_decoder(shape, W)
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    dec.prefill_chunk(0, [int(t) for t in ids], 0, logits_mode=1, logits=logits, argmax=am)
+    got = [int(am.item())]
+    for _ in range(11):
+        dec.decode_step([0], None, argmax=am)    # feeds back its own greedy token on the device
+        got.append(int(am.item()))
+    # the two greedy paths must agree until the first step whose oracle margin is small
+    for i in range(12):
+        lg = want[i]
+        top2 = np.sort(lg)[-2:]
+        if top2[1] - top2[0] <= 5e-2:
+            break
+        assert got[i] == toks[i], f"step {i}"
+
+
+def test_tiny_layer_trace():
+    shape = TINY
+    W = host_weights(shape)
+    ids = prompt(shape, 16)
+    tr = oracle.Model(shape, W).forward(ids, 0, logits_mode=0, trace=True)["trace"]
+    dec, _ = make_decoder(shape, W)
+    x = torch.empty((16, shape.hidden), dtype=torch.float32, device="cuda")
+    for layers in range(shape.n_layers + 1):
+        dec.kv_reset(0)
+        dec.debug_layer_limit(layers)
+        dec.prefill_chunk(0, [int(t) for t in ids], 0, logits_mode=0)
+        dec.debug_read_x(x, 16)
+        torch.cuda.synchronize()
+        got = x.cpu().numpy().astype(np.float64)
+        want = tr[layers]
+        err = np.abs(got - want).max() / np.abs(want).max()
+        log("layer", layers, "rel max err", err)
+        assert err < 1e-2
+
+
+def test_tiny_errors_and_reset():
+    from decoder_only_transformer_step_amd import DecoderError
+    shape = TINY
+    W = host_weights(shape)
+    ids = [int(t) for t in prompt(shape, 16)]
+    dec, _ = make_decoder(shape, W)
+    with pytest.raises(DecoderError) as e:
+        dec.prefill_chunk(0, [], 0)
+    assert e.value.code == 2
+    with pytest.raises(DecoderError) as e:
+        dec.prefill_chunk(0, [shape.vocab], 0)
+    assert e.value.code == 3
+    with pytest.raises(DecoderError) as e:
+        dec.prefill_chunk(0, ids, 3)              # start_pos must equal the length (0)
+    assert e.value.code == 2
+    with pytest.raises(DecoderError) as e:
+        dec.prefill_chunk(0, ids + [1], 0)        # longer than max_chunk
+    assert e.value.code == 2
+    with pytest.raises(DecoderError) as e:
+        dec.decode_step([0], None)                # no greedy token yet
+    assert e.value.code == 2
+    first = run_prefill(dec, ids, 16)
+    # fill the cache exactly: 16 + 3*16 = 64 = max_seq is allowed
+    for c in range(3):
+        dec.prefill_chunk(0, ids, 16 + 16 * c, logits_mode=0)
+    assert dec.seq_len(0) == 64
+    with pytest.raises(DecoderError) as e:
+        dec.decode_step([0], [1])
+    assert e.value.code == 1
+    dec.kv_reset(0)
+    assert dec.seq_len(0) == 0
+    again = run_prefill(dec, ids, 16)
+    assert np.array_equal(first, again)           # deterministic after reset
+
+
+def test_tiny_batched_decode_matches_per_sequence_oracle():
+    shape = TINY.with_(max_batch=3)
+    W = host_weights(shape)
+    dec, _ = make_decoder(shape, W)
+    prompts = [prompt(shape, n, seq=s) for s, n in enumerate((16, 9, 13))]
+    models, last = [], []
+    for s, p in enumerate(prompts):
+        m = oracle.Model(shape, W)
+        last.append(m.forward(p, 0)["logits"])
+        models.append(m)
+        run_prefill(dec, p, 16, seq=s)
+    for step in range(6):
+        toks = [oracle.argmax(l) for l in last]
+        lg, am = decode(dec, [2, 0, 1], [toks[2], toks[0], toks[1]])
+        for b, s in enumerate([2, 0, 1]):
+            want = models[s].forward([toks[s]], len(prompts[s]) + step)["logits"]
+            st = compare_logits(lg[b], want, f"seq {s} step {step}")
+            assert_parity(st, f"seq {s} step {step}")
+            last[s] = want
+
+
+# -------------------------------------------------------------------- MoE --
+
+def small_moe():
+    return Shape("moe-small", hidden=256, n_layers=2, n_heads=4, n_kv_heads=4, head_dim=64, vocab=512,
+                 n_experts=8, top_k=2, expert_inter=96, shared_inter=128, shared_gate=True,
+                 qkv_bias=True, rope_base=1e4, max_seq=64, max_chunk=32)
+
+
+def test_moe_small_parity_and_routes():
+    shape = small_moe()
+    W = host_weights(shape)
+    ids = prompt(shape, 24)
+    m = oracle.Model(shape, W)
+    want = m.forward(ids, 0, routes=True, probs=True)
+    dec, _ = make_decoder(shape, W)
+    logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    dec.prefill_chunk(0, [int(t) for t in ids], 0, logits_mode=1, logits=logits)
+    routes = torch.empty((shape.n_layers, 24, shape.top_k), dtype=torch.int32, device="cuda")
+    dec.debug_read_routes(routes, 24)
+    torch.cuda.synchronize()
+    st = compare_logits(logits.cpu().numpy(), want["logits"], "moe prefill")
+    log("moe prefill", st)
+    assert_parity(st, "moe prefill")
+    got_r = routes.cpu().numpy()
+    mism = np.argwhere(got_r != want["routes"])
+    for l, i, j in mism:
+        p = np.sort(want["probs"][l, i])[::-1]
+        gap = (p[shape.top_k - 1] - p[shape.top_k]) / p[shape.top_k - 1]
+        assert gap < 1e-4, f"route mismatch at layer {l} token {i} with gap {gap:.2e}"
+    # decode steps, teacher-forced
+    for step in range(4):
+        t = oracle.argmax(want["logits"])
+        want = m.forward([t], 24 + step, routes=True, probs=True)
+        lg, _ = decode(dec, [0], [t])
+        st = compare_logits(lg[0], want["logits"], f"moe decode {step}")
+        assert_parity(st, f"moe decode {step}")
+        dec.debug_read_routes(routes, 1)
+        torch.cuda.synchronize()
+        r1 = routes.cpu().numpy().reshape(-1)[: shape.n_layers * shape.top_k].reshape(shape.n_layers, shape.top_k)
+        assert np.array_equal(r1, want["routes"][:, 0, :])
