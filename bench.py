@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark of the decoder step on one MI355X.
+
+Default workload: the 8B-class GQA decoder (hidden 4096, 32 layers, 32/8
+heads of 128, SwiGLU 14336, vocab 128256, bf16 weights ~N(0, 0.02),
+synthetic): a 2048-token random prompt prefilled in chunks of 128, then
+batch-1 greedy decode steps with the bf16 KV cache.  One "step" is one
+decode step (every row of the hot path: embedding, 32 x [RMSNorm, QKV,
+RoPE + KV append, attention, o_proj + residual, RMSNorm, SwiGLU FFN +
+residual], final norm, lm-head, argmax).
+
+Prints ONE JSON line: decode tokens/s (value), prefill tokens/s, the
+roofline of the dominant kernel measured live with HIP events (the
+library's per-node timers) and the fp64 oracle timed on a bounded sample
+on the host cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tok/s @bs1 (% HBM peak) + prefill tok/s (% MFMA peak), 8B-shape GQA"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h"):
+        with open(os.path.join(ROOT, "decoder_only_transformer_step_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(name):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if absent or taken on a different kernel source."""
+    path = os.path.join(PROFILE_DIR, name)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*(\w+)", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(shape, n_prefill, n_decode):
+    """The fp64 oracle (unchanged) on the host cores: a chunk of n_prefill
+    prompt tokens, then n_decode greedy decode steps; tokens/s of the decode
+    steps (and of the prefill) over the tokens actually run."""
+    import oracle
+    from synth.weights import host_weights, prompt
+    t0 = time.time()
+    W = host_weights(shape)
+    log(f"[cpu] host weights generated in {time.time() - t0:.1f}s")
+    m = oracle.Model(shape, W, max_seq=n_prefill + n_decode + 1)
+    ids = prompt(shape, n_prefill)
+    t0 = time.perf_counter()
+    out = m.forward(ids, 0)
+    t_pre = time.perf_counter() - t0
+    tok = oracle.argmax(out["logits"])
+    t0 = time.perf_counter()
+    for i in range(n_decode):
+        out = m.forward([tok], n_prefill + i)
+        tok = oracle.argmax(out["logits"])
+    t_dec = time.perf_counter() - t0
+    del m, W
+    return {"value": n_decode / t_dec, "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{shape.name}: fp64 oracle, one {n_prefill}-token prefill chunk "
+                      f"({n_prefill / t_pre:.3f} tok/s) then {n_decode} decode steps at positions "
+                      f"{n_prefill}..{n_prefill + n_decode - 1}; value = decode tok/s",
+            "prefill_tok_s": n_prefill / t_pre, "seconds": t_pre + t_dec}
+
+
+def summarize_nodes(st):
+    out = {}
+    for n, v in st.items():
+        if v["launches"]:
+            ms = v["ms"] / v["launches"]
+            out[n] = {"launches": v["launches"], "avg_us": round(ms * 1e3, 2),
+                      "GBps": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1) if v["ms"] else None,
+                      "TFps": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2) if v["ms"] else None,
+                      "ms_total": round(v["ms"], 3)}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256, help="timed decode steps")
+    ap.add_argument("--warmup", type=int, default=3, help="untimed decode steps before timing")
+    ap.add_argument("--workload", default="8b", help="8b (default), 135m, tiny, moe, longctx")
+    ap.add_argument("--prefill-runs", type=int, default=3, help="timed whole-prompt prefills (median)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-prefill", type=int, default=16, help="oracle sample: prompt tokens")
+    ap.add_argument("--cpu-decode", type=int, default=2, help="oracle sample: decode steps")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling HBM counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not supported: "
+              "this build runs the whole step on a single MI355X", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from decoder_only_transformer_step_amd import Decoder
+    from synth.device import device_kv, device_weights
+    from synth.weights import prompt
+    from synth.workloads import WORKLOADS
+
+    shape, work = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    W = device_weights(shape)
+    torch.cuda.synchronize()
+    log(f"[gpu] {shape.name}: {shape.n_params() / 1e9:.2f}B params generated on device in {time.time() - t0:.1f}s")
+    dec = Decoder(shape, W)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    result = {"metric": METRIC, "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+              "data": "synthetic (seeded SplitMix64/Box-Muller bf16 weights and uniform token ids)"}
+    batch = work.batch
+    seqs = list(range(batch))
+
+    # ------------------------------------------------------------ prefill --
+    prefill = None
+    if work.prompt:
+        ids = [int(t) for t in prompt(shape, work.prompt)]
+        chunks = [ids[i:i + work.chunk] for i in range(0, len(ids), work.chunk)]
+        times = []
+        for run in range(1 + args.prefill_runs):
+            dec.kv_reset(-1)
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            pos = 0
+            for ci, ch in enumerate(chunks):
+                dec.prefill_chunk(0, ch, pos, logits_mode=1 if ci == len(chunks) - 1 else 0)
+                pos += len(ch)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            if run:
+                times.append(ev0.elapsed_time(ev1) * 1e-3)
+        # one more prefill with the per-node timers, for the MFMA figures
+        dec.kv_reset(-1)
+        dec.stats_enable()
+        pos = 0
+        for ci, ch in enumerate(chunks):
+            dec.prefill_chunk(0, ch, pos, logits_mode=1 if ci == len(chunks) - 1 else 0)
+            pos += len(ch)
+        pst = dec.stats_read()
+        dec.stats_enable(())
+        torch.cuda.synchronize()
+        t_pre = statistics.median(times)
+        flops = sum(v["flops"] for v in pst.values())
+        gemm_nodes = ("qkv", "o", "gate_up", "down", "head", "router", "experts")
+        g_ms = sum(pst[n]["ms"] for n in gemm_nodes)
+        g_fl = sum(pst[n]["flops"] for n in gemm_nodes)
+        g_by = sum(pst[n]["bytes"] for n in gemm_nodes)
+        chunk_bytes = sum(pst[n]["bytes"] for n in gemm_nodes) / len(chunks)
+        chunk_flops = g_fl / len(chunks)
+        ceiling = min(1.0, (chunk_flops / (MFMA_BF16_PEAK_TFS * 1e12)) / (chunk_bytes / (HBM_PEAK_GBS * 1e9)))
+        prefill = {"tok_s": len(ids) / t_pre, "ms": t_pre * 1e3, "prompt": len(ids), "chunk": work.chunk,
+                   "tflops": flops / t_pre / 1e12, "mfma_frac": flops / t_pre / 1e12 / MFMA_BF16_PEAK_TFS,
+                   "gemm_tflops": g_fl / (g_ms * 1e-3) / 1e12,
+                   "gemm_mfma_frac": g_fl / (g_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+                   "gemm_hbm_frac": g_by / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                   "chunk_mfma_ceiling": ceiling, "nodes": summarize_nodes(pst)}
+        log(f"[gpu] prefill {prefill['tok_s']:.0f} tok/s ({t_pre * 1e3:.1f} ms for {len(ids)} tokens)")
+    elif work.context:
+        # long-context batched decode: every sequence starts with a synthetic N(0,1) KV prefix
+        t0 = time.time()
+        buf = None
+        for s in seqs:
+            for l in range(shape.n_layers):
+                buf = device_kv(shape, s, l, work.context, out=buf)
+                dec.kv_load(s, l, buf[0], buf[1], work.context)
+        del buf
+        torch.cuda.synchronize()
+        log(f"[gpu] KV prefix {batch} x {work.context} filled in {time.time() - t0:.1f}s")
+
+    # ------------------------------------------------------------- decode --
+    first_tokens = None if work.prompt else [int(t) for t in prompt(shape, batch, seq=99)]
+    am = torch.empty(batch, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    dec.decode_step(seqs, first_tokens, argmax=am)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    first_ms = ev0.elapsed_time(ev1)
+    # warm-up steps, with every node timed once for the breakdown
+    dec.stats_enable()
+    for _ in range(args.warmup):
+        dec.decode_step(seqs, None, argmax=am)
+    wst = dec.stats_read()
+    dec.stats_enable(())
+    cand = {n: v for n, v in wst.items() if n in ("gate_up", "qkv", "o", "down", "head", "experts", "attn")}
+    dom = max(cand, key=lambda n: cand[n]["ms"])
+    # timed region: only the dominant node's launches are bracketed by HIP events
+    dec.stats_enable([dom])
+    torch.cuda.synchronize()
+    t_host = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        dec.decode_step(seqs, None, argmax=am)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host
+    dst = dec.stats_read()
+    dec.stats_enable(())
+    t_dec = ev0.elapsed_time(ev1) * 1e-3
+    tok_s = args.steps * batch / t_dec
+    step_bytes = sum(v["bytes"] for v in wst.values()) / max(1, args.warmup)
+    log(f"[gpu] decode {tok_s:.1f} tok/s, {t_dec / args.steps * 1e3:.3f} ms/step "
+        f"({step_bytes / 1e9:.2f} GB/step algorithmic)")
+
+    d = dst[dom]
+    per_launch_bytes = d["bytes"] / d["launches"]
+    per_launch_s = d["ms"] / d["launches"] * 1e-3
+    achieved = per_launch_bytes / per_launch_s / 1e9
+    traffic = counter_traffic(f"counters_{dom}_decode_{args.workload}.md")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": f"{dom} projection (gemm_kernel, decode)", "bytes_per_launch": per_launch_bytes,
+                "avg_us": round(per_launch_s * 1e6, 2), "launches": d["launches"]}
+
+    result.update({
+        "value": round(tok_s, 2),
+        "ms_per_step": round(t_dec / args.steps * 1e3, 4),
+        "config": {"workload": shape.name, "global_batch": batch, "decode_positions":
+                   [work.prompt or work.context, (work.prompt or work.context) + args.warmup + args.steps],
+                   "prefill_prompt": work.prompt, "prefill_chunk": work.chunk, "parallelism": "single-gpu"},
+        "decode": {"tok_s": tok_s, "first_step_ms": round(first_ms, 3), "hbm_GBps": step_bytes / (t_dec / args.steps) / 1e9,
+                   "hbm_frac": step_bytes / (t_dec / args.steps) / 1e9 / HBM_PEAK_GBS,
+                   "bytes_per_step": step_bytes, "host_s": t_host,
+                   "nodes_warmup": summarize_nodes(wst)},
+        "prefill": prefill,
+        "roofline": roofline,
+        "kernel_source_sha256": kernel_source_hash(),
+    })
+    dec.close()
+    del W
+    torch.cuda.empty_cache()
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = n
+        del a, b
+
+    if not args.no_cpu_baseline:
+        cpu_shape = shape.with_(max_batch=1)
+        result["cpu_baseline"] = cpu_baseline(cpu_shape, args.cpu_prefill, args.cpu_decode)
+        log(f"[cpu] oracle {result['cpu_baseline']['value']:.4f} tok/s on {result['cpu_baseline']['cores']} threads")
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

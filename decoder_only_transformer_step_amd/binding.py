@@ -40,6 +40,18 @@ class DecoderWeights(ctypes.Structure):
                 ("layers", ctypes.POINTER(DecoderLayerWeights))]
 
 
+NODES = ("qkv", "rope", "attn", "o", "gate_up", "down", "router", "experts", "head", "norm", "embed")
+
+
+class DecoderStats(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int64 * len(NODES)), ("ms", ctypes.c_double * len(NODES)),
+                ("bytes", ctypes.c_double * len(NODES)), ("flops", ctypes.c_double * len(NODES))]
+
+    def as_dict(self):
+        return {n: dict(launches=int(self.launches[i]), ms=float(self.ms[i]), bytes=float(self.bytes[i]),
+                        flops=float(self.flops[i])) for i, n in enumerate(NODES)}
+
+
 # every symbol the headers declare, with its ctypes signature
 SIGNATURES = {
     "decoder_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(DecoderConfig)]),
@@ -56,9 +68,12 @@ SIGNATURES = {
     "decoder_last_error": (ctypes.c_char_p, [_P]),
     "dec_diag_gemm": (ctypes.c_int, [_P, _I32, _I32, _P, _I32, _P, _P]),
     "dec_diag_rmsnorm": (ctypes.c_int, [_P, _P, _I32, _I32, ctypes.c_double, _P, _P]),
+    "dec_diag_gemv": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _P]),
     "decoder_debug_layer_limit": (ctypes.c_int, [_P, _I32]),
     "decoder_debug_read_x": (ctypes.c_int, [_P, _P, _I32]),
     "decoder_debug_read_routes": (ctypes.c_int, [_P, _P, _I32]),
+    "decoder_stats_enable": (ctypes.c_int, [_P, _I32]),
+    "decoder_stats_read": (ctypes.c_int, [_P, ctypes.POINTER(DecoderStats)]),
 }
 
 
@@ -214,6 +229,23 @@ class Decoder:
     def debug_read_x(self, out, rows):
         _check(lib().decoder_debug_read_x(self.handle, _ptr(out), rows), self.handle, "read_x")
 
+    def stats_enable(self, nodes=None):
+        """nodes: iterable of node names to time (None: all), or () / False to stop."""
+        if nodes is None or nodes is True:
+            mask = -1
+        elif not nodes:
+            mask = 0
+        else:
+            mask = 0
+            for n in nodes:
+                mask |= 1 << NODES.index(n)
+        _check(lib().decoder_stats_enable(self.handle, mask), self.handle, "stats_enable")
+
+    def stats_read(self):
+        st = DecoderStats()
+        _check(lib().decoder_stats_read(self.handle, ctypes.byref(st)), self.handle, "stats_read")
+        return st.as_dict()
+
     def debug_read_routes(self, out, rows):
         _check(lib().decoder_debug_read_routes(self.handle, _ptr(out), rows), self.handle, "read_routes")
 
@@ -222,6 +254,11 @@ def diag_gemm(A, W, C, stream):
     M, K = A.shape
     N = W.shape[0]
     _check(lib().dec_diag_gemm(_ptr(A), M, K, _ptr(W), N, _ptr(C), ctypes.c_void_p(stream)), None, "dec_diag_gemm")
+
+
+def diag_gemv(a, W, y, stream):
+    N, K = W.shape
+    _check(lib().dec_diag_gemv(_ptr(a), K, _ptr(W), N, _ptr(y), ctypes.c_void_p(stream)), None, "dec_diag_gemv")
 
 
 def diag_rmsnorm(x, g, eps, out, stream):

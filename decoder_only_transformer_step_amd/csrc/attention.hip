@@ -6,24 +6,25 @@
 // g = floor(h Hkv / Hq), s_t = q . k_t / sqrt(d) for t <= p, w = softmax(s),
 // o = sum_t w_t v_t.
 //
-// gfx950 design (flash-decoding with split KV):
+// gfx950 design (flash-decoding with split KV, one kernel):
 //  * A "column group" is up to 16 query columns that share one kv head and
 //    one sequence: G heads of one decode row, or 16/G rows x G heads of a
 //    prefill chunk.  The kv head's K and V are read once for all of them.
-//  * A task (one wavefront) takes one column group and one contiguous key
-//    range (split).  Per 32-key tile: S^T = K Q^T with 8 MFMA 16x16x32
-//    (K rows straight from HBM as the A operand, Q^T in registers as B),
-//    an online softmax per column in fp32 (exp2 with log2(e)/sqrt(d)
-//    folded into the scale), and O^T += V^T P^T with d/16 MFMAs.
+//  * One block (4 wavefronts) takes one column group and one contiguous key
+//    range (split); its waves take interleaved 32-key tiles.  Per tile:
+//    S^T = K Q^T with 2 d/32 MFMA 16x16x32 (K rows straight from HBM as the
+//    A operand, Q^T in registers as B), an online softmax per column in fp32
+//    (exp2, with log2(e)/sqrt(d) folded into the scale), and O^T += V^T P^T
+//    with d/16 MFMAs.
 //  * V is stored transposed in the cache ([dim][position]), so the A operand
 //    of the PV product is two 8-byte loads per lane, and the B operand
 //    (P^T) is exactly the lane's own scores: the MFMA k index is mapped to
 //    keys {4 (l/16) + j, 16 + 4 (l/16) + j}, the layout the QK product
 //    leaves them in.  No LDS round trip, no cross-lane shuffles for P.
-//  * Each task writes (m, l, O) partials; attn_merge combines the splits of
-//    a column group in fixed order (log-sum-exp), so results do not depend
-//    on scheduling.  With a single split the task normalises and writes the
-//    output itself.
+//  * The 4 waves merge through LDS (log-sum-exp); with one split the block
+//    normalises and writes the output.  With several, each block writes its
+//    (m, l, O) partial and attn_merge combines them in split order, so the
+//    result does not depend on scheduling.
 #include "common.h"
 #include "launch.h"
 
@@ -31,71 +32,79 @@ namespace {
 
 constexpr float NEG_SENTINEL = -1.0e30f;
 
-__device__ __forceinline__ int group_keys(const AttnArgs &a, int rg, int c, bool &valid, int &row,
-                                          int &head, int g) {
+struct Col {
+  bool valid;
+  int row, head, pos;
+};
+
+__device__ __forceinline__ Col column(const AttnArgs &a, int rg, int g, int c) {
+  Col k;
   const int G = a.G;
-  row = rg * a.rows_per_group + c / G;
-  head = g * G + c % G;
-  valid = (c < a.rows_per_group * G) && (row < a.rows);
-  return valid ? a.row_pos[row] : -1;
+  k.row = rg * a.rows_per_group + c / G;
+  k.head = g * G + c % G;
+  k.valid = (c < a.rows_per_group * G) && (k.row < a.rows);
+  k.pos = k.valid ? a.row_pos[k.row] : -1;
+  return k;
+}
+
+// keys of the group: 0 .. max position of its valid columns
+__device__ __forceinline__ int group_keys(const AttnArgs &a, int rg, int g) {
+  int kmax = -1;
+  for (int c = 0; c < 16; ++c) kmax = max(kmax, column(a, rg, g, c).pos);
+  return kmax + 1;
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
-  const int lane = threadIdx.x & (WAVE - 1);
-  const int task = blockIdx.x * 4 + threadIdx.x / WAVE;
-  if (task >= a.n_groups * a.n_splits) return;
-  const int gi = task / a.n_splits, split = task - gi * a.n_splits;
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+  constexpr int NDT = D / 16;
+  __shared__ float lo[4][16][D];
+  __shared__ float lm[4][16], ll[4][16];
+
+  const int gi = blockIdx.x / a.n_splits, split = blockIdx.x - gi * a.n_splits;
   const int g = gi % a.Hkv, rg = gi / a.Hkv;
+  const int keys = group_keys(a, rg, g);
+  const int nact = (keys + a.kc - 1) / a.kc;
+  if (split >= nact) return;
+  const int k0 = split * a.kc, k1 = min(k0 + a.kc, keys);
+
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   const int c = lane & 15, quad = lane >> 4;
-
-  bool valid;
-  int row, head;
-  const int pos = group_keys(a, rg, c, valid, row, head, g);
-  // keys of the group: 0 .. max position of its rows (wave-wide max over columns)
-  int kmax = pos;
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) kmax = max(kmax, __shfl_xor(kmax, o, WAVE));
-  const int keys = kmax + 1;
-  const int k0 = split * a.kc;
-  if (k0 >= keys) return;
-  const int k1 = min(k0 + a.kc, keys);
-
+  const Col col = column(a, rg, g, c);
   const int seq = a.row_seq[rg * a.rows_per_group];
   const uint16_t *kb = a.kcache + (int64_t)seq * a.seq_stride + a.layer_off + (int64_t)g * a.S * D;
   const uint16_t *vb = a.vcache + (int64_t)seq * a.seq_stride + a.layer_off + (int64_t)g * D * a.S;
 
   u32x4 qf[D / 32];
-  const uint16_t *qrow = a.q + ((int64_t)row * a.Hq + head) * D + quad * 8;
+  const uint16_t *qrow = a.q + ((int64_t)col.row * a.Hq + col.head) * D + quad * 8;
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) qf[ks] = valid ? load16(qrow + ks * 32) : u32x4{0u, 0u, 0u, 0u};
+  for (int ks = 0; ks < D / 32; ++ks) qf[ks] = col.valid ? load16(qrow + ks * 32) : u32x4{0u, 0u, 0u, 0u};
 
   float m_run = NEG_SENTINEL, l_run = 0.f;
-  f32x4 acc[D / 16];
+  f32x4 acc[NDT];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int t0 = k0; t0 < k1; t0 += 32) {
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  for (int t0 = k0 + 32 * wave; t0 < k1; t0 += 128) {
     const uint16_t *k_lo = kb + (int64_t)(t0 + c) * D + quad * 8;
     const uint16_t *k_hi = k_lo + 16 * D;
-    u32x4 ka[D / 32], kbv[D / 32];
+    u32x4 ka[D / 32], kh[D / 32];
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
       ka[ks] = load16(k_lo + ks * 32);
-      kbv[ks] = load16(k_hi + ks * 32);
+      kh[ks] = load16(k_hi + ks * 32);
     }
-    u32x2 va[D / 16], vv[D / 16];
+    u32x2 va[NDT], vh[NDT];
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
+    for (int dt = 0; dt < NDT; ++dt) {
       const uint16_t *vr = vb + (int64_t)(dt * 16 + c) * a.S + t0 + quad * 4;
       va[dt] = load8(vr);
-      vv[dt] = load8(vr + 16);
+      vh[dt] = load8(vr + 16);
     }
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
       s0 = mfma16x16x32(as_bf16x8(ka[ks]), as_bf16x8(qf[ks]), s0);
-      s1 = mfma16x16x32(as_bf16x8(kbv[ks]), as_bf16x8(qf[ks]), s1);
+      s1 = mfma16x16x32(as_bf16x8(kh[ks]), as_bf16x8(qf[ks]), s1);
     }
     // lane holds S[key = t0 + 4 quad + i][col c] in s0, key + 16 in s1
     float sv[8];
@@ -103,16 +112,15 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key0 = t0 + quad * 4 + i, key1 = key0 + 16;
-      sv[i] = (key0 <= pos && key0 < k1) ? s0[i] * a.scale_log2 : -INFINITY;
-      sv[4 + i] = (key1 <= pos && key1 < k1) ? s1[i] * a.scale_log2 : -INFINITY;
+      sv[i] = (key0 <= col.pos && key0 < k1) ? s0[i] * a.scale_log2 : -INFINITY;
+      sv[4 + i] = (key1 <= col.pos && key1 < k1) ? s1[i] * a.scale_log2 : -INFINITY;
       tmax = fmaxf(tmax, fmaxf(sv[i], sv[4 + i]));
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, WAVE));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, WAVE));
     const float m_new = fmaxf(m_run, tmax);
     const float alpha = exp2f(m_run - m_new);
-    float psum = 0.f;
-    float p[8];
+    float p[8], psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       p[i] = exp2f(sv[i] - m_new);
@@ -126,92 +134,101 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     pb[2] = pack_bf16x2(p[4], p[5]);
     pb[3] = pack_bf16x2(p[6], p[7]);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
+    for (int dt = 0; dt < NDT; ++dt) {
       acc[dt] *= alpha;
       u32x4 av;
       av[0] = va[dt][0];
       av[1] = va[dt][1];
-      av[2] = vv[dt][0];
-      av[3] = vv[dt][1];
+      av[2] = vh[dt][0];
+      av[3] = vh[dt][1];
       acc[dt] = mfma16x16x32(as_bf16x8(av), as_bf16x8(pb), acc[dt]);
     }
   }
-  // acc[dt][i] = O^T[dim = dt*16 + 4 quad + i][col c]
+  // acc[dt][i] = O^T[dim = dt*16 + 4 quad + i][col c]; merge the 4 waves
   float l_tot = l_run + __shfl_xor(l_run, 16, WAVE);
   l_tot += __shfl_xor(l_tot, 32, WAVE);
-  if (a.n_splits == 1) {
-    if (!valid) return;
-    const float inv = 1.0f / l_tot;
-    uint16_t *orow = a.out + ((int64_t)row * a.Hq + head) * D;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      u32x2 w;
-      w[0] = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
-      w[1] = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
-      *reinterpret_cast<u32x2 *>(orow + dt * 16 + quad * 4) = w;
+  for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(&lo[wave][c][dt * 16 + quad * 4]) = acc[dt];
+  if (quad == 0) {
+    lm[wave][c] = m_run;
+    ll[wave][c] = l_tot;
+  }
+  __syncthreads();
+  // thread -> column cc, dims jj + 16 q
+  const int cc = threadIdx.x >> 4, jj = threadIdx.x & 15;
+  const Col oc = column(a, rg, g, cc);
+  float M = NEG_SENTINEL;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, lm[w][cc]);
+  float L = 0.f, o[NDT];
+#pragma unroll
+  for (int q = 0; q < NDT; ++q) o[q] = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float sc = exp2f(lm[w][cc] - M);
+    L += sc * ll[w][cc];
+#pragma unroll
+    for (int q = 0; q < NDT; ++q) o[q] += sc * lo[w][cc][jj + 16 * q];
+  }
+  if (nact == 1) {
+    if (!oc.valid) return;
+    const float inv = 1.0f / L;
+    const int64_t ob = ((int64_t)oc.row * a.Hq + oc.head) * D;
+#pragma unroll
+    for (int q = 0; q < NDT; ++q) {
+      if (a.out_f32) a.out_f32[ob + jj + 16 * q] = o[q] * inv;
+      else a.out[ob + jj + 16 * q] = (uint16_t)f32_to_bf16_bits(o[q] * inv);
     }
     return;
   }
-  float *po = a.part_o + ((int64_t)task * 16 + c) * D;
+  // several splits: publish this block's partial for attn_merge
+  const int64_t task = blockIdx.x;
+  float *po = a.part_o + (task * 16 + cc) * D;
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4 *>(po + dt * 16 + quad * 4) = acc[dt];
-  if (quad == 0) {
-    a.part_ml[((int64_t)task * 16 + c) * 2 + 0] = m_run;
-    a.part_ml[((int64_t)task * 16 + c) * 2 + 1] = l_tot;
+  for (int q = 0; q < NDT; ++q) po[jj + 16 * q] = o[q];
+  if (jj == 0) {
+    a.part_ml[(task * 16 + cc) * 2 + 0] = M;
+    a.part_ml[(task * 16 + cc) * 2 + 1] = L;
   }
 }
 
-// One block per column group: thread (c, j) combines column c's splits for
-// dims j, j + 16, ... in split order.
+// One block per (group, column), one thread per dim: combine the group's
+// splits in split order.
 template <int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  const int gi = blockIdx.x;
+__global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a) {
+  const int gi = blockIdx.x >> 4, cc = blockIdx.x & 15;
   const int g = gi % a.Hkv, rg = gi / a.Hkv;
-  const int c = threadIdx.x >> 4, j = threadIdx.x & 15;
-  bool valid;
-  int row, head;
-  const int pos = group_keys(a, rg, c, valid, row, head, g);
-  // the group's key count, from its last valid row (positions grow with the row)
-  int kmax = -1;
-  for (int cc = 0; cc < 16; ++cc) {
-    bool v2;
-    int r2, h2;
-    kmax = max(kmax, group_keys(a, rg, cc, v2, r2, h2, g));
-  }
-  (void)pos;
-  if (!valid) return;
-  const int nsp = min(a.n_splits, (kmax + 1 + a.kc - 1) / a.kc);
-  const int64_t base = (int64_t)gi * a.n_splits;
+  const Col oc = column(a, rg, g, cc);
+  if (!oc.valid) return;
+  const int nact = (group_keys(a, rg, g) + a.kc - 1) / a.kc;
+  if (nact <= 1) return;                       // written directly by attn_kernel
+  const int j = threadIdx.x;
+  const float *ml = a.part_ml + ((int64_t)gi * a.n_splits * 16 + cc) * 2;
+  const float *po = a.part_o + ((int64_t)gi * a.n_splits * 16 + cc) * D + j;
   float M = NEG_SENTINEL;
-  for (int s = 0; s < nsp; ++s) M = fmaxf(M, a.part_ml[((base + s) * 16 + c) * 2]);
-  float L = 0.f;
-  float o[D / 16];
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) o[t] = 0.f;
-  for (int s = 0; s < nsp; ++s) {
-    const float m = a.part_ml[((base + s) * 16 + c) * 2], l = a.part_ml[((base + s) * 16 + c) * 2 + 1];
-    const float w = exp2f(m - M);
-    L += w * l;
-    const float *po = a.part_o + ((base + s) * 16 + c) * D;
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) o[t] += w * po[t * 16 + j];
+#pragma unroll 8
+  for (int s = 0; s < nact; ++s) M = fmaxf(M, ml[(int64_t)s * 32]);
+  float L = 0.f, o = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < nact; ++s) {
+    const float sc = exp2f(ml[(int64_t)s * 32] - M);
+    L += sc * ml[(int64_t)s * 32 + 1];
+    o += sc * po[(int64_t)s * 16 * D];
   }
-  const float inv = 1.0f / L;
-  uint16_t *orow = a.out + ((int64_t)row * a.Hq + head) * D;
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) orow[t * 16 + j] = (uint16_t)f32_to_bf16_bits(o[t] * inv);
+  const int64_t oi = ((int64_t)oc.row * a.Hq + oc.head) * D + j;
+  if (a.out_f32) a.out_f32[oi] = o / L;
+  else a.out[oi] = (uint16_t)f32_to_bf16_bits(o / L);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs &a, int head_dim, hipStream_t st) {
-  const int tasks = a.n_groups * a.n_splits;
-  dim3 grid((tasks + 3) / 4);
-  if (head_dim == 128) hipLaunchKernelGGL(attn_partial_kernel<128>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(attn_partial_kernel<64>, grid, dim3(256), 0, st, a);
+  dim3 grid(a.n_groups * a.n_splits);
+  if (head_dim == 128) hipLaunchKernelGGL(attn_kernel<128>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(attn_kernel<64>, grid, dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
-  if (head_dim == 128) hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(a.n_groups), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(a.n_groups), dim3(256), 0, st, a);
+  if (head_dim == 128) hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(a.n_groups * 16), dim3(128), 0, st, a);
+  else hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(a.n_groups * 16), dim3(64), 0, st, a);
   return hipGetLastError();
 }

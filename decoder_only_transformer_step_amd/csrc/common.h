@@ -32,15 +32,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// 16-byte global load that streams past the caches (weights are read once).
-__device__ __forceinline__ u32x4 load_stream16(const void *p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-}
 __device__ __forceinline__ u32x4 load16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 __device__ __forceinline__ u32x2 load8(const void *p) {
   return *reinterpret_cast<const u32x2 *>(p);
+}
+__device__ __forceinline__ f32x4 loadf4(const float *p) {
+  return *reinterpret_cast<const f32x4 *>(p);
 }
 
 // D = A * B + C for a 16x16 tile with K = 32 (bf16 in, fp32 accumulate).
@@ -77,6 +76,11 @@ __device__ __forceinline__ float block_sum(float v, float *lds) {
   return t;
 }
 
+// (value, index) order of the greedy choice: larger value first, lower index on ties.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
 // ------------------------------------------------------ launch structs --
 
 // Epilogues of the projection kernel.
@@ -84,15 +88,37 @@ enum {
   EPI_STORE = 0,     // C[m][n] = acc (+ bias[n])                 fp32
   EPI_ADD = 1,       // C[m][n] += acc                              fp32 (residual stream)
   EPI_SWIGLU = 2,    // H[m][n] = bf16(silu(acc_gate) * acc_up)    gate rows n, up rows n + N
+  EPI_QKV = 3,       // bias + RoPE; q -> bf16 buffer, k/v -> KV cache
+  EPI_LOGITS = 4,    // C = acc (fp32 logits) and each tile's greedy candidate per row
+};
+
+struct QkvEpi {
+  const float *bias;       // fp32 [qkv rows] or null
+  const float2 *cs;        // (cos, sin) [S][d/2]
+  const int32_t *row_seq, *row_pos;
+  uint16_t *q;             // bf16 [rows][Hq][d]
+  uint16_t *kcache, *vcache;
+  int64_t seq_stride, layer_off;
+  int32_t S, Hq, Hkv, d;
+};
+
+struct ArgmaxEpi {
+  float *part_val;         // [rows][ntiles] best logit of each 16-column tile
+  int32_t *part_idx;       // [rows][ntiles]
 };
 
 struct GemmArgs {
   const uint16_t *A;      // bf16 activations, row m at A + row(m) * lda
   const int32_t *a_rows;  // optional gather: A row of output row m (grouped mode: by pair)
   int64_t lda;
-  const uint16_t *W;      // bf16 weights [N(+N)][K] row-major (per group: W + expert * w_group_stride)
+  // fused RMSNorm prologue: when x is set, A = bf16(x * rsqrt(mean(x^2) + eps) * gamma)
+  const float *x;
+  const float *gamma;
+  float eps;
+  const uint16_t *W;      // bf16 weights [rows][K] row-major (per group: W + expert * w_group_stride)
   int64_t w_group_stride;
   int32_t M, N, K;
+  int32_t np_off;         // row offset of the second weight tile (SwiGLU: N, QKV: d / 2)
   float *C;               // fp32 output / residual, row m at C + m * ldc
   uint16_t *Hout;         // bf16 output for EPI_SWIGLU, row m at Hout + m * ldc
   int64_t ldc;
@@ -103,7 +129,9 @@ struct GemmArgs {
   const int32_t *group_expert;
   const int32_t *group_start;
   const int32_t *group_count;
-  // split-K: blockIdx.z = split; partial sums go to Cpart[split][M][N]
+  // split-K: blockIdx.z = split; partial sums go to Cpart[split][M][np * N]
   float *Cpart;
   int32_t ksplit;
+  QkvEpi qkv;
+  ArgmaxEpi am;
 };

@@ -22,7 +22,7 @@
 namespace {
 
 constexpr int STAGE_RING = 64;     // pinned staging slots (one per call in flight)
-constexpr int ATTN_TARGET_TASKS = 2048;
+constexpr int ATTN_TARGET_BLOCKS = 1024;
 constexpr int ATTN_MAX_TASKS = 8192;
 constexpr int GEMM_MAX_SPLIT = 8;
 
@@ -30,7 +30,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
   size_t kcache, vcache, rope, x, act, attn, q, qkv, h, logits, stage, next_token;
-  size_t part_o, part_ml, gpart;
+  size_t part_o, part_ml, gpart, counters, am_val, am_idx, am_out, f32_attn, f32_h, f32_act, f32_hexp;
   size_t rlogits, rids, rids_rec, rwts, rgate, groups, pair_row, pair_of, hexp, yexp, hsh, ysh;
   size_t total;
   int S, R, RL;
@@ -92,6 +92,18 @@ Layout make_layout(const decoder_config_t *c) {
   if (c->n_experts > 0) max_small_n = std::max(max_small_n, 2 * c->shared_inter);
   L.gpart_elems = (size_t)GEMM_MAX_SPLIT * L.R * 2 * (size_t)max_small_n;
   L.gpart = take(L.gpart_elems * 4);
+  L.counters = take((size_t)(1 + ATTN_MAX_TASKS) * 4);
+  // argmax candidates: one per 16-column tile per row (multi-row lm-head),
+  // or one per 8-row block (batch-1 lm-head)
+  const size_t am_n = std::max((size_t)L.RL * ((c->vocab + 15) / 16), (size_t)(c->vocab + 7) / 8);
+  L.am_val = take(am_n * 4);
+  L.am_idx = take(am_n * 4);
+  L.am_out = take((size_t)L.RL * 4);
+  // fp32 activations of the batch-1 decode path
+  L.f32_attn = take((size_t)qd * 4);
+  L.f32_h = take((size_t)std::max(std::max(c->ffn_inter, c->shared_inter), 1) * 4);
+  L.f32_act = take((size_t)H * 4);
+  L.f32_hexp = take((size_t)std::max(c->top_k, 1) * std::max(c->expert_inter, 1) * 4);
   if (c->n_experts > 0) {
     const int E = c->n_experts, k = c->top_k, P = L.R * k;
     L.rlogits = take((size_t)L.R * E * 4);
@@ -124,8 +136,11 @@ struct decoder {
   // carved workspace
   uint16_t *kcache, *vcache, *act, *attn, *q, *h, *hexp, *hsh;
   float2 *rope;
-  float *x, *qkv, *logits, *part_o, *part_ml, *gpart, *rlogits, *rwts, *rgate, *yexp, *ysh;
+  float *x, *qkv, *logits, *part_o, *part_ml, *gpart, *rlogits, *rwts, *rgate, *yexp, *ysh, *am_val;
   int32_t *ids, *row_seq, *row_pos, *next_token, *rids, *rids_rec, *groups, *pair_row, *pair_of;
+  int32_t *counters, *am_idx, *am_out;
+  float *f32_attn, *f32_h, *f32_act, *f32_hexp;
+  bool single_row_ok = false;  // the batch-1 GEMV path fits every K of this config
   // host state
   std::vector<int32_t> len;
   std::vector<char> has_next;
@@ -137,6 +152,16 @@ struct decoder {
   bool ev_used[STAGE_RING];
   int ring = 0;
   std::string err;
+  // per-node timing (decoder_stats_enable)
+  uint32_t stats_mask = 0;
+  std::vector<hipEvent_t> tev;
+  struct Pending {
+    int node, ev;
+    double bytes, flops;
+  };
+  std::vector<Pending> pend;
+  int tnext = 0;
+  decoder_stats_t stats{};
 };
 
 namespace {
@@ -161,6 +186,44 @@ T *carve(decoder *D, size_t off) {
   return reinterpret_cast<T *>(D->ws + off);
 }
 
+constexpr int TIMER_EVENTS = 8192;
+
+int stats_harvest(decoder *D) {
+  if (D->pend.empty()) return DEC_OK;
+  HIP_TRY(D, hipStreamSynchronize(D->stream), "stats sync");
+  for (const auto &p : D->pend) {
+    float ms = 0.f;
+    HIP_TRY(D, hipEventElapsedTime(&ms, D->tev[p.ev], D->tev[p.ev + 1]), "stats elapsed");
+    D->stats.launches[p.node] += 1;
+    D->stats.ms[p.node] += ms;
+    D->stats.bytes[p.node] += p.bytes;
+    D->stats.flops[p.node] += p.flops;
+  }
+  D->pend.clear();
+  D->tnext = 0;
+  return DEC_OK;
+}
+
+// Brackets the launches of one node with events while stats are enabled.
+struct NodeTimer {
+  decoder *D;
+  int node, ev = -1;
+  double bytes, flops;
+  NodeTimer(decoder *D_, int node_, double bytes_, double flops_)
+      : D(D_), node(node_), bytes(bytes_), flops(flops_) {
+    if (!((D->stats_mask >> node) & 1u)) return;
+    if (D->tnext + 2 > (int)D->tev.size() && stats_harvest(D) != DEC_OK) return;
+    ev = D->tnext;
+    if (hipEventRecord(D->tev[ev], D->stream) != hipSuccess) ev = -1;
+  }
+  ~NodeTimer() {
+    if (ev < 0) return;
+    if (hipEventRecord(D->tev[ev + 1], D->stream) != hipSuccess) return;
+    D->pend.push_back({node, ev, bytes, flops});
+    D->tnext += 2;
+  }
+};
+
 // Stage rows' ids / seqs / positions to the device through a pinned slot.
 int stage_rows(decoder *D, int rows, const int32_t *ids, const int32_t *seqs, const int32_t *pos) {
   const int slot = D->ring;
@@ -179,8 +242,30 @@ int stage_rows(decoder *D, int rows, const int32_t *ids, const int32_t *seqs, co
   return DEC_OK;
 }
 
-int gemm(decoder *D, int epi, const uint16_t *A, int64_t lda, const uint16_t *W, int M, int N, int K,
-         float *C, uint16_t *Hout, int64_t ldc, const float *bias) {
+// Launch one projection (plus its split-K reduction) as node `node`.
+int proj(decoder *D, int node, int epi, GemmArgs g, int max_rows) {
+  const double npd = (epi == EPI_SWIGLU || epi == EPI_QKV) ? 2.0 : 1.0;
+  const double out_b = epi == EPI_ADD ? 8.0 : ((epi == EPI_SWIGLU || epi == EPI_QKV) ? 2.0 * npd : 4.0);
+  const double a_b = g.x ? 4.0 : 2.0;
+  const double ncols = epi == EPI_QKV ? g.N / 2.0 : g.N;
+  NodeTimer timer(D, node, npd * ncols * (double)g.K * 2 + (double)g.M * g.K * a_b + (double)g.M * ncols * out_b,
+                  2.0 * npd * g.M * ncols * (double)g.K);
+  const int ntiles = gemm_ntiles(g, epi);
+  const int steps = (g.K + 31) / 32;
+  int ks = 1;
+  if (epi != EPI_LOGITS && !g.n_groups && ntiles < 192 && steps >= 16) {
+    ks = std::min(GEMM_MAX_SPLIT, std::max(1, 384 / ntiles));
+    ks = std::min(ks, steps / 8);
+    while (ks > 1 && (size_t)ks * g.M * (size_t)npd * ntiles * 16 > D->L.gpart_elems) --ks;
+  }
+  g.ksplit = std::max(ks, 1);
+  g.Cpart = D->gpart;
+  hipError_t e = launch_gemm(g, epi, max_rows, 1, D->stream);
+  if (e != hipSuccess) return hip_fail(D, e, "projection");
+  return DEC_OK;
+}
+
+GemmArgs dense_args(const uint16_t *A, int64_t lda, const uint16_t *W, int M, int N, int K) {
   GemmArgs g{};
   g.A = A;
   g.lda = lda;
@@ -188,31 +273,49 @@ int gemm(decoder *D, int epi, const uint16_t *A, int64_t lda, const uint16_t *W,
   g.M = M;
   g.N = N;
   g.K = K;
-  g.C = C;
-  g.Hout = Hout;
-  g.ldc = ldc;
-  g.bias = bias;
-  const int np = epi == EPI_SWIGLU ? 2 : 1;
-  const int ntiles = (N + 15) / 16;
-  const int steps = (K + 31) / 32;
-  int ks = 1;
-  if (ntiles < 192 && steps >= 16) {
-    ks = std::min(GEMM_MAX_SPLIT, std::max(1, 384 / ntiles));
-    ks = std::min(ks, steps / 8);
-    while (ks > 1 && (size_t)ks * M * np * N > D->L.gpart_elems) --ks;
+  g.np_off = N;
+  return g;
+}
+
+// RMSNorm of x rows into the projection's A operand: fused into the
+// projection prologue for decode-size row counts, else a separate kernel.
+int norm_into(decoder *D, GemmArgs &g, const float *x, const float *gamma, int rows) {
+  const int H = D->c.hidden;
+  if (gemm_norm_fits(rows, H)) {
+    g.x = x;
+    g.gamma = gamma;
+    g.eps = (float)D->c.rms_eps;
+    g.lda = H;
+    g.A = nullptr;
+    return DEC_OK;
   }
-  g.ksplit = ks;
-  g.Cpart = D->gpart;
-  hipError_t e = launch_gemm(g, epi, M, 1, D->stream);
-  if (e != hipSuccess) return hip_fail(D, e, "gemm");
+  hipError_t e;
+  {
+    NodeTimer t(D, DEC_NODE_NORM, rows * (double)H * 6 + H * 4.0, rows * (double)H * 4);
+    e = launch_rmsnorm(x, H, gamma, rows, H, (float)D->c.rms_eps, D->act, H, D->stream);
+  }
+  if (e != hipSuccess) return hip_fail(D, e, "rmsnorm");
+  g.A = D->act;
+  g.lda = H;
   return DEC_OK;
 }
 
-int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos) {
+int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, const int32_t *hpos,
+              float *out_f32 = nullptr) {
   const decoder_config_t &c = D->c;
+  double kv_rows = 0, qk = 0;
+  for (int r = 0; r < rows; ++r) {
+    qk += hpos[r] + 1.0;
+    if (rows_per_group == 1) kv_rows += hpos[r] + 1.0;
+  }
+  if (rows_per_group != 1) kv_rows = max_pos + 1.0;
+  NodeTimer timer(D, DEC_NODE_ATTN,
+                  kv_rows * c.n_kv_heads * c.head_dim * 4.0 + (double)rows * c.n_heads * c.head_dim * 4.0,
+                  qk * c.n_heads * c.head_dim * 4.0);
   AttnArgs a{};
   a.q = D->q;
-  a.out = D->attn;
+  a.out = out_f32 ? nullptr : D->attn;
+  a.out_f32 = out_f32;
   a.kcache = D->kcache;
   a.vcache = D->vcache;
   a.row_seq = D->row_seq;
@@ -226,10 +329,11 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos) 
   a.rows = rows;
   a.rows_per_group = rows_per_group;
   a.n_groups = (rows + rows_per_group - 1) / rows_per_group * c.n_kv_heads;
+  // split the keys so that about ATTN_TARGET_BLOCKS blocks run, each at
+  // least one 32-key tile per wave
   const int keys = max_pos + 1;
-  const int tiles = (keys + 31) / 32;
-  int ns = std::max(1, std::min((ATTN_TARGET_TASKS + a.n_groups - 1) / a.n_groups, tiles));
-  int kc = (int)align_up((size_t)((keys + ns - 1) / ns), 32);
+  int ns = std::max(1, (ATTN_TARGET_BLOCKS + a.n_groups - 1) / a.n_groups);
+  int kc = (int)align_up((size_t)((keys + ns - 1) / ns), 128);
   ns = (keys + kc - 1) / kc;
   while ((int64_t)a.n_groups * ns > ATTN_MAX_TASKS) {
     kc *= 2;
@@ -245,51 +349,172 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos) 
   return DEC_OK;
 }
 
-int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos) {
+// Launch one batch-1 projection (GEMV) as node `node`.
+int gemv(decoder *D, int node, int epi, const GemvArgs &g) {
+  const double nr = (epi == EPI_SWIGLU || epi == EPI_QKV) ? 2.0 : 1.0;
+  const double slots = g.slot_expert ? g.n_slots : 1;
+  NodeTimer timer(D, node, slots * (nr * g.n_items * (double)g.K * 2 + g.K * 4.0 + g.n_items * 4.0 * (epi == EPI_ADD ? 2 : 1)),
+                  slots * 2.0 * nr * g.n_items * (double)g.K);
+  hipError_t e = launch_gemv(g, epi, D->stream);
+  if (e != hipSuccess) return hip_fail(D, e, "gemv");
+  return DEC_OK;
+}
+
+GemvArgs gemv_args(const uint16_t *W, const float *a, int K, int n_items, float *C) {
+  GemvArgs g{};
+  g.W = W;
+  g.a_f32 = a;
+  g.K = K;
+  g.N = n_items;
+  g.n_items = n_items;
+  g.C = C;
+  return g;
+}
+
+// One decode row: every projection is a GEMV over fp32 activations.
+int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
+  const decoder_config_t &c = D->c;
+  const decoder_layer_weights_t &W = D->layers[l];
+  const int H = c.hidden, d = c.head_dim, qd = c.n_heads * d;
+  const float eps = (float)c.rms_eps;
+  int rc;
+  hipError_t e;
+
+  GemvArgs q = gemv_args(W.w_qkv, D->x, H, (c.n_heads + 2 * c.n_kv_heads) * d / 2, nullptr);
+  q.gamma = W.attn_norm;
+  q.eps = eps;
+  q.qkv.bias = c.qkv_bias ? W.b_qkv : nullptr;
+  q.qkv.cs = D->rope;
+  q.qkv.row_seq = D->row_seq;
+  q.qkv.row_pos = D->row_pos;
+  q.qkv.q = D->q;
+  q.qkv.kcache = D->kcache;
+  q.qkv.vcache = D->vcache;
+  q.qkv.seq_stride = D->L.seq_stride;
+  q.qkv.layer_off = (int64_t)l * c.n_kv_heads * (int64_t)D->L.S * d;
+  q.qkv.S = D->L.S;
+  q.qkv.Hq = c.n_heads;
+  q.qkv.Hkv = c.n_kv_heads;
+  q.qkv.d = d;
+  if ((rc = gemv(D, DEC_NODE_QKV, EPI_QKV, q))) return rc;
+  if ((rc = attention(D, l, 1, 1, max_pos, hpos, D->f32_attn))) return rc;
+  if ((rc = gemv(D, DEC_NODE_O, EPI_ADD, gemv_args(W.w_o, D->f32_attn, qd, H, D->x)))) return rc;
+
+  if (c.n_experts == 0) {
+    const int I = c.ffn_inter;
+    GemvArgs gu = gemv_args(W.w_gate_up, D->x, H, I, D->f32_h);
+    gu.gamma = W.ffn_norm;
+    gu.eps = eps;
+    if ((rc = gemv(D, DEC_NODE_GATE_UP, EPI_SWIGLU, gu))) return rc;
+    return gemv(D, DEC_NODE_DOWN, EPI_ADD, gemv_args(W.w_down, D->f32_h, I, H, D->x));
+  }
+  const int E = c.n_experts, k = c.top_k, Ie = c.expert_inter, Is = c.shared_inter;
+  {
+    NodeTimer t(D, DEC_NODE_NORM, H * 12.0, H * 4.0);
+    e = launch_rmsnorm(D->x, H, W.ffn_norm, 1, H, eps, nullptr, H, D->stream, D->f32_act);
+  }
+  if (e != hipSuccess) return hip_fail(D, e, "rmsnorm");
+  if ((rc = gemv(D, DEC_NODE_ROUTER, EPI_STORE, gemv_args(W.w_router, D->f32_act, H, E, D->rlogits)))) return rc;
+  MoeRouteArgs mr{};
+  mr.logits = D->rlogits;
+  mr.act_f32 = D->f32_act;
+  mr.w_sh_gate = (Is > 0 && c.shared_gate) ? W.w_sh_gate : nullptr;
+  mr.rows = 1;
+  mr.E = E;
+  mr.k = k;
+  mr.H = H;
+  mr.renorm = c.norm_topk_prob;
+  mr.ids = D->rids;
+  mr.wts = D->rwts;
+  mr.gate = D->rgate;
+  mr.ids_record = D->rids_rec + (size_t)l * k;
+  {
+    NodeTimer t(D, DEC_NODE_ROUTER, E * 4.0 + H * 4.0, E * 8.0);
+    e = launch_moe_route(mr, false, D->stream);
+  }
+  if (e != hipSuccess) return hip_fail(D, e, "moe_route");
+  GemvArgs eg = gemv_args(W.w_exp_gate_up, D->f32_act, H, Ie, D->f32_hexp);
+  eg.slot_expert = D->rids;
+  eg.n_slots = k;
+  eg.w_group_stride = (int64_t)2 * Ie * H;
+  eg.ldc = Ie;
+  if ((rc = gemv(D, DEC_NODE_EXPERTS, EPI_SWIGLU, eg))) return rc;
+  GemvArgs ed = gemv_args(W.w_exp_down, D->f32_hexp, Ie, H, D->yexp);
+  ed.slot_expert = D->rids;
+  ed.n_slots = k;
+  ed.w_group_stride = (int64_t)H * Ie;
+  ed.a_slot_stride = Ie;
+  ed.ldc = H;
+  if ((rc = gemv(D, DEC_NODE_EXPERTS, EPI_STORE, ed))) return rc;
+  if (Is > 0) {
+    if ((rc = gemv(D, DEC_NODE_EXPERTS, EPI_SWIGLU, gemv_args(W.w_sh_gate_up, D->f32_act, H, Is, D->f32_h)))) return rc;
+    if ((rc = gemv(D, DEC_NODE_EXPERTS, EPI_STORE, gemv_args(W.w_sh_down, D->f32_h, Is, H, D->ysh)))) return rc;
+  }
+  NodeTimer tcomb(D, DEC_NODE_EXPERTS, H * (8.0 + 4.0 * k + 4.0), H * 2.0 * (k + 1));
+  e = launch_moe_combine(D->x, D->yexp, Is > 0 ? D->ysh : nullptr, D->rwts, D->rgate, nullptr, 1, k, H, D->stream);
+  if (e != hipSuccess) return hip_fail(D, e, "moe combine");
+  return DEC_OK;
+}
+
+int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, const int32_t *hpos) {
+  if (rows == 1 && D->single_row_ok) return run_layer_single(D, l, max_pos, hpos);
   const decoder_config_t &c = D->c;
   const decoder_layer_weights_t &W = D->layers[l];
   const int H = c.hidden, d = c.head_dim, qd = c.n_heads * d;
   const int qkvr = (c.n_heads + 2 * c.n_kv_heads) * d;
-  const float eps = (float)c.rms_eps;
   hipStream_t st = D->stream;
   int rc;
   hipError_t e;
 
-  e = launch_rmsnorm(D->x, H, W.attn_norm, rows, H, eps, D->act, H, st);
-  if (e != hipSuccess) return hip_fail(D, e, "rmsnorm");
-  if ((rc = gemm(D, EPI_STORE, D->act, H, W.w_qkv, rows, qkvr, H, D->qkv, nullptr, qkvr, nullptr))) return rc;
-  RopeArgs ra{};
-  ra.qkv = D->qkv;
-  ra.bias = c.qkv_bias ? W.b_qkv : nullptr;
-  ra.cs = D->rope;
-  ra.row_seq = D->row_seq;
-  ra.row_pos = D->row_pos;
-  ra.q = D->q;
-  ra.kcache = D->kcache;
-  ra.vcache = D->vcache;
-  ra.seq_stride = D->L.seq_stride;
-  ra.layer_off = (int64_t)l * c.n_kv_heads * (int64_t)D->L.S * d;
-  ra.S = D->L.S;
-  ra.Hq = c.n_heads;
-  ra.Hkv = c.n_kv_heads;
-  ra.d = d;
-  ra.rows = rows;
-  e = launch_rope_append(ra, st);
-  if (e != hipSuccess) return hip_fail(D, e, "rope_append");
-  if ((rc = attention(D, l, rows, rows_per_group, max_pos))) return rc;
-  if ((rc = gemm(D, EPI_ADD, D->attn, qd, W.w_o, rows, H, qd, D->x, nullptr, H, nullptr))) return rc;
-  e = launch_rmsnorm(D->x, H, W.ffn_norm, rows, H, eps, D->act, H, st);
-  if (e != hipSuccess) return hip_fail(D, e, "rmsnorm");
+  // RMSNorm -> QKV (+bias) -> RoPE -> KV append, one projection launch
+  GemmArgs q = dense_args(nullptr, H, W.w_qkv, rows, qkvr, H);
+  if ((rc = norm_into(D, q, D->x, W.attn_norm, rows))) return rc;
+  q.np_off = d / 2;
+  q.qkv.bias = c.qkv_bias ? W.b_qkv : nullptr;
+  q.qkv.cs = D->rope;
+  q.qkv.row_seq = D->row_seq;
+  q.qkv.row_pos = D->row_pos;
+  q.qkv.q = D->q;
+  q.qkv.kcache = D->kcache;
+  q.qkv.vcache = D->vcache;
+  q.qkv.seq_stride = D->L.seq_stride;
+  q.qkv.layer_off = (int64_t)l * c.n_kv_heads * (int64_t)D->L.S * d;
+  q.qkv.S = D->L.S;
+  q.qkv.Hq = c.n_heads;
+  q.qkv.Hkv = c.n_kv_heads;
+  q.qkv.d = d;
+  if ((rc = proj(D, DEC_NODE_QKV, EPI_QKV, q, rows))) return rc;
+  if ((rc = attention(D, l, rows, rows_per_group, max_pos, hpos))) return rc;
+  GemmArgs o = dense_args(D->attn, qd, W.w_o, rows, H, qd);
+  o.C = D->x;
+  o.ldc = H;
+  if ((rc = proj(D, DEC_NODE_O, EPI_ADD, o, rows))) return rc;
 
   if (c.n_experts == 0) {
     const int I = c.ffn_inter;
-    if ((rc = gemm(D, EPI_SWIGLU, D->act, H, W.w_gate_up, rows, I, H, nullptr, D->h, I, nullptr))) return rc;
-    if ((rc = gemm(D, EPI_ADD, D->h, I, W.w_down, rows, H, I, D->x, nullptr, H, nullptr))) return rc;
-    return DEC_OK;
+    GemmArgs gu = dense_args(nullptr, H, W.w_gate_up, rows, I, H);
+    if ((rc = norm_into(D, gu, D->x, W.ffn_norm, rows))) return rc;
+    gu.Hout = D->h;
+    gu.ldc = I;
+    if ((rc = proj(D, DEC_NODE_GATE_UP, EPI_SWIGLU, gu, rows))) return rc;
+    GemmArgs dn = dense_args(D->h, I, W.w_down, rows, H, I);
+    dn.C = D->x;
+    dn.ldc = H;
+    return proj(D, DEC_NODE_DOWN, EPI_ADD, dn, rows);
   }
-  // routed experts + shared expert
+
+  // routed experts + shared expert: the router, the shared gate and the
+  // experts all read the same normed input b (bf16 in D->act)
+  {
+    NodeTimer t(D, DEC_NODE_NORM, rows * (double)H * 6 + H * 4.0, rows * (double)H * 4);
+    e = launch_rmsnorm(D->x, H, W.ffn_norm, rows, H, (float)c.rms_eps, D->act, H, st);
+  }
+  if (e != hipSuccess) return hip_fail(D, e, "rmsnorm");
   const int E = c.n_experts, k = c.top_k, Ie = c.expert_inter, Is = c.shared_inter;
-  if ((rc = gemm(D, EPI_STORE, D->act, H, W.w_router, rows, E, H, D->rlogits, nullptr, E, nullptr))) return rc;
+  GemmArgs r = dense_args(D->act, H, W.w_router, rows, E, H);
+  r.C = D->rlogits;
+  r.ldc = E;
+  if ((rc = proj(D, DEC_NODE_ROUTER, EPI_STORE, r, rows))) return rc;
   MoeRouteArgs mr{};
   mr.logits = D->rlogits;
   mr.act = D->act;
@@ -309,19 +534,17 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos) {
   mr.group_count = D->groups + 1 + 2 * E;
   mr.pair_row = D->pair_row;
   mr.pair_of = D->pair_of;
-  e = launch_moe_route(mr, st);
+  {
+    NodeTimer t(D, DEC_NODE_ROUTER, rows * (double)E * 4 + rows * (double)H * 2, rows * (double)E * 8);
+    e = launch_moe_route(mr, true, st);
+  }
   if (e != hipSuccess) return hip_fail(D, e, "moe_route");
   const int slots = std::min(E, rows * k);
   const int grp_rows = std::min(rows, 32);
-  GemmArgs g{};
-  g.A = D->act;
+  const double exp_bytes = (double)slots * 3.0 * Ie * H * 2;
+  GemmArgs g = dense_args(D->act, H, W.w_exp_gate_up, rows * k, Ie, H);
   g.a_rows = D->pair_row;
-  g.lda = H;
-  g.W = W.w_exp_gate_up;
   g.w_group_stride = (int64_t)2 * Ie * H;
-  g.M = rows * k;
-  g.N = Ie;
-  g.K = H;
   g.Hout = D->hexp;
   g.ldc = Ie;
   g.n_groups = mr.n_groups;
@@ -329,7 +552,11 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos) {
   g.group_start = mr.group_start;
   g.group_count = mr.group_count;
   g.ksplit = 1;
-  e = launch_gemm(g, EPI_SWIGLU, grp_rows, slots, st);
+  {
+    NodeTimer t(D, DEC_NODE_EXPERTS, exp_bytes * 2.0 / 3.0 + rows * (double)H * 2 + rows * (double)k * Ie * 2,
+                2.0 * rows * k * 2.0 * Ie * H);
+    e = launch_gemm(g, EPI_SWIGLU, grp_rows, slots, st);
+  }
   if (e != hipSuccess) return hip_fail(D, e, "moe gate_up");
   g.A = D->hexp;
   g.a_rows = nullptr;
@@ -338,15 +565,27 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos) {
   g.w_group_stride = (int64_t)H * Ie;
   g.N = H;
   g.K = Ie;
+  g.np_off = H;
   g.Hout = nullptr;
   g.C = D->yexp;
   g.ldc = H;
-  e = launch_gemm(g, EPI_STORE, grp_rows, slots, st);
+  {
+    NodeTimer t(D, DEC_NODE_EXPERTS, exp_bytes / 3.0 + rows * (double)k * Ie * 2 + rows * (double)k * H * 4,
+                2.0 * rows * k * (double)Ie * H);
+    e = launch_gemm(g, EPI_STORE, grp_rows, slots, st);
+  }
   if (e != hipSuccess) return hip_fail(D, e, "moe down");
   if (Is > 0) {
-    if ((rc = gemm(D, EPI_SWIGLU, D->act, H, W.w_sh_gate_up, rows, Is, H, nullptr, D->hsh, Is, nullptr))) return rc;
-    if ((rc = gemm(D, EPI_STORE, D->hsh, Is, W.w_sh_down, rows, H, Is, D->ysh, nullptr, H, nullptr))) return rc;
+    GemmArgs sg = dense_args(D->act, H, W.w_sh_gate_up, rows, Is, H);
+    sg.Hout = D->hsh;
+    sg.ldc = Is;
+    if ((rc = proj(D, DEC_NODE_EXPERTS, EPI_SWIGLU, sg, rows))) return rc;
+    GemmArgs sd = dense_args(D->hsh, Is, W.w_sh_down, rows, H, Is);
+    sd.C = D->ysh;
+    sd.ldc = H;
+    if ((rc = proj(D, DEC_NODE_EXPERTS, EPI_STORE, sd, rows))) return rc;
   }
+  NodeTimer tcomb(D, DEC_NODE_EXPERTS, rows * (double)H * (8.0 + 4.0 * k + 4.0), rows * (double)H * 2 * (k + 1));
   e = launch_moe_combine(D->x, D->yexp, Is > 0 ? D->ysh : nullptr, D->rwts, D->rgate, D->pair_of, rows,
                          k, H, st);
   if (e != hipSuccess) return hip_fail(D, e, "moe combine");
@@ -355,32 +594,56 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos) {
 
 // Embedding, all layers, then (optionally) final norm + lm-head + argmax on
 // rows [first, first + nout).
-int run_step(decoder *D, int rows, int rows_per_group, int max_pos, int use_next, int first,
-             int nout, float *d_logits, int32_t *d_argmax, int argmax_rows) {
+int run_step(decoder *D, int rows, int rows_per_group, int max_pos, const int32_t *hpos, int use_next,
+             int first, int nout, float *d_logits, int32_t *d_argmax, int argmax_rows) {
   const decoder_config_t &c = D->c;
   hipStream_t st = D->stream;
-  hipError_t e = launch_embed(D->embed, D->ids, D->next_token, D->row_seq, use_next, rows, c.hidden,
-                              D->x, st);
+  hipError_t e;
+  {
+    NodeTimer t(D, DEC_NODE_EMBED, rows * (double)c.hidden * 6, 0);
+    e = launch_embed(D->embed, D->ids, D->next_token, D->row_seq, use_next, rows, c.hidden, D->x, st);
+  }
   if (e != hipSuccess) return hip_fail(D, e, "embed");
   const int nl = D->layer_limit >= 0 ? std::min(D->layer_limit, c.n_layers) : c.n_layers;
   for (int l = 0; l < nl; ++l) {
-    int rc = run_layer(D, l, rows, rows_per_group, max_pos);
+    int rc = run_layer(D, l, rows, rows_per_group, max_pos, hpos);
     if (rc) return rc;
   }
   D->last_rows = rows;
   if (nout <= 0) return DEC_OK;
+  // final RMSNorm + lm-head + greedy argmax (pipeline.rs lm_head_forward;
+  // decoder.rs folded lm-head + argmax: only the token id has to leave the GPU)
   const int H = c.hidden;
-  e = launch_rmsnorm(D->x + (size_t)first * H, H, D->final_norm, nout, H, (float)c.rms_eps, D->act, H, st);
-  if (e != hipSuccess) return hip_fail(D, e, "final rmsnorm");
   float *out = d_logits ? d_logits : D->logits;
-  int rc = gemm(D, EPI_STORE, D->act, H, D->lm_head, nout, c.vocab, H, out, nullptr, c.vocab, nullptr);
-  if (rc) return rc;
-  // argmax over the last argmax_rows output rows; row r of the output belongs
-  // to input row first + r
-  const int a0 = nout - argmax_rows;
-  e = launch_argmax(out + (size_t)a0 * c.vocab, c.vocab, argmax_rows, c.vocab, d_argmax, D->next_token,
-                    D->row_seq + first + a0, st);
+  int nparts, rc;
+  if (nout == 1 && D->single_row_ok) {
+    GemvArgs g = gemv_args(D->lm_head, D->x + (size_t)first * H, H, c.vocab, out);
+    g.gamma = D->final_norm;
+    g.eps = (float)c.rms_eps;
+    g.part_val = D->am_val;
+    g.part_idx = D->am_idx;
+    if ((rc = gemv(D, DEC_NODE_HEAD, EPI_LOGITS, g))) return rc;
+    nparts = gemv_blocks(c.vocab);
+  } else {
+    GemmArgs g = dense_args(nullptr, H, D->lm_head, nout, c.vocab, H);
+    if ((rc = norm_into(D, g, D->x + (size_t)first * H, D->final_norm, nout))) return rc;
+    g.C = out;
+    g.ldc = c.vocab;
+    g.am.part_val = D->am_val;
+    g.am.part_idx = D->am_idx;
+    if ((rc = proj(D, DEC_NODE_HEAD, EPI_LOGITS, g, nout))) return rc;
+    nparts = gemm_ntiles(g, EPI_LOGITS);
+  }
+  {
+    NodeTimer t(D, DEC_NODE_HEAD, nout * (double)nparts * 8, 0);
+    e = launch_argmax_finalize(D->am_val, D->am_idx, nparts, nout, D->am_out, D->next_token, D->row_seq + first, st);
+  }
   if (e != hipSuccess) return hip_fail(D, e, "argmax");
+  if (d_argmax) {
+    const int a0 = nout - argmax_rows;
+    HIP_TRY(D, hipMemcpyAsync(d_argmax, D->am_out + a0, (size_t)argmax_rows * 4, hipMemcpyDeviceToDevice, st),
+            "argmax copy");
+  }
   return DEC_OK;
 }
 
@@ -456,6 +719,20 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
   D->part_o = carve<float>(D, L.part_o);
   D->part_ml = carve<float>(D, L.part_ml);
   D->gpart = carve<float>(D, L.gpart);
+  D->counters = carve<int32_t>(D, L.counters);
+  D->am_val = carve<float>(D, L.am_val);
+  D->am_idx = carve<int32_t>(D, L.am_idx);
+  D->am_out = carve<int32_t>(D, L.am_out);
+  D->f32_attn = carve<float>(D, L.f32_attn);
+  D->f32_h = carve<float>(D, L.f32_h);
+  D->f32_act = carve<float>(D, L.f32_act);
+  D->f32_hexp = carve<float>(D, L.f32_hexp);
+  {
+    const int qd = cfg->n_heads * cfg->head_dim;
+    const int kmax = std::max(std::max(cfg->hidden, qd), std::max(std::max(cfg->ffn_inter, cfg->shared_inter),
+                                                                      cfg->expert_inter));
+    D->single_row_ok = (size_t)kmax * 4 <= GEMV_MAX_LDS;
+  }
   if (cfg->n_experts > 0) {
     D->rlogits = carve<float>(D, L.rlogits);
     D->rids = carve<int32_t>(D, L.rids);
@@ -508,6 +785,7 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
   if (hipMemsetAsync(D->kcache, 0, kvb, D->stream) != hipSuccess ||
       hipMemsetAsync(D->vcache, 0, kvb, D->stream) != hipSuccess ||
       hipMemsetAsync(D->next_token, 0, (size_t)cfg->max_batch * 4, D->stream) != hipSuccess ||
+      hipMemsetAsync(D->counters, 0, (size_t)(1 + ATTN_MAX_TASKS) * 4, D->stream) != hipSuccess ||
       hipStreamSynchronize(D->stream) != hipSuccess)
     return cleanup(DEC_E_HIP);
   *out = D;
@@ -517,6 +795,7 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
 void decoder_free(decoder_t *D) {
   if (!D) return;
   (void)hipStreamSynchronize(D->stream);
+  for (auto &ev : D->tev) (void)hipEventDestroy(ev);
   if (D->pinned) (void)hipHostFree(D->pinned);
   for (int i = 0; i < STAGE_RING; ++i) (void)hipEventDestroy(D->ev[i]);
   delete D;
@@ -551,7 +830,7 @@ int prefill_chunk(decoder_t *D, int32_t seq, const int32_t *ids, int32_t n, int3
   const int G = c.n_heads / c.n_kv_heads;
   const int nout = logits_mode == 0 ? 0 : (logits_mode == 1 ? 1 : n);
   const int first = logits_mode == 1 ? n - 1 : 0;
-  rc = run_step(D, n, 16 / G, start_pos + n - 1, 0, first, nout, d_logits, d_argmax, nout ? 1 : 0);
+  rc = run_step(D, n, 16 / G, start_pos + n - 1, pos.data(), 0, first, nout, d_logits, d_argmax, nout ? 1 : 0);
   if (rc) return rc;
   D->len[seq] = start_pos + n;
   if (nout) D->has_next[seq] = 1;
@@ -581,7 +860,7 @@ int decode_step(decoder_t *D, int32_t batch, const int32_t *seqs, const int32_t 
   }
   int rc = stage_rows(D, batch, tokens, seqs, pos.data());
   if (rc) return rc;
-  rc = run_step(D, batch, 1, max_pos, tokens ? 0 : 1, 0, batch, d_logits, d_argmax, batch);
+  rc = run_step(D, batch, 1, max_pos, pos.data(), tokens ? 0 : 1, 0, batch, d_logits, d_argmax, batch);
   if (rc) return rc;
   for (int b = 0; b < batch; ++b) {
     D->len[seqs[b]] += 1;
@@ -649,12 +928,44 @@ int dec_diag_gemm(const uint16_t *d_A, int32_t M, int32_t K, const uint16_t *d_W
   return launch_gemm(g, EPI_STORE, M, 1, (hipStream_t)stream) == hipSuccess ? DEC_OK : DEC_E_HIP;
 }
 
+int dec_diag_gemv(const float *d_a, int32_t K, const uint16_t *d_W, int32_t N, float *d_y, void *stream) {
+  if (!d_a || !d_W || !d_y || N < 1 || K < 8 || K % 8 || (size_t)K * 4 > GEMV_MAX_LDS) return DEC_E_INVALID;
+  GemvArgs g = gemv_args(d_W, d_a, K, N, d_y);
+  return launch_gemv(g, EPI_STORE, (hipStream_t)stream) == hipSuccess ? DEC_OK : DEC_E_HIP;
+}
+
 int dec_diag_rmsnorm(const float *d_x, const float *d_g, int32_t rows, int32_t H, double eps, uint16_t *d_out,
                      void *stream) {
   if (!d_x || !d_g || !d_out || rows < 1 || H < 4 || H % 4) return DEC_E_INVALID;
   return launch_rmsnorm(d_x, H, d_g, rows, H, (float)eps, d_out, H, (hipStream_t)stream) == hipSuccess
              ? DEC_OK
              : DEC_E_HIP;
+}
+
+int decoder_stats_enable(decoder_t *D, int32_t node_mask) {
+  if (check_dec(D)) return DEC_E_INVALID;
+  if (node_mask) {
+    if (D->tev.empty()) {
+      D->tev.resize(TIMER_EVENTS);
+      for (auto &ev : D->tev) HIP_TRY(D, hipEventCreate(&ev), "stats events");
+    }
+    int rc = stats_harvest(D);
+    if (rc) return rc;
+    D->stats = decoder_stats_t{};
+  } else {
+    int rc = stats_harvest(D);
+    if (rc) return rc;
+  }
+  D->stats_mask = (uint32_t)node_mask;
+  return DEC_OK;
+}
+
+int decoder_stats_read(decoder_t *D, decoder_stats_t *out) {
+  if (check_dec(D) || !out) return DEC_E_INVALID;
+  int rc = stats_harvest(D);
+  if (rc) return rc;
+  *out = D->stats;
+  return DEC_OK;
 }
 
 int decoder_debug_layer_limit(decoder_t *D, int32_t layers) {

@@ -1,23 +1,28 @@
 // Projection kernel: C[m][n] = sum_k A[m][k] W[n][k] for the QKV, o_proj,
-// gate/up, down, router and lm-head products (engine.zig: every projection
-// is a 1x1 conv y = W x per token column; decoder.rs AttnWeights: weights
-// are row-major [out][in]).
+// gate/up, down, router, expert and lm-head products (engine.zig: every
+// projection is a 1x1 conv y = W x per token column; decoder.rs AttnWeights:
+// weights are row-major [out][in]).
 //
 // Design for gfx950 (weights are read exactly once per call, so the kernel
 // is bound by HBM bandwidth for decode and small chunks):
-//  * One block = 4 wavefronts = one 16-row tile of W (two tiles for the
-//    SwiGLU epilogue: gate rows n and up rows n + N).  The 4 waves split the
-//    K loop by interleaved 32-wide steps, so at every step the block reads
-//    256 contiguous bytes of each weight row.
+//  * One block = NW wavefronts = one 16-row tile of W (two tiles for the
+//    paired epilogues: SwiGLU gate rows n and up rows n + N; QKV rows i and
+//    i + d/2 of a head, the two halves RoPE rotates together).  The waves
+//    split the K loop by interleaved 32-wide steps, so at every step the
+//    block reads NW * 64 contiguous bytes of each weight row.
 //  * Weight fragments go straight from HBM into MFMA B-operand registers
-//    with 16-byte non-temporal loads (lane l reads row l % 16, k offset
-//    8 (l / 16)); activations (tiny, L2-resident) are the A operand, MT
-//    tiles of 16 rows each, so one weight fragment feeds MT MFMAs.
-//  * v_mfma_f32_16x16x32_bf16 accumulates in fp32; the 4 partial tiles are
-//    summed in LDS in fixed wave order (deterministic), then the epilogue
-//    (store / residual add / SwiGLU) runs on the block's 256 threads.
+//    with 16-byte loads (lane l reads row l % 16 at k offset
+//    8 (l / 16)); activations are the A operand, MT tiles of 16 rows, so one
+//    weight fragment feeds MT MFMAs (v_mfma_f32_16x16x32_bf16, fp32 acc).
+//  * A comes from global memory (L2-resident), or, for decode, is built once
+//    per block in LDS by the fused RMSNorm prologue (engine.zig rmsnormColumn:
+//    x / sqrt(mean(x^2) + eps) * g, fp32, rounded to bf16 as the MFMA input).
+//  * The NW partial tiles are summed in LDS in fixed wave order
+//    (deterministic); the epilogue (store / residual add / SwiGLU / bias +
+//    RoPE + KV append / logits with per-tile argmax candidates) runs on 256
+//    threads.
 //  * Optional split-K across blocks (blockIdx.z) writes fp32 partials that
-//    gemm_reduce sums in fixed split order.
+//    gemm_reduce sums in fixed split order and then applies the epilogue.
 //  * Grouped mode (MoE experts): blockIdx.y selects a group (one expert and
 //    a contiguous run of rows); the weight base moves to that expert.
 #include "common.h"
@@ -25,45 +30,111 @@
 
 namespace {
 
-constexpr int NWAVES = 4;
+template <int EPI>
+constexpr int paired() {
+  return (EPI == EPI_SWIGLU || EPI == EPI_QKV) ? 2 : 1;
+}
 
-template <int MT, int NP, int U>
-__device__ __forceinline__ void gemm_tile(const GemmArgs &g, const uint16_t *W, int row0, int rows,
-                                          int mp, int n0, int s0, int s1, f32x4 (&acc)[MT][NP]) {
+// First weight row of tile b.
+template <int EPI>
+__device__ __forceinline__ int tile_n0(const GemmArgs &g, int b) {
+  if (EPI == EPI_QKV) {
+    const int per_head = g.qkv.d / 32;  // tile pairs per head
+    const int hh = b / per_head, j = b - hh * per_head;
+    return hh * g.qkv.d + 16 * j;
+  }
+  return b * 16;
+}
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+// Epilogue of one output element: row orow, weight row n = n0 + c (and its
+// partner row n + np_off for the paired epilogues).
+template <int EPI>
+__device__ __forceinline__ void epi_apply(const GemmArgs &g, int64_t orow, int n, float v0, float v1) {
+  if (EPI == EPI_STORE) {
+    g.C[orow * g.ldc + n] = v0 + (g.bias ? g.bias[n] : 0.f);
+  } else if (EPI == EPI_ADD) {
+    g.C[orow * g.ldc + n] += v0;
+  } else if (EPI == EPI_SWIGLU) {
+    g.Hout[orow * g.ldc + n] = (uint16_t)f32_to_bf16_bits(silu_f(v0) * v1);
+  } else if (EPI == EPI_LOGITS) {
+    g.C[orow * g.ldc + n] = v0;
+  } else if (EPI == EPI_QKV) {
+    // bias, then RoPE on q and k rows, then the KV-cache append (engine.zig
+    // ropeAndCache, "rope" pairing u_i with u_{i+d/2}; decoder.rs AttnWeights:
+    // bias before RoPE).  K goes to row pos of the [S][d] cache, V to
+    // column pos of the transposed [d][S] cache.
+    const QkvEpi &q = g.qkv;
+    const int d = q.d, half = d / 2;
+    const int hh = n / d, i = n - hh * d;  // i < d/2
+    float u0 = v0, u1 = v1;
+    if (q.bias) {
+      u0 += q.bias[n];
+      u1 += q.bias[n + half];
+    }
+    const int pos = q.row_pos[orow], seq = q.row_seq[orow];
+    const int64_t base = (int64_t)seq * q.seq_stride + q.layer_off;
+    if (hh < q.Hq + q.Hkv) {
+      const float2 t = q.cs[(int64_t)pos * half + i];
+      const float r0 = u0 * t.x - u1 * t.y;
+      const float r1 = u0 * t.y + u1 * t.x;
+      uint16_t *dst;
+      if (hh < q.Hq) dst = q.q + (orow * q.Hq + hh) * d;
+      else dst = q.kcache + base + ((int64_t)(hh - q.Hq) * q.S + pos) * d;
+      dst[i] = (uint16_t)f32_to_bf16_bits(r0);
+      dst[i + half] = (uint16_t)f32_to_bf16_bits(r1);
+    } else {
+      uint16_t *vt = q.vcache + base + (int64_t)(hh - q.Hq - q.Hkv) * d * q.S;
+      vt[(int64_t)i * q.S + pos] = (uint16_t)f32_to_bf16_bits(u0);
+      vt[(int64_t)(i + half) * q.S + pos] = (uint16_t)f32_to_bf16_bits(u1);
+    }
+  }
+}
+
+// Accumulate this wave's share of the block tile.  AMODE 0: A from global;
+// AMODE 2: A from the normalised bf16 copy in LDS (row m at a_lds + m * K).
+template <int MT, int NP, int U, int NW, int AMODE>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &g, const uint16_t *W, const uint16_t *a_lds,
+                                          int row0, int rows, int mp, int n0, bool nvalid, int s0,
+                                          int s1, f32x4 (&acc)[MT][NP]) {
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = threadIdx.x / WAVE;
   const int c = lane & 15, quad = lane >> 4;
-  const int N = g.N, K = g.K;
-  const bool nvalid = (n0 + c) < N;
+  const int K = g.K;
   const uint16_t *wrow[NP];
 #pragma unroll
-  for (int p = 0; p < NP; ++p) wrow[p] = W + (int64_t)(n0 + c + p * N) * K + quad * 8;
+  for (int p = 0; p < NP; ++p) wrow[p] = W + (int64_t)(n0 + c + p * g.np_off) * K + quad * 8;
   const uint16_t *arow[MT];
   bool mvalid[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    int m = mp + t * 16 + c;
+    const int m = mp + t * 16 + c;
     mvalid[t] = m < rows;
-    int64_t src = 0;
-    if (mvalid[t]) src = g.a_rows ? g.a_rows[row0 + m] : (row0 + m);
-    arow[t] = g.A + src * g.lda + quad * 8;
+    if (AMODE == 2) {
+      arow[t] = a_lds + (int64_t)(mvalid[t] ? m : 0) * K + quad * 8;
+    } else {
+      int64_t src = 0;
+      if (mvalid[t]) src = g.a_rows ? g.a_rows[row0 + m] : (row0 + m);
+      arow[t] = g.A + src * g.lda + quad * 8;
+    }
   }
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
     for (int p = 0; p < NP; ++p) acc[t][p] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int st = s0 + wave; st < s1; st += NWAVES * U) {
+  for (int st = s0 + wave; st < s1; st += NW * U) {
     u32x4 wf[U][NP];
     u32x4 af[U][MT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int step = st + u * NWAVES;
+      const int step = st + u * NW;
       const int k = step * 32;
       const bool kv = (step < s1) && (k + quad * 8 < K);
 #pragma unroll
       for (int p = 0; p < NP; ++p)
-        wf[u][p] = (kv && nvalid) ? load_stream16(wrow[p] + k) : u32x4{0u, 0u, 0u, 0u};
+        wf[u][p] = (kv && nvalid) ? load16(wrow[p] + k) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int t = 0; t < MT; ++t)
         af[u][t] = (kv && mvalid[t]) ? load16(arow[t] + k) : u32x4{0u, 0u, 0u, 0u};
@@ -78,12 +149,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const uint16_t *W, 
   }
 }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
-
-template <int MT, int EPI, int U>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
-  constexpr int NP = (EPI == EPI_SWIGLU) ? 2 : 1;
-  __shared__ f32x4 red[NWAVES][MT][NP][WAVE];
+template <int MT, int EPI, int U, int NW, int AMODE>
+__global__ __launch_bounds__(NW * WAVE) void gemm_kernel(GemmArgs g) {
+  constexpr int NP = paired<EPI>();
+  __shared__ f32x4 red[NW][NP][WAVE];
+  __shared__ float inv_s[16];
+  __shared__ float sred[NW];
+  extern __shared__ uint4 dyn_lds[];
+  uint16_t *a_lds = reinterpret_cast<uint16_t *>(dyn_lds);
 
   const uint16_t *W = g.W;
   int row0 = 0, rows = g.M;
@@ -94,7 +167,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     row0 = g.group_start[gi];
     rows = g.group_count[gi];
   }
-  const int n0 = blockIdx.x * 16;
+  const int n0 = tile_n0<EPI>(g, blockIdx.x);
+  const bool nvalid = (EPI == EPI_QKV) || (n0 + (threadIdx.x & 15)) < g.N;
   const int steps = (g.K + 31) / 32;
   int s0 = 0, s1 = steps;
   if (g.ksplit > 1) {
@@ -105,87 +179,136 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = threadIdx.x / WAVE;
 
-  for (int mp = 0; mp < rows; mp += 16 * MT) {
-    f32x4 acc[MT][NP];
-    gemm_tile<MT, NP, U>(g, W, row0, rows, mp, n0, s0, s1, acc);
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int p = 0; p < NP; ++p) red[wave][t][p][lane] = acc[t][p];
+  if (AMODE == 2) {
+    // fused RMSNorm prologue (rows <= 16): per-row 1/rms in fixed order, then
+    // the normalised bf16 rows into LDS
+    const int K = g.K;
+    for (int m = 0; m < rows; ++m) {
+      const float *xr = g.x + (int64_t)m * g.lda;
+      float ss = 0.f;
+      for (int k = threadIdx.x * 4; k < K; k += NW * WAVE * 4) {
+        const f32x4 v = loadf4(xr + k);
+        ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+      }
+      ss = block_sum<NW>(ss, sred);
+      if (threadIdx.x == 0) inv_s[m] = 1.0f / sqrtf(ss / (float)K + g.eps);
+    }
     __syncthreads();
-    // thread -> (lane', i): output row 4 (lane' / 16) + i of each m-tile, column lane' % 16
-    const int ol = threadIdx.x >> 2, oi = threadIdx.x & 3;
-    const int n = n0 + (ol & 15);
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int m = mp + t * 16 + (ol >> 4) * 4 + oi;
-      float v[NP];
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        float s = 0.f;
-#pragma unroll
-        for (int w = 0; w < NWAVES; ++w) s += red[w][t][p][ol][oi];
-        v[p] = s;
-      }
-      if (m < rows && n < g.N) {
-        const int64_t orow = row0 + m;
-        if (g.ksplit > 1) {
-          float *dst = g.Cpart + ((int64_t)blockIdx.z * g.M + orow) * (NP * g.N);
-#pragma unroll
-          for (int p = 0; p < NP; ++p) dst[n + p * g.N] = v[p];
-        } else if (EPI == EPI_STORE) {
-          g.C[orow * g.ldc + n] = v[0] + (g.bias ? g.bias[n] : 0.f);
-        } else if (EPI == EPI_ADD) {
-          g.C[orow * g.ldc + n] += v[0];
-        } else {
-          g.Hout[orow * g.ldc + n] = (uint16_t)f32_to_bf16_bits(silu_f(v[0]) * v[NP - 1]);
-        }
-      }
+    const int k8 = K / 8;
+    for (int e = threadIdx.x; e < rows * k8; e += NW * WAVE) {
+      const int m = e / k8, k = (e - m * k8) * 8;
+      const float *xr = g.x + (int64_t)m * g.lda + k;
+      const f32x4 x0 = loadf4(xr), x1 = loadf4(xr + 4);
+      const f32x4 g0 = loadf4(g.gamma + k), g1 = loadf4(g.gamma + k + 4);
+      const float iv = inv_s[m];
+      u32x4 o;
+      o[0] = pack_bf16x2(x0[0] * iv * g0[0], x0[1] * iv * g0[1]);
+      o[1] = pack_bf16x2(x0[2] * iv * g0[2], x0[3] * iv * g0[3]);
+      o[2] = pack_bf16x2(x1[0] * iv * g1[0], x1[1] * iv * g1[1]);
+      o[3] = pack_bf16x2(x1[2] * iv * g1[2], x1[3] * iv * g1[3]);
+      *reinterpret_cast<u32x4 *>(a_lds + (int64_t)m * K + k) = o;
     }
     __syncthreads();
   }
+
+  for (int mp = 0; mp < rows; mp += 16 * MT) {
+    f32x4 acc[MT][NP];
+    gemm_tile<MT, NP, U, NW, AMODE>(g, W, a_lds, row0, rows, mp, n0, nvalid, s0, s1, acc);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) red[wave][p][lane] = acc[t][p];
+      __syncthreads();
+      if (threadIdx.x < 256) {
+        // thread -> (lane', i): output row 4 (lane' / 16) + i of the m-tile, column lane' % 16
+        const int ol = threadIdx.x >> 2, oi = threadIdx.x & 3;
+        const int c = ol & 15;
+        const int n = n0 + c;
+        const int m = mp + t * 16 + (ol >> 4) * 4 + oi;
+        float v[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          float s = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) s += red[w][p][ol][oi];
+          v[p] = s;
+        }
+        const bool ok = m < rows && (EPI == EPI_QKV || n < g.N);
+        if (ok) {
+          const int64_t orow = row0 + m;
+          if (g.ksplit > 1) {
+            const int64_t np_cols = (int64_t)gridDim.x * 16;
+            float *dst = g.Cpart + ((int64_t)blockIdx.z * g.M + orow) * NP * np_cols;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) dst[p * np_cols + blockIdx.x * 16 + c] = v[p];
+          } else {
+            epi_apply<EPI>(g, orow, n, v[0], v[NP - 1]);
+          }
+        }
+        if (EPI == EPI_LOGITS) {
+          // best (value, index) of this tile's 16 columns for row m: the 16
+          // columns of a row sit in lanes that differ in bits 2..5
+          float bv = ok ? v[0] : -INFINITY;
+          int bi = ok ? n : 0x7fffffff;
+#pragma unroll
+          for (int o = 4; o <= 32; o <<= 1) {
+            const float ov = __shfl_xor(bv, o, WAVE);
+            const int oi2 = __shfl_xor(bi, o, WAVE);
+            if (better(ov, oi2, bv, bi)) {
+              bv = ov;
+              bi = oi2;
+            }
+          }
+          if (c == 0 && m < rows) {
+            g.am.part_val[(int64_t)m * gridDim.x + blockIdx.x] = bv;
+            g.am.part_idx[(int64_t)m * gridDim.x + blockIdx.x] = bi;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
 }
 
 template <int EPI>
-__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g) {
-  constexpr int NP = (EPI == EPI_SWIGLU) ? 2 : 1;
-  const int64_t total = (int64_t)g.M * g.N;
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g, int ntiles) {
+  constexpr int NP = paired<EPI>();
+  const int64_t np_cols = (int64_t)ntiles * 16;
+  const int64_t total = (int64_t)g.M * np_cols;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t m = e / g.N;
-    const int n = (int)(e - m * g.N);
+    const int64_t m = e / np_cols;
+    const int pc = (int)(e - m * np_cols);
+    const int n = tile_n0<EPI>(g, pc / 16) + (pc & 15);
+    if (EPI != EPI_QKV && n >= g.N) continue;
     float v[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       float s = 0.f;
-      for (int z = 0; z < g.ksplit; ++z) s += g.Cpart[((int64_t)z * g.M + m) * (NP * g.N) + n + p * g.N];
+      for (int z = 0; z < g.ksplit; ++z) s += g.Cpart[((int64_t)z * g.M + m) * NP * np_cols + p * np_cols + pc];
       v[p] = s;
     }
-    if (EPI == EPI_STORE) {
-      g.C[m * g.ldc + n] = v[0] + (g.bias ? g.bias[n] : 0.f);
-    } else if (EPI == EPI_ADD) {
-      g.C[m * g.ldc + n] += v[0];
-    } else {
-      g.Hout[m * g.ldc + n] = (uint16_t)f32_to_bf16_bits(silu_f(v[0]) * v[NP - 1]);
-    }
+    epi_apply<EPI>(g, m, n, v[0], v[NP - 1]);
   }
 }
 
-template <int MT, int EPI>
-hipError_t launch_mt(const GemmArgs &g, dim3 grid, hipStream_t st) {
-  constexpr int NP = (EPI == EPI_SWIGLU) ? 2 : 1;
-  constexpr int U = (MT * 1 + NP) <= 3 ? 8 : ((MT + NP) <= 6 ? 4 : 2);
-  hipLaunchKernelGGL((gemm_kernel<MT, EPI, U>), grid, dim3(256), 0, st, g);
+template <int MT, int EPI, int NW, int AMODE>
+hipError_t launch_cfg(const GemmArgs &g, dim3 grid, size_t dyn, hipStream_t st) {
+  constexpr int NP = paired<EPI>();
+  constexpr int U = (MT + NP) <= 3 ? 8 : ((MT + NP) <= 6 ? 4 : 2);
+  hipLaunchKernelGGL((gemm_kernel<MT, EPI, U, NW, AMODE>), grid, dim3(NW * WAVE), dyn, st, g);
   return hipGetLastError();
 }
 
 template <int EPI>
-hipError_t launch_epi(const GemmArgs &g, int mt, dim3 grid, hipStream_t st) {
+hipError_t launch_epi(const GemmArgs &g, int mt, bool norm, dim3 grid, size_t dyn, hipStream_t st) {
+  if (norm) return launch_cfg<1, EPI, 8, 2>(g, grid, dyn, st);
   switch (mt) {
-    case 1: return launch_mt<1, EPI>(g, grid, st);
-    case 2: return launch_mt<2, EPI>(g, grid, st);
-    case 4: return launch_mt<4, EPI>(g, grid, st);
-    default: return launch_mt<8, EPI>(g, grid, st);
+    case 1: return launch_cfg<1, EPI, 8, 0>(g, grid, 0, st);
+    case 2: return launch_cfg<2, EPI, 4, 0>(g, grid, 0, st);
+    case 4: return launch_cfg<4, EPI, 4, 0>(g, grid, 0, st);
+    default: return launch_cfg<8, EPI, 4, 0>(g, grid, 0, st);
   }
 }
 
@@ -198,21 +321,36 @@ int gemm_mtiles(int rows) {
   return 8;
 }
 
-hipError_t launch_gemm(const GemmArgs &g_in, int epi, int max_rows, int n_group_slots,
-                       hipStream_t st) {
-  GemmArgs g = g_in;
-  const int ntiles = (g.N + 15) / 16;
+int gemm_ntiles(const GemmArgs &g, int epi) {
+  if (epi == EPI_QKV) return (g.qkv.Hq + 2 * g.qkv.Hkv) * (g.qkv.d / 32);
+  return (g.N + 15) / 16;
+}
+
+bool gemm_norm_fits(int rows, int K) { return rows <= GEMM_NORM_MAX_ROWS && (size_t)rows * K * 2 <= GEMM_NORM_MAX_LDS; }
+
+hipError_t launch_gemm(const GemmArgs &g, int epi, int max_rows, int n_group_slots, hipStream_t st) {
+  const int ntiles = gemm_ntiles(g, epi);
+  const bool norm = g.x != nullptr;
   const int mt = gemm_mtiles(max_rows);
+  const size_t dyn = norm ? (size_t)g.M * g.K * 2 : 0;
   dim3 grid(ntiles, g.n_groups ? n_group_slots : 1, g.ksplit > 1 ? g.ksplit : 1);
   hipError_t e;
-  if (epi == EPI_STORE) e = launch_epi<EPI_STORE>(g, mt, grid, st);
-  else if (epi == EPI_ADD) e = launch_epi<EPI_ADD>(g, mt, grid, st);
-  else e = launch_epi<EPI_SWIGLU>(g, mt, grid, st);
+  switch (epi) {
+    case EPI_STORE: e = launch_epi<EPI_STORE>(g, mt, norm, grid, dyn, st); break;
+    case EPI_ADD: e = launch_epi<EPI_ADD>(g, mt, norm, grid, dyn, st); break;
+    case EPI_SWIGLU: e = launch_epi<EPI_SWIGLU>(g, mt, norm, grid, dyn, st); break;
+    case EPI_QKV: e = launch_epi<EPI_QKV>(g, mt, norm, grid, dyn, st); break;
+    default: e = launch_epi<EPI_LOGITS>(g, mt, norm, grid, dyn, st); break;
+  }
   if (e != hipSuccess || g.ksplit <= 1) return e;
-  const int64_t total = (int64_t)g.M * g.N;
-  int blocks = (int)std::min<int64_t>((total + 255) / 256, 4096);
-  if (epi == EPI_STORE) hipLaunchKernelGGL(gemm_reduce_kernel<EPI_STORE>, dim3(blocks), dim3(256), 0, st, g);
-  else if (epi == EPI_ADD) hipLaunchKernelGGL(gemm_reduce_kernel<EPI_ADD>, dim3(blocks), dim3(256), 0, st, g);
-  else hipLaunchKernelGGL(gemm_reduce_kernel<EPI_SWIGLU>, dim3(blocks), dim3(256), 0, st, g);
+  const int64_t total = (int64_t)g.M * ntiles * 16;
+  const int blocks = (int)std::min<int64_t>((total + 255) / 256, 4096);
+  switch (epi) {
+    case EPI_STORE: hipLaunchKernelGGL(gemm_reduce_kernel<EPI_STORE>, dim3(blocks), dim3(256), 0, st, g, ntiles); break;
+    case EPI_ADD: hipLaunchKernelGGL(gemm_reduce_kernel<EPI_ADD>, dim3(blocks), dim3(256), 0, st, g, ntiles); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL(gemm_reduce_kernel<EPI_SWIGLU>, dim3(blocks), dim3(256), 0, st, g, ntiles); break;
+    case EPI_QKV: hipLaunchKernelGGL(gemm_reduce_kernel<EPI_QKV>, dim3(blocks), dim3(256), 0, st, g, ntiles); break;
+    default: return hipErrorInvalidValue;  // logits are never split
+  }
   return hipGetLastError();
 }

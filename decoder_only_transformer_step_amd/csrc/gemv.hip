@@ -1,0 +1,275 @@
+// Single-token projection (batch-1 decode): y[n] = sum_k W[n][k] a[k]
+// (engine.zig: a projection at activation width 1 reads the whole weight
+// matrix for one column; pipeline.rs lm_head_forward: the row-parallel
+// matvec that dominates a decode step).
+//
+// gfx950 design: the step is a pure weight stream (2 bytes per
+// multiply-add), so the kernel is built around the HBM access shape.
+//  * Each wave owns one item (a weight row, or a row pair for the paired
+//    epilogues: SwiGLU gate/up rows n and n + N, QKV rows i and i + d/2 of
+//    a head) and walks it in 1 KB steps: lane l loads 16 contiguous bytes at
+//    k = 8 l + 512 s, so every load instruction of the wave is one
+//    contiguous kilobyte.  Long contiguous bursts sustain measurably more
+//    HBM bandwidth than 16-rows-by-64-bytes MFMA fragments.
+//  * The activation is kept in fp32 in LDS (the fused RMSNorm prologue
+//    writes it there once per block), so the only rounding on the path is
+//    the weights' own bf16 storage.  Each lane does 8 fp32 FMAs per 16-byte
+//    load, then a 64-lane butterfly sum gives the dot product.
+//  * Software pipeline: the first batch of weight loads is issued before the
+//    activation prologue, and each later batch while the previous one is
+//    consumed, so every wave keeps several kilobytes in flight at all times.
+//    A wave may own two items at once (IPW) when there are many of them.
+//  * Grouped mode (MoE experts): blockIdx.y = routing slot; the weight base
+//    moves to the chosen expert.
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int GV_WAVES = 8;
+
+template <int EPI>
+constexpr int gv_rows() {
+  return (EPI == EPI_SWIGLU || EPI == EPI_QKV) ? 2 : 1;
+}
+
+// weight rows of item `it`
+template <int EPI>
+__device__ __forceinline__ void item_rows(const GemvArgs &g, int it, int &r0, int &r1) {
+  if (EPI == EPI_QKV) {
+    const int half = g.qkv.d / 2;
+    const int hh = it / half, i = it - hh * half;
+    r0 = hh * g.qkv.d + i;
+    r1 = r0 + half;
+  } else if (EPI == EPI_SWIGLU) {
+    r0 = it;
+    r1 = it + g.N;
+  } else {
+    r0 = r1 = it;
+  }
+}
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+// Loads of UNR 1 KB steps for every row the wave owns.
+template <int R, int UNR>
+__device__ __forceinline__ void load_batch(u32x4 (&v)[UNR][R], const uint16_t *const (&wp)[R],
+                                           const bool (&rv)[R], int s0, int steps, int K, int lane) {
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) {
+    const int st = s0 + u;
+    const bool ok = st < steps && st * 512 + lane * 8 < K;
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[u][r] = (ok && rv[r]) ? load16(wp[r] + st * 512) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// acc[r] += dot(weights of batch, activation) over UNR steps.
+template <int R, int UNR>
+__device__ __forceinline__ void fma_batch(float (&acc)[R], const u32x4 (&v)[UNR][R], const float *xs, int s0,
+                                          int steps, int K, int lane) {
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) {
+    const int k = (s0 + u) * 512 + lane * 8;
+    if ((s0 + u) < steps && k < K) {
+      const f32x4 xa = *reinterpret_cast<const f32x4 *>(xs + k);
+      const f32x4 xb = *reinterpret_cast<const f32x4 *>(xs + k + 4);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const u32x4 w = v[u][r];
+        float a = acc[r];
+        a = fmaf(bf16_lo(w[0]), xa[0], a);
+        a = fmaf(bf16_hi(w[0]), xa[1], a);
+        a = fmaf(bf16_lo(w[1]), xa[2], a);
+        a = fmaf(bf16_hi(w[1]), xa[3], a);
+        a = fmaf(bf16_lo(w[2]), xb[0], a);
+        a = fmaf(bf16_hi(w[2]), xb[1], a);
+        a = fmaf(bf16_lo(w[3]), xb[2], a);
+        a = fmaf(bf16_hi(w[3]), xb[3], a);
+        acc[r] = a;
+      }
+    }
+  }
+}
+
+template <int EPI, int IPW, int UNR>
+__global__ __launch_bounds__(GV_WAVES * WAVE) void gemv_kernel(GemvArgs g) {
+  constexpr int NR = gv_rows<EPI>();
+  constexpr int R = NR * IPW;  // weight rows this wave streams at once
+  extern __shared__ float xs[];
+  __shared__ float sred[GV_WAVES];
+  __shared__ float bv_s[GV_WAVES];
+  __shared__ int bi_s[GV_WAVES];
+
+  const uint16_t *W = g.W;
+  const float *xin = g.a_f32;
+  int out_row = 0;
+  if (g.slot_expert) {
+    const int slot = blockIdx.y;
+    W += (int64_t)g.slot_expert[slot] * g.w_group_stride;
+    if (xin) xin += (int64_t)slot * g.a_slot_stride;
+    out_row = slot;
+  }
+  const int K = g.K;
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int it0 = (blockIdx.x * GV_WAVES + wave) * IPW;
+  int rows_[R];
+  bool rv[R];
+  const uint16_t *wp[R];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    int r0 = 0, r1 = 0;
+    const bool ok = it0 + j < g.n_items;
+    if (ok) item_rows<EPI>(g, it0 + j, r0, r1);
+    rows_[j * NR] = r0;
+    rv[j * NR] = ok;
+    if (NR == 2) {
+      rows_[j * NR + NR - 1] = r1;
+      rv[j * NR + NR - 1] = ok;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) wp[r] = W + (int64_t)rows_[r] * K + lane * 8;
+  const int steps = (K + 511) / 512;
+
+  // the first weight loads go out before the activation prologue
+  u32x4 cur[UNR][R];
+  load_batch<R, UNR>(cur, wp, rv, 0, steps, K, lane);
+
+  // activation -> LDS (fp32), with the RMSNorm prologue when gamma is set
+  if (g.gamma) {
+    float ss = 0.f;
+    for (int k = threadIdx.x * 4; k < K; k += GV_WAVES * WAVE * 4) {
+      const f32x4 v = loadf4(xin + k);
+      ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    }
+    ss = block_sum<GV_WAVES>(ss, sred);
+    const float inv = 1.0f / sqrtf(ss / (float)K + g.eps);
+    for (int k = threadIdx.x * 4; k < K; k += GV_WAVES * WAVE * 4) {
+      const f32x4 v = loadf4(xin + k), w = loadf4(g.gamma + k);
+      *reinterpret_cast<f32x4 *>(xs + k) = f32x4{v[0] * inv * w[0], v[1] * inv * w[1], v[2] * inv * w[2], v[3] * inv * w[3]};
+    }
+  } else if (xin) {
+    for (int k = threadIdx.x * 4; k < K; k += GV_WAVES * WAVE * 4)
+      *reinterpret_cast<f32x4 *>(xs + k) = loadf4(xin + k);
+  } else {
+    for (int k = threadIdx.x * 8; k < K; k += GV_WAVES * WAVE * 8) {
+      const u32x4 w = load16(g.a_bf16 + k);
+      *reinterpret_cast<f32x4 *>(xs + k) = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+      *reinterpret_cast<f32x4 *>(xs + k + 4) = f32x4{bf16_lo(w[2]), bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3])};
+    }
+  }
+  __syncthreads();
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  // ping-pong between two load batches: while one is consumed the other is
+  // in flight (no register copies, so no full wait per iteration)
+  u32x4 alt[UNR][R];
+  for (int s0 = 0; s0 < steps; s0 += 2 * UNR) {
+    if (s0 + UNR < steps) load_batch<R, UNR>(alt, wp, rv, s0 + UNR, steps, K, lane);
+    fma_batch<R, UNR>(acc, cur, xs, s0, steps, K, lane);
+    if (s0 + UNR >= steps) break;
+    if (s0 + 2 * UNR < steps) load_batch<R, UNR>(cur, wp, rv, s0 + 2 * UNR, steps, K, lane);
+    fma_batch<R, UNR>(acc, alt, xs, s0 + UNR, steps, K, lane);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    if (!rv[j * NR]) continue;
+    const int r0 = rows_[j * NR], r1 = rows_[j * NR + NR - 1];
+    const float v0 = acc[j * NR], v1 = acc[j * NR + NR - 1];
+    if (EPI == EPI_LOGITS && better(v0, r0, bv, bi)) {
+      bv = v0;
+      bi = r0;
+    }
+    if (lane != 0) continue;
+    if (EPI == EPI_STORE) {
+      g.C[(int64_t)out_row * g.ldc + r0] = v0 + (g.bias ? g.bias[r0] : 0.f);
+    } else if (EPI == EPI_ADD) {
+      g.C[r0] += v0;
+    } else if (EPI == EPI_SWIGLU) {
+      g.C[(int64_t)out_row * g.ldc + r0] = silu_f(v0) * v1;
+    } else if (EPI == EPI_LOGITS) {
+      g.C[r0] = v0;
+    } else if (EPI == EPI_QKV) {
+      // bias, then RoPE on q and k rows, then the KV-cache append
+      // (engine.zig ropeAndCache, "rope" pairing u_i with u_{i+d/2};
+      // decoder.rs AttnWeights: bias before RoPE)
+      const QkvEpi &q = g.qkv;
+      const int d = q.d, half = d / 2;
+      const int hh = r0 / d, i = r0 - hh * d;
+      float u0 = v0, u1 = v1;
+      if (q.bias) {
+        u0 += q.bias[r0];
+        u1 += q.bias[r1];
+      }
+      const int pos = q.row_pos[0], seq = q.row_seq[0];
+      const int64_t base = (int64_t)seq * q.seq_stride + q.layer_off;
+      if (hh < q.Hq + q.Hkv) {
+        const float2 t = q.cs[(int64_t)pos * half + i];
+        const float a0 = u0 * t.x - u1 * t.y, a1 = u0 * t.y + u1 * t.x;
+        uint16_t *dst = hh < q.Hq ? q.q + (int64_t)hh * d : q.kcache + base + ((int64_t)(hh - q.Hq) * q.S + pos) * d;
+        dst[i] = (uint16_t)f32_to_bf16_bits(a0);
+        dst[i + half] = (uint16_t)f32_to_bf16_bits(a1);
+      } else {
+        uint16_t *vt = q.vcache + base + (int64_t)(hh - q.Hq - q.Hkv) * d * q.S;
+        vt[(int64_t)i * q.S + pos] = (uint16_t)f32_to_bf16_bits(u0);
+        vt[(int64_t)(i + half) * q.S + pos] = (uint16_t)f32_to_bf16_bits(u1);
+      }
+    }
+  }
+  if (EPI == EPI_LOGITS) {
+    // this block's best (value, index), for the argmax finalize pass
+    if (lane == 0) {
+      bv_s[wave] = bv;
+      bi_s[wave] = bi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int w = 1; w < GV_WAVES; ++w)
+        if (better(bv_s[w], bi_s[w], bv, bi)) {
+          bv = bv_s[w];
+          bi = bi_s[w];
+        }
+      g.part_val[blockIdx.x] = bv;
+      g.part_idx[blockIdx.x] = bi;
+    }
+  }
+}
+
+template <int EPI>
+hipError_t launch_e(const GemvArgs &g, int ipw, dim3 grid, size_t lds, hipStream_t st) {
+  constexpr int UP = DEC_GEMV_UNR_PAIRED, US = DEC_GEMV_UNR_SINGLE;
+  if (ipw == 2) hipLaunchKernelGGL((gemv_kernel<EPI, 2, UP>), grid, dim3(GV_WAVES * WAVE), lds, st, g);
+  else if (gv_rows<EPI>() == 2) hipLaunchKernelGGL((gemv_kernel<EPI, 1, UP>), grid, dim3(GV_WAVES * WAVE), lds, st, g);
+  else hipLaunchKernelGGL((gemv_kernel<EPI, 1, US>), grid, dim3(GV_WAVES * WAVE), lds, st, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// items per wave: two when there are enough items to keep ~2 blocks per CU busy
+int gemv_ipw(int n_items) { return n_items >= GEMV_IPW2_MIN_ITEMS ? 2 : 1; }
+int gemv_blocks(int n_items) {
+  const int per = GV_WAVES * gemv_ipw(n_items);
+  return (n_items + per - 1) / per;
+}
+
+hipError_t launch_gemv(const GemvArgs &g, int epi, hipStream_t st) {
+  const int ipw = gemv_ipw(g.n_items);
+  dim3 grid(gemv_blocks(g.n_items), g.slot_expert ? g.n_slots : 1);
+  const size_t lds = (size_t)g.K * 4;
+  switch (epi) {
+    case EPI_STORE: return launch_e<EPI_STORE>(g, ipw, grid, lds, st);
+    case EPI_ADD: return launch_e<EPI_ADD>(g, ipw, grid, lds, st);
+    case EPI_SWIGLU: return launch_e<EPI_SWIGLU>(g, ipw, grid, lds, st);
+    case EPI_QKV: return launch_e<EPI_QKV>(g, ipw, grid, lds, st);
+    default: return launch_e<EPI_LOGITS>(g, ipw, grid, lds, st);
+  }
+}

@@ -11,15 +11,62 @@
 #include "common.h"
 
 // ------------------------------------------------------------ projection --
+// decode-size row counts get the RMSNorm fused into the projection prologue
+constexpr int GEMM_NORM_MAX_ROWS = 4;
+constexpr size_t GEMM_NORM_MAX_LDS = 48 * 1024;
 int gemm_mtiles(int rows);
+int gemm_ntiles(const GemmArgs &g, int epi);
+bool gemm_norm_fits(int rows, int K);
 // max_rows: the largest row count of any group (dense: M); n_group_slots:
 // grid size over groups in grouped mode (blocks past *n_groups exit).
 hipError_t launch_gemm(const GemmArgs &g, int epi, int max_rows, int n_group_slots, hipStream_t st);
 
+// ------------------------------------------------ single-token projection --
+struct GemvArgs {
+  const uint16_t *W;          // bf16 [rows][K]
+  int64_t w_group_stride;     // grouped mode: elements between experts
+  const int32_t *slot_expert; // grouped mode: expert of each routing slot (blockIdx.y), else null
+  int32_t n_slots;
+  const float *a_f32;         // fp32 activation [K] (per slot: + slot * a_slot_stride), or null
+  int64_t a_slot_stride;
+  const uint16_t *a_bf16;     // bf16 activation [K] when a_f32 is null
+  const float *gamma;         // fused RMSNorm gain (a_f32 is then the raw residual x)
+  float eps;
+  int32_t K, N, n_items;      // N: rows of the first half (SwiGLU), n_items: rows or row pairs
+  float *C;                   // fp32 output (per slot: + slot * ldc)
+  int64_t ldc;
+  const float *bias;          // EPI_STORE only
+  QkvEpi qkv;                 // EPI_QKV
+  float *part_val;            // EPI_LOGITS: best logit of each block
+  int32_t *part_idx;
+};
+constexpr size_t GEMV_MAX_LDS = 60 * 1024;
+// GEMV launch shape: a wave owns two items from this many items on; UNR
+// steps of 1 KB per row are in flight per batch (tuned on the GPU)
+#ifndef DEC_GEMV_IPW2_MIN_ITEMS
+#define DEC_GEMV_IPW2_MIN_ITEMS (1 << 30)
+#endif
+#ifndef DEC_GEMV_UNR_SINGLE
+#define DEC_GEMV_UNR_SINGLE 4
+#endif
+#ifndef DEC_GEMV_UNR_PAIRED
+#define DEC_GEMV_UNR_PAIRED 2
+#endif
+constexpr int GEMV_IPW2_MIN_ITEMS = DEC_GEMV_IPW2_MIN_ITEMS;
+int gemv_blocks(int n_items);
+hipError_t launch_gemv(const GemvArgs &g, int epi, hipStream_t st);
+
+// idx[r] = argmax over part_val[r][0 .. nparts) (lowest index on ties), and
+// next_token[row_seq[r]] = idx[r] for the last row of each sequence
+hipError_t launch_argmax_finalize(const float *part_val, const int32_t *part_idx, int nparts, int rows,
+                                  int32_t *idx, int32_t *next_token, const int32_t *row_seq,
+                                  hipStream_t st);
+
 // ------------------------------------------------------------- attention --
 struct AttnArgs {
   const uint16_t *q;       // bf16 [rows][Hq][d], rotated
-  uint16_t *out;           // bf16 [rows][Hq][d]
+  uint16_t *out;           // bf16 [rows][Hq][d], or null when out_f32 is set
+  float *out_f32;          // fp32 [rows][Hq][d] (batch-1 decode feeds the fp32 projection)
   const uint16_t *kcache;  // K cache base: [seq][layer][Hkv][S][d]
   const uint16_t *vcache;  // V cache base, transposed: [seq][layer][Hkv][d][S]
   const int32_t *row_seq;  // [rows]
@@ -41,34 +88,19 @@ hipError_t launch_attention(const AttnArgs &a, int head_dim, hipStream_t st);
 hipError_t launch_embed(const uint16_t *E, const int32_t *ids, const int32_t *next_token,
                         const int32_t *row_seq, int use_next, int rows, int H, float *x,
                         hipStream_t st);
-// out[r] = bf16(x[r0 + r] * rsqrt(mean(x^2) + eps) * g)
+// out[r] = bf16(x[r] * rsqrt(mean(x^2) + eps) * g), or fp32 into out_f32 when it is set
 hipError_t launch_rmsnorm(const float *x, int64_t ldx, const float *g, int rows, int H, float eps,
-                          uint16_t *out, int64_t ldo, hipStream_t st);
-
-struct RopeArgs {
-  const float *qkv;        // fp32 [rows][qkv_rows]
-  const float *bias;       // fp32 [qkv_rows] or null
-  const float2 *cs;        // (cos, sin) [S][d/2]
-  const int32_t *row_seq, *row_pos;
-  uint16_t *q;             // bf16 [rows][Hq][d]
-  uint16_t *kcache, *vcache;
-  int64_t seq_stride, layer_off;
-  int32_t S, Hq, Hkv, d, rows;
-};
-hipError_t launch_rope_append(const RopeArgs &a, hipStream_t st);
+                          uint16_t *out, int64_t ldo, hipStream_t st, float *out_f32 = nullptr);
 
 // V^T cache import: src [Hkv][len][d] -> dst [Hkv][d][S] (positions < len)
 hipError_t launch_kv_load_v(const uint16_t *src, uint16_t *dst, int Hkv, int len, int d, int S,
                             hipStream_t st);
 
-// idx[r] = argmax_v logits[r][v] (lowest v on ties); also next_token[row_seq[r]] = idx[r]
-hipError_t launch_argmax(const float *logits, int64_t ld, int rows, int V, int32_t *idx,
-                         int32_t *next_token, const int32_t *row_seq, hipStream_t st);
-
 // ------------------------------------------------------------------- MoE --
 struct MoeRouteArgs {
   const float *logits;     // fp32 [rows][E] router logits
   const uint16_t *act;     // bf16 [rows][H] normed FFN input (for the shared gate)
+  const float *act_f32;    // or fp32 [rows][H] when set
   const uint16_t *w_sh_gate;  // bf16 [H] or null
   int32_t rows, E, k, H, renorm;
   int32_t *ids;            // [rows][k]
@@ -80,9 +112,10 @@ struct MoeRouteArgs {
   int32_t *pair_row;       // [rows*k]: token row of sorted pair p
   int32_t *pair_of;        // [rows*k]: sorted pair index of (row, slot)
 };
-hipError_t launch_moe_route(const MoeRouteArgs &a, hipStream_t st);
+hipError_t launch_moe_route(const MoeRouteArgs &a, bool group, hipStream_t st);
 
 // x[r][:] += sum_j wts[r][j] * y[pair_of[r*k+j]][:] + gate[r] * ysh[r][:]
+// (pair_of null: y is indexed by r*k+j directly)
 hipError_t launch_moe_combine(float *x, const float *y, const float *ysh, const float *wts,
                               const float *gate, const int32_t *pair_of, int rows, int k, int H,
                               hipStream_t st);

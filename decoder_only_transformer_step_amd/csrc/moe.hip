@@ -31,8 +31,13 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(MoeRouteArgs a
   // shared-expert gate: sigmoid(w_sg . b), fp32 dot in fixed order
   float dot = 0.f;
   if (a.w_sh_gate) {
-    const uint16_t *b = a.act + (int64_t)r * a.H;
-    for (int j = threadIdx.x; j < a.H; j += blockDim.x) dot += bf16_to_f32(b[j]) * bf16_to_f32(a.w_sh_gate[j]);
+    if (a.act_f32) {
+      const float *b = a.act_f32 + (int64_t)r * a.H;
+      for (int j = threadIdx.x; j < a.H; j += blockDim.x) dot += b[j] * bf16_to_f32(a.w_sh_gate[j]);
+    } else {
+      const uint16_t *b = a.act + (int64_t)r * a.H;
+      for (int j = threadIdx.x; j < a.H; j += blockDim.x) dot += bf16_to_f32(b[j]) * bf16_to_f32(a.w_sh_gate[j]);
+    }
   }
   dot = block_sum<ROUTE_THREADS / WAVE>(dot, red);
   if (threadIdx.x == 0) {
@@ -104,7 +109,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(float *x, const float 
   float *xr = x + (int64_t)r * H;
   for (int c = threadIdx.x; c < H; c += blockDim.x) {
     float acc = 0.f;
-    for (int j = 0; j < k; ++j) acc += wts[r * k + j] * y[(int64_t)pair_of[r * k + j] * H + c];
+    for (int j = 0; j < k; ++j) acc += wts[r * k + j] * y[(int64_t)(pair_of ? pair_of[r * k + j] : r * k + j) * H + c];
     if (ysh) acc += gate[r] * ysh[(int64_t)r * H + c];
     xr[c] += acc;
   }
@@ -112,10 +117,10 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(float *x, const float 
 
 }  // namespace
 
-hipError_t launch_moe_route(const MoeRouteArgs &a, hipStream_t st) {
+hipError_t launch_moe_route(const MoeRouteArgs &a, bool group, hipStream_t st) {
   hipLaunchKernelGGL(moe_route_kernel, dim3(a.rows), dim3(ROUTE_THREADS), 0, st, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !group) return e;
   hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(256), 0, st, a);
   return hipGetLastError();
 }

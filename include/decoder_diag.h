@@ -25,6 +25,10 @@ extern "C" {
 int dec_diag_gemm(const uint16_t *d_A, int32_t M, int32_t K, const uint16_t *d_W, int32_t N,
                   float *d_C, void *stream);
 
+/* y[n] = sum_k W[n][k] a[k] with the batch-1 decode projection kernel.
+ * a fp32 [K], W bf16 [N][K], y fp32 [N]; K % 8 == 0, K * 4 <= 61440. */
+int dec_diag_gemv(const float *d_a, int32_t K, const uint16_t *d_W, int32_t N, float *d_y, void *stream);
+
 /* out[r] = bf16(x[r] / sqrt(mean(x[r]^2) + eps) * g) for r < rows
  * (engine.zig rmsnormColumn).  x fp32 [rows][H], g fp32 [H], out bf16 [rows][H]. */
 int dec_diag_rmsnorm(const float *d_x, const float *d_g, int32_t rows, int32_t H, double eps,
@@ -41,6 +45,41 @@ int decoder_debug_read_x(decoder_t *dec, float *d_out, int32_t rows);
 /* Copy the MoE expert choices of the last call, int32 [n_layers][rows][top_k]
  * in router order, to d_out. */
 int decoder_debug_read_routes(decoder_t *dec, int32_t *d_out, int32_t rows);
+
+/* Per-node timing (engine.zig Engine Stats: time and evaluation count per
+ * node, so a slow node shows by itself).  While enabled, every kernel launch
+ * of a node is bracketed by HIP events on the decoder's stream, and the
+ * node's algorithmic traffic (bytes that must cross HBM: weights read once,
+ * KV rows read, activations in and out) and arithmetic (2 flops per
+ * multiply-add) are added up on the host. */
+enum {
+  DEC_NODE_QKV = 0,      /* QKV projection (+ its split-K reduction) */
+  DEC_NODE_ROPE = 1,     /* bias + RoPE + KV append */
+  DEC_NODE_ATTN = 2,     /* attention (+ split merge) */
+  DEC_NODE_O = 3,        /* o_proj + residual */
+  DEC_NODE_GATE_UP = 4,  /* dense gate/up projection with the SwiGLU epilogue */
+  DEC_NODE_DOWN = 5,     /* dense down projection + residual */
+  DEC_NODE_ROUTER = 6,   /* MoE router logits, top-k and grouping */
+  DEC_NODE_EXPERTS = 7,  /* MoE routed + shared experts and the combine */
+  DEC_NODE_HEAD = 8,     /* final norm, lm-head, argmax */
+  DEC_NODE_NORM = 9,     /* RMSNorm launches inside the layers */
+  DEC_NODE_EMBED = 10,   /* embedding gather */
+  DEC_NODE_COUNT = 11
+};
+
+typedef struct {
+  int64_t launches[DEC_NODE_COUNT]; /* kernel launches timed */
+  double ms[DEC_NODE_COUNT];        /* summed kernel time (event to event) */
+  double bytes[DEC_NODE_COUNT];     /* summed algorithmic HBM bytes */
+  double flops[DEC_NODE_COUNT];     /* summed algorithmic flops */
+} decoder_stats_t;
+
+/* node_mask != 0: clear the counters and start timing the nodes whose bit
+ * (1 << DEC_NODE_*) is set (-1: every node); 0: stop timing (counters are
+ * kept for decoder_stats_read).  Timing fewer nodes perturbs the step less. */
+int decoder_stats_enable(decoder_t *dec, int32_t node_mask);
+/* Wait for the decoder's stream, then return the totals since enabling. */
+int decoder_stats_read(decoder_t *dec, decoder_stats_t *out);
 
 #ifdef __cplusplus
 }

@@ -18,8 +18,10 @@ def build_host():
 def build_device():
     src = os.path.join(HERE, "synth_dev.hip")
     out = os.path.join(HERE, "libsynth_dev.so")
-    subprocess.check_call(["hipcc"] + HIP_FLAGS + ["-o", out, src],
-                          stderr=subprocess.DEVNULL if os.environ.get("QUIET_BUILD") else None)
+    res = subprocess.run(["hipcc"] + HIP_FLAGS + ["-o", out, src], capture_output=True, text=True)
+    if res.returncode != 0:
+        msgs = [l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l]
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     return out
 
 

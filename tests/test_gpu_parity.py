@@ -232,3 +232,19 @@ def test_moe_small_parity_and_routes():
         torch.cuda.synchronize()
         r1 = routes.cpu().numpy().reshape(-1)[: shape.n_layers * shape.top_k].reshape(shape.n_layers, shape.top_k)
         assert np.array_equal(r1, want["routes"][:, 0, :])
+
+
+@pytest.mark.parametrize("N,K", [(16, 32), (60, 2048), (100, 688), (777, 4096), (4096, 14336)])
+def test_gemv_kernel_matches_oracle(N, K):
+    from decoder_only_transformer_step_amd.binding import diag_gemv
+    log("gemv", N, K)
+    a = np.random.default_rng(N).normal(size=K).astype(np.float32)
+    W = synth.normal_bf16(N * K, 31 + N, 0.02)
+    dW = torch.from_numpy(W.view(np.int16)).cuda()
+    y = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+    diag_gemv(torch.from_numpy(a).cuda(), dW.view(N, K), y, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    want = oracle.matmul(W, N, K, a.astype(np.float64)[None, :])[0]
+    scale = np.abs(bits_of(W)).reshape(N, K).astype(np.float64) @ np.abs(a).astype(np.float64)
+    assert np.all(np.abs(got - want) <= 1e-6 * np.sqrt(K) * scale + 1e-30)
