@@ -20,7 +20,7 @@ class OrcConfig(ctypes.Structure):
         "hidden", "n_layers", "n_heads", "n_kv_heads", "head_dim", "ffn_inter", "n_experts",
         "top_k", "expert_inter", "shared_inter", "norm_topk_prob", "vocab", "qkv_bias")] + [
         ("rope_base", ctypes.c_double), ("rms_eps", ctypes.c_double),
-        ("max_seq", ctypes.c_int32), ("n_seqs", ctypes.c_int32)]
+        ("max_seq", ctypes.c_int32), ("n_seqs", ctypes.c_int32), ("kv_bf16", ctypes.c_int32)]
 
 
 LAYER_FIELDS = ("attn_norm", "ffn_norm", "w_qkv", "b_qkv", "w_o", "w_gate_up", "w_down",
@@ -45,6 +45,8 @@ def lib():
             _b.build()
         L = ctypes.CDLL(path)
         L.orc_num_threads.restype = _I
+        L.orc_round_bf16.restype = _D
+        L.orc_round_bf16.argtypes = [_D]
         L.orc_rmsnorm.argtypes = [_P, _P, _I, _D, _P]
         L.orc_matmul.argtypes = [_P, _I, _I, _P, _I, _P]
         L.orc_matvec.argtypes = [_P, _I, _I, _P, _P]
@@ -77,6 +79,10 @@ def _f64(x):
 
 def num_threads():
     return lib().orc_num_threads()
+
+
+def round_bf16(v):
+    return lib().orc_round_bf16(float(v))
 
 
 # ------------------------------------------------------------ primitives --
@@ -146,9 +152,11 @@ ERRORS = {1: "context overflow", 2: "invalid argument", 3: "token out of range",
 
 
 class Model:
-    """fp64 reference decoder over host weights from synth.weights.host_weights."""
+    """fp64 reference decoder over host weights from synth.weights.host_weights.
 
-    def __init__(self, shape, weights, n_seqs=1, max_seq=None):
+    kv_bf16 (default: the shape's kv_bf16) stores the KV cache as bf16 values."""
+
+    def __init__(self, shape, weights, n_seqs=1, max_seq=None, kv_bf16=None):
         self.shape = shape
         self._keep = []
         s = shape
@@ -157,7 +165,8 @@ class Model:
                         n_experts=s.n_experts, top_k=s.top_k, expert_inter=s.expert_inter,
                         shared_inter=s.shared_inter, norm_topk_prob=s.norm_topk_prob,
                         vocab=s.vocab, qkv_bias=int(s.qkv_bias), rope_base=s.rope_base,
-                        rms_eps=s.rms_eps, max_seq=max_seq or s.max_seq, n_seqs=n_seqs)
+                        rms_eps=s.rms_eps, max_seq=max_seq or s.max_seq, n_seqs=n_seqs,
+                        kv_bf16=int(s.kv_bf16 if kv_bf16 is None else kv_bf16))
         self.max_seq = cfg.max_seq
         layers = (OrcLayer * s.n_layers)()
         for l in range(s.n_layers):

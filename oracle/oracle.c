@@ -31,6 +31,12 @@
  *                                        over all experts, top-k, optional renorm),
  *                                        lm_head_forward, embed_single.
  *
+ * The KV cache is the one stored quantity whose precision the workloads fix
+ * (a bf16 KV cache; engine.zig keeps its cache in f16): with kv_bf16 set,
+ * keys (after RoPE) and values are rounded to bf16 (round to nearest even)
+ * as they enter the cache, exactly where the method stores them, and every
+ * later read sees the stored value.  All arithmetic stays fp64.
+ *
  * Readings where the pages leave a step open (all listed in the design notes):
  *   RoPE pairs element i with element i + d/2 ("rope", not "ropeAdjacent"),
  *   with inverse frequency base^(-2i/d); GQA maps q head h to kv head
@@ -54,6 +60,7 @@ typedef struct {
   int32_t vocab, qkv_bias;
   double rope_base, rms_eps;
   int32_t max_seq, n_seqs;
+  int32_t kv_bf16;                                 /* 1: the KV cache stores bf16 values */
 } orc_config_t;
 
 typedef struct {
@@ -95,6 +102,18 @@ static inline double bf(uint16_t h) {            /* bf16 -> fp64, exact */
   float f;
   memcpy(&f, &u, 4);
   return (double)f;
+}
+
+/* Round to the nearest bf16 value (8 significant bits), ties to even: the
+ * value is scaled by a power of two so that its 8 significant bits are the
+ * integer part, rounded with nearbyint (round-half-even in the default
+ * rounding mode), and scaled back; both scalings are exact. */
+double orc_round_bf16(double v) {
+  if (v == 0.0 || !isfinite(v)) return v;
+  int e;
+  frexp(v, &e);                                  /* v = m 2^e, 0.5 <= |m| < 1 */
+  double scale = ldexp(1.0, 8 - e);
+  return nearbyint(v * scale) / scale;
 }
 
 int orc_num_threads(void) {
@@ -471,8 +490,11 @@ int orc_forward(orc_model_t *m, int seq, const int32_t *ids, int n, int start_po
       long pos = (long)start_pos + i;
       orc_rope(q, Hq, d, pos, c->rope_base);
       orc_rope(k, Hkv, d, pos, c->rope_base);
-      memcpy(kv_row(m, m->kc, seq, l, (int)pos), k, sizeof(double) * kvd);
-      memcpy(kv_row(m, m->vc, seq, l, (int)pos), v, sizeof(double) * kvd);
+      double *kr = kv_row(m, m->kc, seq, l, (int)pos), *vr = kv_row(m, m->vc, seq, l, (int)pos);
+      for (int j = 0; j < kvd; ++j) {
+        kr[j] = c->kv_bf16 ? orc_round_bf16(k[j]) : k[j];
+        vr[j] = c->kv_bf16 ? orc_round_bf16(v[j]) : v[j];
+      }
     }
 #pragma omp parallel for schedule(dynamic, 1)
     for (int i = 0; i < n; ++i) {

@@ -32,6 +32,7 @@ class Shape:
     max_seq: int = 2048
     max_chunk: int = 128
     max_batch: int = 1
+    kv_bf16: bool = True      # the KV cache stores bf16 values
 
     @property
     def is_moe(self):

@@ -218,8 +218,10 @@ def test_argmax_lowest_index_on_ties():
 # ------------------------------------------------------------ whole model --
 
 def small_shape(**kw):
+    # exact-arithmetic pins use an fp64 KV cache; the bf16 cache has its own test
     base = dict(name="pin", hidden=32, n_layers=2, n_heads=4, n_kv_heads=2, head_dim=8,
-                vocab=64, ffn_inter=48, rope_base=1e4, rms_eps=1e-5, max_seq=32, max_chunk=16)
+                vocab=64, ffn_inter=48, rope_base=1e4, rms_eps=1e-5, max_seq=32, max_chunk=16,
+                kv_bf16=False)
     base.update(kw)
     return Shape(**base)
 
@@ -455,3 +457,44 @@ def test_boundary_errors():
         m.forward([1], 8)
     with pytest.raises(oracle.OracleError, match="invalid"):
         oracle.Model(s, rand_weights(s)).forward([1], 3)   # start_pos must equal the length
+
+
+# ------------------------------------------------------------- bf16 KV --
+
+def test_round_bf16_matches_rne_reference():
+    # exact on fp32 inputs: the result must equal the bit-level fp32 -> bf16
+    # round-to-nearest-even of the generator (a separate implementation)
+    vals = np.random.default_rng(5).normal(size=2000).astype(np.float32) * np.float32(3.7)
+    for v in vals:
+        want = synth.bf16_to_f32(np.array([synth.f32_to_bf16(float(v))], np.uint16))[0]
+        assert oracle.round_bf16(float(v)) == float(want)
+    assert oracle.round_bf16(1.0 + 2 ** -8) == 1.0                 # tie -> even
+    assert oracle.round_bf16(1.0 + 3 * 2 ** -8) == 1.0 + 2 ** -6   # tie -> even (up)
+    assert oracle.round_bf16(-(1.0 + 2 ** -8 + 2 ** -30)) == -(1.0 + 2 ** -7)
+    assert oracle.round_bf16(0.0) == 0.0
+
+
+def test_bf16_kv_cache_rounds_only_the_cache():
+    # with one cached position the attention output is v itself, so x after
+    # the layer carries exactly the bf16 rounding of v (and nothing else)
+    s = small_shape(hidden=4, n_layers=1, n_heads=1, n_kv_heads=1, head_dim=4, vocab=4,
+                    ffn_inter=4, qkv_bias=True)
+    I4 = np.eye(4, dtype=np.float32)
+    bias = np.zeros(12, np.float32)
+    bias[8:12] = [0.5, -1.0, 0.25, 2.0]
+    w_qkv = np.zeros((12, 4), np.float32)
+    w_qkv[8:12] = I4 * np.float32(1.0 + 2 ** -7)     # v = 1.0078125 * a + b_v
+    embed = np.zeros((4, 4), np.float32)
+    embed[0] = [1.0, 0, 0, 0]
+    W = {"embed": bits(embed), "lm_head": bits(I4), "final_norm": np.ones(4, np.float32),
+         "layers": [{"attn_norm": np.ones(4, np.float32), "ffn_norm": np.ones(4, np.float32),
+                     "w_qkv": bits(w_qkv), "b_qkv": bias,
+                     "w_o": bits(I4), "w_gate_up": bits(np.zeros((8, 4), np.float32)),
+                     "w_down": bits(np.zeros((4, 4), np.float32))}]}
+    a0 = 2.0 / math.sqrt(1.0 + 4 * s.rms_eps)         # x = (1,0,0,0): mean(x^2) = 1/4
+    v_exact = np.array([(1 + 2 ** -7) * a0 + 0.5, -1.0, 0.25, 2.0])
+    x_exact = oracle.Model(s, W, kv_bf16=False).forward([0], 0, trace=True)["trace"][1, 0]
+    x_bf = oracle.Model(s, W, kv_bf16=True).forward([0], 0, trace=True)["trace"][1, 0]
+    assert np.allclose(x_exact, np.array([1.0, 0, 0, 0]) + v_exact, atol=1e-15)
+    assert np.allclose(x_bf, np.array([1.0, 0, 0, 0]) + [oracle.round_bf16(t) for t in v_exact], atol=1e-15)
+    assert not np.allclose(x_exact, x_bf, atol=1e-6)
