@@ -69,6 +69,7 @@ SIGNATURES = {
     "dec_diag_gemm": (ctypes.c_int, [_P, _I32, _I32, _P, _I32, _P, _P]),
     "dec_diag_rmsnorm": (ctypes.c_int, [_P, _P, _I32, _I32, ctypes.c_double, _P, _P]),
     "dec_diag_gemv": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _P]),
+    "dec_diag_moe_route": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "decoder_debug_layer_limit": (ctypes.c_int, [_P, _I32]),
     "decoder_debug_read_x": (ctypes.c_int, [_P, _P, _I32]),
     "decoder_debug_read_routes": (ctypes.c_int, [_P, _P, _I32]),
@@ -259,6 +260,12 @@ def diag_gemm(A, W, C, stream):
 def diag_gemv(a, W, y, stream):
     N, K = W.shape
     _check(lib().dec_diag_gemv(_ptr(a), K, _ptr(W), N, _ptr(y), ctypes.c_void_p(stream)), None, "dec_diag_gemv")
+
+
+def diag_moe_route(logits, k, renorm, ids, wts, stream):
+    rows, E = logits.shape
+    _check(lib().dec_diag_moe_route(_ptr(logits), rows, E, k, int(renorm), _ptr(ids), _ptr(wts),
+                                    ctypes.c_void_p(stream)), None, "dec_diag_moe_route")
 
 
 def diag_rmsnorm(x, g, eps, out, stream):

@@ -15,7 +15,8 @@
 //    S^T = K Q^T with 2 d/32 MFMA 16x16x32 (K rows straight from HBM as the
 //    A operand, Q^T in registers as B), an online softmax per column in fp32
 //    (exp2, with log2(e)/sqrt(d) folded into the scale), and O^T += V^T P^T
-//    with d/16 MFMAs.
+//    with d/16 MFMAs.  Q and P enter the MFMAs as split bf16 (hi and lo
+//    products), so only the cache itself is bf16-limited.
 //  * V is stored transposed in the cache ([dim][position]), so the A operand
 //    of the PV product is two 8-byte loads per lane, and the B operand
 //    (P^T) is exactly the lane's own scores: the MFMA k index is mapped to
@@ -47,6 +48,17 @@ __device__ __forceinline__ Col column(const AttnArgs &a, int rg, int g, int c) {
   return k;
 }
 
+__device__ __forceinline__ void store_out(const AttnArgs &a, int64_t i, float v) {
+  if (a.out_f32) {
+    a.out_f32[i] = v;
+  } else {
+    uint32_t hi, lo;
+    split_bf16(v, hi, lo);
+    a.out[i] = (uint16_t)hi;
+    a.out[a.out_lo + i] = (uint16_t)lo;
+  }
+}
+
 // keys of the group: 0 .. max position of its valid columns
 __device__ __forceinline__ int group_keys(const AttnArgs &a, int rg, int g) {
   int kmax = -1;
@@ -74,10 +86,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const uint16_t *kb = a.kcache + (int64_t)seq * a.seq_stride + a.layer_off + (int64_t)g * a.S * D;
   const uint16_t *vb = a.vcache + (int64_t)seq * a.seq_stride + a.layer_off + (int64_t)g * D * a.S;
 
-  u32x4 qf[D / 32];
+  u32x4 qf[D / 32], ql[D / 32];
   const uint16_t *qrow = a.q + ((int64_t)col.row * a.Hq + col.head) * D + quad * 8;
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) qf[ks] = col.valid ? load16(qrow + ks * 32) : u32x4{0u, 0u, 0u, 0u};
+  for (int ks = 0; ks < D / 32; ++ks) {
+    qf[ks] = col.valid ? load16(qrow + ks * 32) : u32x4{0u, 0u, 0u, 0u};
+    ql[ks] = col.valid ? load16(qrow + a.q_lo + ks * 32) : u32x4{0u, 0u, 0u, 0u};
+  }
 
   float m_run = NEG_SENTINEL, l_run = 0.f;
   f32x4 acc[NDT];
@@ -104,7 +119,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
       s0 = mfma16x16x32(as_bf16x8(ka[ks]), as_bf16x8(qf[ks]), s0);
+      s0 = mfma16x16x32(as_bf16x8(ka[ks]), as_bf16x8(ql[ks]), s0);
       s1 = mfma16x16x32(as_bf16x8(kh[ks]), as_bf16x8(qf[ks]), s1);
+      s1 = mfma16x16x32(as_bf16x8(kh[ks]), as_bf16x8(ql[ks]), s1);
     }
     // lane holds S[key = t0 + 4 quad + i][col c] in s0, key + 16 in s1
     float sv[8];
@@ -128,11 +145,11 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    u32x4 pb;
-    pb[0] = pack_bf16x2(p[0], p[1]);
-    pb[1] = pack_bf16x2(p[2], p[3]);
-    pb[2] = pack_bf16x2(p[4], p[5]);
-    pb[3] = pack_bf16x2(p[6], p[7]);
+    u32x4 pb, pl;
+    { const u32pair t_ = pack_split2(p[0], p[1]); pb[0] = t_.hi; pl[0] = t_.lo; }
+    { const u32pair t_ = pack_split2(p[2], p[3]); pb[1] = t_.hi; pl[1] = t_.lo; }
+    { const u32pair t_ = pack_split2(p[4], p[5]); pb[2] = t_.hi; pl[2] = t_.lo; }
+    { const u32pair t_ = pack_split2(p[6], p[7]); pb[3] = t_.hi; pl[3] = t_.lo; }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       acc[dt] *= alpha;
@@ -142,6 +159,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       av[2] = vh[dt][0];
       av[3] = vh[dt][1];
       acc[dt] = mfma16x16x32(as_bf16x8(av), as_bf16x8(pb), acc[dt]);
+      acc[dt] = mfma16x16x32(as_bf16x8(av), as_bf16x8(pl), acc[dt]);
     }
   }
   // acc[dt][i] = O^T[dim = dt*16 + 4 quad + i][col c]; merge the 4 waves
@@ -175,10 +193,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const float inv = 1.0f / L;
     const int64_t ob = ((int64_t)oc.row * a.Hq + oc.head) * D;
 #pragma unroll
-    for (int q = 0; q < NDT; ++q) {
-      if (a.out_f32) a.out_f32[ob + jj + 16 * q] = o[q] * inv;
-      else a.out[ob + jj + 16 * q] = (uint16_t)f32_to_bf16_bits(o[q] * inv);
-    }
+    for (int q = 0; q < NDT; ++q) store_out(a, ob + jj + 16 * q, o[q] * inv);
     return;
   }
   // several splits: publish this block's partial for attn_merge
@@ -215,9 +230,7 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a) {
     L += sc * ml[(int64_t)s * 32 + 1];
     o += sc * po[(int64_t)s * 16 * D];
   }
-  const int64_t oi = ((int64_t)oc.row * a.Hq + oc.head) * D + j;
-  if (a.out_f32) a.out_f32[oi] = o / L;
-  else a.out[oi] = (uint16_t)f32_to_bf16_bits(o / L);
+  store_out(a, ((int64_t)oc.row * a.Hq + oc.head) * D + j, o / L);
 }
 
 }  // namespace

@@ -32,6 +32,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Split-bf16 activations: v ~ hi + lo with hi = bf16(v), lo = bf16(v - hi),
+// about 16 significant bits.  Activations that feed an MFMA are stored as a
+// hi plane and a lo plane (same layout, lo at a fixed element offset) and
+// multiplied twice against the exact bf16 weights; a single bf16 rounding
+// of an activation costs more accuracy than a deep random-weight model can
+// absorb within the logits tolerance.
+__device__ __forceinline__ void split_bf16(float v, uint32_t &hi, uint32_t &lo) {
+  hi = f32_to_bf16_bits(v);
+  lo = f32_to_bf16_bits(v - __uint_as_float(hi << 16));
+}
+struct u32pair {
+  uint32_t hi, lo;
+};
+// two values -> packed hi pair and packed lo pair
+__device__ __forceinline__ u32pair pack_split2(float a, float b) {
+  uint32_t ha, la, hb, lb;
+  split_bf16(a, ha, la);
+  split_bf16(b, hb, lb);
+  return u32pair{ha | (hb << 16), la | (lb << 16)};
+}
+
 __device__ __forceinline__ u32x4 load16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
@@ -87,7 +108,7 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 enum {
   EPI_STORE = 0,     // C[m][n] = acc (+ bias[n])                 fp32
   EPI_ADD = 1,       // C[m][n] += acc                              fp32 (residual stream)
-  EPI_SWIGLU = 2,    // H[m][n] = bf16(silu(acc_gate) * acc_up)    gate rows n, up rows n + N
+  EPI_SWIGLU = 2,    // H[m][n] = split(silu(acc_gate) * acc_up)   gate rows n, up rows n + N
   EPI_QKV = 3,       // bias + RoPE; q -> bf16 buffer, k/v -> KV cache
   EPI_LOGITS = 4,    // C = acc (fp32 logits) and each tile's greedy candidate per row
 };
@@ -96,7 +117,8 @@ struct QkvEpi {
   const float *bias;       // fp32 [qkv rows] or null
   const float2 *cs;        // (cos, sin) [S][d/2]
   const int32_t *row_seq, *row_pos;
-  uint16_t *q;             // bf16 [rows][Hq][d]
+  uint16_t *q;             // split bf16 [rows][Hq][d], lo plane at q + q_lo
+  int64_t q_lo;
   uint16_t *kcache, *vcache;
   int64_t seq_stride, layer_off;
   int32_t S, Hq, Hkv, d;
@@ -109,6 +131,7 @@ struct ArgmaxEpi {
 
 struct GemmArgs {
   const uint16_t *A;      // bf16 activations, row m at A + row(m) * lda
+  int64_t a_lo;           // element offset of A's lo plane (0: A is plain bf16)
   const int32_t *a_rows;  // optional gather: A row of output row m (grouped mode: by pair)
   int64_t lda;
   // fused RMSNorm prologue: when x is set, A = bf16(x * rsqrt(mean(x^2) + eps) * gamma)
@@ -120,7 +143,8 @@ struct GemmArgs {
   int32_t M, N, K;
   int32_t np_off;         // row offset of the second weight tile (SwiGLU: N, QKV: d / 2)
   float *C;               // fp32 output / residual, row m at C + m * ldc
-  uint16_t *Hout;         // bf16 output for EPI_SWIGLU, row m at Hout + m * ldc
+  uint16_t *Hout;         // split bf16 output for EPI_SWIGLU, row m at Hout + m * ldc
+  int64_t h_lo;           // element offset of Hout's lo plane
   int64_t ldc;
   const float *bias;      // optional, EPI_STORE only
   // grouped (MoE) mode: blockIdx.y = group; rows of group g are

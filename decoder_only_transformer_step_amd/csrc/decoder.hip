@@ -78,11 +78,12 @@ Layout make_layout(const decoder_config_t *c) {
   L.vcache = take(kv);
   L.rope = take((size_t)L.S * (d / 2) * sizeof(float2));
   L.x = take((size_t)L.R * H * 4);
-  L.act = take((size_t)L.R * H * 2);
-  L.attn = take((size_t)L.R * qd * 2);
-  L.q = take((size_t)L.R * qd * 2);
+  // split-bf16 activations: hi plane then lo plane
+  L.act = take((size_t)L.R * H * 4);
+  L.attn = take((size_t)L.R * qd * 4);
+  L.q = take((size_t)L.R * qd * 4);
   L.qkv = take((size_t)L.R * qkvr * 4);
-  L.h = take((size_t)L.R * std::max(c->ffn_inter, 1) * 2);
+  L.h = take((size_t)L.R * std::max(c->ffn_inter, 1) * 4);
   L.logits = take((size_t)L.RL * c->vocab * 4);
   L.stage = take((size_t)3 * L.R * 4);
   L.next_token = take((size_t)c->max_batch * 4);
@@ -114,9 +115,9 @@ Layout make_layout(const decoder_config_t *c) {
     L.groups = take((size_t)(1 + 3 * E) * 4);
     L.pair_row = take((size_t)P * 4);
     L.pair_of = take((size_t)P * 4);
-    L.hexp = take((size_t)P * c->expert_inter * 2);
+    L.hexp = take((size_t)P * c->expert_inter * 4);
     L.yexp = take((size_t)P * H * 4);
-    L.hsh = take((size_t)L.R * std::max(c->shared_inter, 1) * 2);
+    L.hsh = take((size_t)L.R * std::max(c->shared_inter, 1) * 4);
     L.ysh = take((size_t)L.R * H * 4);
   }
   L.total = off;
@@ -141,6 +142,7 @@ struct decoder {
   int32_t *counters, *am_idx, *am_out;
   float *f32_attn, *f32_h, *f32_act, *f32_hexp;
   bool single_row_ok = false;  // the batch-1 GEMV path fits every K of this config
+  int64_t act_lo = 0, attn_lo = 0, q_lo = 0, h_lo = 0, hexp_lo = 0, hsh_lo = 0;  // lo-plane offsets
   // host state
   std::vector<int32_t> len;
   std::vector<char> has_next;
@@ -292,10 +294,11 @@ int norm_into(decoder *D, GemmArgs &g, const float *x, const float *gamma, int r
   hipError_t e;
   {
     NodeTimer t(D, DEC_NODE_NORM, rows * (double)H * 6 + H * 4.0, rows * (double)H * 4);
-    e = launch_rmsnorm(x, H, gamma, rows, H, (float)D->c.rms_eps, D->act, H, D->stream);
+    e = launch_rmsnorm(x, H, gamma, rows, H, (float)D->c.rms_eps, D->act, H, D->act_lo, D->stream);
   }
   if (e != hipSuccess) return hip_fail(D, e, "rmsnorm");
   g.A = D->act;
+  g.a_lo = D->act_lo;
   g.lda = H;
   return DEC_OK;
 }
@@ -314,7 +317,9 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
                   qk * c.n_heads * c.head_dim * 4.0);
   AttnArgs a{};
   a.q = D->q;
+  a.q_lo = D->q_lo;
   a.out = out_f32 ? nullptr : D->attn;
+  a.out_lo = D->attn_lo;
   a.out_f32 = out_f32;
   a.kcache = D->kcache;
   a.vcache = D->vcache;
@@ -388,6 +393,7 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
   q.qkv.row_seq = D->row_seq;
   q.qkv.row_pos = D->row_pos;
   q.qkv.q = D->q;
+  q.qkv.q_lo = D->q_lo;
   q.qkv.kcache = D->kcache;
   q.qkv.vcache = D->vcache;
   q.qkv.seq_stride = D->L.seq_stride;
@@ -411,7 +417,7 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
   const int E = c.n_experts, k = c.top_k, Ie = c.expert_inter, Is = c.shared_inter;
   {
     NodeTimer t(D, DEC_NODE_NORM, H * 12.0, H * 4.0);
-    e = launch_rmsnorm(D->x, H, W.ffn_norm, 1, H, eps, nullptr, H, D->stream, D->f32_act);
+    e = launch_rmsnorm(D->x, H, W.ffn_norm, 1, H, eps, nullptr, H, 0, D->stream, D->f32_act);
   }
   if (e != hipSuccess) return hip_fail(D, e, "rmsnorm");
   if ((rc = gemv(D, DEC_NODE_ROUTER, EPI_STORE, gemv_args(W.w_router, D->f32_act, H, E, D->rlogits)))) return rc;
@@ -475,6 +481,7 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   q.qkv.row_seq = D->row_seq;
   q.qkv.row_pos = D->row_pos;
   q.qkv.q = D->q;
+  q.qkv.q_lo = D->q_lo;
   q.qkv.kcache = D->kcache;
   q.qkv.vcache = D->vcache;
   q.qkv.seq_stride = D->L.seq_stride;
@@ -486,6 +493,7 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   if ((rc = proj(D, DEC_NODE_QKV, EPI_QKV, q, rows))) return rc;
   if ((rc = attention(D, l, rows, rows_per_group, max_pos, hpos))) return rc;
   GemmArgs o = dense_args(D->attn, qd, W.w_o, rows, H, qd);
+  o.a_lo = D->attn_lo;
   o.C = D->x;
   o.ldc = H;
   if ((rc = proj(D, DEC_NODE_O, EPI_ADD, o, rows))) return rc;
@@ -495,9 +503,11 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
     GemmArgs gu = dense_args(nullptr, H, W.w_gate_up, rows, I, H);
     if ((rc = norm_into(D, gu, D->x, W.ffn_norm, rows))) return rc;
     gu.Hout = D->h;
+    gu.h_lo = D->h_lo;
     gu.ldc = I;
     if ((rc = proj(D, DEC_NODE_GATE_UP, EPI_SWIGLU, gu, rows))) return rc;
     GemmArgs dn = dense_args(D->h, I, W.w_down, rows, H, I);
+    dn.a_lo = D->h_lo;
     dn.C = D->x;
     dn.ldc = H;
     return proj(D, DEC_NODE_DOWN, EPI_ADD, dn, rows);
@@ -507,17 +517,19 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   // experts all read the same normed input b (bf16 in D->act)
   {
     NodeTimer t(D, DEC_NODE_NORM, rows * (double)H * 6 + H * 4.0, rows * (double)H * 4);
-    e = launch_rmsnorm(D->x, H, W.ffn_norm, rows, H, (float)c.rms_eps, D->act, H, st);
+    e = launch_rmsnorm(D->x, H, W.ffn_norm, rows, H, (float)c.rms_eps, D->act, H, D->act_lo, st);
   }
   if (e != hipSuccess) return hip_fail(D, e, "rmsnorm");
   const int E = c.n_experts, k = c.top_k, Ie = c.expert_inter, Is = c.shared_inter;
   GemmArgs r = dense_args(D->act, H, W.w_router, rows, E, H);
+  r.a_lo = D->act_lo;
   r.C = D->rlogits;
   r.ldc = E;
   if ((rc = proj(D, DEC_NODE_ROUTER, EPI_STORE, r, rows))) return rc;
   MoeRouteArgs mr{};
   mr.logits = D->rlogits;
   mr.act = D->act;
+  mr.act_lo = D->act_lo;
   mr.w_sh_gate = (Is > 0 && c.shared_gate) ? W.w_sh_gate : nullptr;
   mr.rows = rows;
   mr.E = E;
@@ -543,9 +555,11 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   const int grp_rows = std::min(rows, 32);
   const double exp_bytes = (double)slots * 3.0 * Ie * H * 2;
   GemmArgs g = dense_args(D->act, H, W.w_exp_gate_up, rows * k, Ie, H);
+  g.a_lo = D->act_lo;
   g.a_rows = D->pair_row;
   g.w_group_stride = (int64_t)2 * Ie * H;
   g.Hout = D->hexp;
+  g.h_lo = D->hexp_lo;
   g.ldc = Ie;
   g.n_groups = mr.n_groups;
   g.group_expert = mr.group_expert;
@@ -559,6 +573,7 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   }
   if (e != hipSuccess) return hip_fail(D, e, "moe gate_up");
   g.A = D->hexp;
+  g.a_lo = D->hexp_lo;
   g.a_rows = nullptr;
   g.lda = Ie;
   g.W = W.w_exp_down;
@@ -577,10 +592,13 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   if (e != hipSuccess) return hip_fail(D, e, "moe down");
   if (Is > 0) {
     GemmArgs sg = dense_args(D->act, H, W.w_sh_gate_up, rows, Is, H);
+    sg.a_lo = D->act_lo;
     sg.Hout = D->hsh;
+    sg.h_lo = D->hsh_lo;
     sg.ldc = Is;
     if ((rc = proj(D, DEC_NODE_EXPERTS, EPI_SWIGLU, sg, rows))) return rc;
     GemmArgs sd = dense_args(D->hsh, Is, W.w_sh_down, rows, H, Is);
+    sd.a_lo = D->hsh_lo;
     sd.C = D->ysh;
     sd.ldc = H;
     if ((rc = proj(D, DEC_NODE_EXPERTS, EPI_STORE, sd, rows))) return rc;
@@ -723,6 +741,11 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
   D->am_val = carve<float>(D, L.am_val);
   D->am_idx = carve<int32_t>(D, L.am_idx);
   D->am_out = carve<int32_t>(D, L.am_out);
+  D->act_lo = (int64_t)L.R * cfg->hidden;
+  D->attn_lo = D->q_lo = (int64_t)L.R * cfg->n_heads * cfg->head_dim;
+  D->h_lo = (int64_t)L.R * std::max(cfg->ffn_inter, 1);
+  D->hexp_lo = (int64_t)L.R * std::max(cfg->top_k, 1) * std::max(cfg->expert_inter, 1);
+  D->hsh_lo = (int64_t)L.R * std::max(cfg->shared_inter, 1);
   D->f32_attn = carve<float>(D, L.f32_attn);
   D->f32_h = carve<float>(D, L.f32_h);
   D->f32_act = carve<float>(D, L.f32_act);
@@ -934,10 +957,25 @@ int dec_diag_gemv(const float *d_a, int32_t K, const uint16_t *d_W, int32_t N, f
   return launch_gemv(g, EPI_STORE, (hipStream_t)stream) == hipSuccess ? DEC_OK : DEC_E_HIP;
 }
 
+int dec_diag_moe_route(const float *d_logits, int32_t rows, int32_t E, int32_t k, int32_t renorm,
+                       int32_t *d_ids, float *d_wts, void *stream) {
+  if (!d_logits || !d_ids || !d_wts || rows < 1 || E < 1 || E > 256 || k < 1 || k > 8 || k > E)
+    return DEC_E_INVALID;
+  MoeRouteArgs mr{};
+  mr.logits = d_logits;
+  mr.rows = rows;
+  mr.E = E;
+  mr.k = k;
+  mr.renorm = renorm;
+  mr.ids = d_ids;
+  mr.wts = d_wts;
+  return launch_moe_route(mr, false, (hipStream_t)stream) == hipSuccess ? DEC_OK : DEC_E_HIP;
+}
+
 int dec_diag_rmsnorm(const float *d_x, const float *d_g, int32_t rows, int32_t H, double eps, uint16_t *d_out,
                      void *stream) {
   if (!d_x || !d_g || !d_out || rows < 1 || H < 4 || H % 4) return DEC_E_INVALID;
-  return launch_rmsnorm(d_x, H, d_g, rows, H, (float)eps, d_out, H, (hipStream_t)stream) == hipSuccess
+  return launch_rmsnorm(d_x, H, d_g, rows, H, (float)eps, d_out, H, 0, (hipStream_t)stream) == hipSuccess
              ? DEC_OK
              : DEC_E_HIP;
 }

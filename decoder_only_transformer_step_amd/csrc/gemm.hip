@@ -57,7 +57,10 @@ __device__ __forceinline__ void epi_apply(const GemmArgs &g, int64_t orow, int n
   } else if (EPI == EPI_ADD) {
     g.C[orow * g.ldc + n] += v0;
   } else if (EPI == EPI_SWIGLU) {
-    g.Hout[orow * g.ldc + n] = (uint16_t)f32_to_bf16_bits(silu_f(v0) * v1);
+    uint32_t hi, lo;
+    split_bf16(silu_f(v0) * v1, hi, lo);
+    g.Hout[orow * g.ldc + n] = (uint16_t)hi;
+    g.Hout[g.h_lo + orow * g.ldc + n] = (uint16_t)lo;
   } else if (EPI == EPI_LOGITS) {
     g.C[orow * g.ldc + n] = v0;
   } else if (EPI == EPI_QKV) {
@@ -79,11 +82,20 @@ __device__ __forceinline__ void epi_apply(const GemmArgs &g, int64_t orow, int n
       const float2 t = q.cs[(int64_t)pos * half + i];
       const float r0 = u0 * t.x - u1 * t.y;
       const float r1 = u0 * t.y + u1 * t.x;
-      uint16_t *dst;
-      if (hh < q.Hq) dst = q.q + (orow * q.Hq + hh) * d;
-      else dst = q.kcache + base + ((int64_t)(hh - q.Hq) * q.S + pos) * d;
-      dst[i] = (uint16_t)f32_to_bf16_bits(r0);
-      dst[i + half] = (uint16_t)f32_to_bf16_bits(r1);
+      if (hh < q.Hq) {
+        uint16_t *dst = q.q + (orow * q.Hq + hh) * d;
+        uint32_t h0, l0, h1, l1;
+        split_bf16(r0, h0, l0);
+        split_bf16(r1, h1, l1);
+        dst[i] = (uint16_t)h0;
+        dst[i + half] = (uint16_t)h1;
+        dst[q.q_lo + i] = (uint16_t)l0;
+        dst[q.q_lo + i + half] = (uint16_t)l1;
+      } else {
+        uint16_t *dst = q.kcache + base + ((int64_t)(hh - q.Hq) * q.S + pos) * d;
+        dst[i] = (uint16_t)f32_to_bf16_bits(r0);
+        dst[i + half] = (uint16_t)f32_to_bf16_bits(r1);
+      }
     } else {
       uint16_t *vt = q.vcache + base + (int64_t)(hh - q.Hq - q.Hkv) * d * q.S;
       vt[(int64_t)i * q.S + pos] = (uint16_t)f32_to_bf16_bits(u0);
@@ -93,11 +105,12 @@ __device__ __forceinline__ void epi_apply(const GemmArgs &g, int64_t orow, int n
 }
 
 // Accumulate this wave's share of the block tile.  AMODE 0: A from global;
-// AMODE 2: A from the normalised bf16 copy in LDS (row m at a_lds + m * K).
-template <int MT, int NP, int U, int NW, int AMODE>
+// AMODE 2: A from the normalised copy in LDS (row m at a_lds + m * K, lo
+// plane at a_lo).  SPLIT: A carries a lo plane, multiplied as well.
+template <int MT, int NP, int U, int NW, int AMODE, bool SPLIT>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const uint16_t *W, const uint16_t *a_lds,
-                                          int row0, int rows, int mp, int n0, bool nvalid, int s0,
-                                          int s1, f32x4 (&acc)[MT][NP]) {
+                                          int64_t a_lo, int row0, int rows, int mp, int n0, bool nvalid,
+                                          int s0, int s1, f32x4 (&acc)[MT][NP]) {
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = threadIdx.x / WAVE;
   const int c = lane & 15, quad = lane >> 4;
@@ -124,9 +137,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const uint16_t *W, 
 #pragma unroll
     for (int p = 0; p < NP; ++p) acc[t][p] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  constexpr int NS = SPLIT ? 2 : 1;
   for (int st = s0 + wave; st < s1; st += NW * U) {
     u32x4 wf[U][NP];
-    u32x4 af[U][MT];
+    u32x4 af[U][MT][NS];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int step = st + u * NW;
@@ -137,7 +151,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const uint16_t *W, 
         wf[u][p] = (kv && nvalid) ? load16(wrow[p] + k) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int t = 0; t < MT; ++t)
-        af[u][t] = (kv && mvalid[t]) ? load16(arow[t] + k) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp)
+          af[u][t][sp] = (kv && mvalid[t]) ? load16(arow[t] + sp * a_lo + k) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -145,11 +161,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const uint16_t *W, 
       for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int p = 0; p < NP; ++p)
-          acc[t][p] = mfma16x16x32(as_bf16x8(af[u][t]), as_bf16x8(wf[u][p]), acc[t][p]);
+#pragma unroll
+          for (int sp = 0; sp < NS; ++sp)
+            acc[t][p] = mfma16x16x32(as_bf16x8(af[u][t][sp]), as_bf16x8(wf[u][p]), acc[t][p]);
   }
 }
 
-template <int MT, int EPI, int U, int NW, int AMODE>
+template <int MT, int EPI, int U, int NW, int AMODE, bool SPLIT>
 __global__ __launch_bounds__(NW * WAVE) void gemm_kernel(GemmArgs g) {
   constexpr int NP = paired<EPI>();
   __shared__ f32x4 red[NW][NP][WAVE];
@@ -201,19 +219,21 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_kernel(GemmArgs g) {
       const f32x4 x0 = loadf4(xr), x1 = loadf4(xr + 4);
       const f32x4 g0 = loadf4(g.gamma + k), g1 = loadf4(g.gamma + k + 4);
       const float iv = inv_s[m];
-      u32x4 o;
-      o[0] = pack_bf16x2(x0[0] * iv * g0[0], x0[1] * iv * g0[1]);
-      o[1] = pack_bf16x2(x0[2] * iv * g0[2], x0[3] * iv * g0[3]);
-      o[2] = pack_bf16x2(x1[0] * iv * g1[0], x1[1] * iv * g1[1]);
-      o[3] = pack_bf16x2(x1[2] * iv * g1[2], x1[3] * iv * g1[3]);
-      *reinterpret_cast<u32x4 *>(a_lds + (int64_t)m * K + k) = o;
+      u32x4 oh, ol;
+      { const u32pair t_ = pack_split2(x0[0] * iv * g0[0], x0[1] * iv * g0[1]); oh[0] = t_.hi; ol[0] = t_.lo; }
+      { const u32pair t_ = pack_split2(x0[2] * iv * g0[2], x0[3] * iv * g0[3]); oh[1] = t_.hi; ol[1] = t_.lo; }
+      { const u32pair t_ = pack_split2(x1[0] * iv * g1[0], x1[1] * iv * g1[1]); oh[2] = t_.hi; ol[2] = t_.lo; }
+      { const u32pair t_ = pack_split2(x1[2] * iv * g1[2], x1[3] * iv * g1[3]); oh[3] = t_.hi; ol[3] = t_.lo; }
+      *reinterpret_cast<u32x4 *>(a_lds + (int64_t)m * K + k) = oh;
+      *reinterpret_cast<u32x4 *>(a_lds + (int64_t)(rows + m) * K + k) = ol;
     }
     __syncthreads();
   }
 
   for (int mp = 0; mp < rows; mp += 16 * MT) {
     f32x4 acc[MT][NP];
-    gemm_tile<MT, NP, U, NW, AMODE>(g, W, a_lds, row0, rows, mp, n0, nvalid, s0, s1, acc);
+    const int64_t a_lo = AMODE == 2 ? (int64_t)rows * g.K : g.a_lo;
+    gemm_tile<MT, NP, U, NW, AMODE, SPLIT>(g, W, a_lds, a_lo, row0, rows, mp, n0, nvalid, s0, s1, acc);
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
 #pragma unroll
@@ -293,22 +313,32 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g, int ntiles
   }
 }
 
-template <int MT, int EPI, int NW, int AMODE>
+// U: weight steps per load batch, so that a batch holds about 16 fragments
+template <int MT, int EPI, int NW, int AMODE, bool SPLIT>
 hipError_t launch_cfg(const GemmArgs &g, dim3 grid, size_t dyn, hipStream_t st) {
   constexpr int NP = paired<EPI>();
-  constexpr int U = (MT + NP) <= 3 ? 8 : ((MT + NP) <= 6 ? 4 : 2);
-  hipLaunchKernelGGL((gemm_kernel<MT, EPI, U, NW, AMODE>), grid, dim3(NW * WAVE), dyn, st, g);
+  constexpr int F = MT * (SPLIT ? 2 : 1) + NP;
+  constexpr int U = F <= 4 ? 4 : (F <= 8 ? 2 : 1);
+  hipLaunchKernelGGL((gemm_kernel<MT, EPI, U, NW, AMODE, SPLIT>), grid, dim3(NW * WAVE), dyn, st, g);
   return hipGetLastError();
 }
 
 template <int EPI>
 hipError_t launch_epi(const GemmArgs &g, int mt, bool norm, dim3 grid, size_t dyn, hipStream_t st) {
-  if (norm) return launch_cfg<1, EPI, 8, 2>(g, grid, dyn, st);
+  if (norm) return launch_cfg<1, EPI, 8, 2, true>(g, grid, dyn, st);
+  if (!g.a_lo) {
+    switch (mt) {
+      case 1: return launch_cfg<1, EPI, 8, 0, false>(g, grid, 0, st);
+      case 2: return launch_cfg<2, EPI, 4, 0, false>(g, grid, 0, st);
+      case 4: return launch_cfg<4, EPI, 4, 0, false>(g, grid, 0, st);
+      default: return launch_cfg<8, EPI, 4, 0, false>(g, grid, 0, st);
+    }
+  }
   switch (mt) {
-    case 1: return launch_cfg<1, EPI, 8, 0>(g, grid, 0, st);
-    case 2: return launch_cfg<2, EPI, 4, 0>(g, grid, 0, st);
-    case 4: return launch_cfg<4, EPI, 4, 0>(g, grid, 0, st);
-    default: return launch_cfg<8, EPI, 4, 0>(g, grid, 0, st);
+    case 1: return launch_cfg<1, EPI, 8, 0, true>(g, grid, 0, st);
+    case 2: return launch_cfg<2, EPI, 4, 0, true>(g, grid, 0, st);
+    case 4: return launch_cfg<4, EPI, 4, 0, true>(g, grid, 0, st);
+    default: return launch_cfg<8, EPI, 4, 0, true>(g, grid, 0, st);
   }
 }
 
@@ -326,13 +356,13 @@ int gemm_ntiles(const GemmArgs &g, int epi) {
   return (g.N + 15) / 16;
 }
 
-bool gemm_norm_fits(int rows, int K) { return rows <= GEMM_NORM_MAX_ROWS && (size_t)rows * K * 2 <= GEMM_NORM_MAX_LDS; }
+bool gemm_norm_fits(int rows, int K) { return rows <= GEMM_NORM_MAX_ROWS && (size_t)rows * K * 4 <= GEMM_NORM_MAX_LDS; }
 
 hipError_t launch_gemm(const GemmArgs &g, int epi, int max_rows, int n_group_slots, hipStream_t st) {
   const int ntiles = gemm_ntiles(g, epi);
   const bool norm = g.x != nullptr;
   const int mt = gemm_mtiles(max_rows);
-  const size_t dyn = norm ? (size_t)g.M * g.K * 2 : 0;
+  const size_t dyn = norm ? (size_t)g.M * g.K * 4 : 0;  // hi and lo planes
   dim3 grid(ntiles, g.n_groups ? n_group_slots : 1, g.ksplit > 1 ? g.ksplit : 1);
   hipError_t e;
   switch (epi) {

@@ -18,7 +18,9 @@
 //  * Software pipeline: the first batch of weight loads is issued before the
 //    activation prologue, and each later batch while the previous one is
 //    consumed, so every wave keeps several kilobytes in flight at all times.
-//    A wave may own two items at once (IPW) when there are many of them.
+//  * Persistent grid (about two blocks per compute unit): the activation
+//    prologue runs once per block, and each wave streams its items back to
+//    back, the next item's first loads overlapping the current reduction.
 //  * Grouped mode (MoE experts): blockIdx.y = routing slot; the weight base
 //    moves to the chosen expert.
 #include "common.h"
@@ -92,10 +94,79 @@ __device__ __forceinline__ void fma_batch(float (&acc)[R], const u32x4 (&v)[UNR]
   }
 }
 
-template <int EPI, int IPW, int UNR>
+// Rows of item `it` and their weight pointers (lane offset included).
+template <int EPI, int NR>
+__device__ __forceinline__ void item_ptrs(const GemvArgs &g, const uint16_t *W, int it, int lane,
+                                          int (&rows)[NR], const uint16_t *(&wp)[NR], bool (&rv)[NR]) {
+  int r0 = 0, r1 = 0;
+  const bool ok = it < g.n_items;
+  if (ok) item_rows<EPI>(g, it, r0, r1);
+  rows[0] = r0;
+  rows[NR - 1] = r1;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    rv[r] = ok;
+    wp[r] = W + (int64_t)rows[r] * g.K + lane * 8;
+  }
+}
+
+// Epilogue of one item (lane 0 writes).
+template <int EPI>
+__device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, int r0, int r1, float v0, float v1) {
+  if (EPI == EPI_STORE) {
+    g.C[(int64_t)out_row * g.ldc + r0] = v0 + (g.bias ? g.bias[r0] : 0.f);
+  } else if (EPI == EPI_ADD) {
+    g.C[r0] += v0;
+  } else if (EPI == EPI_SWIGLU) {
+    g.C[(int64_t)out_row * g.ldc + r0] = silu_f(v0) * v1;
+  } else if (EPI == EPI_LOGITS) {
+    g.C[r0] = v0;
+  } else if (EPI == EPI_QKV) {
+    // bias, then RoPE on q and k rows, then the KV-cache append
+    // (engine.zig ropeAndCache, "rope" pairing u_i with u_{i+d/2};
+    // decoder.rs AttnWeights: bias before RoPE)
+    const QkvEpi &q = g.qkv;
+    const int d = q.d, half = d / 2;
+    const int hh = r0 / d, i = r0 - hh * d;
+    float u0 = v0, u1 = v1;
+    if (q.bias) {
+      u0 += q.bias[r0];
+      u1 += q.bias[r1];
+    }
+    const int pos = q.row_pos[0], seq = q.row_seq[0];
+    const int64_t base = (int64_t)seq * q.seq_stride + q.layer_off;
+    if (hh < q.Hq + q.Hkv) {
+      const float2 t = q.cs[(int64_t)pos * half + i];
+      const float a0 = u0 * t.x - u1 * t.y, a1 = u0 * t.y + u1 * t.x;
+      if (hh < q.Hq) {
+        uint16_t *dst = q.q + (int64_t)hh * d;
+        uint32_t h0, l0, h1, l1;
+        split_bf16(a0, h0, l0);
+        split_bf16(a1, h1, l1);
+        dst[i] = (uint16_t)h0;
+        dst[i + half] = (uint16_t)h1;
+        dst[q.q_lo + i] = (uint16_t)l0;
+        dst[q.q_lo + i + half] = (uint16_t)l1;
+      } else {
+        uint16_t *dst = q.kcache + base + ((int64_t)(hh - q.Hq) * q.S + pos) * d;
+        dst[i] = (uint16_t)f32_to_bf16_bits(a0);
+        dst[i + half] = (uint16_t)f32_to_bf16_bits(a1);
+      }
+    } else {
+      uint16_t *vt = q.vcache + base + (int64_t)(hh - q.Hq - q.Hkv) * d * q.S;
+      vt[(int64_t)i * q.S + pos] = (uint16_t)f32_to_bf16_bits(u0);
+      vt[(int64_t)(i + half) * q.S + pos] = (uint16_t)f32_to_bf16_bits(u1);
+    }
+  }
+}
+
+// Persistent grid: each wave walks the items it, it + stride, ... as one
+// sequence of UNR-step load batches, ping-ponging between two register
+// buffers, so the first batch of the next item is already in flight while
+// the current item is reduced and written.
+template <int EPI, int UNR>
 __global__ __launch_bounds__(GV_WAVES * WAVE) void gemv_kernel(GemvArgs g) {
   constexpr int NR = gv_rows<EPI>();
-  constexpr int R = NR * IPW;  // weight rows this wave streams at once
   extern __shared__ float xs[];
   __shared__ float sred[GV_WAVES];
   __shared__ float bv_s[GV_WAVES];
@@ -112,29 +183,20 @@ __global__ __launch_bounds__(GV_WAVES * WAVE) void gemv_kernel(GemvArgs g) {
   }
   const int K = g.K;
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-  const int it0 = (blockIdx.x * GV_WAVES + wave) * IPW;
-  int rows_[R];
-  bool rv[R];
-  const uint16_t *wp[R];
-#pragma unroll
-  for (int j = 0; j < IPW; ++j) {
-    int r0 = 0, r1 = 0;
-    const bool ok = it0 + j < g.n_items;
-    if (ok) item_rows<EPI>(g, it0 + j, r0, r1);
-    rows_[j * NR] = r0;
-    rv[j * NR] = ok;
-    if (NR == 2) {
-      rows_[j * NR + NR - 1] = r1;
-      rv[j * NR + NR - 1] = ok;
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < R; ++r) wp[r] = W + (int64_t)rows_[r] * K + lane * 8;
+  const int stride = gridDim.x * GV_WAVES;
   const int steps = (K + 511) / 512;
+  const int nb = (steps + UNR - 1) / UNR;  // batches per item
 
+  // batch sequence position of the next load: item `li`, batch `lb`
+  int li = blockIdx.x * GV_WAVES + wave, lb = 0;
+  int lrows[NR];
+  const uint16_t *lwp[NR];
+  bool lrv[NR];
+  item_ptrs<EPI, NR>(g, W, li, lane, lrows, lwp, lrv);
+
+  u32x4 buf0[UNR][NR], buf1[UNR][NR];
   // the first weight loads go out before the activation prologue
-  u32x4 cur[UNR][R];
-  load_batch<R, UNR>(cur, wp, rv, 0, steps, K, lane);
+  load_batch<NR, UNR>(buf0, lwp, lrv, 0, steps, K, lane);
 
   // activation -> LDS (fp32), with the RMSNorm prologue when gamma is set
   if (g.gamma) {
@@ -161,69 +223,54 @@ __global__ __launch_bounds__(GV_WAVES * WAVE) void gemv_kernel(GemvArgs g) {
   }
   __syncthreads();
 
-  float acc[R];
+  // consumption state: item `ci` (rows crows), batch `cb`
+  int ci = li, cb = 0;
+  int crows[NR];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.f;
-  // ping-pong between two load batches: while one is consumed the other is
-  // in flight (no register copies, so no full wait per iteration)
-  u32x4 alt[UNR][R];
-  for (int s0 = 0; s0 < steps; s0 += 2 * UNR) {
-    if (s0 + UNR < steps) load_batch<R, UNR>(alt, wp, rv, s0 + UNR, steps, K, lane);
-    fma_batch<R, UNR>(acc, cur, xs, s0, steps, K, lane);
-    if (s0 + UNR >= steps) break;
-    if (s0 + 2 * UNR < steps) load_batch<R, UNR>(cur, wp, rv, s0 + 2 * UNR, steps, K, lane);
-    fma_batch<R, UNR>(acc, alt, xs, s0 + UNR, steps, K, lane);
-  }
+  for (int r = 0; r < NR; ++r) crows[r] = lrows[r];
+  float acc[NR];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
-
+  for (int r = 0; r < NR; ++r) acc[r] = 0.f;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
+
+  // advance the load position by one batch and issue it into `dst`
+  auto issue_next = [&](u32x4 (&dst)[UNR][NR]) {
+    if (++lb == nb) {
+      lb = 0;
+      li += stride;
+      item_ptrs<EPI, NR>(g, W, li, lane, lrows, lwp, lrv);
+    }
+    if (li < g.n_items) load_batch<NR, UNR>(dst, lwp, lrv, lb * UNR, steps, K, lane);
+  };
+  // consume `src` as batch cb of item ci; finish the item on its last batch
+  auto consume = [&](const u32x4 (&src)[UNR][NR]) {
+    fma_batch<NR, UNR>(acc, src, xs, cb * UNR, steps, K, lane);
+    if (++cb == nb) {
 #pragma unroll
-  for (int j = 0; j < IPW; ++j) {
-    if (!rv[j * NR]) continue;
-    const int r0 = rows_[j * NR], r1 = rows_[j * NR + NR - 1];
-    const float v0 = acc[j * NR], v1 = acc[j * NR + NR - 1];
-    if (EPI == EPI_LOGITS && better(v0, r0, bv, bi)) {
-      bv = v0;
-      bi = r0;
-    }
-    if (lane != 0) continue;
-    if (EPI == EPI_STORE) {
-      g.C[(int64_t)out_row * g.ldc + r0] = v0 + (g.bias ? g.bias[r0] : 0.f);
-    } else if (EPI == EPI_ADD) {
-      g.C[r0] += v0;
-    } else if (EPI == EPI_SWIGLU) {
-      g.C[(int64_t)out_row * g.ldc + r0] = silu_f(v0) * v1;
-    } else if (EPI == EPI_LOGITS) {
-      g.C[r0] = v0;
-    } else if (EPI == EPI_QKV) {
-      // bias, then RoPE on q and k rows, then the KV-cache append
-      // (engine.zig ropeAndCache, "rope" pairing u_i with u_{i+d/2};
-      // decoder.rs AttnWeights: bias before RoPE)
-      const QkvEpi &q = g.qkv;
-      const int d = q.d, half = d / 2;
-      const int hh = r0 / d, i = r0 - hh * d;
-      float u0 = v0, u1 = v1;
-      if (q.bias) {
-        u0 += q.bias[r0];
-        u1 += q.bias[r1];
+      for (int r = 0; r < NR; ++r) acc[r] = wave_sum(acc[r]);
+      if (EPI == EPI_LOGITS && better(acc[0], crows[0], bv, bi)) {
+        bv = acc[0];
+        bi = crows[0];
       }
-      const int pos = q.row_pos[0], seq = q.row_seq[0];
-      const int64_t base = (int64_t)seq * q.seq_stride + q.layer_off;
-      if (hh < q.Hq + q.Hkv) {
-        const float2 t = q.cs[(int64_t)pos * half + i];
-        const float a0 = u0 * t.x - u1 * t.y, a1 = u0 * t.y + u1 * t.x;
-        uint16_t *dst = hh < q.Hq ? q.q + (int64_t)hh * d : q.kcache + base + ((int64_t)(hh - q.Hq) * q.S + pos) * d;
-        dst[i] = (uint16_t)f32_to_bf16_bits(a0);
-        dst[i + half] = (uint16_t)f32_to_bf16_bits(a1);
-      } else {
-        uint16_t *vt = q.vcache + base + (int64_t)(hh - q.Hq - q.Hkv) * d * q.S;
-        vt[(int64_t)i * q.S + pos] = (uint16_t)f32_to_bf16_bits(u0);
-        vt[(int64_t)(i + half) * q.S + pos] = (uint16_t)f32_to_bf16_bits(u1);
-      }
+      if (lane == 0) item_epilogue<EPI>(g, out_row, crows[0], crows[NR - 1], acc[0], acc[NR - 1]);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r] = 0.f;
+      cb = 0;
+      ci += stride;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) crows[r] = lrows[r];  // the load position is already on item ci
     }
+  };
+
+  while (ci < g.n_items) {
+    issue_next(buf1);
+    consume(buf0);
+    if (ci >= g.n_items) break;
+    issue_next(buf0);
+    consume(buf1);
   }
+
   if (EPI == EPI_LOGITS) {
     // this block's best (value, index), for the argmax finalize pass
     if (lane == 0) {
@@ -244,32 +291,38 @@ __global__ __launch_bounds__(GV_WAVES * WAVE) void gemv_kernel(GemvArgs g) {
 }
 
 template <int EPI>
-hipError_t launch_e(const GemvArgs &g, int ipw, dim3 grid, size_t lds, hipStream_t st) {
-  constexpr int UP = DEC_GEMV_UNR_PAIRED, US = DEC_GEMV_UNR_SINGLE;
-  if (ipw == 2) hipLaunchKernelGGL((gemv_kernel<EPI, 2, UP>), grid, dim3(GV_WAVES * WAVE), lds, st, g);
-  else if (gv_rows<EPI>() == 2) hipLaunchKernelGGL((gemv_kernel<EPI, 1, UP>), grid, dim3(GV_WAVES * WAVE), lds, st, g);
-  else hipLaunchKernelGGL((gemv_kernel<EPI, 1, US>), grid, dim3(GV_WAVES * WAVE), lds, st, g);
+hipError_t launch_e(const GemvArgs &g, dim3 grid, size_t lds, hipStream_t st) {
+  constexpr int U = gv_rows<EPI>() == 2 ? DEC_GEMV_UNR_PAIRED : DEC_GEMV_UNR_SINGLE;
+  hipLaunchKernelGGL((gemv_kernel<EPI, U>), grid, dim3(GV_WAVES * WAVE), lds, st, g);
   return hipGetLastError();
+}
+
+int device_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    hipDeviceProp_t p;
+    cus = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&p, dev) == hipSuccess) ? p.multiProcessorCount : 256;
+  }
+  return cus;
 }
 
 }  // namespace
 
-// items per wave: two when there are enough items to keep ~2 blocks per CU busy
-int gemv_ipw(int n_items) { return n_items >= GEMV_IPW2_MIN_ITEMS ? 2 : 1; }
+// persistent grid: at most DEC_GEMV_BLOCKS_PER_CU blocks per compute unit
 int gemv_blocks(int n_items) {
-  const int per = GV_WAVES * gemv_ipw(n_items);
-  return (n_items + per - 1) / per;
+  const int need = (n_items + GV_WAVES - 1) / GV_WAVES;
+  return std::max(1, std::min(need, DEC_GEMV_BLOCKS_PER_CU * device_cus()));
 }
 
 hipError_t launch_gemv(const GemvArgs &g, int epi, hipStream_t st) {
-  const int ipw = gemv_ipw(g.n_items);
   dim3 grid(gemv_blocks(g.n_items), g.slot_expert ? g.n_slots : 1);
   const size_t lds = (size_t)g.K * 4;
   switch (epi) {
-    case EPI_STORE: return launch_e<EPI_STORE>(g, ipw, grid, lds, st);
-    case EPI_ADD: return launch_e<EPI_ADD>(g, ipw, grid, lds, st);
-    case EPI_SWIGLU: return launch_e<EPI_SWIGLU>(g, ipw, grid, lds, st);
-    case EPI_QKV: return launch_e<EPI_QKV>(g, ipw, grid, lds, st);
-    default: return launch_e<EPI_LOGITS>(g, ipw, grid, lds, st);
+    case EPI_STORE: return launch_e<EPI_STORE>(g, grid, lds, st);
+    case EPI_ADD: return launch_e<EPI_ADD>(g, grid, lds, st);
+    case EPI_SWIGLU: return launch_e<EPI_SWIGLU>(g, grid, lds, st);
+    case EPI_QKV: return launch_e<EPI_QKV>(g, grid, lds, st);
+    default: return launch_e<EPI_LOGITS>(g, grid, lds, st);
   }
 }

@@ -41,10 +41,10 @@ struct GemvArgs {
   int32_t *part_idx;
 };
 constexpr size_t GEMV_MAX_LDS = 60 * 1024;
-// GEMV launch shape: a wave owns two items from this many items on; UNR
-// steps of 1 KB per row are in flight per batch (tuned on the GPU)
-#ifndef DEC_GEMV_IPW2_MIN_ITEMS
-#define DEC_GEMV_IPW2_MIN_ITEMS (1 << 30)
+// GEMV launch shape: persistent blocks per compute unit, and UNR steps of
+// 1 KB per row in each load batch (tuned on the GPU)
+#ifndef DEC_GEMV_BLOCKS_PER_CU
+#define DEC_GEMV_BLOCKS_PER_CU 2
 #endif
 #ifndef DEC_GEMV_UNR_SINGLE
 #define DEC_GEMV_UNR_SINGLE 4
@@ -52,7 +52,6 @@ constexpr size_t GEMV_MAX_LDS = 60 * 1024;
 #ifndef DEC_GEMV_UNR_PAIRED
 #define DEC_GEMV_UNR_PAIRED 2
 #endif
-constexpr int GEMV_IPW2_MIN_ITEMS = DEC_GEMV_IPW2_MIN_ITEMS;
 int gemv_blocks(int n_items);
 hipError_t launch_gemv(const GemvArgs &g, int epi, hipStream_t st);
 
@@ -64,8 +63,10 @@ hipError_t launch_argmax_finalize(const float *part_val, const int32_t *part_idx
 
 // ------------------------------------------------------------- attention --
 struct AttnArgs {
-  const uint16_t *q;       // bf16 [rows][Hq][d], rotated
-  uint16_t *out;           // bf16 [rows][Hq][d], or null when out_f32 is set
+  const uint16_t *q;       // split bf16 [rows][Hq][d], rotated; lo plane at q + q_lo
+  int64_t q_lo;
+  uint16_t *out;           // split bf16 [rows][Hq][d] (lo plane at out + out_lo), or null
+  int64_t out_lo;
   float *out_f32;          // fp32 [rows][Hq][d] (batch-1 decode feeds the fp32 projection)
   const uint16_t *kcache;  // K cache base: [seq][layer][Hkv][S][d]
   const uint16_t *vcache;  // V cache base, transposed: [seq][layer][Hkv][d][S]
@@ -88,9 +89,10 @@ hipError_t launch_attention(const AttnArgs &a, int head_dim, hipStream_t st);
 hipError_t launch_embed(const uint16_t *E, const int32_t *ids, const int32_t *next_token,
                         const int32_t *row_seq, int use_next, int rows, int H, float *x,
                         hipStream_t st);
-// out[r] = bf16(x[r] * rsqrt(mean(x^2) + eps) * g), or fp32 into out_f32 when it is set
+// out[r] = x[r] * rsqrt(mean(x^2) + eps) * g as split bf16 (lo plane at out + out_lo),
+// or fp32 into out_f32 when it is set
 hipError_t launch_rmsnorm(const float *x, int64_t ldx, const float *g, int rows, int H, float eps,
-                          uint16_t *out, int64_t ldo, hipStream_t st, float *out_f32 = nullptr);
+                          uint16_t *out, int64_t ldo, int64_t out_lo, hipStream_t st, float *out_f32 = nullptr);
 
 // V^T cache import: src [Hkv][len][d] -> dst [Hkv][d][S] (positions < len)
 hipError_t launch_kv_load_v(const uint16_t *src, uint16_t *dst, int Hkv, int len, int d, int S,
@@ -99,13 +101,14 @@ hipError_t launch_kv_load_v(const uint16_t *src, uint16_t *dst, int Hkv, int len
 // ------------------------------------------------------------------- MoE --
 struct MoeRouteArgs {
   const float *logits;     // fp32 [rows][E] router logits
-  const uint16_t *act;     // bf16 [rows][H] normed FFN input (for the shared gate)
+  const uint16_t *act;     // split bf16 [rows][H] normed FFN input (for the shared gate)
+  int64_t act_lo;
   const float *act_f32;    // or fp32 [rows][H] when set
   const uint16_t *w_sh_gate;  // bf16 [H] or null
   int32_t rows, E, k, H, renorm;
   int32_t *ids;            // [rows][k]
   float *wts;              // [rows][k]
-  float *gate;             // [rows] shared-expert scale
+  float *gate;             // [rows] shared-expert scale (optional)
   int32_t *ids_record;     // optional copy of ids (per-layer record)
   // grouping outputs
   int32_t *n_groups, *group_expert, *group_start, *group_count;

@@ -36,7 +36,8 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(MoeRouteArgs a
       for (int j = threadIdx.x; j < a.H; j += blockDim.x) dot += b[j] * bf16_to_f32(a.w_sh_gate[j]);
     } else {
       const uint16_t *b = a.act + (int64_t)r * a.H;
-      for (int j = threadIdx.x; j < a.H; j += blockDim.x) dot += bf16_to_f32(b[j]) * bf16_to_f32(a.w_sh_gate[j]);
+      for (int j = threadIdx.x; j < a.H; j += blockDim.x)
+        dot += (bf16_to_f32(b[j]) + bf16_to_f32(b[a.act_lo + j])) * bf16_to_f32(a.w_sh_gate[j]);
     }
   }
   dot = block_sum<ROUTE_THREADS / WAVE>(dot, red);
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(MoeRouteArgs a
       for (int j = 0; j < a.k; ++j) w[j] /= sel;
     if (a.ids_record)
       for (int j = 0; j < a.k; ++j) a.ids_record[(int64_t)r * a.k + j] = ids[j];
-    a.gate[r] = a.w_sh_gate ? 1.0f / (1.0f + expf(-dot)) : 1.0f;
+    if (a.gate) a.gate[r] = a.w_sh_gate ? 1.0f / (1.0f + expf(-dot)) : 1.0f;
   }
 }
 

@@ -27,11 +27,12 @@ __global__ __launch_bounds__(256) void embed_kernel(const uint16_t *E, const int
   }
 }
 
-// out = bf16(x / sqrt(mean(x^2) + eps) * g): engine.zig rmsnormColumn (eps
-// inside the root, gain after), accumulated in fp32.
+// out = x / sqrt(mean(x^2) + eps) * g: engine.zig rmsnormColumn (eps inside
+// the root, gain after), accumulated in fp32, stored as split bf16 (or as
+// plain bf16 when out_lo is 0, or as fp32).
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x, int64_t ldx, const float *g,
                                                       int H, float eps, uint16_t *out,
-                                                      int64_t ldo, float *out_f32) {
+                                                      int64_t ldo, int64_t out_lo, float *out_f32) {
   __shared__ float lds[4];
   const float *xr = x + (int64_t)blockIdx.x * ldx;
   float ss = 0.f;
@@ -50,10 +51,11 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x, int64_t ld
           f32x4{v[0] * inv * w[0], v[1] * inv * w[1], v[2] * inv * w[2], v[3] * inv * w[3]};
       continue;
     }
-    u32x2 o;
-    o[0] = pack_bf16x2(v[0] * inv * w[0], v[1] * inv * w[1]);
-    o[1] = pack_bf16x2(v[2] * inv * w[2], v[3] * inv * w[3]);
-    *reinterpret_cast<u32x2 *>(orow + j) = o;
+    u32x2 oh, ol;
+    { const u32pair t_ = pack_split2(v[0] * inv * w[0], v[1] * inv * w[1]); oh[0] = t_.hi; ol[0] = t_.lo; }
+    { const u32pair t_ = pack_split2(v[2] * inv * w[2], v[3] * inv * w[3]); oh[1] = t_.hi; ol[1] = t_.lo; }
+    *reinterpret_cast<u32x2 *>(orow + j) = oh;
+    if (out_lo) *reinterpret_cast<u32x2 *>(orow + out_lo + j) = ol;
   }
 }
 
@@ -68,8 +70,8 @@ hipError_t launch_embed(const uint16_t *E, const int32_t *ids, const int32_t *ne
 }
 
 hipError_t launch_rmsnorm(const float *x, int64_t ldx, const float *g, int rows, int H, float eps,
-                          uint16_t *out, int64_t ldo, hipStream_t st, float *out_f32) {
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, st, x, ldx, g, H, eps, out, ldo, out_f32);
+                          uint16_t *out, int64_t ldo, int64_t out_lo, hipStream_t st, float *out_f32) {
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, st, x, ldx, g, H, eps, out, ldo, out_lo, out_f32);
   return hipGetLastError();
 }
 

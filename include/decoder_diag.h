@@ -34,6 +34,13 @@ int dec_diag_gemv(const float *d_a, int32_t K, const uint16_t *d_W, int32_t N, f
 int dec_diag_rmsnorm(const float *d_x, const float *d_g, int32_t rows, int32_t H, double eps,
                      uint16_t *d_out, void *stream);
 
+/* MoE routing of rows router-logit vectors (pipeline.rs MoeFfn: softmax
+ * over all experts, top-k, optional renormalisation; lower index first on
+ * ties).  logits fp32 [rows][E]; ids int32 [rows][k] in router order,
+ * wts fp32 [rows][k]; E <= 256, k <= 8. */
+int dec_diag_moe_route(const float *d_logits, int32_t rows, int32_t E, int32_t k, int32_t renorm,
+                       int32_t *d_ids, float *d_wts, void *stream);
+
 /* Run only the first `layers` layers in later calls (-1: all of them); the
  * final norm and lm-head still run (engine.zig Engine.stopAfterLayer). */
 int decoder_debug_layer_limit(decoder_t *dec, int32_t layers);
