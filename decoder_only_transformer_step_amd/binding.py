@@ -75,6 +75,7 @@ SIGNATURES = {
     "decoder_debug_read_routes": (ctypes.c_int, [_P, _P, _I32]),
     "decoder_stats_enable": (ctypes.c_int, [_P, _I32]),
     "decoder_stats_read": (ctypes.c_int, [_P, ctypes.POINTER(DecoderStats)]),
+    "decoder_stats_mask": (ctypes.c_int, [_P, _I32]),
 }
 
 
@@ -241,6 +242,13 @@ class Decoder:
             for n in nodes:
                 mask |= 1 << NODES.index(n)
         _check(lib().decoder_stats_enable(self.handle, mask), self.handle, "stats_enable")
+
+    def stats_mask(self, nodes):
+        """Time only `nodes` from now on (no clearing, no wait)."""
+        mask = 0
+        for n in nodes:
+            mask |= 1 << NODES.index(n)
+        _check(lib().decoder_stats_mask(self.handle, mask), self.handle, "stats_mask")
 
     def stats_read(self):
         st = DecoderStats()

@@ -35,7 +35,7 @@ struct Layout {
   size_t total;
   int S, R, RL;
   int64_t seq_stride;
-  size_t gpart_elems;
+  size_t gpart_elems, am_n;
 };
 
 bool config_ok(const decoder_config_t *c) {
@@ -96,7 +96,8 @@ Layout make_layout(const decoder_config_t *c) {
   L.counters = take((size_t)(1 + ATTN_MAX_TASKS) * 4);
   // argmax candidates: one per 16-column tile per row (multi-row lm-head),
   // or one per 8-row block (batch-1 lm-head)
-  const size_t am_n = std::max((size_t)L.RL * ((c->vocab + 15) / 16), (size_t)(c->vocab + 7) / 8);
+  const size_t am_n = std::max((size_t)L.RL * ((c->vocab + 15) / 16), (size_t)(c->vocab + 3) / 4);
+  L.am_n = am_n;
   L.am_val = take(am_n * 4);
   L.am_idx = take(am_n * 4);
   L.am_out = take((size_t)L.RL * 4);
@@ -141,6 +142,7 @@ struct decoder {
   int32_t *ids, *row_seq, *row_pos, *next_token, *rids, *rids_rec, *groups, *pair_row, *pair_of;
   int32_t *counters, *am_idx, *am_out;
   float *f32_attn, *f32_h, *f32_act, *f32_hexp;
+  size_t am_cap = 0;           // argmax partials the am_val / am_idx buffers hold
   bool single_row_ok = false;  // the batch-1 GEMV path fits every K of this config
   int64_t act_lo = 0, attn_lo = 0, q_lo = 0, h_lo = 0, hexp_lo = 0, hsh_lo = 0;  // lo-plane offsets
   // host state
@@ -355,12 +357,12 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
 }
 
 // Launch one batch-1 projection (GEMV) as node `node`.
-int gemv(decoder *D, int node, int epi, const GemvArgs &g) {
+int gemv(decoder *D, int node, int epi, const GemvArgs &g, int *blocks = nullptr) {
   const double nr = (epi == EPI_SWIGLU || epi == EPI_QKV) ? 2.0 : 1.0;
   const double slots = g.slot_expert ? g.n_slots : 1;
   NodeTimer timer(D, node, slots * (nr * g.n_items * (double)g.K * 2 + g.K * 4.0 + g.n_items * 4.0 * (epi == EPI_ADD ? 2 : 1)),
                   slots * 2.0 * nr * g.n_items * (double)g.K);
-  hipError_t e = launch_gemv(g, epi, D->stream);
+  hipError_t e = launch_gemv(g, epi, D->stream, blocks);
   if (e != hipSuccess) return hip_fail(D, e, "gemv");
   return DEC_OK;
 }
@@ -640,8 +642,9 @@ int run_step(decoder *D, int rows, int rows_per_group, int max_pos, const int32_
     g.eps = (float)c.rms_eps;
     g.part_val = D->am_val;
     g.part_idx = D->am_idx;
-    if ((rc = gemv(D, DEC_NODE_HEAD, EPI_LOGITS, g))) return rc;
-    nparts = gemv_blocks(c.vocab);
+    const GemvShape sh = gemv_shape(c.vocab, H, EPI_LOGITS);
+    if ((size_t)sh.blocks > D->am_cap) return fail(D, DEC_E_HIP, "lm-head grid exceeds the argmax partial buffer");
+    if ((rc = gemv(D, DEC_NODE_HEAD, EPI_LOGITS, g, &nparts))) return rc;
   } else {
     GemmArgs g = dense_args(nullptr, H, D->lm_head, nout, c.vocab, H);
     if ((rc = norm_into(D, g, D->x + (size_t)first * H, D->final_norm, nout))) return rc;
@@ -739,6 +742,7 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
   D->gpart = carve<float>(D, L.gpart);
   D->counters = carve<int32_t>(D, L.counters);
   D->am_val = carve<float>(D, L.am_val);
+  D->am_cap = L.am_n;
   D->am_idx = carve<int32_t>(D, L.am_idx);
   D->am_out = carve<int32_t>(D, L.am_out);
   D->act_lo = (int64_t)L.R * cfg->hidden;
@@ -994,6 +998,13 @@ int decoder_stats_enable(decoder_t *D, int32_t node_mask) {
     int rc = stats_harvest(D);
     if (rc) return rc;
   }
+  D->stats_mask = (uint32_t)node_mask;
+  return DEC_OK;
+}
+
+int decoder_stats_mask(decoder_t *D, int32_t node_mask) {
+  if (check_dec(D)) return DEC_E_INVALID;
+  if (node_mask && D->tev.empty()) return fail(D, DEC_E_INVALID, "stats not enabled");
   D->stats_mask = (uint32_t)node_mask;
   return DEC_OK;
 }

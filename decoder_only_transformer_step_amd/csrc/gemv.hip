@@ -23,12 +23,14 @@
 //    back, the next item's first loads overlapping the current reduction.
 //  * Grouped mode (MoE experts): blockIdx.y = routing slot; the weight base
 //    moves to the chosen expert.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
 namespace {
 
-constexpr int GV_WAVES = 8;
+constexpr int GV_MAX_WAVES = 8;
 
 template <int EPI>
 constexpr int gv_rows() {
@@ -164,13 +166,13 @@ __device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, in
 // sequence of UNR-step load batches, ping-ponging between two register
 // buffers, so the first batch of the next item is already in flight while
 // the current item is reduced and written.
-template <int EPI, int UNR>
+template <int EPI, int UNR, int GV_WAVES>
 __global__ __launch_bounds__(GV_WAVES * WAVE) void gemv_kernel(GemvArgs g) {
   constexpr int NR = gv_rows<EPI>();
   extern __shared__ float xs[];
-  __shared__ float sred[GV_WAVES];
-  __shared__ float bv_s[GV_WAVES];
-  __shared__ int bi_s[GV_WAVES];
+  __shared__ float sred[GV_MAX_WAVES];
+  __shared__ float bv_s[GV_MAX_WAVES];
+  __shared__ int bi_s[GV_MAX_WAVES];
 
   const uint16_t *W = g.W;
   const float *xin = g.a_f32;
@@ -290,11 +292,46 @@ __global__ __launch_bounds__(GV_WAVES * WAVE) void gemv_kernel(GemvArgs g) {
   }
 }
 
+// A load batch holds DEC_GEMV_LOADS kilobytes (twice that when deep) across
+// the item's rows.
+template <int EPI, int W, bool DEEP>
+constexpr auto gv_kernel() {
+  constexpr int NR = gv_rows<EPI>();
+  return gemv_kernel<EPI, (DEEP ? 2 : 1) * DEC_GEMV_LOADS / NR, W>;
+}
+
 template <int EPI>
-hipError_t launch_e(const GemvArgs &g, dim3 grid, size_t lds, hipStream_t st) {
-  constexpr int U = gv_rows<EPI>() == 2 ? DEC_GEMV_UNR_PAIRED : DEC_GEMV_UNR_SINGLE;
-  hipLaunchKernelGGL((gemv_kernel<EPI, U>), grid, dim3(GV_WAVES * WAVE), lds, st, g);
+hipError_t launch_e(const GemvArgs &g, const GemvShape &sh, dim3 grid, size_t lds, hipStream_t st) {
+  if (sh.waves == 4) {
+    if (sh.deep) hipLaunchKernelGGL((gv_kernel<EPI, 4, true>()), grid, dim3(4 * WAVE), lds, st, g);
+    else hipLaunchKernelGGL((gv_kernel<EPI, 4, false>()), grid, dim3(4 * WAVE), lds, st, g);
+  } else {
+    if (sh.deep) hipLaunchKernelGGL((gv_kernel<EPI, 8, true>()), grid, dim3(8 * WAVE), lds, st, g);
+    else hipLaunchKernelGGL((gv_kernel<EPI, 8, false>()), grid, dim3(8 * WAVE), lds, st, g);
+  }
   return hipGetLastError();
+}
+
+// Blocks of one kernel instance resident per compute unit (registers and
+// the block's LDS), or 1 if the runtime cannot say.
+template <int EPI, int W, bool DEEP>
+int resident_e(size_t lds) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(gv_kernel<EPI, W, DEEP>()),
+                                                   W * WAVE, lds) != hipSuccess || n < 1)
+    n = 1;
+  return n;
+}
+
+template <int W, bool DEEP>
+int resident(int epi, size_t lds) {
+  switch (epi) {
+    case EPI_STORE: return resident_e<EPI_STORE, W, DEEP>(lds);
+    case EPI_ADD: return resident_e<EPI_ADD, W, DEEP>(lds);
+    case EPI_SWIGLU: return resident_e<EPI_SWIGLU, W, DEEP>(lds);
+    case EPI_QKV: return resident_e<EPI_QKV, W, DEEP>(lds);
+    default: return resident_e<EPI_LOGITS, W, DEEP>(lds);
+  }
 }
 
 int device_cus() {
@@ -309,20 +346,53 @@ int device_cus() {
 
 }  // namespace
 
-// persistent grid: at most DEC_GEMV_BLOCKS_PER_CU blocks per compute unit
-int gemv_blocks(int n_items) {
-  const int need = (n_items + GV_WAVES - 1) / GV_WAVES;
-  return std::max(1, std::min(need, DEC_GEMV_BLOCKS_PER_CU * device_cus()));
+// Persistent grid shape: blocks of 4 or 8 waves, m blocks per compute unit
+// (m at most DEC_GEMV_BLOCKS_PER_CU and at most what fits in registers and
+// LDS at once), chosen so that the busiest compute unit has as few items as
+// possible (items spread evenly over the waves of evenly loaded CUs, no tail
+// round with idle waves), then for the most waves in flight.  Deep batches
+// when a wave owns a single item (nothing to pipeline across items) or there
+// are few waves per compute unit, if they fit.
+GemvShape gemv_shape(int n_items, int K, int epi) {
+  const int cus = device_cus();
+  const size_t lds = (size_t)K * 4;
+  GemvShape best{8, 1, 1, false};
+  long best_load = -1;
+  int best_waves = 0, best_m = 1;
+  for (int w : {8, 4}) {
+    const int fit = std::min(DEC_GEMV_BLOCKS_PER_CU, w == 8 ? resident<8, false>(epi, lds) : resident<4, false>(epi, lds));
+    for (int m = 1; m <= fit; ++m) {
+      const long waves = (long)cus * m * w;
+      const int per = (int)((n_items + waves - 1) / waves);
+      const int blocks = (n_items + w * per - 1) / (w * per);
+      // items on the busiest compute unit (blocks spread evenly over the CUs)
+      const long load = (long)((blocks + cus - 1) / cus) * w * per;
+      const int wpc = (int)((long)blocks * w / cus);
+      if (best_load < 0 || load < best_load || (load == best_load && wpc > best_waves)) {
+        best_load = load;
+        best_waves = wpc;
+        best_m = (blocks + cus - 1) / cus;
+        best = GemvShape{w, blocks, per, false};
+      }
+    }
+  }
+  if (best.per_wave == 1 || (long)best.blocks * best.waves <= 8L * cus) {
+    const int fit = best.waves == 8 ? resident<8, true>(epi, lds) : resident<4, true>(epi, lds);
+    best.deep = best_m <= fit;
+  }
+  return best;
 }
 
-hipError_t launch_gemv(const GemvArgs &g, int epi, hipStream_t st) {
-  dim3 grid(gemv_blocks(g.n_items), g.slot_expert ? g.n_slots : 1);
+hipError_t launch_gemv(const GemvArgs &g, int epi, hipStream_t st, int *blocks) {
+  const GemvShape sh = gemv_shape(g.n_items, g.K, epi);
+  if (blocks) *blocks = sh.blocks;
+  dim3 grid(sh.blocks, g.slot_expert ? g.n_slots : 1);
   const size_t lds = (size_t)g.K * 4;
   switch (epi) {
-    case EPI_STORE: return launch_e<EPI_STORE>(g, grid, lds, st);
-    case EPI_ADD: return launch_e<EPI_ADD>(g, grid, lds, st);
-    case EPI_SWIGLU: return launch_e<EPI_SWIGLU>(g, grid, lds, st);
-    case EPI_QKV: return launch_e<EPI_QKV>(g, grid, lds, st);
-    default: return launch_e<EPI_LOGITS>(g, grid, lds, st);
+    case EPI_STORE: return launch_e<EPI_STORE>(g, sh, grid, lds, st);
+    case EPI_ADD: return launch_e<EPI_ADD>(g, sh, grid, lds, st);
+    case EPI_SWIGLU: return launch_e<EPI_SWIGLU>(g, sh, grid, lds, st);
+    case EPI_QKV: return launch_e<EPI_QKV>(g, sh, grid, lds, st);
+    default: return launch_e<EPI_LOGITS>(g, sh, grid, lds, st);
   }
 }

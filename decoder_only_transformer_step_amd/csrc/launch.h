@@ -41,19 +41,22 @@ struct GemvArgs {
   int32_t *part_idx;
 };
 constexpr size_t GEMV_MAX_LDS = 60 * 1024;
-// GEMV launch shape: persistent blocks per compute unit, and UNR steps of
-// 1 KB per row in each load batch (tuned on the GPU)
+// GEMV launch shape: at most this many persistent blocks per compute unit,
+// and kilobytes per load batch (doubled for deep batches; tuned on the GPU)
 #ifndef DEC_GEMV_BLOCKS_PER_CU
-#define DEC_GEMV_BLOCKS_PER_CU 2
+#define DEC_GEMV_BLOCKS_PER_CU 4
 #endif
-#ifndef DEC_GEMV_UNR_SINGLE
-#define DEC_GEMV_UNR_SINGLE 4
+#ifndef DEC_GEMV_LOADS
+#define DEC_GEMV_LOADS 4
 #endif
-#ifndef DEC_GEMV_UNR_PAIRED
-#define DEC_GEMV_UNR_PAIRED 2
-#endif
-int gemv_blocks(int n_items);
-hipError_t launch_gemv(const GemvArgs &g, int epi, hipStream_t st);
+struct GemvShape {
+  int waves, blocks, per_wave;
+  bool deep;
+};
+GemvShape gemv_shape(int n_items, int K, int epi);
+// `blocks` (optional) receives the grid size, i.e. the number of argmax
+// partials an EPI_LOGITS launch writes
+hipError_t launch_gemv(const GemvArgs &g, int epi, hipStream_t st, int *blocks = nullptr);
 
 // idx[r] = argmax over part_val[r][0 .. nparts) (lowest index on ties), and
 // next_token[row_seq[r]] = idx[r] for the last row of each sequence

@@ -85,6 +85,9 @@ typedef struct {
  * (1 << DEC_NODE_*) is set (-1: every node); 0: stop timing (counters are
  * kept for decoder_stats_read).  Timing fewer nodes perturbs the step less. */
 int decoder_stats_enable(decoder_t *dec, int32_t node_mask);
+/* Change which nodes are timed without clearing the counters or waiting
+ * for the stream (for timing a sample of the steps of a timed region). */
+int decoder_stats_mask(decoder_t *dec, int32_t node_mask);
 /* Wait for the decoder's stream, then return the totals since enabling. */
 int decoder_stats_read(decoder_t *dec, decoder_stats_t *out);
 
