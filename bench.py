@@ -36,9 +36,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# sources of the batch-1 projection kernel (the dominant decode kernel)
+KERNEL_SOURCES = ("gemv.hip", "common.h", "launch.h")
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h"):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "decoder_only_transformer_step_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -98,21 +102,124 @@ def summarize_nodes(st):
     return out
 
 
+# ------------------------------------------------ profile summaries --
+# Text summaries of rocprofv3 output for the profiles folder: the per-kernel
+# statistics of a --kernel-trace --stats run, and the HBM bytes of the
+# dominant kernel from two --pmc runs (FETCH_SIZE, WRITE_SIZE), scaled by
+# what the same counters read for a plain device copy of known size.
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _short_name(n):
+    m = re.search(r"(\w+)(<[^>]*>)?\(", n)
+    return (m.group(1) + (m.group(2) or "")) if m else n[:60]
+
+
+def summarize_stats(stats_csv, bench_json, out, command):
+    rows = _read_csv(stats_csv)
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    tot = sum(float(r["TotalDurationNs"]) for r in rows)
+    res = json.loads(open(bench_json).read().strip().splitlines()[-1]) if bench_json else None
+    lines = ["# rocprofv3 kernel statistics", "", "Command (from the repository root):", "", "```", command, "```", ""]
+    if res:
+        rf = res["roofline"]
+        lines += [f"bench line: value {res['value']} {res['unit']}, ms_per_step {res['ms_per_step']}, "
+                  f"workload {res['config']['workload']}", "",
+                  f"bench roofline kernel: {rf['kernel']}: avg {rf['avg_us']} us per launch over "
+                  f"{rf['launches']} sampled launches (HIP events), {rf['achieved']} GB/s, frac {rf['frac']}", ""]
+    lines += ["| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
+    for r in rows[:25]:
+        lines.append(f"| `{_short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{100 * float(r['TotalDurationNs']) / tot:.1f} |")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def _counter_per_dispatch(path, pattern, counter):
+    """Average counter value (KiB) per dispatch of kernels whose name matches."""
+    vals, grids = {}, {}
+    for r in _read_csv(path):
+        if r.get("Counter_Name") != counter or not re.search(pattern, r["Kernel_Name"]):
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        grids[key] = int(r.get("Grid_Size", "0") or 0)
+    return vals, grids
+
+
+def summarize_counters(fetch_csv, write_csv, kernel_pattern, copy_bytes, algo_bytes, out, commands):
+    copy_pat = r"copyBuffer|elementwise|copy"
+    res = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        kv, _ = _counter_per_dispatch(path, kernel_pattern, name)
+        cv, cg = _counter_per_dispatch(path, copy_pat, name)
+        # the calibration copy: the dispatches with the largest grid
+        big = max(cg.values())
+        cvals = [cv[k] for k in cv if cg[k] == big]
+        kib_copy = statistics.mean(cvals)
+        factor = copy_bytes / (kib_copy * 1024.0)
+        kib = statistics.mean(kv.values())
+        res[name] = {"dispatches": len(kv), "kib_per_dispatch": kib, "copy_kib": kib_copy,
+                     "copy_dispatches": len(cvals), "factor": factor, "bytes": kib * 1024.0 * factor}
+    traffic = res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"]
+    lines = ["# HBM traffic of the dominant decode kernel (rocprofv3 --pmc)", "",
+             "Commands (from the repository root), one counter per run:", ""]
+    lines += ["```"] + commands + ["```", ""]
+    lines += [f"kernel: `{kernel_pattern}` (regex on the kernel name)", "",
+              f"calibration: a plain device copy of {copy_bytes} bytes in the same process "
+              "(the counters of its dispatches give the scale factor bytes / (KiB x 1024))", "",
+              "| counter | kernel dispatches | KiB per dispatch | copy KiB | factor | bytes per launch |",
+              "|---|---:|---:|---:|---:|---:|"]
+    for name, r in res.items():
+        lines.append(f"| {name} | {r['dispatches']} | {r['kib_per_dispatch']:.0f} | {r['copy_kib']:.0f} | "
+                     f"{r['factor']:.4f} | {r['bytes']:.4g} |")
+    lines += ["", f"algorithmic bytes per launch: {algo_bytes:.6g}",
+              f"traffic / algorithmic: {traffic / algo_bytes:.4f}", "",
+              f"traffic_bytes_per_launch: {traffic:.6g}",
+              f"kernel_source_sha256: {kernel_source_hash()}", ""]
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256, help="timed decode steps")
     ap.add_argument("--warmup", type=int, default=3, help="untimed decode steps before timing")
     ap.add_argument("--workload", default="8b", help="8b (default), 135m, tiny, moe, longctx")
-    ap.add_argument("--prefill-runs", type=int, default=3, help="timed whole-prompt prefills (median)")
+    ap.add_argument("--prefill-runs", type=int, default=5, help="timed whole-prompt prefills (median)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill measurement: the decode context is a synthetic N(0,1) KV "
+                         "prefix of the prompt's length (for counter runs of the decode kernels)")
     ap.add_argument("--cpu-prefill", type=int, default=16, help="oracle sample: prompt tokens")
     ap.add_argument("--cpu-decode", type=int, default=2, help="oracle sample: decode steps")
     ap.add_argument("--sample-every", type=int, default=8,
                     help="time the dominant kernel with HIP events in every N-th timed step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "BENCH_JSON"),
+                    help="write a kernel statistics summary (with --out and --command) and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic summary of --kernel (with --out, --command, "
+                         "--algo-bytes) and exit")
+    ap.add_argument("--kernel", default=r"gemv_kernel<2,")
+    ap.add_argument("--algo-bytes", type=float, default=0.0)
+    ap.add_argument("--copy-bytes", type=float, default=float(1 << 30))
+    ap.add_argument("--out")
+    ap.add_argument("--command", action="append", default=[])
     args = ap.parse_args()
+
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.out, "\n".join(args.command))
+        return 0
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.kernel, args.copy_bytes,
+                           args.algo_bytes, args.out, args.command)
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -146,7 +253,8 @@ def main():
 
     # ------------------------------------------------------------ prefill --
     prefill = None
-    if work.prompt:
+    context = work.context or (work.prompt if args.no_prefill else 0)
+    if work.prompt and not args.no_prefill:
         ids = [int(t) for t in prompt(shape, work.prompt)]
         chunks = [ids[i:i + work.chunk] for i in range(0, len(ids), work.chunk)]
         times = []
@@ -188,20 +296,20 @@ def main():
                    "gemm_hbm_frac": g_by / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                    "chunk_mfma_ceiling": ceiling, "nodes": summarize_nodes(pst)}
         log(f"[gpu] prefill {prefill['tok_s']:.0f} tok/s ({t_pre * 1e3:.1f} ms for {len(ids)} tokens)")
-    elif work.context:
-        # long-context batched decode: every sequence starts with a synthetic N(0,1) KV prefix
+    elif context:
+        # every sequence starts with a synthetic N(0,1) KV prefix (long-context batched decode)
         t0 = time.time()
         buf = None
         for s in seqs:
             for l in range(shape.n_layers):
-                buf = device_kv(shape, s, l, work.context, out=buf)
-                dec.kv_load(s, l, buf[0], buf[1], work.context)
+                buf = device_kv(shape, s, l, context, out=buf)
+                dec.kv_load(s, l, buf[0], buf[1], context)
         del buf
         torch.cuda.synchronize()
-        log(f"[gpu] KV prefix {batch} x {work.context} filled in {time.time() - t0:.1f}s")
+        log(f"[gpu] KV prefix {batch} x {context} filled in {time.time() - t0:.1f}s")
 
     # ------------------------------------------------------------- decode --
-    first_tokens = None if work.prompt else [int(t) for t in prompt(shape, batch, seq=99)]
+    first_tokens = None if prefill else [int(t) for t in prompt(shape, batch, seq=99)]
     am = torch.empty(batch, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     ev0.record(stream)
@@ -249,15 +357,18 @@ def main():
     traffic = counter_traffic(f"counters_{dom}_decode_{args.workload}.md")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": f"{dom} projection (gemm_kernel, decode)", "bytes_per_launch": per_launch_bytes,
+                "kernel": f"{dom} ({'gemv_kernel, batch-1 projection' if dom != 'attn' else 'attn_kernel'}, decode)", "bytes_per_launch": per_launch_bytes,
                 "avg_us": round(per_launch_s * 1e6, 2), "launches": d["launches"],
-                "timing": f"HIP events around every {dom} launch of every {args.sample_every}th timed step"}
+                "timing": f"HIP events (no system fence) around every {dom} launch of every {args.sample_every}th "
+                          "timed step; an event pair adds about 4.5 us of dispatch latency to the "
+                          "bracketed kernel, so this is an upper bound on the kernel's own duration"}
 
     result.update({
         "value": round(tok_s, 2),
         "ms_per_step": round(t_dec / args.steps * 1e3, 4),
         "config": {"workload": shape.name, "global_batch": batch, "decode_positions":
                    [work.prompt or work.context, (work.prompt or work.context) + args.warmup + args.steps],
+                   "kv_prefix": "prefill" if prefill else "synthetic N(0,1)",
                    "prefill_prompt": work.prompt, "prefill_chunk": work.chunk, "parallelism": "single-gpu"},
         "decode": {"tok_s": tok_s, "first_step_ms": round(first_ms, 3), "hbm_GBps": step_bytes / (t_dec / args.steps) / 1e9,
                    "hbm_frac": step_bytes / (t_dec / args.steps) / 1e9 / HBM_PEAK_GBS,

@@ -989,7 +989,10 @@ int decoder_stats_enable(decoder_t *D, int32_t node_mask) {
   if (node_mask) {
     if (D->tev.empty()) {
       D->tev.resize(TIMER_EVENTS);
-      for (auto &ev : D->tev) HIP_TRY(D, hipEventCreate(&ev), "stats events");
+      // timing-only events: no system-scope cache writeback when they are
+      // recorded, which would add to the bracketed kernel's time (the
+      // results are read after a stream synchronisation)
+      for (auto &ev : D->tev) HIP_TRY(D, hipEventCreateWithFlags(&ev, hipEventDisableSystemFence), "stats events");
     }
     int rc = stats_harvest(D);
     if (rc) return rc;
