@@ -119,7 +119,7 @@ def _short_name(n):
     return (m.group(1) + (m.group(2) or "")) if m else n[:60]
 
 
-def summarize_stats(stats_csv, bench_json, out, command):
+def summarize_stats(stats_csv, bench_json, out, command, plain_json=None):
     rows = _read_csv(stats_csv)
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     tot = sum(float(r["TotalDurationNs"]) for r in rows)
@@ -131,6 +131,12 @@ def summarize_stats(stats_csv, bench_json, out, command):
                   f"workload {res['config']['workload']}", "",
                   f"bench roofline kernel: {rf['kernel']}: avg {rf['avg_us']} us per launch over "
                   f"{rf['launches']} sampled launches (HIP events), {rf['achieved']} GB/s, frac {rf['frac']}", ""]
+    if plain_json:
+        r2 = json.loads(open(plain_json).read().strip().splitlines()[-1])
+        rf2 = r2["roofline"]
+        lines += [f"the same bench without the profiler (`python bench.py`): value {r2['value']} {r2['unit']}, "
+                  f"roofline avg {rf2['avg_us']} us per launch over {rf2['launches']} sampled launches, "
+                  f"{rf2['achieved']} GB/s, frac {rf2['frac']}", ""]
     lines += ["| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
     for r in rows[:25]:
         lines.append(f"| `{_short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -209,12 +215,14 @@ def main():
     ap.add_argument("--kernel", default=r"gemv_kernel<2,")
     ap.add_argument("--algo-bytes", type=float, default=0.0)
     ap.add_argument("--copy-bytes", type=float, default=float(1 << 30))
+    ap.add_argument("--plain-json", help="with --summarize-stats: the bench line of an unprofiled run")
     ap.add_argument("--out")
     ap.add_argument("--command", action="append", default=[])
     args = ap.parse_args()
 
     if args.summarize_stats:
-        summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.out, "\n".join(args.command))
+        summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.out, "\n".join(args.command),
+                        args.plain_json)
         return 0
     if args.summarize_counters:
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.kernel, args.copy_bytes,
