@@ -25,6 +25,8 @@ constexpr int STAGE_RING = 64;     // pinned staging slots (one per call in flig
 constexpr int ATTN_TARGET_BLOCKS = 1024;
 constexpr int ATTN_MAX_TASKS = 8192;
 constexpr int GEMM_MAX_SPLIT = 8;
+constexpr int CHUNK_MIN_ROWS = 16;   // more rows than this take the chunk projection kernel
+constexpr int CHUNK_MAX_SPLIT = 16;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -143,6 +145,7 @@ struct decoder {
   int32_t *counters, *am_idx, *am_out;
   float *f32_attn, *f32_h, *f32_act, *f32_hexp;
   size_t am_cap = 0;           // argmax partials the am_val / am_idx buffers hold
+  int cus = 256;               // compute units of the device
   bool single_row_ok = false;  // the batch-1 GEMV path fits every K of this config
   int64_t act_lo = 0, attn_lo = 0, q_lo = 0, h_lo = 0, hexp_lo = 0, hsh_lo = 0;  // lo-plane offsets
   // host state
@@ -250,11 +253,29 @@ int stage_rows(decoder *D, int rows, const int32_t *ids, const int32_t *seqs, co
 int proj(decoder *D, int node, int epi, GemmArgs g, int max_rows) {
   const double npd = (epi == EPI_SWIGLU || epi == EPI_QKV) ? 2.0 : 1.0;
   const double out_b = epi == EPI_ADD ? 8.0 : ((epi == EPI_SWIGLU || epi == EPI_QKV) ? 2.0 * npd : 4.0);
-  const double a_b = g.x ? 4.0 : 2.0;
+  const double a_b = (g.x || g.a_lo) ? 4.0 : 2.0;
   const double ncols = epi == EPI_QKV ? g.N / 2.0 : g.N;
   NodeTimer timer(D, node, npd * ncols * (double)g.K * 2 + (double)g.M * g.K * a_b + (double)g.M * ncols * out_b,
                   2.0 * npd * g.M * ncols * (double)g.K);
   const int ntiles = gemm_ntiles(g, epi);
+  g.Cpart = D->gpart;
+  if (g.M > CHUNK_MIN_ROWS && gemm_chunk_fits(g, epi)) {
+    // chunk kernel: split K so that the blocks (weight tiles x row blocks x
+    // splits) fill the compute units about once, with at least two 64-wide k
+    // steps per split (fewer, longer blocks measured faster than two rounds)
+    const int nbt = gemm_chunk_tiles(g, epi) * gemm_chunk_mblocks(g.M);
+    const int nsteps = (g.K + 63) / 64;
+    int kc = 1;
+    if (epi != EPI_LOGITS) {
+      kc = std::max(1, D->cus / nbt);
+      kc = std::min(std::min(kc, CHUNK_MAX_SPLIT), std::max(1, nsteps / 2));
+      while (kc > 1 && (size_t)kc * g.M * (size_t)npd * ntiles * 16 > D->L.gpart_elems) --kc;
+    }
+    g.ksplit = kc;
+    hipError_t e = launch_gemm_chunk(g, epi, D->stream);
+    if (e != hipSuccess) return hip_fail(D, e, "chunk projection");
+    return DEC_OK;
+  }
   const int steps = (g.K + 31) / 32;
   int ks = 1;
   if (epi != EPI_LOGITS && !g.n_groups && ntiles < 192 && steps >= 16) {
@@ -263,7 +284,6 @@ int proj(decoder *D, int node, int epi, GemmArgs g, int max_rows) {
     while (ks > 1 && (size_t)ks * g.M * (size_t)npd * ntiles * 16 > D->L.gpart_elems) --ks;
   }
   g.ksplit = std::max(ks, 1);
-  g.Cpart = D->gpart;
   hipError_t e = launch_gemm(g, epi, max_rows, 1, D->stream);
   if (e != hipSuccess) return hip_fail(D, e, "projection");
   return DEC_OK;
@@ -717,6 +737,12 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
   decoder *D = new decoder();
   D->c = *cfg;
   D->L = L;
+  {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      D->cus = cus;
+  }
   D->layers.assign(w->layers, w->layers + cfg->n_layers);
   D->embed = w->embed;
   D->lm_head = w->lm_head;
@@ -953,6 +979,29 @@ int dec_diag_gemm(const uint16_t *d_A, int32_t M, int32_t K, const uint16_t *d_W
   g.ldc = N;
   g.ksplit = 1;
   return launch_gemm(g, EPI_STORE, M, 1, (hipStream_t)stream) == hipSuccess ? DEC_OK : DEC_E_HIP;
+}
+
+int dec_diag_gemm_chunk(const uint16_t *d_A, int32_t planes, int32_t M, int32_t K, const uint16_t *d_W, int32_t N,
+                        float *d_C, int32_t ksplit, float *d_part, int64_t part_elems, void *stream) {
+  if (!d_A || !d_W || !d_C || (planes != 1 && planes != 2) || M < 1 || M > 128 || N < 1 || K < 8 || K % 8 ||
+      ksplit < 1 || ksplit > 64)
+    return DEC_E_INVALID;
+  GemmArgs g{};
+  g.A = d_A;
+  g.a_lo = planes == 2 ? (int64_t)M * K : 0;
+  g.lda = K;
+  g.W = d_W;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.np_off = N;
+  g.C = d_C;
+  g.ldc = N;
+  g.ksplit = ksplit;
+  g.Cpart = d_part;
+  if (ksplit > 1 && (!d_part || part_elems < (int64_t)ksplit * M * gemm_ntiles(g, EPI_STORE) * 16)) return DEC_E_INVALID;
+  if (!gemm_chunk_fits(g, EPI_STORE)) return DEC_E_INVALID;
+  return launch_gemm_chunk(g, EPI_STORE, (hipStream_t)stream) == hipSuccess ? DEC_OK : DEC_E_HIP;
 }
 
 int dec_diag_gemv(const float *d_a, int32_t K, const uint16_t *d_W, int32_t N, float *d_y, void *stream) {

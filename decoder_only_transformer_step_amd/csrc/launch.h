@@ -20,6 +20,15 @@ bool gemm_norm_fits(int rows, int K);
 // max_rows: the largest row count of any group (dense: M); n_group_slots:
 // grid size over groups in grouped mode (blocks past *n_groups exit).
 hipError_t launch_gemm(const GemmArgs &g, int epi, int max_rows, int n_group_slots, hipStream_t st);
+// the fixed-order split-K reduction plus epilogue over Cpart (ntiles 16-row tiles)
+hipError_t launch_gemm_reduce(const GemmArgs &g, int epi, int ntiles, hipStream_t st);
+// Chunk projection (up to 128 rows, A in global memory, no grouping): blocks
+// of 256 weight rows (128 row pairs for the paired epilogues) times g.ksplit
+// k ranges.
+bool gemm_chunk_fits(const GemmArgs &g, int epi);
+int gemm_chunk_tiles(const GemmArgs &g, int epi);
+int gemm_chunk_mblocks(int rows);
+hipError_t launch_gemm_chunk(const GemmArgs &g, int epi, hipStream_t st);
 
 // ------------------------------------------------ single-token projection --
 struct GemvArgs {

@@ -25,6 +25,17 @@ extern "C" {
 int dec_diag_gemm(const uint16_t *d_A, int32_t M, int32_t K, const uint16_t *d_W, int32_t N,
                   float *d_C, void *stream);
 
+/* C = A W^T with the chunk projection kernel (prefill chunks; engine.zig
+ * Engine.prefill: a chunk of token columns shares one pass over the
+ * weights).  A bf16 [planes][M][K]: planes 1 = plain bf16, 2 = hi plane then
+ * lo plane (the activation is their sum); W bf16 [N][K]; C fp32 [M][N].
+ * 1 <= M <= 128, K % 8 == 0.  ksplit > 1 splits K over blocks; the fp32
+ * partials need part_elems >= ksplit * M * 16 * ceil(N / 16) floats at
+ * d_part, reduced in fixed split order.  DEC_E_INVALID on bad sizes. */
+int dec_diag_gemm_chunk(const uint16_t *d_A, int32_t planes, int32_t M, int32_t K, const uint16_t *d_W,
+                        int32_t N, float *d_C, int32_t ksplit, float *d_part, int64_t part_elems,
+                        void *stream);
+
 /* y[n] = sum_k W[n][k] a[k] with the batch-1 decode projection kernel.
  * a fp32 [K], W bf16 [N][K], y fp32 [N]; K % 8 == 0, K * 4 <= 61440. */
 int dec_diag_gemv(const float *d_a, int32_t K, const uint16_t *d_W, int32_t N, float *d_y, void *stream);
