@@ -26,6 +26,8 @@
 //    normalises and writes the output.  With several, each block writes its
 //    (m, l, O) partial and attn_merge combines them in split order, so the
 //    result does not depend on scheduling.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -38,13 +40,32 @@ struct Col {
   int row, head, pos;
 };
 
+// Position of query row `row` of row group rg, by where the positions live
+// (PM = AttnArgs::pos_mode; mode 1 has one row per group, so its lookup
+// index is the block-uniform rg and the value comes from the kernel
+// arguments, with no memory round trip before the cache reads).
+template <int PM>
+__device__ __forceinline__ int row_position(const AttnArgs &a, int rg, int row) {
+  if (PM == 1) return a.pos_arg[rg];
+  if (PM == 2) return a.pos0 + row;
+  return a.row_pos[row];
+}
+
+template <int PM>
+__device__ __forceinline__ int group_seq(const AttnArgs &a, int rg) {
+  if (PM == 1) return a.seq_arg[rg];
+  if (PM == 2) return a.seq0;
+  return a.row_seq[rg * a.rows_per_group];
+}
+
+template <int PM>
 __device__ __forceinline__ Col column(const AttnArgs &a, int rg, int g, int c) {
   Col k;
   const int G = a.G;
   k.row = rg * a.rows_per_group + c / G;
   k.head = g * G + c % G;
   k.valid = (c < a.rows_per_group * G) && (k.row < a.rows);
-  k.pos = k.valid ? a.row_pos[k.row] : -1;
+  k.pos = k.valid ? row_position<PM>(a, rg, k.row) : -1;
   return k;
 }
 
@@ -60,13 +81,16 @@ __device__ __forceinline__ void store_out(const AttnArgs &a, int64_t i, float v)
 }
 
 // keys of the group: 0 .. max position of its valid columns
+template <int PM>
 __device__ __forceinline__ int group_keys(const AttnArgs &a, int rg, int g) {
+  if (PM == 1) return a.pos_arg[rg] + 1;
+  if (PM == 2) return a.pos0 + min(a.rows - 1, (rg + 1) * a.rows_per_group - 1) + 1;
   int kmax = -1;
-  for (int c = 0; c < 16; ++c) kmax = max(kmax, column(a, rg, g, c).pos);
+  for (int c = 0; c < 16; ++c) kmax = max(kmax, column<0>(a, rg, g, c).pos);
   return kmax + 1;
 }
 
-template <int D>
+template <int D, int PM>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   constexpr int NDT = D / 16;
   __shared__ float lo[4][16][D];
@@ -74,24 +98,51 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
   const int gi = blockIdx.x / a.n_splits, split = blockIdx.x - gi * a.n_splits;
   const int g = gi % a.Hkv, rg = gi / a.Hkv;
-  const int keys = group_keys(a, rg, g);
+  const int keys = group_keys<PM>(a, rg, g);
   const int nact = (keys + a.kc - 1) / a.kc;
   if (split >= nact) return;
   const int k0 = split * a.kc, k1 = min(k0 + a.kc, keys);
 
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   const int c = lane & 15, quad = lane >> 4;
-  const Col col = column(a, rg, g, c);
-  const int seq = a.row_seq[rg * a.rows_per_group];
+  const Col col = column<PM>(a, rg, g, c);
+  const int seq = group_seq<PM>(a, rg);
   const uint16_t *kb = a.kcache + (int64_t)seq * a.seq_stride + a.layer_off + (int64_t)g * a.S * D;
   const uint16_t *vb = a.vcache + (int64_t)seq * a.seq_stride + a.layer_off + (int64_t)g * D * a.S;
 
+  // K / V tile loads of the 32 keys at t (K rows straight into MFMA A
+  // operands; V^T rows as two 8-byte pieces per lane)
+  u32x4 ka[D / 32], kh[D / 32];
+  u32x2 va[NDT], vh[NDT];
+  auto load_tile = [&](int t) {
+    const uint16_t *k_lo = kb + (int64_t)(t + c) * D + quad * 8;
+    const uint16_t *k_hi = k_lo + 16 * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      ka[ks] = load16(k_lo + ks * 32);
+      kh[ks] = load16(k_hi + ks * 32);
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const uint16_t *vr = vb + (int64_t)(dt * 16 + c) * a.S + t + quad * 4;
+      va[dt] = load8(vr);
+      vh[dt] = load8(vr + 16);
+    }
+  };
+  // the first tile goes out before q (a wave without a tile of its own
+  // reloads the split's first tile, which stays inside the cache rows)
+  const int t_first = k0 + 32 * wave;
+  load_tile(t_first < k1 ? t_first : k0);
+
+  // q of the column (an invalid column reads row 0 / head 0 and is zeroed:
+  // unconditional loads keep the wait counts exact)
   u32x4 qf[D / 32], ql[D / 32];
-  const uint16_t *qrow = a.q + ((int64_t)col.row * a.Hq + col.head) * D + quad * 8;
+  const uint16_t *qrow = a.q + (col.valid ? ((int64_t)col.row * a.Hq + col.head) * D : 0) + quad * 8;
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
-    qf[ks] = col.valid ? load16(qrow + ks * 32) : u32x4{0u, 0u, 0u, 0u};
-    ql[ks] = col.valid ? load16(qrow + a.q_lo + ks * 32) : u32x4{0u, 0u, 0u, 0u};
+    qf[ks] = load16(qrow + ks * 32);
+    ql[ks] = load16(qrow + a.q_lo + ks * 32);
+    if (!col.valid) qf[ks] = ql[ks] = u32x4{0u, 0u, 0u, 0u};
   }
 
   float m_run = NEG_SENTINEL, l_run = 0.f;
@@ -99,22 +150,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int t0 = k0 + 32 * wave; t0 < k1; t0 += 128) {
-    const uint16_t *k_lo = kb + (int64_t)(t0 + c) * D + quad * 8;
-    const uint16_t *k_hi = k_lo + 16 * D;
-    u32x4 ka[D / 32], kh[D / 32];
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      ka[ks] = load16(k_lo + ks * 32);
-      kh[ks] = load16(k_hi + ks * 32);
-    }
-    u32x2 va[NDT], vh[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const uint16_t *vr = vb + (int64_t)(dt * 16 + c) * a.S + t0 + quad * 4;
-      va[dt] = load8(vr);
-      vh[dt] = load8(vr + 16);
-    }
+  for (int t0 = t_first; t0 < k1; t0 += 128) {
+    if (t0 != t_first) load_tile(t0);
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
@@ -174,7 +211,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   __syncthreads();
   // thread -> column cc, dims jj + 16 q
   const int cc = threadIdx.x >> 4, jj = threadIdx.x & 15;
-  const Col oc = column(a, rg, g, cc);
+  const Col oc = column<PM>(a, rg, g, cc);
   float M = NEG_SENTINEL;
 #pragma unroll
   for (int w = 0; w < 4; ++w) M = fmaxf(M, lm[w][cc]);
@@ -207,27 +244,43 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 }
 
-// One block per (group, column), one thread per dim: combine the group's
-// splits in split order.
-template <int D>
-__global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a) {
-  const int gi = blockIdx.x >> 4, cc = blockIdx.x & 15;
+// One block per (group, valid column), one thread per dim: combine the
+// group's splits in split order.  The splits' (m, l) pairs are staged in
+// LDS with one load per thread; each thread's O partials are independent
+// loads, so they are in flight together.
+constexpr int MERGE_MAX_SPLITS = 1024;
+
+template <int D, int PM>
+__global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int ncols) {
+  __shared__ float sm[MERGE_MAX_SPLITS], sl[MERGE_MAX_SPLITS];
+  __shared__ float red[D / WAVE];
+  const int gi = blockIdx.x / ncols, cc = blockIdx.x - gi * ncols;
   const int g = gi % a.Hkv, rg = gi / a.Hkv;
-  const Col oc = column(a, rg, g, cc);
+  const Col oc = column<PM>(a, rg, g, cc);
   if (!oc.valid) return;
-  const int nact = (group_keys(a, rg, g) + a.kc - 1) / a.kc;
+  const int nact = min((group_keys<PM>(a, rg, g) + a.kc - 1) / a.kc, MERGE_MAX_SPLITS);
   if (nact <= 1) return;                       // written directly by attn_kernel
   const int j = threadIdx.x;
   const float *ml = a.part_ml + ((int64_t)gi * a.n_splits * 16 + cc) * 2;
   const float *po = a.part_o + ((int64_t)gi * a.n_splits * 16 + cc) * D + j;
-  float M = NEG_SENTINEL;
-#pragma unroll 8
-  for (int s = 0; s < nact; ++s) M = fmaxf(M, ml[(int64_t)s * 32]);
+  float mx = NEG_SENTINEL;
+  for (int s = j; s < nact; s += D) {
+    const float m = ml[(int64_t)s * 32], l = ml[(int64_t)s * 32 + 1];
+    sm[s] = m;
+    sl[s] = l;
+    mx = fmaxf(mx, m);
+  }
+  mx = wave_max(mx);
+  if ((j & (WAVE - 1)) == 0) red[j / WAVE] = mx;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int w = 1; w < D / WAVE; ++w) M = fmaxf(M, red[w]);
   float L = 0.f, o = 0.f;
 #pragma unroll 8
   for (int s = 0; s < nact; ++s) {
-    const float sc = exp2f(ml[(int64_t)s * 32] - M);
-    L += sc * ml[(int64_t)s * 32 + 1];
+    const float sc = exp2f(sm[s] - M);
+    L += sc * sl[s];
     o += sc * po[(int64_t)s * 16 * D];
   }
   store_out(a, ((int64_t)oc.row * a.Hq + oc.head) * D + j, o / L);
@@ -235,13 +288,30 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a) {
 
 }  // namespace
 
-hipError_t launch_attention(const AttnArgs &a, int head_dim, hipStream_t st) {
-  dim3 grid(a.n_groups * a.n_splits);
-  if (head_dim == 128) hipLaunchKernelGGL(attn_kernel<128>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(attn_kernel<64>, grid, dim3(256), 0, st, a);
+namespace {
+
+template <int D, int PM>
+hipError_t launch_pm(const AttnArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL((attn_kernel<D, PM>), dim3(a.n_groups * a.n_splits), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
-  if (head_dim == 128) hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(a.n_groups * 16), dim3(128), 0, st, a);
-  else hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(a.n_groups * 16), dim3(64), 0, st, a);
+  const int ncols = std::min(16, a.rows_per_group * a.G);  // valid columns of a group
+  hipLaunchKernelGGL((attn_merge_kernel<D, PM>), dim3(a.n_groups * ncols), dim3(D), 0, st, a, ncols);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const AttnArgs &a, hipStream_t st) {
+  switch (a.pos_mode) {
+    case 1: return launch_pm<D, 1>(a, st);
+    case 2: return launch_pm<D, 2>(a, st);
+    default: return launch_pm<D, 0>(a, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs &a, int head_dim, hipStream_t st) {
+  if (a.n_splits > MERGE_MAX_SPLITS) return hipErrorInvalidValue;
+  return head_dim == 128 ? launch_d<128>(a, st) : launch_d<64>(a, st);
 }

@@ -150,6 +150,7 @@ struct decoder {
   int64_t act_lo = 0, attn_lo = 0, q_lo = 0, h_lo = 0, hexp_lo = 0, hsh_lo = 0;  // lo-plane offsets
   // host state
   std::vector<int32_t> len;
+  std::vector<int32_t> hseq;  // host copy of the current call's row sequences
   std::vector<char> has_next;
   std::vector<std::vector<int32_t>> kv_pending;  // per seq: layers loaded with the pending len
   int layer_limit = -1;
@@ -237,6 +238,7 @@ int stage_rows(decoder *D, int rows, const int32_t *ids, const int32_t *seqs, co
   D->ring = (D->ring + 1) % STAGE_RING;
   if (D->ev_used[slot]) HIP_TRY(D, hipEventSynchronize(D->ev[slot]), "stage wait");
   int32_t *h = D->pinned + (size_t)slot * 3 * D->L.R;
+  D->hseq.assign(seqs, seqs + rows);
   for (int r = 0; r < rows; ++r) {
     h[r] = ids ? ids[r] : 0;
     h[D->L.R + r] = seqs[r];
@@ -371,6 +373,21 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
   a.part_o = D->part_o;
   a.part_ml = D->part_ml;
+  // positions as kernel arguments where the host has them in a usable form
+  if (rows_per_group == 1 && rows <= 16 && (int)D->hseq.size() == rows) {
+    a.pos_mode = 1;
+    for (int r = 0; r < rows; ++r) {
+      a.pos_arg[r] = hpos[r];
+      a.seq_arg[r] = D->hseq[r];
+    }
+  } else if (rows_per_group > 1 && (int)D->hseq.size() == rows) {
+    // a prefill chunk: one sequence, consecutive positions
+    a.pos_mode = 2;
+    a.pos0 = hpos[0];
+    a.seq0 = D->hseq[0];
+    for (int r = 1; r < rows; ++r)
+      if (hpos[r] != hpos[0] + r || D->hseq[r] != a.seq0) a.pos_mode = 0;
+  }
   hipError_t e = launch_attention(a, c.head_dim, D->stream);
   if (e != hipSuccess) return hip_fail(D, e, "attention");
   return DEC_OK;

@@ -93,6 +93,12 @@ struct AttnArgs {
   float scale_log2;        // log2(e) / sqrt(d)
   float *part_o;           // [n_groups * n_splits][16][d]
   float *part_ml;          // [n_groups * n_splits][16][2]
+  // Where the kernel takes each row's position and sequence from:
+  // 0: row_pos / row_seq in device memory; 1: pos_arg / seq_arg (one row per
+  // group, rows <= 16; no dependent load before the cache reads); 2: a chunk
+  // of one sequence, row r at position pos0 + r of sequence seq0.
+  int32_t pos_mode, pos0, seq0;
+  int32_t pos_arg[16], seq_arg[16];
 };
 hipError_t launch_attention(const AttnArgs &a, int head_dim, hipStream_t st);
 
