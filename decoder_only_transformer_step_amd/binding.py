@@ -68,6 +68,7 @@ SIGNATURES = {
     "decoder_last_error": (ctypes.c_char_p, [_P]),
     "dec_diag_gemm": (ctypes.c_int, [_P, _I32, _I32, _P, _I32, _P, _P]),
     "dec_diag_gemm_chunk": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, ctypes.c_int64, _P]),
+    "dec_diag_pack_w32": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "dec_diag_rmsnorm": (ctypes.c_int, [_P, _P, _I32, _I32, ctypes.c_double, _P, _P]),
     "dec_diag_gemv": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _P]),
     "dec_diag_moe_route": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P]),
@@ -266,13 +267,20 @@ def diag_gemm(A, W, C, stream):
     _check(lib().dec_diag_gemm(_ptr(A), M, K, _ptr(W), N, _ptr(C), ctypes.c_void_p(stream)), None, "dec_diag_gemm")
 
 
-def diag_gemm_chunk(A, W, C, ksplit, part, stream):
-    """A: bf16 [planes][M][K] (planes 1 or 2), W bf16 [N][K], C fp32 [M][N];
-    part: fp32 scratch for the split partials (or None when ksplit == 1)."""
+def diag_pack_w32(W, P, stream):
+    """W bf16 [rows][K] -> P (same size): 32-row x 16-k MFMA tiles."""
+    rows, K = W.shape
+    _check(lib().dec_diag_pack_w32(_ptr(W), rows, K, _ptr(P), ctypes.c_void_p(stream)), None, "dec_diag_pack_w32")
+
+
+def diag_gemm_chunk(A, Wp, C, ksplit, part, stream):
+    """A: bf16 [planes][M][K] (planes 1 or 2), Wp: W [N][K] packed by
+    diag_pack_w32, C fp32 [M][N]; part: fp32 scratch for the split partials
+    (or None when ksplit == 1)."""
     planes, M, K = A.shape
-    N = W.shape[0]
+    N = Wp.shape[0]
     n_part = part.numel() if part is not None else 0
-    _check(lib().dec_diag_gemm_chunk(_ptr(A), planes, M, K, _ptr(W), N, _ptr(C), ksplit,
+    _check(lib().dec_diag_gemm_chunk(_ptr(A), planes, M, K, _ptr(Wp), N, _ptr(C), ksplit,
                                      _ptr(part) if part is not None else None, n_part,
                                      ctypes.c_void_p(stream)), None, "dec_diag_gemm_chunk")
 

@@ -11,6 +11,7 @@
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
@@ -76,6 +77,14 @@ __device__ __forceinline__ f32x4 loadf4(const float *p) {
 // for j < 8, and receives D[m = 4 (l / 16) + i][n = l % 16] for i < 4.
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D[32][32] += A[32][16] B[16][32] (v_mfma_f32_32x32x16_bf16; on gfx950 it
+// runs at twice the flop rate of the 16x16x32 form).  Lane l holds
+// A[m = l % 32][k = 8 (l / 32) + e], B[k = 8 (l / 32) + e][n = l % 32], and
+// D[m = 8 (i / 4) + 4 (l / 32) + i % 4][n = l % 32] in register i.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // ------------------------------------------------------- wave reductions --
@@ -147,6 +156,7 @@ struct GemmArgs {
   const float *gamma;
   float eps;
   const uint16_t *W;      // bf16 weights [rows][K] row-major (per group: W + expert * w_group_stride)
+  const uint16_t *Wp;     // the same weights packed in 32-row x 16-k MFMA tiles (chunk kernel), or null
   int64_t w_group_stride;
   int32_t M, N, K;
   int32_t np_off;         // row offset of the second weight tile (SwiGLU: N, QKV: d / 2)

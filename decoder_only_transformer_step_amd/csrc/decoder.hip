@@ -38,7 +38,38 @@ struct Layout {
   int S, R, RL;
   int64_t seq_stride;
   size_t gpart_elems, am_n;
+  size_t packed;               // packed weight copies for the chunk kernel (or 0 bytes)
 };
+
+// Weight matrices that get a packed copy for the chunk projection kernel:
+// only when prefill chunks can exceed the small-row kernels, and only the
+// shapes the packed tiles cover.  Order within a layer: qkv, o, gate_up /
+// shared gate_up, down / shared down.
+struct PackSpec {
+  int64_t rows[4];
+  int K[4];
+};
+
+PackSpec pack_spec(const decoder_config_t *c) {
+  PackSpec p{};
+  if (c->max_chunk <= CHUNK_MIN_ROWS) return p;
+  const int d = c->head_dim, H = c->hidden, qd = c->n_heads * d, qkvr = (c->n_heads + 2 * c->n_kv_heads) * d;
+  const int I = c->n_experts > 0 ? c->shared_inter : c->ffn_inter;
+  const int64_t rows[4] = {qkvr, H, 2 * (int64_t)I, I > 0 ? H : 0};
+  const int K[4] = {H, qd, H, I};
+  for (int i = 0; i < 4; ++i) {
+    const bool ok = rows[i] > 0 && K[i] > 0 && pack_w32_fits(rows[i], K[i]);
+    p.rows[i] = ok ? rows[i] : 0;
+    p.K[i] = ok ? K[i] : 0;
+  }
+  return p;
+}
+
+size_t pack_layer_elems(const PackSpec &p) {
+  size_t n = 0;
+  for (int i = 0; i < 4; ++i) n += (size_t)p.rows[i] * p.K[i];
+  return n;
+}
 
 bool config_ok(const decoder_config_t *c) {
   if (!c) return false;
@@ -123,6 +154,9 @@ Layout make_layout(const decoder_config_t *c) {
     L.hsh = take((size_t)L.R * std::max(c->shared_inter, 1) * 4);
     L.ysh = take((size_t)L.R * H * 4);
   }
+  // packed weight copies (each matrix 256-byte aligned: element counts are
+  // multiples of 512)
+  L.packed = take(pack_layer_elems(pack_spec(c)) * 2 * c->n_layers);
   L.total = off;
   return L;
 }
@@ -133,6 +167,10 @@ struct decoder {
   decoder_config_t c;
   Layout L;
   std::vector<decoder_layer_weights_t> layers;
+  struct Packed {
+    const uint16_t *w[4];  // qkv, o, gate_up (or shared gate_up), down (or shared down); null if not packed
+  };
+  std::vector<Packed> packed;
   const uint16_t *embed = nullptr, *lm_head = nullptr;
   const float *final_norm = nullptr;
   hipStream_t stream = nullptr;
@@ -529,9 +567,11 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   q.qkv.Hq = c.n_heads;
   q.qkv.Hkv = c.n_kv_heads;
   q.qkv.d = d;
+  q.Wp = D->packed[l].w[0];
   if ((rc = proj(D, DEC_NODE_QKV, EPI_QKV, q, rows))) return rc;
   if ((rc = attention(D, l, rows, rows_per_group, max_pos, hpos))) return rc;
   GemmArgs o = dense_args(D->attn, qd, W.w_o, rows, H, qd);
+  o.Wp = D->packed[l].w[1];
   o.a_lo = D->attn_lo;
   o.C = D->x;
   o.ldc = H;
@@ -544,8 +584,10 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
     gu.Hout = D->h;
     gu.h_lo = D->h_lo;
     gu.ldc = I;
+    gu.Wp = D->packed[l].w[2];
     if ((rc = proj(D, DEC_NODE_GATE_UP, EPI_SWIGLU, gu, rows))) return rc;
     GemmArgs dn = dense_args(D->h, I, W.w_down, rows, H, I);
+    dn.Wp = D->packed[l].w[3];
     dn.a_lo = D->h_lo;
     dn.C = D->x;
     dn.ldc = H;
@@ -635,9 +677,11 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
     sg.Hout = D->hsh;
     sg.h_lo = D->hsh_lo;
     sg.ldc = Is;
+    sg.Wp = D->packed[l].w[2];
     if ((rc = proj(D, DEC_NODE_EXPERTS, EPI_SWIGLU, sg, rows))) return rc;
     GemmArgs sd = dense_args(D->hsh, Is, W.w_sh_down, rows, H, Is);
     sd.a_lo = D->hsh_lo;
+    sd.Wp = D->packed[l].w[3];
     sd.C = D->ysh;
     sd.ldc = H;
     if ((rc = proj(D, DEC_NODE_EXPERTS, EPI_STORE, sd, rows))) return rc;
@@ -821,6 +865,30 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
     D->rids = D->rids_rec = D->groups = D->pair_row = D->pair_of = nullptr;
     D->hexp = D->hsh = nullptr;
   }
+  // packed weight copies for the chunk projections, made on the stream now
+  {
+    const PackSpec ps = pack_spec(cfg);
+    uint16_t *pk = carve<uint16_t>(D, L.packed);
+    D->packed.assign(cfg->n_layers, decoder::Packed{});
+    for (int l = 0; l < cfg->n_layers; ++l) {
+      const decoder_layer_weights_t &lw = w->layers[l];
+      const uint16_t *src[4] = {
+          (const uint16_t *)lw.w_qkv, (const uint16_t *)lw.w_o,
+          (const uint16_t *)(cfg->n_experts > 0 ? lw.w_sh_gate_up : lw.w_gate_up),
+          (const uint16_t *)(cfg->n_experts > 0 ? lw.w_sh_down : lw.w_down)};
+      for (int i = 0; i < 4; ++i) {
+        D->packed[l].w[i] = nullptr;
+        if (!ps.rows[i] || !src[i]) continue;
+        if (launch_pack_w32(src[i], ps.rows[i], ps.K[i], pk, (hipStream_t)stream) != hipSuccess) {
+          D->err = "weight packing failed";
+          delete D;
+          return DEC_E_HIP;
+        }
+        D->packed[l].w[i] = pk;
+        pk += (size_t)ps.rows[i] * ps.K[i];
+      }
+    }
+  }
   D->len.assign(cfg->max_batch, 0);
   D->has_next.assign(cfg->max_batch, 0);
   D->kv_pending.assign(cfg->max_batch, std::vector<int32_t>(cfg->n_layers, -1));
@@ -998,16 +1066,22 @@ int dec_diag_gemm(const uint16_t *d_A, int32_t M, int32_t K, const uint16_t *d_W
   return launch_gemm(g, EPI_STORE, M, 1, (hipStream_t)stream) == hipSuccess ? DEC_OK : DEC_E_HIP;
 }
 
-int dec_diag_gemm_chunk(const uint16_t *d_A, int32_t planes, int32_t M, int32_t K, const uint16_t *d_W, int32_t N,
+int dec_diag_pack_w32(const uint16_t *d_W, int32_t rows, int32_t K, uint16_t *d_P, void *stream) {
+  if (!d_W || !d_P || !pack_w32_fits(rows, K)) return DEC_E_INVALID;
+  return launch_pack_w32(d_W, rows, K, d_P, (hipStream_t)stream) == hipSuccess ? DEC_OK : DEC_E_HIP;
+}
+
+int dec_diag_gemm_chunk(const uint16_t *d_A, int32_t planes, int32_t M, int32_t K, const uint16_t *d_Wp, int32_t N,
                         float *d_C, int32_t ksplit, float *d_part, int64_t part_elems, void *stream) {
-  if (!d_A || !d_W || !d_C || (planes != 1 && planes != 2) || M < 1 || M > 128 || N < 1 || K < 8 || K % 8 ||
+  if (!d_A || !d_Wp || !d_C || (planes != 1 && planes != 2) || M < 1 || M > 128 || N < 1 || K < 16 || K % 16 ||
       ksplit < 1 || ksplit > 64)
     return DEC_E_INVALID;
   GemmArgs g{};
   g.A = d_A;
   g.a_lo = planes == 2 ? (int64_t)M * K : 0;
   g.lda = K;
-  g.W = d_W;
+  g.W = d_Wp;
+  g.Wp = d_Wp;
   g.M = M;
   g.N = N;
   g.K = K;

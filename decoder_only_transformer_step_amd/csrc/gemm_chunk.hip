@@ -4,29 +4,30 @@
 // weights are row-major [out][in]).
 //
 // gfx950 design.  A chunk projection streams each weight matrix once and
-// does 2 M flops per weight element, so with M = 128 it sits on the HBM /
-// MFMA ridge: the kernel must keep the weight stream at full HBM rate while
-// the matrix cores do the arithmetic.
-//  * Block = 4 waves.  Each wave owns 4 weight subtiles of 16 rows (64 rows;
-//    for the paired epilogues two tiles and their partner rows) for all M
-//    rows, so a weight fragment feeds MT MFMAs and the whole output tile of
-//    the wave stays in its accumulators (MT x 4 16x16 fp32 tiles).
-//  * Weights go straight from HBM into MFMA B-operand registers.  In a
-//    64-wide k step lane l loads the 32 contiguous bytes at k0 + 16 (l / 16)
-//    of each of its rows, so the 4 lane groups read each row's full 128-byte
-//    line; MFMA j (0, 1) takes the 8 elements at k0 + 16 (l / 16) + 8 j.
-//    The next step's weights are in flight while the current step computes
-//    (loads are unconditional, past the k range they read zeros through the
-//    buffer bound, so the compiler's wait counts stay exact).
+// does 2 M flops per weight element (4 M with the split-bf16 activations),
+// so with M = 128 it sits near the HBM / MFMA ridge.
+//  * MFMA v_mfma_f32_32x32x16_bf16: on gfx950 it has twice the flop rate of
+//    the 16x16x32 form.
+//  * Weights are read from a packed copy made once at init: 32-row x 16-k
+//    tiles of 1 KB in MFMA lane order, so every weight load instruction of a
+//    wave reads one contiguous kilobyte (coalesced, one page), straight into
+//    the B-operand registers.  Row-major fragments would touch 32 rows per
+//    instruction and stall the L1 TLB and the address path.
+//  * Block = 4 waves over 64 activation rows x 256 weight rows; a wave owns
+//    2 weight tiles of 32 rows (for the paired epilogues one tile and its
+//    partner rows) for all 64 rows, accumulating 2 x 2 32x32 fp32 tiles.
 //  * Activations (split bf16: hi and lo planes, two MFMAs per product) are
-//    staged per k step into LDS by the whole block, in MFMA fragment order
-//    with the same k mapping, so each fragment read is one conflict-free
-//    64 x 16-byte ds_read.  Two LDS stages: the next step's activations are
-//    loaded from L2 during the current step's MFMAs.
-//  * Split-K across blocks (a block = one 256-row weight tile and one k
-//    range) fills the 256 compute units when a matrix has few tiles;
-//    partials go to Cpart and gemm_reduce sums them in fixed split order.
-//    Without a split the epilogue runs straight from the accumulators.
+//    staged per 64-wide k step into LDS with coalesced loads (8 threads per
+//    128-byte row piece), in MFMA fragment order with an XOR swizzle that
+//    keeps both the stores and the fragment reads free of bank conflicts.
+//  * Two LDS stages and two weight register buffers: the next step's loads
+//    are in flight during the current step's MFMAs.  Loads are
+//    unconditional (masked lanes read a zero page), so the compiler's wait
+//    counts stay exact.
+//  * Split-K across blocks fills the compute units when a matrix has few
+//    tiles; partials go to Cpart and gemm_reduce sums them in fixed split
+//    order.  Without a split the epilogue runs straight from the
+//    accumulators.
 #include <algorithm>
 
 #include "common.h"
@@ -36,89 +37,103 @@
 namespace {
 
 constexpr int CK_WAVES = 4;  // waves per block
-constexpr int CK_SUB = 4;    // 16-row weight subtiles per wave
-constexpr int CK_STEP = 64;  // k per pipeline step
-constexpr int CK_ROWS = 64;  // activation rows per block (MT <= 4)
+constexpr int CK_NS = 2;     // 32-row weight tiles per wave
+constexpr int CK_STEP = 64;  // k per pipeline step (4 MFMA k groups of 16)
+constexpr int CK_ROWS = 64;  // activation rows per block
 constexpr int CK_XCDS = 8;   // blocks are dispatched round-robin over 8 XCDs
 
+// 1 KB of zeros: masked-off lanes load from here (16 bytes each), so loads
+// need no value select, which would force a wait right after the load.
+__device__ u32x4 ck_zero[64];  // never written: zero-initialised
+
+// Activation stage = MFMA A fragments (t, s, plane) of 64 lanes x 16 bytes:
+// 32 rows x 16 k, fragment f = (t * 4 + s) * PL + plane at LDS slots f * 64.
+// Lane l of a fragment holds row 32 t + l % 32 at k0 + 16 s + 8 g
+// (g = l / 32), kept in slot a_swz(l % 32, g, s).
 template <int MT, bool SPLIT>
-struct Stage {
-  static constexpr int PLANES = SPLIT ? 2 : 1;
-  static constexpr int PIECES = MT * 16 * 8 * PLANES;  // 16-byte pieces per stage
+struct AStage {
+  static constexpr int PL = SPLIT ? 2 : 1;
+  static constexpr int PIECES = MT * 32 * 8 * PL;  // 16-byte pieces per stage
   static constexpr int PER_THREAD = (PIECES + CK_WAVES * WAVE - 1) / (CK_WAVES * WAVE);
+  static constexpr int NFRAG = MT * 4 * PL;
 };
 
-// Global -> registers: this thread's pieces of the activation stage at k0
-// (rows past M and k past K read zeros through the buffer bound `oob`).
+__device__ __forceinline__ int a_swz(int r32, int g, int s) { return (r32 ^ (2 * (2 * s + g))) + 32 * g; }
+
+// Global -> registers, coalesced: piece e = (plane, row r, 16-byte chunk c8
+// of the step's 128 bytes); rows past `rows` and k past kend read zeros.
 template <int MT, bool SPLIT>
-__device__ __forceinline__ void a_load(__amdgpu_buffer_rsrc_t ra, uint32_t oob, const GemmArgs &g, int rows, int k0,
-                                       int kend, u32x4 (&ar)[Stage<MT, SPLIT>::PER_THREAD]) {
-  constexpr int PER_PLANE = MT * 128;
+__device__ __forceinline__ void a_load(const uint16_t *abase, const GemmArgs &g, int rows, int k0, int kend,
+                                       u32x4 (&ar)[AStage<MT, SPLIT>::PER_THREAD]) {
+  constexpr int PER_PLANE = MT * 256, PIECES = AStage<MT, SPLIT>::PIECES;
 #pragma unroll
-  for (int i = 0; i < Stage<MT, SPLIT>::PER_THREAD; ++i) {
+  for (int i = 0; i < AStage<MT, SPLIT>::PER_THREAD; ++i) {
     const int e = threadIdx.x + i * CK_WAVES * WAVE;
     const int plane = e / PER_PLANE, rem = e - plane * PER_PLANE;
     const int r = rem >> 3, k = k0 + (rem & 7) * 8;
-    const bool ok = (Stage<MT, SPLIT>::PIECES % (CK_WAVES * WAVE) == 0 || e < Stage<MT, SPLIT>::PIECES) && r < rows && k < kend;
-    const uint32_t off = (uint32_t)((plane * g.a_lo + (int64_t)r * g.lda + k) * 2);
-    ar[i] = buf_load16(ra, ok ? off : oob);
+    const bool ok = (PIECES % (CK_WAVES * WAVE) == 0 || e < PIECES) && r < rows && k < kend;
+    ar[i] = load16(ok ? static_cast<const void *>(abase + plane * g.a_lo + (int64_t)r * g.lda + k)
+                      : static_cast<const void *>(ck_zero + (threadIdx.x & 63)));
   }
 }
 
-// Registers -> LDS in fragment order: piece (row r, k offset kk, plane) goes
-// to fragment (t = r / 16, j = (kk / 8) & 1, plane), lane r % 16 + 16 (kk / 16).
+// Registers -> LDS: chunk c8 of row r is k group g = c8 % 2 of MFMA step
+// s = c8 / 2.  The swizzle spreads the 16 lanes of each store cycle (two
+// rows x eight chunks) over all 16 bank groups.
 template <int MT, bool SPLIT>
-__device__ __forceinline__ void a_store(u32x4 *dst, const u32x4 (&ar)[Stage<MT, SPLIT>::PER_THREAD]) {
-  constexpr int PER_PLANE = MT * 128, PL = Stage<MT, SPLIT>::PLANES;
+__device__ __forceinline__ void a_store(u32x4 *dst, const u32x4 (&ar)[AStage<MT, SPLIT>::PER_THREAD]) {
+  constexpr int PER_PLANE = MT * 256, PIECES = AStage<MT, SPLIT>::PIECES, PL = AStage<MT, SPLIT>::PL;
 #pragma unroll
-  for (int i = 0; i < Stage<MT, SPLIT>::PER_THREAD; ++i) {
+  for (int i = 0; i < AStage<MT, SPLIT>::PER_THREAD; ++i) {
     const int e = threadIdx.x + i * CK_WAVES * WAVE;
     const int plane = e / PER_PLANE, rem = e - plane * PER_PLANE;
-    const int r = rem >> 3, kk = (rem & 7) * 8;
-    const int t = r >> 4, j = (kk >> 3) & 1, ln = (r & 15) + 16 * (kk >> 4);
-    if (Stage<MT, SPLIT>::PIECES % (CK_WAVES * WAVE) == 0 || e < Stage<MT, SPLIT>::PIECES)
-      dst[((t * 2 + j) * PL + plane) * WAVE + ln] = ar[i];
+    const int r = rem >> 3, c8 = rem & 7;
+    const int t = r >> 5, s = c8 >> 1, gk = c8 & 1;
+    if (PIECES % (CK_WAVES * WAVE) == 0 || e < PIECES)
+      dst[((t * 4 + s) * PL + plane) * WAVE + a_swz(r & 31, gk, s)] = ar[i];
   }
 }
 
-// This wave's weight fragments of the k step at k0: subtile p, half j
-// (byte offsets wo[p] of the lane's row and k group; invalid rows carry `oob`).
-template <int NSUB>
-__device__ __forceinline__ void w_load(__amdgpu_buffer_rsrc_t rw, uint32_t oob, const uint32_t (&wo)[NSUB], int k0,
-                                       int K, int q, u32x4 (&w)[NSUB][2]) {
+// This wave's weight fragments of the step at k0: tile p, k group s (one
+// contiguous kilobyte of the packed copy per load).
+__device__ __forceinline__ void w_load(const uint16_t *const (&wp)[CK_NS], const bool (&wv)[CK_NS], int k0,
+                                       int kend, u32x4 (&w)[CK_NS][4]) {
+  const int lane = threadIdx.x & (WAVE - 1);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const bool kok = k0 + 16 * q + 8 * j < K;
+  for (int s = 0; s < 4; ++s) {
+    const bool kok = k0 + 16 * s < kend;
 #pragma unroll
-    for (int p = 0; p < NSUB; ++p) w[p][j] = buf_load16(rw, (kok && wo[p] != oob) ? wo[p] + (k0 + 8 * j) * 2 : oob);
+    for (int p = 0; p < CK_NS; ++p)
+      w[p][s] = load16(kok && wv[p] ? static_cast<const void *>(wp[p] + (k0 / 16 + s) * 512)
+                                    : static_cast<const void *>(ck_zero + lane));
   }
 }
 
-// One k step: for each (j, t) the A fragments (hi, lo) from LDS feed
-// 4 (x2) MFMAs; the next pair's LDS reads are issued before the current
-// MFMAs, and scheduling barriers keep the compiler from hoisting every read
-// of the step (which would cost a register per read).
+// One k step: for each (s, t) the A fragments (hi, lo) from LDS feed
+// CK_NS (x2) MFMAs; the next pair's LDS reads are issued before the
+// current MFMAs, and scheduling barriers keep the compiler from hoisting
+// every read of the step.
 template <int MT, bool SPLIT>
-__device__ __forceinline__ void mma_step(const u32x4 *src, const u32x4 (&w)[CK_SUB][2], int lane,
-                                         f32x4 (&acc)[MT][CK_SUB]) {
-  constexpr int PL = Stage<MT, SPLIT>::PLANES;
+__device__ __forceinline__ void mma_step(const u32x4 *src, const u32x4 (&w)[CK_NS][4], const int (&sw)[4],
+                                         f32x16 (&acc)[MT][CK_NS]) {
+  constexpr int PL = AStage<MT, SPLIT>::PL;
   u32x4 cur[PL], nxt[PL];
 #pragma unroll
-  for (int pl = 0; pl < PL; ++pl) cur[pl] = src[pl * WAVE + lane];
+  for (int pl = 0; pl < PL; ++pl) cur[pl] = src[pl * WAVE + sw[0]];
 #pragma unroll
-  for (int idx = 0; idx < 2 * MT; ++idx) {
-    const int j = idx / MT, t = idx % MT;  // fragment (t, j) sits at (t * 2 + j) * PL
-    if (idx + 1 < 2 * MT) {
-      const int j1 = (idx + 1) / MT, t1 = (idx + 1) % MT;
+  for (int idx = 0; idx < 4 * MT; ++idx) {
+    const int s = idx / MT, t = idx % MT;
+    if (idx + 1 < 4 * MT) {
+      const int s1 = (idx + 1) / MT, t1 = (idx + 1) % MT;
 #pragma unroll
-      for (int pl = 0; pl < PL; ++pl) nxt[pl] = src[((t1 * 2 + j1) * PL + pl) * WAVE + lane];
+      for (int pl = 0; pl < PL; ++pl) nxt[pl] = src[((t1 * 4 + s1) * PL + pl) * WAVE + sw[s1]];
     }
 #pragma unroll
     for (int pl = 0; pl < PL; ++pl)
 #pragma unroll
-      for (int p = 0; p < CK_SUB; ++p) acc[t][p] = mfma16x16x32(as_bf16x8(cur[pl]), as_bf16x8(w[p][j]), acc[t][p]);
+      for (int p = 0; p < CK_NS; ++p) acc[t][p] = mfma32x32x16(as_bf16x8(cur[pl]), as_bf16x8(w[p][s]), acc[t][p]);
     __builtin_amdgcn_sched_barrier(0);
-    if (idx + 1 < 2 * MT) {
+    if (idx + 1 < 4 * MT) {
 #pragma unroll
       for (int pl = 0; pl < PL; ++pl) cur[pl] = nxt[pl];
     }
@@ -132,14 +147,13 @@ __device__ __forceinline__ void mma_step(const u32x4 *src, const u32x4 (&w)[CK_S
 template <int MT, int EPI, bool SPLIT>
 __global__ __launch_bounds__(CK_WAVES * WAVE, 2) void gemm_chunk_kernel(GemmArgs g, int ntiles16, int mblocks) {
   constexpr int NP = paired<EPI>();
-  constexpr int LT = CK_SUB / NP;  // logical 16-row tiles per wave
-  constexpr int PIECES = Stage<MT, SPLIT>::PIECES;
-  __shared__ u32x4 a_s[2][PIECES];
+  constexpr int LT = CK_NS / NP;  // logical 32-row tiles per wave
+  __shared__ u32x4 a_s[2][AStage<MT, SPLIT>::NFRAG * WAVE];
 
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-  const int c = lane & 15, q = lane >> 4;
   const int K = g.K;
-  const int nbt = (ntiles16 + CK_WAVES * LT - 1) / (CK_WAVES * LT);
+  const int ntiles32 = ntiles16 / 2;
+  const int nbt = (ntiles32 + CK_WAVES * LT - 1) / (CK_WAVES * LT);
   const int u = (blockIdx.x / (CK_XCDS * mblocks)) * CK_XCDS + blockIdx.x % CK_XCDS;
   const int mb = (blockIdx.x / CK_XCDS) % mblocks;
   if (u >= nbt * g.ksplit) return;
@@ -148,73 +162,78 @@ __global__ __launch_bounds__(CK_WAVES * WAVE, 2) void gemm_chunk_kernel(GemmArgs
   const int nsteps = (K + CK_STEP - 1) / CK_STEP;
   const int per = (nsteps + g.ksplit - 1) / g.ksplit;
   const int s0 = min(nsteps, z * per), s1 = min(nsteps, s0 + per);
+  const uint16_t *abase = g.A + (int64_t)row0 * g.lda;
 
-  // buffer resources: weights (all rows of the matrix) and the activation planes
-  const int64_t wrows = EPI == EPI_SWIGLU ? 2 * (int64_t)g.N : g.N;
-  const uint32_t w_oob = (uint32_t)(wrows * K * 2);
-  const __amdgpu_buffer_rsrc_t rw = buf_rsrc(g.W, w_oob);
-  const uint32_t a_oob = (uint32_t)(((SPLIT ? g.a_lo : 0) + (int64_t)g.M * g.lda) * 2);
-  const __amdgpu_buffer_rsrc_t ra = buf_rsrc(g.A + (int64_t)row0 * g.lda, a_oob);
-
-  // this wave's weight rows: subtile p = lt * NP + half
-  uint32_t wo[CK_SUB];
-  int tb[LT];
+  // this wave's 32-row tiles T (16-row logical tiles 2T, 2T + 1): weight
+  // tile p = lt * NP + half, in the packed copy at row tile r0 / 32
+  const uint16_t *wp[CK_NS];
+  bool wv[CK_NS];
+  int tt[LT];
 #pragma unroll
   for (int lt = 0; lt < LT; ++lt) {
-    const int b = (bt * CK_WAVES + wave) * LT + lt;
-    tb[lt] = b;
-    const int n = b < ntiles16 ? tile_n0<EPI>(g, b) + c : 0;
-    const bool ok = b < ntiles16 && (EPI == EPI_QKV || n < g.N);
+    const int T = (bt * CK_WAVES + wave) * LT + lt;
+    tt[lt] = T;
+    const bool ok = T < ntiles32;
+    const int r0 = ok ? tile_n0<EPI>(g, 2 * T) : 0;
 #pragma unroll
-    for (int h = 0; h < NP; ++h)
-      wo[lt * NP + h] = ok ? (uint32_t)(((int64_t)(n + h * g.np_off) * K + 16 * q) * 2) : w_oob;
+    for (int h = 0; h < NP; ++h) {
+      wv[lt * NP + h] = ok;
+      wp[lt * NP + h] = g.Wp + (ok ? (int64_t)((r0 + h * g.np_off) / 32) * (K / 16) * 512 : 0) + lane * 8;
+    }
   }
+  int sw[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) sw[s] = a_swz(lane & 31, lane >> 5, s);
 
-  f32x4 acc[MT][CK_SUB];
+  f32x16 acc[MT][CK_NS];
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int p = 0; p < CK_SUB; ++p) acc[t][p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < CK_NS; ++p)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[t][p][i] = 0.f;
 
-  u32x4 w0[CK_SUB][2], w1[CK_SUB][2];
-  u32x4 ar[Stage<MT, SPLIT>::PER_THREAD];
+  u32x4 w0[CK_NS][4], w1[CK_NS][4];
+  u32x4 ar[AStage<MT, SPLIT>::PER_THREAD];
   const int kend = min(K, s1 * CK_STEP);
   if (s0 < s1) {
-    a_load<MT, SPLIT>(ra, a_oob, g, rows, s0 * CK_STEP, kend, ar);
-    w_load<CK_SUB>(rw, w_oob, wo, s0 * CK_STEP, kend, q, w0);
+    a_load<MT, SPLIT>(abase, g, rows, s0 * CK_STEP, kend, ar);
+    w_load(wp, wv, s0 * CK_STEP, kend, w0);
     a_store<MT, SPLIT>(a_s[0], ar);
   }
   __syncthreads();
   // Two steps per iteration, activation loads first (the wait before their
-  // LDS store then leaves the newer weight loads in flight).  No conditional
-  // loads: steps at or past s1 read zeros (k >= kend), so an odd step count
-  // adds one zero step.
+  // LDS store then leaves the newer weight loads in flight).  Steps at or
+  // past s1 read zeros (k >= kend), so an odd step count adds one zero step.
   for (int s = s0; s < s1; s += 2) {
-    a_load<MT, SPLIT>(ra, a_oob, g, rows, (s + 1) * CK_STEP, kend, ar);
-    w_load<CK_SUB>(rw, w_oob, wo, (s + 1) * CK_STEP, kend, q, w1);
-    mma_step<MT, SPLIT>(a_s[0], w0, lane, acc);
+    a_load<MT, SPLIT>(abase, g, rows, (s + 1) * CK_STEP, kend, ar);
+    w_load(wp, wv, (s + 1) * CK_STEP, kend, w1);
+    mma_step<MT, SPLIT>(a_s[0], w0, sw, acc);
     a_store<MT, SPLIT>(a_s[1], ar);
     __syncthreads();
-    a_load<MT, SPLIT>(ra, a_oob, g, rows, (s + 2) * CK_STEP, kend, ar);
-    w_load<CK_SUB>(rw, w_oob, wo, (s + 2) * CK_STEP, kend, q, w0);
-    mma_step<MT, SPLIT>(a_s[1], w1, lane, acc);
+    a_load<MT, SPLIT>(abase, g, rows, (s + 2) * CK_STEP, kend, ar);
+    w_load(wp, wv, (s + 2) * CK_STEP, kend, w0);
+    mma_step<MT, SPLIT>(a_s[1], w1, sw, acc);
     a_store<MT, SPLIT>(a_s[0], ar);
     __syncthreads();
   }
 
-  // epilogue: lane (c, q) holds rows 16 t + 4 q + i, column c of each subtile
+  // epilogue: lane l holds rows 32 t + 8 (i / 4) + 4 (l / 32) + i % 4 of
+  // column l % 32 of each tile, i.e. logical 16-row tile 2 T + (l % 32) / 16,
+  // column c = l % 16
   const int64_t np_cols = (int64_t)ntiles16 * 16;
+  const int c = lane & 15;
 #pragma unroll
   for (int lt = 0; lt < LT; ++lt) {
-    const int b = tb[lt];
-    const bool bok = b < ntiles16;
+    const int b = 2 * tt[lt] + ((lane >> 4) & 1);
+    const bool bok = tt[lt] < ntiles32;
     const int n = bok ? tile_n0<EPI>(g, b) + c : 0;
     const bool nok = bok && (EPI == EPI_QKV || n < g.N);
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * t + 4 * q + i;
+      for (int i = 0; i < 16; ++i) {
+        const int m = 32 * t + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
         const float v0 = acc[t][lt * NP][i], v1 = acc[t][lt * NP + NP - 1][i];
         const bool ok = nok && m < rows;
         if (g.ksplit > 1) {
@@ -226,8 +245,8 @@ __global__ __launch_bounds__(CK_WAVES * WAVE, 2) void gemm_chunk_kernel(GemmArgs
         } else {
           if (ok) epi_apply<EPI>(g, row0 + m, n, v0, v1);
           if (EPI == EPI_LOGITS) {
-            // best (value, index) of this tile's 16 columns for row m: the
-            // columns of a row sit in the 16 lanes that share q
+            // best (value, index) of this logical tile's 16 columns for row
+            // m: they sit in the 16 lanes that share l / 16
             float bv = ok ? v0 : -INFINITY;
             int bi = ok ? n : 0x7fffffff;
 #pragma unroll
@@ -263,29 +282,50 @@ hipError_t launch_mt(const GemmArgs &g, int ntiles16, int blocks, int mblocks, h
 
 template <int EPI>
 hipError_t launch_epi(const GemmArgs &g, int ntiles16, int blocks, int mblocks, hipStream_t st) {
-  const int mt = gemm_mtiles(std::min(g.M, CK_ROWS));
-  switch (mt) {
-    case 1: return launch_mt<1, EPI>(g, ntiles16, blocks, mblocks, st);
-    case 2: return launch_mt<2, EPI>(g, ntiles16, blocks, mblocks, st);
-    default: return launch_mt<4, EPI>(g, ntiles16, blocks, mblocks, st);
+  if (std::min(g.M, CK_ROWS) <= 32) return launch_mt<1, EPI>(g, ntiles16, blocks, mblocks, st);
+  return launch_mt<2, EPI>(g, ntiles16, blocks, mblocks, st);
+}
+
+// P[((nt * K / 16 + kt) * 64 + l) * 8 + e] = W[32 nt + l % 32][16 kt + 8 (l / 32) + e]:
+// one thread per 16-byte piece; the stores are coalesced.
+__global__ __launch_bounds__(256) void pack_w32_kernel(const uint16_t *W, int64_t pieces, int K, uint16_t *P) {
+  const int kt16 = K / 16;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < pieces; i += (int64_t)gridDim.x * 256) {
+    const int l = (int)(i & 63);
+    const int64_t tile = i >> 6;
+    const int64_t nt = tile / kt16;
+    const int kt = (int)(tile - nt * kt16);
+    const int64_t row = 32 * nt + (l & 31);
+    const u32x4 v = load16(W + row * K + 16 * kt + 8 * (l >> 5));
+    *reinterpret_cast<u32x4 *>(P + i * 8) = v;
   }
 }
 
 }  // namespace
 
+bool pack_w32_fits(int64_t rows, int K) { return rows > 0 && rows % 32 == 0 && K > 0 && K % 16 == 0; }
+
+hipError_t launch_pack_w32(const uint16_t *W, int64_t rows, int K, uint16_t *P, hipStream_t st) {
+  if (!pack_w32_fits(rows, K)) return hipErrorInvalidValue;
+  const int64_t pieces = rows * K / 8;
+  const int blocks = (int)std::min<int64_t>((pieces + 255) / 256, 65536);
+  hipLaunchKernelGGL(pack_w32_kernel, dim3(blocks), dim3(256), 0, st, W, pieces, K, P);
+  return hipGetLastError();
+}
+
 int gemm_chunk_tiles(const GemmArgs &g, int epi) {
-  const int lt = (epi == EPI_SWIGLU || epi == EPI_QKV) ? CK_SUB / 2 : CK_SUB;
-  return (gemm_ntiles(g, epi) + CK_WAVES * lt - 1) / (CK_WAVES * lt);
+  const int lt = (epi == EPI_SWIGLU || epi == EPI_QKV) ? CK_NS / 2 : CK_NS;
+  return (gemm_ntiles(g, epi) / 2 + CK_WAVES * lt - 1) / (CK_WAVES * lt);
 }
 
 int gemm_chunk_mblocks(int rows) { return (rows + CK_ROWS - 1) / CK_ROWS; }
 
 bool gemm_chunk_fits(const GemmArgs &g, int epi) {
-  // byte offsets into the weight matrix and the activation planes are 32-bit
+  // the packed copy covers every weight row in 32-row tiles
   const int64_t wrows = epi == EPI_SWIGLU ? 2 * (int64_t)g.N : g.N;
-  const int64_t a_elems = (g.a_lo ? g.a_lo : 0) + (int64_t)g.M * g.lda;
-  return g.M >= 1 && g.M <= 128 && g.A != nullptr && g.x == nullptr && g.n_groups == nullptr && g.a_rows == nullptr &&
-         g.K % 8 == 0 && wrows * g.K * 2 < (int64_t)UINT32_MAX - 64 && a_elems * 2 < (int64_t)UINT32_MAX - 64;
+  return g.Wp != nullptr && g.M >= 2 && g.M <= 128 && g.A != nullptr && g.x == nullptr && g.n_groups == nullptr &&
+         g.a_rows == nullptr && pack_w32_fits(wrows, g.K) && gemm_ntiles(g, epi) % 2 == 0 &&
+         (epi == EPI_QKV ? g.np_off % 32 == 0 : g.N % 32 == 0);
 }
 
 hipError_t launch_gemm_chunk(const GemmArgs &g, int epi, hipStream_t st) {

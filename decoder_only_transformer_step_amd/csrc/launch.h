@@ -26,6 +26,10 @@ hipError_t launch_gemm_reduce(const GemmArgs &g, int epi, int ntiles, hipStream_
 // of 256 weight rows (128 row pairs for the paired epilogues) times g.ksplit
 // k ranges.
 bool gemm_chunk_fits(const GemmArgs &g, int epi);
+// Packed weight copy for the chunk kernel: P[((nt * K / 16 + kt) * 64 + l) * 8 + e]
+// = W[32 nt + l % 32][16 kt + 8 (l / 32) + e] (rows % 32 == 0, K % 16 == 0).
+bool pack_w32_fits(int64_t rows, int K);
+hipError_t launch_pack_w32(const uint16_t *W, int64_t rows, int K, uint16_t *P, hipStream_t st);
 int gemm_chunk_tiles(const GemmArgs &g, int epi);
 int gemm_chunk_mblocks(int rows);
 hipError_t launch_gemm_chunk(const GemmArgs &g, int epi, hipStream_t st);

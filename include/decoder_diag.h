@@ -25,14 +25,21 @@ extern "C" {
 int dec_diag_gemm(const uint16_t *d_A, int32_t M, int32_t K, const uint16_t *d_W, int32_t N,
                   float *d_C, void *stream);
 
+/* Packed copy of a bf16 weight matrix W [rows][K] for the chunk projection
+ * kernel: P[((nt * K / 16 + kt) * 64 + l) * 8 + e] = W[32 nt + l % 32][16 kt + 8 (l / 32) + e]
+ * (32-row x 16-k tiles of 1 KB in MFMA lane order).  rows % 32 == 0,
+ * K % 16 == 0; P holds rows * K bf16 values.  DEC_E_INVALID otherwise. */
+int dec_diag_pack_w32(const uint16_t *d_W, int32_t rows, int32_t K, uint16_t *d_P, void *stream);
+
 /* C = A W^T with the chunk projection kernel (prefill chunks; engine.zig
  * Engine.prefill: a chunk of token columns shares one pass over the
  * weights).  A bf16 [planes][M][K]: planes 1 = plain bf16, 2 = hi plane then
- * lo plane (the activation is their sum); W bf16 [N][K]; C fp32 [M][N].
- * 1 <= M <= 128, K % 8 == 0.  ksplit > 1 splits K over blocks; the fp32
- * partials need part_elems >= ksplit * M * 16 * ceil(N / 16) floats at
- * d_part, reduced in fixed split order.  DEC_E_INVALID on bad sizes. */
-int dec_diag_gemm_chunk(const uint16_t *d_A, int32_t planes, int32_t M, int32_t K, const uint16_t *d_W,
+ * lo plane (the activation is their sum); d_Wp = W [N][K] packed by
+ * dec_diag_pack_w32; C fp32 [M][N].  2 <= M <= 128, N % 32 == 0,
+ * K % 16 == 0.  ksplit > 1 splits K over blocks; the fp32 partials need
+ * part_elems >= ksplit * M * N floats at d_part, reduced in fixed split
+ * order.  DEC_E_INVALID on bad sizes. */
+int dec_diag_gemm_chunk(const uint16_t *d_A, int32_t planes, int32_t M, int32_t K, const uint16_t *d_Wp,
                         int32_t N, float *d_C, int32_t ksplit, float *d_part, int64_t part_elems,
                         void *stream);
 

@@ -44,15 +44,15 @@ def test_projection_kernel_matches_numpy(M, N, K):
     assert np.all(np.abs(got - want) <= 1e-6 * K * scale + 1e-30)
 
 
-@pytest.mark.parametrize("M,N,K,ksplit,planes", [(17, 64, 64, 1, 1), (37, 100, 688, 1, 2), (64, 256, 4096, 1, 2),
-                                                 (100, 48, 576, 3, 2), (128, 512, 4096, 4, 2),
-                                                 (128, 272, 1536, 1, 1), (65, 16, 256, 7, 2)])
+@pytest.mark.parametrize("M,N,K,ksplit,planes", [(17, 64, 64, 1, 1), (37, 96, 688, 1, 2), (64, 256, 4096, 1, 2),
+                                                 (100, 64, 576, 3, 2), (128, 512, 4096, 4, 2),
+                                                 (128, 288, 1536, 1, 1), (65, 32, 256, 7, 2), (2, 32, 16, 1, 2)])
 def test_chunk_projection_kernel_matches_oracle(M, N, K, ksplit, planes):
-    """The prefill chunk kernel: ragged row counts (several 64-row blocks and
-    a tail), N not a multiple of the 256-row block tile, K not a multiple of
-    the 64-wide step, split K (including empty splits), plain and split-bf16
-    activations (the product uses hi + lo)."""
-    from decoder_only_transformer_step_amd.binding import diag_gemm_chunk
+    """The prefill chunk kernel on packed weights: ragged row counts (several
+    64-row blocks and a tail), N not a multiple of the 256-row block tile, K
+    not a multiple of the 64-wide step, split K (including empty splits),
+    plain and split-bf16 activations (the product uses hi + lo)."""
+    from decoder_only_transformer_step_amd.binding import diag_gemm_chunk, diag_pack_w32
     log("gemm_chunk", M, N, K, ksplit, planes)
     hi = synth.normal_bf16(M * K, 31 + M, 1.0)
     lo = synth.normal_bf16(M * K, 37 + M, 2.0 ** -9)
@@ -60,10 +60,11 @@ def test_chunk_projection_kernel_matches_oracle(M, N, K, ksplit, planes):
     W = synth.normal_bf16(N * K, 41 + N, 0.02)
     dA = torch.from_numpy(A.view(np.int16)).cuda().view(planes, M, K)
     dW = torch.from_numpy(W.view(np.int16)).cuda().view(N, K)
+    dP = torch.empty_like(dW)
+    diag_pack_w32(dW, dP, torch.cuda.current_stream().cuda_stream)
     dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
-    part = torch.full((ksplit * M * 16 * ((N + 15) // 16),), float("nan"), dtype=torch.float32, device="cuda") \
-        if ksplit > 1 else None
-    diag_gemm_chunk(dA, dW, dC, ksplit, part, torch.cuda.current_stream().cuda_stream)
+    part = torch.full((ksplit * M * N,), float("nan"), dtype=torch.float32, device="cuda") if ksplit > 1 else None
+    diag_gemm_chunk(dA, dP, dC, ksplit, part, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     got = dC.cpu().numpy().astype(np.float64)
     a = sum(bits_of(A[p]).astype(np.float64).reshape(M, K) for p in range(planes))
