@@ -426,7 +426,8 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
     for (int r = 1; r < rows; ++r)
       if (hpos[r] != hpos[0] + r || D->hseq[r] != a.seq0) a.pos_mode = 0;
   }
-  hipError_t e = launch_attention(a, c.head_dim, D->stream);
+  hipError_t e = attention_chunk_fits(a, c.head_dim) ? launch_attention_chunk(a, c.head_dim, D->stream)
+                                                     : launch_attention(a, c.head_dim, D->stream);
   if (e != hipSuccess) return hip_fail(D, e, "attention");
   return DEC_OK;
 }

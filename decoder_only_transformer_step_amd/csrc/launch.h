@@ -105,6 +105,11 @@ struct AttnArgs {
   int32_t pos_arg[16], seq_arg[16];
 };
 hipError_t launch_attention(const AttnArgs &a, int head_dim, hipStream_t st);
+// Prefill-chunk attention (pos_mode 2, split-bf16 output, d = 64 or 128);
+// sets its own groups and splits.  Uses part_o / part_ml like the general
+// kernel (at most ATTN_MAX_TASKS * 16 columns of partials).
+bool attention_chunk_fits(const AttnArgs &a, int head_dim);
+hipError_t launch_attention_chunk(const AttnArgs &a, int head_dim, hipStream_t st);
 
 // ------------------------------------------------------ row-wise kernels --
 // x[r][:] = E[tok(r)][:], tok(r) = next_token[row_seq[r]] if use_next else ids[r]
