@@ -174,6 +174,12 @@ struct GemmArgs {
   // split-K: blockIdx.z = split; partial sums go to Cpart[split][M][np * N]
   float *Cpart;
   int32_t ksplit;
+  // EPI_ADD with split K: the reduce also writes RMSNorm(new x; norm_gamma)
+  // as split bf16 [M][N] at norm_out (lo plane at + norm_lo), if set
+  const float *norm_gamma;
+  float norm_eps;
+  uint16_t *norm_out;
+  int64_t norm_lo;
   QkvEpi qkv;
   ArgmaxEpi am;
 };

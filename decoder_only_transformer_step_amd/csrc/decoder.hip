@@ -184,6 +184,10 @@ struct decoder {
   float *f32_attn, *f32_h, *f32_act, *f32_hexp;
   size_t am_cap = 0;           // argmax partials the am_val / am_idx buffers hold
   int cus = 256;               // compute units of the device
+  // D->act holds RMSNorm(x; act_norm) of the first act_rows rows of x (split
+  // bf16), written by a fused reduce; null when x has changed since
+  const float *act_norm = nullptr;
+  int act_rows = 0;
   bool single_row_ok = false;  // the batch-1 GEMV path fits every K of this config
   int64_t act_lo = 0, attn_lo = 0, q_lo = 0, h_lo = 0, hexp_lo = 0, hsh_lo = 0;  // lo-plane offsets
   // host state
@@ -299,6 +303,19 @@ int proj(decoder *D, int node, int epi, GemmArgs g, int max_rows) {
                   2.0 * npd * g.M * ncols * (double)g.K);
   const int ntiles = gemm_ntiles(g, epi);
   g.Cpart = D->gpart;
+  if (epi == EPI_ADD) D->act_norm = nullptr;  // x changes
+  if (g.norm_gamma) {
+    g.norm_eps = (float)D->c.rms_eps;
+    g.norm_out = D->act;
+    g.norm_lo = D->act_lo;
+  }
+  // the split reduce of a residual projection also writes the next RMSNorm
+  auto note_norm = [&]() {
+    if (epi == EPI_ADD && g.norm_gamma && g.ksplit > 1 && g.C == D->x) {
+      D->act_norm = g.norm_gamma;
+      D->act_rows = g.M;
+    }
+  };
   if (g.M > CHUNK_MIN_ROWS && gemm_chunk_fits(g, epi)) {
     // chunk kernel: split K so that the blocks (weight tiles x row blocks x
     // splits) fill the compute units about once, with at least two 64-wide k
@@ -312,8 +329,10 @@ int proj(decoder *D, int node, int epi, GemmArgs g, int max_rows) {
       while (kc > 1 && (size_t)kc * g.M * (size_t)npd * ntiles * 16 > D->L.gpart_elems) --kc;
     }
     g.ksplit = kc;
+    if (g.ksplit <= 1) g.norm_out = nullptr;
     hipError_t e = launch_gemm_chunk(g, epi, D->stream);
     if (e != hipSuccess) return hip_fail(D, e, "chunk projection");
+    note_norm();
     return DEC_OK;
   }
   const int steps = (g.K + 31) / 32;
@@ -324,8 +343,10 @@ int proj(decoder *D, int node, int epi, GemmArgs g, int max_rows) {
     while (ks > 1 && (size_t)ks * g.M * (size_t)npd * ntiles * 16 > D->L.gpart_elems) --ks;
   }
   g.ksplit = std::max(ks, 1);
+  if (g.ksplit <= 1 || g.n_groups) g.norm_out = nullptr;
   hipError_t e = launch_gemm(g, epi, max_rows, 1, D->stream);
   if (e != hipSuccess) return hip_fail(D, e, "projection");
+  if (g.norm_out) note_norm();
   return DEC_OK;
 }
 
@@ -351,6 +372,13 @@ int norm_into(decoder *D, GemmArgs &g, const float *x, const float *gamma, int r
     g.eps = (float)D->c.rms_eps;
     g.lda = H;
     g.A = nullptr;
+    return DEC_OK;
+  }
+  if (x == D->x && gamma == D->act_norm && rows == D->act_rows) {
+    // the previous residual projection's reduce already wrote it
+    g.A = D->act;
+    g.a_lo = D->act_lo;
+    g.lda = H;
     return DEC_OK;
   }
   hipError_t e;
@@ -434,6 +462,7 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
 
 // Launch one batch-1 projection (GEMV) as node `node`.
 int gemv(decoder *D, int node, int epi, const GemvArgs &g, int *blocks = nullptr) {
+  if (epi == EPI_ADD) D->act_norm = nullptr;  // x changes
   const double nr = (epi == EPI_SWIGLU || epi == EPI_QKV) ? 2.0 : 1.0;
   const double slots = g.slot_expert ? g.n_slots : 1;
   NodeTimer timer(D, node, slots * (nr * g.n_items * (double)g.K * 2 + g.K * 4.0 + g.n_items * 4.0 * (epi == EPI_ADD ? 2 : 1)),
@@ -535,6 +564,7 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
     if ((rc = gemv(D, DEC_NODE_EXPERTS, EPI_STORE, gemv_args(W.w_sh_down, D->f32_h, Is, H, D->ysh)))) return rc;
   }
   NodeTimer tcomb(D, DEC_NODE_EXPERTS, H * (8.0 + 4.0 * k + 4.0), H * 2.0 * (k + 1));
+  D->act_norm = nullptr;
   e = launch_moe_combine(D->x, D->yexp, Is > 0 ? D->ysh : nullptr, D->rwts, D->rgate, nullptr, 1, k, H, D->stream);
   if (e != hipSuccess) return hip_fail(D, e, "moe combine");
   return DEC_OK;
@@ -573,6 +603,7 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   if ((rc = attention(D, l, rows, rows_per_group, max_pos, hpos))) return rc;
   GemmArgs o = dense_args(D->attn, qd, W.w_o, rows, H, qd);
   o.Wp = D->packed[l].w[1];
+  o.norm_gamma = W.ffn_norm;
   o.a_lo = D->attn_lo;
   o.C = D->x;
   o.ldc = H;
@@ -589,6 +620,7 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
     if ((rc = proj(D, DEC_NODE_GATE_UP, EPI_SWIGLU, gu, rows))) return rc;
     GemmArgs dn = dense_args(D->h, I, W.w_down, rows, H, I);
     dn.Wp = D->packed[l].w[3];
+    if (l + 1 < c.n_layers) dn.norm_gamma = (const float *)D->layers[l + 1].attn_norm;
     dn.a_lo = D->h_lo;
     dn.C = D->x;
     dn.ldc = H;
@@ -599,7 +631,9 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   // experts all read the same normed input b (bf16 in D->act)
   {
     NodeTimer t(D, DEC_NODE_NORM, rows * (double)H * 6 + H * 4.0, rows * (double)H * 4);
-    e = launch_rmsnorm(D->x, H, W.ffn_norm, rows, H, (float)c.rms_eps, D->act, H, D->act_lo, st);
+    e = (D->act_norm == (const float *)W.ffn_norm && D->act_rows == rows)
+            ? hipSuccess
+            : launch_rmsnorm(D->x, H, W.ffn_norm, rows, H, (float)c.rms_eps, D->act, H, D->act_lo, st);
   }
   if (e != hipSuccess) return hip_fail(D, e, "rmsnorm");
   const int E = c.n_experts, k = c.top_k, Ie = c.expert_inter, Is = c.shared_inter;
@@ -688,6 +722,7 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
     if ((rc = proj(D, DEC_NODE_EXPERTS, EPI_STORE, sd, rows))) return rc;
   }
   NodeTimer tcomb(D, DEC_NODE_EXPERTS, rows * (double)H * (8.0 + 4.0 * k + 4.0), rows * (double)H * 2 * (k + 1));
+  D->act_norm = nullptr;
   e = launch_moe_combine(D->x, D->yexp, Is > 0 ? D->ysh : nullptr, D->rwts, D->rgate, D->pair_of, rows,
                          k, H, st);
   if (e != hipSuccess) return hip_fail(D, e, "moe combine");
@@ -703,6 +738,7 @@ int run_step(decoder *D, int rows, int rows_per_group, int max_pos, const int32_
   hipError_t e;
   {
     NodeTimer t(D, DEC_NODE_EMBED, rows * (double)c.hidden * 6, 0);
+    D->act_norm = nullptr;
     e = launch_embed(D->embed, D->ids, D->next_token, D->row_seq, use_next, rows, c.hidden, D->x, st);
   }
   if (e != hipSuccess) return hip_fail(D, e, "embed");

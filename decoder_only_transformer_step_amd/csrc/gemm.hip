@@ -240,6 +240,58 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g, int ntiles
   }
 }
 
+// Split-K reduce of a residual projection fused with the RMSNorm that reads
+// the new residual (engine.zig Engine.forward: x += W o, then the next
+// sub-block's rmsnormColumn): one block per row; the partials are summed in
+// fixed split order, added to x, and x / sqrt(mean(x^2) + eps) * gamma is
+// written as the next projection's split-bf16 activation.
+__global__ __launch_bounds__(1024) void gemm_reduce_norm_kernel(GemmArgs g, int ntiles) {
+  __shared__ float lds[16];
+  const int64_t np_cols = (int64_t)ntiles * 16;
+  const int m = blockIdx.x, N = g.N;
+  float *xr = g.C + (int64_t)m * g.ldc;
+  const float *pr = g.Cpart + (int64_t)m * np_cols;
+  const int64_t zstride = (int64_t)g.M * np_cols;
+  float ss = 0.f;
+  for (int n = threadIdx.x * 4; n < N; n += 1024 * 4) {
+    // x + (p_0 + p_1 + ...), the order of the element-wise reduce; the
+    // partials of up to 8 splits are loaded together
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int z0 = 0; z0 < g.ksplit; z0 += 8) {
+      f32x4 p[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) p[u] = *reinterpret_cast<const f32x4 *>(pr + min(z0 + u, g.ksplit - 1) * zstride + n);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (z0 + u < g.ksplit) {
+          acc[0] += p[u][0];
+          acc[1] += p[u][1];
+          acc[2] += p[u][2];
+          acc[3] += p[u][3];
+        }
+    }
+    f32x4 v = *reinterpret_cast<const f32x4 *>(xr + n);
+    v[0] += acc[0];
+    v[1] += acc[1];
+    v[2] += acc[2];
+    v[3] += acc[3];
+    *reinterpret_cast<f32x4 *>(xr + n) = v;
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  ss = block_sum<16>(ss, lds);
+  const float inv = 1.0f / sqrtf(ss / (float)N + g.norm_eps);
+  uint16_t *orow = g.norm_out + (int64_t)m * N;
+  for (int n = threadIdx.x * 4; n < N; n += 1024 * 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + n);
+    const f32x4 w = *reinterpret_cast<const f32x4 *>(g.norm_gamma + n);
+    u32x2 oh, ol;
+    { const u32pair t_ = pack_split2(v[0] * inv * w[0], v[1] * inv * w[1]); oh[0] = t_.hi; ol[0] = t_.lo; }
+    { const u32pair t_ = pack_split2(v[2] * inv * w[2], v[3] * inv * w[3]); oh[1] = t_.hi; ol[1] = t_.lo; }
+    *reinterpret_cast<u32x2 *>(orow + n) = oh;
+    *reinterpret_cast<u32x2 *>(orow + g.norm_lo + n) = ol;
+  }
+}
+
 // U: weight steps per load batch, so that a batch holds about 16 fragments
 template <int MT, int EPI, int NW, int AMODE, bool SPLIT>
 hipError_t launch_cfg(const GemmArgs &g, dim3 grid, size_t dyn, hipStream_t st) {
@@ -304,6 +356,11 @@ hipError_t launch_gemm(const GemmArgs &g, int epi, int max_rows, int n_group_slo
 }
 
 hipError_t launch_gemm_reduce(const GemmArgs &g, int epi, int ntiles, hipStream_t st) {
+  if (epi == EPI_ADD && g.norm_out) {
+    if (g.N % 4 || ntiles * 16 != g.N) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gemm_reduce_norm_kernel, dim3(g.M), dim3(1024), 0, st, g, ntiles);
+    return hipGetLastError();
+  }
   const int64_t total = (int64_t)g.M * ntiles * 16;
   const int blocks = (int)std::min<int64_t>((total + 255) / 256, 4096);
   switch (epi) {
