@@ -249,6 +249,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 // LDS with one load per thread; each thread's O partials are independent
 // loads, so they are in flight together.
 constexpr int MERGE_MAX_SPLITS = 1024;
+constexpr int MERGE_CHUNK = 32;
 
 template <int D, int PM>
 __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int ncols) {
@@ -276,12 +277,20 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int ncols) {
   float M = red[0];
 #pragma unroll
   for (int w = 1; w < D / WAVE; ++w) M = fmaxf(M, red[w]);
+  // split order; a chunk of MERGE_CHUNK independent loads in flight at a time
   float L = 0.f, o = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < nact; ++s) {
-    const float sc = exp2f(sm[s] - M);
-    L += sc * sl[s];
-    o += sc * po[(int64_t)s * 16 * D];
+  for (int s0 = 0; s0 < nact; s0 += MERGE_CHUNK) {
+    float ov[MERGE_CHUNK];
+#pragma unroll
+    for (int u = 0; u < MERGE_CHUNK; ++u) ov[u] = po[(int64_t)min(s0 + u, nact - 1) * 16 * D];
+#pragma unroll
+    for (int u = 0; u < MERGE_CHUNK; ++u) {
+      if (s0 + u < nact) {
+        const float sc = exp2f(sm[s0 + u] - M);
+        L += sc * sl[s0 + u];
+        o += sc * ov[u];
+      }
+    }
   }
   store_out(a, ((int64_t)oc.row * a.Hq + oc.head) * D + j, o / L);
 }

@@ -133,7 +133,8 @@ enum {
 struct QkvEpi {
   const float *bias;       // fp32 [qkv rows] or null
   const float2 *cs;        // (cos, sin) [S][d/2]
-  const int32_t *row_seq, *row_pos;
+  const int32_t *row_seq, *row_pos;  // device positions, or null: pos_arg / seq_arg (one row)
+  int32_t pos_arg, seq_arg;
   uint16_t *q;             // split bf16 [rows][Hq][d], lo plane at q + q_lo
   int64_t q_lo;
   uint16_t *kcache, *vcache;

@@ -497,8 +497,13 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
   q.eps = eps;
   q.qkv.bias = c.qkv_bias ? W.b_qkv : nullptr;
   q.qkv.cs = D->rope;
-  q.qkv.row_seq = D->row_seq;
-  q.qkv.row_pos = D->row_pos;
+  if (D->hseq.size() == 1) {  // the position as a kernel argument: no load before the RoPE angle
+    q.qkv.pos_arg = hpos[0];
+    q.qkv.seq_arg = D->hseq[0];
+  } else {
+    q.qkv.row_seq = D->row_seq;
+    q.qkv.row_pos = D->row_pos;
+  }
   q.qkv.q = D->q;
   q.qkv.q_lo = D->q_lo;
   q.qkv.kcache = D->kcache;
@@ -586,8 +591,13 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   q.np_off = d / 2;
   q.qkv.bias = c.qkv_bias ? W.b_qkv : nullptr;
   q.qkv.cs = D->rope;
-  q.qkv.row_seq = D->row_seq;
-  q.qkv.row_pos = D->row_pos;
+  if (D->hseq.size() == 1) {  // the position as a kernel argument: no load before the RoPE angle
+    q.qkv.pos_arg = hpos[0];
+    q.qkv.seq_arg = D->hseq[0];
+  } else {
+    q.qkv.row_seq = D->row_seq;
+    q.qkv.row_pos = D->row_pos;
+  }
   q.qkv.q = D->q;
   q.qkv.q_lo = D->q_lo;
   q.qkv.kcache = D->kcache;
@@ -760,8 +770,7 @@ int run_step(decoder *D, int rows, int rows_per_group, int max_pos, const int32_
     g.eps = (float)c.rms_eps;
     g.part_val = D->am_val;
     g.part_idx = D->am_idx;
-    const GemvShape sh = gemv_shape(c.vocab, H, EPI_LOGITS);
-    if ((size_t)sh.blocks > D->am_cap) return fail(D, DEC_E_HIP, "lm-head grid exceeds the argmax partial buffer");
+    if ((size_t)gemv_blocks(c.vocab) > D->am_cap) return fail(D, DEC_E_HIP, "lm-head grid exceeds the argmax partial buffer");
     if ((rc = gemv(D, DEC_NODE_HEAD, EPI_LOGITS, g, &nparts))) return rc;
   } else {
     GemmArgs g = dense_args(nullptr, H, D->lm_head, nout, c.vocab, H);
@@ -882,7 +891,7 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
     const int qd = cfg->n_heads * cfg->head_dim;
     const int kmax = std::max(std::max(cfg->hidden, qd), std::max(std::max(cfg->ffn_inter, cfg->shared_inter),
                                                                       cfg->expert_inter));
-    D->single_row_ok = (size_t)kmax * 4 <= GEMV_MAX_LDS;
+    D->single_row_ok = gemv_lds(kmax) <= GEMV_MAX_LDS;
   }
   if (cfg->n_experts > 0) {
     D->rlogits = carve<float>(D, L.rlogits);
@@ -1133,7 +1142,7 @@ int dec_diag_gemm_chunk(const uint16_t *d_A, int32_t planes, int32_t M, int32_t 
 }
 
 int dec_diag_gemv(const float *d_a, int32_t K, const uint16_t *d_W, int32_t N, float *d_y, void *stream) {
-  if (!d_a || !d_W || !d_y || N < 1 || K < 8 || K % 8 || (size_t)K * 4 > GEMV_MAX_LDS) return DEC_E_INVALID;
+  if (!d_a || !d_W || !d_y || N < 1 || K < 8 || K % 8 || gemv_lds(K) > GEMV_MAX_LDS) return DEC_E_INVALID;
   GemvArgs g = gemv_args(d_W, d_a, K, N, d_y);
   return launch_gemv(g, EPI_STORE, (hipStream_t)stream) == hipSuccess ? DEC_OK : DEC_E_HIP;
 }

@@ -14,13 +14,14 @@
 //  * The activation is kept in fp32 in LDS (the fused RMSNorm prologue
 //    writes it there once per block), so the only rounding on the path is
 //    the weights' own bf16 storage.  Each lane does 8 fp32 FMAs per 16-byte
-//    load, then a 64-lane butterfly sum gives the dot product.
-//  * Software pipeline: the first batch of weight loads is issued before the
-//    activation prologue, and each later batch while the previous one is
-//    consumed, so every wave keeps several kilobytes in flight at all times.
-//  * Persistent grid (about two blocks per compute unit): the activation
-//    prologue runs once per block, and each wave streams its items back to
-//    back, the next item's first loads overlapping the current reduction.
+//    load; the LDS layout makes each wave's 16-byte reads contiguous across
+//    lanes.  A DPP reduction gives the dot product.
+//  * Pipeline: two register buffers of 8 KB per wave; the activation loads
+//    go out first, then the first two weight chunks, so the prologue waits
+//    only for the activation while the weights stream in.  Every load is
+//    unconditional, so the compiler's memory wait counts stay exact.
+//  * One item per wave, 8 waves per block; blocks beyond the resident set
+//    queue up behind the running ones.
 //  * Grouped mode (MoE experts): blockIdx.y = routing slot; the weight base
 //    moves to the chosen expert.
 #include <algorithm>
@@ -30,7 +31,7 @@
 
 namespace {
 
-constexpr int GV_MAX_WAVES = 8;
+constexpr int GV_WAVES = 8;  // waves per block
 
 template <int EPI>
 constexpr int gv_rows() {
@@ -55,29 +56,44 @@ __device__ __forceinline__ void item_rows(const GemvArgs &g, int it, int &r0, in
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
+// Zero page for the lanes of a ragged last step (k >= K): their loads are
+// redirected here by a pointer select, so every load is unconditional and
+// the compiler's wait counts stay exact (a per-lane branch around a load, or
+// a select on its value, makes it wait for everything in flight).
+__device__ u32x4 gv_zero[1];
+
 // Loads of UNR 1 KB steps for every row the wave owns.
 template <int R, int UNR>
-__device__ __forceinline__ void load_batch(u32x4 (&v)[UNR][R], const uint16_t *const (&wp)[R],
-                                           const bool (&rv)[R], int s0, int steps, int K, int lane) {
+__device__ __forceinline__ void load_batch(u32x4 (&v)[UNR][R], const uint16_t *const (&wp)[R], int s0, int K,
+                                           int lane) {
 #pragma unroll
   for (int u = 0; u < UNR; ++u) {
     const int st = s0 + u;
-    const bool ok = st < steps && st * 512 + lane * 8 < K;
+    const bool ok = st * 512 + lane * 8 < K;  // false for every lane past the last step
 #pragma unroll
-    for (int r = 0; r < R; ++r) v[u][r] = (ok && rv[r]) ? load16(wp[r] + st * 512) : u32x4{0u, 0u, 0u, 0u};
+    for (int r = 0; r < R; ++r)
+      v[u][r] = load16(ok ? static_cast<const void *>(wp[r] + st * 512) : static_cast<const void *>(gv_zero));
   }
+}
+
+// Activation layout in LDS: fp32, padded with zeros to whole 512-element
+// steps, with lane l's 8 elements of step s as two 16-byte slots
+// (s * 2 + h) * 64 + l, so that each 16-byte read of a wave is contiguous
+// across the lanes (no bank conflicts).
+__device__ __forceinline__ int xs_slot(int k) {  // k: element index, a multiple of 4
+  return ((k >> 9) * 2 + ((k >> 2) & 1)) * 64 + ((k & 511) >> 3);
 }
 
 // acc[r] += dot(weights of batch, activation) over UNR steps.
 template <int R, int UNR>
-__device__ __forceinline__ void fma_batch(float (&acc)[R], const u32x4 (&v)[UNR][R], const float *xs, int s0,
-                                          int steps, int K, int lane) {
+__device__ __forceinline__ void fma_batch(float (&acc)[R], const u32x4 (&v)[UNR][R], const f32x4 *xs, int s0,
+                                          int steps, int lane) {
 #pragma unroll
   for (int u = 0; u < UNR; ++u) {
-    const int k = (s0 + u) * 512 + lane * 8;
-    if ((s0 + u) < steps && k < K) {
-      const f32x4 xa = *reinterpret_cast<const f32x4 *>(xs + k);
-      const f32x4 xb = *reinterpret_cast<const f32x4 *>(xs + k + 4);
+    const int st = s0 + u;
+    if (st < steps) {
+      const f32x4 xa = xs[(st * 2) * 64 + lane];
+      const f32x4 xb = xs[(st * 2 + 1) * 64 + lane];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const u32x4 w = v[u][r];
@@ -96,29 +112,58 @@ __device__ __forceinline__ void fma_batch(float (&acc)[R], const u32x4 (&v)[UNR]
   }
 }
 
-// Rows of item `it` and their weight pointers (lane offset included).
+// Epilogue inputs of one item that do not depend on the dot product (bias,
+// RoPE angle, the residual value), loaded when the item's first weights are
+// issued so that the epilogue itself waits on nothing.
+struct ItemPre {
+  float a, b, c, e;
+};
+
+template <int EPI>
+__device__ __forceinline__ ItemPre item_prefetch(const GemvArgs &g, int out_row, int r0, int r1) {
+  // loads through pointer selects (a missing bias reads the zero page): a
+  // branch around a load would make the merge wait for it
+  const float *zf = reinterpret_cast<const float *>(gv_zero);
+  ItemPre p{0.f, 0.f, 0.f, 0.f};
+  if (EPI == EPI_STORE) {
+    p.a = *(g.bias ? g.bias + r0 : zf);
+  } else if (EPI == EPI_ADD) {
+    p.a = g.C[r0];
+  } else if (EPI == EPI_QKV) {
+    const QkvEpi &q = g.qkv;
+    const int half = q.d / 2, i = r0 % q.d;
+    p.c = *(q.bias ? q.bias + r0 : zf);
+    p.e = *(q.bias ? q.bias + r1 : zf);
+    const int pos = q.row_pos ? q.row_pos[0] : q.pos_arg;
+    const float2 t = q.cs[(int64_t)pos * half + i];  // unused for v rows
+    p.a = t.x;
+    p.b = t.y;
+  }
+  return p;
+}
+
+// Rows of item `it` (a valid item), their weight pointers (lane offset
+// included) and the item's epilogue inputs.
 template <int EPI, int NR>
-__device__ __forceinline__ void item_ptrs(const GemvArgs &g, const uint16_t *W, int it, int lane,
-                                          int (&rows)[NR], const uint16_t *(&wp)[NR], bool (&rv)[NR]) {
-  int r0 = 0, r1 = 0;
-  const bool ok = it < g.n_items;
-  if (ok) item_rows<EPI>(g, it, r0, r1);
+__device__ __forceinline__ void item_ptrs(const GemvArgs &g, const uint16_t *W, int it, int lane, int out_row,
+                                          int (&rows)[NR], const uint16_t *(&wp)[NR], ItemPre &pre) {
+  int r0, r1;
+  item_rows<EPI>(g, it, r0, r1);
   rows[0] = r0;
   rows[NR - 1] = r1;
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    rv[r] = ok;
-    wp[r] = W + (int64_t)rows[r] * g.K + lane * 8;
-  }
+  for (int r = 0; r < NR; ++r) wp[r] = W + (int64_t)rows[r] * g.K + lane * 8;
+  pre = item_prefetch<EPI>(g, out_row, r0, r1);
 }
 
 // Epilogue of one item (lane 0 writes).
 template <int EPI>
-__device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, int r0, int r1, float v0, float v1) {
+__device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, int r0, int r1, float v0, float v1,
+                                              const ItemPre &pre) {
   if (EPI == EPI_STORE) {
-    g.C[(int64_t)out_row * g.ldc + r0] = v0 + (g.bias ? g.bias[r0] : 0.f);
+    g.C[(int64_t)out_row * g.ldc + r0] = v0 + pre.a;
   } else if (EPI == EPI_ADD) {
-    g.C[r0] += v0;
+    g.C[r0] = pre.a + v0;
   } else if (EPI == EPI_SWIGLU) {
     g.C[(int64_t)out_row * g.ldc + r0] = silu_f(v0) * v1;
   } else if (EPI == EPI_LOGITS) {
@@ -130,16 +175,12 @@ __device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, in
     const QkvEpi &q = g.qkv;
     const int d = q.d, half = d / 2;
     const int hh = r0 / d, i = r0 - hh * d;
-    float u0 = v0, u1 = v1;
-    if (q.bias) {
-      u0 += q.bias[r0];
-      u1 += q.bias[r1];
-    }
-    const int pos = q.row_pos[0], seq = q.row_seq[0];
+    const float u0 = v0 + pre.c, u1 = v1 + pre.e;
+    const int pos = q.row_pos ? q.row_pos[0] : q.pos_arg;
+    const int seq = q.row_seq ? q.row_seq[0] : q.seq_arg;
     const int64_t base = (int64_t)seq * q.seq_stride + q.layer_off;
     if (hh < q.Hq + q.Hkv) {
-      const float2 t = q.cs[(int64_t)pos * half + i];
-      const float a0 = u0 * t.x - u1 * t.y, a1 = u0 * t.y + u1 * t.x;
+      const float a0 = u0 * pre.a - u1 * pre.b, a1 = u0 * pre.b + u1 * pre.a;
       if (hh < q.Hq) {
         uint16_t *dst = q.q + (int64_t)hh * d;
         uint32_t h0, l0, h1, l1;
@@ -162,17 +203,21 @@ __device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, in
   }
 }
 
-// Persistent grid: each wave walks the items it, it + stride, ... as one
-// sequence of UNR-step load batches, ping-ponging between two register
-// buffers, so the first batch of the next item is already in flight while
-// the current item is reduced and written.
-template <int EPI, int UNR, int GV_WAVES>
+// One item per wave, GV_WAVES waves per block.  The wave's weight rows are
+// streamed in chunks of CH 1 KB steps through two register buffers: the
+// first two chunks go out before the activation prologue, and each buffer
+// is refilled as soon as it has been consumed, so two chunks are always in
+// flight.  Every load is unconditional (ragged steps read a zero page), and
+// the activation is loaded ahead of the weights when it fits in registers,
+// so the prologue waits only for it.  NCH: the row's chunk count when it is
+// 1 or 2 (no refills), else 0 (the refill loop).
+template <int EPI, int NCH>
 __global__ __launch_bounds__(GV_WAVES * WAVE) void gemv_kernel(GemvArgs g) {
-  constexpr int NR = gv_rows<EPI>();
-  extern __shared__ float xs[];
-  __shared__ float sred[GV_MAX_WAVES];
-  __shared__ float bv_s[GV_MAX_WAVES];
-  __shared__ int bi_s[GV_MAX_WAVES];
+  constexpr int NR = gv_rows<EPI>(), CH = 8 / NR, NT = GV_WAVES * WAVE;
+  extern __shared__ f32x4 xs[];  // activation, fp32 in the layout of xs_slot
+  __shared__ float sred[GV_WAVES];
+  __shared__ float bv_s[GV_WAVES];
+  __shared__ int bi_s[GV_WAVES];
 
   const uint16_t *W = g.W;
   const float *xin = g.a_f32;
@@ -184,103 +229,126 @@ __global__ __launch_bounds__(GV_WAVES * WAVE) void gemv_kernel(GemvArgs g) {
     out_row = slot;
   }
   const int K = g.K;
-  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-  const int stride = gridDim.x * GV_WAVES;
-  const int steps = (K + 511) / 512;
-  const int nb = (steps + UNR - 1) / UNR;  // batches per item
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+  const int steps = (K + 511) / 512, nch = NCH ? NCH : (steps + CH - 1) / CH;
+  const int it = blockIdx.x * GV_WAVES + wave;
+  const bool valid = it < g.n_items;
+  int rows[NR];
+  const uint16_t *wp[NR];
+  ItemPre pre;
+  item_ptrs<EPI, NR>(g, W, valid ? it : g.n_items - 1, lane, out_row, rows, wp, pre);
 
-  // batch sequence position of the next load: item `li`, batch `lb`
-  int li = blockIdx.x * GV_WAVES + wave, lb = 0;
-  int lrows[NR];
-  const uint16_t *lwp[NR];
-  bool lrv[NR];
-  item_ptrs<EPI, NR>(g, W, li, lane, lrows, lwp, lrv);
+  // activation into registers first when it fits.  Mode 1: x and gamma
+  // (RMSNorm); 2: fp32 x; 3: bf16 x; 0: read after the weights are issued.
+  const int mode = g.gamma ? (K <= 8 * NT ? 1 : 0) : xin ? (K <= 16 * NT ? 2 : 0) : (K <= 32 * NT ? 3 : 0);
+  // (addresses picked by pointer selects, loads unconditional: a branch
+  // around them would make the merge wait for the data)
+  u32x4 pr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k4 = min((int)(threadIdx.x + (i & 1) * NT) * 4, K - 4);
+    const int k2 = min((int)(threadIdx.x + i * NT) * 4, K - 4);
+    const int k8 = min((int)(threadIdx.x + i * NT) * 8, K - 8);
+    const void *src = mode == 1 ? static_cast<const void *>((i < 2 ? xin : g.gamma) + k4)
+                    : mode == 2 ? static_cast<const void *>(xin + k2)
+                    : mode == 3 ? static_cast<const void *>(g.a_bf16 + k8)
+                                : static_cast<const void *>(gv_zero);
+    pr[i] = load16(src);
+  }
 
-  u32x4 buf0[UNR][NR], buf1[UNR][NR];
-  // the first weight loads go out before the activation prologue
-  load_batch<NR, UNR>(buf0, lwp, lrv, 0, steps, K, lane);
+  // (loads past the row read the zero page: no load sits under a branch)
+  u32x4 buf0[CH][NR], buf1[CH][NR];
+  load_batch<NR, CH>(buf0, wp, 0, K, lane);
+  if (NCH != 1) load_batch<NR, CH>(buf1, wp, CH, K, lane);
 
-  // activation -> LDS (fp32), with the RMSNorm prologue when gamma is set
-  if (g.gamma) {
+  // activation -> LDS (fp32, with the RMSNorm when gamma is set)
+  auto put4 = [&](int k, f32x4 v) { xs[xs_slot(k)] = v; };
+  auto as_f4 = [](u32x4 v) { return __builtin_bit_cast(f32x4, v); };
+  if (mode == 1) {
     float ss = 0.f;
-    for (int k = threadIdx.x * 4; k < K; k += GV_WAVES * WAVE * 4) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const f32x4 v = as_f4(pr[i]);
+      if ((int)(threadIdx.x + i * NT) * 4 < K) ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    }
+    ss = block_sum<GV_WAVES>(ss, sred);
+    const float inv = 1.0f / sqrtf(ss / (float)K + g.eps);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int k = (threadIdx.x + i * NT) * 4;
+      const f32x4 v = as_f4(pr[i]), w = as_f4(pr[2 + i]);
+      if (k < K) put4(k, f32x4{v[0] * inv * w[0], v[1] * inv * w[1], v[2] * inv * w[2], v[3] * inv * w[3]});
+    }
+  } else if (mode == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = (threadIdx.x + i * NT) * 4;
+      if (k < K) put4(k, as_f4(pr[i]));
+    }
+  } else if (mode == 3) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = (threadIdx.x + i * NT) * 8;
+      const u32x4 w = pr[i];
+      if (k < K) {
+        put4(k, f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])});
+        put4(k + 4, f32x4{bf16_lo(w[2]), bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3])});
+      }
+    }
+  } else if (g.gamma) {
+    float ss = 0.f;
+    for (int k = threadIdx.x * 4; k < K; k += NT * 4) {
       const f32x4 v = loadf4(xin + k);
       ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
     }
     ss = block_sum<GV_WAVES>(ss, sred);
     const float inv = 1.0f / sqrtf(ss / (float)K + g.eps);
-    for (int k = threadIdx.x * 4; k < K; k += GV_WAVES * WAVE * 4) {
+    for (int k = threadIdx.x * 4; k < K; k += NT * 4) {
       const f32x4 v = loadf4(xin + k), w = loadf4(g.gamma + k);
-      *reinterpret_cast<f32x4 *>(xs + k) = f32x4{v[0] * inv * w[0], v[1] * inv * w[1], v[2] * inv * w[2], v[3] * inv * w[3]};
+      put4(k, f32x4{v[0] * inv * w[0], v[1] * inv * w[1], v[2] * inv * w[2], v[3] * inv * w[3]});
     }
   } else if (xin) {
-    for (int k = threadIdx.x * 4; k < K; k += GV_WAVES * WAVE * 4)
-      *reinterpret_cast<f32x4 *>(xs + k) = loadf4(xin + k);
+    for (int k = threadIdx.x * 4; k < K; k += NT * 4) put4(k, loadf4(xin + k));
   } else {
-    for (int k = threadIdx.x * 8; k < K; k += GV_WAVES * WAVE * 8) {
+    for (int k = threadIdx.x * 8; k < K; k += NT * 8) {
       const u32x4 w = load16(g.a_bf16 + k);
-      *reinterpret_cast<f32x4 *>(xs + k) = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
-      *reinterpret_cast<f32x4 *>(xs + k + 4) = f32x4{bf16_lo(w[2]), bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3])};
+      put4(k, f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])});
+      put4(k + 4, f32x4{bf16_lo(w[2]), bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3])});
     }
   }
+  // zero padding up to whole steps
+  for (int k = K + threadIdx.x * 4; k < steps * 512; k += NT * 4) put4(k, f32x4{0.f, 0.f, 0.f, 0.f});
   __syncthreads();
 
-  // consumption state: item `ci` (rows crows), batch `cb`
-  int ci = li, cb = 0;
-  int crows[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) crows[r] = lrows[r];
   float acc[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) acc[r] = 0.f;
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
-
-  // advance the load position by one batch and issue it into `dst`
-  auto issue_next = [&](u32x4 (&dst)[UNR][NR]) {
-    if (++lb == nb) {
-      lb = 0;
-      li += stride;
-      item_ptrs<EPI, NR>(g, W, li, lane, lrows, lwp, lrv);
+  int c = 0;
+  if (NCH == 0) {
+    for (; c + 2 < nch; c += 2) {
+      fma_batch<NR, CH>(acc, buf0, xs, c * CH, steps, lane);
+      load_batch<NR, CH>(buf0, wp, (c + 2) * CH, K, lane);
+      fma_batch<NR, CH>(acc, buf1, xs, (c + 1) * CH, steps, lane);
+      load_batch<NR, CH>(buf1, wp, (c + 3) * CH, K, lane);
     }
-    if (li < g.n_items) load_batch<NR, UNR>(dst, lwp, lrv, lb * UNR, steps, K, lane);
-  };
-  // consume `src` as batch cb of item ci; finish the item on its last batch
-  auto consume = [&](const u32x4 (&src)[UNR][NR]) {
-    fma_batch<NR, UNR>(acc, src, xs, cb * UNR, steps, K, lane);
-    if (++cb == nb) {
-#pragma unroll
-      for (int r = 0; r < NR; ++r) acc[r] = wave_sum(acc[r]);
-      if (EPI == EPI_LOGITS && better(acc[0], crows[0], bv, bi)) {
-        bv = acc[0];
-        bi = crows[0];
-      }
-      if (lane == 0) item_epilogue<EPI>(g, out_row, crows[0], crows[NR - 1], acc[0], acc[NR - 1]);
-#pragma unroll
-      for (int r = 0; r < NR; ++r) acc[r] = 0.f;
-      cb = 0;
-      ci += stride;
-#pragma unroll
-      for (int r = 0; r < NR; ++r) crows[r] = lrows[r];  // the load position is already on item ci
-    }
-  };
-
-  while (ci < g.n_items) {
-    issue_next(buf1);
-    consume(buf0);
-    if (ci >= g.n_items) break;
-    issue_next(buf0);
-    consume(buf1);
   }
+  fma_batch<NR, CH>(acc, buf0, xs, c * CH, steps, lane);
+  if (NCH != 1) fma_batch<NR, CH>(acc, buf1, xs, (c + 1) * CH, steps, lane);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = wave_sum(acc[r]);
+  if (valid && lane == 0) item_epilogue<EPI>(g, out_row, rows[0], rows[NR - 1], acc[0], acc[NR - 1], pre);
 
   if (EPI == EPI_LOGITS) {
     // this block's best (value, index), for the argmax finalize pass
     if (lane == 0) {
-      bv_s[wave] = bv;
-      bi_s[wave] = bi;
+      bv_s[wave] = valid ? acc[0] : -INFINITY;
+      bi_s[wave] = valid ? rows[0] : 0x7fffffff;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
+      float bv = bv_s[0];
+      int bi = bi_s[0];
       for (int w = 1; w < GV_WAVES; ++w)
         if (better(bv_s[w], bi_s[w], bv, bi)) {
           bv = bv_s[w];
@@ -292,107 +360,31 @@ __global__ __launch_bounds__(GV_WAVES * WAVE) void gemv_kernel(GemvArgs g) {
   }
 }
 
-// A load batch holds DEC_GEMV_LOADS kilobytes (twice that when deep) across
-// the item's rows.
-template <int EPI, int W, bool DEEP>
-constexpr auto gv_kernel() {
-  constexpr int NR = gv_rows<EPI>();
-  return gemv_kernel<EPI, (DEEP ? 2 : 1) * DEC_GEMV_LOADS / NR, W>;
-}
-
 template <int EPI>
-hipError_t launch_e(const GemvArgs &g, const GemvShape &sh, dim3 grid, size_t lds, hipStream_t st) {
-  if (sh.waves == 4) {
-    if (sh.deep) hipLaunchKernelGGL((gv_kernel<EPI, 4, true>()), grid, dim3(4 * WAVE), lds, st, g);
-    else hipLaunchKernelGGL((gv_kernel<EPI, 4, false>()), grid, dim3(4 * WAVE), lds, st, g);
-  } else {
-    if (sh.deep) hipLaunchKernelGGL((gv_kernel<EPI, 8, true>()), grid, dim3(8 * WAVE), lds, st, g);
-    else hipLaunchKernelGGL((gv_kernel<EPI, 8, false>()), grid, dim3(8 * WAVE), lds, st, g);
-  }
-  return hipGetLastError();
-}
-
-// Blocks of one kernel instance resident per compute unit (registers and
-// the block's LDS), or 1 if the runtime cannot say.
-template <int EPI, int W, bool DEEP>
-int resident_e(size_t lds) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(gv_kernel<EPI, W, DEEP>()),
-                                                   W * WAVE, lds) != hipSuccess || n < 1)
-    n = 1;
-  return n;
-}
-
-template <int W, bool DEEP>
-int resident(int epi, size_t lds) {
-  switch (epi) {
-    case EPI_STORE: return resident_e<EPI_STORE, W, DEEP>(lds);
-    case EPI_ADD: return resident_e<EPI_ADD, W, DEEP>(lds);
-    case EPI_SWIGLU: return resident_e<EPI_SWIGLU, W, DEEP>(lds);
-    case EPI_QKV: return resident_e<EPI_QKV, W, DEEP>(lds);
-    default: return resident_e<EPI_LOGITS, W, DEEP>(lds);
-  }
-}
-
-int device_cus() {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
-    hipDeviceProp_t p;
-    cus = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&p, dev) == hipSuccess) ? p.multiProcessorCount : 256;
-  }
-  return cus;
+void launch_e(const GemvArgs &g, dim3 grid, size_t lds, hipStream_t st) {
+  constexpr int CH = 8 / gv_rows<EPI>();
+  const int nch = ((g.K + 511) / 512 + CH - 1) / CH;
+  const dim3 block(GV_WAVES * WAVE);
+  if (nch == 1) hipLaunchKernelGGL((gemv_kernel<EPI, 1>), grid, block, lds, st, g);
+  else if (nch == 2) hipLaunchKernelGGL((gemv_kernel<EPI, 2>), grid, block, lds, st, g);
+  else hipLaunchKernelGGL((gemv_kernel<EPI, 0>), grid, block, lds, st, g);
 }
 
 }  // namespace
 
-// Persistent grid shape: blocks of 4 or 8 waves, m blocks per compute unit
-// (m at most DEC_GEMV_BLOCKS_PER_CU and at most what fits in registers and
-// LDS at once), chosen so that the busiest compute unit has as few items as
-// possible (items spread evenly over the waves of evenly loaded CUs, no tail
-// round with idle waves), then for the most waves in flight.  Deep batches
-// when a wave owns a single item (nothing to pipeline across items) or there
-// are few waves per compute unit, if they fit.
-GemvShape gemv_shape(int n_items, int K, int epi) {
-  const int cus = device_cus();
-  const size_t lds = (size_t)K * 4;
-  GemvShape best{8, 1, 1, false};
-  long best_load = -1;
-  int best_waves = 0, best_m = 1;
-  for (int w : {8, 4}) {
-    const int fit = std::min(DEC_GEMV_BLOCKS_PER_CU, w == 8 ? resident<8, false>(epi, lds) : resident<4, false>(epi, lds));
-    for (int m = 1; m <= fit; ++m) {
-      const long waves = (long)cus * m * w;
-      const int per = (int)((n_items + waves - 1) / waves);
-      const int blocks = (n_items + w * per - 1) / (w * per);
-      // items on the busiest compute unit (blocks spread evenly over the CUs)
-      const long load = (long)((blocks + cus - 1) / cus) * w * per;
-      const int wpc = (int)((long)blocks * w / cus);
-      if (best_load < 0 || load < best_load || (load == best_load && wpc > best_waves)) {
-        best_load = load;
-        best_waves = wpc;
-        best_m = (blocks + cus - 1) / cus;
-        best = GemvShape{w, blocks, per, false};
-      }
-    }
-  }
-  if (best.per_wave == 1 || (long)best.blocks * best.waves <= 8L * cus) {
-    const int fit = best.waves == 8 ? resident<8, true>(epi, lds) : resident<4, true>(epi, lds);
-    best.deep = best_m <= fit;
-  }
-  return best;
-}
+int gemv_blocks(int n_items) { return (n_items + GV_WAVES - 1) / GV_WAVES; }
 
 hipError_t launch_gemv(const GemvArgs &g, int epi, hipStream_t st, int *blocks) {
-  const GemvShape sh = gemv_shape(g.n_items, g.K, epi);
-  if (blocks) *blocks = sh.blocks;
-  dim3 grid(sh.blocks, g.slot_expert ? g.n_slots : 1);
-  const size_t lds = (size_t)g.K * 4;
+  const int nb = gemv_blocks(g.n_items);
+  if (blocks) *blocks = nb;
+  const dim3 grid(nb, g.slot_expert ? g.n_slots : 1);
+  const size_t lds = gemv_lds(g.K);
   switch (epi) {
-    case EPI_STORE: return launch_e<EPI_STORE>(g, sh, grid, lds, st);
-    case EPI_ADD: return launch_e<EPI_ADD>(g, sh, grid, lds, st);
-    case EPI_SWIGLU: return launch_e<EPI_SWIGLU>(g, sh, grid, lds, st);
-    case EPI_QKV: return launch_e<EPI_QKV>(g, sh, grid, lds, st);
-    default: return launch_e<EPI_LOGITS>(g, sh, grid, lds, st);
+    case EPI_STORE: launch_e<EPI_STORE>(g, grid, lds, st); break;
+    case EPI_ADD: launch_e<EPI_ADD>(g, grid, lds, st); break;
+    case EPI_SWIGLU: launch_e<EPI_SWIGLU>(g, grid, lds, st); break;
+    case EPI_QKV: launch_e<EPI_QKV>(g, grid, lds, st); break;
+    default: launch_e<EPI_LOGITS>(g, grid, lds, st); break;
   }
+  return hipGetLastError();
 }

@@ -54,19 +54,10 @@ struct GemvArgs {
   int32_t *part_idx;
 };
 constexpr size_t GEMV_MAX_LDS = 60 * 1024;
-// GEMV launch shape: at most this many persistent blocks per compute unit,
-// and kilobytes per load batch (doubled for deep batches; tuned on the GPU)
-#ifndef DEC_GEMV_BLOCKS_PER_CU
-#define DEC_GEMV_BLOCKS_PER_CU 4
-#endif
-#ifndef DEC_GEMV_LOADS
-#define DEC_GEMV_LOADS 4
-#endif
-struct GemvShape {
-  int waves, blocks, per_wave;
-  bool deep;
-};
-GemvShape gemv_shape(int n_items, int K, int epi);
+// LDS of one GEMV block: the fp32 activation padded to whole 512-element steps
+inline size_t gemv_lds(int K) { return (size_t)(K + 511) / 512 * 512 * 4; }
+// blocks of a GEMV launch over n_items items (one argmax partial each for EPI_LOGITS)
+int gemv_blocks(int n_items);
 // `blocks` (optional) receives the grid size, i.e. the number of argmax
 // partials an EPI_LOGITS launch writes
 hipError_t launch_gemv(const GemvArgs &g, int epi, hipStream_t st, int *blocks = nullptr);
