@@ -245,52 +245,50 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 }
 
 // One block per (group, valid column), one thread per dim: combine the
-// group's splits in split order.  The splits' (m, l) pairs are staged in
-// LDS with one load per thread; each thread's O partials are independent
-// loads, so they are in flight together.
-constexpr int MERGE_MAX_SPLITS = 1024;
+// group's splits in split order.  Each chunk of MERGE_CHUNK splits is one
+// batch of independent loads ((m, l) and the thread's O value per split),
+// folded into running sums rescaled to the chunk's new maximum, so a merge
+// of up to MERGE_CHUNK splits is a single memory round trip.
 constexpr int MERGE_CHUNK = 32;
 
 template <int D, int PM>
 __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int ncols) {
-  __shared__ float sm[MERGE_MAX_SPLITS], sl[MERGE_MAX_SPLITS];
-  __shared__ float red[D / WAVE];
   const int gi = blockIdx.x / ncols, cc = blockIdx.x - gi * ncols;
   const int g = gi % a.Hkv, rg = gi / a.Hkv;
   const Col oc = column<PM>(a, rg, g, cc);
   if (!oc.valid) return;
-  const int nact = min((group_keys<PM>(a, rg, g) + a.kc - 1) / a.kc, MERGE_MAX_SPLITS);
+  const int nact = (group_keys<PM>(a, rg, g) + a.kc - 1) / a.kc;
   if (nact <= 1) return;                       // written directly by attn_kernel
   const int j = threadIdx.x;
   const float *ml = a.part_ml + ((int64_t)gi * a.n_splits * 16 + cc) * 2;
   const float *po = a.part_o + ((int64_t)gi * a.n_splits * 16 + cc) * D + j;
-  float mx = NEG_SENTINEL;
-  for (int s = j; s < nact; s += D) {
-    const float m = ml[(int64_t)s * 32], l = ml[(int64_t)s * 32 + 1];
-    sm[s] = m;
-    sl[s] = l;
-    mx = fmaxf(mx, m);
-  }
-  mx = wave_max(mx);
-  if ((j & (WAVE - 1)) == 0) red[j / WAVE] = mx;
-  __syncthreads();
-  float M = red[0];
-#pragma unroll
-  for (int w = 1; w < D / WAVE; ++w) M = fmaxf(M, red[w]);
-  // split order; a chunk of MERGE_CHUNK independent loads in flight at a time
-  float L = 0.f, o = 0.f;
+  float M = NEG_SENTINEL, L = 0.f, o = 0.f;
   for (int s0 = 0; s0 < nact; s0 += MERGE_CHUNK) {
-    float ov[MERGE_CHUNK];
-#pragma unroll
-    for (int u = 0; u < MERGE_CHUNK; ++u) ov[u] = po[(int64_t)min(s0 + u, nact - 1) * 16 * D];
+    float ms[MERGE_CHUNK], ls[MERGE_CHUNK], ov[MERGE_CHUNK];
 #pragma unroll
     for (int u = 0; u < MERGE_CHUNK; ++u) {
-      if (s0 + u < nact) {
-        const float sc = exp2f(sm[s0 + u] - M);
-        L += sc * sl[s0 + u];
-        o += sc * ov[u];
-      }
+      const int64_t s = min(s0 + u, nact - 1);
+      ms[u] = ml[s * 32];
+      ls[u] = ml[s * 32 + 1];
+      ov[u] = po[s * 16 * D];
     }
+    // splits past nact (clamped duplicates) get weight 0; every loaded
+    // value is used unconditionally, so no load is sunk into a branch
+#pragma unroll
+    for (int u = 0; u < MERGE_CHUNK; ++u) ms[u] = s0 + u < nact ? ms[u] : -INFINITY;
+    float cm = M;
+#pragma unroll
+    for (int u = 0; u < MERGE_CHUNK; ++u) cm = fmaxf(cm, ms[u]);
+    const float r = exp2f(M - cm);
+    L *= r;
+    o *= r;
+#pragma unroll
+    for (int u = 0; u < MERGE_CHUNK; ++u) {
+      const float sc = exp2f(ms[u] - cm);
+      L += sc * ls[u];
+      o += sc * ov[u];
+    }
+    M = cm;
   }
   store_out(a, ((int64_t)oc.row * a.Hq + oc.head) * D + j, o / L);
 }
@@ -321,6 +319,5 @@ hipError_t launch_d(const AttnArgs &a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs &a, int head_dim, hipStream_t st) {
-  if (a.n_splits > MERGE_MAX_SPLITS) return hipErrorInvalidValue;
   return head_dim == 128 ? launch_d<128>(a, st) : launch_d<64>(a, st);
 }

@@ -31,7 +31,6 @@
 
 namespace {
 
-constexpr int GV_WAVES = 8;  // waves per block
 
 template <int EPI>
 constexpr int gv_rows() {
@@ -203,7 +202,7 @@ __device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, in
   }
 }
 
-// One item per wave, GV_WAVES waves per block.  The wave's weight rows are
+// One item per wave, WV (4 or 8) waves per block.  The wave's weight rows are
 // streamed in chunks of CH 1 KB steps through two register buffers: the
 // first two chunks go out before the activation prologue, and each buffer
 // is refilled as soon as it has been consumed, so two chunks are always in
@@ -211,13 +210,13 @@ __device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, in
 // the activation is loaded ahead of the weights when it fits in registers,
 // so the prologue waits only for it.  NCH: the row's chunk count when it is
 // 1 or 2 (no refills), else 0 (the refill loop).
-template <int EPI, int NCH>
-__global__ __launch_bounds__(GV_WAVES * WAVE) void gemv_kernel(GemvArgs g) {
-  constexpr int NR = gv_rows<EPI>(), CH = 8 / NR, NT = GV_WAVES * WAVE;
+template <int EPI, int NCH, int WV>
+__global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs g) {
+  constexpr int NR = gv_rows<EPI>(), CH = 8 / NR, NT = WV * WAVE, PRN = 32 / WV, PRH = PRN / 2;
   extern __shared__ f32x4 xs[];  // activation, fp32 in the layout of xs_slot
-  __shared__ float sred[GV_WAVES];
-  __shared__ float bv_s[GV_WAVES];
-  __shared__ int bi_s[GV_WAVES];
+  __shared__ float sred[WV];
+  __shared__ float bv_s[WV];
+  __shared__ int bi_s[WV];
 
   const uint16_t *W = g.W;
   const float *xin = g.a_f32;
@@ -232,7 +231,7 @@ __global__ __launch_bounds__(GV_WAVES * WAVE) void gemv_kernel(GemvArgs g) {
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
   const int steps = (K + 511) / 512, nch = NCH ? NCH : (steps + CH - 1) / CH;
-  const int it = blockIdx.x * GV_WAVES + wave;
+  const int it = blockIdx.x * WV + wave;
   const bool valid = it < g.n_items;
   int rows[NR];
   const uint16_t *wp[NR];
@@ -241,18 +240,18 @@ __global__ __launch_bounds__(GV_WAVES * WAVE) void gemv_kernel(GemvArgs g) {
 
   // activation into registers first when it fits.  Mode 1: x and gamma
   // (RMSNorm); 2: fp32 x; 3: bf16 x; 0: read after the weights are issued.
-  const int mode = g.gamma ? (K <= 8 * NT ? 1 : 0) : xin ? (K <= 16 * NT ? 2 : 0) : (K <= 32 * NT ? 3 : 0);
+  const int mode = g.gamma ? (K <= PRH * 4 * NT ? 1 : 0) : xin ? (K <= PRN * 4 * NT ? 2 : 0) : (K <= PRN * 8 * NT ? 3 : 0);
   // (addresses picked by pointer selects, loads unconditional: a branch
   // around them would make the merge wait for the data)
-  u32x4 pr[4];
+  u32x4 pr[PRN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int k4 = min((int)(threadIdx.x + (i & 1) * NT) * 4, K - 4);
+  for (int i = 0; i < PRN; ++i) {
+    const int k1 = min((int)(threadIdx.x + (i % PRH) * NT) * 4, K - 4);
     const int k2 = min((int)(threadIdx.x + i * NT) * 4, K - 4);
-    const int k8 = min((int)(threadIdx.x + i * NT) * 8, K - 8);
-    const void *src = mode == 1 ? static_cast<const void *>((i < 2 ? xin : g.gamma) + k4)
+    const int k3 = min((int)(threadIdx.x + i * NT) * 8, K - 8);
+    const void *src = mode == 1 ? static_cast<const void *>((i < PRH ? xin : g.gamma) + k1)
                     : mode == 2 ? static_cast<const void *>(xin + k2)
-                    : mode == 3 ? static_cast<const void *>(g.a_bf16 + k8)
+                    : mode == 3 ? static_cast<const void *>(g.a_bf16 + k3)
                                 : static_cast<const void *>(gv_zero);
     pr[i] = load16(src);
   }
@@ -268,27 +267,27 @@ __global__ __launch_bounds__(GV_WAVES * WAVE) void gemv_kernel(GemvArgs g) {
   if (mode == 1) {
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < PRH; ++i) {
       const f32x4 v = as_f4(pr[i]);
       if ((int)(threadIdx.x + i * NT) * 4 < K) ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
     }
-    ss = block_sum<GV_WAVES>(ss, sred);
+    ss = block_sum<WV>(ss, sred);
     const float inv = 1.0f / sqrtf(ss / (float)K + g.eps);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < PRH; ++i) {
       const int k = (threadIdx.x + i * NT) * 4;
-      const f32x4 v = as_f4(pr[i]), w = as_f4(pr[2 + i]);
+      const f32x4 v = as_f4(pr[i]), w = as_f4(pr[PRH + i]);
       if (k < K) put4(k, f32x4{v[0] * inv * w[0], v[1] * inv * w[1], v[2] * inv * w[2], v[3] * inv * w[3]});
     }
   } else if (mode == 2) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < PRN; ++i) {
       const int k = (threadIdx.x + i * NT) * 4;
       if (k < K) put4(k, as_f4(pr[i]));
     }
   } else if (mode == 3) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < PRN; ++i) {
       const int k = (threadIdx.x + i * NT) * 8;
       const u32x4 w = pr[i];
       if (k < K) {
@@ -302,7 +301,7 @@ __global__ __launch_bounds__(GV_WAVES * WAVE) void gemv_kernel(GemvArgs g) {
       const f32x4 v = loadf4(xin + k);
       ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
     }
-    ss = block_sum<GV_WAVES>(ss, sred);
+    ss = block_sum<WV>(ss, sred);
     const float inv = 1.0f / sqrtf(ss / (float)K + g.eps);
     for (int k = threadIdx.x * 4; k < K; k += NT * 4) {
       const f32x4 v = loadf4(xin + k), w = loadf4(g.gamma + k);
@@ -349,7 +348,7 @@ __global__ __launch_bounds__(GV_WAVES * WAVE) void gemv_kernel(GemvArgs g) {
     if (threadIdx.x == 0) {
       float bv = bv_s[0];
       int bi = bi_s[0];
-      for (int w = 1; w < GV_WAVES; ++w)
+      for (int w = 1; w < WV; ++w)
         if (better(bv_s[w], bi_s[w], bv, bi)) {
           bv = bv_s[w];
           bi = bi_s[w];
@@ -360,31 +359,57 @@ __global__ __launch_bounds__(GV_WAVES * WAVE) void gemv_kernel(GemvArgs g) {
   }
 }
 
+template <int EPI, int WV>
+void launch_w(const GemvArgs &g, int nch, size_t lds, hipStream_t st) {
+  const dim3 grid((g.n_items + WV - 1) / WV, g.slot_expert ? g.n_slots : 1), block(WV * WAVE);
+  if (nch == 1) hipLaunchKernelGGL((gemv_kernel<EPI, 1, WV>), grid, block, lds, st, g);
+  else if (nch == 2) hipLaunchKernelGGL((gemv_kernel<EPI, 2, WV>), grid, block, lds, st, g);
+  else hipLaunchKernelGGL((gemv_kernel<EPI, 0, WV>), grid, block, lds, st, g);
+}
+
 template <int EPI>
-void launch_e(const GemvArgs &g, dim3 grid, size_t lds, hipStream_t st) {
+void launch_e(const GemvArgs &g, int wv, size_t lds, hipStream_t st) {
   constexpr int CH = 8 / gv_rows<EPI>();
   const int nch = ((g.K + 511) / 512 + CH - 1) / CH;
-  const dim3 block(GV_WAVES * WAVE);
-  if (nch == 1) hipLaunchKernelGGL((gemv_kernel<EPI, 1>), grid, block, lds, st, g);
-  else if (nch == 2) hipLaunchKernelGGL((gemv_kernel<EPI, 2>), grid, block, lds, st, g);
-  else hipLaunchKernelGGL((gemv_kernel<EPI, 0>), grid, block, lds, st, g);
+  if (wv == 4) launch_w<EPI, 4>(g, nch, lds, st);
+  else launch_w<EPI, 8>(g, nch, lds, st);
+}
+
+int device_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    hipDeviceProp_t p;
+    cus = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&p, dev) == hipSuccess) ? p.multiProcessorCount : 256;
+  }
+  return cus;
 }
 
 }  // namespace
 
-int gemv_blocks(int n_items) { return (n_items + GV_WAVES - 1) / GV_WAVES; }
+// Waves per block: 8, unless 4-wave blocks spread the items more evenly over
+// the compute units (fewer waves on the busiest one).
+int gemv_waves(int n_items) {
+  const int cus = device_cus();
+  auto busiest = [&](int wv) { return (((n_items + wv - 1) / wv + cus - 1) / cus) * wv; };
+  return busiest(4) < busiest(8) ? 4 : 8;
+}
+
+int gemv_blocks(int n_items) {
+  const int wv = gemv_waves(n_items);
+  return (n_items + wv - 1) / wv;
+}
 
 hipError_t launch_gemv(const GemvArgs &g, int epi, hipStream_t st, int *blocks) {
-  const int nb = gemv_blocks(g.n_items);
-  if (blocks) *blocks = nb;
-  const dim3 grid(nb, g.slot_expert ? g.n_slots : 1);
+  const int wv = gemv_waves(g.n_items);
+  if (blocks) *blocks = (g.n_items + wv - 1) / wv;
   const size_t lds = gemv_lds(g.K);
   switch (epi) {
-    case EPI_STORE: launch_e<EPI_STORE>(g, grid, lds, st); break;
-    case EPI_ADD: launch_e<EPI_ADD>(g, grid, lds, st); break;
-    case EPI_SWIGLU: launch_e<EPI_SWIGLU>(g, grid, lds, st); break;
-    case EPI_QKV: launch_e<EPI_QKV>(g, grid, lds, st); break;
-    default: launch_e<EPI_LOGITS>(g, grid, lds, st); break;
+    case EPI_STORE: launch_e<EPI_STORE>(g, wv, lds, st); break;
+    case EPI_ADD: launch_e<EPI_ADD>(g, wv, lds, st); break;
+    case EPI_SWIGLU: launch_e<EPI_SWIGLU>(g, wv, lds, st); break;
+    case EPI_QKV: launch_e<EPI_QKV>(g, wv, lds, st); break;
+    default: launch_e<EPI_LOGITS>(g, wv, lds, st); break;
   }
   return hipGetLastError();
 }

@@ -81,6 +81,8 @@ hipError_t launch_rmsnorm(const float *x, int64_t ldx, const float *g, int rows,
 // pipeline.rs ppl_ids).  Rows are processed in order, so when several rows of
 // one sequence are reduced in a launch the last row's token is the one kept.
 namespace {
+constexpr int FIN_BATCH = 16;
+
 __global__ __launch_bounds__(1024) void argmax_finalize_kernel(const float *pv, const int32_t *pi, int nparts,
                                                                int rows, int32_t *idx, int32_t *next_token,
                                                                const int32_t *row_seq) {
@@ -89,13 +91,24 @@ __global__ __launch_bounds__(1024) void argmax_finalize_kernel(const float *pv, 
   for (int r = blockIdx.x; r < rows; r += gridDim.x) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int p = threadIdx.x; p < nparts; p += blockDim.x) {
-      const float v = pv[(int64_t)r * nparts + p];
-      const int i = pi[(int64_t)r * nparts + p];
-      if (better(v, i, bv, bi)) {
-        bv = v;
-        bi = i;
+    // FIN_BATCH candidates per thread in flight at a time (clamped indices,
+    // so the loads are unconditional; the order of the comparisons does not
+    // matter, `better` being a total order on distinct indices)
+    for (int p0 = 0; p0 < nparts; p0 += FIN_BATCH * (int)blockDim.x) {
+      float v[FIN_BATCH];
+      int ix[FIN_BATCH];
+#pragma unroll
+      for (int u = 0; u < FIN_BATCH; ++u) {
+        const int p = min(p0 + u * (int)blockDim.x + (int)threadIdx.x, nparts - 1);
+        v[u] = pv[(int64_t)r * nparts + p];
+        ix[u] = pi[(int64_t)r * nparts + p];
       }
+#pragma unroll
+      for (int u = 0; u < FIN_BATCH; ++u)
+        if (better(v[u], ix[u], bv, bi)) {
+          bv = v[u];
+          bi = ix[u];
+        }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -130,6 +143,7 @@ __global__ __launch_bounds__(1024) void argmax_finalize_kernel(const float *pv, 
 hipError_t launch_argmax_finalize(const float *part_val, const int32_t *part_idx, int nparts, int rows,
                                   int32_t *idx, int32_t *next_token, const int32_t *row_seq,
                                   hipStream_t st) {
+  if (nparts < 1 || rows < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(1024), 0, st, part_val, part_idx, nparts, rows, idx,
                      next_token, row_seq);
   return hipGetLastError();
