@@ -193,7 +193,9 @@ def summarize_counters(fetch_csv, write_csv, kernel_pattern, copy_bytes, algo_by
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256, help="timed decode steps")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed decode steps (default: the workload's decode steps minus the first "
+                         "step and the warmup)")
     ap.add_argument("--warmup", type=int, default=3, help="untimed decode steps before timing")
     ap.add_argument("--workload", default="8b", help="8b (default), 135m, tiny, moe, longctx")
     ap.add_argument("--prefill-runs", type=int, default=5, help="timed whole-prompt prefills (median)")
@@ -243,6 +245,15 @@ def main():
     from synth.workloads import WORKLOADS
 
     shape, work = WORKLOADS[args.workload]
+    # the first decode step (reported on its own), the warmup and the timed
+    # steps together make the workload's decode steps
+    if args.steps is None:
+        args.steps = max(1, work.decode_steps - args.warmup - 1)
+    room = shape.max_seq - (work.prompt or work.context)
+    if 1 + args.warmup + args.steps > room:
+        log(f"{shape.name}: 1 + {args.warmup} warmup + {args.steps} timed decode steps exceed the "
+            f"{room} positions left after the prompt (max_seq {shape.max_seq})")
+        return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()
@@ -375,7 +386,7 @@ def main():
         "value": round(tok_s, 2),
         "ms_per_step": round(t_dec / args.steps * 1e3, 4),
         "config": {"workload": shape.name, "global_batch": batch, "decode_positions":
-                   [work.prompt or work.context, (work.prompt or work.context) + args.warmup + args.steps],
+                   [work.prompt or work.context, (work.prompt or work.context) + 1 + args.warmup + args.steps],
                    "kv_prefix": "prefill" if prefill else "synthetic N(0,1)",
                    "prefill_prompt": work.prompt, "prefill_chunk": work.chunk, "parallelism": "single-gpu"},
         "decode": {"tok_s": tok_s, "first_step_ms": round(first_ms, 3), "hbm_GBps": step_bytes / (t_dec / args.steps) / 1e9,
