@@ -26,6 +26,11 @@ constexpr int ATTN_TARGET_BLOCKS = 1024;
 constexpr int ATTN_MAX_TASKS = 8192;
 constexpr int GEMM_MAX_SPLIT = 8;
 constexpr int CHUNK_MIN_ROWS = 16;   // more rows than this take the chunk projection kernel
+// Batched decode: from this many rows, projections whose weights are at least
+// CHUNK_BATCH_MIN_BYTES also take the chunk kernel (measured on the 8B shape
+// at 8 and 16 rows: faster for qkv, gate_up and down; not for the 33.5 MB o_proj)
+constexpr int CHUNK_BATCH_MIN_ROWS = 8;
+constexpr double CHUNK_BATCH_MIN_BYTES = 40e6;
 constexpr int CHUNK_MAX_SPLIT = 16;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -42,8 +47,8 @@ struct Layout {
 };
 
 // Weight matrices that get a packed copy for the chunk projection kernel:
-// only when prefill chunks can exceed the small-row kernels, and only the
-// shapes the packed tiles cover.  Order within a layer: qkv, o, gate_up /
+// only when prefill chunks or decode batches can reach the chunk kernel, and
+// only the shapes the packed tiles cover.  Order within a layer: qkv, o, gate_up /
 // shared gate_up, down / shared down.
 struct PackSpec {
   int64_t rows[4];
@@ -52,7 +57,7 @@ struct PackSpec {
 
 PackSpec pack_spec(const decoder_config_t *c) {
   PackSpec p{};
-  if (c->max_chunk <= CHUNK_MIN_ROWS) return p;
+  if (c->max_chunk <= CHUNK_MIN_ROWS && c->max_batch < CHUNK_BATCH_MIN_ROWS) return p;
   const int d = c->head_dim, H = c->hidden, qd = c->n_heads * d, qkvr = (c->n_heads + 2 * c->n_kv_heads) * d;
   const int I = c->n_experts > 0 ? c->shared_inter : c->ffn_inter;
   const int64_t rows[4] = {qkvr, H, 2 * (int64_t)I, I > 0 ? H : 0};
@@ -316,7 +321,9 @@ int proj(decoder *D, int node, int epi, GemmArgs g, int max_rows) {
       D->act_rows = g.M;
     }
   };
-  if (g.M > CHUNK_MIN_ROWS && gemm_chunk_fits(g, epi)) {
+  const bool chunk_rows =
+      g.M > CHUNK_MIN_ROWS || (g.M >= CHUNK_BATCH_MIN_ROWS && npd * ncols * (double)g.K * 2 >= CHUNK_BATCH_MIN_BYTES);
+  if (chunk_rows && gemm_chunk_fits(g, epi)) {
     // chunk kernel: split K so that the blocks (weight tiles x row blocks x
     // splits) fill the compute units about once, with at least two 64-wide k
     // steps per split (fewer, longer blocks measured faster than two rounds)

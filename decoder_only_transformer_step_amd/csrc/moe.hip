@@ -15,19 +15,28 @@
 namespace {
 
 constexpr int ROUTE_THREADS = 256;
+constexpr int GROUP_MAX_PAIRS = 2048;  // rows x k (rows <= 256, k <= 8)
 
-// One block per row: softmax, top-k, shared gate.
-__global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(MoeRouteArgs a) {
-  __shared__ float lg[256];
-  __shared__ float red[4];
-  __shared__ int taken[256];
-  const int r = blockIdx.x, E = a.E;
-  const float *row = a.logits + (int64_t)r * E;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    lg[e] = row[e];
-    taken[e] = 0;
+// (value, index) of the better of two candidates under `better`
+__device__ __forceinline__ void wave_best(float &v, int &i) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(v, o, WAVE);
+    const int oi = __shfl_xor(i, o, WAVE);
+    if (better(ov, oi, v, i)) {
+      v = ov;
+      i = oi;
+    }
   }
-  __syncthreads();
+}
+
+// One block per row.  All threads take the shared-gate dot product; the
+// first wave then routes: lane l holds experts l, l + 64, l + 128, l + 192,
+// the softmax max and sum are wave reductions, and each of the k picks is a
+// wave arg-max over the experts not yet taken.
+__global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(MoeRouteArgs a) {
+  __shared__ float red[ROUTE_THREADS / WAVE];
+  const int r = blockIdx.x, E = a.E;
   // shared-expert gate: sigmoid(w_sg . b), fp32 dot in fixed order
   float dot = 0.f;
   if (a.w_sh_gate) {
@@ -41,41 +50,65 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(MoeRouteArgs a
     }
   }
   dot = block_sum<ROUTE_THREADS / WAVE>(dot, red);
-  if (threadIdx.x == 0) {
-    float m = -INFINITY;
-    for (int e = 0; e < E; ++e) m = fmaxf(m, lg[e]);
-    float z = 0.f;
-    for (int e = 0; e < E; ++e) z += expf(lg[e] - m);
-    float sel = 0.f;
-    int32_t *ids = a.ids + (int64_t)r * a.k;
-    float *w = a.wts + (int64_t)r * a.k;
-    for (int j = 0; j < a.k; ++j) {
-      int best = -1;
-      for (int e = 0; e < E; ++e)
-        if (!taken[e] && (best < 0 || lg[e] > lg[best])) best = e;
-      taken[best] = 1;
-      ids[j] = best;
-      w[j] = expf(lg[best] - m) / z;
-      sel += w[j];
+  if (threadIdx.x >= WAVE) return;
+  const int lane = threadIdx.x;
+  const float *row = a.logits + (int64_t)r * E;
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + WAVE * i;
+    v[i] = row[min(e, E - 1)];
+    if (e >= E) v[i] = -INFINITY;
+  }
+  const float m = wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+  float zs = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) zs += lane + WAVE * i < E ? expf(v[i] - m) : 0.f;
+  const float z = wave_sum(zs);
+  int32_t *ids = a.ids + (int64_t)r * a.k;
+  float *w = a.wts + (int64_t)r * a.k;
+  float wsel[8], sel = 0.f;
+  int isel[8];
+  unsigned taken = 0;
+  for (int j = 0; j < a.k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + WAVE * i;
+      if (e < E && !(taken >> i & 1u) && better(v[i], e, bv, bi)) {
+        bv = v[i];
+        bi = e;
+      }
     }
-    if (a.renorm)
-      for (int j = 0; j < a.k; ++j) w[j] /= sel;
-    if (a.ids_record)
-      for (int j = 0; j < a.k; ++j) a.ids_record[(int64_t)r * a.k + j] = ids[j];
+    wave_best(bv, bi);
+    if (bi % WAVE == lane) taken |= 1u << (bi / WAVE);
+    isel[j] = bi;
+    wsel[j] = expf(bv - m) / z;
+    sel += wsel[j];
+  }
+  if (lane == 0) {
+    for (int j = 0; j < a.k; ++j) {
+      ids[j] = isel[j];
+      w[j] = a.renorm ? wsel[j] / sel : wsel[j];
+      if (a.ids_record) a.ids_record[(int64_t)r * a.k + j] = isel[j];
+    }
     if (a.gate) a.gate[r] = a.w_sh_gate ? 1.0f / (1.0f + expf(-dot)) : 1.0f;
   }
 }
 
 // One block: group table over experts in increasing order, pairs by row.
+// The ids are staged in LDS; counts by LDS atomics; a pair's slot in its
+// expert's group is the number of earlier pairs with the same expert.
 __global__ __launch_bounds__(256) void moe_group_kernel(MoeRouteArgs a) {
+  __shared__ int ids_s[GROUP_MAX_PAIRS];
   __shared__ int cnt[256];
   __shared__ int start[256];
   const int E = a.E, P = a.rows * a.k;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int c = 0;
-    for (int p = 0; p < P; ++p) c += (a.ids[p] == e);
-    cnt[e] = c;
-  }
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  for (int p = threadIdx.x; p < P; p += blockDim.x) ids_s[p] = a.ids[p];
+  __syncthreads();
+  for (int p = threadIdx.x; p < P; p += blockDim.x) atomicAdd(&cnt[ids_s[p]], 1);
   __syncthreads();
   if (threadIdx.x == 0) {
     int s = 0, ng = 0;
@@ -92,33 +125,43 @@ __global__ __launch_bounds__(256) void moe_group_kernel(MoeRouteArgs a) {
     *a.n_groups = ng;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int o = start[e];
-    for (int p = 0; p < P; ++p)
-      if (a.ids[p] == e) {
-        a.pair_row[o] = p / a.k;
-        a.pair_of[p] = o;
-        ++o;
-      }
+  for (int p = threadIdx.x; p < P; p += blockDim.x) {
+    const int e = ids_s[p];
+    int rank = 0;
+    for (int q = 0; q < p; ++q) rank += ids_s[q] == e;
+    const int o = start[e] + rank;
+    a.pair_row[o] = p / a.k;
+    a.pair_of[p] = o;
   }
 }
 
+// x[r][c] += sum_j w_j y[pair(r, j)][c] + gate_r ysh[r][c]; grid (columns / 256, rows)
 __global__ __launch_bounds__(256) void moe_combine_kernel(float *x, const float *y, const float *ysh,
                                                          const float *wts, const float *gate,
                                                          const int32_t *pair_of, int k, int H) {
-  const int r = blockIdx.x;
-  float *xr = x + (int64_t)r * H;
-  for (int c = threadIdx.x; c < H; c += blockDim.x) {
-    float acc = 0.f;
-    for (int j = 0; j < k; ++j) acc += wts[r * k + j] * y[(int64_t)(pair_of ? pair_of[r * k + j] : r * k + j) * H + c];
-    if (ysh) acc += gate[r] * ysh[(int64_t)r * H + c];
-    xr[c] += acc;
+  const int r = blockIdx.y, c = blockIdx.x * blockDim.x + threadIdx.x;
+  float w[8];
+  int64_t pr[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int jj = min(j, k - 1);
+    w[j] = wts[r * k + jj];
+    pr[j] = pair_of ? pair_of[r * k + jj] : r * k + jj;
   }
+  const float gs = ysh ? gate[r] : 0.f;
+  if (c >= H) return;
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < k) acc += w[j] * y[pr[j] * H + c];
+  if (ysh) acc += gs * ysh[(int64_t)r * H + c];
+  x[(int64_t)r * H + c] += acc;
 }
 
 }  // namespace
 
 hipError_t launch_moe_route(const MoeRouteArgs &a, bool group, hipStream_t st) {
+  if (a.E > 256 || a.k > 8 || (group && a.rows * a.k > GROUP_MAX_PAIRS)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(moe_route_kernel, dim3(a.rows), dim3(ROUTE_THREADS), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !group) return e;
@@ -129,7 +172,8 @@ hipError_t launch_moe_route(const MoeRouteArgs &a, bool group, hipStream_t st) {
 hipError_t launch_moe_combine(float *x, const float *y, const float *ysh, const float *wts,
                               const float *gate, const int32_t *pair_of, int rows, int k, int H,
                               hipStream_t st) {
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(rows), dim3(256), 0, st, x, y, ysh, wts, gate,
+  if (k < 1 || k > 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((H + 255) / 256, rows), dim3(256), 0, st, x, y, ysh, wts, gate,
                      pair_of, k, H);
   return hipGetLastError();
 }
