@@ -128,6 +128,7 @@ enum {
   EPI_SWIGLU = 2,    // H[m][n] = split(silu(acc_gate) * acc_up)   gate rows n, up rows n + N
   EPI_QKV = 3,       // bias + RoPE; q -> bf16 buffer, k/v -> KV cache
   EPI_LOGITS = 4,    // C = acc (fp32 logits) and each tile's greedy candidate per row
+  EPI_MOE_ADD = 5,   // batch-1 GEMV only: C[n] += sum_j w_j y_j[n] + gate * acc (MoE combine)
 };
 
 struct QkvEpi {

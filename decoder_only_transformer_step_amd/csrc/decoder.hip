@@ -469,10 +469,11 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
 
 // Launch one batch-1 projection (GEMV) as node `node`.
 int gemv(decoder *D, int node, int epi, const GemvArgs &g, int *blocks = nullptr) {
-  if (epi == EPI_ADD) D->act_norm = nullptr;  // x changes
+  if (epi == EPI_ADD || epi == EPI_MOE_ADD) D->act_norm = nullptr;  // x changes
   const double nr = (epi == EPI_SWIGLU || epi == EPI_QKV) ? 2.0 : 1.0;
   const double slots = g.slot_expert ? g.n_slots : 1;
-  NodeTimer timer(D, node, slots * (nr * g.n_items * (double)g.K * 2 + g.K * 4.0 + g.n_items * 4.0 * (epi == EPI_ADD ? 2 : 1)),
+  const double out_words = epi == EPI_ADD ? 2 : epi == EPI_MOE_ADD ? 2 + g.moe_k : 1;
+  NodeTimer timer(D, node, slots * (nr * g.n_items * (double)g.K * 2 + g.K * 4.0 + g.n_items * 4.0 * out_words),
                   slots * 2.0 * nr * g.n_items * (double)g.K);
   hipError_t e = launch_gemv(g, epi, D->stream, blocks);
   if (e != hipSuccess) return hip_fail(D, e, "gemv");
@@ -533,16 +534,19 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
     if ((rc = gemv(D, DEC_NODE_GATE_UP, EPI_SWIGLU, gu))) return rc;
     return gemv(D, DEC_NODE_DOWN, EPI_ADD, gemv_args(W.w_down, D->f32_h, I, H, D->x));
   }
+  // MoE FFN for one row: the FFN RMSNorm runs inside the router GEMV, the
+  // route kernel and the expert GEMVs (each from x); the shared expert's
+  // down projection also does the combine into x
   const int E = c.n_experts, k = c.top_k, Ie = c.expert_inter, Is = c.shared_inter;
-  {
-    NodeTimer t(D, DEC_NODE_NORM, H * 12.0, H * 4.0);
-    e = launch_rmsnorm(D->x, H, W.ffn_norm, 1, H, eps, nullptr, H, 0, D->stream, D->f32_act);
-  }
-  if (e != hipSuccess) return hip_fail(D, e, "rmsnorm");
-  if ((rc = gemv(D, DEC_NODE_ROUTER, EPI_STORE, gemv_args(W.w_router, D->f32_act, H, E, D->rlogits)))) return rc;
+  GemvArgs rg = gemv_args(W.w_router, D->x, H, E, D->rlogits);
+  rg.gamma = W.ffn_norm;
+  rg.eps = eps;
+  if ((rc = gemv(D, DEC_NODE_ROUTER, EPI_STORE, rg))) return rc;
   MoeRouteArgs mr{};
   mr.logits = D->rlogits;
-  mr.act_f32 = D->f32_act;
+  mr.act_f32 = D->x;
+  mr.gamma = W.ffn_norm;
+  mr.eps = eps;
   mr.w_sh_gate = (Is > 0 && c.shared_gate) ? W.w_sh_gate : nullptr;
   mr.rows = 1;
   mr.E = E;
@@ -558,7 +562,9 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
     e = launch_moe_route(mr, false, D->stream);
   }
   if (e != hipSuccess) return hip_fail(D, e, "moe_route");
-  GemvArgs eg = gemv_args(W.w_exp_gate_up, D->f32_act, H, Ie, D->f32_hexp);
+  GemvArgs eg = gemv_args(W.w_exp_gate_up, D->x, H, Ie, D->f32_hexp);
+  eg.gamma = W.ffn_norm;
+  eg.eps = eps;
   eg.slot_expert = D->rids;
   eg.n_slots = k;
   eg.w_group_stride = (int64_t)2 * Ie * H;
@@ -572,8 +578,16 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
   ed.ldc = H;
   if ((rc = gemv(D, DEC_NODE_EXPERTS, EPI_STORE, ed))) return rc;
   if (Is > 0) {
-    if ((rc = gemv(D, DEC_NODE_EXPERTS, EPI_SWIGLU, gemv_args(W.w_sh_gate_up, D->f32_act, H, Is, D->f32_h)))) return rc;
-    if ((rc = gemv(D, DEC_NODE_EXPERTS, EPI_STORE, gemv_args(W.w_sh_down, D->f32_h, Is, H, D->ysh)))) return rc;
+    GemvArgs sg = gemv_args(W.w_sh_gate_up, D->x, H, Is, D->f32_h);
+    sg.gamma = W.ffn_norm;
+    sg.eps = eps;
+    if ((rc = gemv(D, DEC_NODE_EXPERTS, EPI_SWIGLU, sg))) return rc;
+    GemvArgs sd = gemv_args(W.w_sh_down, D->f32_h, Is, H, D->x);
+    sd.moe_y = D->yexp;
+    sd.moe_w = D->rwts;
+    sd.moe_gate = D->rgate;
+    sd.moe_k = k;
+    return gemv(D, DEC_NODE_EXPERTS, EPI_MOE_ADD, sd);
   }
   NodeTimer tcomb(D, DEC_NODE_EXPERTS, H * (8.0 + 4.0 * k + 4.0), H * 2.0 * (k + 1));
   D->act_norm = nullptr;

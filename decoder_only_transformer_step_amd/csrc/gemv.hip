@@ -116,6 +116,7 @@ __device__ __forceinline__ void fma_batch(float (&acc)[R], const u32x4 (&v)[UNR]
 // issued so that the epilogue itself waits on nothing.
 struct ItemPre {
   float a, b, c, e;
+  float mw[8], my[8];  // EPI_MOE_ADD: routed weights and outputs of the item's row
 };
 
 template <int EPI>
@@ -123,8 +124,17 @@ __device__ __forceinline__ ItemPre item_prefetch(const GemvArgs &g, int out_row,
   // loads through pointer selects (a missing bias reads the zero page): a
   // branch around a load would make the merge wait for it
   const float *zf = reinterpret_cast<const float *>(gv_zero);
-  ItemPre p{0.f, 0.f, 0.f, 0.f};
-  if (EPI == EPI_STORE) {
+  ItemPre p{};
+  if (EPI == EPI_MOE_ADD) {
+    p.a = g.C[r0];
+    p.b = *g.moe_gate;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int jj = min(j, g.moe_k - 1);
+      p.mw[j] = g.moe_w[jj];
+      p.my[j] = g.moe_y[(int64_t)jj * g.N + r0];
+    }
+  } else if (EPI == EPI_STORE) {
     p.a = *(g.bias ? g.bias + r0 : zf);
   } else if (EPI == EPI_ADD) {
     p.a = g.C[r0];
@@ -163,6 +173,14 @@ __device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, in
     g.C[(int64_t)out_row * g.ldc + r0] = v0 + pre.a;
   } else if (EPI == EPI_ADD) {
     g.C[r0] = pre.a + v0;
+  } else if (EPI == EPI_MOE_ADD) {
+    // the combine's order: routed slots in router order, then the shared expert
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < g.moe_k) acc += pre.mw[j] * pre.my[j];
+    acc += pre.b * v0;
+    g.C[r0] = pre.a + acc;
   } else if (EPI == EPI_SWIGLU) {
     g.C[(int64_t)out_row * g.ldc + r0] = silu_f(v0) * v1;
   } else if (EPI == EPI_LOGITS) {
@@ -409,6 +427,10 @@ hipError_t launch_gemv(const GemvArgs &g, int epi, hipStream_t st, int *blocks) 
     case EPI_ADD: launch_e<EPI_ADD>(g, wv, lds, st); break;
     case EPI_SWIGLU: launch_e<EPI_SWIGLU>(g, wv, lds, st); break;
     case EPI_QKV: launch_e<EPI_QKV>(g, wv, lds, st); break;
+    case EPI_MOE_ADD:
+      if (!g.moe_y || !g.moe_w || !g.moe_gate || g.moe_k < 1 || g.moe_k > 8 || g.slot_expert) return hipErrorInvalidValue;
+      launch_e<EPI_MOE_ADD>(g, wv, lds, st);
+      break;
     default: launch_e<EPI_LOGITS>(g, wv, lds, st); break;
   }
   return hipGetLastError();

@@ -52,6 +52,10 @@ struct GemvArgs {
   QkvEpi qkv;                 // EPI_QKV
   float *part_val;            // EPI_LOGITS: best logit of each block
   int32_t *part_idx;
+  // EPI_MOE_ADD: routed expert outputs y [k][N], their weights w [k] and the
+  // shared-expert scale gate [1] (the kernel's own rows are the shared expert's)
+  const float *moe_y, *moe_w, *moe_gate;
+  int32_t moe_k;
 };
 constexpr size_t GEMV_MAX_LDS = 60 * 1024;
 // LDS of one GEMV block: the fp32 activation padded to whole 512-element steps
@@ -122,6 +126,8 @@ struct MoeRouteArgs {
   const uint16_t *act;     // split bf16 [rows][H] normed FFN input (for the shared gate)
   int64_t act_lo;
   const float *act_f32;    // or fp32 [rows][H] when set
+  const float *gamma;      // with act_f32: act_f32 is the raw residual x, normed here (RMSNorm, gain gamma)
+  float eps;
   const uint16_t *w_sh_gate;  // bf16 [H] or null
   int32_t rows, E, k, H, renorm;
   int32_t *ids;            // [rows][k]

@@ -40,7 +40,15 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(MoeRouteArgs a
   // shared-expert gate: sigmoid(w_sg . b), fp32 dot in fixed order
   float dot = 0.f;
   if (a.w_sh_gate) {
-    if (a.act_f32) {
+    if (a.act_f32 && a.gamma) {
+      // b = RMSNorm(x) computed here: fp32 mean square, then the gain
+      const float *x = a.act_f32 + (int64_t)r * a.H;
+      float ss = 0.f;
+      for (int j = threadIdx.x; j < a.H; j += blockDim.x) ss += x[j] * x[j];
+      ss = block_sum<ROUTE_THREADS / WAVE>(ss, red);
+      const float inv = 1.0f / sqrtf(ss / (float)a.H + a.eps);
+      for (int j = threadIdx.x; j < a.H; j += blockDim.x) dot += (x[j] * inv * a.gamma[j]) * bf16_to_f32(a.w_sh_gate[j]);
+    } else if (a.act_f32) {
       const float *b = a.act_f32 + (int64_t)r * a.H;
       for (int j = threadIdx.x; j < a.H; j += blockDim.x) dot += b[j] * bf16_to_f32(a.w_sh_gate[j]);
     } else {
