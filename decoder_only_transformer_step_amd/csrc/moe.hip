@@ -41,13 +41,33 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(MoeRouteArgs a
   float dot = 0.f;
   if (a.w_sh_gate) {
     if (a.act_f32 && a.gamma) {
-      // b = RMSNorm(x) computed here: fp32 mean square, then the gain
+      // b = RMSNorm(x) computed here: fp32 mean square, then the gain.  Eight
+      // elements per thread per round, loads unconditional (clamped index,
+      // masked in the sum) so that they are all in flight together.
       const float *x = a.act_f32 + (int64_t)r * a.H;
+      const int H = a.H;
       float ss = 0.f;
-      for (int j = threadIdx.x; j < a.H; j += blockDim.x) ss += x[j] * x[j];
+      for (int j0 = threadIdx.x; j0 < H; j0 += 8 * ROUTE_THREADS) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = x[min(j0 + u * ROUTE_THREADS, H - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ss += j0 + u * ROUTE_THREADS < H ? v[u] * v[u] : 0.f;
+      }
       ss = block_sum<ROUTE_THREADS / WAVE>(ss, red);
-      const float inv = 1.0f / sqrtf(ss / (float)a.H + a.eps);
-      for (int j = threadIdx.x; j < a.H; j += blockDim.x) dot += (x[j] * inv * a.gamma[j]) * bf16_to_f32(a.w_sh_gate[j]);
+      const float inv = 1.0f / sqrtf(ss / (float)H + a.eps);
+      for (int j0 = threadIdx.x; j0 < H; j0 += 8 * ROUTE_THREADS) {
+        float v[8], gm[8], wg[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int j = min(j0 + u * ROUTE_THREADS, H - 1);
+          v[u] = x[j];
+          gm[u] = a.gamma[j];
+          wg[u] = bf16_to_f32(a.w_sh_gate[j]);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) dot += j0 + u * ROUTE_THREADS < H ? (v[u] * inv * gm[u]) * wg[u] : 0.f;
+      }
     } else if (a.act_f32) {
       const float *b = a.act_f32 + (int64_t)r * a.H;
       for (int j = threadIdx.x; j < a.H; j += blockDim.x) dot += b[j] * bf16_to_f32(a.w_sh_gate[j]);

@@ -2,6 +2,8 @@
 // cast of the projection input fused in) for the chunk-sized row counts,
 // and the transposing import of a V-cache prefix.  All are HBM/latency bound
 // and move each element once; reductions run in a fixed order.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -144,8 +146,8 @@ hipError_t launch_argmax_finalize(const float *part_val, const int32_t *part_idx
                                   int32_t *idx, int32_t *next_token, const int32_t *row_seq,
                                   hipStream_t st) {
   if (nparts < 1 || rows < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(1024), 0, st, part_val, part_idx, nparts, rows, idx,
-                     next_token, row_seq);
+  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(std::min(rows, 1024)), dim3(1024), 0, st, part_val, part_idx,
+                     nparts, rows, idx, next_token, row_seq);
   return hipGetLastError();
 }
 
