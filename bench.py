@@ -190,6 +190,38 @@ def summarize_counters(fetch_csv, write_csv, kernel_pattern, copy_bytes, algo_by
     open(out, "w").write("\n".join(lines) + "\n")
 
 
+def summarize_mfma(pmc_csv, out, commands):
+    """MFMA work of the prefill chunk projections from one rocprofv3 --pmc run
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts bf16 MFMA work in units of 512 flops;
+    durations from the same run's dispatch timestamps)."""
+    import collections
+    import csv
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(dict)
+    for r in csv.DictReader(open(pmc_csv)):
+        name = r["Kernel_Name"].replace("void ", "").replace("(anonymous namespace)::", "")
+        name = re.sub(r"\([^()]*\)$", "", name)
+        vals[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        dur[name][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    lines = ["# MFMA work of the prefill chunk projections (rocprofv3 --pmc)", "",
+             "Command (from the repository root):", "", "```"] + commands + ["```", "",
+             "`gemm_chunk_kernel<MT, EPI, SPLIT>`: EPI 1 = residual add (o_proj, down), 2 = SwiGLU "
+             "(gate_up), 3 = QKV. The activations enter the MFMAs as two bf16 planes, so the executed "
+             "flops are twice the algorithmic 2 M N K.", "",
+             f"peak: {MFMA_BF16_PEAK_TFS:.0f} TFLOP/s dense bf16", "",
+             "| kernel | dispatches | avg us (counter run) | MFMA flops / dispatch | executed TFLOP/s | "
+             "% of peak | algorithmic % of peak | MFMA-busy cycles / dispatch |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for name, v in sorted(vals.items()):
+        mops = statistics.mean(v["SQ_INSTS_VALU_MFMA_MOPS_BF16"])
+        busy = statistics.mean(v["SQ_VALU_MFMA_BUSY_CYCLES"]) if v.get("SQ_VALU_MFMA_BUSY_CYCLES") else float("nan")
+        t = statistics.mean(dur[name].values())
+        tfs = mops * 512 / t / 1e12
+        lines.append(f"| `{name}` | {len(dur[name])} | {t * 1e6:.2f} | {mops * 512:.4g} | {tfs:.1f} | "
+                     f"{100 * tfs / MFMA_BF16_PEAK_TFS:.1f} | {50 * tfs / MFMA_BF16_PEAK_TFS:.1f} | {busy:.4g} |")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,6 +250,8 @@ def main():
     ap.add_argument("--algo-bytes", type=float, default=0.0)
     ap.add_argument("--copy-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--plain-json", help="with --summarize-stats: the bench line of an unprofiled run")
+    ap.add_argument("--summarize-mfma", metavar="PMC_CSV",
+                    help="write the MFMA summary of a --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 run (with --out, --command)")
     ap.add_argument("--out")
     ap.add_argument("--command", action="append", default=[])
     args = ap.parse_args()
@@ -225,6 +259,9 @@ def main():
     if args.summarize_stats:
         summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.out, "\n".join(args.command),
                         args.plain_json)
+        return 0
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, args.out, args.command)
         return 0
     if args.summarize_counters:
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.kernel, args.copy_bytes,
