@@ -18,10 +18,11 @@
 //    with d/16 MFMAs.  Q and P enter the MFMAs as split bf16 (hi and lo
 //    products), so only the cache itself is bf16-limited.
 //  * V is stored transposed in the cache ([dim][position]), so the A operand
-//    of the PV product is two 8-byte loads per lane, and the B operand
-//    (P^T) is exactly the lane's own scores: the MFMA k index is mapped to
-//    keys {4 (l/16) + j, 16 + 4 (l/16) + j}, the layout the QK product
-//    leaves them in.  No LDS round trip, no cross-lane shuffles for P.
+//    of the PV product is one 16-byte load per lane (8 consecutive keys of
+//    a dim row), and the B operand (P^T) is exactly the lane's own scores:
+//    the K rows of the QK product are permuted so that it leaves each lane
+//    the scores of the same 8 consecutive keys.  No LDS round trip, no
+//    cross-lane shuffles for P.
 //  * The 4 waves merge through LDS (log-sum-exp); with one split the block
 //    normalises and writes the output.  With several, each block writes its
 //    (m, l, O) partial and attn_merge combines them in split order, so the
@@ -110,24 +111,25 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const uint16_t *kb = a.kcache + (int64_t)seq * a.seq_stride + a.layer_off + (int64_t)g * a.S * D;
   const uint16_t *vb = a.vcache + (int64_t)seq * a.seq_stride + a.layer_off + (int64_t)g * D * a.S;
 
-  // K / V tile loads of the 32 keys at t (K rows straight into MFMA A
-  // operands; V^T rows as two 8-byte pieces per lane)
+  // K / V tile loads of the 32 keys at t.  K rows go straight into MFMA A
+  // operands, permuted so that the QK product leaves lane l the scores of
+  // keys 8 (l / 16) + 0..3 (s0) and 8 (l / 16) + 4..7 (s1): MFMA row m of s0
+  // is key 8 (m / 4) + m % 4, of s1 key 8 (m / 4) + 4 + m % 4.  The PV
+  // product then takes P^T as the lane's own 8 consecutive keys, and V^T as
+  // one contiguous 16-byte load per lane (64 bytes of a dim row per quad).
   u32x4 ka[D / 32], kh[D / 32];
-  u32x2 va[NDT], vh[NDT];
+  u32x4 va[NDT];
   auto load_tile = [&](int t) {
-    const uint16_t *k_lo = kb + (int64_t)(t + c) * D + quad * 8;
-    const uint16_t *k_hi = k_lo + 16 * D;
+    const int kr = 8 * (c >> 2) + (c & 3);
+    const uint16_t *k_lo = kb + (int64_t)(t + kr) * D + quad * 8;
+    const uint16_t *k_hi = k_lo + 4 * D;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
       ka[ks] = load16(k_lo + ks * 32);
       kh[ks] = load16(k_hi + ks * 32);
     }
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const uint16_t *vr = vb + (int64_t)(dt * 16 + c) * a.S + t + quad * 4;
-      va[dt] = load8(vr);
-      vh[dt] = load8(vr + 16);
-    }
+    for (int dt = 0; dt < NDT; ++dt) va[dt] = load16(vb + (int64_t)(dt * 16 + c) * a.S + t + quad * 8);
   };
   // the first tile goes out before q (a wave without a tile of its own
   // reloads the split's first tile, which stays inside the cache rows)
@@ -160,12 +162,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       s1 = mfma16x16x32(as_bf16x8(kh[ks]), as_bf16x8(qf[ks]), s1);
       s1 = mfma16x16x32(as_bf16x8(kh[ks]), as_bf16x8(ql[ks]), s1);
     }
-    // lane holds S[key = t0 + 4 quad + i][col c] in s0, key + 16 in s1
+    // lane holds S[key = t0 + 8 quad + i][col c] in s0, key + 4 in s1
     float sv[8];
     float tmax = NEG_SENTINEL;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key0 = t0 + quad * 4 + i, key1 = key0 + 16;
+      const int key0 = t0 + quad * 8 + i, key1 = key0 + 4;
       sv[i] = (key0 <= col.pos && key0 < k1) ? s0[i] * a.scale_log2 : -INFINITY;
       sv[4 + i] = (key1 <= col.pos && key1 < k1) ? s1[i] * a.scale_log2 : -INFINITY;
       tmax = fmaxf(tmax, fmaxf(sv[i], sv[4 + i]));
@@ -190,13 +192,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       acc[dt] *= alpha;
-      u32x4 av;
-      av[0] = va[dt][0];
-      av[1] = va[dt][1];
-      av[2] = vh[dt][0];
-      av[3] = vh[dt][1];
-      acc[dt] = mfma16x16x32(as_bf16x8(av), as_bf16x8(pb), acc[dt]);
-      acc[dt] = mfma16x16x32(as_bf16x8(av), as_bf16x8(pl), acc[dt]);
+      acc[dt] = mfma16x16x32(as_bf16x8(va[dt]), as_bf16x8(pb), acc[dt]);
+      acc[dt] = mfma16x16x32(as_bf16x8(va[dt]), as_bf16x8(pl), acc[dt]);
     }
   }
   // acc[dt][i] = O^T[dim = dt*16 + 4 quad + i][col c]; merge the 4 waves
