@@ -222,6 +222,34 @@ def test_tiny_batched_decode_matches_per_sequence_oracle():
             last[s] = want
 
 
+def test_8b_shape_batched_decode_of_nine_sequences():
+    """Batched decode at 8B layer shapes with 9 rows: the projections with at
+    least 40 MB of weights take the packed chunk kernel from 8 rows on (the
+    prompts of 8 to 12 tokens take it in prefill too); logits per sequence
+    against the oracle over two steps."""
+    from synth.workloads import C8B
+    shape = C8B.with_(name="gqa-8b-layers-2-b9", n_layers=2, vocab=1024, max_seq=64, max_chunk=16, max_batch=9)
+    W = host_weights(shape)
+    dec, _ = make_decoder(shape, W)
+    lens = (3, 12, 5, 8, 4, 10, 6, 9, 7)
+    prompts = [prompt(shape, n, seq=s) for s, n in enumerate(lens)]
+    models, last = [], []
+    for s, p in enumerate(prompts):
+        m = oracle.Model(shape, W)
+        last.append(m.forward(p, 0)["logits"])
+        models.append(m)
+        run_prefill(dec, p, 16, seq=s)
+    order = [4, 0, 8, 2, 6, 1, 3, 7, 5]
+    for step in range(2):
+        toks = [oracle.argmax(l) for l in last]
+        lg, _ = decode(dec, order, [toks[s] for s in order])
+        for b, s in enumerate(order):
+            want = models[s].forward([toks[s]], lens[s] + step)["logits"]
+            st = compare_logits(lg[b], want, f"seq {s} step {step}")
+            assert_parity(st, f"seq {s} step {step}")
+            last[s] = want
+
+
 # -------------------------------------------------------------------- MoE --
 
 def small_moe():
@@ -280,7 +308,7 @@ def test_gemv_kernel_matches_oracle(N, K):
     assert np.all(np.abs(got - want) <= 1e-6 * np.sqrt(K) * scale + 1e-30)
 
 
-@pytest.mark.parametrize("rows", [128, 37, 1])
+@pytest.mark.parametrize("rows", [128, 37, 9, 1])
 def test_8b_shape_two_layer_trace(rows):
     """8B-class layer shapes (hidden 4096, 32/8 heads of 128, SwiGLU 14336) in
     a 2-layer model with a small vocabulary: residual stream after each layer
