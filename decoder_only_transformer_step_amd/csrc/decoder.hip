@@ -473,8 +473,10 @@ int gemv(decoder *D, int node, int epi, const GemvArgs &g, int *blocks = nullptr
   const double nr = (epi == EPI_SWIGLU || epi == EPI_QKV) ? 2.0 : 1.0;
   const double slots = g.slot_expert ? g.n_slots : 1;
   const double out_words = epi == EPI_ADD ? 2 : epi == EPI_MOE_ADD ? 2 + g.moe_k : 1;
-  NodeTimer timer(D, node, slots * (nr * g.n_items * (double)g.K * 2 + g.K * 4.0 + g.n_items * 4.0 * out_words),
-                  slots * 2.0 * nr * g.n_items * (double)g.K);
+  const double part2 = g.W2 ? g.n_items2 * (nr * (double)g.K * 2 + 4.0) : 0.0;
+  NodeTimer timer(D, node,
+                  slots * (nr * g.n_items * (double)g.K * 2 + g.K * 4.0 + g.n_items * 4.0 * out_words) + part2,
+                  slots * 2.0 * nr * g.n_items * (double)g.K + (g.W2 ? 2.0 * nr * g.n_items2 * (double)g.K : 0.0));
   hipError_t e = launch_gemv(g, epi, D->stream, blocks);
   if (e != hipSuccess) return hip_fail(D, e, "gemv");
   return DEC_OK;
@@ -562,6 +564,7 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
     e = launch_moe_route(mr, false, D->stream);
   }
   if (e != hipSuccess) return hip_fail(D, e, "moe_route");
+  // routed gate_up (k slots) and, in the same launch, the shared expert's
   GemvArgs eg = gemv_args(W.w_exp_gate_up, D->x, H, Ie, D->f32_hexp);
   eg.gamma = W.ffn_norm;
   eg.eps = eps;
@@ -569,6 +572,12 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
   eg.n_slots = k;
   eg.w_group_stride = (int64_t)2 * Ie * H;
   eg.ldc = Ie;
+  if (Is > 0) {
+    eg.W2 = W.w_sh_gate_up;
+    eg.N2 = Is;
+    eg.n_items2 = Is;
+    eg.C2 = D->f32_h;
+  }
   if ((rc = gemv(D, DEC_NODE_EXPERTS, EPI_SWIGLU, eg))) return rc;
   GemvArgs ed = gemv_args(W.w_exp_down, D->f32_hexp, Ie, H, D->yexp);
   ed.slot_expert = D->rids;
@@ -578,10 +587,6 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
   ed.ldc = H;
   if ((rc = gemv(D, DEC_NODE_EXPERTS, EPI_STORE, ed))) return rc;
   if (Is > 0) {
-    GemvArgs sg = gemv_args(W.w_sh_gate_up, D->x, H, Is, D->f32_h);
-    sg.gamma = W.ffn_norm;
-    sg.eps = eps;
-    if ((rc = gemv(D, DEC_NODE_EXPERTS, EPI_SWIGLU, sg))) return rc;
     GemvArgs sd = gemv_args(W.w_sh_down, D->f32_h, Is, H, D->x);
     sd.moe_y = D->yexp;
     sd.moe_w = D->rwts;

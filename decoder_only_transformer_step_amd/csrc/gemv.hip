@@ -229,18 +229,36 @@ __device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, in
 // so the prologue waits only for it.  NCH: the row's chunk count when it is
 // 1 or 2 (no refills), else 0 (the refill loop).
 template <int EPI, int NCH, int WV>
-__global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs g) {
+__global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
   constexpr int NR = gv_rows<EPI>(), CH = 8 / NR, NT = WV * WAVE, PRN = 32 / WV, PRH = PRN / 2;
   extern __shared__ f32x4 xs[];  // activation, fp32 in the layout of xs_slot
   __shared__ float sred[WV];
   __shared__ float bv_s[WV];
   __shared__ int bi_s[WV];
 
+  // A second part with its own weights, rows and output (same activation)
+  // can follow the grouped slots in one grid: blocks past blocks1 x n_slots
+  // run it.  Otherwise blockIdx.y is the slot.
+  GemvArgs g = ga;
+  int bx = blockIdx.x, slot = blockIdx.y;
+  if (ga.W2) {
+    const int nb1 = ga.blocks1 * ga.n_slots;
+    if (bx >= nb1) {
+      bx -= nb1;
+      g.W = ga.W2;
+      g.N = ga.N2;
+      g.n_items = ga.n_items2;
+      g.C = ga.C2;
+      g.slot_expert = nullptr;
+    } else {
+      slot = bx / ga.blocks1;
+      bx -= slot * ga.blocks1;
+    }
+  }
   const uint16_t *W = g.W;
   const float *xin = g.a_f32;
   int out_row = 0;
   if (g.slot_expert) {
-    const int slot = blockIdx.y;
     W += (int64_t)g.slot_expert[slot] * g.w_group_stride;
     if (xin) xin += (int64_t)slot * g.a_slot_stride;
     out_row = slot;
@@ -249,7 +267,7 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs g) {
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
   const int steps = (K + 511) / 512, nch = NCH ? NCH : (steps + CH - 1) / CH;
-  const int it = blockIdx.x * WV + wave;
+  const int it = bx * WV + wave;
   const bool valid = it < g.n_items;
   int rows[NR];
   const uint16_t *wp[NR];
@@ -379,7 +397,8 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs g) {
 
 template <int EPI, int WV>
 void launch_w(const GemvArgs &g, int nch, size_t lds, hipStream_t st) {
-  const dim3 grid((g.n_items + WV - 1) / WV, g.slot_expert ? g.n_slots : 1), block(WV * WAVE);
+  dim3 grid((g.n_items + WV - 1) / WV, g.slot_expert ? g.n_slots : 1), block(WV * WAVE);
+  if (g.W2) grid = dim3(g.blocks1 * g.n_slots + (g.n_items2 + WV - 1) / WV, 1);
   if (nch == 1) hipLaunchKernelGGL((gemv_kernel<EPI, 1, WV>), grid, block, lds, st, g);
   else if (nch == 2) hipLaunchKernelGGL((gemv_kernel<EPI, 2, WV>), grid, block, lds, st, g);
   else hipLaunchKernelGGL((gemv_kernel<EPI, 0, WV>), grid, block, lds, st, g);
@@ -418,8 +437,15 @@ int gemv_blocks(int n_items) {
   return (n_items + wv - 1) / wv;
 }
 
-hipError_t launch_gemv(const GemvArgs &g, int epi, hipStream_t st, int *blocks) {
-  const int wv = gemv_waves(g.n_items);
+hipError_t launch_gemv(const GemvArgs &g0, int epi, hipStream_t st, int *blocks) {
+  GemvArgs g = g0;
+  int wv = gemv_waves(g.n_items);
+  if (g.W2) {
+    // second part: SwiGLU after grouped slots only, 8-wave blocks for both parts
+    if (epi != EPI_SWIGLU || !g.slot_expert || g.n_items2 < 1 || !g.C2) return hipErrorInvalidValue;
+    wv = 8;
+    g.blocks1 = (g.n_items + wv - 1) / wv;
+  }
   if (blocks) *blocks = (g.n_items + wv - 1) / wv;
   const size_t lds = gemv_lds(g.K);
   switch (epi) {

@@ -56,6 +56,12 @@ struct GemvArgs {
   // shared-expert scale gate [1] (the kernel's own rows are the shared expert's)
   const float *moe_y, *moe_w, *moe_gate;
   int32_t moe_k;
+  // optional second part of an EPI_SWIGLU grouped launch (the shared expert):
+  // weights W2 [2 N2][K], N2 row pairs into C2 [N2]; blocks1 is set by the launcher
+  const uint16_t *W2;
+  int32_t N2, n_items2;
+  float *C2;
+  int32_t blocks1;
 };
 constexpr size_t GEMV_MAX_LDS = 60 * 1024;
 // LDS of one GEMV block: the fp32 activation padded to whole 512-element steps
