@@ -62,6 +62,50 @@ def counter_traffic(name):
     return float(m_bytes.group(1))
 
 
+def measure_verify(dec, shape, stream, ev0, ev1, reps, ns=(2, 4, 8)):
+    """Multi-position verify, the check of speculatively drafted tokens
+    (pipeline.rs Pipeline::forward_pair and measure_pair_fusion): n drafted
+    positions go through one prefill_chunk call with every row's logits and
+    greedy id, and kv_truncate rolls the sequence back; against n single
+    decode steps at the same positions, also rolled back.  Milliseconds per
+    round from HIP events over `reps` rounds after one untimed round."""
+    import torch
+    from synth.weights import prompt
+    L = dec.seq_len(0)
+    nmax = max(ns)
+    logits = torch.empty((nmax, shape.vocab), dtype=torch.float32, device="cuda")
+    am = torch.empty(nmax, dtype=torch.int32, device="cuda")
+    drafts = [int(t) for t in prompt(shape, nmax, seq=123)]
+    out = {"position": L, "reps": reps}
+
+    def timed(fn):
+        for rep in range(reps + 1):
+            if rep == 1:
+                torch.cuda.synchronize()
+                ev0.record(stream)
+            fn()
+            dec.kv_truncate(0, L)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / reps
+
+    for n in ns:
+        if L + n > shape.max_seq or n > shape.max_chunk:
+            continue
+        v_ms = timed(lambda: dec.prefill_chunk(0, drafts[:n], L, logits_mode=2, logits=logits, argmax=am))
+
+        def singles():
+            for i in range(n):
+                dec.decode_step([0], [drafts[i]], logits=logits[i:i + 1], argmax=am[i:i + 1])
+        s_ms = timed(singles)
+        out[f"n{n}"] = {"verify_ms": round(v_ms, 4), "singles_ms": round(s_ms, 4),
+                        "positions_per_s": round(n / v_ms * 1e3, 1),
+                        "speedup_vs_singles": round(s_ms / v_ms, 3)}
+        log(f"[gpu] verify {n} positions: {v_ms:.3f} ms ({n / v_ms * 1e3:.0f} positions/s), "
+            f"{n} single decode steps {s_ms:.3f} ms")
+    return out
+
+
 def cpu_baseline(shape, n_prefill, n_decode):
     """The fp64 oracle (unchanged) on the host cores: a chunk of n_prefill
     prompt tokens, then n_decode greedy decode steps; tokens/s of the decode
@@ -235,6 +279,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill measurement: the decode context is a synthetic N(0,1) KV "
                          "prefix of the prompt's length (for counter runs of the decode kernels)")
+    ap.add_argument("--no-verify", action="store_true",
+                    help="skip the multi-position verify measurement (batch-1 workloads)")
+    ap.add_argument("--verify-reps", type=int, default=20)
     ap.add_argument("--cpu-prefill", type=int, default=16, help="oracle sample: prompt tokens")
     ap.add_argument("--cpu-decode", type=int, default=2, help="oracle sample: decode steps")
     ap.add_argument("--sample-every", type=int, default=8,
@@ -406,6 +453,11 @@ def main():
     log(f"[gpu] decode {tok_s:.1f} tok/s, {t_dec / args.steps * 1e3:.3f} ms/step "
         f"({step_bytes / 1e9:.2f} GB/step algorithmic)")
 
+    # multi-position verify, after the timed decode region
+    verify = None
+    if batch == 1 and not args.no_verify:
+        verify = measure_verify(dec, shape, stream, ev0, ev1, args.verify_reps)
+
     d = dst[dom]
     per_launch_bytes = d["bytes"] / d["launches"]
     per_launch_s = d["ms"] / d["launches"] * 1e-3
@@ -431,6 +483,7 @@ def main():
                    "bytes_per_step": step_bytes, "host_s": t_host,
                    "nodes_warmup": summarize_nodes(wst)},
         "prefill": prefill,
+        "verify": verify,
         "roofline": roofline,
         "kernel_source_sha256": kernel_source_hash(),
     })

@@ -60,6 +60,7 @@ SIGNATURES = {
     "prefill_chunk": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _I32, _P, _P]),
     "decode_step": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P]),
     "kv_reset": (ctypes.c_int, [_P, _I32]),
+    "kv_truncate": (ctypes.c_int, [_P, _I32, _I32]),
     "kv_load": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _I32]),
     "decoder_seq_len": (_I32, [_P, _I32]),
     "decoder_set_stream": (ctypes.c_int, [_P, _P]),
@@ -172,6 +173,10 @@ def kv_reset(handle, seq=-1):
     _check(lib().kv_reset(handle, seq), handle, "kv_reset")
 
 
+def kv_truncate(handle, seq, length):
+    _check(lib().kv_truncate(handle, seq, length), handle, "kv_truncate")
+
+
 def kv_load(handle, seq, layer, k, v, length):
     _check(lib().kv_load(handle, seq, layer, _ptr(k), _ptr(v), length), handle, "kv_load")
 
@@ -220,6 +225,9 @@ class Decoder:
 
     def kv_reset(self, seq=-1):
         kv_reset(self.handle, seq)
+
+    def kv_truncate(self, seq, length):
+        kv_truncate(self.handle, seq, length)
 
     def kv_load(self, seq, layer, k, v, length):
         kv_load(self.handle, seq, layer, k, v, length)

@@ -1040,7 +1040,9 @@ int prefill_chunk(decoder_t *D, int32_t seq, const int32_t *ids, int32_t n, int3
   const int G = c.n_heads / c.n_kv_heads;
   const int nout = logits_mode == 0 ? 0 : (logits_mode == 1 ? 1 : n);
   const int first = logits_mode == 1 ? n - 1 : 0;
-  rc = run_step(D, n, 16 / G, start_pos + n - 1, pos.data(), 0, first, nout, d_logits, d_argmax, nout ? 1 : 0);
+  // logits_mode 2 (a multi-position verify) returns every row's greedy id
+  rc = run_step(D, n, 16 / G, start_pos + n - 1, pos.data(), 0, first, nout, d_logits, d_argmax,
+                logits_mode == 2 ? n : (nout ? 1 : 0));
   if (rc) return rc;
   D->len[seq] = start_pos + n;
   if (nout) D->has_next[seq] = 1;
@@ -1092,6 +1094,19 @@ int kv_reset(decoder_t *D, int32_t seq) {
     D->has_next[s] = 0;
     std::fill(D->kv_pending[s].begin(), D->kv_pending[s].end(), -1);
   }
+  return DEC_OK;
+}
+
+int kv_truncate(decoder_t *D, int32_t seq, int32_t len) {
+  if (check_dec(D)) return DEC_E_INVALID;
+  if (seq < 0 || seq >= D->c.max_batch) return fail(D, DEC_E_INVALID, "seq out of range");
+  if (len < 0 || len > D->len[seq]) return fail(D, DEC_E_INVALID, "kv_truncate length outside [0, current length]");
+  // Rows past len keep their old values.  No kernel reads them: attention
+  // at position p reads keys 0..p only (later keys of a loaded tile get
+  // probability exactly 0), and every row below the next position is
+  // rewritten before a query at or past it runs.
+  D->len[seq] = len;
+  D->has_next[seq] = 0;
   return DEC_OK;
 }
 

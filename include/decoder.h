@@ -129,7 +129,13 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *weights,
  * 2 every token's logits ([n][V]).  d_logits may be NULL (then logits go to
  * internal scratch).  When logits are computed, the greedy next token of the
  * last row is kept for decode_step(tokens = NULL) and, if d_argmax is not
- * NULL, written to d_argmax[0] (int32). */
+ * NULL, written to d_argmax[0] (int32); with logits_mode 2, d_argmax
+ * receives every row's greedy token ([n] int32, lowest id on ties).
+ * logits_mode 2 is also the multi-position verify of speculative decoding
+ * (pipeline.rs Pipeline::generate_from_ids and forward_pair: the positions
+ * of a drafted continuation go through one pass that streams each weight
+ * matrix once, and row i's logits score the token after position
+ * start_pos + i); kv_truncate rolls back the rows of rejected drafts. */
 int prefill_chunk(decoder_t *dec, int32_t seq, const int32_t *ids, int32_t n,
                   int32_t start_pos, int32_t logits_mode, float *d_logits, int32_t *d_argmax);
 
@@ -144,6 +150,15 @@ int decode_step(decoder_t *dec, int32_t batch, const int32_t *seqs, const int32_
 /* Forget sequence seq (-1: all sequences): its length becomes 0 and its KV
  * rows are zeroed (engine.zig Engine.reset). */
 int kv_reset(decoder_t *dec, int32_t seq);
+
+/* Roll sequence seq back to its first len cached positions
+ * (0 <= len <= current length, else DEC_E_INVALID): the next prefill or
+ * decode of seq writes at position len.  pipeline.rs
+ * Pipeline::generate_from_ids: a rejected draft's KV entry is dropped
+ * (truncate_last).  Host-side only: nothing is launched, and the rows past
+ * len are never read again before they are rewritten.  decode_step with
+ * tokens = NULL is refused for seq until a call with logits has run. */
+int kv_truncate(decoder_t *dec, int32_t seq, int32_t len);
 
 /* Install a KV-cache prefix for one layer of one sequence from device
  * buffers d_k, d_v, both bf16 [Hkv][len][d] (keys already rotated).  The

@@ -65,6 +65,8 @@ def lib():
         L.orc_reset.argtypes = [_P, _I]
         L.orc_kv_load.restype = _I
         L.orc_kv_load.argtypes = [_P, _I, _I, _P, _P, _I]
+        L.orc_truncate.restype = _I
+        L.orc_truncate.argtypes = [_P, _I, _I]
         L.orc_seq_len.restype = ctypes.c_int32
         L.orc_seq_len.argtypes = [_P, _I]
         L.orc_forward.restype = _I
@@ -196,6 +198,11 @@ class Model:
 
     def reset(self, seq=-1):
         lib().orc_reset(self._h, seq)
+
+    def truncate(self, seq, length):
+        rc = lib().orc_truncate(self._h, seq, int(length))
+        if rc != 0:
+            raise ValueError(f"orc_truncate({seq}, {length}) failed: {rc}")
 
     def seq_len(self, seq=0):
         return lib().orc_seq_len(self._h, seq)

@@ -374,6 +374,21 @@ int orc_kv_load(orc_model_t *m, int seq, int layer, const uint16_t *K, const uin
   return ORC_OK;
 }
 
+/* Roll a sequence back to its first len positions (0 <= len <= current
+ * length): the rows past len stop being part of it and are cleared, so the
+ * state equals one that never held them.  pipeline.rs
+ * Pipeline::generate_from_ids (a rejected draft's KV entry is dropped). */
+int orc_truncate(orc_model_t *m, int seq, int len) {
+  if (seq < 0 || seq >= m->c.n_seqs || len < 0 || len > m->len[seq]) return ORC_E_INVALID;
+  size_t rows = (size_t)(m->len[seq] - len) * m->c.n_kv_heads * m->c.head_dim;
+  for (int l = 0; l < m->c.n_layers; ++l) {
+    memset(kv_row(m, m->kc, seq, l, len), 0, rows * sizeof(double));
+    memset(kv_row(m, m->vc, seq, l, len), 0, rows * sizeof(double));
+  }
+  m->len[seq] = len;
+  return ORC_OK;
+}
+
 int32_t orc_seq_len(const orc_model_t *m, int seq) { return m->len[seq]; }
 
 /* Routed MoE FFN with shared expert for n tokens (B: normed inputs [n][H]).

@@ -27,7 +27,7 @@ def declared_functions():
 def test_headers_declare_the_boundary():
     names = declared_functions()
     for n in ("decoder_init", "prefill_chunk", "decode_step", "kv_reset", "decoder_workspace_bytes",
-              "decoder_free", "kv_load", "dec_diag_gemm"):
+              "decoder_free", "kv_load", "kv_truncate", "dec_diag_gemm"):
         assert n in names
 
 

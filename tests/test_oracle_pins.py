@@ -311,6 +311,31 @@ def test_decode_after_prefill_equals_recompute():
         assert np.allclose(step[i], full[8 + i], rtol=0, atol=1e-12)
 
 
+def test_truncate_equals_never_extended():
+    """Rolling a sequence back (pipeline.rs Pipeline::generate_from_ids
+    drops a rejected draft's KV entry) leaves exactly the state of a sequence
+    that never held the dropped rows.  A slip in the rolled-back length (one
+    row too many or too few) changes the next token's attention keys."""
+    s = small_shape()
+    W = rand_weights(s)
+    ids = synth.tokens(14, 9, s.vocab)
+    a = oracle.Model(s, W)
+    a.forward(ids[:8], 0, logits_mode=0)
+    a.forward(ids[8:12], 8, logits_mode=2)          # four drafted positions
+    a.truncate(0, 9)                                # keep one of them
+    assert a.seq_len(0) == 9
+    got = a.forward(ids[12:13], 9)["logits"]
+    b = oracle.Model(s, W)
+    b.forward(ids[:9], 0, logits_mode=0)
+    want = b.forward(ids[12:13], 9)["logits"]
+    assert np.array_equal(got, want)
+    c = oracle.Model(s, W)                          # keeping all four differs
+    c.forward(ids[:12], 0, logits_mode=0)
+    assert not np.allclose(c.forward(ids[12:13], 12)["logits"], want)
+    with pytest.raises(ValueError):
+        a.truncate(0, 11)                           # past the current length
+
+
 def test_chunk_size_invariance():
     s = small_shape()
     W = rand_weights(s)
