@@ -279,6 +279,10 @@ def main():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill measurement: the decode context is a synthetic N(0,1) KV "
                          "prefix of the prompt's length (for counter runs of the decode kernels)")
+    ap.add_argument("--sliding-window", type=int, default=0,
+                    help="attention variant: every query sees only the W most recent positions")
+    ap.add_argument("--attn-softcap", type=float, default=0.0, help="attention variant: logit soft-cap")
+    ap.add_argument("--attn-sinks", action="store_true", help="attention variant: per-head sink logits")
     ap.add_argument("--no-verify", action="store_true",
                     help="skip the multi-position verify measurement (batch-1 workloads)")
     ap.add_argument("--verify-reps", type=int, default=20)
@@ -329,6 +333,15 @@ def main():
     from synth.workloads import WORKLOADS
 
     shape, work = WORKLOADS[args.workload]
+    variant = {}
+    if args.sliding_window:
+        variant["sliding_window"] = args.sliding_window
+    if args.attn_softcap:
+        variant["attn_softcap"] = args.attn_softcap
+    if args.attn_sinks:
+        variant["attn_sinks"] = True
+    if variant:
+        shape = shape.with_(name=shape.name + "-" + "-".join(f"{k}{v}" for k, v in variant.items()), **variant)
     # the first decode step (reported on its own), the warmup and the timed
     # steps together make the workload's decode steps
     if args.steps is None:
@@ -477,7 +490,8 @@ def main():
         "config": {"workload": shape.name, "global_batch": batch, "decode_positions":
                    [work.prompt or work.context, (work.prompt or work.context) + 1 + args.warmup + args.steps],
                    "kv_prefix": "prefill" if prefill else "synthetic N(0,1)",
-                   "prefill_prompt": work.prompt, "prefill_chunk": work.chunk, "parallelism": "single-gpu"},
+                   "prefill_prompt": work.prompt, "prefill_chunk": work.chunk, "parallelism": "single-gpu",
+                   **({"attention_variant": variant} if variant else {})},
         "decode": {"tok_s": tok_s, "first_step_ms": round(first_ms, 3), "hbm_GBps": step_bytes / (t_dec / args.steps) / 1e9,
                    "hbm_frac": step_bytes / (t_dec / args.steps) / 1e9 / HBM_PEAK_GBS,
                    "bytes_per_step": step_bytes, "host_s": t_host,

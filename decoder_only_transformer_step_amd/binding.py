@@ -23,12 +23,13 @@ class DecoderConfig(ctypes.Structure):
         "hidden", "n_layers", "n_heads", "n_kv_heads", "head_dim", "ffn_inter", "n_experts",
         "top_k", "expert_inter", "shared_inter", "shared_gate", "norm_topk_prob", "vocab",
         "qkv_bias")] + [("rope_base", ctypes.c_double), ("rms_eps", ctypes.c_double)] + [
-        (n, _I32) for n in ("max_seq", "max_chunk", "max_batch")]
+        (n, _I32) for n in ("max_seq", "max_chunk", "max_batch", "sliding_window")] + [
+        ("attn_softcap", ctypes.c_double)]
 
 
 LAYER_FIELDS = ("attn_norm", "ffn_norm", "w_qkv", "b_qkv", "w_o", "w_gate_up", "w_down",
                 "w_router", "w_exp_gate_up", "w_exp_down", "w_sh_gate_up", "w_sh_down",
-                "w_sh_gate")
+                "w_sh_gate", "attn_sinks")
 
 
 class DecoderLayerWeights(ctypes.Structure):
@@ -129,7 +130,8 @@ def make_config(shape):
         expert_inter=s.expert_inter, shared_inter=s.shared_inter, shared_gate=int(s.shared_gate),
         norm_topk_prob=int(s.norm_topk_prob), vocab=s.vocab, qkv_bias=int(s.qkv_bias),
         rope_base=float(s.rope_base), rms_eps=float(s.rms_eps), max_seq=s.max_seq,
-        max_chunk=s.max_chunk, max_batch=s.max_batch)
+        max_chunk=s.max_chunk, max_batch=s.max_batch, sliding_window=getattr(s, "sliding_window", 0),
+        attn_softcap=float(getattr(s, "attn_softcap", 0.0)))
 
 
 # ---------------------------------------------------- same-named functions --

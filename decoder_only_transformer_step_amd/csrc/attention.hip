@@ -23,6 +23,10 @@
 //    the K rows of the QK product are permuted so that it leaves each lane
 //    the scores of the same 8 consecutive keys.  No LDS round trip, no
 //    cross-lane shuffles for P.
+//  * Variants: a sliding window masks keys at or below pos - W and moves
+//    the group's first split to the window's start; a soft-cap maps each
+//    scaled score s to c tanh(s / c); a head's sink logit joins the final
+//    denominator (attn_sink_fold) and adds nothing to the output.
 //  * The 4 waves merge through LDS (log-sum-exp); with one split the block
 //    normalises and writes the output.  With several, each block writes its
 //    (m, l, O) partial and attn_merge combines them in split order, so the
@@ -91,6 +95,15 @@ __device__ __forceinline__ int group_keys(const AttnArgs &a, int rg, int g) {
   return kmax + 1;
 }
 
+// First key of the group's splits: with a window, the lowest query position
+// of the group bounds it (mode 0 groups start at key 0 and rely on masking).
+template <int PM>
+__device__ __forceinline__ int group_key_start(const AttnArgs &a, int rg) {
+  if (PM == 1) return attn_key_start(a.window, a.pos_arg[rg]);
+  if (PM == 2) return attn_key_start(a.window, a.pos0 + rg * a.rows_per_group);
+  return 0;
+}
+
 template <int D, int PM>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   constexpr int NDT = D / 16;
@@ -99,10 +112,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
   const int gi = blockIdx.x / a.n_splits, split = blockIdx.x - gi * a.n_splits;
   const int g = gi % a.Hkv, rg = gi / a.Hkv;
-  const int keys = group_keys<PM>(a, rg, g);
-  const int nact = (keys + a.kc - 1) / a.kc;
+  const int keys = group_keys<PM>(a, rg, g), kstart = group_key_start<PM>(a, rg);
+  const int nact = (keys - kstart + a.kc - 1) / a.kc;
   if (split >= nact) return;
-  const int k0 = split * a.kc, k1 = min(k0 + a.kc, keys);
+  const int k0 = kstart + split * a.kc, k1 = min(k0 + a.kc, keys);
 
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   const int c = lane & 15, quad = lane >> 4;
@@ -168,8 +181,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key0 = t0 + quad * 8 + i, key1 = key0 + 4;
-      sv[i] = (key0 <= col.pos && key0 < k1) ? s0[i] * a.scale_log2 : -INFINITY;
-      sv[4 + i] = (key1 <= col.pos && key1 < k1) ? s1[i] * a.scale_log2 : -INFINITY;
+      sv[i] = (attn_key_ok(a, key0, col.pos) && key0 < k1) ? attn_logit2(a, s0[i]) : -INFINITY;
+      sv[4 + i] = (attn_key_ok(a, key1, col.pos) && key1 < k1) ? attn_logit2(a, s1[i]) : -INFINITY;
       tmax = fmaxf(tmax, fmaxf(sv[i], sv[4 + i]));
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, WAVE));
@@ -224,7 +237,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
   if (nact == 1) {
     if (!oc.valid) return;
-    const float inv = 1.0f / L;
+    const float r = attn_sink_fold(a, oc.head, M, L);
+    const float inv = r / L;
     const int64_t ob = ((int64_t)oc.row * a.Hq + oc.head) * D;
 #pragma unroll
     for (int q = 0; q < NDT; ++q) store_out(a, ob + jj + 16 * q, o[q] * inv);
@@ -254,7 +268,7 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int ncols) {
   const int g = gi % a.Hkv, rg = gi / a.Hkv;
   const Col oc = column<PM>(a, rg, g, cc);
   if (!oc.valid) return;
-  const int nact = (group_keys<PM>(a, rg, g) + a.kc - 1) / a.kc;
+  const int nact = (group_keys<PM>(a, rg, g) - group_key_start<PM>(a, rg) + a.kc - 1) / a.kc;
   if (nact <= 1) return;                       // written directly by attn_kernel
   const int j = threadIdx.x;
   const float *ml = a.part_ml + ((int64_t)gi * a.n_splits * 16 + cc) * 2;
@@ -287,7 +301,8 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int ncols) {
     }
     M = cm;
   }
-  store_out(a, ((int64_t)oc.row * a.Hq + oc.head) * D + j, o / L);
+  const float r = attn_sink_fold(a, oc.head, M, L);
+  store_out(a, ((int64_t)oc.row * a.Hq + oc.head) * D + j, o * r / L);
 }
 
 }  // namespace

@@ -58,9 +58,10 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a, int rpb)
   const int g = gi % a.Hkv, rb = gi / a.Hkv;
   const int row_lo = rb * rpb, row_hi = min(a.rows, row_lo + rpb);
   const int keys = a.pos0 + row_hi;  // last position of the block + 1
-  const int nact = (keys + a.kc - 1) / a.kc;
+  const int kstart = attn_key_start(a.window, a.pos0 + row_lo);
+  const int nact = (keys - kstart + a.kc - 1) / a.kc;
   if (split >= nact) return;
-  const int k0 = split * a.kc, k1 = min(k0 + a.kc, keys);
+  const int k0 = kstart + split * a.kc, k1 = min(k0 + a.kc, keys);
 
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE, h = lane >> 5;
   const int G = a.G;
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a, int rpb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = t0 + 8 * (i >> 2) + 4 * h + (i & 3);
-      p[i] = (key <= pos && key < k1) ? s[i] * a.scale_log2 : -INFINITY;
+      p[i] = (attn_key_ok(a, key, pos) && key < k1) ? attn_logit2(a, s[i]) : -INFINITY;
       tmax = fmaxf(tmax, p[i]);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, WAVE));
@@ -192,7 +193,9 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a, int rpb)
   // lane: column l % 32, dims 32 dt + 8 (i / 4) + 4 h + i % 4
   if (nact == 1) {
     if (!valid) return;
-    const float inv = 1.0f / l_tot;
+    float Mv = m_run, Lv = l_tot;
+    const float r = attn_sink_fold(a, head, Mv, Lv);
+    const float inv = r / Lv;
     const int64_t ob = ((int64_t)row * a.Hq + head) * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -223,7 +226,8 @@ __global__ __launch_bounds__(D) void attn_chunk_merge_kernel(AttnArgs a, int rpb
   const int G = a.G;
   const int row = row_lo + col / G, head = g * G + col % G;
   if (!(col < rpb * G && row < row_hi)) return;
-  const int nact = min((a.pos0 + row_hi + a.kc - 1) / a.kc, AC_MAX_TASKS);
+  const int kstart = attn_key_start(a.window, a.pos0 + row_lo);
+  const int nact = min((a.pos0 + row_hi - kstart + a.kc - 1) / a.kc, AC_MAX_TASKS);
   if (nact <= 1) return;  // written by attn_chunk_kernel
   const int j = threadIdx.x;
   const int64_t t0 = (int64_t)gi * a.n_splits;
@@ -247,7 +251,8 @@ __global__ __launch_bounds__(D) void attn_chunk_merge_kernel(AttnArgs a, int rpb
     Ls += sc * sl[s];
     o += sc * a.part_o[((t0 + s) * AC_COLS + col) * D + j];
   }
-  ac_store_out(a, ((int64_t)row * a.Hq + head) * D + j, o / Ls);
+  const float r = attn_sink_fold(a, head, M, Ls);
+  ac_store_out(a, ((int64_t)row * a.Hq + head) * D + j, o * r / Ls);
 }
 
 template <int D>
@@ -258,7 +263,9 @@ hipError_t launch_d(AttnArgs a, hipStream_t st) {
   // split the keys so that about one block per compute unit runs, each at
   // least four 32-key tiles (every split writes 64 KB of partials per 128
   // columns, which the merge reads back)
-  const int keys = a.pos0 + a.rows;
+  // with a window, a block's keys span at most its rows, the window and
+  // the 32-key alignment of its first split
+  const int keys = a.window > 0 ? std::min(a.pos0 + a.rows, a.window + rpb + 31) : a.pos0 + a.rows;
   int ns = std::max(1, 256 / a.n_groups);
   int kc = std::max(128, (int)(((keys + ns - 1) / ns + 31) / 32 * 32));
   ns = (keys + kc - 1) / kc;

@@ -86,6 +86,7 @@ bool config_ok(const decoder_config_t *c) {
       c->max_batch <= 0 || c->max_batch > 256)
     return false;
   if (!(c->rope_base > 0.0) || !(c->rms_eps >= 0.0)) return false;
+  if (c->sliding_window < 0 || !(c->attn_softcap >= 0.0) || c->attn_softcap > 1e30) return false;
   if (c->n_experts > 0) {
     if (c->n_experts > 256 || c->top_k <= 0 || c->top_k > 8 || c->top_k > c->n_experts) return false;
     if (c->expert_inter <= 0 || c->expert_inter % 8 || c->shared_inter < 0 || c->shared_inter % 8)
@@ -403,12 +404,14 @@ int norm_into(decoder *D, GemmArgs &g, const float *x, const float *gamma, int r
 int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, const int32_t *hpos,
               float *out_f32 = nullptr) {
   const decoder_config_t &c = D->c;
+  const int W = c.sliding_window;
   double kv_rows = 0, qk = 0;
   for (int r = 0; r < rows; ++r) {
-    qk += hpos[r] + 1.0;
-    if (rows_per_group == 1) kv_rows += hpos[r] + 1.0;
+    const double seen = W > 0 ? std::min(hpos[r] + 1, W) : hpos[r] + 1.0;
+    qk += seen;
+    if (rows_per_group == 1) kv_rows += seen;
   }
-  if (rows_per_group != 1) kv_rows = max_pos + 1.0;
+  if (rows_per_group != 1) kv_rows = W > 0 ? std::min(max_pos + 1, W + rows) : max_pos + 1.0;
   NodeTimer timer(D, DEC_NODE_ATTN,
                   kv_rows * c.n_kv_heads * c.head_dim * 4.0 + (double)rows * c.n_heads * c.head_dim * 4.0,
                   qk * c.n_heads * c.head_dim * 4.0);
@@ -431,19 +434,11 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
   a.rows = rows;
   a.rows_per_group = rows_per_group;
   a.n_groups = (rows + rows_per_group - 1) / rows_per_group * c.n_kv_heads;
-  // split the keys so that about ATTN_TARGET_BLOCKS blocks run, each at
-  // least one 32-key tile per wave
-  const int keys = max_pos + 1;
-  int ns = std::max(1, (ATTN_TARGET_BLOCKS + a.n_groups - 1) / a.n_groups);
-  int kc = (int)align_up((size_t)((keys + ns - 1) / ns), 128);
-  ns = (keys + kc - 1) / kc;
-  while ((int64_t)a.n_groups * ns > ATTN_MAX_TASKS) {
-    kc *= 2;
-    ns = (keys + kc - 1) / kc;
-  }
-  a.kc = kc;
-  a.n_splits = ns;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+  a.scale = (float)(1.0 / std::sqrt((double)c.head_dim));
+  a.window = W;
+  a.softcap = (float)c.attn_softcap;
+  a.sinks = D->layers[layer].attn_sinks;
   a.part_o = D->part_o;
   a.part_ml = D->part_ml;
   // positions as kernel arguments where the host has them in a usable form
@@ -461,6 +456,21 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
     for (int r = 1; r < rows; ++r)
       if (hpos[r] != hpos[0] + r || D->hseq[r] != a.seq0) a.pos_mode = 0;
   }
+  // split the keys so that about ATTN_TARGET_BLOCKS blocks run, each at
+  // least one 32-key tile per wave; with a window (position modes 1 and 2)
+  // a group's keys start at its window, so they span at most its rows, the
+  // window and the 32-key alignment
+  int keys = max_pos + 1;
+  if (W > 0 && a.pos_mode != 0) keys = std::min(keys, W + rows_per_group + 31);
+  int ns = std::max(1, (ATTN_TARGET_BLOCKS + a.n_groups - 1) / a.n_groups);
+  int kc = (int)align_up((size_t)((keys + ns - 1) / ns), 128);
+  ns = (keys + kc - 1) / kc;
+  while ((int64_t)a.n_groups * ns > ATTN_MAX_TASKS) {
+    kc *= 2;
+    ns = (keys + kc - 1) / kc;
+  }
+  a.kc = kc;
+  a.n_splits = ns;
   hipError_t e = attention_chunk_fits(a, c.head_dim) ? launch_attention_chunk(a, c.head_dim, D->stream)
                                                      : launch_attention(a, c.head_dim, D->stream);
   if (e != hipSuccess) return hip_fail(D, e, "attention");

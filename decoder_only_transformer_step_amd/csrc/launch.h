@@ -104,7 +104,46 @@ struct AttnArgs {
   // of one sequence, row r at position pos0 + r of sequence seq0.
   int32_t pos_mode, pos0, seq0;
   int32_t pos_arg[16], seq_arg[16];
+  // Variants (engine.zig Engine.forward passes a logit soft-cap and, on a
+  // sliding layer, a window to its attention; decoder.rs AttnWeights::sinks)
+  int32_t window;          // 0: every earlier key; W > 0: keys pos - W < t <= pos
+  float softcap;           // 0: off; c > 0: scaled score s -> c tanh(s / c)
+  float scale;             // 1 / sqrt(d), for the soft-cap
+  const float *sinks;      // [Hq] sink logits of this layer, or null
 };
+
+constexpr float ATTN_LOG2E = 1.4426950408889634f;
+
+// Score of a raw q.k product in log2 units (scaled, soft-capped when set).
+__device__ __forceinline__ float attn_logit2(const AttnArgs &a, float s) {
+  if (a.softcap > 0.f) return a.softcap * tanhf(s * a.scale / a.softcap) * ATTN_LOG2E;
+  return s * a.scale_log2;
+}
+
+// Whether key t is visible to a query at position pos (causal, windowed).
+__device__ __forceinline__ bool attn_key_ok(const AttnArgs &a, int t, int pos) {
+  return t <= pos && (a.window <= 0 || t > pos - a.window);
+}
+
+// First key (a multiple of 32) that a group whose lowest query position is
+// minpos can see: the key ranges of its splits start there.
+__host__ __device__ inline int attn_key_start(int window, int minpos) {
+  return window > 0 ? (max(0, minpos - window + 1) & ~31) : 0;
+}
+
+// Fold head's sink logit into a finished softmax with running maximum M and
+// sum L (log2 units): L becomes the full denominator and the return value
+// is the factor that rescales the accumulated output to the new maximum.
+__device__ __forceinline__ float attn_sink_fold(const AttnArgs &a, int head, float &M, float &L) {
+  if (!a.sinks) return 1.f;
+  const float z = a.sinks[head] * ATTN_LOG2E;
+  const float Mn = fmaxf(M, z);
+  const float r = exp2f(M - Mn);
+  L = L * r + exp2f(z - Mn);
+  M = Mn;
+  return r;
+}
+
 hipError_t launch_attention(const AttnArgs &a, int head_dim, hipStream_t st);
 // Prefill-chunk attention (pos_mode 2, split-bf16 output, d = 64 or 128);
 // sets its own groups and splits.  Uses part_o / part_ml like the general

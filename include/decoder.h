@@ -85,6 +85,12 @@ typedef struct {
   int32_t max_seq;         /* KV capacity per sequence (positions) */
   int32_t max_chunk;       /* largest prefill chunk (tokens per call), <= 256 */
   int32_t max_batch;       /* number of sequences (KV slots); largest decode batch */
+  /* Attention variants (engine.zig Engine.forward hands its attention a
+   * logit soft-cap and, on a sliding layer, a window): */
+  int32_t sliding_window;  /* 0: a query attends to every earlier position; W > 0:
+                              the query at position p sees keys t with p - W < t <= p
+                              (every layer) */
+  double attn_softcap;     /* 0: off; c > 0: each scaled score s becomes c tanh(s / c) */
 } decoder_config_t;
 
 typedef struct {
@@ -101,6 +107,9 @@ typedef struct {
   const uint16_t *w_sh_gate_up;    /* MoE shared expert: [2 Is][H] */
   const uint16_t *w_sh_down;       /* MoE shared expert: [H][Is] */
   const uint16_t *w_sh_gate;       /* MoE shared-expert gate vector: [H] (when shared_gate) */
+  const float *attn_sinks;         /* [Hq] one sink logit per query head, or NULL: it joins
+                                      that head's softmax denominator and adds nothing to
+                                      the output (decoder.rs AttnWeights::sinks) */
 } decoder_layer_weights_t;
 
 typedef struct {

@@ -20,12 +20,13 @@ class OrcConfig(ctypes.Structure):
         "hidden", "n_layers", "n_heads", "n_kv_heads", "head_dim", "ffn_inter", "n_experts",
         "top_k", "expert_inter", "shared_inter", "norm_topk_prob", "vocab", "qkv_bias")] + [
         ("rope_base", ctypes.c_double), ("rms_eps", ctypes.c_double),
-        ("max_seq", ctypes.c_int32), ("n_seqs", ctypes.c_int32), ("kv_bf16", ctypes.c_int32)]
+        ("max_seq", ctypes.c_int32), ("n_seqs", ctypes.c_int32), ("kv_bf16", ctypes.c_int32),
+        ("sliding_window", ctypes.c_int32), ("attn_softcap", ctypes.c_double)]
 
 
 LAYER_FIELDS = ("attn_norm", "ffn_norm", "w_qkv", "b_qkv", "w_o", "w_gate_up", "w_down",
                 "w_router", "w_exp_gate_up", "w_exp_down", "w_sh_gate_up", "w_sh_down",
-                "w_sh_gate")
+                "w_sh_gate", "attn_sinks")
 
 
 class OrcLayer(ctypes.Structure):
@@ -51,7 +52,7 @@ def lib():
         L.orc_matmul.argtypes = [_P, _I, _I, _P, _I, _P]
         L.orc_matvec.argtypes = [_P, _I, _I, _P, _P]
         L.orc_rope.argtypes = [_P, _I, _I, ctypes.c_long, _D]
-        L.orc_attend.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P]
+        L.orc_attend.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _D, _P, _P]
         L.orc_silu.restype = _D
         L.orc_silu.argtypes = [_D]
         L.orc_sigmoid.restype = _D
@@ -112,12 +113,15 @@ def rope(v, nheads, d, pos, base):
     return v
 
 
-def attend(q, kc, vc, Hq, Hkv, d):
-    """q [Hq*d]; kc, vc [T][Hkv*d] -> out [Hq*d]."""
+def attend(q, kc, vc, Hq, Hkv, d, window=0, softcap=0.0, sinks=None):
+    """q [Hq*d]; kc, vc [T][Hkv*d] -> out [Hq*d].  window, softcap and sinks
+    ([Hq] fp32) select the attention variants (0 / None: off)."""
     q, kc, vc = _f64(q), _f64(kc), _f64(vc)
     T = kc.size // (Hkv * d)
     out = np.empty(Hq * d, dtype=np.float64)
-    lib().orc_attend(q.ctypes.data, kc.ctypes.data, vc.ctypes.data, T, Hq, Hkv, d, out.ctypes.data)
+    sk = None if sinks is None else np.ascontiguousarray(sinks, dtype=np.float32)
+    lib().orc_attend(q.ctypes.data, kc.ctypes.data, vc.ctypes.data, T, Hq, Hkv, d, int(window),
+                     float(softcap), None if sk is None else sk.ctypes.data, out.ctypes.data)
     return out
 
 
@@ -168,7 +172,9 @@ class Model:
                         shared_inter=s.shared_inter, norm_topk_prob=s.norm_topk_prob,
                         vocab=s.vocab, qkv_bias=int(s.qkv_bias), rope_base=s.rope_base,
                         rms_eps=s.rms_eps, max_seq=max_seq or s.max_seq, n_seqs=n_seqs,
-                        kv_bf16=int(s.kv_bf16 if kv_bf16 is None else kv_bf16))
+                        kv_bf16=int(s.kv_bf16 if kv_bf16 is None else kv_bf16),
+                        sliding_window=getattr(s, "sliding_window", 0),
+                        attn_softcap=float(getattr(s, "attn_softcap", 0.0)))
         self.max_seq = cfg.max_seq
         layers = (OrcLayer * s.n_layers)()
         for l in range(s.n_layers):

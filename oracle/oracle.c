@@ -61,6 +61,8 @@ typedef struct {
   double rope_base, rms_eps;
   int32_t max_seq, n_seqs;
   int32_t kv_bf16;                                 /* 1: the KV cache stores bf16 values */
+  int32_t sliding_window;                          /* 0: every earlier key; W > 0: the W most recent */
+  double attn_softcap;                             /* 0: off; c > 0: score s -> c tanh(s / c) */
 } orc_config_t;
 
 typedef struct {
@@ -76,6 +78,7 @@ typedef struct {
   const uint16_t *w_sh_gate_up;                    /* [2Is][H] */
   const uint16_t *w_sh_down;                       /* [H][Is] */
   const uint16_t *w_sh_gate;                       /* [H] or NULL */
+  const float *attn_sinks;                         /* [Hq] sink logits, or NULL */
 } orc_layer_t;
 
 typedef struct {
@@ -199,31 +202,41 @@ void orc_rope(double *v, int nheads, int d, long pos, double base) {
  * engine.zig Engine.forward (cpu.attentionDecode over pos+1 rows) and
  * pipeline.rs Pipeline::new (scale 1/sqrt(head_dim)).  q: [Hq][d];
  * kc, vc: [T][Hkv*d] (row t holds every kv head of position t);
- * out: [Hq][d].  q head h reads kv head floor(h*Hkv/Hq). */
+ * out: [Hq][d].  q head h reads kv head floor(h*Hkv/Hq).
+ * Variants (engine.zig Engine.forward hands cpu.attentionDecode a logit
+ * soft-cap and, on a sliding layer, a window; decoder.rs AttnWeights::sinks):
+ *   window W > 0: only the W most recent positions (t > T - 1 - W) are keys;
+ *   softcap c > 0: every scaled score s becomes c tanh(s / c);
+ *   sinks (NULL: none): head h's sink logit z_h joins the softmax
+ *   denominator as one more term and adds nothing to the output. */
 void orc_attend(const double *q, const double *kc, const double *vc, int T, int Hq, int Hkv,
-                int d, double *out) {
+                int d, int window, double softcap, const float *sinks, double *out) {
   int kvd = Hkv * d;
   double scale = 1.0 / sqrt((double)d);
+  int t0 = (window > 0 && T > window) ? T - window : 0;
   double *s = (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
   for (int h = 0; h < Hq; ++h) {
     int g = (int)((long)h * Hkv / Hq);
     const double *qh = q + (size_t)h * d;
     double m = -INFINITY;
-    for (int t = 0; t < T; ++t) {
+    for (int t = t0; t < T; ++t) {
       const double *kt = kc + (size_t)t * kvd + (size_t)g * d;
       double acc = 0.0;
       for (int j = 0; j < d; ++j) acc += qh[j] * kt[j];
       s[t] = acc * scale;
+      if (softcap > 0.0) s[t] = softcap * tanh(s[t] / softcap);
       if (s[t] > m) m = s[t];
     }
-    double z = 0.0;
-    for (int t = 0; t < T; ++t) {
+    double zs = sinks ? (double)sinks[h] : 0.0;
+    if (sinks && zs > m) m = zs;
+    double z = sinks ? exp(zs - m) : 0.0;
+    for (int t = t0; t < T; ++t) {
       s[t] = exp(s[t] - m);
       z += s[t];
     }
     double *oh = out + (size_t)h * d;
     for (int j = 0; j < d; ++j) oh[j] = 0.0;
-    for (int t = 0; t < T; ++t) {
+    for (int t = t0; t < T; ++t) {
       const double *vt = vc + (size_t)t * kvd + (size_t)g * d;
       double p = s[t] / z;
       for (int j = 0; j < d; ++j) oh[j] += p * vt[j];
@@ -515,7 +528,7 @@ int orc_forward(orc_model_t *m, int seq, const int32_t *ids, int n, int start_po
     for (int i = 0; i < n; ++i) {
       int T = start_pos + i + 1;              /* causal: keys 0 .. start_pos+i */
       orc_attend(QKV + (size_t)i * nqkv, kv_row(m, m->kc, seq, l, 0), kv_row(m, m->vc, seq, l, 0), T,
-                 Hq, Hkv, d, O + (size_t)i * qd);
+                 Hq, Hkv, d, c->sliding_window, c->attn_softcap, L->attn_sinks, O + (size_t)i * qd);
     }
     orc_matmul(L->w_o, H, qd, O, n, Y);
     for (size_t j = 0; j < nh; ++j) X[j] += Y[j];

@@ -9,6 +9,7 @@ All matrices are bf16, row-major [out][in]:
   w_router [E][H]
   w_exp_gate_up [E][2 Ie][H], w_exp_down [E][H][Ie]
   w_sh_gate_up [2 Is][H], w_sh_down [H][Is], w_sh_gate [H]
+  attn_sinks [Hq]                fp32 holding bf16-rounded N(0, 1) values
   embed, lm_head [V][H]; norm gains fp32 [H] equal to 1.0.
 Matrices and biases are sigma = 0.02 normals; the router uses
 sigma = 1/sqrt(H) so its logits over a unit-RMS input are about N(0, 1).
@@ -25,7 +26,7 @@ SIGMA = 0.02
 
 TID = dict(embed=1, lm_head=2, w_qkv=10, b_qkv=11, w_o=12, w_gate_up=13, w_down=14,
            w_router=15, w_exp_gate_up=16, w_exp_down=17, w_sh_gate_up=18, w_sh_down=19,
-           w_sh_gate=20)
+           w_sh_gate=20, attn_sinks=21)
 
 
 def tensor_specs(shape):
@@ -43,6 +44,8 @@ def tensor_specs(shape):
         if s.qkv_bias:
             specs.append(("b_qkv", l, s.qkv_rows, SIGMA, "f32"))
         specs.append(("w_o", l, H * s.q_dim, SIGMA, "bf16"))
+        if s.attn_sinks:
+            specs.append(("attn_sinks", l, s.n_heads, 1.0, "f32"))
         if s.is_moe:
             E, Ie, Is = s.n_experts, s.expert_inter, s.shared_inter
             specs += [("w_router", l, E * H, 1.0 / np.sqrt(H), "bf16"),

@@ -33,6 +33,9 @@ class Shape:
     max_chunk: int = 128
     max_batch: int = 1
     kv_bf16: bool = True      # the KV cache stores bf16 values
+    sliding_window: int = 0   # 0: full causal attention; W > 0: the W most recent positions
+    attn_softcap: float = 0.0  # 0: off; c > 0: scaled scores s -> c tanh(s / c)
+    attn_sinks: bool = False  # one sink logit per query head and layer
 
     @property
     def is_moe(self):

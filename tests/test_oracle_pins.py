@@ -153,6 +153,81 @@ def test_attention_softmax_weights_closed_form():
     assert np.allclose(o, [1 - w1, w1, 0, 0], atol=1e-15)
 
 
+# attention variants (engine.zig Engine.forward: logit soft-cap and sliding
+# window handed to the attention; decoder.rs AttnWeights::sinks)
+
+def test_window_keeps_exactly_the_most_recent_keys():
+    Hq, Hkv, d, T = 4, 2, 16, 13
+    q = rng.normal(size=Hq * d)
+    k = rng.normal(size=(T, Hkv * d))
+    v = rng.normal(size=(T, Hkv * d))
+    plain = oracle.attend(q, k, v, Hq, Hkv, d)
+    for W in (T, T + 5):                   # a window covering every key changes nothing
+        assert np.array_equal(oracle.attend(q, k, v, Hq, Hkv, d, window=W), plain)
+    for W in (1, 4, T - 1):                # the plain attention over the last W rows
+        got = oracle.attend(q, k, v, Hq, Hkv, d, window=W)
+        assert np.array_equal(got, oracle.attend(q, k[T - W:], v[T - W:], Hq, Hkv, d))
+        assert not np.allclose(got, plain)
+    one = oracle.attend(q, k, v, Hq, Hkv, d, window=1).reshape(Hq, d)
+    for h in range(Hq):                    # window 1: the query's own value
+        g = h * Hkv // Hq
+        assert np.array_equal(one[h], v[T - 1, g * d:(g + 1) * d])
+
+
+def test_softcap_closed_form():
+    # cap 1, raw scaled scores +-atanh(1/2): capped scores +-1/2, so the two
+    # weights are the logistic of 1 and of -1
+    d = 4
+    a = math.atanh(0.5) * 2.0              # scaled by 1/sqrt(4) = 1/2 inside
+    q = np.array([1.0, 0, 0, 0])
+    k = np.array([[a, 0, 0, 0], [-a, 0, 0, 0]])
+    v = np.array([[1.0, 0, 0, 0], [0.0, 1, 0, 0]])
+    o = oracle.attend(q, k, v, 1, 1, d, softcap=1.0)
+    assert np.allclose(o, [0.7310585786300049, 0.2689414213699951, 0, 0], rtol=0, atol=1e-15)
+    # a cap far above every score leaves the plain softmax (tanh(x) = x - x^3/3 ...)
+    Hq, Hkv, d, T = 2, 1, 8, 7
+    q = rng.normal(size=Hq * d)
+    k = rng.normal(size=(T, d))
+    v = rng.normal(size=(T, d))
+    assert np.allclose(oracle.attend(q, k, v, Hq, Hkv, d, softcap=1e6), oracle.attend(q, k, v, Hq, Hkv, d),
+                       rtol=0, atol=1e-10)
+
+
+def test_sinks_closed_form_and_reductions():
+    Hq, Hkv, d, T = 2, 1, 8, 6
+    v = rng.normal(size=(T, d))
+    # zero query: every score is 0, so with a sink logit of 0 the keys share
+    # T/(T+1) of the weight: the output is T/(T+1) times the mean of V
+    o = oracle.attend(np.zeros(Hq * d), rng.normal(size=(T, d)), v, Hq, Hkv, d,
+                      sinks=np.zeros(Hq, np.float32)).reshape(Hq, d)
+    assert np.allclose(o, v.mean(axis=0) * T / (T + 1), rtol=0, atol=1e-15)
+    # a sink far below every score changes nothing; a sink far above takes all weight
+    q = rng.normal(size=Hq * d)
+    k = rng.normal(size=(T, d))
+    plain = oracle.attend(q, k, v, Hq, Hkv, d)
+    assert np.array_equal(oracle.attend(q, k, v, Hq, Hkv, d, sinks=np.full(Hq, -1e30, np.float32)), plain)
+    assert np.allclose(oracle.attend(q, k, v, Hq, Hkv, d, sinks=np.full(Hq, 80.0, np.float32)), 0,
+                       rtol=0, atol=1e-30)
+    # one sink per head: head 1's sink leaves head 0 alone
+    mixed = oracle.attend(q, k, v, Hq, Hkv, d, sinks=np.array([-1e30, 0.5], np.float32)).reshape(Hq, d)
+    assert np.array_equal(mixed[0], plain.reshape(Hq, d)[0])
+    assert not np.allclose(mixed[1], plain.reshape(Hq, d)[1])
+
+
+def test_model_variants_reduce_to_the_plain_model():
+    s = small_shape()
+    W = rand_weights(s)
+    ids = synth.tokens(12, 21, s.vocab)
+    plain = oracle.Model(s, W).forward(ids, 0, logits_mode=2)["logits"]
+    wide = oracle.Model(s.with_(sliding_window=s.max_seq), W).forward(ids, 0, logits_mode=2)["logits"]
+    assert np.array_equal(wide, plain)
+    Ws = dict(W, layers=[dict(L, attn_sinks=np.full(s.n_heads, -1e30, np.float32)) for L in W["layers"]])
+    assert np.array_equal(oracle.Model(s, Ws).forward(ids, 0, logits_mode=2)["logits"], plain)
+    narrow = oracle.Model(s.with_(sliding_window=4), W).forward(ids, 0, logits_mode=2)["logits"]
+    assert np.array_equal(narrow[:4], plain[:4])       # positions 0..3 see every key anyway
+    assert not np.allclose(narrow[4:], plain[4:])
+
+
 def test_gqa_equals_mha_with_repeated_kv_heads():
     Hq, Hkv, d, T = 8, 2, 16, 11
     q = rng.normal(size=Hq * d)
