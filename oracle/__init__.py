@@ -21,12 +21,12 @@ class OrcConfig(ctypes.Structure):
         "top_k", "expert_inter", "shared_inter", "norm_topk_prob", "vocab", "qkv_bias")] + [
         ("rope_base", ctypes.c_double), ("rms_eps", ctypes.c_double),
         ("max_seq", ctypes.c_int32), ("n_seqs", ctypes.c_int32), ("kv_bf16", ctypes.c_int32),
-        ("sliding_window", ctypes.c_int32), ("attn_softcap", ctypes.c_double)]
+        ("sliding_window", ctypes.c_int32), ("attn_softcap", ctypes.c_double), ("qk_norm", ctypes.c_int32)]
 
 
 LAYER_FIELDS = ("attn_norm", "ffn_norm", "w_qkv", "b_qkv", "w_o", "w_gate_up", "w_down",
                 "w_router", "w_exp_gate_up", "w_exp_down", "w_sh_gate_up", "w_sh_down",
-                "w_sh_gate", "attn_sinks")
+                "w_sh_gate", "attn_sinks", "q_norm", "k_norm")
 
 
 class OrcLayer(ctypes.Structure):
@@ -174,7 +174,8 @@ class Model:
                         rms_eps=s.rms_eps, max_seq=max_seq or s.max_seq, n_seqs=n_seqs,
                         kv_bf16=int(s.kv_bf16 if kv_bf16 is None else kv_bf16),
                         sliding_window=getattr(s, "sliding_window", 0),
-                        attn_softcap=float(getattr(s, "attn_softcap", 0.0)))
+                        attn_softcap=float(getattr(s, "attn_softcap", 0.0)),
+                        qk_norm=int(getattr(s, "qk_norm", False)))
         self.max_seq = cfg.max_seq
         layers = (OrcLayer * s.n_layers)()
         for l in range(s.n_layers):

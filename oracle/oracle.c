@@ -63,6 +63,7 @@ typedef struct {
   int32_t kv_bf16;                                 /* 1: the KV cache stores bf16 values */
   int32_t sliding_window;                          /* 0: every earlier key; W > 0: the W most recent */
   double attn_softcap;                             /* 0: off; c > 0: score s -> c tanh(s / c) */
+  int32_t qk_norm;                                 /* 1: RMSNorm of every q and k head before RoPE */
 } orc_config_t;
 
 typedef struct {
@@ -79,6 +80,7 @@ typedef struct {
   const uint16_t *w_sh_down;                       /* [H][Is] */
   const uint16_t *w_sh_gate;                       /* [H] or NULL */
   const float *attn_sinks;                         /* [Hq] sink logits, or NULL */
+  const float *q_norm, *k_norm;                    /* [d] per-head norm gains (qk_norm) */
 } orc_layer_t;
 
 typedef struct {
@@ -516,6 +518,10 @@ int orc_forward(orc_model_t *m, int seq, const int32_t *ids, int n, int start_po
     for (int i = 0; i < n; ++i) {
       double *q = QKV + (size_t)i * nqkv, *k = q + qd, *v = k + kvd;
       long pos = (long)start_pos + i;
+      if (c->qk_norm) {                       /* engine.zig applyHeadNorm: per head, before RoPE */
+        for (int h = 0; h < Hq; ++h) orc_rmsnorm(q + (size_t)h * d, L->q_norm, d, c->rms_eps, q + (size_t)h * d);
+        for (int h = 0; h < Hkv; ++h) orc_rmsnorm(k + (size_t)h * d, L->k_norm, d, c->rms_eps, k + (size_t)h * d);
+      }
       orc_rope(q, Hq, d, pos, c->rope_base);
       orc_rope(k, Hkv, d, pos, c->rope_base);
       double *kr = kv_row(m, m->kc, seq, l, (int)pos), *vr = kv_row(m, m->vc, seq, l, (int)pos);

@@ -67,6 +67,8 @@ def device_weights(shape, device="cuda"):
             dev_normal_bf16(t, seed_of(name, layer), sigma)
             if kind == "f32":
                 t = t.float()
+            elif kind == "gain":
+                t = t.float() + 1.0
         if layer is None:
             out[name] = t
         else:

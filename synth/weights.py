@@ -10,6 +10,7 @@ All matrices are bf16, row-major [out][in]:
   w_exp_gate_up [E][2 Ie][H], w_exp_down [E][H][Ie]
   w_sh_gate_up [2 Is][H], w_sh_down [H][Is], w_sh_gate [H]
   attn_sinks [Hq]                fp32 holding bf16-rounded N(0, 1) values
+  q_norm, k_norm [d]             fp32 1 + bf16-rounded N(0, 0.25^2) (per-head norm gains)
   embed, lm_head [V][H]; norm gains fp32 [H] equal to 1.0.
 Matrices and biases are sigma = 0.02 normals; the router uses
 sigma = 1/sqrt(H) so its logits over a unit-RMS input are about N(0, 1).
@@ -26,12 +27,13 @@ SIGMA = 0.02
 
 TID = dict(embed=1, lm_head=2, w_qkv=10, b_qkv=11, w_o=12, w_gate_up=13, w_down=14,
            w_router=15, w_exp_gate_up=16, w_exp_down=17, w_sh_gate_up=18, w_sh_down=19,
-           w_sh_gate=20, attn_sinks=21)
+           w_sh_gate=20, attn_sinks=21, q_norm=22, k_norm=23)
 
 
 def tensor_specs(shape):
     """[(name, layer or None, numel, sigma, kind)] for every generated tensor.
-    kind is 'bf16' (matrix), 'f32' (bias stored as fp32) or 'ones' (norm gain)."""
+    kind is 'bf16' (matrix), 'f32' (bias stored as fp32), 'ones' (norm gain) or
+    'gain' (fp32 1 + a bf16-rounded normal: the per-head q/k norm gains)."""
     s = shape
     H = s.hidden
     specs = [("embed", None, s.vocab * H, SIGMA, "bf16")]
@@ -46,6 +48,8 @@ def tensor_specs(shape):
         specs.append(("w_o", l, H * s.q_dim, SIGMA, "bf16"))
         if s.attn_sinks:
             specs.append(("attn_sinks", l, s.n_heads, 1.0, "f32"))
+        if s.qk_norm:
+            specs += [("q_norm", l, s.head_dim, 0.25, "gain"), ("k_norm", l, s.head_dim, 0.25, "gain")]
         if s.is_moe:
             E, Ie, Is = s.n_experts, s.expert_inter, s.shared_inter
             specs += [("w_router", l, E * H, 1.0 / np.sqrt(H), "bf16"),
@@ -71,6 +75,8 @@ def host_tensor(name, layer, numel, sigma, kind):
         return np.ones(numel, dtype=np.float32)
     if kind == "f32":
         return normal_bf16_f32(numel, seed_of(name, layer), sigma)
+    if kind == "gain":
+        return normal_bf16_f32(numel, seed_of(name, layer), sigma) + np.float32(1.0)
     return normal_bf16(numel, seed_of(name, layer), sigma)
 
 

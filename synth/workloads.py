@@ -36,6 +36,7 @@ class Shape:
     sliding_window: int = 0   # 0: full causal attention; W > 0: the W most recent positions
     attn_softcap: float = 0.0  # 0: off; c > 0: scaled scores s -> c tanh(s / c)
     attn_sinks: bool = False  # one sink logit per query head and layer
+    qk_norm: bool = False     # RMSNorm of every q and k head (gains q_norm, k_norm [d]) before RoPE
 
     @property
     def is_moe(self):

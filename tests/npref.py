@@ -45,16 +45,35 @@ def forward(shape, W, ids):
         QKV = A @ w(L["w_qkv"]).reshape(s.qkv_rows, H).T
         if s.qkv_bias:
             QKV = QKV + L["b_qkv"].astype(np.float64)
-        Q = rope(QKV[:, :Hq * d].reshape(n, Hq, d), pos, s.rope_base)
-        K = rope(QKV[:, Hq * d:(Hq + Hkv) * d].reshape(n, Hkv, d), pos, s.rope_base)
+        Q = QKV[:, :Hq * d].reshape(n, Hq, d)
+        K = QKV[:, Hq * d:(Hq + Hkv) * d].reshape(n, Hkv, d)
+        if getattr(s, "qk_norm", False):
+            Q = rmsnorm(Q, L["q_norm"], s.rms_eps)
+            K = rmsnorm(K, L["k_norm"], s.rms_eps)
+        Q = rope(Q, pos, s.rope_base)
+        K = rope(K, pos, s.rope_base)
         V = QKV[:, (Hq + Hkv) * d:].reshape(n, Hkv, d)
         grp = Hq // Hkv
         K = np.repeat(K, grp, axis=1)
         V = np.repeat(V, grp, axis=1)
         S = np.einsum("ihd,jhd->hij", Q, K) / np.sqrt(d)
-        S = np.where(mask[None], S, -np.inf)
-        P = np.exp(S - S.max(axis=-1, keepdims=True))
-        P /= P.sum(axis=-1, keepdims=True)
+        cap = getattr(s, "attn_softcap", 0.0)
+        if cap > 0:
+            S = cap * np.tanh(S / cap)
+        seen = mask
+        win = getattr(s, "sliding_window", 0)
+        if win > 0:
+            seen = mask & (np.arange(n)[:, None] - np.arange(n)[None, :] < win)
+        S = np.where(seen[None], S, -np.inf)
+        sinks = L.get("attn_sinks")
+        if sinks is not None:
+            z = sinks.astype(np.float64)[:, None, None]
+            top = np.maximum(S.max(axis=-1, keepdims=True), z)
+            P = np.exp(S - top)
+            P /= P.sum(axis=-1, keepdims=True) + np.exp(z - top)
+        else:
+            P = np.exp(S - S.max(axis=-1, keepdims=True))
+            P /= P.sum(axis=-1, keepdims=True)
         O = np.einsum("hij,jhd->ihd", P, V).reshape(n, Hq * d)
         X = X + O @ w(L["w_o"]).reshape(H, Hq * d).T
         B = rmsnorm(X, L["ffn_norm"], s.rms_eps)

@@ -228,6 +228,33 @@ def test_model_variants_reduce_to_the_plain_model():
     assert not np.allclose(narrow[4:], plain[4:])
 
 
+def test_qk_norm_makes_each_head_scale_free():
+    """With the per-head RMSNorm of q and k (engine.zig applyHeadNorm, before
+    RoPE) and eps 0, scaling one q head's or one k head's weight rows by a
+    power of two (exact in bf16) leaves the logits unchanged; without it they
+    move.  A norm over the wrong slice (the whole q vector, or across heads)
+    would not cancel a single head's scale."""
+    for qk in (True, False):
+        s = small_shape(qk_norm=qk, rms_eps=0.0)
+        W = rand_weights(s)
+        for L in W["layers"]:
+            L["q_norm"] = (1 + 0.2 * rng.normal(size=s.head_dim)).astype(np.float32)
+            L["k_norm"] = (1 + 0.2 * rng.normal(size=s.head_dim)).astype(np.float32)
+        ids = synth.tokens(9, 31, s.vocab)
+        base = oracle.Model(s, W).forward(ids, 0, logits_mode=2)["logits"]
+        d, H = s.head_dim, s.hidden
+        W2 = dict(W, layers=[dict(L) for L in W["layers"]])
+        wq = widen(W2["layers"][0]["w_qkv"]).reshape(s.qkv_rows, H).copy()
+        wq[1 * d:2 * d] *= 4.0                          # q head 1
+        wq[s.q_dim + 0 * d:s.q_dim + 1 * d] *= 0.5      # k head 0
+        W2["layers"][0]["w_qkv"] = bits(wq)
+        got = oracle.Model(s, W2).forward(ids, 0, logits_mode=2)["logits"]
+        if qk:
+            assert np.allclose(got, base, rtol=0, atol=1e-12 * np.abs(base).max())
+        else:
+            assert not np.allclose(got, base, rtol=0, atol=1e-6)
+
+
 def test_gqa_equals_mha_with_repeated_kv_heads():
     Hq, Hkv, d, T = 8, 2, 16, 11
     q = rng.normal(size=Hq * d)
