@@ -283,6 +283,7 @@ def main():
                     help="attention variant: every query sees only the W most recent positions")
     ap.add_argument("--attn-softcap", type=float, default=0.0, help="attention variant: logit soft-cap")
     ap.add_argument("--attn-sinks", action="store_true", help="attention variant: per-head sink logits")
+    ap.add_argument("--qk-norm", action="store_true", help="attention variant: per-head RMSNorm of q and k")
     ap.add_argument("--no-verify", action="store_true",
                     help="skip the multi-position verify measurement (batch-1 workloads)")
     ap.add_argument("--verify-reps", type=int, default=20)
@@ -340,6 +341,8 @@ def main():
         variant["attn_softcap"] = args.attn_softcap
     if args.attn_sinks:
         variant["attn_sinks"] = True
+    if args.qk_norm:
+        variant["qk_norm"] = True
     if variant:
         shape = shape.with_(name=shape.name + "-" + "-".join(f"{k}{v}" for k, v in variant.items()), **variant)
     # the first decode step (reported on its own), the warmup and the timed

@@ -24,12 +24,12 @@ class DecoderConfig(ctypes.Structure):
         "top_k", "expert_inter", "shared_inter", "shared_gate", "norm_topk_prob", "vocab",
         "qkv_bias")] + [("rope_base", ctypes.c_double), ("rms_eps", ctypes.c_double)] + [
         (n, _I32) for n in ("max_seq", "max_chunk", "max_batch", "sliding_window")] + [
-        ("attn_softcap", ctypes.c_double)]
+        ("attn_softcap", ctypes.c_double), ("qk_norm", _I32)]
 
 
 LAYER_FIELDS = ("attn_norm", "ffn_norm", "w_qkv", "b_qkv", "w_o", "w_gate_up", "w_down",
                 "w_router", "w_exp_gate_up", "w_exp_down", "w_sh_gate_up", "w_sh_down",
-                "w_sh_gate", "attn_sinks")
+                "w_sh_gate", "attn_sinks", "q_norm", "k_norm")
 
 
 class DecoderLayerWeights(ctypes.Structure):
@@ -131,7 +131,7 @@ def make_config(shape):
         norm_topk_prob=int(s.norm_topk_prob), vocab=s.vocab, qkv_bias=int(s.qkv_bias),
         rope_base=float(s.rope_base), rms_eps=float(s.rms_eps), max_seq=s.max_seq,
         max_chunk=s.max_chunk, max_batch=s.max_batch, sliding_window=getattr(s, "sliding_window", 0),
-        attn_softcap=float(getattr(s, "attn_softcap", 0.0)))
+        attn_softcap=float(getattr(s, "attn_softcap", 0.0)), qk_norm=int(getattr(s, "qk_norm", False)))
 
 
 # ---------------------------------------------------- same-named functions --

@@ -87,6 +87,7 @@ bool config_ok(const decoder_config_t *c) {
     return false;
   if (!(c->rope_base > 0.0) || !(c->rms_eps >= 0.0)) return false;
   if (c->sliding_window < 0 || !(c->attn_softcap >= 0.0) || c->attn_softcap > 1e30) return false;
+  if (c->qk_norm != 0 && c->qk_norm != 1) return false;
   if (c->n_experts > 0) {
     if (c->n_experts > 256 || c->top_k <= 0 || c->top_k > 8 || c->top_k > c->n_experts) return false;
     if (c->expert_inter <= 0 || c->expert_inter % 8 || c->shared_inter < 0 || c->shared_inter % 8)
@@ -503,6 +504,41 @@ GemvArgs gemv_args(const uint16_t *W, const float *a, int K, int n_items, float 
   return g;
 }
 
+// With per-head QK-norm the QKV projection stores its raw output (bias
+// added) in D->qkv, and this pass norms each q and k head, rotates, stores
+// q and appends K and V (the fused QKV epilogue cannot: one head's outputs
+// come from many waves).
+int qk_norm_pass(decoder *D, int l, int rows) {
+  const decoder_config_t &c = D->c;
+  const decoder_layer_weights_t &W = D->layers[l];
+  const int d = c.head_dim;
+  const int qkvr = (c.n_heads + 2 * c.n_kv_heads) * d;
+  NodeTimer t(D, DEC_NODE_ROPE, rows * (double)qkvr * 8.0, rows * (double)qkvr * 6.0);
+  QkNormArgs a{};
+  a.qkv = D->qkv;
+  a.ld = qkvr;
+  a.q_norm = W.q_norm;
+  a.k_norm = W.k_norm;
+  a.eps = (float)c.rms_eps;
+  a.cs = D->rope;
+  a.row_seq = D->row_seq;
+  a.row_pos = D->row_pos;
+  a.q = D->q;
+  a.q_lo = D->q_lo;
+  a.kcache = D->kcache;
+  a.vcache = D->vcache;
+  a.seq_stride = D->L.seq_stride;
+  a.layer_off = (int64_t)l * c.n_kv_heads * (int64_t)D->L.S * d;
+  a.S = D->L.S;
+  a.Hq = c.n_heads;
+  a.Hkv = c.n_kv_heads;
+  a.d = d;
+  a.rows = rows;
+  hipError_t e = launch_qk_norm_rope(a, D->stream);
+  if (e != hipSuccess) return hip_fail(D, e, "qk norm");
+  return DEC_OK;
+}
+
 // One decode row: every projection is a GEMV over fp32 activations.
 int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
   const decoder_config_t &c = D->c;
@@ -512,6 +548,14 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
   int rc;
   hipError_t e;
 
+  if (c.qk_norm) {
+    GemvArgs qs = gemv_args(W.w_qkv, D->x, H, (c.n_heads + 2 * c.n_kv_heads) * d, D->qkv);
+    qs.gamma = W.attn_norm;
+    qs.eps = eps;
+    qs.bias = c.qkv_bias ? W.b_qkv : nullptr;
+    if ((rc = gemv(D, DEC_NODE_QKV, EPI_STORE, qs))) return rc;
+    if ((rc = qk_norm_pass(D, l, 1))) return rc;
+  }
   GemvArgs q = gemv_args(W.w_qkv, D->x, H, (c.n_heads + 2 * c.n_kv_heads) * d / 2, nullptr);
   q.gamma = W.attn_norm;
   q.eps = eps;
@@ -534,7 +578,7 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
   q.qkv.Hq = c.n_heads;
   q.qkv.Hkv = c.n_kv_heads;
   q.qkv.d = d;
-  if ((rc = gemv(D, DEC_NODE_QKV, EPI_QKV, q))) return rc;
+  if (!c.qk_norm && (rc = gemv(D, DEC_NODE_QKV, EPI_QKV, q))) return rc;
   if ((rc = attention(D, l, 1, 1, max_pos, hpos, D->f32_attn))) return rc;
   if ((rc = gemv(D, DEC_NODE_O, EPI_ADD, gemv_args(W.w_o, D->f32_attn, qd, H, D->x)))) return rc;
 
@@ -645,7 +689,17 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   q.qkv.Hkv = c.n_kv_heads;
   q.qkv.d = d;
   q.Wp = D->packed[l].w[0];
-  if ((rc = proj(D, DEC_NODE_QKV, EPI_QKV, q, rows))) return rc;
+  if (c.qk_norm) {
+    // plain projection (bias added) into D->qkv, then the per-head norm pass
+    q.np_off = qkvr;
+    q.bias = c.qkv_bias ? W.b_qkv : nullptr;
+    q.C = D->qkv;
+    q.ldc = qkvr;
+    if ((rc = proj(D, DEC_NODE_QKV, EPI_STORE, q, rows))) return rc;
+    if ((rc = qk_norm_pass(D, l, rows))) return rc;
+  } else if ((rc = proj(D, DEC_NODE_QKV, EPI_QKV, q, rows))) {
+    return rc;
+  }
   if ((rc = attention(D, l, rows, rows_per_group, max_pos, hpos))) return rc;
   GemmArgs o = dense_args(D->attn, qd, W.w_o, rows, H, qd);
   o.Wp = D->packed[l].w[1];
@@ -870,6 +924,7 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
     const decoder_layer_weights_t &lw = w->layers[l];
     if (!lw.attn_norm || !lw.ffn_norm || !lw.w_qkv || !lw.w_o) return DEC_E_INVALID;
     if (cfg->qkv_bias && !lw.b_qkv) return DEC_E_INVALID;
+    if (cfg->qk_norm && (!lw.q_norm || !lw.k_norm)) return DEC_E_INVALID;
     if (cfg->n_experts == 0 && (!lw.w_gate_up || !lw.w_down)) return DEC_E_INVALID;
     if (cfg->n_experts > 0) {
       if (!lw.w_router || !lw.w_exp_gate_up || !lw.w_exp_down) return DEC_E_INVALID;

@@ -161,6 +161,24 @@ hipError_t launch_embed(const uint16_t *E, const int32_t *ids, const int32_t *ne
 hipError_t launch_rmsnorm(const float *x, int64_t ldx, const float *g, int rows, int H, float eps,
                           uint16_t *out, int64_t ldo, int64_t out_lo, hipStream_t st, float *out_f32 = nullptr);
 
+// Per-head RMSNorm of q and k (gains [d], eps), then RoPE, the q store
+// (split bf16 [rows][Hq][d], lo plane at q + q_lo) and the KV-cache append,
+// from the projection's fp32 output qkv [rows][ld] (bias already added).
+struct QkNormArgs {
+  const float *qkv;
+  int64_t ld;
+  const float *q_norm, *k_norm;
+  float eps;
+  const float2 *cs;                  // (cos, sin) [S][d/2]
+  const int32_t *row_seq, *row_pos;  // [rows]
+  uint16_t *q;
+  int64_t q_lo;
+  uint16_t *kcache, *vcache;
+  int64_t seq_stride, layer_off;
+  int32_t S, Hq, Hkv, d, rows;
+};
+hipError_t launch_qk_norm_rope(const QkNormArgs &a, hipStream_t st);
+
 // V^T cache import: src [Hkv][len][d] -> dst [Hkv][d][S] (positions < len)
 hipError_t launch_kv_load_v(const uint16_t *src, uint16_t *dst, int Hkv, int len, int d, int S,
                             hipStream_t st);

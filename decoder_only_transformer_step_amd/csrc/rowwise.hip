@@ -61,7 +61,58 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x, int64_t ld
   }
 }
 
+// Per-head QK-norm (engine.zig applyHeadNorm: RMSNorm of each q and k head
+// with gains [d] and the model's eps, before RoPE), then RoPE ("rope"
+// pairing u_i with u_{i+d/2}), the q store and the KV append, as the fused
+// QKV epilogue does them when there is no per-head norm.  One 64-lane block
+// per (row, head of q, k or v); lane i owns the pair (i, i + d/2).
+__global__ __launch_bounds__(64) void qk_norm_rope_kernel(QkNormArgs a) {
+  const int nh = a.Hq + 2 * a.Hkv;
+  const int r = blockIdx.x / nh, hh = blockIdx.x - r * nh;
+  const int d = a.d, half = d / 2, i = threadIdx.x;
+  const bool on = i < half;
+  const float *src = a.qkv + (int64_t)r * a.ld + (int64_t)hh * d;
+  float u0 = on ? src[i] : 0.f, u1 = on ? src[i + half] : 0.f;
+  const int pos = a.row_pos[r], seq = a.row_seq[r];
+  const int64_t base = (int64_t)seq * a.seq_stride + a.layer_off;
+  if (hh < a.Hq + a.Hkv) {
+    const float ss = wave_sum(u0 * u0 + u1 * u1);
+    const float inv = 1.0f / sqrtf(ss / (float)d + a.eps);
+    if (!on) return;
+    const float *g = hh < a.Hq ? a.q_norm : a.k_norm;
+    u0 = u0 * inv * g[i];
+    u1 = u1 * inv * g[i + half];
+    const float2 t = a.cs[(int64_t)pos * half + i];
+    const float r0 = u0 * t.x - u1 * t.y;
+    const float r1 = u0 * t.y + u1 * t.x;
+    if (hh < a.Hq) {
+      uint16_t *dst = a.q + ((int64_t)r * a.Hq + hh) * d;
+      uint32_t h0, l0, h1, l1;
+      split_bf16(r0, h0, l0);
+      split_bf16(r1, h1, l1);
+      dst[i] = (uint16_t)h0;
+      dst[i + half] = (uint16_t)h1;
+      dst[a.q_lo + i] = (uint16_t)l0;
+      dst[a.q_lo + i + half] = (uint16_t)l1;
+    } else {
+      uint16_t *dst = a.kcache + base + ((int64_t)(hh - a.Hq) * a.S + pos) * d;
+      dst[i] = (uint16_t)f32_to_bf16_bits(r0);
+      dst[i + half] = (uint16_t)f32_to_bf16_bits(r1);
+    }
+  } else if (on) {
+    uint16_t *vt = a.vcache + base + (int64_t)(hh - a.Hq - a.Hkv) * d * a.S;
+    vt[(int64_t)i * a.S + pos] = (uint16_t)f32_to_bf16_bits(u0);
+    vt[(int64_t)(i + half) * a.S + pos] = (uint16_t)f32_to_bf16_bits(u1);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_qk_norm_rope(const QkNormArgs &a, hipStream_t st) {
+  if (a.d / 2 > 64 || a.rows <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(qk_norm_rope_kernel, dim3(a.rows * (a.Hq + 2 * a.Hkv)), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_embed(const uint16_t *E, const int32_t *ids, const int32_t *next_token,
                         const int32_t *row_seq, int use_next, int rows, int H, float *x,

@@ -91,6 +91,9 @@ typedef struct {
                               the query at position p sees keys t with p - W < t <= p
                               (every layer) */
   double attn_softcap;     /* 0: off; c > 0: each scaled score s becomes c tanh(s / c) */
+  int32_t qk_norm;         /* 1: RMSNorm (gains q_norm / k_norm [d], eps rms_eps) of every q
+                              and k head after the bias and before RoPE (engine.zig
+                              applyHeadNorm) */
 } decoder_config_t;
 
 typedef struct {
@@ -110,6 +113,8 @@ typedef struct {
   const float *attn_sinks;         /* [Hq] one sink logit per query head, or NULL: it joins
                                       that head's softmax denominator and adds nothing to
                                       the output (decoder.rs AttnWeights::sinks) */
+  const float *q_norm;             /* [d] per-head q norm gains (required when qk_norm) */
+  const float *k_norm;             /* [d] per-head k norm gains (required when qk_norm) */
 } decoder_layer_weights_t;
 
 typedef struct {

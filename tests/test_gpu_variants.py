@@ -1,6 +1,7 @@
-"""Attention variants against the oracle: a sliding window, a logit soft-cap
-and per-head sink logits (engine.zig Engine.forward hands its attention a
-soft-cap and, on a sliding layer, a window; decoder.rs AttnWeights::sinks),
+"""Attention variants against the oracle: a sliding window, a logit soft-cap,
+per-head sink logits and per-head QK-norm (engine.zig Engine.forward hands
+its attention a soft-cap and, on a sliding layer, a window, and
+applyHeadNorm norms q and k heads before RoPE; decoder.rs AttnWeights::sinks),
 alone and together.  Each runs a chunked prefill (several rows per block
 and several key splits on the 8B shape, with the window crossing chunk and
 split boundaries) and teacher-forced decode steps, logits compared with the
@@ -24,7 +25,7 @@ BASES = {
     "tiny": (TINY, 16, 16, 8, 8, 0.05),
     "8b2": (C8B.with_(name="gqa-8b-layers-2", n_layers=2, vocab=1024, max_seq=512), 200, 128, 6, 100, 2.0),
 }
-VARIANTS = ("window", "softcap", "sinks", "all")
+VARIANTS = ("window", "softcap", "sinks", "qknorm", "all")
 
 
 def variant_shape(which, variant):
@@ -36,6 +37,8 @@ def variant_shape(which, variant):
         kw["attn_softcap"] = cap
     if variant in ("sinks", "all"):
         kw["attn_sinks"] = True
+    if variant in ("qknorm", "all"):
+        kw["qk_norm"] = True
     return base.with_(name=f"{base.name}-{variant}", **kw)
 
 
