@@ -66,6 +66,8 @@ def lib():
         L.orc_reset.argtypes = [_P, _I]
         L.orc_kv_load.restype = _I
         L.orc_kv_load.argtypes = [_P, _I, _I, _P, _P, _I]
+        L.orc_quantize_rows.restype = None
+        L.orc_quantize_rows.argtypes = [_P, _I, _I, _P, _P]
         L.orc_truncate.restype = _I
         L.orc_truncate.argtypes = [_P, _I, _I]
         L.orc_seq_len.restype = ctypes.c_int32
@@ -148,6 +150,39 @@ def argmax(v):
     return int(lib().orc_argmax(v.ctypes.data, v.size))
 
 
+def quantize_rows(W_bits, rows, cols):
+    """int8 codes with one power-of-two scale per row, returned dequantised
+    (bf16 bit patterns, exact) together with the per-row exponents."""
+    W_bits = np.ascontiguousarray(W_bits, dtype=np.uint16).reshape(rows, cols)
+    out = np.empty_like(W_bits)
+    e = np.empty(rows, dtype=np.int32)
+    lib().orc_quantize_rows(W_bits.ctypes.data, rows, cols, out.ctypes.data, e.ctypes.data)
+    return out, e
+
+
+# matrices whose decode projections stream quantised weights
+QUANT_FIELDS = ("w_qkv", "w_o", "w_gate_up", "w_down")
+
+
+def quantized_weights(shape, weights):
+    """The model's weights as the quantised decoder holds them: every layer
+    matrix and the lm-head dequantised (the embedding gather keeps its bf16
+    table)."""
+    s = shape
+    H = s.hidden
+    dims = {"w_qkv": (s.qkv_rows, H), "w_o": (H, s.q_dim), "w_gate_up": (2 * s.ffn_inter, H),
+            "w_down": (H, s.ffn_inter)}
+    out = dict(weights)
+    out["layers"] = []
+    for L in weights["layers"]:
+        L2 = dict(L)
+        for f in QUANT_FIELDS:
+            L2[f] = quantize_rows(L[f], *dims[f])[0].reshape(-1)
+        out["layers"].append(L2)
+    out["lm_head"] = quantize_rows(weights["lm_head"], s.vocab, H)[0].reshape(-1)
+    return out
+
+
 # ----------------------------------------------------------------- model --
 
 class OracleError(RuntimeError):
@@ -164,6 +199,8 @@ class Model:
 
     def __init__(self, shape, weights, n_seqs=1, max_seq=None, kv_bf16=None):
         self.shape = shape
+        if getattr(shape, "weight_quant", 0):
+            weights = quantized_weights(shape, weights)
         self._keep = []
         s = shape
         cfg = OrcConfig(hidden=s.hidden, n_layers=s.n_layers, n_heads=s.n_heads,

@@ -389,6 +389,38 @@ int orc_kv_load(orc_model_t *m, int seq, int layer, const uint16_t *K, const uin
   return ORC_OK;
 }
 
+/* Weight quantisation (quantised weight streaming for decode): each row of
+ * a bf16 matrix W [rows][K] becomes int8 codes q and one power-of-two scale
+ * 2^e, with e the smallest integer for which 127 * 2^e covers the row's
+ * largest magnitude a, and q_k = w_k / 2^e rounded to the nearest integer
+ * (ties to even).  Every step is exact in fp64 (a bf16 value divided by a
+ * power of two, then rounded), so the codes follow from the definition
+ * alone.  The dequantised weight q_k * 2^e has at most 7 significant bits,
+ * so it is itself a bf16 value; out receives those bf16 bit patterns and
+ * e_out (optional) the exponents. */
+void orc_quantize_rows(const uint16_t *W, int rows, int K, uint16_t *out, int32_t *e_out) {
+  for (int r = 0; r < rows; ++r) {
+    const uint16_t *w = W + (size_t)r * K;
+    double a = 0.0;
+    for (int k = 0; k < K; ++k) a = fmax(a, fabs(bf(w[k])));
+    int e = 0;
+    if (a > 0.0) {
+      int p;
+      double m = frexp(a, &p);          /* a = m 2^p, m in [0.5, 1) */
+      e = (m <= 127.0 / 128.0) ? p - 7 : p - 6;
+    }
+    if (e_out) e_out[r] = e;
+    for (int k = 0; k < K; ++k) {
+      double q = nearbyint(ldexp(bf(w[k]), -e));  /* default rounding: to nearest, ties to even */
+      double v = ldexp(q, e);
+      float f = (float)v;                          /* exact: q 2^e fits bf16 */
+      uint32_t u;
+      memcpy(&u, &f, 4);
+      out[(size_t)r * K + k] = (uint16_t)(u >> 16);
+    }
+  }
+}
+
 /* Roll a sequence back to its first len positions (0 <= len <= current
  * length): the rows past len stop being part of it and are cleared, so the
  * state equals one that never held them.  pipeline.rs

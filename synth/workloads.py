@@ -37,6 +37,7 @@ class Shape:
     attn_softcap: float = 0.0  # 0: off; c > 0: scaled scores s -> c tanh(s / c)
     attn_sinks: bool = False  # one sink logit per query head and layer
     qk_norm: bool = False     # RMSNorm of every q and k head (gains q_norm, k_norm [d]) before RoPE
+    weight_quant: int = 0     # 1: layer matrices and lm-head as int8 with a power-of-two scale per row
 
     @property
     def is_moe(self):

@@ -625,3 +625,38 @@ def test_bf16_kv_cache_rounds_only_the_cache():
     assert np.allclose(x_exact, np.array([1.0, 0, 0, 0]) + v_exact, atol=1e-15)
     assert np.allclose(x_bf, np.array([1.0, 0, 0, 0]) + [oracle.round_bf16(t) for t in v_exact], atol=1e-15)
     assert not np.allclose(x_exact, x_bf, atol=1e-6)
+
+
+# ------------------------------------------------------ weight quantisation --
+
+def test_quantize_rows_worked_example():
+    """int8 codes with a power-of-two scale per row: row 0 has largest
+    magnitude 1, so 127 * 2^e >= 1 first holds at e = -6 (codes 64, -32, 16,
+    and 0.0078125 * 64 = 0.5 rounds to the even 0); row 1's largest magnitude
+    0.3125 gives e = -8 (127 / 256 >= 0.3125 > 127 / 512), and 0.3828125 *
+    256 = 98 exactly; row 2 checks the tie 1.5 -> 2 and -2.5 -> -2."""
+    W = bits(np.array([[1.0, -0.5, 0.25, 0.0078125],
+                       [0.3125, -0.0625, 0.3828125, 0.015625],
+                       [1.5 / 64, -2.5 / 64, 1.0, 0.0]], np.float32))
+    deq, e = oracle.quantize_rows(W, 3, 4)
+    got = synth.bf16_to_f32(deq)
+    assert list(e) == [-6, -8, -6]
+    assert np.array_equal(got[0], np.array([1.0, -0.5, 0.25, 0.0], np.float32))
+    assert np.array_equal(got[1], np.array([0.3125, -0.0625, 0.3828125, 0.015625], np.float32))
+    assert np.array_equal(got[2], np.array([2 / 64, -2 / 64, 1.0, 0.0], np.float32))
+
+
+def test_quantize_rows_properties():
+    rows, K = 64, 96
+    W = rand_bits((rows, K), 0.05)
+    w = widen(W)
+    deq, e = oracle.quantize_rows(W, rows, K)
+    d = widen(deq)
+    step = np.ldexp(1.0, e)[:, None]
+    q = d / step
+    assert np.array_equal(q, np.rint(q))                      # integer codes
+    assert np.abs(q).max() <= 127                             # in int8 range
+    assert np.all(np.abs(q).max(axis=1) >= 64)                # e is the smallest that covers the row
+    assert np.all(np.abs(w - d) <= step / 2)                  # rounded to the nearest code
+    again, e2 = oracle.quantize_rows(deq, rows, K)            # idempotent
+    assert np.array_equal(again, deq) and np.array_equal(e2, e)
