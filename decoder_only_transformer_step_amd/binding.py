@@ -24,7 +24,7 @@ class DecoderConfig(ctypes.Structure):
         "top_k", "expert_inter", "shared_inter", "shared_gate", "norm_topk_prob", "vocab",
         "qkv_bias")] + [("rope_base", ctypes.c_double), ("rms_eps", ctypes.c_double)] + [
         (n, _I32) for n in ("max_seq", "max_chunk", "max_batch", "sliding_window")] + [
-        ("attn_softcap", ctypes.c_double), ("qk_norm", _I32)]
+        ("attn_softcap", ctypes.c_double), ("qk_norm", _I32), ("weight_quant", _I32)]
 
 
 LAYER_FIELDS = ("attn_norm", "ffn_norm", "w_qkv", "b_qkv", "w_o", "w_gate_up", "w_down",
@@ -72,6 +72,7 @@ SIGNATURES = {
     "dec_diag_gemm_chunk": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, ctypes.c_int64, _P]),
     "dec_diag_pack_w32": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "dec_diag_rmsnorm": (ctypes.c_int, [_P, _P, _I32, _I32, ctypes.c_double, _P, _P]),
+    "dec_diag_quantize_rows": (ctypes.c_int, [_P, ctypes.c_int64, _I32, _P, _P, _P, _P]),
     "dec_diag_gemv": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _P]),
     "dec_diag_moe_route": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "decoder_debug_layer_limit": (ctypes.c_int, [_P, _I32]),
@@ -131,7 +132,8 @@ def make_config(shape):
         norm_topk_prob=int(s.norm_topk_prob), vocab=s.vocab, qkv_bias=int(s.qkv_bias),
         rope_base=float(s.rope_base), rms_eps=float(s.rms_eps), max_seq=s.max_seq,
         max_chunk=s.max_chunk, max_batch=s.max_batch, sliding_window=getattr(s, "sliding_window", 0),
-        attn_softcap=float(getattr(s, "attn_softcap", 0.0)), qk_norm=int(getattr(s, "qk_norm", False)))
+        attn_softcap=float(getattr(s, "attn_softcap", 0.0)), qk_norm=int(getattr(s, "qk_norm", False)),
+        weight_quant=int(getattr(s, "weight_quant", 0)))
 
 
 # ---------------------------------------------------- same-named functions --
@@ -304,6 +306,11 @@ def diag_moe_route(logits, k, renorm, ids, wts, stream):
     rows, E = logits.shape
     _check(lib().dec_diag_moe_route(_ptr(logits), rows, E, k, int(renorm), _ptr(ids), _ptr(wts),
                                     ctypes.c_void_p(stream)), None, "dec_diag_moe_route")
+
+
+def diag_quantize_rows(W, rows, K, q, scale, deq, stream=0):
+    _check(lib().dec_diag_quantize_rows(_ptr(W), rows, K, _ptr(q), _ptr(scale), _ptr(deq), ctypes.c_void_p(stream)),
+           None, "dec_diag_quantize_rows")
 
 
 def diag_rmsnorm(x, g, eps, out, stream):

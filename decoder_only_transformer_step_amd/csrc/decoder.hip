@@ -9,6 +9,7 @@
 // pinned staging ring, and enqueues the kernels of the step on the stream.
 #include <hip/hip_runtime.h>
 
+#include <array>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -44,7 +45,36 @@ struct Layout {
   int64_t seq_stride;
   size_t gpart_elems, am_n;
   size_t packed;               // packed weight copies for the chunk kernel (or 0 bytes)
+  size_t quant;                // quantised weights (codes, scales, dequantised copies), or 0
 };
+
+// Matrices of a quantised model (weight_quant): per layer qkv, o, gate_up,
+// down, then the lm-head; each takes int8 codes, fp32 scales and a
+// dequantised bf16 copy, every piece 256-byte aligned.
+struct QuantSpec {
+  int64_t rows[4];
+  int K[4];
+};
+
+QuantSpec quant_spec(const decoder_config_t *c) {
+  const int d = c->head_dim, H = c->hidden, qd = c->n_heads * d, qkvr = (c->n_heads + 2 * c->n_kv_heads) * d;
+  const int I = c->ffn_inter;
+  return QuantSpec{{qkvr, H, 2 * (int64_t)I, H}, {H, qd, H, I}};
+}
+
+size_t quant_piece(size_t bytes) { return (bytes + 255) / 256 * 256; }
+
+size_t quant_matrix_bytes(int64_t rows, int K) {
+  return quant_piece((size_t)rows * K) + quant_piece((size_t)rows * 4) + quant_piece((size_t)rows * K * 2);
+}
+
+size_t quant_bytes(const decoder_config_t *c) {
+  if (!c->weight_quant) return 0;
+  const QuantSpec qs = quant_spec(c);
+  size_t b = quant_matrix_bytes(c->vocab, c->hidden);
+  for (int i = 0; i < 4; ++i) b += (size_t)c->n_layers * quant_matrix_bytes(qs.rows[i], qs.K[i]);
+  return b;
+}
 
 // Weight matrices that get a packed copy for the chunk projection kernel:
 // only when prefill chunks or decode batches can reach the chunk kernel, and
@@ -88,6 +118,7 @@ bool config_ok(const decoder_config_t *c) {
   if (!(c->rope_base > 0.0) || !(c->rms_eps >= 0.0)) return false;
   if (c->sliding_window < 0 || !(c->attn_softcap >= 0.0) || c->attn_softcap > 1e30) return false;
   if (c->qk_norm != 0 && c->qk_norm != 1) return false;
+  if (c->weight_quant != 0 && (c->weight_quant != 1 || c->n_experts > 0)) return false;
   if (c->n_experts > 0) {
     if (c->n_experts > 256 || c->top_k <= 0 || c->top_k > 8 || c->top_k > c->n_experts) return false;
     if (c->expert_inter <= 0 || c->expert_inter % 8 || c->shared_inter < 0 || c->shared_inter % 8)
@@ -164,6 +195,7 @@ Layout make_layout(const decoder_config_t *c) {
   // packed weight copies (each matrix 256-byte aligned: element counts are
   // multiples of 512)
   L.packed = take(pack_layer_elems(pack_spec(c)) * 2 * c->n_layers);
+  L.quant = take(quant_bytes(c));
   L.total = off;
   return L;
 }
@@ -178,6 +210,12 @@ struct decoder {
     const uint16_t *w[4];  // qkv, o, gate_up (or shared gate_up), down (or shared down); null if not packed
   };
   std::vector<Packed> packed;
+  struct QuantW {
+    const int8_t *q = nullptr;  // int8 codes [rows][K]
+    const float *s = nullptr;   // per-row scales 2^e
+  };
+  std::vector<std::array<QuantW, 4>> qw;  // per layer: qkv, o, gate_up, down (weight_quant)
+  QuantW qhead;                           // the lm-head (weight_quant)
   const uint16_t *embed = nullptr, *lm_head = nullptr;
   const float *final_norm = nullptr;
   hipStream_t stream = nullptr;
@@ -1002,13 +1040,43 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
     D->rids = D->rids_rec = D->groups = D->pair_row = D->pair_of = nullptr;
     D->hexp = D->hsh = nullptr;
   }
+  // quantised weights: codes, scales and dequantised copies, made on the
+  // stream now; every bf16 consumer then reads the dequantised copies
+  if (cfg->weight_quant) {
+    const QuantSpec qs = quant_spec(cfg);
+    char *qp = carve<char>(D, L.quant);
+    auto quant = [&](const uint16_t *src, int64_t rows, int K, const uint16_t **dst, decoder::QuantW &qw) {
+      int8_t *q = reinterpret_cast<int8_t *>(qp);
+      qp += quant_piece((size_t)rows * K);
+      float *sc = reinterpret_cast<float *>(qp);
+      qp += quant_piece((size_t)rows * 4);
+      uint16_t *dq = reinterpret_cast<uint16_t *>(qp);
+      qp += quant_piece((size_t)rows * K * 2);
+      qw.q = q;
+      qw.s = sc;
+      *dst = dq;
+      return launch_quantize_rows(src, rows, K, q, sc, dq, (hipStream_t)stream) == hipSuccess;
+    };
+    D->qw.assign(cfg->n_layers, std::array<decoder::QuantW, 4>{});
+    bool ok = quant(D->lm_head, cfg->vocab, cfg->hidden, &D->lm_head, D->qhead);
+    for (int l = 0; l < cfg->n_layers && ok; ++l) {
+      decoder_layer_weights_t &lw = D->layers[l];
+      const uint16_t **m[4] = {&lw.w_qkv, &lw.w_o, &lw.w_gate_up, &lw.w_down};
+      for (int i = 0; i < 4 && ok; ++i) ok = quant(*m[i], qs.rows[i], qs.K[i], m[i], D->qw[l][i]);
+    }
+    if (!ok) {
+      D->err = "weight quantisation failed";
+      delete D;
+      return DEC_E_HIP;
+    }
+  }
   // packed weight copies for the chunk projections, made on the stream now
   {
     const PackSpec ps = pack_spec(cfg);
     uint16_t *pk = carve<uint16_t>(D, L.packed);
     D->packed.assign(cfg->n_layers, decoder::Packed{});
     for (int l = 0; l < cfg->n_layers; ++l) {
-      const decoder_layer_weights_t &lw = w->layers[l];
+      const decoder_layer_weights_t &lw = D->layers[l];
       const uint16_t *src[4] = {
           (const uint16_t *)lw.w_qkv, (const uint16_t *)lw.w_o,
           (const uint16_t *)(cfg->n_experts > 0 ? lw.w_sh_gate_up : lw.w_gate_up),
@@ -1274,6 +1342,13 @@ int dec_diag_rmsnorm(const float *d_x, const float *d_g, int32_t rows, int32_t H
   return launch_rmsnorm(d_x, H, d_g, rows, H, (float)eps, d_out, H, 0, (hipStream_t)stream) == hipSuccess
              ? DEC_OK
              : DEC_E_HIP;
+}
+
+int dec_diag_quantize_rows(const uint16_t *d_W, int64_t rows, int32_t K, int8_t *d_q, float *d_scale,
+                           uint16_t *d_deq, void *stream) {
+  if (!d_W || !d_q || !d_scale || !d_deq || rows < 1 || K < 1) return DEC_E_INVALID;
+  return launch_quantize_rows(d_W, rows, K, d_q, d_scale, d_deq, (hipStream_t)stream) == hipSuccess ? DEC_OK
+                                                                                                 : DEC_E_HIP;
 }
 
 int decoder_stats_enable(decoder_t *D, int32_t node_mask) {

@@ -179,6 +179,11 @@ struct QkNormArgs {
 };
 hipError_t launch_qk_norm_rope(const QkNormArgs &a, hipStream_t st);
 
+// Per-row int8 quantisation with a power-of-two scale: q [rows][K] int8,
+// scale [rows] fp32 (= 2^e), deq [rows][K] the dequantised bf16 weights.
+hipError_t launch_quantize_rows(const uint16_t *W, int64_t rows, int K, int8_t *q, float *scale, uint16_t *deq,
+                                hipStream_t st);
+
 // V^T cache import: src [Hkv][len][d] -> dst [Hkv][d][S] (positions < len)
 hipError_t launch_kv_load_v(const uint16_t *src, uint16_t *dst, int Hkv, int len, int d, int S,
                             hipStream_t st);

@@ -106,7 +106,46 @@ __global__ __launch_bounds__(64) void qk_norm_rope_kernel(QkNormArgs a) {
   }
 }
 
+// Per-row int8 quantisation: e is the smallest integer with 127 * 2^e >= a
+// (a = the row's largest magnitude; a = m 2^p with m in [0.5, 1) gives
+// e = p - 7 when m <= 127/128, else p - 6), q = rint(w / 2^e) (ties to
+// even; the division by a power of two is exact).  The dequantised q 2^e
+// has at most 7 significant bits and is stored exactly as bf16.  One block
+// per row.
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *W, int K, int8_t *q, float *scale,
+                                                            uint16_t *deq) {
+  __shared__ float red[4];
+  const int64_t r = blockIdx.x;
+  const uint16_t *w = W + r * K;
+  float a = 0.f;
+  for (int k = threadIdx.x; k < K; k += 256) a = fmaxf(a, fabsf(bf16_to_f32(w[k])));
+  a = wave_max(a);
+  if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int e = 0;
+  if (a > 0.f) {
+    int p;
+    const float m = frexpf(a, &p);
+    e = (m <= 0.9921875f) ? p - 7 : p - 6;
+  }
+  const float inv = ldexpf(1.0f, -e), s = ldexpf(1.0f, e);
+  for (int k = threadIdx.x; k < K; k += 256) {
+    const float c = rintf(bf16_to_f32(w[k]) * inv);
+    q[r * K + k] = (int8_t)c;
+    deq[r * K + k] = (uint16_t)f32_to_bf16_bits(c * s);
+  }
+  if (threadIdx.x == 0) scale[r] = s;
+}
+
 }  // namespace
+
+hipError_t launch_quantize_rows(const uint16_t *W, int64_t rows, int K, int8_t *q, float *scale, uint16_t *deq,
+                                hipStream_t st) {
+  if (rows <= 0 || rows > 0x7fffffff || K <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)rows), dim3(256), 0, st, W, K, q, scale, deq);
+  return hipGetLastError();
+}
 
 hipError_t launch_qk_norm_rope(const QkNormArgs &a, hipStream_t st) {
   if (a.d / 2 > 64 || a.rows <= 0) return hipErrorInvalidValue;

@@ -52,6 +52,14 @@ int dec_diag_gemv(const float *d_a, int32_t K, const uint16_t *d_W, int32_t N, f
 int dec_diag_rmsnorm(const float *d_x, const float *d_g, int32_t rows, int32_t H, double eps,
                      uint16_t *d_out, void *stream);
 
+/* Per-row int8 weight quantisation as decoder_init does it with
+ * weight_quant (a power-of-two scale 2^e per row, e the smallest integer
+ * with 127 * 2^e >= the row's largest magnitude, codes rounded to nearest,
+ * ties to even).  W bf16 [rows][K]; q int8 [rows][K]; scale fp32 [rows];
+ * deq bf16 [rows][K] the dequantised weights. */
+int dec_diag_quantize_rows(const uint16_t *d_W, int64_t rows, int32_t K, int8_t *d_q, float *d_scale,
+                           uint16_t *d_deq, void *stream);
+
 /* MoE routing of rows router-logit vectors (pipeline.rs MoeFfn: softmax
  * over all experts, top-k, optional renormalisation; lower index first on
  * ties).  logits fp32 [rows][E]; ids int32 [rows][k] in router order,

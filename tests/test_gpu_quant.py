@@ -1,0 +1,76 @@
+"""Quantised weight streaming against the oracle.
+
+decoder_init turns every layer matrix and the lm-head into int8 codes with
+one power-of-two scale per row; the model then computes with the
+dequantised weights on every path.  The codes are integers, so the kernel's
+must equal the oracle's bit for bit (and so must the dequantised bf16
+weights, which are exact).  End to end, the quantised model's prefill and
+teacher-forced decode meet the acceptance rule against the oracle run on
+the same quantised weights.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth.weights import host_weights, prompt
+from synth.workloads import C8B, TINY
+from tests.gpu_util import assert_parity, compare_logits, decode, log, make_decoder, run_prefill
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.mark.parametrize("rows,K,sigma", [(37, 4096, 0.02), (8, 1000, 3.0), (5, 64, 1e-3)])
+def test_quantize_kernel_bit_exact(rows, K, sigma):
+    from decoder_only_transformer_step_amd.binding import diag_quantize_rows
+    W = synth.normal_bf16(rows * K, 900 + rows, sigma).reshape(rows, K)
+    W[0, :] = 0                                           # an all-zero row: scale 1, codes 0
+    W[1, 3] = 0x8000                                      # a negative zero
+    want_deq, want_e = oracle.quantize_rows(W, rows, K)
+    dW = torch.from_numpy(W.view(np.int16)).cuda()
+    q = torch.empty((rows, K), dtype=torch.int8, device="cuda")
+    sc = torch.empty(rows, dtype=torch.float32, device="cuda")
+    deq = torch.empty((rows, K), dtype=torch.int16, device="cuda")
+    diag_quantize_rows(dW, rows, K, q, sc, deq, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got_deq = deq.cpu().numpy().view(np.uint16)
+    got_q = q.cpu().numpy().astype(np.int64)
+    got_s = sc.cpu().numpy()
+    assert np.array_equal(got_s, np.ldexp(np.float32(1.0), want_e).astype(np.float32))
+    want_q = np.rint(synth.bf16_to_f32(want_deq).astype(np.float64) / np.ldexp(1.0, want_e)[:, None])
+    assert np.array_equal(got_q, want_q.astype(np.int64))
+    # dequantised weights: equal values (a zero code may carry either sign)
+    assert np.array_equal(synth.bf16_to_f32(got_deq), synth.bf16_to_f32(want_deq))
+
+
+SHAPES = {
+    "tiny": (TINY.with_(name="gqa-tiny-q8", weight_quant=1), 16, 16, 8),
+    "8b2": (C8B.with_(name="gqa-8b-layers-2-q8", n_layers=2, vocab=1024, max_seq=512, weight_quant=1),
+            200, 128, 6),
+}
+
+
+@pytest.mark.parametrize("which", ["tiny", "8b2"])
+def test_quantized_model_prefill_and_decode(which):
+    shape, P, chunk, steps = SHAPES[which]
+    W = host_weights(shape)
+    ids = prompt(shape, P)
+    m = oracle.Model(shape, W)
+    want = m.prefill(ids, chunk)["logits"]
+    plain = oracle.Model(shape.with_(weight_quant=0), W).prefill(ids, chunk)["logits"]
+    assert np.abs(plain - want).max() > 1e-3            # the quantisation moves the model
+    dec, _ = make_decoder(shape, W)
+    got = run_prefill(dec, ids, chunk)
+    st = compare_logits(got, want, f"{which} q8 prefill")
+    log(which, "q8 prefill", st)
+    assert_parity(st, f"{which} q8 prefill")
+    for i in range(steps):
+        t = oracle.argmax(want)
+        want = m.forward([t], P + i)["logits"]
+        lg, _ = decode(dec, [0], [t])
+        st = compare_logits(lg[0], want, f"{which} q8 decode {i}")
+        log(which, "q8 decode", i, st)
+        assert_parity(st, f"{which} q8 decode {i}")
+    dec.close()
