@@ -284,6 +284,8 @@ def main():
     ap.add_argument("--attn-softcap", type=float, default=0.0, help="attention variant: logit soft-cap")
     ap.add_argument("--attn-sinks", action="store_true", help="attention variant: per-head sink logits")
     ap.add_argument("--qk-norm", action="store_true", help="attention variant: per-head RMSNorm of q and k")
+    ap.add_argument("--weight-quant", action="store_true",
+                    help="int8 weights with a power-of-two scale per row (decode streams the codes)")
     ap.add_argument("--no-verify", action="store_true",
                     help="skip the multi-position verify measurement (batch-1 workloads)")
     ap.add_argument("--verify-reps", type=int, default=20)
@@ -343,6 +345,8 @@ def main():
         variant["attn_sinks"] = True
     if args.qk_norm:
         variant["qk_norm"] = True
+    if args.weight_quant:
+        variant["weight_quant"] = 1
     if variant:
         shape = shape.with_(name=shape.name + "-" + "-".join(f"{k}{v}" for k, v in variant.items()), **variant)
     # the first decode step (reported on its own), the warmup and the timed
@@ -367,6 +371,8 @@ def main():
     result = {"metric": METRIC, "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
               "data": "synthetic (seeded SplitMix64/Box-Muller bf16 weights and uniform token ids)"}
+    if variant.get("weight_quant"):
+        result["dtype"] = "int8 weights (power-of-two row scales), fp32 accumulate"
     batch = work.batch
     seqs = list(range(batch))
 

@@ -118,7 +118,9 @@ bool config_ok(const decoder_config_t *c) {
   if (!(c->rope_base > 0.0) || !(c->rms_eps >= 0.0)) return false;
   if (c->sliding_window < 0 || !(c->attn_softcap >= 0.0) || c->attn_softcap > 1e30) return false;
   if (c->qk_norm != 0 && c->qk_norm != 1) return false;
-  if (c->weight_quant != 0 && (c->weight_quant != 1 || c->n_experts > 0)) return false;
+  // quantised GEMVs load 16 codes per lane: every row length a multiple of 16
+  if (c->weight_quant != 0 && (c->weight_quant != 1 || c->n_experts > 0 || c->hidden % 16 || c->ffn_inter % 16))
+    return false;
   if (c->n_experts > 0) {
     if (c->n_experts > 256 || c->top_k <= 0 || c->top_k > 8 || c->top_k > c->n_experts) return false;
     if (c->expert_inter <= 0 || c->expert_inter % 8 || c->shared_inter < 0 || c->shared_inter % 8)
@@ -523,12 +525,23 @@ int gemv(decoder *D, int node, int epi, const GemvArgs &g, int *blocks = nullptr
   const double slots = g.slot_expert ? g.n_slots : 1;
   const double out_words = epi == EPI_ADD ? 2 : epi == EPI_MOE_ADD ? 2 + g.moe_k : 1;
   const double part2 = g.W2 ? g.n_items2 * (nr * (double)g.K * 2 + 4.0) : 0.0;
+  const double wrow = g.Wq ? (double)g.K + 4.0 : (double)g.K * 2;  // weight bytes per row (+ its scale)
   NodeTimer timer(D, node,
-                  slots * (nr * g.n_items * (double)g.K * 2 + g.K * 4.0 + g.n_items * 4.0 * out_words) + part2,
+                  slots * (nr * g.n_items * wrow + g.K * 4.0 + g.n_items * 4.0 * out_words) + part2,
                   slots * 2.0 * nr * g.n_items * (double)g.K + (g.W2 ? 2.0 * nr * g.n_items2 * (double)g.K : 0.0));
   hipError_t e = launch_gemv(g, epi, D->stream, blocks);
   if (e != hipSuccess) return hip_fail(D, e, "gemv");
   return DEC_OK;
+}
+
+// With quantised weights, GEMVs stream the int8 codes (and row scales) of
+// matrix i of layer l (i: 0 qkv, 1 o, 2 gate_up, 3 down; l < 0: the lm-head).
+GemvArgs quant(const decoder *D, GemvArgs g, int l, int i) {
+  if (!D->c.weight_quant) return g;
+  const decoder::QuantW &w = l < 0 ? D->qhead : D->qw[l][i];
+  g.Wq = w.q;
+  g.wscale = w.s;
+  return g;
 }
 
 GemvArgs gemv_args(const uint16_t *W, const float *a, int K, int n_items, float *C) {
@@ -591,7 +604,7 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
     qs.gamma = W.attn_norm;
     qs.eps = eps;
     qs.bias = c.qkv_bias ? W.b_qkv : nullptr;
-    if ((rc = gemv(D, DEC_NODE_QKV, EPI_STORE, qs))) return rc;
+    if ((rc = gemv(D, DEC_NODE_QKV, EPI_STORE, quant(D, qs, l, 0)))) return rc;
     if ((rc = qk_norm_pass(D, l, 1))) return rc;
   }
   GemvArgs q = gemv_args(W.w_qkv, D->x, H, (c.n_heads + 2 * c.n_kv_heads) * d / 2, nullptr);
@@ -616,17 +629,17 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
   q.qkv.Hq = c.n_heads;
   q.qkv.Hkv = c.n_kv_heads;
   q.qkv.d = d;
-  if (!c.qk_norm && (rc = gemv(D, DEC_NODE_QKV, EPI_QKV, q))) return rc;
+  if (!c.qk_norm && (rc = gemv(D, DEC_NODE_QKV, EPI_QKV, quant(D, q, l, 0)))) return rc;
   if ((rc = attention(D, l, 1, 1, max_pos, hpos, D->f32_attn))) return rc;
-  if ((rc = gemv(D, DEC_NODE_O, EPI_ADD, gemv_args(W.w_o, D->f32_attn, qd, H, D->x)))) return rc;
+  if ((rc = gemv(D, DEC_NODE_O, EPI_ADD, quant(D, gemv_args(W.w_o, D->f32_attn, qd, H, D->x), l, 1)))) return rc;
 
   if (c.n_experts == 0) {
     const int I = c.ffn_inter;
     GemvArgs gu = gemv_args(W.w_gate_up, D->x, H, I, D->f32_h);
     gu.gamma = W.ffn_norm;
     gu.eps = eps;
-    if ((rc = gemv(D, DEC_NODE_GATE_UP, EPI_SWIGLU, gu))) return rc;
-    return gemv(D, DEC_NODE_DOWN, EPI_ADD, gemv_args(W.w_down, D->f32_h, I, H, D->x));
+    if ((rc = gemv(D, DEC_NODE_GATE_UP, EPI_SWIGLU, quant(D, gu, l, 2)))) return rc;
+    return gemv(D, DEC_NODE_DOWN, EPI_ADD, quant(D, gemv_args(W.w_down, D->f32_h, I, H, D->x), l, 3));
   }
   // MoE FFN for one row: the FFN RMSNorm runs inside the router GEMV, the
   // route kernel and the expert GEMVs (each from x); the shared expert's
@@ -899,7 +912,7 @@ int run_step(decoder *D, int rows, int rows_per_group, int max_pos, const int32_
     g.part_val = D->am_val;
     g.part_idx = D->am_idx;
     if ((size_t)gemv_blocks(c.vocab) > D->am_cap) return fail(D, DEC_E_HIP, "lm-head grid exceeds the argmax partial buffer");
-    if ((rc = gemv(D, DEC_NODE_HEAD, EPI_LOGITS, g, &nparts))) return rc;
+    if ((rc = gemv(D, DEC_NODE_HEAD, EPI_LOGITS, quant(D, g, -1, 0), &nparts))) return rc;
   } else {
     GemmArgs g = dense_args(nullptr, H, D->lm_head, nout, c.vocab, H);
     if ((rc = norm_into(D, g, D->x + (size_t)first * H, D->final_norm, nout))) return rc;
@@ -1020,7 +1033,7 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
     const int qd = cfg->n_heads * cfg->head_dim;
     const int kmax = std::max(std::max(cfg->hidden, qd), std::max(std::max(cfg->ffn_inter, cfg->shared_inter),
                                                                       cfg->expert_inter));
-    D->single_row_ok = gemv_lds(kmax) <= GEMV_MAX_LDS;
+    D->single_row_ok = gemv_lds(kmax, cfg->weight_quant != 0) <= GEMV_MAX_LDS;
   }
   if (cfg->n_experts > 0) {
     D->rlogits = carve<float>(D, L.rlogits);

@@ -24,6 +24,10 @@
 //    queue up behind the running ones.
 //  * Grouped mode (MoE experts): blockIdx.y = routing slot; the weight base
 //    moves to the chosen expert.
+//  * Quantised weights (Q = 1): int8 codes with one scale per row.  The same
+//    1 KB loads then carry 16 weights per lane (k = 16 l + 1024 s), the
+//    activation slots hold 16 elements per lane and step, and the row's
+//    scale multiplies the finished dot product: half the bytes per weight.
 #include <algorithm>
 
 #include "common.h"
@@ -61,17 +65,25 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)
 // a select on its value, makes it wait for everything in flight).
 __device__ u32x4 gv_zero[1];
 
-// Loads of UNR 1 KB steps for every row the wave owns.
-template <int R, int UNR>
-__device__ __forceinline__ void load_batch(u32x4 (&v)[UNR][R], const uint16_t *const (&wp)[R], int s0, int K,
+// Elements per lane and per 1 KB step: 8 bf16 or 16 int8 weights.
+template <int Q>
+constexpr int gv_epl() {
+  return Q ? 16 : 8;
+}
+
+// Loads of UNR 1 KB steps for every row the wave owns (wp: byte pointers
+// with the lane's offset included).
+template <int R, int UNR, int Q>
+__device__ __forceinline__ void load_batch(u32x4 (&v)[UNR][R], const char *const (&wp)[R], int s0, int K,
                                            int lane) {
+  constexpr int EPL = gv_epl<Q>();
 #pragma unroll
   for (int u = 0; u < UNR; ++u) {
     const int st = s0 + u;
-    const bool ok = st * 512 + lane * 8 < K;  // false for every lane past the last step
+    const bool ok = st * 64 * EPL + lane * EPL < K;  // false for every lane past the last step
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      v[u][r] = load16(ok ? static_cast<const void *>(wp[r] + st * 512) : static_cast<const void *>(gv_zero));
+      v[u][r] = load16(ok ? static_cast<const void *>(wp[r] + st * 1024) : static_cast<const void *>(gv_zero));
   }
 }
 
@@ -82,15 +94,42 @@ __device__ __forceinline__ void load_batch(u32x4 (&v)[UNR][R], const uint16_t *c
 __device__ __forceinline__ int xs_slot(int k) {  // k: element index, a multiple of 4
   return ((k >> 9) * 2 + ((k >> 2) & 1)) * 64 + ((k & 511) >> 3);
 }
+// int8 weights: lane l's 16 elements of step s in four slots (4 s + h) 64 + l.
+__device__ __forceinline__ int xs_slot_q(int k) {
+  return ((k >> 10) * 4 + ((k >> 2) & 3)) * 64 + ((k & 1023) >> 4);
+}
+template <int Q>
+__device__ __forceinline__ int xs_slot_t(int k) {
+  return Q ? xs_slot_q(k) : xs_slot(k);
+}
+
+__device__ __forceinline__ float i8f(uint32_t w, int j) { return (float)(int8_t)(w >> (8 * j)); }
 
 // acc[r] += dot(weights of batch, activation) over UNR steps.
-template <int R, int UNR>
+template <int R, int UNR, int Q>
 __device__ __forceinline__ void fma_batch(float (&acc)[R], const u32x4 (&v)[UNR][R], const f32x4 *xs, int s0,
                                           int steps, int lane) {
 #pragma unroll
   for (int u = 0; u < UNR; ++u) {
     const int st = s0 + u;
-    if (st < steps) {
+    if (Q && st < steps) {
+      f32x4 x[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) x[h] = xs[(st * 4 + h) * 64 + lane];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const u32x4 w = v[u][r];
+        float a = acc[r];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          a = fmaf(i8f(w[h], 0), x[h][0], a);
+          a = fmaf(i8f(w[h], 1), x[h][1], a);
+          a = fmaf(i8f(w[h], 2), x[h][2], a);
+          a = fmaf(i8f(w[h], 3), x[h][3], a);
+        }
+        acc[r] = a;
+      }
+    } else if (!Q && st < steps) {
       const f32x4 xa = xs[(st * 2) * 64 + lane];
       const f32x4 xb = xs[(st * 2 + 1) * 64 + lane];
 #pragma unroll
@@ -153,15 +192,16 @@ __device__ __forceinline__ ItemPre item_prefetch(const GemvArgs &g, int out_row,
 
 // Rows of item `it` (a valid item), their weight pointers (lane offset
 // included) and the item's epilogue inputs.
-template <int EPI, int NR>
-__device__ __forceinline__ void item_ptrs(const GemvArgs &g, const uint16_t *W, int it, int lane, int out_row,
-                                          int (&rows)[NR], const uint16_t *(&wp)[NR], ItemPre &pre) {
+template <int EPI, int NR, int Q>
+__device__ __forceinline__ void item_ptrs(const GemvArgs &g, const char *W, int it, int lane, int out_row,
+                                          int (&rows)[NR], const char *(&wp)[NR], ItemPre &pre) {
+  constexpr int EB = Q ? 1 : 2;  // bytes per weight
   int r0, r1;
   item_rows<EPI>(g, it, r0, r1);
   rows[0] = r0;
   rows[NR - 1] = r1;
 #pragma unroll
-  for (int r = 0; r < NR; ++r) wp[r] = W + (int64_t)rows[r] * g.K + lane * 8;
+  for (int r = 0; r < NR; ++r) wp[r] = W + ((int64_t)rows[r] * g.K) * EB + lane * 16;
   pre = item_prefetch<EPI>(g, out_row, r0, r1);
 }
 
@@ -228,9 +268,10 @@ __device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, in
 // the activation is loaded ahead of the weights when it fits in registers,
 // so the prologue waits only for it.  NCH: the row's chunk count when it is
 // 1 or 2 (no refills), else 0 (the refill loop).
-template <int EPI, int NCH, int WV>
+template <int EPI, int NCH, int WV, int Q>
 __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
   constexpr int NR = gv_rows<EPI>(), CH = 8 / NR, NT = WV * WAVE, PRN = 32 / WV, PRH = PRN / 2;
+  constexpr int SE = 64 * gv_epl<Q>();  // elements per 1 KB step
   extern __shared__ f32x4 xs[];  // activation, fp32 in the layout of xs_slot
   __shared__ float sred[WV];
   __shared__ float bv_s[WV];
@@ -255,24 +296,28 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
       bx -= slot * ga.blocks1;
     }
   }
-  const uint16_t *W = g.W;
+  const char *W = Q ? reinterpret_cast<const char *>(g.Wq) : reinterpret_cast<const char *>(g.W);
   const float *xin = g.a_f32;
   int out_row = 0;
   if (g.slot_expert) {
-    W += (int64_t)g.slot_expert[slot] * g.w_group_stride;
+    W += (int64_t)g.slot_expert[slot] * g.w_group_stride * (Q ? 1 : 2);
     if (xin) xin += (int64_t)slot * g.a_slot_stride;
     out_row = slot;
   }
   const int K = g.K;
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
-  const int steps = (K + 511) / 512, nch = NCH ? NCH : (steps + CH - 1) / CH;
+  const int steps = (K + SE - 1) / SE, nch = NCH ? NCH : (steps + CH - 1) / CH;
   const int it = bx * WV + wave;
   const bool valid = it < g.n_items;
   int rows[NR];
-  const uint16_t *wp[NR];
+  const char *wp[NR];
   ItemPre pre;
-  item_ptrs<EPI, NR>(g, W, valid ? it : g.n_items - 1, lane, out_row, rows, wp, pre);
+  item_ptrs<EPI, NR, Q>(g, W, valid ? it : g.n_items - 1, lane, out_row, rows, wp, pre);
+  // the rows' scales, loaded with the first weights (quantised weights only)
+  float wsc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) wsc[r] = Q ? g.wscale[rows[r]] : 1.0f;
 
   // activation into registers first when it fits.  Mode 1: x and gamma
   // (RMSNorm); 2: fp32 x; 3: bf16 x; 0: read after the weights are issued.
@@ -294,11 +339,11 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
 
   // (loads past the row read the zero page: no load sits under a branch)
   u32x4 buf0[CH][NR], buf1[CH][NR];
-  load_batch<NR, CH>(buf0, wp, 0, K, lane);
-  if (NCH != 1) load_batch<NR, CH>(buf1, wp, CH, K, lane);
+  load_batch<NR, CH, Q>(buf0, wp, 0, K, lane);
+  if (NCH != 1) load_batch<NR, CH, Q>(buf1, wp, CH, K, lane);
 
   // activation -> LDS (fp32, with the RMSNorm when gamma is set)
-  auto put4 = [&](int k, f32x4 v) { xs[xs_slot(k)] = v; };
+  auto put4 = [&](int k, f32x4 v) { xs[xs_slot_t<Q>(k)] = v; };
   auto as_f4 = [](u32x4 v) { return __builtin_bit_cast(f32x4, v); };
   if (mode == 1) {
     float ss = 0.f;
@@ -353,7 +398,7 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
     }
   }
   // zero padding up to whole steps
-  for (int k = K + threadIdx.x * 4; k < steps * 512; k += NT * 4) put4(k, f32x4{0.f, 0.f, 0.f, 0.f});
+  for (int k = K + threadIdx.x * 4; k < steps * SE; k += NT * 4) put4(k, f32x4{0.f, 0.f, 0.f, 0.f});
   __syncthreads();
 
   float acc[NR];
@@ -362,16 +407,16 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
   int c = 0;
   if (NCH == 0) {
     for (; c + 2 < nch; c += 2) {
-      fma_batch<NR, CH>(acc, buf0, xs, c * CH, steps, lane);
-      load_batch<NR, CH>(buf0, wp, (c + 2) * CH, K, lane);
-      fma_batch<NR, CH>(acc, buf1, xs, (c + 1) * CH, steps, lane);
-      load_batch<NR, CH>(buf1, wp, (c + 3) * CH, K, lane);
+      fma_batch<NR, CH, Q>(acc, buf0, xs, c * CH, steps, lane);
+      load_batch<NR, CH, Q>(buf0, wp, (c + 2) * CH, K, lane);
+      fma_batch<NR, CH, Q>(acc, buf1, xs, (c + 1) * CH, steps, lane);
+      load_batch<NR, CH, Q>(buf1, wp, (c + 3) * CH, K, lane);
     }
   }
-  fma_batch<NR, CH>(acc, buf0, xs, c * CH, steps, lane);
-  if (NCH != 1) fma_batch<NR, CH>(acc, buf1, xs, (c + 1) * CH, steps, lane);
+  fma_batch<NR, CH, Q>(acc, buf0, xs, c * CH, steps, lane);
+  if (NCH != 1) fma_batch<NR, CH, Q>(acc, buf1, xs, (c + 1) * CH, steps, lane);
 #pragma unroll
-  for (int r = 0; r < NR; ++r) acc[r] = wave_sum(acc[r]);
+  for (int r = 0; r < NR; ++r) acc[r] = wave_sum(acc[r]) * wsc[r];
   if (valid && lane == 0) item_epilogue<EPI>(g, out_row, rows[0], rows[NR - 1], acc[0], acc[NR - 1], pre);
 
   if (EPI == EPI_LOGITS) {
@@ -395,21 +440,27 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
   }
 }
 
-template <int EPI, int WV>
+template <int EPI, int WV, int Q>
 void launch_w(const GemvArgs &g, int nch, size_t lds, hipStream_t st) {
   dim3 grid((g.n_items + WV - 1) / WV, g.slot_expert ? g.n_slots : 1), block(WV * WAVE);
   if (g.W2) grid = dim3(g.blocks1 * g.n_slots + (g.n_items2 + WV - 1) / WV, 1);
-  if (nch == 1) hipLaunchKernelGGL((gemv_kernel<EPI, 1, WV>), grid, block, lds, st, g);
-  else if (nch == 2) hipLaunchKernelGGL((gemv_kernel<EPI, 2, WV>), grid, block, lds, st, g);
-  else hipLaunchKernelGGL((gemv_kernel<EPI, 0, WV>), grid, block, lds, st, g);
+  if (nch == 1) hipLaunchKernelGGL((gemv_kernel<EPI, 1, WV, Q>), grid, block, lds, st, g);
+  else if (nch == 2) hipLaunchKernelGGL((gemv_kernel<EPI, 2, WV, Q>), grid, block, lds, st, g);
+  else hipLaunchKernelGGL((gemv_kernel<EPI, 0, WV, Q>), grid, block, lds, st, g);
+}
+
+template <int EPI, int Q>
+void launch_eq(const GemvArgs &g, int wv, size_t lds, hipStream_t st) {
+  constexpr int CH = 8 / gv_rows<EPI>(), SE = 64 * gv_epl<Q>();
+  const int nch = ((g.K + SE - 1) / SE + CH - 1) / CH;
+  if (wv == 4) launch_w<EPI, 4, Q>(g, nch, lds, st);
+  else launch_w<EPI, 8, Q>(g, nch, lds, st);
 }
 
 template <int EPI>
 void launch_e(const GemvArgs &g, int wv, size_t lds, hipStream_t st) {
-  constexpr int CH = 8 / gv_rows<EPI>();
-  const int nch = ((g.K + 511) / 512 + CH - 1) / CH;
-  if (wv == 4) launch_w<EPI, 4>(g, nch, lds, st);
-  else launch_w<EPI, 8>(g, nch, lds, st);
+  if (g.Wq) launch_eq<EPI, 1>(g, wv, lds, st);
+  else launch_eq<EPI, 0>(g, wv, lds, st);
 }
 
 int device_cus() {
@@ -447,7 +498,9 @@ hipError_t launch_gemv(const GemvArgs &g0, int epi, hipStream_t st, int *blocks)
     g.blocks1 = (g.n_items + wv - 1) / wv;
   }
   if (blocks) *blocks = (g.n_items + wv - 1) / wv;
-  const size_t lds = gemv_lds(g.K);
+  // quantised weights: dense launches only (no grouped slots, no second part)
+  if (g.Wq && (!g.wscale || g.K % 16 || g.slot_expert || g.W2 || epi == EPI_MOE_ADD)) return hipErrorInvalidValue;
+  const size_t lds = gemv_lds(g.K, g.Wq != nullptr);
   switch (epi) {
     case EPI_STORE: launch_e<EPI_STORE>(g, wv, lds, st); break;
     case EPI_ADD: launch_e<EPI_ADD>(g, wv, lds, st); break;

@@ -37,6 +37,8 @@ hipError_t launch_gemm_chunk(const GemmArgs &g, int epi, hipStream_t st);
 // ------------------------------------------------ single-token projection --
 struct GemvArgs {
   const uint16_t *W;          // bf16 [rows][K]
+  const int8_t *Wq;           // or int8 codes [rows][K] with per-row scales wscale [rows]
+  const float *wscale;
   int64_t w_group_stride;     // grouped mode: elements between experts
   const int32_t *slot_expert; // grouped mode: expert of each routing slot (blockIdx.y), else null
   int32_t n_slots;
@@ -64,8 +66,12 @@ struct GemvArgs {
   int32_t blocks1;
 };
 constexpr size_t GEMV_MAX_LDS = 60 * 1024;
-// LDS of one GEMV block: the fp32 activation padded to whole 512-element steps
-inline size_t gemv_lds(int K) { return (size_t)(K + 511) / 512 * 512 * 4; }
+// LDS of one GEMV block: the fp32 activation padded to whole load steps
+// (512 elements of bf16 weights, 1024 of int8 weights)
+inline size_t gemv_lds(int K, bool q8 = false) {
+  const size_t step = q8 ? 1024 : 512;
+  return (size_t)(K + step - 1) / step * step * 4;
+}
 // blocks of a GEMV launch over n_items items (one argmax partial each for EPI_LOGITS)
 int gemv_blocks(int n_items);
 // `blocks` (optional) receives the grid size, i.e. the number of argmax
