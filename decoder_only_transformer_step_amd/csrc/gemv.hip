@@ -70,6 +70,13 @@ template <int Q>
 constexpr int gv_epl() {
   return Q ? 16 : 8;
 }
+// 1 KB steps per register buffer (all rows of the item together): 8 KB for
+// bf16; 4 KB for int8, so that a row of a K = 14336 projection still takes
+// more than two chunks and its loads overlap the (heavier) int8 arithmetic.
+template <int Q>
+constexpr int gv_ch() {
+  return Q ? 4 : 8;
+}
 
 // Loads of UNR 1 KB steps for every row the wave owns (wp: byte pointers
 // with the lane's offset included).
@@ -270,7 +277,7 @@ __device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, in
 // 1 or 2 (no refills), else 0 (the refill loop).
 template <int EPI, int NCH, int WV, int Q>
 __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
-  constexpr int NR = gv_rows<EPI>(), CH = 8 / NR, NT = WV * WAVE, PRN = 32 / WV, PRH = PRN / 2;
+  constexpr int NR = gv_rows<EPI>(), CH = gv_ch<Q>() / NR, NT = WV * WAVE, PRN = 32 / WV, PRH = PRN / 2;
   constexpr int SE = 64 * gv_epl<Q>();  // elements per 1 KB step
   extern __shared__ f32x4 xs[];  // activation, fp32 in the layout of xs_slot
   __shared__ float sred[WV];
@@ -451,7 +458,7 @@ void launch_w(const GemvArgs &g, int nch, size_t lds, hipStream_t st) {
 
 template <int EPI, int Q>
 void launch_eq(const GemvArgs &g, int wv, size_t lds, hipStream_t st) {
-  constexpr int CH = 8 / gv_rows<EPI>(), SE = 64 * gv_epl<Q>();
+  constexpr int CH = gv_ch<Q>() / gv_rows<EPI>(), SE = 64 * gv_epl<Q>();
   const int nch = ((g.K + SE - 1) / SE + CH - 1) / CH;
   if (wv == 4) launch_w<EPI, 4, Q>(g, nch, lds, st);
   else launch_w<EPI, 8, Q>(g, nch, lds, st);
