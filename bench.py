@@ -484,7 +484,7 @@ def main():
     per_launch_bytes = d["bytes"] / d["launches"]
     per_launch_s = d["ms"] / d["launches"] * 1e-3
     achieved = per_launch_bytes / per_launch_s / 1e9
-    traffic = counter_traffic(f"counters_{dom}_decode_{args.workload}.md")
+    traffic = counter_traffic(f"counters_{dom}_decode_{args.workload}{'_q8' if variant.get('weight_quant') else ''}.md")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": f"{dom} ({'gemv_kernel, batch-1 projection' if dom != 'attn' else 'attn_kernel'}, decode)", "bytes_per_launch": per_launch_bytes,
