@@ -286,6 +286,8 @@ def main():
     ap.add_argument("--qk-norm", action="store_true", help="attention variant: per-head RMSNorm of q and k")
     ap.add_argument("--weight-quant", action="store_true",
                     help="int8 weights with a power-of-two scale per row (decode streams the codes)")
+    ap.add_argument("--kv-page", type=int, default=0,
+                    help="paged KV cache: pages of this many positions (the pool holds every sequence's max_seq)")
     ap.add_argument("--no-verify", action="store_true",
                     help="skip the multi-position verify measurement (batch-1 workloads)")
     ap.add_argument("--verify-reps", type=int, default=20)
@@ -347,6 +349,9 @@ def main():
         variant["qk_norm"] = True
     if args.weight_quant:
         variant["weight_quant"] = 1
+    if args.kv_page:
+        variant["kv_page_size"] = args.kv_page
+        variant["kv_pages"] = work.batch * -(-shape.max_seq // args.kv_page)
     if variant:
         shape = shape.with_(name=shape.name + "-" + "-".join(f"{k}{v}" for k, v in variant.items()), **variant)
     # the first decode step (reported on its own), the warmup and the timed

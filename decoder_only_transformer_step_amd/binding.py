@@ -24,7 +24,8 @@ class DecoderConfig(ctypes.Structure):
         "top_k", "expert_inter", "shared_inter", "shared_gate", "norm_topk_prob", "vocab",
         "qkv_bias")] + [("rope_base", ctypes.c_double), ("rms_eps", ctypes.c_double)] + [
         (n, _I32) for n in ("max_seq", "max_chunk", "max_batch", "sliding_window")] + [
-        ("attn_softcap", ctypes.c_double), ("qk_norm", _I32), ("weight_quant", _I32)]
+        ("attn_softcap", ctypes.c_double), ("qk_norm", _I32), ("weight_quant", _I32),
+        ("kv_page_size", _I32), ("kv_pages", _I32)]
 
 
 LAYER_FIELDS = ("attn_norm", "ffn_norm", "w_qkv", "b_qkv", "w_o", "w_gate_up", "w_down",
@@ -133,7 +134,8 @@ def make_config(shape):
         rope_base=float(s.rope_base), rms_eps=float(s.rms_eps), max_seq=s.max_seq,
         max_chunk=s.max_chunk, max_batch=s.max_batch, sliding_window=getattr(s, "sliding_window", 0),
         attn_softcap=float(getattr(s, "attn_softcap", 0.0)), qk_norm=int(getattr(s, "qk_norm", False)),
-        weight_quant=int(getattr(s, "weight_quant", 0)))
+        weight_quant=int(getattr(s, "weight_quant", 0)), kv_page_size=int(getattr(s, "kv_page_size", 0)),
+        kv_pages=int(getattr(s, "kv_pages", 0)))
 
 
 # ---------------------------------------------------- same-named functions --

@@ -104,7 +104,7 @@ __device__ __forceinline__ int group_key_start(const AttnArgs &a, int rg) {
   return 0;
 }
 
-template <int D, int PM>
+template <int D, int PM, bool PG>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   constexpr int NDT = D / 16;
   __shared__ float lo[4][16][D];
@@ -133,8 +133,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   u32x4 ka[D / 32], kh[D / 32];
   u32x4 va[NDT];
   auto load_tile = [&](int t) {
+    // a paged cache: the tile's page (a 32-key tile never straddles one)
+    const uint16_t *kt = kb, *vt = vb;
+    int tt = t;
+    if (PG) {
+      const int64_t pb = (int64_t)a.pt[(int64_t)seq * a.mp + t / a.S] * a.seq_stride + a.layer_off;
+      kt = a.kcache + pb + (int64_t)g * a.S * D;
+      vt = a.vcache + pb + (int64_t)g * D * a.S;
+      tt = t % a.S;
+    }
     const int kr = 8 * (c >> 2) + (c & 3);
-    const uint16_t *k_lo = kb + (int64_t)(t + kr) * D + quad * 8;
+    const uint16_t *k_lo = kt + (int64_t)(tt + kr) * D + quad * 8;
     const uint16_t *k_hi = k_lo + 4 * D;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
@@ -142,7 +151,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       kh[ks] = load16(k_hi + ks * 32);
     }
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) va[dt] = load16(vb + (int64_t)(dt * 16 + c) * a.S + t + quad * 8);
+    for (int dt = 0; dt < NDT; ++dt) va[dt] = load16(vt + (int64_t)(dt * 16 + c) * a.S + tt + quad * 8);
   };
   // the first tile goes out before q (a wave without a tile of its own
   // reloads the split's first tile, which stays inside the cache rows)
@@ -311,7 +320,8 @@ namespace {
 
 template <int D, int PM>
 hipError_t launch_pm(const AttnArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((attn_kernel<D, PM>), dim3(a.n_groups * a.n_splits), dim3(256), 0, st, a);
+  if (a.pt) hipLaunchKernelGGL((attn_kernel<D, PM, true>), dim3(a.n_groups * a.n_splits), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attn_kernel<D, PM, false>), dim3(a.n_groups * a.n_splits), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
   const int ncols = std::min(16, a.rows_per_group * a.G);  // valid columns of a group

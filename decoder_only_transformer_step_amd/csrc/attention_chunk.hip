@@ -48,7 +48,7 @@ __device__ __forceinline__ void ac_store_out(const AttnArgs &a, int64_t i, float
   a.out[a.out_lo + i] = (uint16_t)lo;
 }
 
-template <int D>
+template <int D, bool PG>
 __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a, int rpb) {
   using L = AcLay<D>;
   constexpr int NJ = D / 16, NDT = D / 32;
@@ -76,15 +76,24 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a, int rpb)
   // tile loads: thread -> 16-byte pieces of the K rows and the V^T columns
   u32x4 kr[L::KP], vr[L::VP];
   auto load_tile = [&](int t0) {
+    // a paged cache: the tile's page (a 32-key tile never straddles one)
+    const uint16_t *kt = kb, *vt = vb;
+    int tt = t0;
+    if (PG) {
+      const int64_t pb = (int64_t)a.pt[(int64_t)a.seq0 * a.mp + t0 / a.S] * a.seq_stride + a.layer_off;
+      kt = a.kcache + pb + (int64_t)g * a.S * D;
+      vt = a.vcache + pb + (int64_t)g * D * a.S;
+      tt = t0 % a.S;
+    }
 #pragma unroll
     for (int i = 0; i < L::KP; ++i) {
       const int p = threadIdx.x + 256 * i, key = p / (D / 8), ch = p % (D / 8);
-      kr[i] = load16(kb + (int64_t)(t0 + key) * D + ch * 8);
+      kr[i] = load16(kt + (int64_t)(tt + key) * D + ch * 8);
     }
 #pragma unroll
     for (int i = 0; i < L::VP; ++i) {
       const int p = threadIdx.x + 256 * i, dim = p >> 2, pc = p & 3;
-      vr[i] = load16(vb + (int64_t)dim * a.S + t0 + pc * 8);
+      vr[i] = load16(vt + (int64_t)dim * a.S + tt + pc * 8);
     }
   };
   auto store_tile = [&](uint16_t *st) {
@@ -275,7 +284,8 @@ hipError_t launch_d(AttnArgs a, hipStream_t st) {
   }
   a.kc = kc;
   a.n_splits = ns;
-  hipLaunchKernelGGL(attn_chunk_kernel<D>, dim3(a.n_groups * ns), dim3(256), 0, st, a, rpb);
+  if (a.pt) hipLaunchKernelGGL((attn_chunk_kernel<D, true>), dim3(a.n_groups * ns), dim3(256), 0, st, a, rpb);
+  else hipLaunchKernelGGL((attn_chunk_kernel<D, false>), dim3(a.n_groups * ns), dim3(256), 0, st, a, rpb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
   hipLaunchKernelGGL(attn_chunk_merge_kernel<D>, dim3(a.n_groups * AC_COLS), dim3(D), 0, st, a, rpb);

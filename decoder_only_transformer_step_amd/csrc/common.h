@@ -131,6 +131,21 @@ enum {
   EPI_MOE_ADD = 5,   // batch-1 GEMV only: C[n] += sum_j w_j y_j[n] + gate * acc (MoE combine)
 };
 
+// Where position pos of sequence seq sits in a KV cache: in the sequence's
+// own contiguous region (pt null: unit seq, row pos) or, with a paged cache,
+// in pool page pt[seq * mp + pos / P] at row pos % P.  `stride` is the
+// elements of one unit (a sequence, or a page); the caller adds the layer
+// offset and indexes rows with the unit's positions per head (S, or P).
+__device__ __forceinline__ int64_t kv_loc(const int32_t *pt, int32_t mp, int32_t P, int64_t stride, int seq,
+                                          int pos, int &row) {
+  if (pt) {
+    row = pos % P;
+    return (int64_t)pt[(int64_t)seq * mp + pos / P] * stride;
+  }
+  row = pos;
+  return (int64_t)seq * stride;
+}
+
 struct QkvEpi {
   const float *bias;       // fp32 [qkv rows] or null
   const float2 *cs;        // (cos, sin) [S][d/2]
@@ -139,8 +154,10 @@ struct QkvEpi {
   uint16_t *q;             // split bf16 [rows][Hq][d], lo plane at q + q_lo
   int64_t q_lo;
   uint16_t *kcache, *vcache;
-  int64_t seq_stride, layer_off;
-  int32_t S, Hq, Hkv, d;
+  int64_t seq_stride, layer_off;  // elements per sequence (per page when paged); layer offset
+  int32_t S, Hq, Hkv, d;          // S: positions per (unit, layer, head) (the page size when paged)
+  const int32_t *pt;              // paged cache: page table [seq][mp], else null
+  int32_t mp, P;
 };
 
 struct ArgmaxEpi {

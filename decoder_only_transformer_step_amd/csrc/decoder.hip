@@ -46,6 +46,12 @@ struct Layout {
   size_t gpart_elems, am_n;
   size_t packed;               // packed weight copies for the chunk kernel (or 0 bytes)
   size_t quant;                // quantised weights (codes, scales, dequantised copies), or 0
+  // KV-cache units: a sequence each (contiguous), or pool pages (paged)
+  int kvS;                     // positions per (unit, layer, head): S, or the page size
+  int64_t kv_unit;             // elements of one unit in either cache
+  size_t kv_units;             // max_batch, or the pool's page count
+  int mp;                      // page-table entries per sequence (0: contiguous)
+  size_t stage_n;              // int32 words of one staging slot (rows, then the page table)
 };
 
 // Matrices of a quantised model (weight_quant): per layer qkv, o, gate_up,
@@ -118,6 +124,8 @@ bool config_ok(const decoder_config_t *c) {
   if (!(c->rope_base > 0.0) || !(c->rms_eps >= 0.0)) return false;
   if (c->sliding_window < 0 || !(c->attn_softcap >= 0.0) || c->attn_softcap > 1e30) return false;
   if (c->qk_norm != 0 && c->qk_norm != 1) return false;
+  if (c->kv_page_size < 0 || (c->kv_page_size > 0 && (c->kv_page_size % 32 || c->kv_pages < 1)))
+    return false;
   // quantised GEMVs load 16 codes per lane: every row length a multiple of 16
   if (c->weight_quant != 0 && (c->weight_quant != 1 || c->n_experts > 0 || c->hidden % 16 || c->ffn_inter % 16))
     return false;
@@ -146,7 +154,19 @@ Layout make_layout(const decoder_config_t *c) {
     off = align_up(off + std::max<size_t>(bytes, 1), A);
     return o;
   };
-  const size_t kv = (size_t)c->max_batch * L.seq_stride * 2;
+  if (c->kv_page_size > 0) {
+    L.kvS = c->kv_page_size;
+    L.kv_unit = (int64_t)c->n_layers * Hkv * (int64_t)L.kvS * d;
+    L.kv_units = (size_t)c->kv_pages;
+    L.mp = (c->max_seq + c->kv_page_size - 1) / c->kv_page_size;
+  } else {
+    L.kvS = L.S;
+    L.kv_unit = L.seq_stride;
+    L.kv_units = (size_t)c->max_batch;
+    L.mp = 0;
+  }
+  L.stage_n = (size_t)3 * L.R + (size_t)c->max_batch * L.mp;
+  const size_t kv = L.kv_units * L.kv_unit * 2;
   L.kcache = take(kv);
   L.vcache = take(kv);
   L.rope = take((size_t)L.S * (d / 2) * sizeof(float2));
@@ -158,7 +178,7 @@ Layout make_layout(const decoder_config_t *c) {
   L.qkv = take((size_t)L.R * qkvr * 4);
   L.h = take((size_t)L.R * std::max(c->ffn_inter, 1) * 4);
   L.logits = take((size_t)L.RL * c->vocab * 4);
-  L.stage = take((size_t)3 * L.R * 4);
+  L.stage = take(L.stage_n * 4);
   L.next_token = take((size_t)c->max_batch * 4);
   L.part_o = take((size_t)ATTN_MAX_TASKS * 16 * d * 4);
   L.part_ml = take((size_t)ATTN_MAX_TASKS * 16 * 2 * 4);
@@ -245,6 +265,11 @@ struct decoder {
   int layer_limit = -1;
   int last_rows = 0;
   int32_t *pinned = nullptr;
+  // paged KV cache: device page table [max_batch][mp] (staged with the rows),
+  // each sequence's pages in position order, and the free pages
+  int32_t *page_table = nullptr;
+  std::vector<std::vector<int32_t>> seq_pages;
+  std::vector<int32_t> free_pages;
   hipEvent_t ev[STAGE_RING];
   bool ev_used[STAGE_RING];
   int ring = 0;
@@ -326,18 +351,62 @@ int stage_rows(decoder *D, int rows, const int32_t *ids, const int32_t *seqs, co
   const int slot = D->ring;
   D->ring = (D->ring + 1) % STAGE_RING;
   if (D->ev_used[slot]) HIP_TRY(D, hipEventSynchronize(D->ev[slot]), "stage wait");
-  int32_t *h = D->pinned + (size_t)slot * 3 * D->L.R;
+  int32_t *h = D->pinned + (size_t)slot * D->L.stage_n;
   D->hseq.assign(seqs, seqs + rows);
   for (int r = 0; r < rows; ++r) {
     h[r] = ids ? ids[r] : 0;
     h[D->L.R + r] = seqs[r];
     h[2 * D->L.R + r] = pos[r];
   }
-  HIP_TRY(D, hipMemcpyAsync(D->ids, h, (size_t)3 * D->L.R * 4, hipMemcpyHostToDevice, D->stream),
-          "stage copy");
+  if (D->L.mp) {  // the page table travels with the rows
+    int32_t *t = h + 3 * D->L.R;
+    for (int s = 0; s < D->c.max_batch; ++s) {
+      const std::vector<int32_t> &pg = D->seq_pages[s];
+      for (int j = 0; j < D->L.mp; ++j) t[(size_t)s * D->L.mp + j] = j < (int)pg.size() ? pg[j] : 0;
+    }
+  }
+  HIP_TRY(D, hipMemcpyAsync(D->ids, h, D->L.stage_n * 4, hipMemcpyHostToDevice, D->stream), "stage copy");
   HIP_TRY(D, hipEventRecord(D->ev[slot], D->stream), "stage event");
   D->ev_used[slot] = true;
   return DEC_OK;
+}
+
+// Element offset of layer l inside a KV unit, and the page table (or null).
+int64_t kv_layer_off(const decoder *D, int l) {
+  return (int64_t)l * D->c.n_kv_heads * (int64_t)D->L.kvS * D->c.head_dim;
+}
+const int32_t *kv_pt(const decoder *D) { return D->L.mp ? D->page_table : nullptr; }
+
+// Paged cache: give each listed sequence the pages its new length needs
+// (all or nothing: a pool too small for the call launches nothing).
+int ensure_pages(decoder *D, int n, const int32_t *seqs, const int32_t *new_len) {
+  if (!D->L.mp) return DEC_OK;
+  const int P = D->c.kv_page_size;
+  size_t need = 0;
+  for (int i = 0; i < n; ++i) {
+    const size_t want = (size_t)(new_len[i] + P - 1) / P, have = D->seq_pages[seqs[i]].size();
+    if (want > have) need += want - have;
+  }
+  if (need > D->free_pages.size()) return fail(D, DEC_E_CONTEXT_OVERFLOW, "KV page pool exhausted");
+  for (int i = 0; i < n; ++i) {
+    std::vector<int32_t> &pg = D->seq_pages[seqs[i]];
+    while ((int64_t)pg.size() * P < new_len[i]) {
+      pg.push_back(D->free_pages.back());
+      D->free_pages.pop_back();
+    }
+  }
+  return DEC_OK;
+}
+
+// Paged cache: return the pages of sequence s past its first keep positions.
+void release_pages(decoder *D, int s, int keep) {
+  if (!D->L.mp) return;
+  const int P = D->c.kv_page_size;
+  std::vector<int32_t> &pg = D->seq_pages[s];
+  while ((int64_t)pg.size() * P >= (int64_t)keep + P) {
+    D->free_pages.push_back(pg.back());
+    pg.pop_back();
+  }
 }
 
 // Launch one projection (plus its split-K reduction) as node `node`.
@@ -466,9 +535,11 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
   a.vcache = D->vcache;
   a.row_seq = D->row_seq;
   a.row_pos = D->row_pos;
-  a.seq_stride = D->L.seq_stride;
-  a.layer_off = (int64_t)layer * c.n_kv_heads * (int64_t)D->L.S * c.head_dim;
-  a.S = D->L.S;
+  a.seq_stride = D->L.kv_unit;
+  a.layer_off = kv_layer_off(D, layer);
+  a.S = D->L.kvS;
+  a.pt = kv_pt(D);
+  a.mp = D->L.mp;
   a.Hq = c.n_heads;
   a.Hkv = c.n_kv_heads;
   a.G = c.n_heads / c.n_kv_heads;
@@ -578,9 +649,11 @@ int qk_norm_pass(decoder *D, int l, int rows) {
   a.q_lo = D->q_lo;
   a.kcache = D->kcache;
   a.vcache = D->vcache;
-  a.seq_stride = D->L.seq_stride;
-  a.layer_off = (int64_t)l * c.n_kv_heads * (int64_t)D->L.S * d;
-  a.S = D->L.S;
+  a.seq_stride = D->L.kv_unit;
+  a.layer_off = kv_layer_off(D, l);
+  a.S = D->L.kvS;
+  a.pt = kv_pt(D);
+  a.mp = D->L.mp;
   a.Hq = c.n_heads;
   a.Hkv = c.n_kv_heads;
   a.d = d;
@@ -623,9 +696,12 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
   q.qkv.q_lo = D->q_lo;
   q.qkv.kcache = D->kcache;
   q.qkv.vcache = D->vcache;
-  q.qkv.seq_stride = D->L.seq_stride;
-  q.qkv.layer_off = (int64_t)l * c.n_kv_heads * (int64_t)D->L.S * d;
-  q.qkv.S = D->L.S;
+  q.qkv.seq_stride = D->L.kv_unit;
+  q.qkv.layer_off = kv_layer_off(D, l);
+  q.qkv.S = D->L.kvS;
+  q.qkv.pt = kv_pt(D);
+  q.qkv.mp = D->L.mp;
+  q.qkv.P = D->L.kvS;
   q.qkv.Hq = c.n_heads;
   q.qkv.Hkv = c.n_kv_heads;
   q.qkv.d = d;
@@ -733,9 +809,12 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   q.qkv.q_lo = D->q_lo;
   q.qkv.kcache = D->kcache;
   q.qkv.vcache = D->vcache;
-  q.qkv.seq_stride = D->L.seq_stride;
-  q.qkv.layer_off = (int64_t)l * c.n_kv_heads * (int64_t)D->L.S * d;
-  q.qkv.S = D->L.S;
+  q.qkv.seq_stride = D->L.kv_unit;
+  q.qkv.layer_off = kv_layer_off(D, l);
+  q.qkv.S = D->L.kvS;
+  q.qkv.pt = kv_pt(D);
+  q.qkv.mp = D->L.mp;
+  q.qkv.P = D->L.kvS;
   q.qkv.Hq = c.n_heads;
   q.qkv.Hkv = c.n_kv_heads;
   q.qkv.d = d;
@@ -1011,6 +1090,10 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
   D->ids = carve<int32_t>(D, L.stage);
   D->row_seq = D->ids + L.R;
   D->row_pos = D->ids + 2 * L.R;
+  D->page_table = D->ids + 3 * L.R;
+  D->seq_pages.assign(cfg->max_batch, std::vector<int32_t>());
+  D->free_pages.clear();
+  for (int64_t p = (int64_t)L.kv_units - 1; L.mp && p >= 0; --p) D->free_pages.push_back((int32_t)p);
   D->next_token = carve<int32_t>(D, L.next_token);
   D->part_o = carve<float>(D, L.part_o);
   D->part_ml = carve<float>(D, L.part_ml);
@@ -1118,7 +1201,7 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
     delete D;
     return code;
   };
-  if (hipHostMalloc((void **)&D->pinned, (size_t)STAGE_RING * 3 * L.R * 4, hipHostMallocDefault) != hipSuccess) {
+  if (hipHostMalloc((void **)&D->pinned, (size_t)STAGE_RING * L.stage_n * 4, hipHostMallocDefault) != hipSuccess) {
     D->pinned = nullptr;
     return cleanup(DEC_E_HIP);
   }
@@ -1137,7 +1220,7 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
     }
   if (hipMemcpy(D->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess)
     return cleanup(DEC_E_HIP);
-  const size_t kvb = (size_t)cfg->max_batch * L.seq_stride * 2;
+  const size_t kvb = L.kv_units * L.kv_unit * 2;
   if (hipMemsetAsync(D->kcache, 0, kvb, D->stream) != hipSuccess ||
       hipMemsetAsync(D->vcache, 0, kvb, D->stream) != hipSuccess ||
       hipMemsetAsync(D->next_token, 0, (size_t)cfg->max_batch * 4, D->stream) != hipSuccess ||
@@ -1181,7 +1264,10 @@ int prefill_chunk(decoder_t *D, int32_t seq, const int32_t *ids, int32_t n, int3
     if (ids[i] < 0 || ids[i] >= c.vocab) return fail(D, DEC_E_TOKEN, "token id out of range");
   std::vector<int32_t> seqs(n, seq), pos(n);
   for (int i = 0; i < n; ++i) pos[i] = start_pos + i;
-  int rc = stage_rows(D, n, ids, seqs.data(), pos.data());
+  const int32_t new_len = start_pos + n;
+  int rc = ensure_pages(D, 1, &seq, &new_len);
+  if (rc) return rc;
+  rc = stage_rows(D, n, ids, seqs.data(), pos.data());
   if (rc) return rc;
   const int G = c.n_heads / c.n_kv_heads;
   const int nout = logits_mode == 0 ? 0 : (logits_mode == 1 ? 1 : n);
@@ -1216,7 +1302,11 @@ int decode_step(decoder_t *D, int32_t batch, const int32_t *seqs, const int32_t 
     pos[b] = D->len[s];
     max_pos = std::max(max_pos, pos[b]);
   }
-  int rc = stage_rows(D, batch, tokens, seqs, pos.data());
+  std::vector<int32_t> new_len(batch);
+  for (int b = 0; b < batch; ++b) new_len[b] = pos[b] + 1;
+  int rc = ensure_pages(D, batch, seqs, new_len.data());
+  if (rc) return rc;
+  rc = stage_rows(D, batch, tokens, seqs, pos.data());
   if (rc) return rc;
   rc = run_step(D, batch, 1, max_pos, pos.data(), tokens ? 0 : 1, 0, batch, d_logits, d_argmax, batch);
   if (rc) return rc;
@@ -1232,9 +1322,15 @@ int kv_reset(decoder_t *D, int32_t seq) {
   const decoder_config_t &c = D->c;
   if (seq < -1 || seq >= c.max_batch) return fail(D, DEC_E_INVALID, "seq out of range");
   const int s0 = seq < 0 ? 0 : seq, s1 = seq < 0 ? c.max_batch : seq + 1;
-  const size_t bytes = (size_t)(s1 - s0) * D->L.seq_stride * 2;
-  HIP_TRY(D, hipMemsetAsync(D->kcache + (size_t)s0 * D->L.seq_stride, 0, bytes, D->stream), "kv_reset");
-  HIP_TRY(D, hipMemsetAsync(D->vcache + (size_t)s0 * D->L.seq_stride, 0, bytes, D->stream), "kv_reset");
+  if (D->L.mp) {
+    // paged: the pages go back to the pool (their stale rows are finite and
+    // never read: a key past a query's position gets probability exactly 0)
+    for (int s = s0; s < s1; ++s) release_pages(D, s, 0);
+  } else {
+    const size_t bytes = (size_t)(s1 - s0) * D->L.seq_stride * 2;
+    HIP_TRY(D, hipMemsetAsync(D->kcache + (size_t)s0 * D->L.seq_stride, 0, bytes, D->stream), "kv_reset");
+    HIP_TRY(D, hipMemsetAsync(D->vcache + (size_t)s0 * D->L.seq_stride, 0, bytes, D->stream), "kv_reset");
+  }
   for (int s = s0; s < s1; ++s) {
     D->len[s] = 0;
     D->has_next[s] = 0;
@@ -1253,6 +1349,7 @@ int kv_truncate(decoder_t *D, int32_t seq, int32_t len) {
   // rewritten before a query at or past it runs.
   D->len[seq] = len;
   D->has_next[seq] = 0;
+  release_pages(D, seq, len);
   return DEC_OK;
 }
 
@@ -1263,6 +1360,7 @@ int kv_load(decoder_t *D, int32_t seq, int32_t layer, const uint16_t *d_k, const
   if (seq < 0 || seq >= c.max_batch || layer < 0 || layer >= c.n_layers || !d_k || !d_v)
     return fail(D, DEC_E_INVALID, "kv_load argument");
   if (len < 0) return fail(D, DEC_E_INVALID, "kv_load length");
+  if (D->L.mp) return fail(D, DEC_E_INVALID, "kv_load needs the contiguous KV cache (kv_page_size 0)");
   if (len > c.max_seq) return fail(D, DEC_E_CONTEXT_OVERFLOW, "kv_load past max_seq");
   const int d = c.head_dim, S = D->L.S;
   const int64_t loff = (int64_t)seq * D->L.seq_stride + (int64_t)layer * c.n_kv_heads * (int64_t)S * d;

@@ -54,7 +54,8 @@ __device__ __forceinline__ void epi_apply(const GemmArgs &g, int64_t orow, int n
       u1 += q.bias[n + half];
     }
     const int pos = q.row_pos[orow], seq = q.row_seq[orow];
-    const int64_t base = (int64_t)seq * q.seq_stride + q.layer_off;
+    int prow;
+    const int64_t base = kv_loc(q.pt, q.mp, q.P, q.seq_stride, seq, pos, prow) + q.layer_off;
     if (hh < q.Hq + q.Hkv) {
       const float2 t = q.cs[(int64_t)pos * half + i];
       const float r0 = u0 * t.x - u1 * t.y;
@@ -69,14 +70,14 @@ __device__ __forceinline__ void epi_apply(const GemmArgs &g, int64_t orow, int n
         dst[q.q_lo + i] = (uint16_t)l0;
         dst[q.q_lo + i + half] = (uint16_t)l1;
       } else {
-        uint16_t *dst = q.kcache + base + ((int64_t)(hh - q.Hq) * q.S + pos) * d;
+        uint16_t *dst = q.kcache + base + ((int64_t)(hh - q.Hq) * q.S + prow) * d;
         dst[i] = (uint16_t)f32_to_bf16_bits(r0);
         dst[i + half] = (uint16_t)f32_to_bf16_bits(r1);
       }
     } else {
       uint16_t *vt = q.vcache + base + (int64_t)(hh - q.Hq - q.Hkv) * d * q.S;
-      vt[(int64_t)i * q.S + pos] = (uint16_t)f32_to_bf16_bits(u0);
-      vt[(int64_t)(i + half) * q.S + pos] = (uint16_t)f32_to_bf16_bits(u1);
+      vt[(int64_t)i * q.S + prow] = (uint16_t)f32_to_bf16_bits(u0);
+      vt[(int64_t)(i + half) * q.S + prow] = (uint16_t)f32_to_bf16_bits(u1);
     }
   }
 }

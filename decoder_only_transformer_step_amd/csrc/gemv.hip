@@ -242,7 +242,8 @@ __device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, in
     const float u0 = v0 + pre.c, u1 = v1 + pre.e;
     const int pos = q.row_pos ? q.row_pos[0] : q.pos_arg;
     const int seq = q.row_seq ? q.row_seq[0] : q.seq_arg;
-    const int64_t base = (int64_t)seq * q.seq_stride + q.layer_off;
+    int prow;
+    const int64_t base = kv_loc(q.pt, q.mp, q.P, q.seq_stride, seq, pos, prow) + q.layer_off;
     if (hh < q.Hq + q.Hkv) {
       const float a0 = u0 * pre.a - u1 * pre.b, a1 = u0 * pre.b + u1 * pre.a;
       if (hh < q.Hq) {
@@ -255,14 +256,14 @@ __device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, in
         dst[q.q_lo + i] = (uint16_t)l0;
         dst[q.q_lo + i + half] = (uint16_t)l1;
       } else {
-        uint16_t *dst = q.kcache + base + ((int64_t)(hh - q.Hq) * q.S + pos) * d;
+        uint16_t *dst = q.kcache + base + ((int64_t)(hh - q.Hq) * q.S + prow) * d;
         dst[i] = (uint16_t)f32_to_bf16_bits(a0);
         dst[i + half] = (uint16_t)f32_to_bf16_bits(a1);
       }
     } else {
       uint16_t *vt = q.vcache + base + (int64_t)(hh - q.Hq - q.Hkv) * d * q.S;
-      vt[(int64_t)i * q.S + pos] = (uint16_t)f32_to_bf16_bits(u0);
-      vt[(int64_t)(i + half) * q.S + pos] = (uint16_t)f32_to_bf16_bits(u1);
+      vt[(int64_t)i * q.S + prow] = (uint16_t)f32_to_bf16_bits(u0);
+      vt[(int64_t)(i + half) * q.S + prow] = (uint16_t)f32_to_bf16_bits(u1);
     }
   }
 }

@@ -95,9 +95,11 @@ struct AttnArgs {
   const uint16_t *vcache;  // V cache base, transposed: [seq][layer][Hkv][d][S]
   const int32_t *row_seq;  // [rows]
   const int32_t *row_pos;  // [rows]: absolute position of each query row
-  int64_t seq_stride;      // elements per sequence in either cache
-  int64_t layer_off;       // element offset of this layer inside a sequence
-  int32_t S;               // positions allocated per (seq, layer, head), multiple of 32
+  int64_t seq_stride;      // elements per sequence in either cache (per page when paged)
+  int64_t layer_off;       // element offset of this layer inside a sequence (a page)
+  int32_t S;               // positions per (seq or page, layer, head), multiple of 32
+  const int32_t *pt;       // paged cache: page table [seq][mp] (pages of S positions), else null
+  int32_t mp;
   int32_t Hq, Hkv, G;
   int32_t rows, rows_per_group, n_groups;
   int32_t kc, n_splits;    // keys per split (multiple of 32), splits per group
@@ -182,6 +184,8 @@ struct QkNormArgs {
   uint16_t *kcache, *vcache;
   int64_t seq_stride, layer_off;
   int32_t S, Hq, Hkv, d, rows;
+  const int32_t *pt;                 // paged cache: page table [seq][mp] (pages of S positions)
+  int32_t mp;
 };
 hipError_t launch_qk_norm_rope(const QkNormArgs &a, hipStream_t st);
 

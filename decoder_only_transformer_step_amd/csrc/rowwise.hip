@@ -74,7 +74,8 @@ __global__ __launch_bounds__(64) void qk_norm_rope_kernel(QkNormArgs a) {
   const float *src = a.qkv + (int64_t)r * a.ld + (int64_t)hh * d;
   float u0 = on ? src[i] : 0.f, u1 = on ? src[i + half] : 0.f;
   const int pos = a.row_pos[r], seq = a.row_seq[r];
-  const int64_t base = (int64_t)seq * a.seq_stride + a.layer_off;
+  int prow;
+  const int64_t base = kv_loc(a.pt, a.mp, a.S, a.seq_stride, seq, pos, prow) + a.layer_off;
   if (hh < a.Hq + a.Hkv) {
     const float ss = wave_sum(u0 * u0 + u1 * u1);
     const float inv = 1.0f / sqrtf(ss / (float)d + a.eps);
@@ -95,14 +96,14 @@ __global__ __launch_bounds__(64) void qk_norm_rope_kernel(QkNormArgs a) {
       dst[a.q_lo + i] = (uint16_t)l0;
       dst[a.q_lo + i + half] = (uint16_t)l1;
     } else {
-      uint16_t *dst = a.kcache + base + ((int64_t)(hh - a.Hq) * a.S + pos) * d;
+      uint16_t *dst = a.kcache + base + ((int64_t)(hh - a.Hq) * a.S + prow) * d;
       dst[i] = (uint16_t)f32_to_bf16_bits(r0);
       dst[i + half] = (uint16_t)f32_to_bf16_bits(r1);
     }
   } else if (on) {
     uint16_t *vt = a.vcache + base + (int64_t)(hh - a.Hq - a.Hkv) * d * a.S;
-    vt[(int64_t)i * a.S + pos] = (uint16_t)f32_to_bf16_bits(u0);
-    vt[(int64_t)(i + half) * a.S + pos] = (uint16_t)f32_to_bf16_bits(u1);
+    vt[(int64_t)i * a.S + prow] = (uint16_t)f32_to_bf16_bits(u0);
+    vt[(int64_t)(i + half) * a.S + prow] = (uint16_t)f32_to_bf16_bits(u1);
   }
 }
 

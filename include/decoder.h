@@ -55,7 +55,8 @@ extern "C" {
 
 enum {
   DEC_OK = 0,
-  DEC_E_CONTEXT_OVERFLOW = 1, /* start_pos + n > max_seq, or a full sequence on decode */
+  DEC_E_CONTEXT_OVERFLOW = 1, /* start_pos + n > max_seq, a full sequence on decode, or no free
+                                 page left in a paged cache */
   DEC_E_INVALID = 2,          /* bad argument: n <= 0, n > max_chunk, batch > max_batch,
                                  start_pos != current length, bad seq, bad config, ... */
   DEC_E_TOKEN = 3,            /* token id outside [0, vocab) */
@@ -101,6 +102,11 @@ typedef struct {
                               rounded to nearest (ties to even).  The model then computes with
                               the dequantised weights (exactly bf16 values) on every path; the
                               embedding gather keeps the caller's table */
+  int32_t kv_page_size;    /* 0: each sequence owns max_seq cache rows; P > 0 (a multiple of 32):
+                              the cache is a pool of kv_pages pages of P positions, handed to
+                              sequences as they grow and returned by kv_reset / kv_truncate
+                              (a paged cache for sequences of ragged lengths; kv_load needs 0) */
+  int32_t kv_pages;        /* pages in the pool when kv_page_size > 0 */
 } decoder_config_t;
 
 typedef struct {

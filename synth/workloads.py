@@ -38,6 +38,8 @@ class Shape:
     attn_sinks: bool = False  # one sink logit per query head and layer
     qk_norm: bool = False     # RMSNorm of every q and k head (gains q_norm, k_norm [d]) before RoPE
     weight_quant: int = 0     # 1: layer matrices and lm-head as int8 with a power-of-two scale per row
+    kv_page_size: int = 0     # 0: contiguous KV per sequence; P: a pool of kv_pages pages of P positions
+    kv_pages: int = 0
 
     @property
     def is_moe(self):
