@@ -53,7 +53,9 @@ def test_strerror_and_workspace_sizes():
 
 
 @pytest.mark.parametrize("field,value", [("n_kv_heads", 3), ("head_dim", 96), ("max_chunk", 0),
-                                         ("hidden", 100), ("max_chunk", 512)])
+                                         ("hidden", 100), ("max_chunk", 512), ("sliding_window", -1),
+                                         ("attn_softcap", -1.0), ("qk_norm", 2), ("weight_quant", 2),
+                                         ("kv_page_size", 48), ("kv_page_size", -32)])
 def test_invalid_configs_rejected(field, value):
     shape = WORKLOADS["tiny"][0].with_(**{field: value})
     assert binding.decoder_workspace_bytes(binding.make_config(shape)) == 0
@@ -65,3 +67,21 @@ def test_init_rejects_missing_workspace():
     w = binding.DecoderWeights()
     rc = binding.lib().decoder_init(ctypes.byref(cfg), ctypes.byref(w), None, 0, None, ctypes.byref(h))
     assert rc == binding.DEC_E_INVALID     # weights missing
+
+
+def test_variant_configs_and_their_workspace():
+    tiny = WORKLOADS["tiny"][0]
+    base = binding.decoder_workspace_bytes(binding.make_config(tiny))
+    # a paged cache needs its pages; with them its KV pool replaces the
+    # per-sequence regions (4 pages of 32 positions vs 64 positions of 1 sequence)
+    assert binding.decoder_workspace_bytes(binding.make_config(tiny.with_(kv_page_size=32))) == 0
+    paged = binding.decoder_workspace_bytes(binding.make_config(tiny.with_(kv_page_size=32, kv_pages=4)))
+    assert paged > 0
+    # quantised weights add codes, scales and dequantised copies: 3 bytes per weight and more
+    q8 = binding.decoder_workspace_bytes(binding.make_config(tiny.with_(weight_quant=1)))
+    assert q8 - base >= 3 * (tiny.n_params() - tiny.vocab * tiny.hidden)
+    # MoE models and rows that are not a multiple of 16 cannot stream int8 codes
+    assert binding.decoder_workspace_bytes(binding.make_config(WORKLOADS["moe"][0].with_(weight_quant=1))) == 0
+    assert binding.decoder_workspace_bytes(binding.make_config(tiny.with_(weight_quant=1, ffn_inter=680))) == 0
+    for kw in (dict(sliding_window=8), dict(attn_softcap=30.0), dict(qk_norm=True)):
+        assert binding.decoder_workspace_bytes(binding.make_config(tiny.with_(**kw))) == base
