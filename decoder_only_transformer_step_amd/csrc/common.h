@@ -57,14 +57,6 @@ __device__ __forceinline__ u32pair pack_split2(float a, float b) {
 __device__ __forceinline__ u32x4 load16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
-// Buffer-resource loads: a lane whose byte offset is at or past the
-// resource's size reads zeros, so masked loads need no branch.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
-}
 __device__ __forceinline__ u32x2 load8(const void *p) {
   return *reinterpret_cast<const u32x2 *>(p);
 }

@@ -16,7 +16,8 @@
 //    the weights' own bf16 storage.  Each lane does 8 fp32 FMAs per 16-byte
 //    load; the LDS layout makes each wave's 16-byte reads contiguous across
 //    lanes.  A DPP reduction gives the dot product.
-//  * Pipeline: two register buffers of 8 KB per wave; the activation loads
+//  * Pipeline: two register buffers per wave (8 KB each for bf16 weights,
+//    4 KB for int8 codes); the activation loads
 //    go out first, then the first two weight chunks, so the prologue waits
 //    only for the activation while the weights stream in.  Every load is
 //    unconditional, so the compiler's memory wait counts stay exact.
