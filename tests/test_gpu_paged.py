@@ -99,3 +99,40 @@ def test_paged_ragged_batch_reset_rollback_and_exhaustion():
     log("ragged paged batch matches the contiguous decoder bit for bit")
     flat.close()
     paged.close()
+
+
+def test_paged_with_every_option_and_verify():
+    """Paging under int8 weights, a window, a soft-cap, sinks and QK-norm at
+    once, through a verify of four drafts and a rollback: bit for bit the
+    contiguous decoder, and within the acceptance rule of the oracle."""
+    shape = C8B.with_(name="gqa-8b-layers-2-all", n_layers=2, vocab=1024, max_seq=512, weight_quant=1,
+                      sliding_window=100, attn_softcap=2.0, attn_sinks=True, qk_norm=True)
+    W = host_weights(shape)
+    flat, _ = make_decoder(shape, W)
+    paged, _ = make_decoder(shape.with_(kv_page_size=64, kv_pages=5), W)
+    m = oracle.Model(shape, W)
+    ids = prompt(shape, 150)
+    a = run_prefill(flat, ids, 128)
+    b = run_prefill(paged, ids, 128)
+    assert np.array_equal(a, b)
+    want = m.prefill(ids, 128)["logits"]
+    assert_parity(compare_logits(b, want, "all options prefill"), "all options prefill")
+    drafts = [int(t) for t in prompt(shape, 4, seq=9)]
+    outs = []
+    for d in (flat, paged):
+        lg = torch.empty((4, shape.vocab), dtype=torch.float32, device="cuda")
+        d.prefill_chunk(0, drafts, 150, logits_mode=2, logits=lg)
+        torch.cuda.synchronize()
+        outs.append(lg.cpu().numpy())
+        d.kv_truncate(0, 152)
+    assert np.array_equal(outs[0], outs[1])
+    m.forward(drafts, 150, logits_mode=0)
+    m.truncate(0, 152)
+    nxt = int(prompt(shape, 1, seq=10)[0])
+    la, _ = decode(flat, [0], [nxt])
+    lb, _ = decode(paged, [0], [nxt])
+    assert np.array_equal(la, lb)
+    want = m.forward([nxt], 152)["logits"]
+    assert_parity(compare_logits(lb[0], want, "all options decode after rollback"), "all options decode")
+    flat.close()
+    paged.close()
