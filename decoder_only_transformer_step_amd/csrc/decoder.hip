@@ -57,15 +57,24 @@ struct Layout {
 // Matrices of a quantised model (weight_quant): per layer qkv, o, gate_up,
 // down, then the lm-head; each takes int8 codes, fp32 scales and a
 // dequantised bf16 copy, every piece 256-byte aligned.
+// Dense: qkv, o, gate_up, down.  MoE: qkv, o, the shared expert's gate_up
+// and down (when it has one), then every routed expert's gate_up rows
+// [E * 2 Ie][H] and down rows [E * H][Ie].  Rows 0 leave a matrix out.
+constexpr int QUANT_MATS = 6;
 struct QuantSpec {
-  int64_t rows[4];
-  int K[4];
+  int64_t rows[QUANT_MATS];
+  int K[QUANT_MATS];
 };
 
 QuantSpec quant_spec(const decoder_config_t *c) {
   const int d = c->head_dim, H = c->hidden, qd = c->n_heads * d, qkvr = (c->n_heads + 2 * c->n_kv_heads) * d;
+  if (c->n_experts > 0) {
+    const int E = c->n_experts, Ie = c->expert_inter, Is = c->shared_inter;
+    return QuantSpec{{qkvr, H, 2 * (int64_t)Is, Is > 0 ? H : 0, (int64_t)E * 2 * Ie, (int64_t)E * H},
+                     {H, qd, H, Is, H, Ie}};
+  }
   const int I = c->ffn_inter;
-  return QuantSpec{{qkvr, H, 2 * (int64_t)I, H}, {H, qd, H, I}};
+  return QuantSpec{{qkvr, H, 2 * (int64_t)I, H, 0, 0}, {H, qd, H, I, 0, 0}};
 }
 
 size_t quant_piece(size_t bytes) { return (bytes + 255) / 256 * 256; }
@@ -78,7 +87,8 @@ size_t quant_bytes(const decoder_config_t *c) {
   if (!c->weight_quant) return 0;
   const QuantSpec qs = quant_spec(c);
   size_t b = quant_matrix_bytes(c->vocab, c->hidden);
-  for (int i = 0; i < 4; ++i) b += (size_t)c->n_layers * quant_matrix_bytes(qs.rows[i], qs.K[i]);
+  for (int i = 0; i < QUANT_MATS; ++i)
+    if (qs.rows[i] > 0) b += (size_t)c->n_layers * quant_matrix_bytes(qs.rows[i], qs.K[i]);
   return b;
 }
 
@@ -127,7 +137,8 @@ bool config_ok(const decoder_config_t *c) {
   if (c->kv_page_size < 0 || (c->kv_page_size > 0 && (c->kv_page_size % 32 || c->kv_pages < 1)))
     return false;
   // quantised GEMVs load 16 codes per lane: every row length a multiple of 16
-  if (c->weight_quant != 0 && (c->weight_quant != 1 || c->n_experts > 0 || c->hidden % 16 || c->ffn_inter % 16))
+  if (c->weight_quant != 0 &&
+      (c->weight_quant != 1 || c->hidden % 16 || c->ffn_inter % 16 || c->expert_inter % 16 || c->shared_inter % 16))
     return false;
   if (c->n_experts > 0) {
     if (c->n_experts > 256 || c->top_k <= 0 || c->top_k > 8 || c->top_k > c->n_experts) return false;
@@ -236,7 +247,7 @@ struct decoder {
     const int8_t *q = nullptr;  // int8 codes [rows][K]
     const float *s = nullptr;   // per-row scales 2^e
   };
-  std::vector<std::array<QuantW, 4>> qw;  // per layer: qkv, o, gate_up, down (weight_quant)
+  std::vector<std::array<QuantW, 6>> qw;  // per layer, in quant_spec order (weight_quant)
   QuantW qhead;                           // the lm-head (weight_quant)
   const uint16_t *embed = nullptr, *lm_head = nullptr;
   const float *final_norm = nullptr;
@@ -595,8 +606,8 @@ int gemv(decoder *D, int node, int epi, const GemvArgs &g, int *blocks = nullptr
   const double nr = (epi == EPI_SWIGLU || epi == EPI_QKV) ? 2.0 : 1.0;
   const double slots = g.slot_expert ? g.n_slots : 1;
   const double out_words = epi == EPI_ADD ? 2 : epi == EPI_MOE_ADD ? 2 + g.moe_k : 1;
-  const double part2 = g.W2 ? g.n_items2 * (nr * (double)g.K * 2 + 4.0) : 0.0;
   const double wrow = g.Wq ? (double)g.K + 4.0 : (double)g.K * 2;  // weight bytes per row (+ its scale)
+  const double part2 = g.W2 ? g.n_items2 * (nr * wrow + 4.0) : 0.0;
   NodeTimer timer(D, node,
                   slots * (nr * g.n_items * wrow + g.K * 4.0 + g.n_items * 4.0 * out_words) + part2,
                   slots * 2.0 * nr * g.n_items * (double)g.K + (g.W2 ? 2.0 * nr * g.n_items2 * (double)g.K : 0.0));
@@ -759,6 +770,11 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
     eg.n_items2 = Is;
     eg.C2 = D->f32_h;
   }
+  eg = quant(D, eg, l, 4);
+  if (c.weight_quant && Is > 0) {
+    eg.W2q = D->qw[l][2].q;
+    eg.w2scale = D->qw[l][2].s;
+  }
   if ((rc = gemv(D, DEC_NODE_EXPERTS, EPI_SWIGLU, eg))) return rc;
   GemvArgs ed = gemv_args(W.w_exp_down, D->f32_hexp, Ie, H, D->yexp);
   ed.slot_expert = D->rids;
@@ -766,14 +782,14 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
   ed.w_group_stride = (int64_t)H * Ie;
   ed.a_slot_stride = Ie;
   ed.ldc = H;
-  if ((rc = gemv(D, DEC_NODE_EXPERTS, EPI_STORE, ed))) return rc;
+  if ((rc = gemv(D, DEC_NODE_EXPERTS, EPI_STORE, quant(D, ed, l, 5)))) return rc;
   if (Is > 0) {
     GemvArgs sd = gemv_args(W.w_sh_down, D->f32_h, Is, H, D->x);
     sd.moe_y = D->yexp;
     sd.moe_w = D->rwts;
     sd.moe_gate = D->rgate;
     sd.moe_k = k;
-    return gemv(D, DEC_NODE_EXPERTS, EPI_MOE_ADD, sd);
+    return gemv(D, DEC_NODE_EXPERTS, EPI_MOE_ADD, quant(D, sd, l, 3));
   }
   NodeTimer tcomb(D, DEC_NODE_EXPERTS, H * (8.0 + 4.0 * k + 4.0), H * 2.0 * (k + 1));
   D->act_norm = nullptr;
@@ -1153,12 +1169,15 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
       *dst = dq;
       return launch_quantize_rows(src, rows, K, q, sc, dq, (hipStream_t)stream) == hipSuccess;
     };
-    D->qw.assign(cfg->n_layers, std::array<decoder::QuantW, 4>{});
+    D->qw.assign(cfg->n_layers, std::array<decoder::QuantW, 6>{});
     bool ok = quant(D->lm_head, cfg->vocab, cfg->hidden, &D->lm_head, D->qhead);
     for (int l = 0; l < cfg->n_layers && ok; ++l) {
       decoder_layer_weights_t &lw = D->layers[l];
-      const uint16_t **m[4] = {&lw.w_qkv, &lw.w_o, &lw.w_gate_up, &lw.w_down};
-      for (int i = 0; i < 4 && ok; ++i) ok = quant(*m[i], qs.rows[i], qs.K[i], m[i], D->qw[l][i]);
+      const bool moe = cfg->n_experts > 0;
+      const uint16_t **m[QUANT_MATS] = {&lw.w_qkv, &lw.w_o, moe ? &lw.w_sh_gate_up : &lw.w_gate_up,
+                                        moe ? &lw.w_sh_down : &lw.w_down, &lw.w_exp_gate_up, &lw.w_exp_down};
+      for (int i = 0; i < QUANT_MATS && ok; ++i)
+        if (qs.rows[i] > 0) ok = quant(*m[i], qs.rows[i], qs.K[i], m[i], D->qw[l][i]);
     }
     if (!ok) {
       D->err = "weight quantisation failed";

@@ -296,6 +296,8 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
     if (bx >= nb1) {
       bx -= nb1;
       g.W = ga.W2;
+      g.Wq = ga.W2q;
+      g.wscale = ga.w2scale;
       g.N = ga.N2;
       g.n_items = ga.n_items2;
       g.C = ga.C2;
@@ -310,6 +312,7 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
   int out_row = 0;
   if (g.slot_expert) {
     W += (int64_t)g.slot_expert[slot] * g.w_group_stride * (Q ? 1 : 2);
+    if (Q) g.wscale += (int64_t)g.slot_expert[slot] * (g.w_group_stride / g.K);  // the expert's row scales
     if (xin) xin += (int64_t)slot * g.a_slot_stride;
     out_row = slot;
   }
@@ -507,8 +510,9 @@ hipError_t launch_gemv(const GemvArgs &g0, int epi, hipStream_t st, int *blocks)
     g.blocks1 = (g.n_items + wv - 1) / wv;
   }
   if (blocks) *blocks = (g.n_items + wv - 1) / wv;
-  // quantised weights: dense launches only (no grouped slots, no second part)
-  if (g.Wq && (!g.wscale || g.K % 16 || g.slot_expert || g.W2 || epi == EPI_MOE_ADD)) return hipErrorInvalidValue;
+  // quantised weights: codes in 16-byte lane loads, and a quantised second part
+  if (g.Wq && (!g.wscale || g.K % 16 || (g.W2 && (!g.W2q || !g.w2scale)) || (g.slot_expert && g.w_group_stride % g.K)))
+    return hipErrorInvalidValue;
   const size_t lds = gemv_lds(g.K, g.Wq != nullptr);
   switch (epi) {
     case EPI_STORE: launch_e<EPI_STORE>(g, wv, lds, st); break;

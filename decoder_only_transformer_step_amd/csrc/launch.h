@@ -61,6 +61,8 @@ struct GemvArgs {
   // optional second part of an EPI_SWIGLU grouped launch (the shared expert):
   // weights W2 [2 N2][K], N2 row pairs into C2 [N2]; blocks1 is set by the launcher
   const uint16_t *W2;
+  const int8_t *W2q;          // its int8 codes and row scales when the first part is quantised
+  const float *w2scale;
   int32_t N2, n_items2;
   float *C2;
   int32_t blocks1;

@@ -95,9 +95,10 @@ typedef struct {
   int32_t qk_norm;         /* 1: RMSNorm (gains q_norm / k_norm [d], eps rms_eps) of every q
                               and k head after the bias and before RoPE (engine.zig
                               applyHeadNorm) */
-  int32_t weight_quant;    /* 1: quantised weight streaming (dense models; pipeline.rs streams
-                              row-quantised int8 "q8_row" weights): decoder_init turns
-                              every layer matrix and the lm-head into int8 codes with one
+  int32_t weight_quant;    /* 1: quantised weight streaming (pipeline.rs streams row-quantised
+                              int8 "q8_row" weights): decoder_init turns the attention
+                              projections, the FFN (dense, or every routed expert and the
+                              shared expert) and the lm-head into int8 codes with one
                               power-of-two scale per row, 2^e with e the smallest integer for
                               which 127 * 2^e covers the row's largest magnitude, codes
                               rounded to nearest (ties to even).  The model then computes with

@@ -160,24 +160,36 @@ def quantize_rows(W_bits, rows, cols):
     return out, e
 
 
-# matrices whose decode projections stream quantised weights
-QUANT_FIELDS = ("w_qkv", "w_o", "w_gate_up", "w_down")
+def quant_dims(shape):
+    """(rows, cols) of every matrix the quantised decoder streams as int8
+    rows: the attention projections, the dense or shared-expert FFN, and
+    every routed expert's rows (the router and the shared gate stay bf16)."""
+    s = shape
+    H = s.hidden
+    dims = {"w_qkv": (s.qkv_rows, H), "w_o": (H, s.q_dim)}
+    if s.is_moe:
+        E, Ie, Is = s.n_experts, s.expert_inter, s.shared_inter
+        dims.update(w_exp_gate_up=(E * 2 * Ie, H), w_exp_down=(E * H, Ie))
+        if Is:
+            dims.update(w_sh_gate_up=(2 * Is, H), w_sh_down=(H, Is))
+    else:
+        dims.update(w_gate_up=(2 * s.ffn_inter, H), w_down=(H, s.ffn_inter))
+    return dims
 
 
 def quantized_weights(shape, weights):
-    """The model's weights as the quantised decoder holds them: every layer
-    matrix and the lm-head dequantised (the embedding gather keeps its bf16
-    table)."""
+    """The model's weights as the quantised decoder holds them: those
+    matrices and the lm-head dequantised (the embedding gather keeps its
+    bf16 table)."""
     s = shape
     H = s.hidden
-    dims = {"w_qkv": (s.qkv_rows, H), "w_o": (H, s.q_dim), "w_gate_up": (2 * s.ffn_inter, H),
-            "w_down": (H, s.ffn_inter)}
+    dims = quant_dims(s)
     out = dict(weights)
     out["layers"] = []
     for L in weights["layers"]:
         L2 = dict(L)
-        for f in QUANT_FIELDS:
-            L2[f] = quantize_rows(L[f], *dims[f])[0].reshape(-1)
+        for f, (r, c) in dims.items():
+            L2[f] = quantize_rows(L[f], r, c)[0].reshape(-1)
         out["layers"].append(L2)
     out["lm_head"] = quantize_rows(weights["lm_head"], s.vocab, H)[0].reshape(-1)
     return out

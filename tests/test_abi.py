@@ -80,8 +80,11 @@ def test_variant_configs_and_their_workspace():
     # quantised weights add codes, scales and dequantised copies: 3 bytes per weight and more
     q8 = binding.decoder_workspace_bytes(binding.make_config(tiny.with_(weight_quant=1)))
     assert q8 - base >= 3 * (tiny.n_params() - tiny.vocab * tiny.hidden)
-    # MoE models and rows that are not a multiple of 16 cannot stream int8 codes
-    assert binding.decoder_workspace_bytes(binding.make_config(WORKLOADS["moe"][0].with_(weight_quant=1))) == 0
+    # rows that are not a multiple of 16 cannot stream int8 codes
     assert binding.decoder_workspace_bytes(binding.make_config(tiny.with_(weight_quant=1, ffn_inter=680))) == 0
+    moe = WORKLOADS["moe"][0]
+    assert binding.decoder_workspace_bytes(binding.make_config(moe.with_(weight_quant=1))) > \
+        binding.decoder_workspace_bytes(binding.make_config(moe))
+    assert binding.decoder_workspace_bytes(binding.make_config(moe.with_(weight_quant=1, expert_inter=1400))) == 0
     for kw in (dict(sliding_window=8), dict(attn_softcap=30.0), dict(qk_norm=True)):
         assert binding.decoder_workspace_bytes(binding.make_config(tiny.with_(**kw))) == base
