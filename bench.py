@@ -106,6 +106,43 @@ def measure_verify(dec, shape, stream, ev0, ev1, reps, ns=(2, 4, 8)):
     return out
 
 
+def measure_graph(dec, shape, n_steps):
+    """Graph-replayed decode: decode_run captures one greedy step into a HIP
+    graph and replays it, against the eager decode_step loop of the timed
+    region.  Each call is synchronous and includes its capture and
+    instantiation, so the replay cost per step is the difference of a long
+    and a short run over the difference of their lengths (host clock, median
+    of three pairs); every run starts from the same position."""
+    import torch
+    L = dec.seq_len(0)
+    short = 8
+    if n_steps <= short or L < 1 or L + n_steps > shape.max_seq:
+        return None
+    toks = torch.empty(n_steps, dtype=torch.int32, device="cuda")
+
+    def run(n):
+        # a rollback forgets the greedy token, so the last position is
+        # decoded again (untimed) with a fixed token to start the run from
+        dec.kv_truncate(0, L - 1)
+        dec.decode_step([0], [1])
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        dec.decode_run(0, n, toks)
+        return time.perf_counter() - t
+
+    run(short)                                   # untimed: first capture on this decoder
+    pairs = [(run(short), run(n_steps)) for _ in range(3)]
+    step_s = statistics.median([(b - a) / (n_steps - short) for a, b in pairs])
+    call_s = statistics.median([b for _, b in pairs])
+    out = {"position": L, "steps": n_steps, "replay_ms_per_step": round(step_s * 1e3, 4),
+           "tok_s": round(1.0 / step_s, 2), "call_ms": round(call_s * 1e3, 3),
+           "call_tok_s": round(n_steps / call_s, 2),
+           "timing": f"host clock; per step = (t({n_steps}) - t({short})) / {n_steps - short}, median of 3"}
+    log(f"[gpu] graph decode {out['tok_s']:.1f} tok/s per replayed step "
+        f"({out['call_tok_s']:.1f} tok/s for a whole {n_steps}-step call)")
+    return out
+
+
 def cpu_baseline(shape, n_prefill, n_decode):
     """The fp64 oracle (unchanged) on the host cores: a chunk of n_prefill
     prompt tokens, then n_decode greedy decode steps; tokens/s of the decode
@@ -291,6 +328,8 @@ def main():
     ap.add_argument("--no-verify", action="store_true",
                     help="skip the multi-position verify measurement (batch-1 workloads)")
     ap.add_argument("--verify-reps", type=int, default=20)
+    ap.add_argument("--graph-steps", type=int, default=128,
+                    help="steps of the graph-replayed decode_run measurement (0: skip; batch-1 workloads)")
     ap.add_argument("--cpu-prefill", type=int, default=16, help="oracle sample: prompt tokens")
     ap.add_argument("--cpu-decode", type=int, default=2, help="oracle sample: decode steps")
     ap.add_argument("--sample-every", type=int, default=8,
@@ -484,6 +523,9 @@ def main():
     verify = None
     if batch == 1 and not args.no_verify:
         verify = measure_verify(dec, shape, stream, ev0, ev1, args.verify_reps)
+    graph = None
+    if batch == 1 and args.graph_steps > 0:
+        graph = measure_graph(dec, shape, args.graph_steps)
 
     d = dst[dom]
     per_launch_bytes = d["bytes"] / d["launches"]
@@ -512,6 +554,7 @@ def main():
                    "nodes_warmup": summarize_nodes(wst)},
         "prefill": prefill,
         "verify": verify,
+        "graph_decode": graph,
         "roofline": roofline,
         "kernel_source_sha256": kernel_source_hash(),
     })

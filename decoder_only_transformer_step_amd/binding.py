@@ -63,6 +63,7 @@ SIGNATURES = {
     "decode_step": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P]),
     "kv_reset": (ctypes.c_int, [_P, _I32]),
     "kv_truncate": (ctypes.c_int, [_P, _I32, _I32]),
+    "decode_run": (ctypes.c_int, [_P, _I32, _I32, _P]),
     "kv_load": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _I32]),
     "decoder_seq_len": (_I32, [_P, _I32]),
     "decoder_set_stream": (ctypes.c_int, [_P, _P]),
@@ -179,6 +180,10 @@ def kv_reset(handle, seq=-1):
     _check(lib().kv_reset(handle, seq), handle, "kv_reset")
 
 
+def decode_run(handle, seq, n_steps, tokens):
+    _check(lib().decode_run(handle, seq, n_steps, _ptr(tokens)), handle, "decode_run")
+
+
 def kv_truncate(handle, seq, length):
     _check(lib().kv_truncate(handle, seq, length), handle, "kv_truncate")
 
@@ -234,6 +239,9 @@ class Decoder:
 
     def kv_truncate(self, seq, length):
         kv_truncate(self.handle, seq, length)
+
+    def decode_run(self, seq, n_steps, tokens):
+        decode_run(self.handle, seq, n_steps, tokens)
 
     def kv_load(self, seq, layer, k, v, length):
         kv_load(self.handle, seq, layer, k, v, length)

@@ -39,6 +39,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 struct Layout {
   size_t kcache, vcache, rope, x, act, attn, q, qkv, h, logits, stage, next_token;
   size_t part_o, part_ml, gpart, counters, am_val, am_idx, am_out, f32_attn, f32_h, f32_act, f32_hexp;
+  size_t gout;                 // decode_run: step counter, then the generated tokens [max_seq]
   size_t rlogits, rids, rids_rec, rwts, rgate, groups, pair_row, pair_of, hexp, yexp, hsh, ysh;
   size_t total;
   int S, R, RL;
@@ -191,6 +192,7 @@ Layout make_layout(const decoder_config_t *c) {
   L.logits = take((size_t)L.RL * c->vocab * 4);
   L.stage = take(L.stage_n * 4);
   L.next_token = take((size_t)c->max_batch * 4);
+  L.gout = take((size_t)(c->max_seq + 1) * 4);
   L.part_o = take((size_t)ATTN_MAX_TASKS * 16 * d * 4);
   L.part_ml = take((size_t)ATTN_MAX_TASKS * 16 * 2 * 4);
   int max_small_n = std::max(qkvr, H);
@@ -259,6 +261,11 @@ struct decoder {
   float *x, *qkv, *logits, *part_o, *part_ml, *gpart, *rlogits, *rwts, *rgate, *yexp, *ysh, *am_val;
   int32_t *ids, *row_seq, *row_pos, *next_token, *rids, *rids_rec, *groups, *pair_row, *pair_of;
   int32_t *counters, *am_idx, *am_out;
+  int32_t *gout;
+  // decode_run captures a step: positions come from device memory (row_pos)
+  // instead of kernel arguments, so one captured step serves every position
+  bool graph_mode = false;
+  hipStream_t gstream = nullptr;  // decode_run's capture stream (the caller's may be the null stream)
   float *f32_attn, *f32_h, *f32_act, *f32_hexp;
   size_t am_cap = 0;           // argmax partials the am_val / am_idx buffers hold
   int cus = 256;               // compute units of the device
@@ -565,7 +572,7 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
   a.part_o = D->part_o;
   a.part_ml = D->part_ml;
   // positions as kernel arguments where the host has them in a usable form
-  if (rows_per_group == 1 && rows <= 16 && (int)D->hseq.size() == rows) {
+  if (rows_per_group == 1 && rows <= 16 && (int)D->hseq.size() == rows && !D->graph_mode) {
     a.pos_mode = 1;
     for (int r = 0; r < rows; ++r) {
       a.pos_arg[r] = hpos[r];
@@ -696,7 +703,7 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
   q.eps = eps;
   q.qkv.bias = c.qkv_bias ? W.b_qkv : nullptr;
   q.qkv.cs = D->rope;
-  if (D->hseq.size() == 1) {  // the position as a kernel argument: no load before the RoPE angle
+  if (D->hseq.size() == 1 && !D->graph_mode) {  // the position as a kernel argument: no load before RoPE
     q.qkv.pos_arg = hpos[0];
     q.qkv.seq_arg = D->hseq[0];
   } else {
@@ -814,7 +821,7 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   q.np_off = d / 2;
   q.qkv.bias = c.qkv_bias ? W.b_qkv : nullptr;
   q.qkv.cs = D->rope;
-  if (D->hseq.size() == 1) {  // the position as a kernel argument: no load before the RoPE angle
+  if (D->hseq.size() == 1 && !D->graph_mode) {  // the position as a kernel argument: no load before RoPE
     q.qkv.pos_arg = hpos[0];
     q.qkv.seq_arg = D->hseq[0];
   } else {
@@ -1111,6 +1118,7 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
   D->free_pages.clear();
   for (int64_t p = (int64_t)L.kv_units - 1; L.mp && p >= 0; --p) D->free_pages.push_back((int32_t)p);
   D->next_token = carve<int32_t>(D, L.next_token);
+  D->gout = carve<int32_t>(D, L.gout);
   D->part_o = carve<float>(D, L.part_o);
   D->part_ml = carve<float>(D, L.part_ml);
   D->gpart = carve<float>(D, L.gpart);
@@ -1256,6 +1264,7 @@ void decoder_free(decoder_t *D) {
   for (auto &ev : D->tev) (void)hipEventDestroy(ev);
   if (D->pinned) (void)hipHostFree(D->pinned);
   for (int i = 0; i < STAGE_RING; ++i) (void)hipEventDestroy(D->ev[i]);
+  if (D->gstream) (void)hipStreamDestroy(D->gstream);
   delete D;
 }
 
@@ -1333,6 +1342,60 @@ int decode_step(decoder_t *D, int32_t batch, const int32_t *seqs, const int32_t 
     D->len[seqs[b]] += 1;
     D->has_next[seqs[b]] = 1;
   }
+  return DEC_OK;
+}
+
+int decode_run(decoder_t *D, int32_t seq, int32_t n_steps, int32_t *d_tokens) {
+  if (check_dec(D)) return DEC_E_INVALID;
+  const decoder_config_t &c = D->c;
+  if (seq < 0 || seq >= c.max_batch) return fail(D, DEC_E_INVALID, "seq out of range");
+  if (n_steps < 1 || !d_tokens) return fail(D, DEC_E_INVALID, "decode_run needs n_steps >= 1 and d_tokens");
+  if (!D->has_next[seq]) return fail(D, DEC_E_INVALID, "no previous greedy token for this sequence");
+  if ((int64_t)D->len[seq] + n_steps > c.max_seq) return fail(D, DEC_E_CONTEXT_OVERFLOW, "decode_run past max_seq");
+  if (D->stats_mask) return fail(D, DEC_E_INVALID, "decode_run with node timers enabled");
+  if (!D->gstream) HIP_TRY(D, hipStreamCreateWithFlags(&D->gstream, hipStreamNonBlocking), "decode_run stream");
+  const int32_t pos0 = D->len[seq], last = pos0 + n_steps;
+  int rc = ensure_pages(D, 1, &seq, &last);
+  if (rc) return rc;
+  rc = stage_rows(D, 1, nullptr, &seq, &pos0);
+  if (rc) return rc;
+  HIP_TRY(D, hipMemsetAsync(D->gout, 0, 4, D->stream), "decode_run counter");
+  // everything before (the caller's work, the staged rows) is done before
+  // the capture stream starts
+  HIP_TRY(D, hipStreamSynchronize(D->stream), "decode_run sync");
+  // capture one step: attention splits sized for the run's last position
+  // (splits past a step's keys exit at once), positions read from row_pos
+  hipStream_t user = D->stream;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  D->stream = D->gstream;
+  hipError_t e = hipStreamBeginCapture(D->stream, hipStreamCaptureModeRelaxed);
+  if (e != hipSuccess) {
+    D->stream = user;
+    return hip_fail(D, e, "decode_run capture");
+  }
+  D->graph_mode = true;
+  rc = run_step(D, 1, 1, last - 1, &pos0, 1, 0, 1, nullptr, nullptr, 0);
+  e = rc ? hipSuccess : launch_decode_advance(D->row_pos, D->next_token, seq, D->gout, D->stream);
+  D->graph_mode = false;
+  const hipError_t ec = hipStreamEndCapture(D->stream, &graph);
+  D->stream = user;
+  if (rc || e != hipSuccess || ec != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    if (rc) return rc;
+    return hip_fail(D, e != hipSuccess ? e : ec, "decode_run capture");
+  }
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  for (int i = 0; e == hipSuccess && i < n_steps; ++i) e = hipGraphLaunch(exec, D->gstream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(d_tokens, D->gout + 1, (size_t)n_steps * 4, hipMemcpyDeviceToDevice, D->gstream);
+  // the graph is released only after its launches have drained
+  const hipError_t es = hipStreamSynchronize(D->gstream);
+  if (exec) (void)hipGraphExecDestroy(exec);
+  (void)hipGraphDestroy(graph);
+  if (e != hipSuccess || es != hipSuccess) return hip_fail(D, e != hipSuccess ? e : es, "decode_run");
+  D->len[seq] = last;
+  D->has_next[seq] = 1;
   return DEC_OK;
 }
 

@@ -191,6 +191,11 @@ struct QkNormArgs {
 };
 hipError_t launch_qk_norm_rope(const QkNormArgs &a, hipStream_t st);
 
+// One thread: out[1 + out[0]] = next_token[seq], out[0] += 1, row_pos[0] += 1
+// (the last node of a captured decode step).
+hipError_t launch_decode_advance(int32_t *row_pos, const int32_t *next_token, int seq, int32_t *out,
+                                 hipStream_t st);
+
 // Per-row int8 quantisation with a power-of-two scale: q [rows][K] int8,
 // scale [rows] fp32 (= 2^e), deq [rows][K] the dequantised bf16 weights.
 hipError_t launch_quantize_rows(const uint16_t *W, int64_t rows, int K, int8_t *q, float *scale, uint16_t *deq,

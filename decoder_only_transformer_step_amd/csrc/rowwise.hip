@@ -139,7 +139,24 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *W, i
   if (threadIdx.x == 0) scale[r] = s;
 }
 
+// The last node of a captured decode step: record the step's greedy token
+// and move the row to the next position (the next replay reads it there).
+__global__ __launch_bounds__(64) void decode_advance_kernel(int32_t *row_pos, const int32_t *next_token, int seq,
+                                                            int32_t *out) {
+  if (threadIdx.x != 0) return;
+  const int i = out[0];
+  out[1 + i] = next_token[seq];
+  out[0] = i + 1;
+  row_pos[0] += 1;
+}
+
 }  // namespace
+
+hipError_t launch_decode_advance(int32_t *row_pos, const int32_t *next_token, int seq, int32_t *out,
+                                 hipStream_t st) {
+  hipLaunchKernelGGL(decode_advance_kernel, dim3(1), dim3(64), 0, st, row_pos, next_token, seq, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_rows(const uint16_t *W, int64_t rows, int K, int8_t *q, float *scale, uint16_t *deq,
                                 hipStream_t st) {

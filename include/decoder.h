@@ -176,6 +176,20 @@ int prefill_chunk(decoder_t *dec, int32_t seq, const int32_t *ids, int32_t n,
 int decode_step(decoder_t *dec, int32_t batch, const int32_t *seqs, const int32_t *tokens,
                 float *d_logits, int32_t *d_argmax);
 
+/* n_steps greedy decode steps of sequence seq (batch 1), each feeding the
+ * previous step's greedy token, as decode_step(tokens = NULL) would; the n
+ * generated ids go to d_tokens ([n_steps] int32, device).  One step is
+ * captured into a HIP graph (positions read from device memory, attention
+ * splits sized for the run's last position) and replayed n_steps times,
+ * so the host does no work per step.  Captured on a stream of the
+ * library's own; the caller's stream is synchronised first.  Needs a
+ * previous greedy token (a call with logits, not followed by kv_truncate),
+ * len + n_steps <= max_seq (DEC_E_CONTEXT_OVERFLOW otherwise, or when a
+ * paged pool lacks the pages) and the node timers off.  Synchronous:
+ * returns after the steps have run.  No per-step logits.  d_tokens is
+ * borrowed, written only. */
+int decode_run(decoder_t *dec, int32_t seq, int32_t n_steps, int32_t *d_tokens);
+
 /* Forget sequence seq (-1: all sequences): its length becomes 0 and its KV
  * rows are zeroed (engine.zig Engine.reset). */
 int kv_reset(decoder_t *dec, int32_t seq);

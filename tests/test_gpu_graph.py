@@ -1,0 +1,79 @@
+"""decode_run: greedy decode steps replayed from one captured HIP graph.
+
+The captured step reads its position from device memory and is replayed
+once per token; between two runs the program does its own eager step.  Each
+generated token must be the oracle's greedy token wherever the oracle's
+top-2 margin exceeds 5e-2 (the oracle is fed the tokens the GPU produced),
+the last logits must meet the acceptance rule, and the eager decoder on the
+same inputs must agree with the graph-replayed one on those tokens.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from synth.weights import host_weights, prompt
+from synth.workloads import C8B, TINY
+from tests.gpu_util import MARGIN, assert_parity, compare_logits, decode, log, make_decoder, run_prefill
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def shapes():
+    from tests.test_gpu_parity import small_moe
+    return {
+        "tiny": (TINY, 16, 16),
+        "8b2": (C8B.with_(name="gqa-8b-layers-2", n_layers=2, vocab=1024, max_seq=512), 130, 128),
+        "moe": (small_moe(), 24, 32),
+    }
+
+
+@pytest.mark.parametrize("which", ["tiny", "8b2", "moe"])
+def test_decode_run_matches_oracle_and_eager(which):
+    shape, P, chunk = shapes()[which]
+    W = host_weights(shape)
+    ids = prompt(shape, P)
+    dec, _ = make_decoder(shape, W)
+    g0 = int(np.argmax(run_prefill(dec, ids, chunk)))   # the prefill's greedy token: step 0's input
+    n1, n2 = 6, 5
+    t1 = torch.full((n1,), -1, dtype=torch.int32, device="cuda")
+    dec.decode_run(0, n1, t1)
+    # an eager step between the two runs (feeds back the last greedy token)
+    am = torch.empty(1, dtype=torch.int32, device="cuda")
+    mid_logits = torch.empty((1, shape.vocab), dtype=torch.float32, device="cuda")
+    dec.decode_step([0], None, logits=mid_logits, argmax=am)
+    t2 = torch.full((n2,), -1, dtype=torch.int32, device="cuda")
+    dec.decode_run(0, n2, t2)
+    torch.cuda.synchronize()
+    assert dec.seq_len(0) == P + n1 + 1 + n2
+    got = [int(t) for t in t1.cpu().numpy()] + [int(am.cpu().numpy()[0])] + [int(t) for t in t2.cpu().numpy()]
+    inputs = [g0] + got[:-1]
+
+    # the oracle, fed the tokens the GPU generated: step i reads inputs[i] at
+    # position P + i and must emit got[i] wherever its margin is clear
+    m = oracle.Model(shape, W)
+    m.prefill(ids, chunk)
+    wants = []
+    for i, t in enumerate(got):
+        want = m.forward([inputs[i]], P + i)["logits"]
+        wants.append(want)
+        top2 = np.sort(want)[-2:]
+        if top2[1] - top2[0] > MARGIN:
+            assert t == oracle.argmax(want), f"{which} step {i}: {t} vs {oracle.argmax(want)}"
+        if i == n1:   # the eager step's logits
+            assert_parity(compare_logits(mid_logits.cpu().numpy()[0], want, f"{which} eager step"), which)
+    clear = sum(1 for w in wants if np.diff(np.sort(w)[-2:])[0] > MARGIN)
+    log(which, "decode_run tokens", got, "checked against the oracle:", clear)
+    assert clear >= 1
+
+    # an eager decoder fed the same tokens agrees where the margin is clear
+    eager, _ = make_decoder(shape, W)
+    run_prefill(eager, ids, chunk)
+    for i in range(len(got)):
+        _, ia = decode(eager, [0], [inputs[i]])
+        top2 = np.sort(wants[i])[-2:]
+        if top2[1] - top2[0] > MARGIN:
+            assert int(ia[0]) == got[i], f"{which} eager step {i}"
+    dec.close()
+    eager.close()
