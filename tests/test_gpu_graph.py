@@ -26,10 +26,15 @@ def shapes():
         "tiny": (TINY, 16, 16),
         "8b2": (C8B.with_(name="gqa-8b-layers-2", n_layers=2, vocab=1024, max_seq=512), 130, 128),
         "moe": (small_moe(), 24, 32),
+        # every option at once, the run crossing a page boundary (positions
+        # 120..131 over 32-position pages) with keys outside the window
+        "8b2-all": (C8B.with_(name="gqa-8b-layers-2-all", n_layers=2, vocab=1024, max_seq=512, weight_quant=1,
+                              sliding_window=100, attn_softcap=2.0, attn_sinks=True, qk_norm=True,
+                              kv_page_size=32, kv_pages=8), 120, 64),
     }
 
 
-@pytest.mark.parametrize("which", ["tiny", "8b2", "moe"])
+@pytest.mark.parametrize("which", ["tiny", "8b2", "moe", "8b2-all"])
 def test_decode_run_matches_oracle_and_eager(which):
     shape, P, chunk = shapes()[which]
     W = host_weights(shape)
@@ -67,8 +72,9 @@ def test_decode_run_matches_oracle_and_eager(which):
     log(which, "decode_run tokens", got, "checked against the oracle:", clear)
     assert clear >= 1
 
-    # an eager decoder fed the same tokens agrees where the margin is clear
-    eager, _ = make_decoder(shape, W)
+    # an eager decoder fed the same tokens (contiguous cache) agrees where
+    # the margin is clear
+    eager, _ = make_decoder(shape.with_(kv_page_size=0, kv_pages=0), W)
     run_prefill(eager, ids, chunk)
     for i in range(len(got)):
         _, ia = decode(eager, [0], [inputs[i]])
