@@ -183,11 +183,13 @@ int decode_step(decoder_t *dec, int32_t batch, const int32_t *seqs, const int32_
  * splits sized for the run's last position) and replayed n_steps times,
  * so the host does no work per step.  Captured on a stream of the
  * library's own; the caller's stream is synchronised first.  Needs a
- * previous greedy token (a call with logits, not followed by kv_truncate),
- * len + n_steps <= max_seq (DEC_E_CONTEXT_OVERFLOW otherwise, or when a
- * paged pool lacks the pages) and the node timers off.  Synchronous:
- * returns after the steps have run.  No per-step logits.  d_tokens is
- * borrowed, written only. */
+ * previous greedy token (a decode_step, or a prefill_chunk with
+ * logits_mode > 0, not followed by kv_truncate or kv_reset), len + n_steps
+ * <= max_seq (DEC_E_CONTEXT_OVERFLOW otherwise, or when a paged pool lacks
+ * the pages) and the node timers off; these are checked before anything
+ * runs.  Synchronous: returns after the steps have run.  No per-step
+ * logits.  d_tokens is borrowed, written only.  A DEC_E_HIP error after the
+ * checks leaves the sequence's cache and greedy token undefined: reset it. */
 int decode_run(decoder_t *dec, int32_t seq, int32_t n_steps, int32_t *d_tokens);
 
 /* Forget sequence seq (-1: all sequences): its length becomes 0 and its KV

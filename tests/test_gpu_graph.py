@@ -83,3 +83,42 @@ def test_decode_run_matches_oracle_and_eager(which):
             assert int(ia[0]) == got[i], f"{which} eager step {i}"
     dec.close()
     eager.close()
+
+
+def test_decode_run_refusals_change_nothing():
+    """Calls decode_run must refuse: no previous greedy token (after a
+    rollback), a run past max_seq, node timers on, n_steps < 1.  Each is
+    refused before anything runs; the sequence then still decodes as an
+    untouched one would."""
+    from decoder_only_transformer_step_amd.binding import DecoderError
+    shape = TINY
+    W = host_weights(shape)
+    ids = prompt(shape, 16)
+    dec, _ = make_decoder(shape, W)
+    ref, _ = make_decoder(shape, W)
+    for d in (dec, ref):
+        run_prefill(d, ids, 16)
+    toks = torch.zeros(shape.max_seq, dtype=torch.int32, device="cuda")
+    with pytest.raises(DecoderError):
+        dec.decode_run(0, shape.max_seq - 16 + 1, toks)      # past max_seq
+    with pytest.raises(DecoderError):
+        dec.decode_run(0, 0, toks)
+    dec.stats_enable()
+    with pytest.raises(DecoderError):
+        dec.decode_run(0, 2, toks)
+    dec.stats_enable(())
+    assert dec.seq_len(0) == 16
+    a = decode(dec, [0], None)
+    b = decode(ref, [0], None)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    dec.kv_truncate(0, 17)                                   # forgets the greedy token
+    with pytest.raises(DecoderError):
+        dec.decode_run(0, 2, toks)
+    # a run that ends exactly at max_seq is accepted
+    dec.kv_truncate(0, 16)
+    decode(dec, [0], [int(ids[-1])])
+    n = shape.max_seq - dec.seq_len(0)
+    dec.decode_run(0, n, toks)
+    assert dec.seq_len(0) == shape.max_seq
+    dec.close()
+    ref.close()
