@@ -366,7 +366,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not supported: "
-              "this build runs the whole step on a single MI355X", file=sys.stderr)
+              "the library runs the whole step on a single MI355X (no sharding across GPUs)", file=sys.stderr)
         return 2
 
     import torch
