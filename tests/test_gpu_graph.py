@@ -26,6 +26,7 @@ def shapes():
         "tiny": (TINY, 16, 16),
         "8b2": (C8B.with_(name="gqa-8b-layers-2", n_layers=2, vocab=1024, max_seq=512), 130, 128),
         "moe": (small_moe(), 24, 32),
+        "moe-q8": (small_moe().with_(name="moe-small-q8", weight_quant=1), 24, 32),
         # every option at once, the run crossing a page boundary (positions
         # 120..131 over 32-position pages) with keys outside the window
         "8b2-all": (C8B.with_(name="gqa-8b-layers-2-all", n_layers=2, vocab=1024, max_seq=512, weight_quant=1,
@@ -34,7 +35,7 @@ def shapes():
     }
 
 
-@pytest.mark.parametrize("which", ["tiny", "8b2", "moe", "8b2-all"])
+@pytest.mark.parametrize("which", ["tiny", "8b2", "moe", "moe-q8", "8b2-all"])
 def test_decode_run_matches_oracle_and_eager(which):
     shape, P, chunk = shapes()[which]
     W = host_weights(shape)

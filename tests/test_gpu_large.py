@@ -18,7 +18,7 @@ import pytest
 import oracle
 from synth.weights import host_kv, host_weights, prompt
 from synth.workloads import C135M, C8B, LONGCTX, MOE
-from tests.gpu_util import assert_parity, compare_logits, decode, log, make_decoder, run_prefill
+from tests.gpu_util import MARGIN, assert_parity, compare_logits, decode, log, make_decoder, run_prefill
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -49,6 +49,7 @@ def teacher_forced(dec, m, start_logits, pos, steps, what, moe_shape=None, cones
         else:
             assert_parity(st, f"{what} decode {i}")
         last = want["logits"]
+    return last
 
 
 def route_mismatch_ok(got, ref, probs, k, tie=1e-3):
@@ -110,7 +111,28 @@ def test_135m_full_prompt_and_decode():
     st = compare_logits(got, want, "135m prefill")
     log("135m prefill", st)
     assert_parity(st, "135m prefill")
-    teacher_forced(dec, m, want, 512, 24, "135m")
+    last = teacher_forced(dec, m, want, 512, 24, "135m")
+    # then graph-replayed greedy decode (decode_run) at full size: each
+    # token equals the oracle's wherever its top-2 margin exceeds 5e-2
+    t = oracle.argmax(last)
+    want = m.forward([t], 536)["logits"]
+    lg, am = decode(dec, [0], [t])
+    assert_parity(compare_logits(lg[0], want, "135m decode 24"), "135m decode 24")
+    n = 12
+    toks = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    dec.decode_run(0, n, toks)
+    torch.cuda.synchronize()
+    got = [int(x) for x in toks.cpu().numpy()]
+    inputs = [int(am[0])] + got[:-1]
+    clear = 0
+    for i in range(n):
+        w = m.forward([inputs[i]], 537 + i)["logits"]
+        top2 = np.sort(w)[-2:]
+        if top2[1] - top2[0] > MARGIN:
+            assert got[i] == oracle.argmax(w), f"135m decode_run step {i}"
+            clear += 1
+    log("135m decode_run tokens", got, "checked against the oracle:", clear)
+    assert clear >= 1
 
 
 def test_8b_chunk_and_decode(w8b):
