@@ -123,3 +123,31 @@ def test_decode_run_refusals_change_nothing():
     assert dec.seq_len(0) == shape.max_seq
     dec.close()
     ref.close()
+
+
+def test_decode_run_on_a_caller_stream():
+    """A decoder on a caller's (non-default) stream: the prefill is only
+    enqueued there when decode_run starts, so the run must order itself
+    after it.  Tokens equal those of the same run on the default stream."""
+    from decoder_only_transformer_step_amd import Decoder
+    from synth.device import upload_weights
+    shape, P, chunk = shapes()["8b2"]
+    W = host_weights(shape)
+    ids = [int(t) for t in prompt(shape, P)]
+    dw = upload_weights(W)
+    torch.cuda.synchronize()                # the uploads ran on the default stream
+    out = []
+    for stream in (torch.cuda.Stream(), None):
+        dec = Decoder(shape, dw, stream=stream)
+        torch.cuda.synchronize()
+        logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+        for c0 in range(0, P, chunk):
+            part = ids[c0:c0 + chunk]
+            dec.prefill_chunk(0, part, c0, logits_mode=1, logits=logits)
+        toks = torch.full((8,), -1, dtype=torch.int32, device="cuda")
+        dec.decode_run(0, 8, toks)          # no host synchronisation before it
+        torch.cuda.synchronize()
+        out.append([int(t) for t in toks.cpu().numpy()])
+        dec.close()
+    log("caller-stream decode_run", out[0], "default stream", out[1])
+    assert out[0] == out[1]
