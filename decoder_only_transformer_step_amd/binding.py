@@ -79,6 +79,7 @@ SIGNATURES = {
     "dec_diag_moe_route": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "decoder_debug_layer_limit": (ctypes.c_int, [_P, _I32]),
     "decoder_debug_read_x": (ctypes.c_int, [_P, _P, _I32]),
+    "decoder_debug_stop_after_attention": (ctypes.c_int, [_P, _I32]),
     "decoder_debug_read_routes": (ctypes.c_int, [_P, _P, _I32]),
     "decoder_stats_enable": (ctypes.c_int, [_P, _I32]),
     "decoder_stats_read": (ctypes.c_int, [_P, ctypes.POINTER(DecoderStats)]),
@@ -251,6 +252,9 @@ class Decoder:
 
     def debug_layer_limit(self, layers):
         _check(lib().decoder_debug_layer_limit(self.handle, layers), self.handle, "layer_limit")
+
+    def debug_stop_after_attention(self, on):
+        _check(lib().decoder_debug_stop_after_attention(self.handle, int(on)), self.handle, "stop_after_attention")
 
     def debug_read_x(self, out, rows):
         _check(lib().decoder_debug_read_x(self.handle, _ptr(out), rows), self.handle, "read_x")

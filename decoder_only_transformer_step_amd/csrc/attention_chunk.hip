@@ -278,10 +278,11 @@ hipError_t launch_d(AttnArgs a, hipStream_t st) {
   int ns = std::max(1, 256 / a.n_groups);
   int kc = std::max(128, (int)(((keys + ns - 1) / ns + 31) / 32 * 32));
   ns = (keys + kc - 1) / kc;
-  while ((int64_t)a.n_groups * ns > AC_MAX_TASKS) {
+  while ((int64_t)a.n_groups * ns > AC_MAX_TASKS && ns > 1) {
     kc *= 2;
     ns = (keys + kc - 1) / kc;
   }
+  if ((int64_t)a.n_groups * ns > AC_MAX_TASKS) return hipErrorInvalidValue;
   a.kc = kc;
   a.n_splits = ns;
   if (a.pt) hipLaunchKernelGGL((attn_chunk_kernel<D, true>), dim3(a.n_groups * ns), dim3(256), 0, st, a, rpb);
@@ -295,8 +296,11 @@ hipError_t launch_d(AttnArgs a, hipStream_t st) {
 }  // namespace
 
 bool attention_chunk_fits(const AttnArgs &a, int head_dim) {
+  // (the block count with one split must fit the partial buffers; larger
+  // work lists take the general attention kernel)
   return a.pos_mode == 2 && a.out != nullptr && a.out_f32 == nullptr && (head_dim == 64 || head_dim == 128) &&
-         a.G >= 1 && a.G <= AC_COLS && a.S % 32 == 0;
+         a.G >= 1 && a.G <= AC_COLS && a.S % 32 == 0 &&
+         (int64_t)((a.rows + AC_COLS / a.G - 1) / (AC_COLS / a.G)) * a.Hkv <= AC_MAX_TASKS;
 }
 
 hipError_t launch_attention_chunk(const AttnArgs &a, int head_dim, hipStream_t st) {

@@ -128,6 +128,15 @@ bool config_ok(const decoder_config_t *c) {
   if (c->hidden <= 0 || c->hidden % 8 || c->n_layers <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0)
     return false;
   if (c->n_heads % c->n_kv_heads || c->n_heads / c->n_kv_heads > 16) return false;
+  // attention work lists: a decode batch has max_batch x Hkv (row, kv head)
+  // groups, a prefill chunk ceil(max_chunk / (16 / G)) x Hkv; each must fit
+  // the split partial buffers with at least one split
+  {
+    const int64_t G = c->n_heads / c->n_kv_heads, rpg = 16 / G;
+    if ((int64_t)c->max_batch * c->n_kv_heads > ATTN_MAX_TASKS ||
+        ((int64_t)c->max_chunk + rpg - 1) / rpg * c->n_kv_heads > ATTN_MAX_TASKS)
+      return false;
+  }
   if (c->head_dim != 64 && c->head_dim != 128) return false;
   if (c->vocab <= 0 || c->max_seq <= 0 || c->max_chunk <= 0 || c->max_chunk > 256 ||
       c->max_batch <= 0 || c->max_batch > 256)
@@ -281,6 +290,8 @@ struct decoder {
   std::vector<char> has_next;
   std::vector<std::vector<int32_t>> kv_pending;  // per seq: layers loaded with the pending len
   int layer_limit = -1;
+  bool stop_after_attn = false;  // the last layer run stops after o_proj + residual
+  int stop_mid_layer = -1;       // that layer, for the current step (-1: none)
   int last_rows = 0;
   int32_t *pinned = nullptr;
   // paged KV cache: device page table [max_batch][mp] (staged with the rows),
@@ -595,10 +606,11 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
   int ns = std::max(1, (ATTN_TARGET_BLOCKS + a.n_groups - 1) / a.n_groups);
   int kc = (int)align_up((size_t)((keys + ns - 1) / ns), 128);
   ns = (keys + kc - 1) / kc;
-  while ((int64_t)a.n_groups * ns > ATTN_MAX_TASKS) {
+  while ((int64_t)a.n_groups * ns > ATTN_MAX_TASKS && ns > 1) {
     kc *= 2;
     ns = (keys + kc - 1) / kc;
   }
+  if ((int64_t)a.n_groups * ns > ATTN_MAX_TASKS) return fail(D, DEC_E_INVALID, "attention work list too long");
   a.kc = kc;
   a.n_splits = ns;
   hipError_t e = attention_chunk_fits(a, c.head_dim) ? launch_attention_chunk(a, c.head_dim, D->stream)
@@ -726,6 +738,7 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
   if (!c.qk_norm && (rc = gemv(D, DEC_NODE_QKV, EPI_QKV, quant(D, q, l, 0)))) return rc;
   if ((rc = attention(D, l, 1, 1, max_pos, hpos, D->f32_attn))) return rc;
   if ((rc = gemv(D, DEC_NODE_O, EPI_ADD, quant(D, gemv_args(W.w_o, D->f32_attn, qd, H, D->x), l, 1)))) return rc;
+  if (l == D->stop_mid_layer) return DEC_OK;
 
   if (c.n_experts == 0) {
     const int I = c.ffn_inter;
@@ -861,6 +874,7 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   o.C = D->x;
   o.ldc = H;
   if ((rc = proj(D, DEC_NODE_O, EPI_ADD, o, rows))) return rc;
+  if (l == D->stop_mid_layer) return DEC_OK;
 
   if (c.n_experts == 0) {
     const int I = c.ffn_inter;
@@ -996,6 +1010,7 @@ int run_step(decoder *D, int rows, int rows_per_group, int max_pos, const int32_
   }
   if (e != hipSuccess) return hip_fail(D, e, "embed");
   const int nl = D->layer_limit >= 0 ? std::min(D->layer_limit, c.n_layers) : c.n_layers;
+  D->stop_mid_layer = D->stop_after_attn ? nl - 1 : -1;
   for (int l = 0; l < nl; ++l) {
     int rc = run_layer(D, l, rows, rows_per_group, max_pos, hpos);
     if (rc) return rc;
@@ -1583,6 +1598,12 @@ int decoder_stats_read(decoder_t *D, decoder_stats_t *out) {
 int decoder_debug_layer_limit(decoder_t *D, int32_t layers) {
   if (check_dec(D)) return DEC_E_INVALID;
   D->layer_limit = layers;
+  return DEC_OK;
+}
+
+int decoder_debug_stop_after_attention(decoder_t *D, int32_t on) {
+  if (check_dec(D) || (on != 0 && on != 1)) return DEC_E_INVALID;
+  D->stop_after_attn = on != 0;
   return DEC_OK;
 }
 

@@ -16,7 +16,9 @@
 //    weight fragment feeds MT MFMAs (v_mfma_f32_16x16x32_bf16, fp32 acc).
 //  * A comes from global memory (L2-resident), or, for decode, is built once
 //    per block in LDS by the fused RMSNorm prologue (engine.zig rmsnormColumn:
-//    x / sqrt(mean(x^2) + eps) * g, fp32, rounded to bf16 as the MFMA input).
+//    x / sqrt(mean(x^2) + eps) * g, in fp32, then stored as split bf16: a hi
+//    plane bf16(v) and a lo plane bf16(v - hi), each multiplied by the
+//    weight fragment, so the MFMA input keeps about 16 mantissa bits).
 //  * The NW partial tiles are summed in LDS in fixed wave order
 //    (deterministic); the epilogue (store / residual add / SwiGLU / bias +
 //    RoPE + KV append / logits with per-tile argmax candidates) runs on 256
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_kernel(GemmArgs g) {
 
   if (AMODE == 2) {
     // fused RMSNorm prologue (rows <= 16): per-row 1/rms in fixed order, then
-    // the normalised bf16 rows into LDS
+    // the normalised rows into LDS as split bf16 (hi plane, then lo plane)
     const int K = g.K;
     for (int m = 0; m < rows; ++m) {
       const float *xr = g.x + (int64_t)m * g.lda;

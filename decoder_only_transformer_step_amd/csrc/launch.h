@@ -81,7 +81,8 @@ int gemv_blocks(int n_items);
 hipError_t launch_gemv(const GemvArgs &g, int epi, hipStream_t st, int *blocks = nullptr);
 
 // idx[r] = argmax over part_val[r][0 .. nparts) (lowest index on ties), and
-// next_token[row_seq[r]] = idx[r] for the last row of each sequence
+// next_token[row_seq[r]] = idx[r] for the last row of each run of rows with
+// equal row_seq (callers keep a sequence's rows consecutive)
 hipError_t launch_argmax_finalize(const float *part_val, const int32_t *part_idx, int nparts, int rows,
                                   int32_t *idx, int32_t *next_token, const int32_t *row_seq,
                                   hipStream_t st);

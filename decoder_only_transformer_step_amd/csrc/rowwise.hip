@@ -188,8 +188,10 @@ hipError_t launch_rmsnorm(const float *x, int64_t ldx, const float *g, int rows,
 
 // Greedy argmax over per-tile candidates (value, index) of one row, lowest
 // index on ties (the strict '>' scans of engine.zig's MoE prefill test and
-// pipeline.rs ppl_ids).  Rows are processed in order, so when several rows of
-// one sequence are reduced in a launch the last row's token is the one kept.
+// pipeline.rs ppl_ids).  Rows of one sequence are consecutive (a prefill
+// chunk, or one row per sequence in a decode batch); blocks reduce rows in
+// parallel, so only the last row of each run of equal sequences writes that
+// sequence's next token.
 namespace {
 constexpr int FIN_BATCH = 16;
 
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(1024) void argmax_finalize_kernel(const float *pv, 
         }
       if (bi == 0x7fffffff) bi = 0;
       if (idx) idx[r] = bi;
-      if (next_token) next_token[row_seq[r]] = bi;
+      if (next_token && (r == rows - 1 || row_seq[r + 1] != row_seq[r])) next_token[row_seq[r]] = bi;
     }
     __syncthreads();
   }

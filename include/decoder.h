@@ -37,6 +37,12 @@
  *    table and all scratch inside it and never allocates device memory.
  *  - Token ids and sequence indices are HOST arrays (validated on the host
  *    before anything is launched).  Output buffers are DEVICE pointers.
+ *    Host ids are a deliberate choice over device id arrays: the checks that
+ *    refuse a bad call before anything runs (ids in [0, vocab), distinct
+ *    sequences, lengths against max_seq, pages available) and the sizing of
+ *    the attention splits need the values on the host, and they reach the
+ *    device in one pinned copy per call.  Greedy decode keeps its tokens on
+ *    the device (decode_step with tokens = NULL, decode_run).
  *  - Every call is asynchronous on the decoder's stream; only the returned
  *    status is synchronous.  Outputs are valid once the stream has drained.
  *  - A failing call returns a nonzero DEC_E_* code and launches nothing
@@ -140,13 +146,24 @@ typedef struct {
 } decoder_weights_t;
 
 /* Bytes of device workspace decoder_init needs for this config (KV cache,
- * RoPE table, activations and scratch), or 0 if the config is invalid. */
+ * RoPE table, activations and scratch), or 0 if the config is invalid.
+ * pipeline.rs ForwardScratch: the forward pass's buffers are allocated once,
+ * sized from the model, and reused by every steady-state step; here that
+ * one allocation is the caller's (engine.zig Engine.init sizes its KV
+ * cache and activation buffers from the config in the same way).  Pure
+ * host arithmetic: nothing is launched or allocated. */
 size_t decoder_workspace_bytes(const decoder_config_t *cfg);
 
 /* Validate the config, record the borrowed weights, lay out the workspace
  * (256-byte aligned; its contents are overwritten), upload the RoPE table
  * and zero the KV cache.  stream is a hipStream_t (NULL = default stream).
- * On success *out owns host-side state only; free it with decoder_free. */
+ * On success *out owns host-side state only; free it with decoder_free.
+ * engine.zig Engine.init: validate the config first, then build everything
+ * a step needs from the borrowed layer weights, so that no later step has
+ * to allocate.  Errors: DEC_E_INVALID (bad config, a required weight
+ * pointer NULL), DEC_E_WORKSPACE (workspace NULL, misaligned or smaller
+ * than decoder_workspace_bytes), DEC_E_HIP (a copy or launch of the set-up
+ * failed; nothing is kept and *out stays NULL). */
 int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *weights,
                  void *d_workspace, size_t workspace_bytes, void *stream, decoder_t **out);
 
@@ -172,11 +189,23 @@ int prefill_chunk(decoder_t *dec, int32_t seq, const int32_t *ids, int32_t n,
  * forwards one token at position len[seq] and appends it to its cache.
  * tokens: host [batch] ids, or NULL to feed each sequence's own previous
  * greedy token (kept on the device; no host round trip).  d_logits
- * ([batch][V] fp32) and d_argmax ([batch] int32) may each be NULL. */
+ * ([batch][V] fp32) and d_argmax ([batch] int32) may each be NULL.
+ * engine.zig Engine.forward: one decode step for a token at a position,
+ * refused with a context-overflow error when the position has no cache row;
+ * pipeline.rs module doc: decode rows of several sequences share one pass
+ * over the weights, attention reads each sequence's own cache.  Errors:
+ * DEC_E_INVALID (batch outside [1, max_batch], a seq out of range or
+ * repeated, tokens NULL for a sequence with no previous greedy token),
+ * DEC_E_TOKEN (an id outside [0, vocab)), DEC_E_CONTEXT_OVERFLOW (a
+ * sequence already holds max_seq positions, or a paged pool has no page
+ * left); nothing is launched on these.  DEC_E_HIP: a launch failed. */
 int decode_step(decoder_t *dec, int32_t batch, const int32_t *seqs, const int32_t *tokens,
                 float *d_logits, int32_t *d_argmax);
 
-/* n_steps greedy decode steps of sequence seq (batch 1), each feeding the
+/* pipeline.rs Pipeline::generate_from_ids (its greedy loop: each step feeds
+ * the previous step's argmax back in; decoder.rs folds the argmax into the
+ * lm-head so only the token id leaves the device):
+ * n_steps greedy decode steps of sequence seq (batch 1), each feeding the
  * previous step's greedy token, as decode_step(tokens = NULL) would; the n
  * generated ids go to d_tokens ([n_steps] int32, device).  One step is
  * captured into a HIP graph (positions read from device memory, attention
@@ -193,7 +222,10 @@ int decode_step(decoder_t *dec, int32_t batch, const int32_t *seqs, const int32_
 int decode_run(decoder_t *dec, int32_t seq, int32_t n_steps, int32_t *d_tokens);
 
 /* Forget sequence seq (-1: all sequences): its length becomes 0 and its KV
- * rows are zeroed (engine.zig Engine.reset). */
+ * rows are zeroed (engine.zig Engine.reset: forget the KV cache to start a
+ * new conversation).  A paged cache returns the sequence's pages to the
+ * pool instead of zeroing them.  DEC_E_INVALID for seq outside
+ * [-1, max_batch); DEC_E_HIP if the clearing launch fails. */
 int kv_reset(decoder_t *dec, int32_t seq);
 
 /* Roll sequence seq back to its first len cached positions
@@ -209,19 +241,34 @@ int kv_truncate(decoder_t *dec, int32_t seq, int32_t len);
  * buffers d_k, d_v, both bf16 [Hkv][len][d] (keys already rotated).  The
  * sequence's length becomes len once every layer has been loaded with the
  * same len (call in any layer order; the length is set on the last layer).
- * decoder.rs: restoring a prefix into a resident device KV. */
+ * decoder.rs (its per-layer device-resident KV: a prefix restore uploads
+ * host K/V rows into it).  DEC_E_INVALID: bad seq, layer or pointer,
+ * len < 0, or a paged cache; DEC_E_CONTEXT_OVERFLOW: len > max_seq. */
 int kv_load(decoder_t *dec, int32_t seq, int32_t layer, const uint16_t *d_k,
             const uint16_t *d_v, int32_t len);
 
-/* Current length (cached positions) of sequence seq, or -1 if seq is invalid. */
+/* Current length (cached positions) of sequence seq, or -1 if seq is invalid.
+ * decoder.rs: a prefill must start at the cache's current position count
+ * (start_pos equal to cache.positions()); this reports that count. */
 int32_t decoder_seq_len(const decoder_t *dec, int32_t seq);
 
-/* Replace the stream all later calls launch on (hipStream_t). */
+/* Replace the stream all later calls launch on (hipStream_t).  Stream
+ * plumbing only; no passage of the pages defines an operation here (their
+ * engines run on one queue of their own).  Always DEC_OK for a live
+ * decoder; DEC_E_INVALID for NULL. */
 int decoder_set_stream(decoder_t *dec, void *stream);
 
+/* engine.zig Engine.deinit: release what init made.  Waits for the stream,
+ * then frees the host state, pinned staging memory and events; the
+ * caller's workspace and the borrowed weights stay the caller's.  NULL is a
+ * no-op. */
 void decoder_free(decoder_t *dec);
+/* Static text for a DEC_* code ("unknown error" for others). */
 const char *decoder_strerror(int code);
-/* Text of the last failure on this decoder (empty if none). */
+/* Text of the last failure on this decoder (empty if none), naming the
+ * check or the HIP call and its error string: engine.zig prints why a
+ * kernel build failed instead of a bare error code.  Valid until the next
+ * call on the same decoder. */
 const char *decoder_last_error(const decoder_t *dec);
 
 #ifdef __cplusplus

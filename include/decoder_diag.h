@@ -71,6 +71,14 @@ int dec_diag_moe_route(const float *d_logits, int32_t rows, int32_t E, int32_t k
  * final norm and lm-head still run (engine.zig Engine.stopAfterLayer). */
 int decoder_debug_layer_limit(decoder_t *dec, int32_t layers);
 
+/* on = 1: the last layer that later calls run (the layer limit's last, or
+ * the model's last) stops after its attention sub-block, o_proj and the
+ * residual add included, so decoder_debug_read_x returns that layer's FFN
+ * input before its RMSNorm (the residual the router and the experts read).
+ * engine.zig Engine.stopAfterLayer, taken to the sub-block inside a layer.
+ * on = 0 restores full layers.  DEC_E_INVALID for other values. */
+int decoder_debug_stop_after_attention(decoder_t *dec, int32_t on);
+
 /* Copy the residual stream x (fp32 [rows][H]) left by the last prefill_chunk
  * or decode_step (row i = token i of the chunk, or batch entry i) to d_out. */
 int decoder_debug_read_x(decoder_t *dec, float *d_out, int32_t rows);

@@ -88,3 +88,13 @@ def test_variant_configs_and_their_workspace():
     assert binding.decoder_workspace_bytes(binding.make_config(moe.with_(weight_quant=1, expert_inter=1400))) == 0
     for kw in (dict(sliding_window=8), dict(attn_softcap=30.0), dict(qk_norm=True)):
         assert binding.decoder_workspace_bytes(binding.make_config(tiny.with_(**kw))) == base
+
+
+def test_attention_work_list_bounds():
+    """Configs whose attention work lists cannot fit the split buffers (a
+    decode batch of max_batch x n_kv_heads groups, or a prefill chunk's row
+    groups x n_kv_heads) are refused up front instead of failing at a step."""
+    tiny = WORKLOADS["tiny"][0]
+    wide = tiny.with_(n_heads=64, n_kv_heads=64, head_dim=64)
+    assert binding.decoder_workspace_bytes(binding.make_config(wide.with_(max_batch=128))) > 0   # 8192 groups
+    assert binding.decoder_workspace_bytes(binding.make_config(wide.with_(max_batch=129))) == 0

@@ -259,37 +259,68 @@ def small_moe():
 
 
 def test_moe_small_parity_and_routes():
+    from tests.moe_routes import check_routes_exact
     shape = small_moe()
     W = host_weights(shape)
-    ids = prompt(shape, 24)
+    ids = [int(t) for t in prompt(shape, 24)]
     m = oracle.Model(shape, W)
-    want = m.forward(ids, 0, routes=True, probs=True)
+    want = m.forward(ids, 0)
     dec, _ = make_decoder(shape, W)
     logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
-    dec.prefill_chunk(0, [int(t) for t in ids], 0, logits_mode=1, logits=logits)
-    routes = torch.empty((shape.n_layers, 24, shape.top_k), dtype=torch.int32, device="cuda")
-    dec.debug_read_routes(routes, 24)
+
+    def prefill():
+        dec.kv_truncate(0, 0)
+        dec.prefill_chunk(0, ids, 0, logits_mode=1, logits=logits)
+
+    prefill()
     torch.cuda.synchronize()
     st = compare_logits(logits.cpu().numpy(), want["logits"], "moe prefill")
     log("moe prefill", st)
     assert_parity(st, "moe prefill")
-    got_r = routes.cpu().numpy()
-    mism = np.argwhere(got_r != want["routes"])
-    for l, i, j in mism:
-        p = np.sort(want["probs"][l, i])[::-1]
-        gap = (p[shape.top_k - 1] - p[shape.top_k]) / p[shape.top_k - 1]
-        assert gap < 1e-4, f"route mismatch at layer {l} token {i} with gap {gap:.2e}"
-    # decode steps, teacher-forced
+    check_routes_exact(dec, shape, W, 24, prefill, "moe prefill")
+    # decode steps, teacher-forced, routes checked on the GEMV path too
     for step in range(4):
         t = oracle.argmax(want["logits"])
-        want = m.forward([t], 24 + step, routes=True, probs=True)
+        want = m.forward([t], 24 + step)
         lg, _ = decode(dec, [0], [t])
         st = compare_logits(lg[0], want["logits"], f"moe decode {step}")
         assert_parity(st, f"moe decode {step}")
-        dec.debug_read_routes(routes, 1)
+        check_routes_exact(dec, shape, W, 1,
+                           lambda: (dec.kv_truncate(0, 24 + step), decode(dec, [0], [t])),
+                           f"moe decode {step}")
+
+
+def test_moe_small_multi_chunk_prefill():
+    """A 40-token prompt in chunks of 16, 16 and 8 (max_chunk 16): the later
+    chunks attend to the cached rows of the earlier ones and route their
+    own rows; logits after every chunk and the routes of every chunk are
+    checked, then decode continues."""
+    from tests.moe_routes import check_routes_exact
+    shape = small_moe().with_(max_chunk=16)
+    W = host_weights(shape)
+    ids = [int(t) for t in prompt(shape, 40, seq=3)]
+    m = oracle.Model(shape, W)
+    dec, _ = make_decoder(shape, W)
+    logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    for c0 in range(0, 40, 16):
+        part = ids[c0:c0 + 16]
+        want = m.forward(part, c0)
+
+        def run(c0=c0, part=part):
+            dec.kv_truncate(0, c0)
+            dec.prefill_chunk(0, part, c0, logits_mode=1, logits=logits)
+
+        run()
         torch.cuda.synchronize()
-        r1 = routes.cpu().numpy().reshape(-1)[: shape.n_layers * shape.top_k].reshape(shape.n_layers, shape.top_k)
-        assert np.array_equal(r1, want["routes"][:, 0, :])
+        st = compare_logits(logits.cpu().numpy(), want["logits"], f"moe chunk at {c0}")
+        log("moe chunk at", c0, st)
+        assert_parity(st, f"moe chunk at {c0}")
+        check_routes_exact(dec, shape, W, len(part), run, f"moe chunk at {c0}")
+    for step in range(3):
+        t = oracle.argmax(want["logits"])
+        want = m.forward([t], 40 + step)
+        lg, _ = decode(dec, [0], [t])
+        assert_parity(compare_logits(lg[0], want["logits"], f"moe decode {step}"), f"moe decode {step}")
 
 
 @pytest.mark.parametrize("N,K", [(16, 32), (60, 2048), (100, 688), (777, 4096), (4096, 14336)])

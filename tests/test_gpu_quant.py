@@ -79,37 +79,37 @@ def test_quantized_model_prefill_and_decode(which):
 def test_quantized_moe_prefill_decode_and_routes():
     """int8 routed and shared experts (the grouped expert GEMV streams each
     chosen expert's codes with that expert's row scales): the small MoE
-    model's logits and expert ids against the oracle on the same quantised
-    weights (route differences only at near-ties of the k-th expert)."""
+    model's logits against the oracle on the same quantised weights, and its
+    expert ids layer by layer on the GPU's own router input."""
+    from tests.moe_routes import check_routes_exact
     from tests.test_gpu_parity import small_moe
     shape = small_moe().with_(name="moe-small-q8", weight_quant=1)
     W = host_weights(shape)
-    ids = prompt(shape, 24)
+    ids = [int(t) for t in prompt(shape, 24)]
     m = oracle.Model(shape, W)
-    want = m.forward(ids, 0, routes=True, probs=True)
+    want = m.forward(ids, 0)
     plain = oracle.Model(shape.with_(weight_quant=0), W).forward(ids, 0)["logits"]
     assert np.abs(plain - want["logits"]).max() > 1e-3
     dec, _ = make_decoder(shape, W)
     logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
-    dec.prefill_chunk(0, [int(t) for t in ids], 0, logits_mode=1, logits=logits)
+
+    def prefill():
+        dec.kv_truncate(0, 0)
+        dec.prefill_chunk(0, ids, 0, logits_mode=1, logits=logits)
+
+    prefill()
     torch.cuda.synchronize()
     st = compare_logits(logits.cpu().numpy(), want["logits"], "moe q8 prefill")
     log("moe q8 prefill", st)
     assert_parity(st, "moe q8 prefill")
-    routes = torch.empty((shape.n_layers, 24, shape.top_k), dtype=torch.int32, device="cuda")
+    check_routes_exact(dec, shape, W, 24, prefill, "moe q8 prefill")
     for step in range(4):
         t = oracle.argmax(want["logits"])
-        want = m.forward([t], 24 + step, routes=True, probs=True)
+        want = m.forward([t], 24 + step)
         lg, _ = decode(dec, [0], [t])
         st = compare_logits(lg[0], want["logits"], f"moe q8 decode {step}")
         log("moe q8 decode", step, st)
         assert_parity(st, f"moe q8 decode {step}")
-        dec.debug_read_routes(routes, 1)
-        torch.cuda.synchronize()
-        r1 = routes.cpu().numpy().reshape(-1)[: shape.n_layers * shape.top_k].reshape(shape.n_layers, shape.top_k)
-        for l in range(shape.n_layers):
-            if not np.array_equal(r1[l], want["routes"][l, 0]):
-                p = np.sort(want["probs"][l, 0])[::-1]
-                gap = (p[shape.top_k - 1] - p[shape.top_k]) / p[shape.top_k - 1]
-                assert gap < 1e-4, f"route mismatch at layer {l} with gap {gap:.2e}"
+        check_routes_exact(dec, shape, W, 1, lambda: (dec.kv_truncate(0, 24 + step), decode(dec, [0], [t])),
+                           f"moe q8 decode {step}")
     dec.close()

@@ -93,3 +93,26 @@ def test_rollback_then_decode_matches_oracle(models, which, keep):
     assert_parity(st, f"{which} rollback keep {keep}")
     assert dec.seq_len(0) == P + keep + 1
     dec.close()
+
+
+@pytest.mark.parametrize("which", ["tiny", "8b2"])
+def test_accepted_verify_feeds_its_last_greedy_token(models, which):
+    """After a verify whose drafts are all accepted (no rollback), a decode
+    with tokens = NULL feeds the greedy token of the verify's LAST row, the
+    one after the last drafted position: every row of the pass computes a
+    greedy id, and only the last row's may become the sequence's next
+    token.  The logits equal those of a decode given that token."""
+    shape, P, W = models(which)
+    n = 4
+    ids = [int(t) for t in prompt(shape, P + n)]
+    dec, _ = make_decoder(shape, W)
+    run_prefill(dec, ids[:P], 128)
+    am = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    dec.prefill_chunk(0, ids[P:], P, logits_mode=2, argmax=am)
+    torch.cuda.synchronize()
+    last = int(am.cpu().numpy()[-1])
+    lg_fed, _ = decode(dec, [0], None)
+    dec.kv_truncate(0, P + n)
+    lg_given, _ = decode(dec, [0], [last])
+    assert np.array_equal(lg_fed, lg_given), which
+    dec.close()

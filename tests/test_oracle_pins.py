@@ -401,6 +401,108 @@ def test_bias_reaches_v_before_attention():
     assert np.allclose(x1, [1.5, -1.0, 0.25, 2.0], atol=1e-15)
 
 
+def _kv_load_model(w_q):
+    """H = 4, one layer, two heads of d = 2 with one kv head each; W_k = W_v = 0
+    (the query's own key and value are zero), W_o = I, no FFN, lm-head = I,
+    E[0] = (1, 0, 0, 0)."""
+    s = small_shape(hidden=4, n_layers=1, n_heads=2, n_kv_heads=2, head_dim=2, vocab=4, ffn_inter=4)
+    I4 = np.eye(4, dtype=np.float32)
+    embed = np.zeros((4, 4), np.float32)
+    embed[0] = [1.0, 0, 0, 0]
+    w_qkv = np.concatenate([w_q, np.zeros((8, 4), np.float32)])
+    W = {"embed": bits(embed), "lm_head": bits(I4), "final_norm": np.ones(4, np.float32),
+         "layers": [{"attn_norm": np.ones(4, np.float32), "ffn_norm": np.ones(4, np.float32),
+                     "w_qkv": bits(w_qkv), "w_o": bits(I4), "w_gate_up": bits(np.zeros((8, 4), np.float32)),
+                     "w_down": bits(np.zeros((4, 4), np.float32))}]}
+    return s, W
+
+
+def _norm_logits(x1, eps):
+    x1 = np.asarray(x1, dtype=np.float64)
+    return x1 / math.sqrt(float(np.mean(x1 * x1)) + eps)
+
+
+def test_kv_load_values_and_length():
+    """A loaded prefix is the cache (decoder.rs: a prefix restore uploads
+    host K/V rows into the resident cache): with W_q = 0 every score is 0, so
+    each head's output is the mean of its kv head's V rows over the two loaded
+    positions and the query's own (zero) value.  V is [Hkv][len][d]: a
+    position-major reading or a swapped head would change the mean."""
+    s, W = _kv_load_model(np.zeros((4, 4), np.float32))
+    m = oracle.Model(s, W)
+    V = np.array([[[1.0, 2.0], [3.0, -4.0]],          # kv head 0: positions 0, 1
+                  [[0.5, 8.0], [-6.0, 0.25]]], np.float32)
+    K = np.array([[[7.0, -1.0], [2.0, 3.0]], [[-5.0, 1.5], [4.0, 0.5]]], np.float32)
+    m.kv_load(0, 0, bits(K), bits(V), 2)
+    assert m.seq_len(0) == 2
+    with pytest.raises(oracle.OracleError):
+        m.forward([0], 1)                              # the next position is 2
+    lg = m.forward([0], 2)["logits"]
+    V64 = V.astype(np.float64)
+    out = np.concatenate([(V64[0, 0] + V64[0, 1]) / 3.0, (V64[1, 0] + V64[1, 1]) / 3.0])
+    want = _norm_logits(np.array([1.0, 0, 0, 0]) + out, s.rms_eps)
+    assert np.allclose(lg, want, rtol=1e-13, atol=1e-15)
+
+
+def test_kv_load_keys_select_their_value():
+    """One loaded key per head dominates its head's softmax, so the head's
+    output is that key's V row: head 0 is steered to position 1 and head 1 to
+    position 0 through K alone.  The query q_h = (a_0, 0) of both heads is
+    rotated at position 2 by 2 radians (d = 2: theta_0 = 1), and each chosen
+    key points along it with length 200, a score of about 283 against 0 for the
+    other keys.  K read with heads and positions swapped selects the wrong
+    rows."""
+    w_q = np.zeros((4, 4), np.float32)
+    w_q[0, 0] = 1.0        # head 0: q = (a_0, 0)
+    w_q[2, 0] = 1.0        # head 1: q = (a_0, 0)
+    s, W = _kv_load_model(w_q)
+    m = oracle.Model(s, W)
+    k = 200.0 * np.array([math.cos(2.0), math.sin(2.0)])
+    kb = synth.bf16_to_f32(np.array([synth.f32_to_bf16(v) for v in k], np.uint16))
+    K = np.zeros((2, 2, 2), np.float32)
+    K[0, 1] = kb            # head 0 -> position 1
+    K[1, 0] = kb            # head 1 -> position 0
+    V = np.array([[[1.0, 2.0], [3.0, -4.0]], [[0.5, 8.0], [-6.0, 0.25]]], np.float32)
+    m.kv_load(0, 0, bits(K), bits(V), 2)
+    lg = m.forward([0], 2)["logits"]
+    out = np.concatenate([V[0, 1], V[1, 0]]).astype(np.float64)
+    want = _norm_logits(np.array([1.0, 0, 0, 0]) + out, s.rms_eps)
+    assert np.allclose(lg, want, rtol=1e-13, atol=1e-15)
+
+
+def test_kv_load_errors():
+    s, W = _kv_load_model(np.zeros((4, 4), np.float32))
+    m = oracle.Model(s, W)
+    z = np.zeros((2, 40, 2), np.uint16)
+    with pytest.raises(oracle.OracleError):
+        m.kv_load(0, 0, z, z, s.max_seq + 1)           # past max_seq
+    with pytest.raises(oracle.OracleError):
+        m.kv_load(0, 1, z, z, 2)                       # no layer 1
+
+
+def test_reset_equals_a_fresh_model():
+    """engine.zig Engine.reset forgets the cache: after a reset, a sequence
+    computes bit for bit what a fresh model computes, and resetting one
+    sequence leaves another untouched."""
+    s = small_shape()
+    W = rand_weights(s)
+    a_ids, b_ids = synth.tokens(9, 11, s.vocab), synth.tokens(7, 12, s.vocab)
+    fresh = oracle.Model(s, W).forward(a_ids, 0, logits_mode=2)["logits"]
+    m = oracle.Model(s, W, n_seqs=2)
+    m.forward(b_ids, 0, seq=0, logits_mode=0)
+    m.forward(a_ids[:4], 0, seq=1, logits_mode=0)
+    m.reset(0)
+    assert m.seq_len(0) == 0 and m.seq_len(1) == 4
+    got = m.forward(a_ids, 0, seq=0, logits_mode=2)["logits"]
+    assert np.array_equal(got, fresh)
+    # seq 1 kept its 4 positions: its continuation equals an unbroken run
+    tail = m.forward(a_ids[4:], 4, seq=1, logits_mode=2)["logits"]
+    assert np.array_equal(tail, fresh[4:])
+    m.reset(-1)
+    assert m.seq_len(0) == 0 and m.seq_len(1) == 0
+    assert np.array_equal(m.forward(a_ids, 0, seq=1, logits_mode=2)["logits"], fresh)
+
+
 def test_decode_after_prefill_equals_recompute():
     s = small_shape()
     W = rand_weights(s)
