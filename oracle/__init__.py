@@ -73,7 +73,7 @@ def lib():
         L.orc_seq_len.restype = ctypes.c_int32
         L.orc_seq_len.argtypes = [_P, _I]
         L.orc_forward.restype = _I
-        L.orc_forward.argtypes = [_P, _I, _P, _I, _I, _I, _P, _P, _P, _P]
+        L.orc_forward.argtypes = [_P, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P]
         _LIB = L
     return _LIB
 
@@ -270,8 +270,11 @@ class Model:
         if rc:
             raise OracleError(ERRORS.get(rc, rc))
 
-    def forward(self, ids, start_pos, seq=0, logits_mode=1, routes=False, probs=False, trace=False):
-        """Forward a chunk; returns dict with 'logits' ([V] or [n][V]), 'routes', 'probs', 'trace'."""
+    def forward(self, ids, start_pos, seq=0, logits_mode=1, routes=False, probs=False, trace=False,
+                force_routes=None):
+        """Forward a chunk; returns dict with 'logits' ([V] or [n][V]), 'routes', 'probs', 'trace'.
+        force_routes ([L][n][k] int32): teacher-forced expert ids (each keeps
+        its own softmax probability as its weight)."""
         s = self.shape
         ids = np.ascontiguousarray(ids, dtype=np.int32)
         n = ids.size
@@ -285,8 +288,12 @@ class Model:
         pr = np.empty((s.n_layers, n, s.n_experts), dtype=np.float64) if (probs and s.is_moe) else None
         tr = np.empty((s.n_layers + 1, n, s.hidden), dtype=np.float64) if trace else None
         ptr = lambda a: a.ctypes.data if a is not None else None
+        fr = None
+        if force_routes is not None:
+            fr = np.ascontiguousarray(force_routes, dtype=np.int32)
+            assert fr.shape == (s.n_layers, n, s.top_k), fr.shape
         rc = lib().orc_forward(self._h, seq, ids.ctypes.data, n, int(start_pos), logits_mode,
-                               ptr(lg), ptr(rt), ptr(pr), ptr(tr))
+                               ptr(lg), ptr(rt), ptr(pr), ptr(tr), ptr(fr))
         if rc:
             raise OracleError(ERRORS.get(rc, rc))
         out["logits"] = lg

@@ -445,16 +445,35 @@ int32_t orc_seq_len(const orc_model_t *m, int seq) { return m->len[seq]; }
  * each chosen expert once for all the columns that chose it);
  * decoder.rs MoeWeights (router [E,H], shared_expert_gate [H]). */
 static void orc_moe(const orc_model_t *m, const orc_layer_t *L, const double *B, int n,
-                    double *F, int32_t *routes, double *probs) {
+                    double *F, int32_t *routes, double *probs, const int32_t *force) {
   int H = m->c.hidden, E = m->c.n_experts, k = m->c.top_k, Ie = m->c.expert_inter;
   int Is = m->c.shared_inter;
   double *logits = (double *)malloc(sizeof(double) * (size_t)n * E);
   int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)n * k);
   double *wts = (double *)malloc(sizeof(double) * (size_t)n * k);
+  double *P = (double *)malloc(sizeof(double) * (size_t)E);
   orc_matmul(L->w_router, E, H, B, n, logits);
-  for (int i = 0; i < n; ++i)
+  for (int i = 0; i < n; ++i) {
     orc_route(logits + (size_t)i * E, E, k, m->c.norm_topk_prob, idx + (size_t)i * k,
-              wts + (size_t)i * k, probs ? probs + (size_t)i * E : NULL);
+              wts + (size_t)i * k, P);
+    if (probs) memcpy(probs + (size_t)i * E, P, sizeof(double) * E);
+    if (force) {
+      /* teacher-forced expert choice: the given ids replace the top-k; each
+       * keeps its own softmax probability as its weight (renormalised over
+       * the given set when norm_topk_prob), exactly as if the router had
+       * chosen it */
+      double sum = 0.0;
+      for (int j = 0; j < k; ++j) {
+        int e = force[(size_t)i * k + j];
+        idx[(size_t)i * k + j] = e;
+        wts[(size_t)i * k + j] = P[e];
+        sum += P[e];
+      }
+      if (m->c.norm_topk_prob)
+        for (int j = 0; j < k; ++j) wts[(size_t)i * k + j] /= sum;
+    }
+  }
+  free(P);
   if (routes) memcpy(routes, idx, sizeof(int32_t) * (size_t)n * k);
   memset(F, 0, sizeof(double) * (size_t)n * H);
 
@@ -512,17 +531,31 @@ static void orc_moe(const orc_model_t *m, const orc_layer_t *L, const double *B,
  *
  * logits_mode: 0 none, 1 the last token only (logits: [V]), 2 every token
  * (logits: [n][V]).  routes ([L][n][k]) and router_probs ([L][n][E]) are
- * optional MoE records.  x_trace ([L+1][n][H], optional) receives the
+ * optional MoE records.  force_routes ([L][n][k], optional) teacher-forces
+ * the expert choice: where two expert sets are both correct (a near-tie of
+ * the k-th expert), the oracle follows the given one, as a teacher-forced
+ * decode follows a given token.  x_trace ([L+1][n][H], optional) receives the
  * residual stream after the embedding and after every layer. */
 int orc_forward(orc_model_t *m, int seq, const int32_t *ids, int n, int start_pos,
                 int logits_mode, double *logits, int32_t *routes, double *router_probs,
-                double *x_trace) {
+                double *x_trace, const int32_t *force_routes) {
   const orc_config_t *c = &m->c;
   if (seq < 0 || seq >= c->n_seqs || n <= 0) return ORC_E_INVALID;
   if (start_pos != m->len[seq]) return ORC_E_INVALID;
   if ((long)start_pos + n > c->max_seq) return ORC_E_OVERFLOW;
   for (int i = 0; i < n; ++i)
     if (ids[i] < 0 || ids[i] >= c->vocab) return ORC_E_TOKEN;
+  /* forced expert ids must be k distinct experts per (layer, token) */
+  if (force_routes && c->n_experts > 0) {
+    int k = c->top_k;
+    for (size_t r = 0; r < (size_t)c->n_layers * n; ++r)
+      for (int j = 0; j < k; ++j) {
+        int e = force_routes[r * k + j];
+        if (e < 0 || e >= c->n_experts) return ORC_E_INVALID;
+        for (int j2 = 0; j2 < j; ++j2)
+          if (force_routes[r * k + j2] == e) return ORC_E_INVALID;
+      }
+  }
 
   int H = c->hidden, Hq = c->n_heads, Hkv = c->n_kv_heads, d = c->head_dim;
   int qd = Hq * d, kvd = Hkv * d, nqkv = qd + 2 * kvd;
@@ -573,7 +606,8 @@ int orc_forward(orc_model_t *m, int seq, const int32_t *ids, int n, int start_po
     for (int i = 0; i < n; ++i) orc_rmsnorm(X + (size_t)i * H, L->ffn_norm, H, c->rms_eps, A + (size_t)i * H);
     if (c->n_experts > 0)
       orc_moe(m, L, A, n, Y, routes ? routes + (size_t)l * n * c->top_k : NULL,
-              router_probs ? router_probs + (size_t)l * n * c->n_experts : NULL);
+              router_probs ? router_probs + (size_t)l * n * c->n_experts : NULL,
+              force_routes ? force_routes + (size_t)l * n * c->top_k : NULL);
     else
       orc_swiglu(L->w_gate_up, L->w_down, H, c->ffn_inter, A, n, Y);
     for (size_t j = 0; j < nh; ++j) X[j] += Y[j];

@@ -26,6 +26,15 @@ from tests.gpu_util import log
 TIE = 1e-4
 
 
+def forced(dec, shape, rows):
+    """The GPU's expert ids of its last call ([L][rows][k]), for the oracle to
+    follow (force_routes): the end-to-end comparison then runs both sides on
+    the same expert sets, as a teacher-forced decode runs both on the same
+    token; that those sets are the router's correct choice on the GPU's own
+    input is what check_routes_exact shows."""
+    return read_routes(dec, shape, rows)
+
+
 def read_routes(dec, shape, rows):
     import torch
     got = torch.empty((shape.n_layers, rows, shape.top_k), dtype=torch.int32, device="cuda")

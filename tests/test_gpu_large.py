@@ -21,7 +21,7 @@ import oracle
 from synth.weights import host_kv, host_weights, prompt
 from synth.workloads import C135M, C8B, LONGCTX, MOE
 from tests.gpu_util import MARGIN, assert_parity, compare_logits, decode, log, make_decoder, run_prefill
-from tests.moe_routes import check_routes_exact
+from tests.moe_routes import check_routes_exact, forced
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -38,13 +38,13 @@ def w8b():
 
 def teacher_forced(dec, m, start_logits, pos, steps, what, moe=None):
     """Teacher-forced decode: both sides take the oracle's greedy token.
-    moe = (shape, host weights): the expert ids of every step are checked
-    layer by layer on the GPU's own router input."""
+    moe = (shape, host weights): the oracle follows the GPU's expert ids, and
+    those are checked layer by layer on the GPU's own router input."""
     last = start_logits
     for i in range(steps):
         t = oracle.argmax(last)
-        want = m.forward([t], pos + i)
         lg, am = decode(dec, [0], [t])
+        want = m.forward([t], pos + i, force_routes=None if moe is None else forced(dec, moe[0], 1))
         st = compare_logits(lg[0], want["logits"], f"{what} decode {i}")
         log(what, "decode", i, st)
         assert_parity(st, f"{what} decode {i}")
@@ -138,8 +138,9 @@ def test_8b_full_prompt_properties(w8b):
 def test_moe_two_chunks_decode_and_routes():
     """The MoE workload's first 256 prompt tokens in its chunks of 128: the
     second chunk reads the first chunk's cache.  Logits after each chunk and
-    at 4 teacher-forced decode steps meet the acceptance rule; expert ids are
-    checked at every (layer, token) on the GPU's own router input."""
+    at 4 teacher-forced decode steps meet the acceptance rule with the oracle
+    following the GPU's expert ids; those ids are checked at every (layer,
+    token) on the GPU's own router input."""
     shape = MOE.with_(max_seq=320)
     W = host_weights(shape)
     m = oracle.Model(shape, W)
@@ -148,7 +149,6 @@ def test_moe_two_chunks_decode_and_routes():
     logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
     for c0 in (0, 128):
         part = ids[c0:c0 + 128]
-        want = m.forward(part, c0)
 
         def run(c0=c0, part=part):
             dec.kv_truncate(0, c0)
@@ -156,6 +156,7 @@ def test_moe_two_chunks_decode_and_routes():
 
         run()
         torch.cuda.synchronize()
+        want = m.forward(part, c0, force_routes=forced(dec, shape, 128))
         st = compare_logits(logits.cpu().numpy(), want["logits"], f"moe chunk at {c0}")
         log("moe chunk at", c0, st)
         assert_parity(st, f"moe chunk at {c0}")

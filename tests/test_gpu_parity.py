@@ -259,12 +259,11 @@ def small_moe():
 
 
 def test_moe_small_parity_and_routes():
-    from tests.moe_routes import check_routes_exact
+    from tests.moe_routes import check_routes_exact, forced
     shape = small_moe()
     W = host_weights(shape)
     ids = [int(t) for t in prompt(shape, 24)]
     m = oracle.Model(shape, W)
-    want = m.forward(ids, 0)
     dec, _ = make_decoder(shape, W)
     logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
 
@@ -274,6 +273,7 @@ def test_moe_small_parity_and_routes():
 
     prefill()
     torch.cuda.synchronize()
+    want = m.forward(ids, 0, force_routes=forced(dec, shape, 24))
     st = compare_logits(logits.cpu().numpy(), want["logits"], "moe prefill")
     log("moe prefill", st)
     assert_parity(st, "moe prefill")
@@ -281,8 +281,8 @@ def test_moe_small_parity_and_routes():
     # decode steps, teacher-forced, routes checked on the GEMV path too
     for step in range(4):
         t = oracle.argmax(want["logits"])
-        want = m.forward([t], 24 + step)
         lg, _ = decode(dec, [0], [t])
+        want = m.forward([t], 24 + step, force_routes=forced(dec, shape, 1))
         st = compare_logits(lg[0], want["logits"], f"moe decode {step}")
         assert_parity(st, f"moe decode {step}")
         check_routes_exact(dec, shape, W, 1,
@@ -295,7 +295,7 @@ def test_moe_small_multi_chunk_prefill():
     chunks attend to the cached rows of the earlier ones and route their
     own rows; logits after every chunk and the routes of every chunk are
     checked, then decode continues."""
-    from tests.moe_routes import check_routes_exact
+    from tests.moe_routes import check_routes_exact, forced
     shape = small_moe().with_(max_chunk=16)
     W = host_weights(shape)
     ids = [int(t) for t in prompt(shape, 40, seq=3)]
@@ -304,7 +304,6 @@ def test_moe_small_multi_chunk_prefill():
     logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
     for c0 in range(0, 40, 16):
         part = ids[c0:c0 + 16]
-        want = m.forward(part, c0)
 
         def run(c0=c0, part=part):
             dec.kv_truncate(0, c0)
@@ -312,14 +311,15 @@ def test_moe_small_multi_chunk_prefill():
 
         run()
         torch.cuda.synchronize()
+        want = m.forward(part, c0, force_routes=forced(dec, shape, len(part)))
         st = compare_logits(logits.cpu().numpy(), want["logits"], f"moe chunk at {c0}")
         log("moe chunk at", c0, st)
         assert_parity(st, f"moe chunk at {c0}")
         check_routes_exact(dec, shape, W, len(part), run, f"moe chunk at {c0}")
     for step in range(3):
         t = oracle.argmax(want["logits"])
-        want = m.forward([t], 40 + step)
         lg, _ = decode(dec, [0], [t])
+        want = m.forward([t], 40 + step, force_routes=forced(dec, shape, 1))
         assert_parity(compare_logits(lg[0], want["logits"], f"moe decode {step}"), f"moe decode {step}")
 
 

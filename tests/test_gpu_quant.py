@@ -81,15 +81,13 @@ def test_quantized_moe_prefill_decode_and_routes():
     chosen expert's codes with that expert's row scales): the small MoE
     model's logits against the oracle on the same quantised weights, and its
     expert ids layer by layer on the GPU's own router input."""
-    from tests.moe_routes import check_routes_exact
+    from tests.moe_routes import check_routes_exact, forced
     from tests.test_gpu_parity import small_moe
     shape = small_moe().with_(name="moe-small-q8", weight_quant=1)
     W = host_weights(shape)
     ids = [int(t) for t in prompt(shape, 24)]
     m = oracle.Model(shape, W)
-    want = m.forward(ids, 0)
     plain = oracle.Model(shape.with_(weight_quant=0), W).forward(ids, 0)["logits"]
-    assert np.abs(plain - want["logits"]).max() > 1e-3
     dec, _ = make_decoder(shape, W)
     logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
 
@@ -99,14 +97,16 @@ def test_quantized_moe_prefill_decode_and_routes():
 
     prefill()
     torch.cuda.synchronize()
+    want = m.forward(ids, 0, force_routes=forced(dec, shape, 24))
+    assert np.abs(plain - want["logits"]).max() > 1e-3
     st = compare_logits(logits.cpu().numpy(), want["logits"], "moe q8 prefill")
     log("moe q8 prefill", st)
     assert_parity(st, "moe q8 prefill")
     check_routes_exact(dec, shape, W, 24, prefill, "moe q8 prefill")
     for step in range(4):
         t = oracle.argmax(want["logits"])
-        want = m.forward([t], 24 + step)
         lg, _ = decode(dec, [0], [t])
+        want = m.forward([t], 24 + step, force_routes=forced(dec, shape, 1))
         st = compare_logits(lg[0], want["logits"], f"moe q8 decode {step}")
         log("moe q8 decode", step, st)
         assert_parity(st, f"moe q8 decode {step}")

@@ -672,6 +672,41 @@ def test_moe_routes_are_distinct_and_chunk_invariant():
         assert np.array_equal(step[i]["routes"][:, 0], full["routes"][:, i])
 
 
+@pytest.mark.parametrize("renorm", [0, 1])
+def test_moe_forced_routes(renorm):
+    """Teacher-forced expert ids (the oracle follows a given expert set where
+    two are correct): with a zero router every probability is 1/E, so
+    forcing experts {3, 1} must equal a dense SwiGLU made of those two
+    experts with the down rows scaled by their weight, 1/E, or 1/2 when
+    the top-k is renormalised (both exact: powers of two).  Forcing the
+    oracle's own choice changes nothing, and invalid sets are refused."""
+    E, Ie = 4, 12
+    s = moe_shape(top_k=2, norm_topk_prob=renorm, n_layers=1)
+    W = rand_weights(s)
+    ids = synth.tokens(6, 21, s.vocab)
+    own = oracle.Model(s, W).forward(ids, 0, logits_mode=2, routes=True)
+    again = oracle.Model(s, W).forward(ids, 0, logits_mode=2, force_routes=own["routes"])
+    assert np.array_equal(own["logits"], again["logits"])
+    L = W["layers"][0]
+    L["w_router"] = bits(np.zeros((E, s.hidden), np.float32))
+    force = np.tile(np.array([3, 1], np.int32), (1, 6, 1))
+    a = oracle.Model(s, W).forward(ids, 0, logits_mode=2, force_routes=force, routes=True)
+    assert np.all(a["routes"] == force)
+    sel = [3, 1]
+    g = np.concatenate([L["w_exp_gate_up"][e][:Ie] for e in sel])
+    u = np.concatenate([L["w_exp_gate_up"][e][Ie:] for e in sel])
+    down = np.concatenate([L["w_exp_down"][e] for e in sel], axis=1)
+    w = 0.5 if renorm else 1.0 / E
+    sd = small_shape(hidden=32, n_layers=1, n_heads=2, n_kv_heads=2, head_dim=8, vocab=64, ffn_inter=2 * Ie)
+    b = oracle.Model(sd, dense_from(W, np.concatenate([g, u]), bits(widen(down) * w))).forward(
+        ids, 0, logits_mode=2)["logits"]
+    assert np.allclose(a["logits"], b, rtol=0, atol=1e-12)
+    for bad in ([1, 1], [0, E]):
+        with pytest.raises(oracle.OracleError):
+            oracle.Model(s, W).forward(ids, 0, logits_mode=2,
+                                       force_routes=np.tile(np.array(bad, np.int32), (1, 6, 1)))
+
+
 # ----------------------------------------------------------------- errors --
 
 def test_boundary_errors():
