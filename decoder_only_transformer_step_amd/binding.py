@@ -73,6 +73,7 @@ SIGNATURES = {
     "dec_diag_gemm": (ctypes.c_int, [_P, _I32, _I32, _P, _I32, _P, _P]),
     "dec_diag_gemm_chunk": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, ctypes.c_int64, _P]),
     "dec_diag_pack_w32": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
+    "dec_diag_gemm_chunk_noalloc": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _P, _I32, _P]),
     "dec_diag_rmsnorm": (ctypes.c_int, [_P, _P, _I32, _I32, ctypes.c_double, _P, _P]),
     "dec_diag_quantize_rows": (ctypes.c_int, [_P, ctypes.c_int64, _I32, _P, _P, _P, _P]),
     "dec_diag_gemv": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _P]),
@@ -309,6 +310,15 @@ def diag_gemm_chunk(A, Wp, C, ksplit, part, stream):
     _check(lib().dec_diag_gemm_chunk(_ptr(A), planes, M, K, _ptr(Wp), N, _ptr(C), ksplit,
                                      _ptr(part) if part is not None else None, n_part,
                                      ctypes.c_void_p(stream)), None, "dec_diag_gemm_chunk")
+
+
+def diag_gemm_chunk_noalloc(A, Wp, C, ksplit, stream):
+    """diag_gemm_chunk with the split partials in the library's static
+    per-device array (no workspace, no allocation)."""
+    planes, M, K = A.shape
+    N = Wp.shape[0]
+    _check(lib().dec_diag_gemm_chunk_noalloc(_ptr(A), planes, M, K, _ptr(Wp), N, _ptr(C), ksplit,
+                                             ctypes.c_void_p(stream)), None, "dec_diag_gemm_chunk_noalloc")
 
 
 def diag_gemv(a, W, y, stream):

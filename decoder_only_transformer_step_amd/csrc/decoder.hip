@@ -11,6 +11,7 @@
 
 #include <array>
 #include <cmath>
+#include <mutex>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -1520,6 +1521,68 @@ int dec_diag_gemm_chunk(const uint16_t *d_A, int32_t planes, int32_t M, int32_t 
   g.Cpart = d_part;
   if (ksplit > 1 && (!d_part || part_elems < (int64_t)ksplit * M * gemm_ntiles(g, EPI_STORE) * 16)) return DEC_E_INVALID;
   if (!gemm_chunk_fits(g, EPI_STORE)) return DEC_E_INVALID;
+  return launch_gemm_chunk(g, EPI_STORE, (hipStream_t)stream) == hipSuccess ? DEC_OK : DEC_E_HIP;
+}
+
+}  // extern "C"
+
+// Split-K partials of dec_diag_gemm_chunk_noalloc: a file-scope device array,
+// so that entry point allocates nothing.  Each device holds its own copy at
+// its own address; host code uses that address (scratch_device), never the
+// array's name, which on the host only stands in for the symbol.
+constexpr int64_t NOALLOC_SCRATCH_FLOATS = int64_t(4) << 20;  // 16 MiB per device
+static __device__ __align__(256) float scratch[NOALLOC_SCRATCH_FLOATS];
+
+namespace {
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex scratch_mu;
+float *scratch_addr[NOALLOC_MAX_DEVICES] = {};
+
+// The current device's address of `scratch`, looked up once per device.
+hipError_t scratch_device(float **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_addr[dev] = static_cast<float *>(p);
+  }
+  *out = scratch_addr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" {
+
+int dec_diag_gemm_chunk_noalloc(const uint16_t *d_A, int32_t planes, int32_t M, int32_t K, const uint16_t *d_Wp,
+                                int32_t N, float *d_C, int32_t ksplit, void *stream) {
+  if (!d_A || !d_Wp || !d_C || (planes != 1 && planes != 2) || M < 1 || M > 128 || N < 1 || K < 16 || K % 16 ||
+      ksplit < 1 || ksplit > 64)
+    return DEC_E_INVALID;
+  GemmArgs g{};
+  g.A = d_A;
+  g.a_lo = planes == 2 ? (int64_t)M * K : 0;
+  g.lda = K;
+  g.W = d_Wp;
+  g.Wp = d_Wp;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.np_off = N;
+  g.C = d_C;
+  g.ldc = N;
+  g.ksplit = ksplit;
+  if (!gemm_chunk_fits(g, EPI_STORE)) return DEC_E_INVALID;
+  if (ksplit > 1) {
+    // every partial the reduce reads is rewritten by this call's blocks, so
+    // the previous call's contents need no clearing
+    if ((int64_t)ksplit * M * gemm_ntiles(g, EPI_STORE) * 16 > NOALLOC_SCRATCH_FLOATS) return DEC_E_WORKSPACE;
+    if (scratch_device(&g.Cpart) != hipSuccess) return DEC_E_HIP;
+  }
   return launch_gemm_chunk(g, EPI_STORE, (hipStream_t)stream) == hipSuccess ? DEC_OK : DEC_E_HIP;
 }
 

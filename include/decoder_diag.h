@@ -43,6 +43,22 @@ int dec_diag_gemm_chunk(const uint16_t *d_A, int32_t planes, int32_t M, int32_t 
                         int32_t N, float *d_C, int32_t ksplit, float *d_part, int64_t part_elems,
                         void *stream);
 
+/* dec_diag_gemm_chunk without the partial-sum workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments,
+ * layouts and results as dec_diag_gemm_chunk; with ksplit > 1 the fp32
+ * partials live in a 16 MiB array that the library holds on each device
+ * (static device memory, kept until the process ends), so this call never
+ * allocates.  ksplit * M * ceil(N / 16) * 16 floats must fit in 4 Mi
+ * (4 194 304) floats, else DEC_E_WORKSPACE and nothing is launched.  Every
+ * call on one device shares that device's array: two calls that overlap on
+ * one device (different streams, no ordering between them) race and give
+ * undefined results; calls ordered on one stream are safe.  The first call
+ * on a device looks the array's address up once (DEC_E_HIP if that fails). */
+int dec_diag_gemm_chunk_noalloc(const uint16_t *d_A, int32_t planes, int32_t M, int32_t K,
+                                const uint16_t *d_Wp, int32_t N, float *d_C, int32_t ksplit,
+                                void *stream);
+
 /* y[n] = sum_k W[n][k] a[k] with the batch-1 decode projection kernel.
  * a fp32 [K], W bf16 [N][K], y fp32 [N]; K % 8 == 0, K * 4 <= 61440. */
 int dec_diag_gemv(const float *d_a, int32_t K, const uint16_t *d_W, int32_t N, float *d_y, void *stream);
