@@ -68,6 +68,8 @@ def lib():
         L.orc_kv_load.argtypes = [_P, _I, _I, _P, _P, _I]
         L.orc_quantize_rows.restype = None
         L.orc_quantize_rows.argtypes = [_P, _I, _I, _P, _P]
+        L.orc_quantize_q4.restype = None
+        L.orc_quantize_q4.argtypes = [_P, _I, _I, _P, _P, _P]
         L.orc_truncate.restype = _I
         L.orc_truncate.argtypes = [_P, _I, _I]
         L.orc_seq_len.restype = ctypes.c_int32
@@ -160,6 +162,18 @@ def quantize_rows(W_bits, rows, cols):
     return out, e
 
 
+def quantize_q4(W_bits, rows, cols):
+    """4-bit codes with one power-of-two scale per group of 32 weights:
+    returns the dequantised weights (bf16 bit patterns, exact), the codes
+    [rows][cols] (int8 values in [-7, 7]) and the exponents [rows][cols / 32]."""
+    W_bits = np.ascontiguousarray(W_bits, dtype=np.uint16).reshape(rows, cols)
+    out = np.empty_like(W_bits)
+    q = np.empty((rows, cols), dtype=np.int8)
+    e = np.empty((rows, cols // 32), dtype=np.int32)
+    lib().orc_quantize_q4(W_bits.ctypes.data, rows, cols, out.ctypes.data, q.ctypes.data, e.ctypes.data)
+    return out, q, e
+
+
 def quant_dims(shape):
     """(rows, cols) of every matrix the quantised decoder streams as int8
     rows: the attention projections, the dense or shared-expert FFN, and
@@ -180,18 +194,21 @@ def quant_dims(shape):
 def quantized_weights(shape, weights):
     """The model's weights as the quantised decoder holds them: those
     matrices and the lm-head dequantised (the embedding gather keeps its
-    bf16 table)."""
+    bf16 table).  weight_quant 1: int8 codes, one scale per row; 2: 4-bit
+    codes, one scale per group of 32 weights."""
     s = shape
     H = s.hidden
     dims = quant_dims(s)
+    q = (lambda W, r, c: quantize_rows(W, r, c)[0]) if s.weight_quant == 1 else \
+        (lambda W, r, c: quantize_q4(W, r, c)[0])
     out = dict(weights)
     out["layers"] = []
     for L in weights["layers"]:
         L2 = dict(L)
         for f, (r, c) in dims.items():
-            L2[f] = quantize_rows(L[f], r, c)[0].reshape(-1)
+            L2[f] = q(L[f], r, c).reshape(-1)
         out["layers"].append(L2)
-    out["lm_head"] = quantize_rows(weights["lm_head"], s.vocab, H)[0].reshape(-1)
+    out["lm_head"] = q(weights["lm_head"], s.vocab, H).reshape(-1)
     return out
 
 

@@ -421,6 +421,41 @@ void orc_quantize_rows(const uint16_t *W, int rows, int K, uint16_t *out, int32_
   }
 }
 
+/* 4-bit weight quantisation (quantised weight streaming with 4-bit codes;
+ * decoder.rs names packed 4-bit expert planes): every group of 32
+ * consecutive weights of a row gets one power-of-two scale 2^e, with e the
+ * smallest integer for which 7 * 2^e covers the group's largest magnitude a,
+ * and codes q = w / 2^e rounded to the nearest integer (ties to even), so
+ * |q| <= 7.  All steps are exact in fp64.  The dequantised q 2^e has at most
+ * 3 significant bits, a bf16 value; out receives those bf16 bit patterns,
+ * q_out (optional) the codes [rows][K] and e_out (optional) the exponents
+ * [rows][K / 32].  K must be a multiple of 32.  An all-zero group takes e = 0. */
+void orc_quantize_q4(const uint16_t *W, int rows, int K, uint16_t *out, int8_t *q_out, int32_t *e_out) {
+  int groups = K / 32;
+  for (int r = 0; r < rows; ++r)
+    for (int gi = 0; gi < groups; ++gi) {
+      const uint16_t *w = W + (size_t)r * K + (size_t)gi * 32;
+      double a = 0.0;
+      for (int j = 0; j < 32; ++j) a = fmax(a, fabs(bf(w[j])));
+      int e = 0;
+      if (a > 0.0) {
+        int p;
+        frexp(a, &p);                              /* a < 2^p, so 7 * 2^(p-2) > a */
+        e = p - 2;
+        while (7.0 * ldexp(1.0, e - 1) >= a) --e;  /* smallest e with 7 * 2^e >= a */
+      }
+      if (e_out) e_out[(size_t)r * groups + gi] = e;
+      for (int j = 0; j < 32; ++j) {
+        double q = nearbyint(ldexp(bf(w[j]), -e));  /* to nearest, ties to even */
+        float f = (float)ldexp(q, e);                /* exact: 3 significant bits */
+        uint32_t u;
+        memcpy(&u, &f, 4);
+        out[(size_t)r * K + (size_t)gi * 32 + j] = (uint16_t)(u >> 16);
+        if (q_out) q_out[(size_t)r * K + (size_t)gi * 32 + j] = (int8_t)q;
+      }
+    }
+}
+
 /* Roll a sequence back to its first len positions (0 <= len <= current
  * length): the rows past len stop being part of it and are cleared, so the
  * state equals one that never held them.  pipeline.rs

@@ -797,3 +797,44 @@ def test_quantize_rows_properties():
     assert np.all(np.abs(w - d) <= step / 2)                  # rounded to the nearest code
     again, e2 = oracle.quantize_rows(deq, rows, K)            # idempotent
     assert np.array_equal(again, deq) and np.array_equal(e2, e)
+
+
+def test_quantize_q4_worked_example():
+    """4-bit codes with a power-of-two scale per group of 32 weights.
+    Row 0, group 0: largest magnitude 1.75, and 7 * 2^e >= 1.75 first holds
+    at e = -2 (step 0.25): codes 7, -2, 1, 0.5 -> 0 and 1.5 -> 2 (ties to
+    even), -2.5 -> -2, 1.25 -> 1.  Group 1: largest 3/128, e = -8 (7/256
+    covers it, 7/512 does not): codes 6 and -3.  Group 2 is all zero: e = 0.
+    Row 1 sits on the boundary: a group whose largest magnitude is exactly
+    7 * 2^-5 takes e = -5 (code 7); the next bf16 value up, 0.2197265625,
+    needs e = -4 and becomes code 4 (3.515625 rounded)."""
+    W = np.zeros((2, 96), np.float32)
+    W[0, :7] = [1.75, -0.5, 0.25, 0.125, 0.375, -0.625, 0.3125]
+    W[0, 32:34] = [3 / 128, -3 / 256]
+    W[1, 0] = 0.21875
+    W[1, 32] = 0.2197265625
+    deq, q, e = oracle.quantize_q4(bits(W), 2, 96)
+    assert e.tolist() == [[-2, -8, 0], [-5, -4, 0]]
+    assert q[0, :7].tolist() == [7, -2, 1, 0, 2, -2, 1]
+    assert q[0, 32:34].tolist() == [6, -3]
+    assert q[1, 0] == 7 and q[1, 32] == 4
+    got = synth.bf16_to_f32(deq)
+    assert np.array_equal(got[0, :7], np.array([1.75, -0.5, 0.25, 0.0, 0.5, -0.5, 0.25], np.float32))
+    assert got[1, 32] == 0.25
+    assert np.count_nonzero(q) == 10
+
+
+def test_quantize_q4_properties():
+    rows, K = 48, 128
+    W = rand_bits((rows, K), 0.05)
+    w = widen(W)
+    deq, q, e = oracle.quantize_q4(W, rows, K)
+    d = widen(deq)
+    step = np.repeat(np.ldexp(1.0, e), 32, axis=1)
+    assert np.array_equal(d, q.astype(np.float64) * step)       # deq = code x 2^e exactly
+    assert np.abs(q).max() <= 7                                  # 4-bit signed range
+    gmax = np.abs(q).reshape(rows, K // 32, 32).max(axis=2)
+    assert np.all(gmax >= 4)                                     # e is the smallest that covers the group
+    assert np.all(np.abs(w - d) <= step / 2)                     # rounded to the nearest code
+    again, q2, e2 = oracle.quantize_q4(deq, rows, K)             # idempotent
+    assert np.array_equal(again, deq) and np.array_equal(q2, q) and np.array_equal(e2, e)
