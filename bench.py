@@ -62,6 +62,89 @@ def counter_traffic(name):
     return float(m_bytes.group(1))
 
 
+def measure_prefill(dec, ids, chunk, stream, ev0, ev1, runs):
+    """Whole prompt in chunks of `chunk` (median of `runs` after one untimed
+    run), then once more with the per-node timers for the MFMA figures."""
+    import torch
+    chunks = [ids[i:i + chunk] for i in range(0, len(ids), chunk)]
+
+    def prompt_once():
+        pos = 0
+        for ci, ch in enumerate(chunks):
+            dec.prefill_chunk(0, ch, pos, logits_mode=1 if ci == len(chunks) - 1 else 0)
+            pos += len(ch)
+
+    times = []
+    for run in range(1 + runs):
+        dec.kv_reset(-1)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        prompt_once()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        if run:
+            times.append(ev0.elapsed_time(ev1) * 1e-3)
+    dec.kv_reset(-1)
+    dec.stats_enable()
+    prompt_once()
+    pst = dec.stats_read()
+    dec.stats_enable(())
+    torch.cuda.synchronize()
+    t_pre = statistics.median(times)
+    flops = sum(v["flops"] for v in pst.values())
+    gemm_nodes = ("qkv", "o", "gate_up", "down", "head", "router", "experts")
+    g_ms = sum(pst[n]["ms"] for n in gemm_nodes)
+    g_fl = sum(pst[n]["flops"] for n in gemm_nodes)
+    g_by = sum(pst[n]["bytes"] for n in gemm_nodes)
+    chunk_bytes = g_by / len(chunks)
+    chunk_flops = g_fl / len(chunks)
+    ceiling = min(1.0, (chunk_flops / (MFMA_BF16_PEAK_TFS * 1e12)) / (chunk_bytes / (HBM_PEAK_GBS * 1e9)))
+    return {"tok_s": len(ids) / t_pre, "ms": t_pre * 1e3, "prompt": len(ids), "chunk": chunk,
+            "tflops": flops / t_pre / 1e12, "mfma_frac": flops / t_pre / 1e12 / MFMA_BF16_PEAK_TFS,
+            "gemm_tflops": g_fl / (g_ms * 1e-3) / 1e12,
+            "gemm_mfma_frac": g_fl / (g_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+            "gemm_mfma_frac_executed": 2 * g_fl / (g_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+            "gemm_hbm_frac": g_by / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "chunk_mfma_ceiling": ceiling, "nodes": summarize_nodes(pst)}
+
+
+def measure_gemm_capability(shape, rows, stream, ev0, ev1, reps=20):
+    """The prefill projection kernel on the gate/up shape at `rows` rows
+    (C[rows][2I] = A W^T, K = H; packed weights, no split): TFLOP/s with
+    plain bf16 activations (one MFMA per product) and with the split-bf16
+    activations the model runs (hi and lo planes, two MFMAs per product)."""
+    import torch
+    from decoder_only_transformer_step_amd.binding import diag_gemm_chunk, diag_pack_w32
+    N, K = 2 * shape.ffn_inter, shape.hidden
+    g = torch.Generator(device="cuda").manual_seed(5)
+    A = (torch.randn((2, rows, K), device="cuda", generator=g) * 0.5).to(torch.bfloat16).view(torch.int16)
+    Wt = (torch.randn((N, K), device="cuda", generator=g) * 0.02).to(torch.bfloat16).view(torch.int16)
+    P = torch.empty_like(Wt)
+    diag_pack_w32(Wt, P, stream.cuda_stream)
+    del Wt
+    C = torch.empty((rows, N), dtype=torch.float32, device="cuda")
+    out = {"rows": rows, "N": N, "K": K}
+    for planes in (1, 2):
+        a = A[:planes]
+        diag_gemm_chunk(a, P, C, 1, None, stream.cuda_stream)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(reps):
+            diag_gemm_chunk(a, P, C, 1, None, stream.cuda_stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        s = ev0.elapsed_time(ev1) * 1e-3 / reps
+        fl = 2.0 * rows * N * K
+        out[f"planes{planes}"] = {"us": s * 1e6, "tflops_algorithmic": fl / s / 1e12,
+                                  "mfma_frac_algorithmic": fl / s / 1e12 / MFMA_BF16_PEAK_TFS,
+                                  "mfma_frac_executed": planes * fl / s / 1e12 / MFMA_BF16_PEAK_TFS}
+        log(f"[gpu] gemm {rows}x{N}x{K} planes {planes}: {s * 1e6:.1f} us, "
+            f"{fl / s / 1e12:.0f} TFLOP/s algorithmic")
+    del A, P, C
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_verify(dec, shape, stream, ev0, ev1, reps, ns=(2, 4, 8)):
     """Multi-position verify, the check of speculatively drafted tokens
     (pipeline.rs Pipeline::forward_pair and measure_pair_fusion): n drafted
@@ -325,6 +408,9 @@ def main():
                     help="int8 weights with a power-of-two scale per row (decode streams the codes)")
     ap.add_argument("--kv-page", type=int, default=0,
                     help="paged KV cache: pages of this many positions (the pool holds every sequence's max_seq)")
+    ap.add_argument("--wide-chunk", type=int, default=512,
+                    help="also time the prompt in chunks of this many tokens (0: off), and the gate_up "
+                         "GEMM at that many rows")
     ap.add_argument("--no-verify", action="store_true",
                     help="skip the multi-position verify measurement (batch-1 workloads)")
     ap.add_argument("--verify-reps", type=int, default=20)
@@ -421,50 +507,18 @@ def main():
     seqs = list(range(batch))
 
     # ------------------------------------------------------------ prefill --
-    prefill = None
+    prefill = prefill_wide = gemm_cap = None
     context = work.context or (work.prompt if args.no_prefill else 0)
     if work.prompt and not args.no_prefill:
         ids = [int(t) for t in prompt(shape, work.prompt)]
-        chunks = [ids[i:i + work.chunk] for i in range(0, len(ids), work.chunk)]
-        times = []
-        for run in range(1 + args.prefill_runs):
-            dec.kv_reset(-1)
-            torch.cuda.synchronize()
-            ev0.record(stream)
-            pos = 0
-            for ci, ch in enumerate(chunks):
-                dec.prefill_chunk(0, ch, pos, logits_mode=1 if ci == len(chunks) - 1 else 0)
-                pos += len(ch)
-            ev1.record(stream)
-            torch.cuda.synchronize()
-            if run:
-                times.append(ev0.elapsed_time(ev1) * 1e-3)
-        # one more prefill with the per-node timers, for the MFMA figures
-        dec.kv_reset(-1)
-        dec.stats_enable()
-        pos = 0
-        for ci, ch in enumerate(chunks):
-            dec.prefill_chunk(0, ch, pos, logits_mode=1 if ci == len(chunks) - 1 else 0)
-            pos += len(ch)
-        pst = dec.stats_read()
-        dec.stats_enable(())
-        torch.cuda.synchronize()
-        t_pre = statistics.median(times)
-        flops = sum(v["flops"] for v in pst.values())
-        gemm_nodes = ("qkv", "o", "gate_up", "down", "head", "router", "experts")
-        g_ms = sum(pst[n]["ms"] for n in gemm_nodes)
-        g_fl = sum(pst[n]["flops"] for n in gemm_nodes)
-        g_by = sum(pst[n]["bytes"] for n in gemm_nodes)
-        chunk_bytes = sum(pst[n]["bytes"] for n in gemm_nodes) / len(chunks)
-        chunk_flops = g_fl / len(chunks)
-        ceiling = min(1.0, (chunk_flops / (MFMA_BF16_PEAK_TFS * 1e12)) / (chunk_bytes / (HBM_PEAK_GBS * 1e9)))
-        prefill = {"tok_s": len(ids) / t_pre, "ms": t_pre * 1e3, "prompt": len(ids), "chunk": work.chunk,
-                   "tflops": flops / t_pre / 1e12, "mfma_frac": flops / t_pre / 1e12 / MFMA_BF16_PEAK_TFS,
-                   "gemm_tflops": g_fl / (g_ms * 1e-3) / 1e12,
-                   "gemm_mfma_frac": g_fl / (g_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
-                   "gemm_hbm_frac": g_by / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                   "chunk_mfma_ceiling": ceiling, "nodes": summarize_nodes(pst)}
-        log(f"[gpu] prefill {prefill['tok_s']:.0f} tok/s ({t_pre * 1e3:.1f} ms for {len(ids)} tokens)")
+        if args.wide_chunk and shape.max_chunk >= args.wide_chunk and work.prompt >= args.wide_chunk:
+            prefill_wide = measure_prefill(dec, ids, args.wide_chunk, stream, ev0, ev1, args.prefill_runs)
+            log(f"[gpu] prefill in chunks of {args.wide_chunk}: {prefill_wide['tok_s']:.0f} tok/s "
+                f"(GEMM nodes {prefill_wide['gemm_mfma_frac']:.3f} of bf16 MFMA peak)")
+        prefill = measure_prefill(dec, ids, work.chunk, stream, ev0, ev1, args.prefill_runs)
+        log(f"[gpu] prefill {prefill['tok_s']:.0f} tok/s ({prefill['ms']:.1f} ms for {len(ids)} tokens)")
+        if args.wide_chunk and shape.max_chunk >= args.wide_chunk and not shape.is_moe:
+            gemm_cap = measure_gemm_capability(shape, args.wide_chunk, stream, ev0, ev1)
     elif context:
         # every sequence starts with a synthetic N(0,1) KV prefix (long-context batched decode)
         t0 = time.time()
@@ -553,6 +607,8 @@ def main():
                    "bytes_per_step": step_bytes, "host_s": t_host,
                    "nodes_warmup": summarize_nodes(wst)},
         "prefill": prefill,
+        "prefill_wide_chunk": prefill_wide,
+        "prefill_gemm_capability": gemm_cap,
         "verify": verify,
         "graph_decode": graph,
         "roofline": roofline,

@@ -34,6 +34,7 @@ constexpr int CHUNK_MIN_ROWS = 16;   // more rows than this take the chunk proje
 constexpr int CHUNK_BATCH_MIN_ROWS = 8;
 constexpr double CHUNK_BATCH_MIN_BYTES = 40e6;
 constexpr int CHUNK_MAX_SPLIT = 16;
+constexpr int MAX_CHUNK = 512;     // largest prefill chunk (rows per call)
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -139,7 +140,7 @@ bool config_ok(const decoder_config_t *c) {
       return false;
   }
   if (c->head_dim != 64 && c->head_dim != 128) return false;
-  if (c->vocab <= 0 || c->max_seq <= 0 || c->max_chunk <= 0 || c->max_chunk > 256 ||
+  if (c->vocab <= 0 || c->max_seq <= 0 || c->max_chunk <= 0 || c->max_chunk > MAX_CHUNK ||
       c->max_batch <= 0 || c->max_batch > 256)
     return false;
   if (!(c->rope_base > 0.0) || !(c->rms_eps >= 0.0)) return false;
@@ -1502,8 +1503,8 @@ int dec_diag_pack_w32(const uint16_t *d_W, int32_t rows, int32_t K, uint16_t *d_
 
 int dec_diag_gemm_chunk(const uint16_t *d_A, int32_t planes, int32_t M, int32_t K, const uint16_t *d_Wp, int32_t N,
                         float *d_C, int32_t ksplit, float *d_part, int64_t part_elems, void *stream) {
-  if (!d_A || !d_Wp || !d_C || (planes != 1 && planes != 2) || M < 1 || M > 128 || N < 1 || K < 16 || K % 16 ||
-      ksplit < 1 || ksplit > 64)
+  if (!d_A || !d_Wp || !d_C || (planes != 1 && planes != 2) || M < 1 || M > MAX_CHUNK || N < 1 || K < 16 ||
+      K % 16 || ksplit < 1 || ksplit > 64)
     return DEC_E_INVALID;
   GemmArgs g{};
   g.A = d_A;
@@ -1560,8 +1561,8 @@ extern "C" {
 
 int dec_diag_gemm_chunk_noalloc(const uint16_t *d_A, int32_t planes, int32_t M, int32_t K, const uint16_t *d_Wp,
                                 int32_t N, float *d_C, int32_t ksplit, void *stream) {
-  if (!d_A || !d_Wp || !d_C || (planes != 1 && planes != 2) || M < 1 || M > 128 || N < 1 || K < 16 || K % 16 ||
-      ksplit < 1 || ksplit > 64)
+  if (!d_A || !d_Wp || !d_C || (planes != 1 && planes != 2) || M < 1 || M > MAX_CHUNK || N < 1 || K < 16 ||
+      K % 16 || ksplit < 1 || ksplit > 64)
     return DEC_E_INVALID;
   GemmArgs g{};
   g.A = d_A;

@@ -1,5 +1,5 @@
 // Multi-row projection for prefill chunks: C[m][n] = sum_k A[m][k] W[n][k]
-// for up to 128 activation rows (engine.zig Engine.prefill: a chunk of token
+// for up to 512 activation rows (engine.zig Engine.prefill: a chunk of token
 // columns shares one pass over every weight matrix; decoder.rs AttnWeights:
 // weights are row-major [out][in]).
 //
@@ -323,7 +323,7 @@ int gemm_chunk_mblocks(int rows) { return (rows + CK_ROWS - 1) / CK_ROWS; }
 bool gemm_chunk_fits(const GemmArgs &g, int epi) {
   // the packed copy covers every weight row in 32-row tiles
   const int64_t wrows = epi == EPI_SWIGLU ? 2 * (int64_t)g.N : g.N;
-  return g.Wp != nullptr && g.M >= 2 && g.M <= 128 && g.A != nullptr && g.x == nullptr && g.n_groups == nullptr &&
+  return g.Wp != nullptr && g.M >= 2 && g.M <= 512 && g.A != nullptr && g.x == nullptr && g.n_groups == nullptr &&
          g.a_rows == nullptr && pack_w32_fits(wrows, g.K) && gemm_ntiles(g, epi) % 2 == 0 &&
          (epi == EPI_QKV ? g.np_off % 32 == 0 : g.N % 32 == 0);
 }

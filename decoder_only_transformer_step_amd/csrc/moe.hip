@@ -15,7 +15,7 @@
 namespace {
 
 constexpr int ROUTE_THREADS = 256;
-constexpr int GROUP_MAX_PAIRS = 2048;  // rows x k (rows <= 256, k <= 8)
+constexpr int GROUP_MAX_PAIRS = 4096;  // rows x k (rows <= 512, k <= 8)
 
 // (value, index) of the better of two candidates under `better`
 __device__ __forceinline__ void wave_best(float &v, int &i) {

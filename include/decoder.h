@@ -90,7 +90,7 @@ typedef struct {
   double rope_base;        /* RoPE base */
   double rms_eps;          /* RMSNorm epsilon */
   int32_t max_seq;         /* KV capacity per sequence (positions) */
-  int32_t max_chunk;       /* largest prefill chunk (tokens per call), <= 256 */
+  int32_t max_chunk;       /* largest prefill chunk (tokens per call), <= 512 */
   int32_t max_batch;       /* number of sequences (KV slots); largest decode batch */
   /* Attention variants (engine.zig Engine.forward hands its attention a
    * logit soft-cap and, on a sliding layer, a window): */

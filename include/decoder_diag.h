@@ -35,7 +35,7 @@ int dec_diag_pack_w32(const uint16_t *d_W, int32_t rows, int32_t K, uint16_t *d_
  * Engine.prefill: a chunk of token columns shares one pass over the
  * weights).  A bf16 [planes][M][K]: planes 1 = plain bf16, 2 = hi plane then
  * lo plane (the activation is their sum); d_Wp = W [N][K] packed by
- * dec_diag_pack_w32; C fp32 [M][N].  2 <= M <= 128, N % 32 == 0,
+ * dec_diag_pack_w32; C fp32 [M][N].  2 <= M <= 512, N % 32 == 0,
  * K % 16 == 0.  ksplit > 1 splits K over blocks; the fp32 partials need
  * part_elems >= ksplit * M * N floats at d_part, reduced in fixed split
  * order.  DEC_E_INVALID on bad sizes. */

@@ -92,7 +92,7 @@ TINY = Shape("gqa-tiny-h256-l2", hidden=256, n_layers=2, n_heads=4, n_kv_heads=2
 C135M = Shape("gqa-135m-h576-l30", hidden=576, n_layers=30, n_heads=9, n_kv_heads=3, head_dim=64,
               vocab=49152, ffn_inter=1536, tied=True, rope_base=1e4, max_seq=2048)
 C8B = Shape("gqa-8b-h4096-l32", hidden=4096, n_layers=32, n_heads=32, n_kv_heads=8, head_dim=128,
-            vocab=128256, ffn_inter=14336, rope_base=5e5, max_seq=4096, kv_bf16=True)
+            vocab=128256, ffn_inter=14336, rope_base=5e5, max_seq=4096, max_chunk=512, kv_bf16=True)
 MOE = Shape("moe-e60x1408-top4-h2048-l24", hidden=2048, n_layers=24, n_heads=16, n_kv_heads=16,
             head_dim=128, vocab=151936, n_experts=60, top_k=4, expert_inter=1408,
             shared_inter=5632, shared_gate=True, norm_topk_prob=0, qkv_bias=True,

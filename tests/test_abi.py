@@ -53,7 +53,7 @@ def test_strerror_and_workspace_sizes():
 
 
 @pytest.mark.parametrize("field,value", [("n_kv_heads", 3), ("head_dim", 96), ("max_chunk", 0),
-                                         ("hidden", 100), ("max_chunk", 512), ("sliding_window", -1),
+                                         ("hidden", 100), ("max_chunk", 1024), ("sliding_window", -1),
                                          ("attn_softcap", -1.0), ("qk_norm", 2), ("weight_quant", 2),
                                          ("kv_page_size", 48), ("kv_page_size", -32)])
 def test_invalid_configs_rejected(field, value):

@@ -46,7 +46,8 @@ def test_projection_kernel_matches_numpy(M, N, K):
 
 @pytest.mark.parametrize("M,N,K,ksplit,planes", [(17, 64, 64, 1, 1), (37, 96, 688, 1, 2), (64, 256, 4096, 1, 2),
                                                  (100, 64, 576, 3, 2), (128, 512, 4096, 4, 2),
-                                                 (128, 288, 1536, 1, 1), (65, 32, 256, 7, 2), (2, 32, 16, 1, 2)])
+                                                 (128, 288, 1536, 1, 1), (65, 32, 256, 7, 2), (2, 32, 16, 1, 2),
+                                                 (512, 256, 4096, 2, 2), (300, 96, 1536, 1, 2), (512, 128, 256, 1, 1)])
 def test_chunk_projection_kernel_matches_oracle(M, N, K, ksplit, planes):
     """The prefill chunk kernel on packed weights: ragged row counts (several
     64-row blocks and a tail), N not a multiple of the 256-row block tile, K
@@ -339,13 +340,13 @@ def test_gemv_kernel_matches_oracle(N, K):
     assert np.all(np.abs(got - want) <= 1e-6 * np.sqrt(K) * scale + 1e-30)
 
 
-@pytest.mark.parametrize("rows", [128, 37, 9, 1])
+@pytest.mark.parametrize("rows", [512, 300, 128, 37, 9, 1])
 def test_8b_shape_two_layer_trace(rows):
     """8B-class layer shapes (hidden 4096, 32/8 heads of 128, SwiGLU 14336) in
     a 2-layer model with a small vocabulary: residual stream after each layer
     for a chunk of `rows` tokens, against the oracle."""
     from synth.workloads import C8B
-    shape = C8B.with_(name="gqa-8b-layers-2", n_layers=2, vocab=1024, max_seq=256)
+    shape = C8B.with_(name="gqa-8b-layers-2", n_layers=2, vocab=1024, max_seq=576)
     W = host_weights(shape)
     ids = prompt(shape, rows)
     tr = oracle.Model(shape, W).forward(ids, 0, logits_mode=0, trace=True)["trace"]
@@ -363,6 +364,37 @@ def test_8b_shape_two_layer_trace(rows):
         rel = np.linalg.norm(got - want) / np.linalg.norm(want)
         log("rows", rows, "layer", layers, "rel max err", err, "rel l2", rel)
         assert rel < 5e-3
+
+
+def test_8b_shape_prefill_in_chunks_of_512():
+    """Compute-bound prefill chunks (engine.zig Options.chunk: a wider chunk
+    reads the weights once for more tokens; pipeline.rs prefill_chunk: tall
+    panels keep the matrix units busy): a 1000-token prompt in chunks of
+    512 and 488 on the 8B-class layer shapes (2 layers, small vocabulary),
+    every row's logits of the second chunk against the oracle, then a
+    decode step."""
+    from synth.workloads import C8B
+    shape = C8B.with_(name="gqa-8b-layers-2", n_layers=2, vocab=1024, max_seq=1024)
+    W = host_weights(shape)
+    ids = [int(t) for t in prompt(shape, 1001)]
+    m = oracle.Model(shape, W)
+    m.forward(ids[:512], 0, logits_mode=0)
+    want = m.forward(ids[512:1000], 512, logits_mode=2)["logits"]
+    dec, _ = make_decoder(shape, W)
+    dec.prefill_chunk(0, ids[:512], 0, logits_mode=0)
+    logits = torch.empty((488, shape.vocab), dtype=torch.float32, device="cuda")
+    dec.prefill_chunk(0, ids[512:1000], 512, logits_mode=2, logits=logits)
+    torch.cuda.synchronize()
+    got = logits.cpu().numpy()
+    worst = None
+    for i in range(488):
+        st = compare_logits(got[i], want[i], f"chunk 512 row {i}")
+        assert_parity(st, f"chunk 512 row {i}")
+        worst = st if worst is None or st["max_abs"] > worst["max_abs"] else worst
+    log("8b2 chunk of 488 after 512, worst row", worst)
+    want = m.forward([ids[1000]], 1000)["logits"]
+    lg, _ = decode(dec, [0], [ids[1000]])
+    assert_parity(compare_logits(lg[0], want, "decode after 512-row chunks"), "decode after 512-row chunks")
 
 
 @pytest.mark.parametrize("E,k,renorm", [(60, 4, 0), (60, 4, 1), (8, 2, 0), (256, 8, 1)])
