@@ -404,8 +404,9 @@ def main():
     ap.add_argument("--attn-softcap", type=float, default=0.0, help="attention variant: logit soft-cap")
     ap.add_argument("--attn-sinks", action="store_true", help="attention variant: per-head sink logits")
     ap.add_argument("--qk-norm", action="store_true", help="attention variant: per-head RMSNorm of q and k")
-    ap.add_argument("--weight-quant", action="store_true",
-                    help="int8 weights with a power-of-two scale per row (decode streams the codes)")
+    ap.add_argument("--weight-quant", nargs="?", const=8, type=int, default=0, choices=(0, 8, 4),
+                    help="quantised weights: 8 = int8 with a power-of-two scale per row, 4 = 4-bit with a "
+                         "power-of-two scale per group of 32 (decode streams the codes)")
     ap.add_argument("--kv-page", type=int, default=0,
                     help="paged KV cache: pages of this many positions (the pool holds every sequence's max_seq)")
     ap.add_argument("--wide-chunk", type=int, default=512,
@@ -473,7 +474,7 @@ def main():
     if args.qk_norm:
         variant["qk_norm"] = True
     if args.weight_quant:
-        variant["weight_quant"] = 1
+        variant["weight_quant"] = 1 if args.weight_quant == 8 else 2
     if args.kv_page:
         variant["kv_page_size"] = args.kv_page
         variant["kv_pages"] = work.batch * -(-shape.max_seq // args.kv_page)
@@ -501,8 +502,10 @@ def main():
     result = {"metric": METRIC, "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
               "data": "synthetic (seeded SplitMix64/Box-Muller bf16 weights and uniform token ids)"}
-    if variant.get("weight_quant"):
+    if variant.get("weight_quant") == 1:
         result["dtype"] = "int8 weights (power-of-two row scales), fp32 accumulate"
+    elif variant.get("weight_quant") == 2:
+        result["dtype"] = "4-bit weights (power-of-two scale per 32), fp32 accumulate"
     batch = work.batch
     seqs = list(range(batch))
 
@@ -585,7 +588,8 @@ def main():
     per_launch_bytes = d["bytes"] / d["launches"]
     per_launch_s = d["ms"] / d["launches"] * 1e-3
     achieved = per_launch_bytes / per_launch_s / 1e9
-    traffic = counter_traffic(f"counters_{dom}_decode_{args.workload}{'_q8' if variant.get('weight_quant') else ''}.md")
+    qsuf = {1: "_q8", 2: "_q4"}.get(variant.get("weight_quant", 0), "")
+    traffic = counter_traffic(f"counters_{dom}_decode_{args.workload}{qsuf}.md")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": f"{dom} ({'gemv_kernel, batch-1 projection' if dom != 'attn' else 'attn_kernel'}, decode)", "bytes_per_launch": per_launch_bytes,

@@ -77,6 +77,8 @@ SIGNATURES = {
     "dec_diag_rmsnorm": (ctypes.c_int, [_P, _P, _I32, _I32, ctypes.c_double, _P, _P]),
     "dec_diag_quantize_rows": (ctypes.c_int, [_P, ctypes.c_int64, _I32, _P, _P, _P, _P]),
     "dec_diag_gemv": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _P]),
+    "dec_diag_quantize_q4": (ctypes.c_int, [_P, ctypes.c_int64, _I32, _P, _P, _P, _P]),
+    "dec_diag_gemv_q4": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _P]),
     "dec_diag_moe_route": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "decoder_debug_layer_limit": (ctypes.c_int, [_P, _I32]),
     "decoder_debug_read_x": (ctypes.c_int, [_P, _P, _I32]),
@@ -319,6 +321,20 @@ def diag_gemm_chunk_noalloc(A, Wp, C, ksplit, stream):
     N = Wp.shape[0]
     _check(lib().dec_diag_gemm_chunk_noalloc(_ptr(A), planes, M, K, _ptr(Wp), N, _ptr(C), ksplit,
                                              ctypes.c_void_p(stream)), None, "dec_diag_gemm_chunk_noalloc")
+
+
+def diag_quantize_q4(W, codes, exps, deq, stream):
+    """W bf16 [rows][K] -> codes uint8 [rows][K / 2], exps int8 [rows][K / 32], deq bf16 [rows][K]."""
+    rows, K = W.shape
+    _check(lib().dec_diag_quantize_q4(_ptr(W), rows, K, _ptr(codes), _ptr(exps), _ptr(deq),
+                                      ctypes.c_void_p(stream)), None, "dec_diag_quantize_q4")
+
+
+def diag_gemv_q4(a, codes, exps, y, stream):
+    N = codes.shape[0]
+    K = a.shape[0]
+    _check(lib().dec_diag_gemv_q4(_ptr(a), K, _ptr(codes), _ptr(exps), N, _ptr(y), ctypes.c_void_p(stream)),
+           None, "dec_diag_gemv_q4")
 
 
 def diag_gemv(a, W, y, stream):

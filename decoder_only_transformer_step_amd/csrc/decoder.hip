@@ -82,16 +82,22 @@ QuantSpec quant_spec(const decoder_config_t *c) {
 
 size_t quant_piece(size_t bytes) { return (bytes + 255) / 256 * 256; }
 
-size_t quant_matrix_bytes(int64_t rows, int K) {
-  return quant_piece((size_t)rows * K) + quant_piece((size_t)rows * 4) + quant_piece((size_t)rows * K * 2);
+// int8: codes [rows][K], scales [rows] fp32; 4-bit: codes [rows][K / 2],
+// exponents [rows][K / 32] int8; both: the dequantised bf16 copy [rows][K]
+size_t quant_code_bytes(int wq, int64_t rows, int K) { return wq == 2 ? (size_t)rows * K / 2 : (size_t)rows * K; }
+size_t quant_scale_bytes(int wq, int64_t rows, int K) { return wq == 2 ? (size_t)rows * (K / 32) : (size_t)rows * 4; }
+
+size_t quant_matrix_bytes(int wq, int64_t rows, int K) {
+  return quant_piece(quant_code_bytes(wq, rows, K)) + quant_piece(quant_scale_bytes(wq, rows, K)) +
+         quant_piece((size_t)rows * K * 2);
 }
 
 size_t quant_bytes(const decoder_config_t *c) {
   if (!c->weight_quant) return 0;
   const QuantSpec qs = quant_spec(c);
-  size_t b = quant_matrix_bytes(c->vocab, c->hidden);
+  size_t b = quant_matrix_bytes(c->weight_quant, c->vocab, c->hidden);
   for (int i = 0; i < QUANT_MATS; ++i)
-    if (qs.rows[i] > 0) b += (size_t)c->n_layers * quant_matrix_bytes(qs.rows[i], qs.K[i]);
+    if (qs.rows[i] > 0) b += (size_t)c->n_layers * quant_matrix_bytes(c->weight_quant, qs.rows[i], qs.K[i]);
   return b;
 }
 
@@ -148,10 +154,13 @@ bool config_ok(const decoder_config_t *c) {
   if (c->qk_norm != 0 && c->qk_norm != 1) return false;
   if (c->kv_page_size < 0 || (c->kv_page_size > 0 && (c->kv_page_size % 32 || c->kv_pages < 1)))
     return false;
-  // quantised GEMVs load 16 codes per lane: every row length a multiple of 16
-  if (c->weight_quant != 0 &&
-      (c->weight_quant != 1 || c->hidden % 16 || c->ffn_inter % 16 || c->expert_inter % 16 || c->shared_inter % 16))
-    return false;
+  // quantised GEMVs load 16 int8 codes (one row scale) or 32 4-bit codes (one
+  // group of 32 with its scale) per lane: every row length a multiple of that
+  if (c->weight_quant < 0 || c->weight_quant > 2) return false;
+  if (c->weight_quant != 0) {
+    const int m = c->weight_quant == 2 ? 32 : 16;
+    if (c->hidden % m || c->ffn_inter % m || c->expert_inter % m || c->shared_inter % m) return false;
+  }
   if (c->n_experts > 0) {
     if (c->n_experts > 256 || c->top_k <= 0 || c->top_k > 8 || c->top_k > c->n_experts) return false;
     if (c->expert_inter <= 0 || c->expert_inter % 8 || c->shared_inter < 0 || c->shared_inter % 8)
@@ -257,8 +266,9 @@ struct decoder {
   };
   std::vector<Packed> packed;
   struct QuantW {
-    const int8_t *q = nullptr;  // int8 codes [rows][K]
-    const float *s = nullptr;   // per-row scales 2^e
+    const int8_t *q = nullptr;  // int8 codes [rows][K], or 4-bit codes [rows][K / 2]
+    const float *s = nullptr;   // int8: per-row scales 2^e
+    const int8_t *e = nullptr;  // 4-bit: per-group exponents [rows][K / 32]
   };
   std::vector<std::array<QuantW, 6>> qw;  // per layer, in quant_spec order (weight_quant)
   QuantW qhead;                           // the lm-head (weight_quant)
@@ -627,7 +637,8 @@ int gemv(decoder *D, int node, int epi, const GemvArgs &g, int *blocks = nullptr
   const double nr = (epi == EPI_SWIGLU || epi == EPI_QKV) ? 2.0 : 1.0;
   const double slots = g.slot_expert ? g.n_slots : 1;
   const double out_words = epi == EPI_ADD ? 2 : epi == EPI_MOE_ADD ? 2 + g.moe_k : 1;
-  const double wrow = g.Wq ? (double)g.K + 4.0 : (double)g.K * 2;  // weight bytes per row (+ its scale)
+  // weight bytes per row (+ its scale or group exponents)
+  const double wrow = g.qbits == 8 ? (double)g.K + 4.0 : g.qbits == 4 ? g.K / 2.0 + g.K / 32.0 : (double)g.K * 2;
   const double part2 = g.W2 ? g.n_items2 * (nr * wrow + 4.0) : 0.0;
   NodeTimer timer(D, node,
                   slots * (nr * g.n_items * wrow + g.K * 4.0 + g.n_items * 4.0 * out_words) + part2,
@@ -644,6 +655,8 @@ GemvArgs quant(const decoder *D, GemvArgs g, int l, int i) {
   const decoder::QuantW &w = l < 0 ? D->qhead : D->qw[l][i];
   g.Wq = w.q;
   g.wscale = w.s;
+  g.wexp = w.e;
+  g.qbits = D->c.weight_quant == 2 ? 4 : 8;
   return g;
 }
 
@@ -796,6 +809,7 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
   if (c.weight_quant && Is > 0) {
     eg.W2q = D->qw[l][2].q;
     eg.w2scale = D->qw[l][2].s;
+    eg.w2exp = D->qw[l][2].e;
   }
   if ((rc = gemv(D, DEC_NODE_EXPERTS, EPI_SWIGLU, eg))) return rc;
   GemvArgs ed = gemv_args(W.w_exp_down, D->f32_hexp, Ie, H, D->yexp);
@@ -1157,7 +1171,7 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
     const int qd = cfg->n_heads * cfg->head_dim;
     const int kmax = std::max(std::max(cfg->hidden, qd), std::max(std::max(cfg->ffn_inter, cfg->shared_inter),
                                                                       cfg->expert_inter));
-    D->single_row_ok = gemv_lds(kmax, cfg->weight_quant != 0) <= GEMV_MAX_LDS;
+    D->single_row_ok = gemv_lds(kmax, cfg->weight_quant == 2 ? 4 : cfg->weight_quant == 1 ? 8 : 0) <= GEMV_MAX_LDS;
   }
   if (cfg->n_experts > 0) {
     D->rlogits = carve<float>(D, L.rlogits);
@@ -1182,17 +1196,25 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
   if (cfg->weight_quant) {
     const QuantSpec qs = quant_spec(cfg);
     char *qp = carve<char>(D, L.quant);
+    const int wq = cfg->weight_quant;
     auto quant = [&](const uint16_t *src, int64_t rows, int K, const uint16_t **dst, decoder::QuantW &qw) {
       int8_t *q = reinterpret_cast<int8_t *>(qp);
-      qp += quant_piece((size_t)rows * K);
-      float *sc = reinterpret_cast<float *>(qp);
-      qp += quant_piece((size_t)rows * 4);
+      qp += quant_piece(quant_code_bytes(wq, rows, K));
+      char *sc = qp;
+      qp += quant_piece(quant_scale_bytes(wq, rows, K));
       uint16_t *dq = reinterpret_cast<uint16_t *>(qp);
       qp += quant_piece((size_t)rows * K * 2);
       qw.q = q;
-      qw.s = sc;
       *dst = dq;
-      return launch_quantize_rows(src, rows, K, q, sc, dq, (hipStream_t)stream) == hipSuccess;
+      if (wq == 2) {
+        int8_t *ex = reinterpret_cast<int8_t *>(sc);
+        qw.e = ex;
+        return launch_quantize_q4(src, rows, K, reinterpret_cast<uint8_t *>(q), ex, dq, (hipStream_t)stream) ==
+               hipSuccess;
+      }
+      qw.s = reinterpret_cast<float *>(sc);
+      return launch_quantize_rows(src, rows, K, q, reinterpret_cast<float *>(sc), dq, (hipStream_t)stream) ==
+             hipSuccess;
     };
     D->qw.assign(cfg->n_layers, std::array<decoder::QuantW, 6>{});
     bool ok = quant(D->lm_head, cfg->vocab, cfg->hidden, &D->lm_head, D->qhead);
@@ -1590,6 +1612,24 @@ int dec_diag_gemm_chunk_noalloc(const uint16_t *d_A, int32_t planes, int32_t M, 
 int dec_diag_gemv(const float *d_a, int32_t K, const uint16_t *d_W, int32_t N, float *d_y, void *stream) {
   if (!d_a || !d_W || !d_y || N < 1 || K < 8 || K % 8 || gemv_lds(K) > GEMV_MAX_LDS) return DEC_E_INVALID;
   GemvArgs g = gemv_args(d_W, d_a, K, N, d_y);
+  return launch_gemv(g, EPI_STORE, (hipStream_t)stream) == hipSuccess ? DEC_OK : DEC_E_HIP;
+}
+
+int dec_diag_quantize_q4(const uint16_t *d_W, int64_t rows, int32_t K, uint8_t *d_codes, int8_t *d_exps,
+                         uint16_t *d_deq, void *stream) {
+  if (!d_W || !d_codes || !d_exps || !d_deq || rows < 1 || K < 32 || K % 32) return DEC_E_INVALID;
+  return launch_quantize_q4(d_W, rows, K, d_codes, d_exps, d_deq, (hipStream_t)stream) == hipSuccess ? DEC_OK
+                                                                                                 : DEC_E_HIP;
+}
+
+int dec_diag_gemv_q4(const float *d_a, int32_t K, const uint8_t *d_codes, const int8_t *d_exps, int32_t N,
+                     float *d_y, void *stream) {
+  if (!d_a || !d_codes || !d_exps || !d_y || N < 1 || K < 32 || K % 32 || gemv_lds(K, 4) > GEMV_MAX_LDS)
+    return DEC_E_INVALID;
+  GemvArgs g = gemv_args(nullptr, d_a, K, N, d_y);
+  g.Wq = reinterpret_cast<const int8_t *>(d_codes);
+  g.wexp = d_exps;
+  g.qbits = 4;
   return launch_gemv(g, EPI_STORE, (hipStream_t)stream) == hipSuccess ? DEC_OK : DEC_E_HIP;
 }
 

@@ -29,6 +29,14 @@
 //    1 KB loads then carry 16 weights per lane (k = 16 l + 1024 s), the
 //    activation slots hold 16 elements per lane and step, and the row's
 //    scale multiplies the finished dot product: half the bytes per weight.
+//  * 4-bit weights (Q = 2): one 16-byte lane load is 32 codes, exactly one
+//    group with its own power-of-two scale (k = 32 l + 2048 s).  Codes are
+//    stored offset by 8 (nibble n = q + 8), so a code converts with one
+//    unsigned byte-to-float instruction after the nibbles are split into
+//    bytes; the offset comes back as 8 times the group's activation sum,
+//    computed once per block in LDS.  The group's dot product is then scaled
+//    by its 2^e: a quarter of the bf16 bytes per weight, plus one exponent
+//    byte per 32 weights.
 #include <algorithm>
 
 #include "common.h"
@@ -66,10 +74,15 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)
 // a select on its value, makes it wait for everything in flight).
 __device__ u32x4 gv_zero[1];
 
-// Elements per lane and per 1 KB step: 8 bf16 or 16 int8 weights.
+// Elements per lane and per 1 KB step: 8 bf16, 16 int8 or 32 4-bit weights.
 template <int Q>
 constexpr int gv_epl() {
-  return Q ? 16 : 8;
+  return Q == 2 ? 32 : Q ? 16 : 8;
+}
+// Bytes of a row of K weights.
+template <int Q>
+__device__ __forceinline__ int64_t gv_row_bytes(int K) {
+  return Q == 2 ? K / 2 : Q ? K : 2 * (int64_t)K;
 }
 // 1 KB steps per register buffer (all rows of the item together): 8 KB for
 // bf16; 4 KB for int8, so that a row of a K = 14336 projection still takes
@@ -106,21 +119,75 @@ __device__ __forceinline__ int xs_slot(int k) {  // k: element index, a multiple
 __device__ __forceinline__ int xs_slot_q(int k) {
   return ((k >> 10) * 4 + ((k >> 2) & 3)) * 64 + ((k & 1023) >> 4);
 }
+// 4-bit weights: lane l's 32 elements of step s in eight slots (8 s + h) 64 + l.
+__device__ __forceinline__ int xs_slot_q4(int k) {
+  return ((k >> 11) * 8 + ((k >> 2) & 7)) * 64 + ((k & 2047) >> 5);
+}
 template <int Q>
 __device__ __forceinline__ int xs_slot_t(int k) {
-  return Q ? xs_slot_q(k) : xs_slot(k);
+  return Q == 2 ? xs_slot_q4(k) : Q ? xs_slot_q(k) : xs_slot(k);
+}
+
+// 4-bit weights: the group exponents of UNR steps for every row (one byte per
+// lane and step; lanes past the row read the zero page: exponent 0, and
+// their codes and activations are zero).
+template <int R, int UNR>
+__device__ __forceinline__ void load_exps(int (&ev)[UNR][R], const int8_t *const (&ep)[R], int s0, int K,
+                                          int lane) {
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) {
+    const int st = s0 + u;
+    const bool ok = st * 2048 + lane * 32 < K;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      ev[u][r] = *(ok ? ep[r] + st * 64 : reinterpret_cast<const int8_t *>(gv_zero));
+  }
+}
+
+// 4-bit dot product of one lane's group: nibbles n = q + 8, split into the
+// bytes of lo (even elements) and hi (odd elements) of each 32-bit word;
+// returns sum n_j x_j.  The empty asm statements only pin lo and hi as
+// values: without them the compiler extracts every nibble with its own
+// bit-field instruction instead of converting each byte of the two masked
+// words directly (v_cvt_f32_ubyte0..3), one VALU instruction more per code.
+__device__ __forceinline__ float q4_dot(const u32x4 &w, const f32x4 (&x)[8]) {
+  float d = 0.f;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    uint32_t lo = w[h] & 0x0F0F0F0Fu, hi = (w[h] >> 4) & 0x0F0F0F0Fu;
+    asm("" : "+v"(lo));
+    asm("" : "+v"(hi));
+    const f32x4 xa = x[2 * h], xb = x[2 * h + 1];
+    d = fmaf((float)(lo & 0xFFu), xa[0], d);
+    d = fmaf((float)(hi & 0xFFu), xa[1], d);
+    d = fmaf((float)((lo >> 8) & 0xFFu), xa[2], d);
+    d = fmaf((float)((hi >> 8) & 0xFFu), xa[3], d);
+    d = fmaf((float)((lo >> 16) & 0xFFu), xb[0], d);
+    d = fmaf((float)((hi >> 16) & 0xFFu), xb[1], d);
+    d = fmaf((float)(lo >> 24), xb[2], d);
+    d = fmaf((float)(hi >> 24), xb[3], d);
+  }
+  return d;
 }
 
 __device__ __forceinline__ float i8f(uint32_t w, int j) { return (float)(int8_t)(w >> (8 * j)); }
 
 // acc[r] += dot(weights of batch, activation) over UNR steps.
-template <int R, int UNR, int Q>
-__device__ __forceinline__ void fma_batch(float (&acc)[R], const u32x4 (&v)[UNR][R], const f32x4 *xs, int s0,
-                                          int steps, int lane) {
+template <int R, int UNR, int Q, int EU>
+__device__ __forceinline__ void fma_batch(float (&acc)[R], const u32x4 (&v)[UNR][R], const int (&ev)[EU][R],
+                                          const f32x4 *xs, const float *gsum, int s0, int steps, int lane) {
 #pragma unroll
   for (int u = 0; u < UNR; ++u) {
     const int st = s0 + u;
-    if (Q && st < steps) {
+    if (Q == 2 && st < steps) {
+      f32x4 x[8];
+#pragma unroll
+      for (int h = 0; h < 8; ++h) x[h] = xs[(st * 8 + h) * 64 + lane];
+      const float off = 8.0f * gsum[st * 64 + lane];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        acc[r] = fmaf(q4_dot(v[u][r], x) - off, __builtin_amdgcn_ldexpf(1.0f, ev[EU == UNR ? u : 0][r]), acc[r]);
+    } else if (Q == 1 && st < steps) {
       f32x4 x[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h) x[h] = xs[(st * 4 + h) * 64 + lane];
@@ -203,13 +270,12 @@ __device__ __forceinline__ ItemPre item_prefetch(const GemvArgs &g, int out_row,
 template <int EPI, int NR, int Q>
 __device__ __forceinline__ void item_ptrs(const GemvArgs &g, const char *W, int it, int lane, int out_row,
                                           int (&rows)[NR], const char *(&wp)[NR], ItemPre &pre) {
-  constexpr int EB = Q ? 1 : 2;  // bytes per weight
   int r0, r1;
   item_rows<EPI>(g, it, r0, r1);
   rows[0] = r0;
   rows[NR - 1] = r1;
 #pragma unroll
-  for (int r = 0; r < NR; ++r) wp[r] = W + ((int64_t)rows[r] * g.K) * EB + lane * 16;
+  for (int r = 0; r < NR; ++r) wp[r] = W + (int64_t)rows[r] * gv_row_bytes<Q>(g.K) + lane * 16;
   pre = item_prefetch<EPI>(g, out_row, r0, r1);
 }
 
@@ -277,7 +343,11 @@ __device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, in
 // the activation is loaded ahead of the weights when it fits in registers,
 // so the prologue waits only for it.  NCH: the row's chunk count when it is
 // 1 or 2 (no refills), else 0 (the refill loop).
-template <int EPI, int NCH, int WV, int Q>
+// IPW > 1 (4-bit weights, one chunk per item): each wave takes IPW items,
+// wave w of block b items (b IPW + j) WV + w, and loads item j + 1 into the
+// other register buffer while item j is summed, so the activation prologue
+// of a block is paid once for IPW times the weights.
+template <int EPI, int NCH, int WV, int Q, int IPW>
 __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
   constexpr int NR = gv_rows<EPI>(), CH = gv_ch<Q>() / NR, NT = WV * WAVE, PRN = 32 / WV, PRH = PRN / 2;
   constexpr int SE = 64 * gv_epl<Q>();  // elements per 1 KB step
@@ -298,6 +368,7 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
       g.W = ga.W2;
       g.Wq = ga.W2q;
       g.wscale = ga.w2scale;
+      g.wexp = ga.w2exp;
       g.N = ga.N2;
       g.n_items = ga.n_items2;
       g.C = ga.C2;
@@ -311,8 +382,10 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
   const float *xin = g.a_f32;
   int out_row = 0;
   if (g.slot_expert) {
-    W += (int64_t)g.slot_expert[slot] * g.w_group_stride * (Q ? 1 : 2);
-    if (Q) g.wscale += (int64_t)g.slot_expert[slot] * (g.w_group_stride / g.K);  // the expert's row scales
+    const int64_t ex = g.slot_expert[slot];
+    W += Q == 2 ? ex * g.w_group_stride / 2 : ex * g.w_group_stride * (Q ? 1 : 2);
+    if (Q == 1) g.wscale += ex * (g.w_group_stride / g.K);  // the expert's row scales
+    if (Q == 2) g.wexp += ex * (g.w_group_stride / 32);     // the expert's group exponents
     if (xin) xin += (int64_t)slot * g.a_slot_stride;
     out_row = slot;
   }
@@ -320,16 +393,22 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
   const int steps = (K + SE - 1) / SE, nch = NCH ? NCH : (steps + CH - 1) / CH;
-  const int it = bx * WV + wave;
+  static_assert(IPW == 1 || (NCH == 1 && Q == 2), "several items per wave: 4-bit weights, one chunk per item");
+  const int it = bx * WV * IPW + wave;
   const bool valid = it < g.n_items;
   int rows[NR];
   const char *wp[NR];
   ItemPre pre;
   item_ptrs<EPI, NR, Q>(g, W, valid ? it : g.n_items - 1, lane, out_row, rows, wp, pre);
-  // the rows' scales, loaded with the first weights (quantised weights only)
+  // the rows' scales, loaded with the first weights (int8 weights only)
   float wsc[NR];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) wsc[r] = Q ? g.wscale[rows[r]] : 1.0f;
+  for (int r = 0; r < NR; ++r) wsc[r] = Q == 1 ? g.wscale[rows[r]] : 1.0f;
+  // 4-bit weights: the rows' group exponents, lane l's at step s in byte 64 s + l
+  constexpr int EU = Q == 2 ? CH : 1;
+  const int8_t *ep[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) ep[r] = Q == 2 ? g.wexp + (int64_t)rows[r] * (K / 32) + lane : nullptr;
 
   // activation into registers first when it fits.  Mode 1: x and gamma
   // (RMSNorm); 2: fp32 x; 3: bf16 x; 0: read after the weights are issued.
@@ -351,8 +430,13 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
 
   // (loads past the row read the zero page: no load sits under a branch)
   u32x4 buf0[CH][NR], buf1[CH][NR];
+  int ex0[EU][NR], ex1[EU][NR];
   load_batch<NR, CH, Q>(buf0, wp, 0, K, lane);
-  if (NCH != 1) load_batch<NR, CH, Q>(buf1, wp, CH, K, lane);
+  if (Q == 2) load_exps<NR, EU>(ex0, ep, 0, K, lane);
+  if (NCH != 1) {
+    load_batch<NR, CH, Q>(buf1, wp, CH, K, lane);
+    if (Q == 2) load_exps<NR, EU>(ex1, ep, CH, K, lane);
+  }
 
   // activation -> LDS (fp32, with the RMSNorm when gamma is set)
   auto put4 = [&](int k, f32x4 v) { xs[xs_slot_t<Q>(k)] = v; };
@@ -412,6 +496,83 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
   // zero padding up to whole steps
   for (int k = K + threadIdx.x * 4; k < steps * SE; k += NT * 4) put4(k, f32x4{0.f, 0.f, 0.f, 0.f});
   __syncthreads();
+  // 4-bit weights: each lane's group sum of the activation, for the code offset
+  float *gsum = reinterpret_cast<float *>(xs + (int64_t)steps * SE / 4);
+  if (Q == 2) {
+    for (int i = threadIdx.x; i < steps * 64; i += NT) {
+      const int s = i >> 6, l = i & 63;
+      float t = 0.f;
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        const f32x4 v = xs[(s * 8 + h) * 64 + l];
+        t += (v[0] + v[1]) + (v[2] + v[3]);
+      }
+      gsum[i] = t;
+    }
+    __syncthreads();
+  }
+
+  if constexpr (IPW > 1) {
+    // item j from one buffer while item j + 1 streams into the other
+    int rows_n[NR];
+    const char *wp_n[NR];
+    const int8_t *ep_n[NR];
+    ItemPre pre_n;
+    float bvw = -INFINITY;
+    int biw = 0x7fffffff;
+    auto one = [&](u32x4 (&cur)[CH][NR], int (&cex)[EU][NR], u32x4 (&nxt)[CH][NR], int (&nex)[EU][NR], int j) {
+      const int itj = it + j * WV;
+      if (j + 1 < IPW) {
+        const int itn = min(itj + WV, g.n_items - 1);
+        item_ptrs<EPI, NR, Q>(g, W, itn, lane, out_row, rows_n, wp_n, pre_n);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) ep_n[r] = g.wexp + (int64_t)rows_n[r] * (K / 32) + lane;
+        load_batch<NR, CH, Q>(nxt, wp_n, 0, K, lane);
+        load_exps<NR, EU>(nex, ep_n, 0, K, lane);
+      }
+      float a[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) a[r] = 0.f;
+      fma_batch<NR, CH, Q, EU>(a, cur, cex, xs, gsum, 0, steps, lane);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) a[r] = wave_sum(a[r]);
+      const bool vj = itj < g.n_items;
+      if (vj && lane == 0) item_epilogue<EPI>(g, out_row, rows[0], rows[NR - 1], a[0], a[NR - 1], pre);
+      if (EPI == EPI_LOGITS && vj && better(a[0], rows[0], bvw, biw)) {
+        bvw = a[0];
+        biw = rows[0];
+      }
+      if (j + 1 < IPW) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) rows[r] = rows_n[r];
+        pre = pre_n;
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < IPW; j += 2) {
+      one(buf0, ex0, buf1, ex1, j);
+      if (j + 1 < IPW) one(buf1, ex1, buf0, ex0, j + 1);
+    }
+    if (EPI == EPI_LOGITS) {
+      if (lane == 0) {
+        bv_s[wave] = bvw;
+        bi_s[wave] = biw;
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        float bv = bv_s[0];
+        int bi = bi_s[0];
+        for (int w = 1; w < WV; ++w)
+          if (better(bv_s[w], bi_s[w], bv, bi)) {
+            bv = bv_s[w];
+            bi = bi_s[w];
+          }
+        g.part_val[blockIdx.x] = bv;
+        g.part_idx[blockIdx.x] = bi;
+      }
+    }
+    return;
+  }
 
   float acc[NR];
 #pragma unroll
@@ -419,14 +580,16 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
   int c = 0;
   if (NCH == 0) {
     for (; c + 2 < nch; c += 2) {
-      fma_batch<NR, CH, Q>(acc, buf0, xs, c * CH, steps, lane);
+      fma_batch<NR, CH, Q, EU>(acc, buf0, ex0, xs, gsum, c * CH, steps, lane);
       load_batch<NR, CH, Q>(buf0, wp, (c + 2) * CH, K, lane);
-      fma_batch<NR, CH, Q>(acc, buf1, xs, (c + 1) * CH, steps, lane);
+      if (Q == 2) load_exps<NR, EU>(ex0, ep, (c + 2) * CH, K, lane);
+      fma_batch<NR, CH, Q, EU>(acc, buf1, ex1, xs, gsum, (c + 1) * CH, steps, lane);
       load_batch<NR, CH, Q>(buf1, wp, (c + 3) * CH, K, lane);
+      if (Q == 2) load_exps<NR, EU>(ex1, ep, (c + 3) * CH, K, lane);
     }
   }
-  fma_batch<NR, CH, Q>(acc, buf0, xs, c * CH, steps, lane);
-  if (NCH != 1) fma_batch<NR, CH, Q>(acc, buf1, xs, (c + 1) * CH, steps, lane);
+  fma_batch<NR, CH, Q, EU>(acc, buf0, ex0, xs, gsum, c * CH, steps, lane);
+  if (NCH != 1) fma_batch<NR, CH, Q, EU>(acc, buf1, ex1, xs, gsum, (c + 1) * CH, steps, lane);
 #pragma unroll
   for (int r = 0; r < NR; ++r) acc[r] = wave_sum(acc[r]) * wsc[r];
   if (valid && lane == 0) item_epilogue<EPI>(g, out_row, rows[0], rows[NR - 1], acc[0], acc[NR - 1], pre);
@@ -452,27 +615,65 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
   }
 }
 
+int device_cus();
+
+// Items per wave of a launch: 4-bit weights whose rows fit one chunk and
+// plain (not grouped) launches take GV_IPW items per wave.
+constexpr int GV_IPW = 4;
+template <int EPI, int Q>
+int gv_ipw(const GemvArgs &g) {
+  constexpr int CH = gv_ch<Q>() / gv_rows<EPI>(), SE = 64 * gv_epl<Q>();
+  const int nch = ((g.K + SE - 1) / SE + CH - 1) / CH;
+  if (Q != 2 || nch != 1 || g.slot_expert || g.W2) return 1;
+  // only while the grid keeps at least two 8-wave blocks per compute unit
+  return g.n_items >= 8 * GV_IPW * 2 * device_cus() ? GV_IPW : 1;
+}
+
 template <int EPI, int WV, int Q>
-void launch_w(const GemvArgs &g, int nch, size_t lds, hipStream_t st) {
-  dim3 grid((g.n_items + WV - 1) / WV, g.slot_expert ? g.n_slots : 1), block(WV * WAVE);
+void launch_w(const GemvArgs &g, int nch, int ipw, size_t lds, hipStream_t st) {
+  const int per_block = WV * ipw;
+  dim3 grid((g.n_items + per_block - 1) / per_block, g.slot_expert ? g.n_slots : 1), block(WV * WAVE);
   if (g.W2) grid = dim3(g.blocks1 * g.n_slots + (g.n_items2 + WV - 1) / WV, 1);
-  if (nch == 1) hipLaunchKernelGGL((gemv_kernel<EPI, 1, WV, Q>), grid, block, lds, st, g);
-  else if (nch == 2) hipLaunchKernelGGL((gemv_kernel<EPI, 2, WV, Q>), grid, block, lds, st, g);
-  else hipLaunchKernelGGL((gemv_kernel<EPI, 0, WV, Q>), grid, block, lds, st, g);
+  if (ipw > 1) {
+    if constexpr (Q == 2) hipLaunchKernelGGL((gemv_kernel<EPI, 1, WV, Q, GV_IPW>), grid, block, lds, st, g);
+  } else if (nch == 1) {
+    hipLaunchKernelGGL((gemv_kernel<EPI, 1, WV, Q, 1>), grid, block, lds, st, g);
+  } else if (nch == 2) {
+    hipLaunchKernelGGL((gemv_kernel<EPI, 2, WV, Q, 1>), grid, block, lds, st, g);
+  } else {
+    hipLaunchKernelGGL((gemv_kernel<EPI, 0, WV, Q, 1>), grid, block, lds, st, g);
+  }
 }
 
 template <int EPI, int Q>
-void launch_eq(const GemvArgs &g, int wv, size_t lds, hipStream_t st) {
+void launch_eq(const GemvArgs &g, int wv, int ipw, size_t lds, hipStream_t st) {
   constexpr int CH = gv_ch<Q>() / gv_rows<EPI>(), SE = 64 * gv_epl<Q>();
   const int nch = ((g.K + SE - 1) / SE + CH - 1) / CH;
-  if (wv == 4) launch_w<EPI, 4, Q>(g, nch, lds, st);
-  else launch_w<EPI, 8, Q>(g, nch, lds, st);
+  if (wv == 4) launch_w<EPI, 4, Q>(g, nch, ipw, lds, st);
+  else launch_w<EPI, 8, Q>(g, nch, ipw, lds, st);
+}
+
+template <int EPI>
+int ipw_of(const GemvArgs &g) {
+  return g.qbits == 4 ? gv_ipw<EPI, 2>(g) : 1;
 }
 
 template <int EPI>
 void launch_e(const GemvArgs &g, int wv, size_t lds, hipStream_t st) {
-  if (g.Wq) launch_eq<EPI, 1>(g, wv, lds, st);
-  else launch_eq<EPI, 0>(g, wv, lds, st);
+  if (g.qbits == 4) launch_eq<EPI, 2>(g, wv, ipw_of<EPI>(g), lds, st);
+  else if (g.qbits == 8) launch_eq<EPI, 1>(g, wv, 1, lds, st);
+  else launch_eq<EPI, 0>(g, wv, 1, lds, st);
+}
+
+int epi_ipw(const GemvArgs &g, int epi) {
+  switch (epi) {
+    case EPI_STORE: return ipw_of<EPI_STORE>(g);
+    case EPI_ADD: return ipw_of<EPI_ADD>(g);
+    case EPI_SWIGLU: return ipw_of<EPI_SWIGLU>(g);
+    case EPI_QKV: return ipw_of<EPI_QKV>(g);
+    case EPI_MOE_ADD: return ipw_of<EPI_MOE_ADD>(g);
+    default: return ipw_of<EPI_LOGITS>(g);
+  }
 }
 
 int device_cus() {
@@ -502,18 +703,25 @@ int gemv_blocks(int n_items) {
 
 hipError_t launch_gemv(const GemvArgs &g0, int epi, hipStream_t st, int *blocks) {
   GemvArgs g = g0;
-  int wv = gemv_waves(g.n_items);
+  const int ipw = epi_ipw(g, epi);
+  int wv = gemv_waves((g.n_items + ipw - 1) / ipw);
   if (g.W2) {
     // second part: SwiGLU after grouped slots only, 8-wave blocks for both parts
     if (epi != EPI_SWIGLU || !g.slot_expert || g.n_items2 < 1 || !g.C2) return hipErrorInvalidValue;
     wv = 8;
     g.blocks1 = (g.n_items + wv - 1) / wv;
   }
-  if (blocks) *blocks = (g.n_items + wv - 1) / wv;
+  if (blocks) *blocks = (g.n_items + wv * ipw - 1) / (wv * ipw);
   // quantised weights: codes in 16-byte lane loads, and a quantised second part
-  if (g.Wq && (!g.wscale || g.K % 16 || (g.W2 && (!g.W2q || !g.w2scale)) || (g.slot_expert && g.w_group_stride % g.K)))
+  if (g.qbits != 0 && g.qbits != 8 && g.qbits != 4) return hipErrorInvalidValue;
+  if ((g.qbits != 0) != (g.Wq != nullptr)) return hipErrorInvalidValue;
+  if (g.qbits == 8 && (!g.wscale || g.K % 16 || (g.W2 && (!g.W2q || !g.w2scale)) ||
+                       (g.slot_expert && g.w_group_stride % g.K)))
     return hipErrorInvalidValue;
-  const size_t lds = gemv_lds(g.K, g.Wq != nullptr);
+  if (g.qbits == 4 && (!g.wexp || g.K % 32 || (g.W2 && (!g.W2q || !g.w2exp)) ||
+                       (g.slot_expert && g.w_group_stride % g.K)))
+    return hipErrorInvalidValue;
+  const size_t lds = gemv_lds(g.K, g.qbits);
   switch (epi) {
     case EPI_STORE: launch_e<EPI_STORE>(g, wv, lds, st); break;
     case EPI_ADD: launch_e<EPI_ADD>(g, wv, lds, st); break;

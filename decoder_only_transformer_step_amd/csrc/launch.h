@@ -37,8 +37,10 @@ hipError_t launch_gemm_chunk(const GemmArgs &g, int epi, hipStream_t st);
 // ------------------------------------------------ single-token projection --
 struct GemvArgs {
   const uint16_t *W;          // bf16 [rows][K]
-  const int8_t *Wq;           // or int8 codes [rows][K] with per-row scales wscale [rows]
-  const float *wscale;
+  const int8_t *Wq;           // or int8 codes [rows][K] with per-row scales wscale [rows],
+  const float *wscale;        //   or (qbits 4) 4-bit codes [rows][K / 2] with exponents wexp
+  const int8_t *wexp;         //   [rows][K / 32] (one power of two per group of 32 weights)
+  int32_t qbits;              // 0 bf16 W, 8 int8 Wq + wscale, 4 packed 4-bit Wq + wexp
   int64_t w_group_stride;     // grouped mode: elements between experts
   const int32_t *slot_expert; // grouped mode: expert of each routing slot (blockIdx.y), else null
   int32_t n_slots;
@@ -61,18 +63,21 @@ struct GemvArgs {
   // optional second part of an EPI_SWIGLU grouped launch (the shared expert):
   // weights W2 [2 N2][K], N2 row pairs into C2 [N2]; blocks1 is set by the launcher
   const uint16_t *W2;
-  const int8_t *W2q;          // its int8 codes and row scales when the first part is quantised
+  const int8_t *W2q;          // its codes and row scales (or exponents) when the first part is quantised
   const float *w2scale;
+  const int8_t *w2exp;
   int32_t N2, n_items2;
   float *C2;
   int32_t blocks1;
 };
 constexpr size_t GEMV_MAX_LDS = 60 * 1024;
 // LDS of one GEMV block: the fp32 activation padded to whole load steps
-// (512 elements of bf16 weights, 1024 of int8 weights)
-inline size_t gemv_lds(int K, bool q8 = false) {
-  const size_t step = q8 ? 1024 : 512;
-  return (size_t)(K + step - 1) / step * step * 4;
+// (512 elements of bf16 weights, 1024 of int8, 2048 of 4-bit weights; the
+// 4-bit path adds one fp32 group sum per lane and step)
+inline size_t gemv_lds(int K, int qbits = 0) {
+  const size_t step = qbits == 4 ? 2048 : qbits == 8 ? 1024 : 512;
+  const size_t steps = (size_t)(K + step - 1) / step;
+  return steps * step * 4 + (qbits == 4 ? steps * 64 * 4 : 0);
 }
 // blocks of a GEMV launch over n_items items (one argmax partial each for EPI_LOGITS)
 int gemv_blocks(int n_items);
@@ -201,6 +206,11 @@ hipError_t launch_decode_advance(int32_t *row_pos, const int32_t *next_token, in
 // scale [rows] fp32 (= 2^e), deq [rows][K] the dequantised bf16 weights.
 hipError_t launch_quantize_rows(const uint16_t *W, int64_t rows, int K, int8_t *q, float *scale, uint16_t *deq,
                                 hipStream_t st);
+// 4-bit quantisation, one power-of-two scale per group of 32 weights: codes
+// [rows][K / 2] (nibble q + 8; element 2j low, 2j + 1 high in byte j), exps
+// [rows][K / 32] int8, deq [rows][K] the dequantised bf16 weights.  K % 32 == 0.
+hipError_t launch_quantize_q4(const uint16_t *W, int64_t rows, int K, uint8_t *codes, int8_t *exps, uint16_t *deq,
+                              hipStream_t st);
 
 // V^T cache import: src [Hkv][len][d] -> dst [Hkv][d][S] (positions < len)
 hipError_t launch_kv_load_v(const uint16_t *src, uint16_t *dst, int Hkv, int len, int d, int S,

@@ -139,6 +139,52 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *W, i
   if (threadIdx.x == 0) scale[r] = s;
 }
 
+// 4-bit quantisation, one thread per group of 32 consecutive weights of a
+// row: e is the smallest integer with 7 * 2^e >= a (a = the group's largest
+// magnitude; a < 2^p from frexp, so e starts at p - 2 and steps down while
+// 7 * 2^(e-1) still covers a), q = rint(w / 2^e) (ties to even), |q| <= 7.
+// Codes are stored offset by 8 as nibbles (element 2j in the low nibble of
+// byte j, 2j + 1 in the high one), the exponent as one int8, and the
+// dequantised q 2^e (3 significant bits) exactly as bf16.
+__global__ __launch_bounds__(256) void quantize_q4_kernel(const uint16_t *W, int64_t groups, int K, uint8_t *codes,
+                                                          int8_t *exps, uint16_t *deq) {
+  const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gi >= groups) return;
+  const int gpr = K / 32;
+  const int64_t r = gi / gpr;
+  const int64_t k0 = r * K + (gi - r * gpr) * 32;
+  float w[32];
+#pragma unroll
+  for (int j = 0; j < 32; j += 8) {
+    const u32x4 v = load16(W + k0 + j);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      w[j + 2 * h] = bf16_lo(v[h]);
+      w[j + 2 * h + 1] = bf16_hi(v[h]);
+    }
+  }
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) a = fmaxf(a, fabsf(w[j]));
+  int e = 0;
+  if (a > 0.f) {
+    int p;
+    (void)frexpf(a, &p);
+    e = p - 2;
+    while (7.0f * ldexpf(1.0f, e - 1) >= a) --e;
+  }
+  const float inv = ldexpf(1.0f, -e), s = ldexpf(1.0f, e);
+  uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const float c = rintf(w[j] * inv);
+    packed[j >> 3] |= (uint32_t)((int)c + 8) << (4 * (j & 7));
+    deq[k0 + j] = (uint16_t)f32_to_bf16_bits(c * s);
+  }
+  *reinterpret_cast<u32x4 *>(codes + k0 / 2) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+  exps[gi] = (int8_t)e;
+}
+
 // The last node of a captured decode step: record the step's greedy token
 // and move the row to the next position (the next replay reads it there).
 __global__ __launch_bounds__(64) void decode_advance_kernel(int32_t *row_pos, const int32_t *next_token, int seq,
@@ -162,6 +208,16 @@ hipError_t launch_quantize_rows(const uint16_t *W, int64_t rows, int K, int8_t *
                                 hipStream_t st) {
   if (rows <= 0 || rows > 0x7fffffff || K <= 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)rows), dim3(256), 0, st, W, K, q, scale, deq);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_q4(const uint16_t *W, int64_t rows, int K, uint8_t *codes, int8_t *exps, uint16_t *deq,
+                              hipStream_t st) {
+  if (rows <= 0 || K <= 0 || K % 32) return hipErrorInvalidValue;
+  const int64_t groups = rows * (K / 32);
+  const int64_t blocks = (groups + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quantize_q4_kernel, dim3((unsigned)blocks), dim3(256), 0, st, W, groups, K, codes, exps, deq);
   return hipGetLastError();
 }
 

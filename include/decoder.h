@@ -109,7 +109,14 @@ typedef struct {
                               which 127 * 2^e covers the row's largest magnitude, codes
                               rounded to nearest (ties to even).  The model then computes with
                               the dequantised weights (exactly bf16 values) on every path; the
-                              embedding gather keeps the caller's table */
+                              embedding gather keeps the caller's table.
+                              2: the same matrices as 4-bit codes (decoder.rs names packed
+                              4-bit expert planes) with one power-of-two scale 2^e per group of
+                              32 consecutive weights of a row, e the smallest integer for which
+                              7 * 2^e covers the group's largest magnitude, codes in [-7, 7]
+                              rounded to nearest (ties to even); every row length must be a
+                              multiple of 32.  Batch-1 decode streams the codes (a quarter of
+                              the bf16 bytes); the other paths read the dequantised copies */
   int32_t kv_page_size;    /* 0: each sequence owns max_seq cache rows; P > 0 (a multiple of 32):
                               the cache is a pool of kv_pages pages of P positions, handed to
                               sequences as they grow and returned by kv_reset / kv_truncate

@@ -76,6 +76,21 @@ int dec_diag_rmsnorm(const float *d_x, const float *d_g, int32_t rows, int32_t H
 int dec_diag_quantize_rows(const uint16_t *d_W, int64_t rows, int32_t K, int8_t *d_q, float *d_scale,
                            uint16_t *d_deq, void *stream);
 
+/* 4-bit quantisation as decoder_init does it with weight_quant 2: per group
+ * of 32 consecutive weights of a row, e is the smallest integer with
+ * 7 * 2^e >= the group's largest magnitude, codes q = rint(w / 2^e) (ties to
+ * even, |q| <= 7).  W bf16 [rows][K], K % 32 == 0; codes [rows][K / 2] bytes,
+ * q + 8 of element 2j in the low nibble of byte j and of 2j + 1 in the high
+ * one; exps int8 [rows][K / 32]; deq bf16 [rows][K] the dequantised weights. */
+int dec_diag_quantize_q4(const uint16_t *d_W, int64_t rows, int32_t K, uint8_t *d_codes, int8_t *d_exps,
+                         uint16_t *d_deq, void *stream);
+
+/* y[n] = sum_k W[n][k] a[k] with the batch-1 decode projection kernel on
+ * 4-bit weights (codes and exps as dec_diag_quantize_q4 writes them; W is
+ * their dequantised value).  a fp32 [K], y fp32 [N]; K % 32 == 0. */
+int dec_diag_gemv_q4(const float *d_a, int32_t K, const uint8_t *d_codes, const int8_t *d_exps, int32_t N,
+                     float *d_y, void *stream);
+
 /* MoE routing of rows router-logit vectors (pipeline.rs MoeFfn: softmax
  * over all experts, top-k, optional renormalisation; lower index first on
  * ties).  logits fp32 [rows][E]; ids int32 [rows][k] in router order,
