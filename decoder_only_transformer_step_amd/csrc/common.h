@@ -168,6 +168,11 @@ struct GemmArgs {
   float eps;
   const uint16_t *W;      // bf16 weights [rows][K] row-major (per group: W + expert * w_group_stride)
   const uint16_t *Wp;     // the same weights packed in 32-row x 16-k MFMA tiles (chunk kernel), or null
+  // int8 codes of W [rows][K] with per-row scales (power-of-two): when set,
+  // the multi-row kernel streams these instead of W and scales each output
+  // by its row's scale (the dequantised W is exactly code x scale)
+  const int8_t *Wq;
+  const float *wscale;
   int64_t w_group_stride;
   int32_t M, N, K;
   int32_t np_off;         // row offset of the second weight tile (SwiGLU: N, QKV: d / 2)

@@ -456,7 +456,13 @@ int proj(decoder *D, int node, int epi, GemmArgs g, int max_rows) {
   const double out_b = epi == EPI_ADD ? 8.0 : ((epi == EPI_SWIGLU || epi == EPI_QKV) ? 2.0 * npd : 4.0);
   const double a_b = (g.x || g.a_lo) ? 4.0 : 2.0;
   const double ncols = epi == EPI_QKV ? g.N / 2.0 : g.N;
-  NodeTimer timer(D, node, npd * ncols * (double)g.K * 2 + (double)g.M * g.K * a_b + (double)g.M * ncols * out_b,
+  // int8 codes stream on the one-tile (<= 16 rows) path only; wider calls
+  // read the dequantised copies.  For a batch of 8-16 rows the packed bf16
+  // chunk kernel is the faster one on long rows (8B-class down projection,
+  // K = 14336, 16 rows: 32 us against 41 us on codes), so those keep it.
+  if (g.M > 16 || (g.M >= CHUNK_BATCH_MIN_ROWS && g.K > 8192 && g.Wp)) g.Wq = nullptr;
+  const double wrow = g.Wq ? (double)g.K + 4.0 : (double)g.K * 2;
+  NodeTimer timer(D, node, npd * ncols * wrow + (double)g.M * g.K * a_b + (double)g.M * ncols * out_b,
                   2.0 * npd * g.M * ncols * (double)g.K);
   const int ntiles = gemm_ntiles(g, epi);
   g.Cpart = D->gpart;
@@ -473,8 +479,8 @@ int proj(decoder *D, int node, int epi, GemmArgs g, int max_rows) {
       D->act_rows = g.M;
     }
   };
-  const bool chunk_rows =
-      g.M > CHUNK_MIN_ROWS || (g.M >= CHUNK_BATCH_MIN_ROWS && npd * ncols * (double)g.K * 2 >= CHUNK_BATCH_MIN_BYTES);
+  const bool chunk_rows = g.M > CHUNK_MIN_ROWS ||
+                          (!g.Wq && g.M >= CHUNK_BATCH_MIN_ROWS && npd * ncols * (double)g.K * 2 >= CHUNK_BATCH_MIN_BYTES);
   if (chunk_rows && gemm_chunk_fits(g, epi)) {
     // chunk kernel: split K so that the blocks (weight tiles x row blocks x
     // splits) fill the compute units about once, with at least two 64-wide k
@@ -499,14 +505,29 @@ int proj(decoder *D, int node, int epi, GemmArgs g, int max_rows) {
   if (epi != EPI_LOGITS && !g.n_groups && ntiles < 192 && steps >= 16) {
     ks = std::min(GEMM_MAX_SPLIT, std::max(1, 384 / ntiles));
     ks = std::min(ks, steps / 8);
-    while (ks > 1 && (size_t)ks * g.M * (size_t)npd * ntiles * 16 > D->L.gpart_elems) --ks;
   }
+  // a residual projection of a batch on int8 codes splits K in two, so its
+  // reduce also writes the next RMSNorm (the fused prologue cannot hold
+  // 8-16 rows of a wide activation), which saves that norm's own launch
+  if (g.Wq && epi == EPI_ADD && g.norm_gamma && g.M >= CHUNK_BATCH_MIN_ROWS && steps >= 16) ks = std::max(ks, 2);
+  while (ks > 1 && (size_t)ks * g.M * (size_t)npd * ntiles * 16 > D->L.gpart_elems) --ks;
   g.ksplit = std::max(ks, 1);
   if (g.ksplit <= 1 || g.n_groups) g.norm_out = nullptr;
   hipError_t e = launch_gemm(g, epi, max_rows, 1, D->stream);
   if (e != hipSuccess) return hip_fail(D, e, "projection");
   if (g.norm_out) note_norm();
   return DEC_OK;
+}
+
+// With int8 weights, the multi-row projection of a decode batch or a verify
+// pass (<= 16 rows) streams the codes of matrix i of layer l (as quant());
+// 4-bit weights keep the dequantised copies on this path.
+GemmArgs qcodes(const decoder *D, GemmArgs g, int l, int i) {
+  if (D->c.weight_quant != 1) return g;
+  const decoder::QuantW &w = l < 0 ? D->qhead : D->qw[l][i];
+  g.Wq = w.q;
+  g.wscale = w.s;
+  return g;
 }
 
 GemmArgs dense_args(const uint16_t *A, int64_t lda, const uint16_t *W, int M, int N, int K) {
@@ -871,6 +892,7 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   q.qkv.Hkv = c.n_kv_heads;
   q.qkv.d = d;
   q.Wp = D->packed[l].w[0];
+  q = qcodes(D, q, l, 0);
   if (c.qk_norm) {
     // plain projection (bias added) into D->qkv, then the per-head norm pass
     q.np_off = qkvr;
@@ -885,6 +907,7 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   if ((rc = attention(D, l, rows, rows_per_group, max_pos, hpos))) return rc;
   GemmArgs o = dense_args(D->attn, qd, W.w_o, rows, H, qd);
   o.Wp = D->packed[l].w[1];
+  o = qcodes(D, o, l, 1);
   o.norm_gamma = W.ffn_norm;
   o.a_lo = D->attn_lo;
   o.C = D->x;
@@ -900,9 +923,11 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
     gu.h_lo = D->h_lo;
     gu.ldc = I;
     gu.Wp = D->packed[l].w[2];
+    gu = qcodes(D, gu, l, 2);
     if ((rc = proj(D, DEC_NODE_GATE_UP, EPI_SWIGLU, gu, rows))) return rc;
     GemmArgs dn = dense_args(D->h, I, W.w_down, rows, H, I);
     dn.Wp = D->packed[l].w[3];
+    dn = qcodes(D, dn, l, 3);
     if (l + 1 < c.n_layers) dn.norm_gamma = (const float *)D->layers[l + 1].attn_norm;
     dn.a_lo = D->h_lo;
     dn.C = D->x;
@@ -952,7 +977,7 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   if (e != hipSuccess) return hip_fail(D, e, "moe_route");
   const int slots = std::min(E, rows * k);
   const int grp_rows = std::min(rows, 32);
-  const double exp_bytes = (double)slots * 3.0 * Ie * H * 2;
+  double exp_bytes = (double)slots * 3.0 * Ie * H;
   GemmArgs g = dense_args(D->act, H, W.w_exp_gate_up, rows * k, Ie, H);
   g.a_lo = D->act_lo;
   g.a_rows = D->pair_row;
@@ -965,8 +990,10 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   g.group_start = mr.group_start;
   g.group_count = mr.group_count;
   g.ksplit = 1;
+  if (rows <= 16) g = qcodes(D, g, l, 4);
+  const double exp_wb = g.Wq ? 1.0 : 2.0;  // weight bytes per expert weight streamed
   {
-    NodeTimer t(D, DEC_NODE_EXPERTS, exp_bytes * 2.0 / 3.0 + rows * (double)H * 2 + rows * (double)k * Ie * 2,
+    NodeTimer t(D, DEC_NODE_EXPERTS, exp_bytes * exp_wb * 2.0 / 3.0 + rows * (double)H * 2 + rows * (double)k * Ie * 2,
                 2.0 * rows * k * 2.0 * Ie * H);
     e = launch_gemm(g, EPI_SWIGLU, grp_rows, slots, st);
   }
@@ -976,6 +1003,7 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   g.a_rows = nullptr;
   g.lda = Ie;
   g.W = W.w_exp_down;
+  if (g.Wq) g = qcodes(D, g, l, 5);
   g.w_group_stride = (int64_t)H * Ie;
   g.N = H;
   g.K = Ie;
@@ -984,7 +1012,7 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   g.C = D->yexp;
   g.ldc = H;
   {
-    NodeTimer t(D, DEC_NODE_EXPERTS, exp_bytes / 3.0 + rows * (double)k * Ie * 2 + rows * (double)k * H * 4,
+    NodeTimer t(D, DEC_NODE_EXPERTS, exp_bytes * exp_wb / 3.0 + rows * (double)k * Ie * 2 + rows * (double)k * H * 4,
                 2.0 * rows * k * (double)Ie * H);
     e = launch_gemm(g, EPI_STORE, grp_rows, slots, st);
   }
@@ -996,10 +1024,12 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
     sg.h_lo = D->hsh_lo;
     sg.ldc = Is;
     sg.Wp = D->packed[l].w[2];
+    sg = qcodes(D, sg, l, 2);
     if ((rc = proj(D, DEC_NODE_EXPERTS, EPI_SWIGLU, sg, rows))) return rc;
     GemmArgs sd = dense_args(D->hsh, Is, W.w_sh_down, rows, H, Is);
     sd.a_lo = D->hsh_lo;
     sd.Wp = D->packed[l].w[3];
+    sd = qcodes(D, sd, l, 3);
     sd.C = D->ysh;
     sd.ldc = H;
     if ((rc = proj(D, DEC_NODE_EXPERTS, EPI_STORE, sd, rows))) return rc;
@@ -1048,6 +1078,7 @@ int run_step(decoder *D, int rows, int rows_per_group, int max_pos, const int32_
     if ((rc = gemv(D, DEC_NODE_HEAD, EPI_LOGITS, quant(D, g, -1, 0), &nparts))) return rc;
   } else {
     GemmArgs g = dense_args(nullptr, H, D->lm_head, nout, c.vocab, H);
+    g = qcodes(D, g, -1, 0);
     if ((rc = norm_into(D, g, D->x + (size_t)first * H, D->final_norm, nout))) return rc;
     g.C = out;
     g.ldc = c.vocab;

@@ -36,8 +36,25 @@ namespace {
 // Accumulate this wave's share of the block tile.  AMODE 0: A from global;
 // AMODE 2: A from the normalised copy in LDS (row m at a_lds + m * K, lo
 // plane at a_lo).  SPLIT: A carries a lo plane, multiplied as well.
-template <int MT, int NP, int U, int NW, int AMODE, bool SPLIT>
-__device__ __forceinline__ void gemm_tile(const GemmArgs &g, const uint16_t *W, const uint16_t *a_lds,
+// int8 weights: 8 codes (8 bytes) -> 8 bf16 values, exactly (|q| <= 127
+// has 7 significant bits, so the fp32 conversion's top half is the bf16).
+__device__ __forceinline__ u32x4 i8x8_to_bf16(u32x2 w) {
+  u32x4 o;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t v = w[h];
+    const uint32_t f0 = __float_as_uint((float)(int8_t)(v & 0xFFu));
+    const uint32_t f1 = __float_as_uint((float)(int8_t)((v >> 8) & 0xFFu));
+    const uint32_t f2 = __float_as_uint((float)(int8_t)((v >> 16) & 0xFFu));
+    const uint32_t f3 = __float_as_uint((float)(int8_t)(v >> 24));
+    o[2 * h] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+    o[2 * h + 1] = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+  }
+  return o;
+}
+
+template <int MT, int NP, int U, int NW, int AMODE, bool SPLIT, bool QW>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &g, const void *Wv, const uint16_t *a_lds,
                                           int64_t a_lo, int row0, int rows, int mp, int n0, bool nvalid,
                                           int s0, int s1, f32x4 (&acc)[MT][NP]) {
   const int lane = threadIdx.x & (WAVE - 1);
@@ -45,8 +62,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const uint16_t *W, 
   const int c = lane & 15, quad = lane >> 4;
   const int K = g.K;
   const uint16_t *wrow[NP];
+  const int8_t *qrow[NP];
 #pragma unroll
-  for (int p = 0; p < NP; ++p) wrow[p] = W + (int64_t)(n0 + c + p * g.np_off) * K + quad * 8;
+  for (int p = 0; p < NP; ++p) {
+    wrow[p] = static_cast<const uint16_t *>(Wv) + (int64_t)(n0 + c + p * g.np_off) * K + quad * 8;
+    qrow[p] = static_cast<const int8_t *>(Wv) + (int64_t)(n0 + c + p * g.np_off) * K + quad * 8;
+  }
   const uint16_t *arow[MT];
   bool mvalid[MT];
 #pragma unroll
@@ -67,6 +88,50 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const uint16_t *W, 
     for (int p = 0; p < NP; ++p) acc[t][p] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int NS = SPLIT ? 2 : 1;
+  if constexpr (QW) {
+    // int8 codes: a 64-wide step is two MFMA k groups whose k are permuted
+    // so that lane l's 16 codes of a row are contiguous (k = 64 s + 16 q +
+    // 0..15, group 0 taking the first 8, group 1 the last 8); the
+    // activation fragments follow the same permutation, and a dot product
+    // does not depend on the order of its terms.  Each load instruction of a
+    // wave then reads 16 rows x 64 contiguous bytes, as the bf16 path does.
+    constexpr int UQ = U >= 2 ? U / 2 : 1;
+    for (int st = s0 + wave; st < s1; st += NW * UQ) {
+      u32x4 wf[UQ][2][NP];
+      u32x4 af[UQ][2][MT][NS];
+#pragma unroll
+      for (int u = 0; u < UQ; ++u) {
+        const int step = st + u * NW;
+        const int k = step * 64 + quad * 8;  // + the row pointers' quad * 8: 64 s + 16 q
+        const bool kv = (step < s1) && (step * 64 + quad * 16 < K);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const u32x4 raw = (kv && nvalid) ? load16(qrow[p] + k) : u32x4{0u, 0u, 0u, 0u};
+          wf[u][0][p] = i8x8_to_bf16(u32x2{raw[0], raw[1]});
+          wf[u][1][p] = i8x8_to_bf16(u32x2{raw[2], raw[3]});
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int sp = 0; sp < NS; ++sp) {
+            af[u][0][t][sp] = (kv && mvalid[t]) ? load16(arow[t] + sp * a_lo + k) : u32x4{0u, 0u, 0u, 0u};
+            af[u][1][t][sp] = (kv && mvalid[t]) ? load16(arow[t] + sp * a_lo + k + 8) : u32x4{0u, 0u, 0u, 0u};
+          }
+      }
+#pragma unroll
+      for (int u = 0; u < UQ; ++u)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+#pragma unroll
+              for (int sp = 0; sp < NS; ++sp)
+                acc[t][p] = mfma16x16x32(as_bf16x8(af[u][h][t][sp]), as_bf16x8(wf[u][h][p]), acc[t][p]);
+    }
+    return;
+  }
   for (int st = s0 + wave; st < s1; st += NW * U) {
     u32x4 wf[U][NP];
     u32x4 af[U][MT][NS];
@@ -76,8 +141,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const uint16_t *W, 
       const int k = step * 32;
       const bool kv = (step < s1) && (k + quad * 8 < K);
 #pragma unroll
-      for (int p = 0; p < NP; ++p)
-        wf[u][p] = (kv && nvalid) ? load16(wrow[p] + k) : u32x4{0u, 0u, 0u, 0u};
+      for (int p = 0; p < NP; ++p) wf[u][p] = (kv && nvalid) ? load16(wrow[p] + k) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -96,7 +160,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const uint16_t *W, 
   }
 }
 
-template <int MT, int EPI, int U, int NW, int AMODE, bool SPLIT>
+template <int MT, int EPI, int U, int NW, int AMODE, bool SPLIT, bool QW>
 __global__ __launch_bounds__(NW * WAVE) void gemm_kernel(GemmArgs g) {
   constexpr int NP = paired<EPI>();
   __shared__ f32x4 red[NW][NP][WAVE];
@@ -105,18 +169,27 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_kernel(GemmArgs g) {
   extern __shared__ uint4 dyn_lds[];
   uint16_t *a_lds = reinterpret_cast<uint16_t *>(dyn_lds);
 
-  const uint16_t *W = g.W;
+  // bf16 weights, or int8 codes with their row scales (QW)
+  const void *W = QW ? static_cast<const void *>(g.Wq) : static_cast<const void *>(g.W);
+  const float *wscale = g.wscale;
   int row0 = 0, rows = g.M;
   if (g.n_groups) {
     const int gi = blockIdx.y;
     if (gi >= *g.n_groups) return;
-    W += (int64_t)g.group_expert[gi] * g.w_group_stride;
+    const int64_t ex = g.group_expert[gi];
+    if (QW) {
+      W = static_cast<const int8_t *>(W) + ex * g.w_group_stride;
+      wscale += ex * (g.w_group_stride / g.K);
+    } else {
+      W = static_cast<const uint16_t *>(W) + ex * g.w_group_stride;
+    }
     row0 = g.group_start[gi];
     rows = g.group_count[gi];
   }
   const int n0 = tile_n0<EPI>(g, blockIdx.x);
   const bool nvalid = (EPI == EPI_QKV) || (n0 + (threadIdx.x & 15)) < g.N;
-  const int steps = (g.K + 31) / 32;
+  // k steps: 32 wide (one MFMA k group), 64 wide for int8 codes (two groups)
+  const int steps = QW ? (g.K + 63) / 64 : (g.K + 31) / 32;
   int s0 = 0, s1 = steps;
   if (g.ksplit > 1) {
     const int per = (steps + g.ksplit - 1) / g.ksplit;
@@ -162,7 +235,7 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_kernel(GemmArgs g) {
   for (int mp = 0; mp < rows; mp += 16 * MT) {
     f32x4 acc[MT][NP];
     const int64_t a_lo = AMODE == 2 ? (int64_t)rows * g.K : g.a_lo;
-    gemm_tile<MT, NP, U, NW, AMODE, SPLIT>(g, W, a_lds, a_lo, row0, rows, mp, n0, nvalid, s0, s1, acc);
+    gemm_tile<MT, NP, U, NW, AMODE, SPLIT, QW>(g, W, a_lds, a_lo, row0, rows, mp, n0, nvalid, s0, s1, acc);
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
 #pragma unroll
@@ -183,6 +256,11 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_kernel(GemmArgs g) {
           v[p] = s;
         }
         const bool ok = m < rows && (EPI == EPI_QKV || n < g.N);
+        if (QW) {
+          // the row scales (powers of two: exact); a column past N scales by 1
+#pragma unroll
+          for (int p = 0; p < NP; ++p) v[p] *= (EPI == EPI_QKV || n < g.N) ? wscale[n + p * g.np_off] : 1.0f;
+        }
         if (ok) {
           const int64_t orow = row0 + m;
           if (g.ksplit > 1) {
@@ -295,17 +373,24 @@ __global__ __launch_bounds__(1024) void gemm_reduce_norm_kernel(GemmArgs g, int 
 }
 
 // U: weight steps per load batch, so that a batch holds about 16 fragments
-template <int MT, int EPI, int NW, int AMODE, bool SPLIT>
+template <int MT, int EPI, int NW, int AMODE, bool SPLIT, bool QW = false>
 hipError_t launch_cfg(const GemmArgs &g, dim3 grid, size_t dyn, hipStream_t st) {
   constexpr int NP = paired<EPI>();
   constexpr int F = MT * (SPLIT ? 2 : 1) + NP;
   constexpr int U = F <= 4 ? 4 : (F <= 8 ? 2 : 1);
-  hipLaunchKernelGGL((gemm_kernel<MT, EPI, U, NW, AMODE, SPLIT>), grid, dim3(NW * WAVE), dyn, st, g);
+  hipLaunchKernelGGL((gemm_kernel<MT, EPI, U, NW, AMODE, SPLIT, QW>), grid, dim3(NW * WAVE), dyn, st, g);
   return hipGetLastError();
 }
 
 template <int EPI>
 hipError_t launch_epi(const GemmArgs &g, int mt, bool norm, dim3 grid, size_t dyn, hipStream_t st) {
+  if (g.Wq) {
+    // int8 codes: decode batches and verify passes (one 16-row tile of rows)
+    if (mt != 1 || !g.wscale) return hipErrorInvalidValue;
+    if (norm) return launch_cfg<1, EPI, 8, 2, true, true>(g, grid, dyn, st);
+    if (g.a_lo) return launch_cfg<1, EPI, 8, 0, true, true>(g, grid, 0, st);
+    return launch_cfg<1, EPI, 8, 0, false, true>(g, grid, 0, st);
+  }
   if (norm) return launch_cfg<1, EPI, 8, 2, true>(g, grid, dyn, st);
   if (!g.a_lo) {
     switch (mt) {

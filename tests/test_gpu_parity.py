@@ -223,13 +223,18 @@ def test_tiny_batched_decode_matches_per_sequence_oracle():
             last[s] = want
 
 
-def test_8b_shape_batched_decode_of_nine_sequences():
+@pytest.mark.parametrize("wq", [0, 1])
+def test_8b_shape_batched_decode_of_nine_sequences(wq):
     """Batched decode at 8B layer shapes with 9 rows: the projections with at
     least 40 MB of weights take the packed chunk kernel from 8 rows on (the
     prompts of 8 to 12 tokens take it in prefill too); logits per sequence
     against the oracle over two steps."""
     from synth.workloads import C8B
-    shape = C8B.with_(name="gqa-8b-layers-2-b9", n_layers=2, vocab=1024, max_seq=64, max_chunk=16, max_batch=9)
+    # wq 1: int8 weights; the batch then streams the int8 codes of every
+    # projection through the one-tile kernel (the oracle runs on the
+    # dequantised weights)
+    shape = C8B.with_(name="gqa-8b-layers-2-b9", n_layers=2, vocab=1024, max_seq=64, max_chunk=16, max_batch=9,
+                      weight_quant=wq)
     W = host_weights(shape)
     dec, _ = make_decoder(shape, W)
     lens = (3, 12, 5, 8, 4, 10, 6, 9, 7)

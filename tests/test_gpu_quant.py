@@ -174,3 +174,37 @@ def test_quantized_moe_prefill_decode_and_routes(bits):
         check_routes_exact(dec, shape, W, 1, lambda: (dec.kv_truncate(0, 24 + step), decode(dec, [0], [t])),
                            f"moe q8 decode {step}")
     dec.close()
+
+
+def test_quantized_moe_verify_streams_codes():
+    """A 4-position verify pass of the small MoE model with int8 experts: the
+    grouped expert projections of a pass of at most 16 rows stream each
+    chosen expert's int8 codes with its row scales.  Every row's logits meet
+    the acceptance rule against the oracle (which follows the GPU's expert
+    ids), and those ids are exact on the GPU's own router input."""
+    from tests.moe_routes import check_routes_exact, forced
+    from tests.test_gpu_parity import small_moe
+    shape = small_moe().with_(name="moe-small-q8", weight_quant=1)
+    W = host_weights(shape)
+    ids = [int(t) for t in prompt(shape, 28, seq=4)]
+    m = oracle.Model(shape, W)
+    dec, _ = make_decoder(shape, W)
+    dec.prefill_chunk(0, ids[:24], 0, logits_mode=0)
+    torch.cuda.synchronize()
+    m.forward(ids[:24], 0, logits_mode=0, force_routes=forced(dec, shape, 24))
+    logits = torch.empty((4, shape.vocab), dtype=torch.float32, device="cuda")
+
+    def verify():
+        dec.kv_truncate(0, 24)
+        dec.prefill_chunk(0, ids[24:], 24, logits_mode=2, logits=logits)
+
+    verify()
+    torch.cuda.synchronize()
+    want = m.forward(ids[24:], 24, logits_mode=2, force_routes=forced(dec, shape, 4))["logits"]
+    got = logits.cpu().numpy()
+    for i in range(4):
+        st = compare_logits(got[i], want[i], f"moe q8 verify row {i}")
+        log("moe q8 verify row", i, st)
+        assert_parity(st, f"moe q8 verify row {i}")
+    check_routes_exact(dec, shape, W, 4, verify, "moe q8 verify")
+    dec.close()

@@ -26,6 +26,9 @@ SHAPES = {
     "tiny": (TINY, 16),
     # 8B-class layer shapes in two layers with a small vocabulary
     "8b2": (C8B.with_(name="gqa-8b-layers-2", n_layers=2, vocab=1024, max_seq=256), 40),
+    # int8 weights: the verify pass streams the codes (the oracle runs on the
+    # dequantised weights)
+    "8b2-q8": (C8B.with_(name="gqa-8b-layers-2-q8", n_layers=2, vocab=1024, max_seq=256, weight_quant=1), 40),
 }
 
 
@@ -42,7 +45,7 @@ def models():
 
 
 @pytest.mark.parametrize("n", [2, 4, 8])
-@pytest.mark.parametrize("which", ["tiny", "8b2"])
+@pytest.mark.parametrize("which", ["tiny", "8b2", "8b2-q8"])
 def test_verify_rows_match_oracle(models, which, n):
     shape, P, W = models(which)
     ids = [int(t) for t in prompt(shape, P + n)]
