@@ -40,7 +40,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
   size_t kcache, vcache, rope, x, act, attn, q, qkv, h, logits, stage, next_token;
-  size_t part_o, part_ml, gpart, counters, am_val, am_idx, am_out, f32_attn, f32_h, f32_act, f32_hexp;
+  size_t part_o, part_ml, gpart, am_val, am_idx, am_out, f32_attn, f32_h, f32_act, f32_hexp;
   size_t gout;                 // decode_run: step counter, then the generated tokens [max_seq]
   size_t rlogits, rids, rids_rec, rwts, rgate, groups, pair_row, pair_of, hexp, yexp, hsh, ysh;
   size_t total;
@@ -219,7 +219,6 @@ Layout make_layout(const decoder_config_t *c) {
   if (c->n_experts > 0) max_small_n = std::max(max_small_n, 2 * c->shared_inter);
   L.gpart_elems = (size_t)GEMM_MAX_SPLIT * L.R * 2 * (size_t)max_small_n;
   L.gpart = take(L.gpart_elems * 4);
-  L.counters = take((size_t)(1 + ATTN_MAX_TASKS) * 4);
   // argmax candidates: one per 16-column tile per row (multi-row lm-head),
   // or one per 8-row block (batch-1 lm-head)
   const size_t am_n = std::max((size_t)L.RL * ((c->vocab + 15) / 16), (size_t)(c->vocab + 3) / 4);
@@ -281,7 +280,7 @@ struct decoder {
   float2 *rope;
   float *x, *qkv, *logits, *part_o, *part_ml, *gpart, *rlogits, *rwts, *rgate, *yexp, *ysh, *am_val;
   int32_t *ids, *row_seq, *row_pos, *next_token, *rids, *rids_rec, *groups, *pair_row, *pair_of;
-  int32_t *counters, *am_idx, *am_out;
+  int32_t *am_idx, *am_out;
   int32_t *gout;
   // decode_run captures a step: positions come from device memory (row_pos)
   // instead of kernel arguments, so one captured step serves every position
@@ -1184,7 +1183,6 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
   D->part_o = carve<float>(D, L.part_o);
   D->part_ml = carve<float>(D, L.part_ml);
   D->gpart = carve<float>(D, L.gpart);
-  D->counters = carve<int32_t>(D, L.counters);
   D->am_val = carve<float>(D, L.am_val);
   D->am_cap = L.am_n;
   D->am_idx = carve<int32_t>(D, L.am_idx);
@@ -1321,7 +1319,6 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
   if (hipMemsetAsync(D->kcache, 0, kvb, D->stream) != hipSuccess ||
       hipMemsetAsync(D->vcache, 0, kvb, D->stream) != hipSuccess ||
       hipMemsetAsync(D->next_token, 0, (size_t)cfg->max_batch * 4, D->stream) != hipSuccess ||
-      hipMemsetAsync(D->counters, 0, (size_t)(1 + ATTN_MAX_TASKS) * 4, D->stream) != hipSuccess ||
       hipStreamSynchronize(D->stream) != hipSuccess)
     return cleanup(DEC_E_HIP);
   *out = D;
