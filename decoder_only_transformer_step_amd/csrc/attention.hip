@@ -132,12 +132,15 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   // one contiguous 16-byte load per lane (64 bytes of a dim row per quad).
   u32x4 ka[D / 32], kh[D / 32];
   u32x4 va[NDT];
-  auto load_tile = [&](int t) {
-    // a paged cache: the tile's page (a 32-key tile never straddles one)
+  // a paged cache: the page of the tile at t (a 32-key tile never straddles
+  // one); the loop reads the next tile's page one tile ahead, so a tile's
+  // cache loads never wait on its page-table entry
+  auto page_of = [&](int t) { return PG ? a.pt[(int64_t)seq * a.mp + t / a.S] : 0; };
+  auto load_tile = [&](int t, int page) {
     const uint16_t *kt = kb, *vt = vb;
     int tt = t;
     if (PG) {
-      const int64_t pb = (int64_t)a.pt[(int64_t)seq * a.mp + t / a.S] * a.seq_stride + a.layer_off;
+      const int64_t pb = (int64_t)page * a.seq_stride + a.layer_off;
       kt = a.kcache + pb + (int64_t)g * a.S * D;
       vt = a.vcache + pb + (int64_t)g * D * a.S;
       tt = t % a.S;
@@ -156,7 +159,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   // the first tile goes out before q (a wave without a tile of its own
   // reloads the split's first tile, which stays inside the cache rows)
   const int t_first = k0 + 32 * wave;
-  load_tile(t_first < k1 ? t_first : k0);
+  const int t_load = t_first < k1 ? t_first : k0;
+  load_tile(t_load, page_of(t_load));
 
   // q of the column (an invalid column reads row 0 / head 0 and is zeroed:
   // unconditional loads keep the wait counts exact)
@@ -174,8 +178,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // (clamped to the split's last key, so the entry load is unconditional)
+  int page_next = page_of(min(t_first + 128, k1 - 1));
   for (int t0 = t_first; t0 < k1; t0 += 128) {
-    if (t0 != t_first) load_tile(t0);
+    if (t0 != t_first) {
+      const int page = page_next;
+      page_next = page_of(min(t0 + 128, k1 - 1));
+      load_tile(t0, page);
+    }
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {

@@ -1509,14 +1509,28 @@ int kv_load(decoder_t *D, int32_t seq, int32_t layer, const uint16_t *d_k, const
   if (seq < 0 || seq >= c.max_batch || layer < 0 || layer >= c.n_layers || !d_k || !d_v)
     return fail(D, DEC_E_INVALID, "kv_load argument");
   if (len < 0) return fail(D, DEC_E_INVALID, "kv_load length");
-  if (D->L.mp) return fail(D, DEC_E_INVALID, "kv_load needs the contiguous KV cache (kv_page_size 0)");
   if (len > c.max_seq) return fail(D, DEC_E_CONTEXT_OVERFLOW, "kv_load past max_seq");
-  const int d = c.head_dim, S = D->L.S;
-  const int64_t loff = (int64_t)seq * D->L.seq_stride + (int64_t)layer * c.n_kv_heads * (int64_t)S * d;
-  for (int g = 0; g < c.n_kv_heads; ++g)
-    HIP_TRY(D, hipMemcpyAsync(D->kcache + loff + (int64_t)g * S * d, d_k + (int64_t)g * len * d,
-                              (size_t)len * d * 2, hipMemcpyDeviceToDevice, D->stream), "kv_load k");
-  if (len > 0) HIP_TRY(D, launch_kv_load_v(d_v, D->vcache + loff, c.n_kv_heads, len, d, S, D->stream), "kv_load v");
+  if (D->L.mp) {
+    // paged: the sequence gets the pages len needs (all or nothing), the
+    // page table travels to the device in a staging slot, and one kernel
+    // scatters K rows and V^T columns into the pages
+    int rc = ensure_pages(D, 1, &seq, &len);
+    if (rc) return rc;
+    if (len > 0) {
+      rc = stage_rows(D, 0, nullptr, &seq, nullptr);
+      if (rc) return rc;
+      HIP_TRY(D, launch_kv_load_paged(d_k, d_v, D->kcache, D->vcache, D->page_table + (int64_t)seq * D->L.mp,
+                                      D->L.kv_unit, kv_layer_off(D, layer), c.n_kv_heads, len, c.head_dim,
+                                      D->L.kvS, D->stream), "kv_load paged");
+    }
+  } else {
+    const int d = c.head_dim, S = D->L.S;
+    const int64_t loff = (int64_t)seq * D->L.seq_stride + (int64_t)layer * c.n_kv_heads * (int64_t)S * d;
+    for (int g = 0; g < c.n_kv_heads; ++g)
+      HIP_TRY(D, hipMemcpyAsync(D->kcache + loff + (int64_t)g * S * d, d_k + (int64_t)g * len * d,
+                                (size_t)len * d * 2, hipMemcpyDeviceToDevice, D->stream), "kv_load k");
+    if (len > 0) HIP_TRY(D, launch_kv_load_v(d_v, D->vcache + loff, c.n_kv_heads, len, d, S, D->stream), "kv_load v");
+  }
   D->kv_pending[seq][layer] = len;
   bool all = true;
   for (int l = 0; l < c.n_layers; ++l) all = all && D->kv_pending[seq][l] == len;
@@ -1524,6 +1538,7 @@ int kv_load(decoder_t *D, int32_t seq, int32_t layer, const uint16_t *d_k, const
     D->len[seq] = len;
     D->has_next[seq] = 0;
     std::fill(D->kv_pending[seq].begin(), D->kv_pending[seq].end(), -1);
+    release_pages(D, seq, len);  // a paged sequence keeps only the pages len needs
   }
   return DEC_OK;
 }

@@ -212,6 +212,13 @@ hipError_t launch_quantize_rows(const uint16_t *W, int64_t rows, int K, int8_t *
 hipError_t launch_quantize_q4(const uint16_t *W, int64_t rows, int K, uint8_t *codes, int8_t *exps, uint16_t *deq,
                               hipStream_t st);
 
+// Paged-cache import of one layer of one sequence: K and V [Hkv][len][d]
+// into the pages listed by pt (that sequence's page-table row; pages of P
+// positions, unit elements per page, the layer at layer_off inside a page)
+hipError_t launch_kv_load_paged(const uint16_t *src_k, const uint16_t *src_v, uint16_t *kpool, uint16_t *vpool,
+                                const int32_t *pt, int64_t unit, int64_t layer_off, int Hkv, int len, int d, int P,
+                                hipStream_t st);
+
 // V^T cache import: src [Hkv][len][d] -> dst [Hkv][d][S] (positions < len)
 hipError_t launch_kv_load_v(const uint16_t *src, uint16_t *dst, int Hkv, int len, int d, int S,
                             hipStream_t st);

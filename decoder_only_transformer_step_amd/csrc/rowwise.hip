@@ -341,6 +341,49 @@ __global__ __launch_bounds__(256) void kv_load_v_kernel(const uint16_t *src, uin
 }
 }  // namespace
 
+namespace {
+// KV-prefix import into a paged cache: position t of the sequence lives in
+// page pt[t / P] at row t % P; K rows [P][d] and V^T rows [d][P] per kv head
+// inside a page's layer.  K and V both come as [Hkv][len][d]; each block
+// moves a 64-position x 64-dim tile of one head (V through LDS, so both the
+// read and the transposed write are coalesced).
+__global__ __launch_bounds__(256) void kv_load_paged_kernel(const uint16_t *src_k, const uint16_t *src_v,
+                                                            uint16_t *kpool, uint16_t *vpool, const int32_t *pt,
+                                                            int64_t unit, int64_t layer_off, int len, int d, int P) {
+  __shared__ uint16_t tile[64][65];
+  const int t0 = blockIdx.x * 64, j0 = blockIdx.y * 64, g = blockIdx.z;
+  const uint16_t *sk = src_k + (int64_t)g * len * d, *sv = src_v + (int64_t)g * len * d;
+  for (int e = threadIdx.x; e < 64 * 64; e += blockDim.x) {
+    const int tt = e / 64, jj = e % 64;
+    const int t = t0 + tt, j = j0 + jj;
+    if (t < len && j < d) {
+      const int64_t base = (int64_t)pt[t / P] * unit + layer_off;
+      kpool[base + ((int64_t)g * P + t % P) * d + j] = sk[(int64_t)t * d + j];
+    }
+    tile[tt][jj] = (t < len && j < d) ? sv[(int64_t)t * d + j] : 0;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * 64; e += blockDim.x) {
+    const int jj = e / 64, tt = e % 64;
+    const int t = t0 + tt, j = j0 + jj;
+    if (t < len && j < d) {
+      const int64_t base = (int64_t)pt[t / P] * unit + layer_off;
+      vpool[base + ((int64_t)g * d + j) * P + t % P] = tile[tt][jj];
+    }
+  }
+}
+}  // namespace
+
+hipError_t launch_kv_load_paged(const uint16_t *src_k, const uint16_t *src_v, uint16_t *kpool, uint16_t *vpool,
+                                const int32_t *pt, int64_t unit, int64_t layer_off, int Hkv, int len, int d, int P,
+                                hipStream_t st) {
+  if (len <= 0 || P <= 0 || d <= 0) return hipErrorInvalidValue;
+  dim3 grid((len + 63) / 64, (d + 63) / 64, Hkv);
+  hipLaunchKernelGGL(kv_load_paged_kernel, grid, dim3(256), 0, st, src_k, src_v, kpool, vpool, pt, unit, layer_off,
+                     len, d, P);
+  return hipGetLastError();
+}
+
 hipError_t launch_kv_load_v(const uint16_t *src, uint16_t *dst, int Hkv, int len, int d, int S,
                             hipStream_t st) {
   dim3 grid((len + 63) / 64, (d + 63) / 64, Hkv);

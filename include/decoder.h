@@ -120,7 +120,7 @@ typedef struct {
   int32_t kv_page_size;    /* 0: each sequence owns max_seq cache rows; P > 0 (a multiple of 32):
                               the cache is a pool of kv_pages pages of P positions, handed to
                               sequences as they grow and returned by kv_reset / kv_truncate
-                              (a paged cache for sequences of ragged lengths; kv_load needs 0) */
+                              (a paged cache for sequences of ragged lengths) */
   int32_t kv_pages;        /* pages in the pool when kv_page_size > 0 */
 } decoder_config_t;
 
@@ -249,8 +249,10 @@ int kv_truncate(decoder_t *dec, int32_t seq, int32_t len);
  * sequence's length becomes len once every layer has been loaded with the
  * same len (call in any layer order; the length is set on the last layer).
  * decoder.rs (its per-layer device-resident KV: a prefix restore uploads
- * host K/V rows into it).  DEC_E_INVALID: bad seq, layer or pointer,
- * len < 0, or a paged cache; DEC_E_CONTEXT_OVERFLOW: len > max_seq. */
+ * host K/V rows into it).  A paged cache gives the sequence the pages len
+ * needs at its first call (all or nothing) and keeps only those once every
+ * layer is loaded.  DEC_E_INVALID: bad seq, layer or pointer, len < 0;
+ * DEC_E_CONTEXT_OVERFLOW: len > max_seq, or the page pool lacks the pages. */
 int kv_load(decoder_t *dec, int32_t seq, int32_t layer, const uint16_t *d_k,
             const uint16_t *d_v, int32_t len);
 

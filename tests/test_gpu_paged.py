@@ -136,3 +136,48 @@ def test_paged_with_every_option_and_verify():
     assert_parity(compare_logits(lb[0], want, "all options decode after rollback"), "all options decode")
     flat.close()
     paged.close()
+
+
+def test_paged_kv_load_equals_contiguous():
+    """A KV prefix loaded into a paged cache (kv_load scatters K rows and V^T
+    columns into the sequence's pages) decodes bit for bit like the same
+    prefix loaded into the contiguous cache: three sequences of ragged
+    lengths on the 8B-class layer shapes with pages of 64 positions, a
+    reload to a shorter length that hands pages back, a pool too small for a
+    further load (refused, nothing changed), then batched decode."""
+    from synth.device import to_device
+    from synth.weights import host_kv
+    shape = C8B.with_(name="gqa-8b-layers-2-b3", n_layers=2, vocab=1024, max_seq=512, max_batch=3, max_chunk=16)
+    W = host_weights(shape)
+    P, pages = 64, 14
+    flat, _ = make_decoder(shape, W)
+    paged, _ = make_decoder(shape.with_(kv_page_size=P, kv_pages=pages), W)
+    lens = [300, 130, 380]                       # 5 + 3 + 6 = 14 pages: the whole pool
+    for s, n in enumerate(lens):
+        for l in range(shape.n_layers):
+            K, V = host_kv(shape, s, l, n)
+            dk, dv = to_device(K), to_device(V)
+            flat.kv_load(s, l, dk, dv, n)
+            paged.kv_load(s, l, dk, dv, n)
+    # reload seq 2 shorter: it keeps 3 of its 6 pages
+    lens[2] = 190
+    for l in range(shape.n_layers):
+        K, V = host_kv(shape, 2, l, lens[2])
+        dk, dv = to_device(K), to_device(V)
+        flat.kv_load(2, l, dk, dv, lens[2])
+        paged.kv_load(2, l, dk, dv, lens[2])
+    assert [paged.seq_len(s) for s in range(3)] == lens
+    # 5 + 3 + 3 = 11 pages in use: a load of seq 1 to 512 positions (8 pages) needs 5 more than the 3 left
+    K, V = host_kv(shape, 1, 0, 512)
+    with pytest.raises(Exception):
+        paged.kv_load(1, 0, to_device(K), to_device(V), 512)
+    assert paged.seq_len(1) == lens[1]
+    toks = [int(t) for t in prompt(shape, 3, seq=17)]
+    for step in range(3):
+        a, am = decode(flat, [0, 1, 2], toks)
+        b, _ = decode(paged, [0, 1, 2], toks)
+        assert np.array_equal(a, b), f"step {step}"
+        toks = [int(t) for t in am]
+    log("paged kv_load equals the contiguous cache through 3 batched decode steps")
+    flat.close()
+    paged.close()
