@@ -226,6 +226,9 @@ hipError_t launch_kv_load_v(const uint16_t *src, uint16_t *dst, int Hkv, int len
 // ------------------------------------------------------------------- MoE --
 struct MoeRouteArgs {
   const float *logits;     // fp32 [rows][E] router logits
+  const uint16_t *w_router;  // bf16 [E][H]: when set, the route launch computes the logits itself
+                             // from RMSNorm(act_f32 rows; gamma) (act_f32 and gamma required)
+  float *logits_out;       // with w_router: optional copy of the computed logits [rows][E]
   const uint16_t *act;     // split bf16 [rows][H] normed FFN input (for the shared gate)
   int64_t act_lo;
   const float *act_f32;    // or fp32 [rows][H] when set
@@ -243,6 +246,8 @@ struct MoeRouteArgs {
   int32_t *pair_of;        // [rows*k]: sorted pair index of (row, slot)
 };
 hipError_t launch_moe_route(const MoeRouteArgs &a, bool group, hipStream_t st);
+// the largest hidden size the fused router (w_router set) keeps in LDS
+constexpr int MOE_ROUTER_MAX_H = 8192;
 
 // x[r][:] += sum_j wts[r][j] * y[pair_of[r*k+j]][:] + gate[r] * ysh[r][:]
 // (pair_of null: y is indexed by r*k+j directly)

@@ -163,6 +163,128 @@ __global__ __launch_bounds__(256) void moe_group_kernel(MoeRouteArgs a) {
   }
 }
 
+// Router and route in one launch (pipeline.rs MoeFfn: router logits of the
+// normed FFN input, softmax over all experts, top-k): one block of 16 waves
+// per row.  b = RMSNorm(x; gamma) goes to LDS in fp32; wave w computes the
+// logits of experts w, w + 16, ... (lane l takes 8 consecutive elements at
+// 8 l + 512 s, one 16-byte weight load each; loads of a wave's experts are
+// issued together), the shared-gate dot product joins them, and the first
+// wave then routes exactly as moe_route_kernel does.
+constexpr int RR_THREADS = 1024;
+
+__global__ __launch_bounds__(RR_THREADS) void moe_router_route_kernel(MoeRouteArgs a) {
+  extern __shared__ float bsh[];       // b [H], then the logits [E]
+  __shared__ float red[RR_THREADS / WAVE];
+  const int r = blockIdx.x, E = a.E, H = a.H;
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  float *lg = bsh + H;
+  const float *x = a.act_f32 + (int64_t)r * H;
+  // RMSNorm in fp32: mean square in fixed order, then the gain
+  float ss = 0.f;
+  for (int j = threadIdx.x * 4; j < H; j += RR_THREADS * 4) {
+    const f32x4 v = loadf4(x + j);
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  ss = block_sum<RR_THREADS / WAVE>(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)H + a.eps);
+  for (int j = threadIdx.x * 4; j < H; j += RR_THREADS * 4) {
+    const f32x4 v = loadf4(x + j), gm = loadf4(a.gamma + j);
+    *reinterpret_cast<f32x4 *>(bsh + j) = f32x4{v[0] * inv * gm[0], v[1] * inv * gm[1], v[2] * inv * gm[2],
+                                                v[3] * inv * gm[3]};
+  }
+  __syncthreads();
+  // logits: wave w takes experts w + 16 i, four at a time (their loads go
+  // out together); per expert, lane l takes the elements 8 l + 512 s
+  // (H % 8 == 0; lanes past H, and experts past E, read a valid chunk and
+  // drop it)
+  constexpr int NW = RR_THREADS / WAVE, EU = 4;
+  const int steps = (H + 511) / 512;
+  for (int e0 = wave; e0 < E; e0 += NW * EU) {
+    float acc[EU];
+#pragma unroll
+    for (int u = 0; u < EU; ++u) acc[u] = 0.f;
+    for (int s = 0; s < steps; ++s) {
+      const int k = s * 512 + lane * 8;
+      const bool ok = k < H;
+      const int kk = ok ? k : 0;
+      u32x4 w[EU];
+#pragma unroll
+      for (int u = 0; u < EU; ++u) w[u] = load16(a.w_router + (int64_t)min(e0 + NW * u, E - 1) * H + kk);
+      const f32x4 b0 = *reinterpret_cast<const f32x4 *>(bsh + kk);
+      const f32x4 b1 = *reinterpret_cast<const f32x4 *>(bsh + kk + 4);
+#pragma unroll
+      for (int u = 0; u < EU; ++u) {
+        float d = bf16_lo(w[u][0]) * b0[0];
+        d = fmaf(bf16_hi(w[u][0]), b0[1], d);
+        d = fmaf(bf16_lo(w[u][1]), b0[2], d);
+        d = fmaf(bf16_hi(w[u][1]), b0[3], d);
+        d = fmaf(bf16_lo(w[u][2]), b1[0], d);
+        d = fmaf(bf16_hi(w[u][2]), b1[1], d);
+        d = fmaf(bf16_lo(w[u][3]), b1[2], d);
+        d = fmaf(bf16_hi(w[u][3]), b1[3], d);
+        acc[u] += ok ? d : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < EU; ++u) {
+      const int e = e0 + NW * u;
+      const float t = wave_sum(acc[u]);
+      if (lane == 0 && e < E) {
+        lg[e] = t;
+        if (a.logits_out) a.logits_out[(int64_t)r * E + e] = t;
+      }
+    }
+  }
+  // shared-expert gate: sigmoid(w_sg . b), fp32 dot in fixed order
+  float dot = 0.f;
+  if (a.w_sh_gate)
+    for (int j = threadIdx.x; j < H; j += RR_THREADS) dot += bsh[j] * bf16_to_f32(a.w_sh_gate[j]);
+  dot = block_sum<RR_THREADS / WAVE>(dot, red);   // (its barriers also publish the logits)
+  if (threadIdx.x >= WAVE) return;
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + WAVE * i;
+    v[i] = lg[min(e, E - 1)];
+    if (e >= E) v[i] = -INFINITY;
+  }
+  const float m = wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+  float zs = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) zs += lane + WAVE * i < E ? expf(v[i] - m) : 0.f;
+  const float z = wave_sum(zs);
+  int32_t *ids = a.ids + (int64_t)r * a.k;
+  float *w = a.wts + (int64_t)r * a.k;
+  float wsel[8], sel = 0.f;
+  int isel[8];
+  unsigned taken = 0;
+  for (int j = 0; j < a.k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + WAVE * i;
+      if (e < E && !(taken >> i & 1u) && better(v[i], e, bv, bi)) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+    wave_best(bv, bi);
+    if (bi % WAVE == lane) taken |= 1u << (bi / WAVE);
+    isel[j] = bi;
+    wsel[j] = expf(bv - m) / z;
+    sel += wsel[j];
+  }
+  if (lane == 0) {
+    for (int j = 0; j < a.k; ++j) {
+      ids[j] = isel[j];
+      w[j] = a.renorm ? wsel[j] / sel : wsel[j];
+      if (a.ids_record) a.ids_record[(int64_t)r * a.k + j] = isel[j];
+    }
+    if (a.gate) a.gate[r] = a.w_sh_gate ? 1.0f / (1.0f + expf(-dot)) : 1.0f;
+  }
+}
+
 // x[r][c] += sum_j w_j y[pair(r, j)][c] + gate_r ysh[r][c]; grid (columns / 256, rows)
 __global__ __launch_bounds__(256) void moe_combine_kernel(float *x, const float *y, const float *ysh,
                                                          const float *wts, const float *gate,
@@ -190,7 +312,12 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(float *x, const float 
 
 hipError_t launch_moe_route(const MoeRouteArgs &a, bool group, hipStream_t st) {
   if (a.E > 256 || a.k > 8 || (group && a.rows * a.k > GROUP_MAX_PAIRS)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(moe_route_kernel, dim3(a.rows), dim3(ROUTE_THREADS), 0, st, a);
+  if (a.w_router) {
+    if (!a.act_f32 || !a.gamma || a.H % 8 || a.H > MOE_ROUTER_MAX_H) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(moe_router_route_kernel, dim3(a.rows), dim3(RR_THREADS), (size_t)(a.H + a.E) * 4, st, a);
+  } else {
+    hipLaunchKernelGGL(moe_route_kernel, dim3(a.rows), dim3(ROUTE_THREADS), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !group) return e;
   hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(256), 0, st, a);
