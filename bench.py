@@ -360,29 +360,35 @@ def summarize_mfma(pmc_csv, out, commands):
     durations from the same run's dispatch timestamps)."""
     import collections
     import csv
-    vals = collections.defaultdict(lambda: collections.defaultdict(list))
-    dur = collections.defaultdict(dict)
+    disp = collections.defaultdict(dict)
     for r in csv.DictReader(open(pmc_csv)):
         name = r["Kernel_Name"].replace("void ", "").replace("(anonymous namespace)::", "")
         name = re.sub(r"\([^()]*\)$", "", name)
-        vals[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
-        dur[name][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        d = disp[r["Dispatch_Id"]]
+        d["name"], d["grid"] = name, int(r["Grid_Size"])
+        d["dur"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    # one group per GEMM shape: same kernel, same grid, same MFMA work per dispatch
+    groups = collections.defaultdict(list)
+    for d in disp.values():
+        groups[(d["name"], d["grid"], d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0))].append(d)
     lines = ["# MFMA work of the prefill chunk projections (rocprofv3 --pmc)", "",
              "Command (from the repository root):", "", "```"] + commands + ["```", "",
-             "`gemm_chunk_kernel<MT, EPI, SPLIT>`: EPI 1 = residual add (o_proj, down), 2 = SwiGLU "
-             "(gate_up), 3 = QKV. The activations enter the MFMAs as two bf16 planes, so the executed "
-             "flops are twice the algorithmic 2 M N K.", "",
+             "`gemm_chunk_kernel<MT, EPI, SPLIT>`: EPI 0 = plain product (the bench's gate_up GEMM "
+             "capability probe), 1 = residual add (o_proj, down), 2 = SwiGLU (gate_up), 3 = QKV. "
+             "One row per GEMM shape (kernel, grid size, MFMA work per dispatch). The model's "
+             "activations enter the MFMAs as two bf16 planes, so their executed flops are twice the "
+             "algorithmic 2 M N K.", "",
              f"peak: {MFMA_BF16_PEAK_TFS:.0f} TFLOP/s dense bf16", "",
-             "| kernel | dispatches | avg us (counter run) | MFMA flops / dispatch | executed TFLOP/s | "
-             "% of peak | algorithmic % of peak | MFMA-busy cycles / dispatch |",
+             "| kernel | grid | dispatches | avg us (counter run) | MFMA flops / dispatch | executed TFLOP/s | "
+             "% of peak | MFMA-busy cycles / dispatch |",
              "|---|---:|---:|---:|---:|---:|---:|---:|"]
-    for name, v in sorted(vals.items()):
-        mops = statistics.mean(v["SQ_INSTS_VALU_MFMA_MOPS_BF16"])
-        busy = statistics.mean(v["SQ_VALU_MFMA_BUSY_CYCLES"]) if v.get("SQ_VALU_MFMA_BUSY_CYCLES") else float("nan")
-        t = statistics.mean(dur[name].values())
+    for (name, grid, mops), ds in sorted(groups.items()):
+        busy = statistics.mean(d.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) for d in ds)
+        t = statistics.mean(d["dur"] for d in ds)
         tfs = mops * 512 / t / 1e12
-        lines.append(f"| `{name}` | {len(dur[name])} | {t * 1e6:.2f} | {mops * 512:.4g} | {tfs:.1f} | "
-                     f"{100 * tfs / MFMA_BF16_PEAK_TFS:.1f} | {50 * tfs / MFMA_BF16_PEAK_TFS:.1f} | {busy:.4g} |")
+        lines.append(f"| `{name}` | {grid} | {len(ds)} | {t * 1e6:.2f} | {mops * 512:.4g} | {tfs:.1f} | "
+                     f"{100 * tfs / MFMA_BF16_PEAK_TFS:.1f} | {busy:.4g} |")
     open(out, "w").write("\n".join(lines) + "\n")
 
 
