@@ -111,6 +111,61 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// The better (value, index) of a wave under `better`, in every lane.
+__device__ __forceinline__ void wave_best(float &v, int &i) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(v, o, WAVE);
+    const int oi = __shfl_xor(i, o, WAVE);
+    if (better(ov, oi, v, i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
+
+// MoE routing of one row by one wave (pipeline.rs MoeFfn): softmax over all
+// E <= 256 router logits (lane l holds experts l + 64 i), then the kk <= 8
+// largest, one wave arg-max per pick over the experts not yet taken (larger
+// first, lower index on ties).  Every lane returns the same ids isel[0..kk),
+// their probabilities wsel[0..kk) and the probabilities' sum.
+__device__ __forceinline__ void moe_topk(const float *row, int E, int kk, int lane, int (&isel)[8],
+                                         float (&wsel)[8], float &sel) {
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + WAVE * i;
+    v[i] = row[min(e, E - 1)];
+    if (e >= E) v[i] = -INFINITY;
+  }
+  const float m = wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+  float zs = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) zs += lane + WAVE * i < E ? expf(v[i] - m) : 0.f;
+  const float z = wave_sum(zs);
+  unsigned taken = 0;
+  sel = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= kk) break;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + WAVE * i;
+      if (e < E && !(taken >> i & 1u) && better(v[i], e, bv, bi)) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+    wave_best(bv, bi);
+    if (bi % WAVE == lane) taken |= 1u << (bi / WAVE);
+    isel[j] = bi;
+    wsel[j] = expf(bv - m) / z;
+    sel += wsel[j];
+  }
+}
+
 // ------------------------------------------------------ launch structs --
 
 // Epilogues of the projection kernel.

@@ -656,7 +656,7 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
 int gemv(decoder *D, int node, int epi, const GemvArgs &g, int *blocks = nullptr) {
   if (epi == EPI_ADD || epi == EPI_MOE_ADD) D->act_norm = nullptr;  // x changes
   const double nr = (epi == EPI_SWIGLU || epi == EPI_QKV) ? 2.0 : 1.0;
-  const double slots = g.slot_expert ? g.n_slots : 1;
+  const double slots = (g.slot_expert || g.route_logits) ? g.n_slots : 1;
   const double out_words = epi == EPI_ADD ? 2 : epi == EPI_MOE_ADD ? 2 + g.moe_k : 1;
   // weight bytes per row (+ its scale or group exponents)
   const double wrow = g.qbits == 8 ? (double)g.K + 4.0 : g.qbits == 4 ? g.K / 2.0 + g.K / 32.0 : (double)g.K * 2;
@@ -784,42 +784,31 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
     if ((rc = gemv(D, DEC_NODE_GATE_UP, EPI_SWIGLU, quant(D, gu, l, 2)))) return rc;
     return gemv(D, DEC_NODE_DOWN, EPI_ADD, quant(D, gemv_args(W.w_down, D->f32_h, I, H, D->x), l, 3));
   }
-  // MoE FFN for one row: the FFN RMSNorm runs inside the router GEMV, the
-  // route kernel and the expert GEMVs (each from x); the shared expert's
-  // down projection also does the combine into x.  (The router GEMV spreads
-  // the router rows over many compute units; one block computing all the
-  // logits and routing, as the multi-row path does, measured slower for a
-  // single row: 13.4 us against 2 x 5.8 us.)
+  // MoE FFN for one row: the FFN RMSNorm runs inside the router GEMV and the
+  // expert GEMVs (each from x).  The routed gate/up launch routes by itself
+  // (each block takes the top-k of the router logits) and publishes the ids,
+  // weights and shared gate; the shared expert's down projection also does
+  // the combine into x.  (The router GEMV spreads the router rows over many
+  // compute units; one block computing all the logits and routing, as the
+  // multi-row path does, measured slower for a single row: 13.4 us against
+  // 2 x 5.8 us for the router GEMV and a route kernel.)
   const int E = c.n_experts, k = c.top_k, Ie = c.expert_inter, Is = c.shared_inter;
   GemvArgs rg = gemv_args(W.w_router, D->x, H, E, D->rlogits);
   rg.gamma = W.ffn_norm;
   rg.eps = eps;
   if ((rc = gemv(D, DEC_NODE_ROUTER, EPI_STORE, rg))) return rc;
-  MoeRouteArgs mr{};
-  mr.logits = D->rlogits;
-  mr.act_f32 = D->x;
-  mr.gamma = W.ffn_norm;
-  mr.eps = eps;
-  mr.w_sh_gate = (Is > 0 && c.shared_gate) ? W.w_sh_gate : nullptr;
-  mr.rows = 1;
-  mr.E = E;
-  mr.k = k;
-  mr.H = H;
-  mr.renorm = c.norm_topk_prob;
-  mr.ids = D->rids;
-  mr.wts = D->rwts;
-  mr.gate = D->rgate;
-  mr.ids_record = D->rids_rec + (size_t)l * k;
-  {
-    NodeTimer t(D, DEC_NODE_ROUTER, E * 4.0 + H * 4.0, E * 8.0);
-    e = launch_moe_route(mr, false, D->stream);
-  }
-  if (e != hipSuccess) return hip_fail(D, e, "moe_route");
   // routed gate_up (k slots) and, in the same launch, the shared expert's
   GemvArgs eg = gemv_args(W.w_exp_gate_up, D->x, H, Ie, D->f32_hexp);
   eg.gamma = W.ffn_norm;
   eg.eps = eps;
-  eg.slot_expert = D->rids;
+  eg.route_logits = D->rlogits;
+  eg.route_E = E;
+  eg.route_renorm = c.norm_topk_prob;
+  eg.route_ids = D->rids;
+  eg.route_rec = D->rids_rec + (size_t)l * k;
+  eg.route_wts = D->rwts;
+  eg.route_gate = D->rgate;
+  eg.route_w_sg = (Is > 0 && c.shared_gate) ? W.w_sh_gate : nullptr;
   eg.n_slots = k;
   eg.w_group_stride = (int64_t)2 * Ie * H;
   eg.ldc = Ie;

@@ -24,7 +24,10 @@
 //  * One item per wave, 8 waves per block; blocks beyond the resident set
 //    queue up behind the running ones.
 //  * Grouped mode (MoE experts): blockIdx.y = routing slot; the weight base
-//    moves to the chosen expert.
+//    moves to the chosen expert.  For batch-1 decode the kernel routes by
+//    itself: each wave takes the top-k of the router logits (moe_topk, the
+//    same selection as the route kernels) and moves to its slot's pick, so
+//    no separate route launch sits between the router and the experts.
 //  * Quantised weights (Q = 1): int8 codes with one scale per row.  The same
 //    1 KB loads then carry 16 weights per lane (k = 16 l + 1024 s), the
 //    activation slots hold 16 elements per lane and step, and the row's
@@ -335,6 +338,41 @@ __device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, in
   }
 }
 
+// In-kernel routing (batch-1 MoE decode): one block publishes the route for
+// the launches that follow.  Wave 0 writes the top-k ids and their weights;
+// the block's threads take the shared-gate dot product w_sg . b from the
+// normed activation in LDS (slot i of the layout holds elements k0 .. k0 + 3).
+template <int Q, int WV>
+__device__ __forceinline__ void publish_route(const GemvArgs &g, const f32x4 *xs, int steps, float *sred) {
+  constexpr int EPL = gv_epl<Q>(), HPL = EPL / 4;
+  float dot = 0.f;
+  if (g.route_w_sg) {
+    for (int i = threadIdx.x; i < steps * 64 * HPL; i += WV * WAVE) {
+      const int s = i / (64 * HPL), h = (i / 64) % HPL, l = i % 64;
+      const int k0 = s * 64 * EPL + l * EPL + 4 * h;
+      if (k0 < g.K) {
+        const f32x4 b = xs[i];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dot += b[u] * bf16_to_f32(g.route_w_sg[k0 + u]);
+      }
+    }
+  }
+  dot = block_sum<WV>(dot, sred);
+  if (threadIdx.x >= WAVE) return;
+  const int lane = threadIdx.x, k = g.n_slots;
+  int isel[8];
+  float wsel[8], sel;
+  moe_topk(g.route_logits, g.route_E, k, lane, isel, wsel, sel);
+  if (lane == 0) {
+    for (int j = 0; j < k; ++j) {
+      g.route_ids[j] = isel[j];
+      g.route_wts[j] = g.route_renorm ? wsel[j] / sel : wsel[j];
+      if (g.route_rec) g.route_rec[j] = isel[j];
+    }
+    *g.route_gate = g.route_w_sg ? 1.0f / (1.0f + expf(-dot)) : 1.0f;
+  }
+}
+
 // One item per wave, WV (4 or 8) waves per block.  The wave's weight rows are
 // streamed in chunks of CH 1 KB steps through two register buffers: the
 // first two chunks go out before the activation prologue, and each buffer
@@ -373,6 +411,7 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
       g.n_items = ga.n_items2;
       g.C = ga.C2;
       g.slot_expert = nullptr;
+      g.route_logits = nullptr;
     } else {
       slot = bx / ga.blocks1;
       bx -= slot * ga.blocks1;
@@ -381,8 +420,16 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
   const char *W = Q ? reinterpret_cast<const char *>(g.Wq) : reinterpret_cast<const char *>(g.W);
   const float *xin = g.a_f32;
   int out_row = 0;
-  if (g.slot_expert) {
-    const int64_t ex = g.slot_expert[slot];
+  if (g.slot_expert || g.route_logits) {
+    int64_t ex;
+    if (g.route_logits) {
+      int isel[8];
+      float wsel[8], sel;
+      moe_topk(g.route_logits, g.route_E, slot + 1, threadIdx.x & (WAVE - 1), isel, wsel, sel);
+      ex = __builtin_amdgcn_readfirstlane(isel[min(slot, 7)]);
+    } else {
+      ex = g.slot_expert[slot];
+    }
     W += Q == 2 ? ex * g.w_group_stride / 2 : ex * g.w_group_stride * (Q ? 1 : 2);
     if (Q == 1) g.wscale += ex * (g.w_group_stride / g.K);  // the expert's row scales
     if (Q == 2) g.wexp += ex * (g.w_group_stride / 32);     // the expert's group exponents
@@ -594,6 +641,8 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
   for (int r = 0; r < NR; ++r) acc[r] = wave_sum(acc[r]) * wsc[r];
   if (valid && lane == 0) item_epilogue<EPI>(g, out_row, rows[0], rows[NR - 1], acc[0], acc[NR - 1], pre);
 
+  if (g.route_logits && bx == 0 && slot == 0) publish_route<Q, WV>(g, xs, steps, sred);
+
   if (EPI == EPI_LOGITS) {
     // this block's best (value, index), for the argmax finalize pass
     if (lane == 0) {
@@ -624,7 +673,7 @@ template <int EPI, int Q>
 int gv_ipw(const GemvArgs &g) {
   constexpr int CH = gv_ch<Q>() / gv_rows<EPI>(), SE = 64 * gv_epl<Q>();
   const int nch = ((g.K + SE - 1) / SE + CH - 1) / CH;
-  if (Q != 2 || nch != 1 || g.slot_expert || g.W2) return 1;
+  if (Q != 2 || nch != 1 || g.slot_expert || g.route_logits || g.W2) return 1;
   // only while the grid keeps at least two 8-wave blocks per compute unit
   return g.n_items >= 8 * GV_IPW * 2 * device_cus() ? GV_IPW : 1;
 }
@@ -632,7 +681,8 @@ int gv_ipw(const GemvArgs &g) {
 template <int EPI, int WV, int Q>
 void launch_w(const GemvArgs &g, int nch, int ipw, size_t lds, hipStream_t st) {
   const int per_block = WV * ipw;
-  dim3 grid((g.n_items + per_block - 1) / per_block, g.slot_expert ? g.n_slots : 1), block(WV * WAVE);
+  const bool grouped = g.slot_expert || g.route_logits;
+  dim3 grid((g.n_items + per_block - 1) / per_block, grouped ? g.n_slots : 1), block(WV * WAVE);
   if (g.W2) grid = dim3(g.blocks1 * g.n_slots + (g.n_items2 + WV - 1) / WV, 1);
   if (ipw > 1) {
     if constexpr (Q == 2) hipLaunchKernelGGL((gemv_kernel<EPI, 1, WV, Q, GV_IPW>), grid, block, lds, st, g);
@@ -707,19 +757,23 @@ hipError_t launch_gemv(const GemvArgs &g0, int epi, hipStream_t st, int *blocks)
   int wv = gemv_waves((g.n_items + ipw - 1) / ipw);
   if (g.W2) {
     // second part: SwiGLU after grouped slots only, 8-wave blocks for both parts
-    if (epi != EPI_SWIGLU || !g.slot_expert || g.n_items2 < 1 || !g.C2) return hipErrorInvalidValue;
+    if (epi != EPI_SWIGLU || !(g.slot_expert || g.route_logits) || g.n_items2 < 1 || !g.C2) return hipErrorInvalidValue;
     wv = 8;
     g.blocks1 = (g.n_items + wv - 1) / wv;
   }
   if (blocks) *blocks = (g.n_items + wv * ipw - 1) / (wv * ipw);
   // quantised weights: codes in 16-byte lane loads, and a quantised second part
   if (g.qbits != 0 && g.qbits != 8 && g.qbits != 4) return hipErrorInvalidValue;
+  // in-kernel routing: a grouped launch of k <= 8 slots over E <= 256 logits
+  if (g.route_logits && (g.slot_expert || g.n_slots < 1 || g.n_slots > 8 || g.route_E < g.n_slots ||
+                         g.route_E > 256 || !g.route_ids || !g.route_wts || !g.route_gate))
+    return hipErrorInvalidValue;
   if ((g.qbits != 0) != (g.Wq != nullptr)) return hipErrorInvalidValue;
   if (g.qbits == 8 && (!g.wscale || g.K % 16 || (g.W2 && (!g.W2q || !g.w2scale)) ||
-                       (g.slot_expert && g.w_group_stride % g.K)))
+                       ((g.slot_expert || g.route_logits) && g.w_group_stride % g.K)))
     return hipErrorInvalidValue;
   if (g.qbits == 4 && (!g.wexp || g.K % 32 || (g.W2 && (!g.W2q || !g.w2exp)) ||
-                       (g.slot_expert && g.w_group_stride % g.K)))
+                       ((g.slot_expert || g.route_logits) && g.w_group_stride % g.K)))
     return hipErrorInvalidValue;
   const size_t lds = gemv_lds(g.K, g.qbits);
   switch (epi) {
@@ -728,7 +782,8 @@ hipError_t launch_gemv(const GemvArgs &g0, int epi, hipStream_t st, int *blocks)
     case EPI_SWIGLU: launch_e<EPI_SWIGLU>(g, wv, lds, st); break;
     case EPI_QKV: launch_e<EPI_QKV>(g, wv, lds, st); break;
     case EPI_MOE_ADD:
-      if (!g.moe_y || !g.moe_w || !g.moe_gate || g.moe_k < 1 || g.moe_k > 8 || g.slot_expert) return hipErrorInvalidValue;
+      if (!g.moe_y || !g.moe_w || !g.moe_gate || g.moe_k < 1 || g.moe_k > 8 || g.slot_expert || g.route_logits)
+        return hipErrorInvalidValue;
       launch_e<EPI_MOE_ADD>(g, wv, lds, st);
       break;
     default: launch_e<EPI_LOGITS>(g, wv, lds, st); break;

@@ -69,6 +69,18 @@ struct GemvArgs {
   int32_t N2, n_items2;
   float *C2;
   int32_t blocks1;
+  // grouped mode routed in the kernel (batch-1 MoE decode), in place of
+  // slot_expert: the expert of slot j is the j-th pick of the top-k of the
+  // router logits route_logits [route_E] (moe_topk).  Block (0, slot 0)
+  // also publishes the ids (route_ids [k], route_rec [k] if set), their
+  // weights (route_wts [k], renormalised over the picks if route_renorm) and
+  // the shared-expert scale route_gate [1] = sigmoid(route_w_sg . b), or 1
+  // without a gate vector, for the launches that follow.
+  const float *route_logits;
+  int32_t route_E, route_renorm;
+  int32_t *route_ids, *route_rec;
+  float *route_wts, *route_gate;
+  const uint16_t *route_w_sg;
 };
 constexpr size_t GEMV_MAX_LDS = 60 * 1024;
 // LDS of one GEMV block: the fp32 activation padded to whole load steps

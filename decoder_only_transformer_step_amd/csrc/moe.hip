@@ -17,23 +17,10 @@ namespace {
 constexpr int ROUTE_THREADS = 256;
 constexpr int GROUP_MAX_PAIRS = 4096;  // rows x k (rows <= 512, k <= 8)
 
-// (value, index) of the better of two candidates under `better`
-__device__ __forceinline__ void wave_best(float &v, int &i) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float ov = __shfl_xor(v, o, WAVE);
-    const int oi = __shfl_xor(i, o, WAVE);
-    if (better(ov, oi, v, i)) {
-      v = ov;
-      i = oi;
-    }
-  }
-}
-
 // One block per row.  All threads take the shared-gate dot product; the
-// first wave then routes: lane l holds experts l, l + 64, l + 128, l + 192,
-// the softmax max and sum are wave reductions, and each of the k picks is a
-// wave arg-max over the experts not yet taken.
+// first wave then routes (moe_topk: the softmax max and sum are wave
+// reductions, and each of the k picks is a wave arg-max over the experts not
+// yet taken).
 __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(MoeRouteArgs a) {
   __shared__ float red[ROUTE_THREADS / WAVE];
   const int r = blockIdx.x, E = a.E;
@@ -80,41 +67,11 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(MoeRouteArgs a
   dot = block_sum<ROUTE_THREADS / WAVE>(dot, red);
   if (threadIdx.x >= WAVE) return;
   const int lane = threadIdx.x;
-  const float *row = a.logits + (int64_t)r * E;
-  float v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + WAVE * i;
-    v[i] = row[min(e, E - 1)];
-    if (e >= E) v[i] = -INFINITY;
-  }
-  const float m = wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-  float zs = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) zs += lane + WAVE * i < E ? expf(v[i] - m) : 0.f;
-  const float z = wave_sum(zs);
   int32_t *ids = a.ids + (int64_t)r * a.k;
   float *w = a.wts + (int64_t)r * a.k;
-  float wsel[8], sel = 0.f;
+  float wsel[8], sel;
   int isel[8];
-  unsigned taken = 0;
-  for (int j = 0; j < a.k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + WAVE * i;
-      if (e < E && !(taken >> i & 1u) && better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-    wave_best(bv, bi);
-    if (bi % WAVE == lane) taken |= 1u << (bi / WAVE);
-    isel[j] = bi;
-    wsel[j] = expf(bv - m) / z;
-    sel += wsel[j];
-  }
+  moe_topk(a.logits + (int64_t)r * E, E, a.k, lane, isel, wsel, sel);
   if (lane == 0) {
     for (int j = 0; j < a.k; ++j) {
       ids[j] = isel[j];
@@ -241,40 +198,11 @@ __global__ __launch_bounds__(RR_THREADS) void moe_router_route_kernel(MoeRouteAr
     for (int j = threadIdx.x; j < H; j += RR_THREADS) dot += bsh[j] * bf16_to_f32(a.w_sh_gate[j]);
   dot = block_sum<RR_THREADS / WAVE>(dot, red);   // (its barriers also publish the logits)
   if (threadIdx.x >= WAVE) return;
-  float v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + WAVE * i;
-    v[i] = lg[min(e, E - 1)];
-    if (e >= E) v[i] = -INFINITY;
-  }
-  const float m = wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-  float zs = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) zs += lane + WAVE * i < E ? expf(v[i] - m) : 0.f;
-  const float z = wave_sum(zs);
   int32_t *ids = a.ids + (int64_t)r * a.k;
   float *w = a.wts + (int64_t)r * a.k;
-  float wsel[8], sel = 0.f;
+  float wsel[8], sel;
   int isel[8];
-  unsigned taken = 0;
-  for (int j = 0; j < a.k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + WAVE * i;
-      if (e < E && !(taken >> i & 1u) && better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-    wave_best(bv, bi);
-    if (bi % WAVE == lane) taken |= 1u << (bi / WAVE);
-    isel[j] = bi;
-    wsel[j] = expf(bv - m) / z;
-    sel += wsel[j];
-  }
+  moe_topk(lg, E, a.k, lane, isel, wsel, sel);
   if (lane == 0) {
     for (int j = 0; j < a.k; ++j) {
       ids[j] = isel[j];
