@@ -181,9 +181,16 @@ def measure_verify(dec, shape, stream, ev0, ev1, reps, ns=(2, 4, 8)):
             for i in range(n):
                 dec.decode_step([0], [drafts[i]], logits=logits[i:i + 1], argmax=am[i:i + 1])
         s_ms = timed(singles)
+        # one more verify pass with the per-node timers on
+        dec.stats_enable()
+        dec.prefill_chunk(0, drafts[:n], L, logits_mode=2, logits=logits, argmax=am)
+        vst = dec.stats_read()
+        dec.stats_enable(())
+        dec.kv_truncate(0, L)
+        torch.cuda.synchronize()
         out[f"n{n}"] = {"verify_ms": round(v_ms, 4), "singles_ms": round(s_ms, 4),
                         "positions_per_s": round(n / v_ms * 1e3, 1),
-                        "speedup_vs_singles": round(s_ms / v_ms, 3)}
+                        "speedup_vs_singles": round(s_ms / v_ms, 3), "nodes": summarize_nodes(vst)}
         log(f"[gpu] verify {n} positions: {v_ms:.3f} ms ({n / v_ms * 1e3:.0f} positions/s), "
             f"{n} single decode steps {s_ms:.3f} ms")
     return out

@@ -450,8 +450,9 @@ void release_pages(decoder *D, int s, int keep) {
   }
 }
 
-// Launch one projection (plus its split-K reduction) as node `node`.
-int proj(decoder *D, int node, int epi, GemmArgs g, int max_rows) {
+// Launch one projection (plus its split-K reduction) as node `node`.  For
+// EPI_LOGITS, *nparts receives the number of argmax partials per row.
+int proj(decoder *D, int node, int epi, GemmArgs g, int max_rows, int *nparts = nullptr) {
   const double npd = (epi == EPI_SWIGLU || epi == EPI_QKV) ? 2.0 : 1.0;
   const double out_b = epi == EPI_ADD ? 8.0 : ((epi == EPI_SWIGLU || epi == EPI_QKV) ? 2.0 * npd : 4.0);
   const double a_b = (g.x || g.a_lo) ? 4.0 : 2.0;
@@ -479,6 +480,14 @@ int proj(decoder *D, int node, int epi, GemmArgs g, int max_rows) {
       D->act_rows = g.M;
     }
   };
+  if (nparts) *nparts = gemm_ntiles(g, epi);
+  // 2-8 rows of bf16 weights: the multi-row GEMV streams each weight row once
+  if (gemv_rows_fits(g, epi)) {
+    if (nparts) *nparts = gemv_rows_grid(g, epi);
+    hipError_t e = launch_gemv_rows(g, epi, D->stream);
+    if (e != hipSuccess) return hip_fail(D, e, "multi-row projection");
+    return DEC_OK;
+  }
   const bool chunk_rows = g.M > CHUNK_MIN_ROWS ||
                           (!g.Wq && g.M >= CHUNK_BATCH_MIN_ROWS && npd * ncols * (double)g.K * 2 >= CHUNK_BATCH_MIN_BYTES);
   if (chunk_rows && gemm_chunk_fits(g, epi)) {
@@ -546,7 +555,9 @@ GemmArgs dense_args(const uint16_t *A, int64_t lda, const uint16_t *W, int M, in
 // projection prologue for decode-size row counts, else a separate kernel.
 int norm_into(decoder *D, GemmArgs &g, const float *x, const float *gamma, int rows) {
   const int H = D->c.hidden;
-  if (gemm_norm_fits(rows, H)) {
+  // fused into the projection's prologue: decode-size row counts of the
+  // one-tile GEMM, and the 2-8 rows of the multi-row GEMV (bf16 weights)
+  if (gemm_norm_fits(rows, H) || (D->c.weight_quant != 1 && gemv_rows_takes(rows, H))) {
     g.x = x;
     g.gamma = gamma;
     g.eps = (float)D->c.rms_eps;
@@ -646,8 +657,12 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
   if ((int64_t)a.n_groups * ns > ATTN_MAX_TASKS) return fail(D, DEC_E_INVALID, "attention work list too long");
   a.kc = kc;
   a.n_splits = ns;
-  hipError_t e = attention_chunk_fits(a, c.head_dim) ? launch_attention_chunk(a, c.head_dim, D->stream)
-                                                     : launch_attention(a, c.head_dim, D->stream);
+  // the chunk kernel shares each key tile among up to 128 query columns; a
+  // chunk that fits one column group per kv head (a verify pass of a few
+  // drafted rows) takes the decode kernel, whose waves each own a tile
+  const bool chunk_kernel = rows > rows_per_group && attention_chunk_fits(a, c.head_dim);
+  hipError_t e = chunk_kernel ? launch_attention_chunk(a, c.head_dim, D->stream)
+                              : launch_attention(a, c.head_dim, D->stream);
   if (e != hipSuccess) return hip_fail(D, e, "attention");
   return DEC_OK;
 }
@@ -1076,8 +1091,7 @@ int run_step(decoder *D, int rows, int rows_per_group, int max_pos, const int32_
     g.ldc = c.vocab;
     g.am.part_val = D->am_val;
     g.am.part_idx = D->am_idx;
-    if ((rc = proj(D, DEC_NODE_HEAD, EPI_LOGITS, g, nout))) return rc;
-    nparts = gemm_ntiles(g, EPI_LOGITS);
+    if ((rc = proj(D, DEC_NODE_HEAD, EPI_LOGITS, g, nout, &nparts))) return rc;
   }
   {
     NodeTimer t(D, DEC_NODE_HEAD, nout * (double)nparts * 8, 0);

@@ -22,7 +22,7 @@ bool gemm_norm_fits(int rows, int K);
 hipError_t launch_gemm(const GemmArgs &g, int epi, int max_rows, int n_group_slots, hipStream_t st);
 // the fixed-order split-K reduction plus epilogue over Cpart (ntiles 16-row tiles)
 hipError_t launch_gemm_reduce(const GemmArgs &g, int epi, int ntiles, hipStream_t st);
-// Chunk projection (up to 128 rows, A in global memory, no grouping): blocks
+// Chunk projection (up to 512 rows, A in global memory, no grouping): blocks
 // of 256 weight rows (128 row pairs for the paired epilogues) times g.ksplit
 // k ranges.
 bool gemm_chunk_fits(const GemmArgs &g, int epi);
@@ -33,6 +33,18 @@ hipError_t launch_pack_w32(const uint16_t *W, int64_t rows, int K, uint16_t *P, 
 int gemm_chunk_tiles(const GemmArgs &g, int epi);
 int gemm_chunk_mblocks(int rows);
 hipError_t launch_gemm_chunk(const GemmArgs &g, int epi, hipStream_t st);
+// Projection of 2 .. GEMV_ROWS_MAX rows with bf16 weights, each weight row
+// streamed once (verify passes, small decode batches): K split over the waves
+// of a block, the rows' activations in registers (x + gamma: fused RMSNorm;
+// else split-bf16 A).  No split-K partials, no grouping.
+constexpr int GEMV_ROWS_MAX = 8;
+bool gemv_rows_fits(const GemmArgs &g, int epi);
+// whether rows x K activations fit the kernel's registers (for choosing the
+// fused RMSNorm prologue before the weights are known)
+bool gemv_rows_takes(int rows, int K);
+// grid size: the argmax partials per row of an EPI_LOGITS launch
+int gemv_rows_grid(const GemmArgs &g, int epi);
+hipError_t launch_gemv_rows(const GemmArgs &g, int epi, hipStream_t st);
 
 // ------------------------------------------------ single-token projection --
 struct GemvArgs {
