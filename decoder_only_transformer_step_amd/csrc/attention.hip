@@ -29,8 +29,13 @@
 //    denominator (attn_sink_fold) and adds nothing to the output.
 //  * The 4 waves merge through LDS (log-sum-exp); with one split the block
 //    normalises and writes the output.  With several, each block writes its
-//    (m, l, O) partial and attn_merge combines them in split order, so the
-//    result does not depend on scheduling.
+//    (m, l, O) partial and the splits are combined in split order, so the
+//    result does not depend on scheduling: by the group's last block to
+//    finish (an arrival counter per group), or by attn_merge.  The partials
+//    and the counter use relaxed device-scope accesses (stores and loads
+//    that are coherent across the XCDs' L2 caches by themselves), so neither
+//    side needs an L2 write-back or invalidate, and no block waits on
+//    another.
 #include <algorithm>
 
 #include "common.h"
@@ -104,11 +109,122 @@ __device__ __forceinline__ int group_key_start(const AttnArgs &a, int rg) {
   return 0;
 }
 
+// Combine one (column, dim j) of a group's split partials in split order.
+// Each chunk of MERGE_CHUNK splits is one batch of independent loads ((m, l)
+// and the O value per split), folded into running sums rescaled to the
+// chunk's new maximum, so a merge of up to MERGE_CHUNK splits is a single
+// memory round trip.  AT: the partials are read with relaxed device-scope
+// loads (the merge inside attn_kernel; attn_merge reads them after a kernel
+// boundary with plain loads).
+constexpr int MERGE_CHUNK = 32;
+
+template <bool AT>
+__device__ __forceinline__ float part_load(const float *p) {
+  if (AT) return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
+
+template <int D, bool AT>
+__device__ __forceinline__ float merge_splits(const AttnArgs &a, int gi, int cc, int j, int nact, int head) {
+  const float *ml = a.part_ml + ((int64_t)gi * a.n_splits * 16 + cc) * 2;
+  const float *po = a.part_o + ((int64_t)gi * a.n_splits * 16 + cc) * D + j;
+  float M = NEG_SENTINEL, L = 0.f, o = 0.f;
+  for (int s0 = 0; s0 < nact; s0 += MERGE_CHUNK) {
+    float ms[MERGE_CHUNK], ls[MERGE_CHUNK], ov[MERGE_CHUNK];
+#pragma unroll
+    for (int u = 0; u < MERGE_CHUNK; ++u) {
+      const int64_t s = min(s0 + u, nact - 1);
+      ms[u] = part_load<AT>(ml + s * 32);
+      ls[u] = part_load<AT>(ml + s * 32 + 1);
+      ov[u] = part_load<AT>(po + s * 16 * D);
+    }
+    // splits past nact (clamped duplicates) get weight 0; every loaded
+    // value is used unconditionally, so no load is sunk into a branch
+#pragma unroll
+    for (int u = 0; u < MERGE_CHUNK; ++u) ms[u] = s0 + u < nact ? ms[u] : -INFINITY;
+    float cm = M;
+#pragma unroll
+    for (int u = 0; u < MERGE_CHUNK; ++u) cm = fmaxf(cm, ms[u]);
+    const float r = exp2f(M - cm);
+    L *= r;
+    o *= r;
+#pragma unroll
+    for (int u = 0; u < MERGE_CHUNK; ++u) {
+      const float sc = exp2f(ms[u] - cm);
+      L += sc * ls[u];
+      o += sc * ov[u];
+    }
+    M = cm;
+  }
+  const float r = attn_sink_fold(a, head, M, L);
+  return o * r / L;
+}
+
+// The merge inside attn_kernel: up to two (column, dim) values per thread
+// in one pass, so their loads form a single round trip (chunks of 16 splits
+// bound the registers).  v1 = false: the second value is absent.
+constexpr int MERGE2_CHUNK = 16;
+
+template <int D>
+__device__ __forceinline__ void merge_splits2(const AttnArgs &a, int gi, int c0, int j0, int c1, int j1, bool v1,
+                                              int nact, int h0, int h1, float &out0, float &out1) {
+  const int cb = v1 ? c1 : c0, jb = v1 ? j1 : j0;
+  const float *ml0 = a.part_ml + ((int64_t)gi * a.n_splits * 16 + c0) * 2;
+  const float *ml1 = a.part_ml + ((int64_t)gi * a.n_splits * 16 + cb) * 2;
+  const float *po0 = a.part_o + ((int64_t)gi * a.n_splits * 16 + c0) * D + j0;
+  const float *po1 = a.part_o + ((int64_t)gi * a.n_splits * 16 + cb) * D + jb;
+  float M0 = NEG_SENTINEL, L0 = 0.f, o0 = 0.f, M1 = NEG_SENTINEL, L1 = 0.f, o1 = 0.f;
+  for (int s0 = 0; s0 < nact; s0 += MERGE2_CHUNK) {
+    float m0[MERGE2_CHUNK], l0[MERGE2_CHUNK], x0[MERGE2_CHUNK], m1[MERGE2_CHUNK], l1[MERGE2_CHUNK], x1[MERGE2_CHUNK];
+#pragma unroll
+    for (int u = 0; u < MERGE2_CHUNK; ++u) {
+      const int64_t s = min(s0 + u, nact - 1);
+      m0[u] = part_load<true>(ml0 + s * 32);
+      l0[u] = part_load<true>(ml0 + s * 32 + 1);
+      x0[u] = part_load<true>(po0 + s * 16 * D);
+      m1[u] = part_load<true>(ml1 + s * 32);
+      l1[u] = part_load<true>(ml1 + s * 32 + 1);
+      x1[u] = part_load<true>(po1 + s * 16 * D);
+    }
+#pragma unroll
+    for (int u = 0; u < MERGE2_CHUNK; ++u) {
+      m0[u] = s0 + u < nact ? m0[u] : -INFINITY;
+      m1[u] = s0 + u < nact ? m1[u] : -INFINITY;
+    }
+    float cm0 = M0, cm1 = M1;
+#pragma unroll
+    for (int u = 0; u < MERGE2_CHUNK; ++u) {
+      cm0 = fmaxf(cm0, m0[u]);
+      cm1 = fmaxf(cm1, m1[u]);
+    }
+    const float r0 = exp2f(M0 - cm0), r1 = exp2f(M1 - cm1);
+    L0 *= r0;
+    o0 *= r0;
+    L1 *= r1;
+    o1 *= r1;
+#pragma unroll
+    for (int u = 0; u < MERGE2_CHUNK; ++u) {
+      const float sc0 = exp2f(m0[u] - cm0), sc1 = exp2f(m1[u] - cm1);
+      L0 += sc0 * l0[u];
+      o0 += sc0 * x0[u];
+      L1 += sc1 * l1[u];
+      o1 += sc1 * x1[u];
+    }
+    M0 = cm0;
+    M1 = cm1;
+  }
+  const float f0 = attn_sink_fold(a, h0, M0, L0);
+  out0 = o0 * f0 / L0;
+  const float f1 = attn_sink_fold(a, v1 ? h1 : h0, M1, L1);
+  out1 = o1 * f1 / L1;
+}
+
 template <int D, int PM, bool PG>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   constexpr int NDT = D / 16;
   __shared__ float lo[4][16][D];
   __shared__ float lm[4][16], ll[4][16];
+  __shared__ int last_s;
 
   const int gi = blockIdx.x / a.n_splits, split = blockIdx.x - gi * a.n_splits;
   const int g = gi % a.Hkv, rg = gi / a.Hkv;
@@ -263,24 +379,50 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int q = 0; q < NDT; ++q) store_out(a, ob + jj + 16 * q, o[q] * inv);
     return;
   }
-  // several splits: publish this block's partial for attn_merge
+  // several splits: publish this block's partial
   const int64_t task = blockIdx.x;
   float *po = a.part_o + (task * 16 + cc) * D;
+  if (!a.counters) {  // for attn_merge
 #pragma unroll
-  for (int q = 0; q < NDT; ++q) po[jj + 16 * q] = o[q];
-  if (jj == 0) {
-    a.part_ml[(task * 16 + cc) * 2 + 0] = M;
-    a.part_ml[(task * 16 + cc) * 2 + 1] = L;
+    for (int q = 0; q < NDT; ++q) po[jj + 16 * q] = o[q];
+    if (jj == 0) {
+      a.part_ml[(task * 16 + cc) * 2 + 0] = M;
+      a.part_ml[(task * 16 + cc) * 2 + 1] = L;
+    }
+    return;
   }
+  if (oc.valid) {
+#pragma unroll
+    for (int q = 0; q < NDT; ++q) __hip_atomic_store(po + jj + 16 * q, o[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (jj == 0) {
+      __hip_atomic_store(a.part_ml + (task * 16 + cc) * 2 + 0, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.part_ml + (task * 16 + cc) * 2 + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // every thread's partial stores complete, then one arrival for the block;
+  // the group's last block to arrive (counter nact - 1) merges
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last_s = __hip_atomic_fetch_add(a.counters + gi, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nact - 1;
+  __syncthreads();
+  if (!last_s) return;
+  if (threadIdx.x == 0) __hip_atomic_store(a.counters + gi, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // (the launcher sets counters only when a group has at most 512 values)
+  const int ncols = min(16, a.rows_per_group * a.G);
+  const int p0 = threadIdx.x, p1 = threadIdx.x + 256;
+  if (p0 >= ncols * D) return;
+  const int c0 = p0 / D, j0 = p0 - c0 * D, c1 = p1 / D, j1 = p1 - c1 * D;
+  const bool has1 = p1 < ncols * D;
+  const Col col0 = column<PM>(a, rg, g, c0), col1 = column<PM>(a, rg, g, has1 ? c1 : c0);
+  float r0, r1;
+  merge_splits2<D>(a, gi, c0, j0, c1, j1, has1, nact, col0.head, col1.head, r0, r1);
+  if (col0.valid) store_out(a, ((int64_t)col0.row * a.Hq + col0.head) * D + j0, r0);
+  if (has1 && col1.valid) store_out(a, ((int64_t)col1.row * a.Hq + col1.head) * D + j1, r1);
 }
 
 // One block per (group, valid column), one thread per dim: combine the
-// group's splits in split order.  Each chunk of MERGE_CHUNK splits is one
-// batch of independent loads ((m, l) and the thread's O value per split),
-// folded into running sums rescaled to the chunk's new maximum, so a merge
-// of up to MERGE_CHUNK splits is a single memory round trip.
-constexpr int MERGE_CHUNK = 32;
-
+// group's splits in split order (merge_splits).
 template <int D, int PM>
 __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int ncols) {
   const int gi = blockIdx.x / ncols, cc = blockIdx.x - gi * ncols;
@@ -290,38 +432,7 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a, int ncols) {
   const int nact = (group_keys<PM>(a, rg, g) - group_key_start<PM>(a, rg) + a.kc - 1) / a.kc;
   if (nact <= 1) return;                       // written directly by attn_kernel
   const int j = threadIdx.x;
-  const float *ml = a.part_ml + ((int64_t)gi * a.n_splits * 16 + cc) * 2;
-  const float *po = a.part_o + ((int64_t)gi * a.n_splits * 16 + cc) * D + j;
-  float M = NEG_SENTINEL, L = 0.f, o = 0.f;
-  for (int s0 = 0; s0 < nact; s0 += MERGE_CHUNK) {
-    float ms[MERGE_CHUNK], ls[MERGE_CHUNK], ov[MERGE_CHUNK];
-#pragma unroll
-    for (int u = 0; u < MERGE_CHUNK; ++u) {
-      const int64_t s = min(s0 + u, nact - 1);
-      ms[u] = ml[s * 32];
-      ls[u] = ml[s * 32 + 1];
-      ov[u] = po[s * 16 * D];
-    }
-    // splits past nact (clamped duplicates) get weight 0; every loaded
-    // value is used unconditionally, so no load is sunk into a branch
-#pragma unroll
-    for (int u = 0; u < MERGE_CHUNK; ++u) ms[u] = s0 + u < nact ? ms[u] : -INFINITY;
-    float cm = M;
-#pragma unroll
-    for (int u = 0; u < MERGE_CHUNK; ++u) cm = fmaxf(cm, ms[u]);
-    const float r = exp2f(M - cm);
-    L *= r;
-    o *= r;
-#pragma unroll
-    for (int u = 0; u < MERGE_CHUNK; ++u) {
-      const float sc = exp2f(ms[u] - cm);
-      L += sc * ls[u];
-      o += sc * ov[u];
-    }
-    M = cm;
-  }
-  const float r = attn_sink_fold(a, oc.head, M, L);
-  store_out(a, ((int64_t)oc.row * a.Hq + oc.head) * D + j, o * r / L);
+  store_out(a, ((int64_t)oc.row * a.Hq + oc.head) * D + j, merge_splits<D, false>(a, gi, cc, j, nact, oc.head));
 }
 
 }  // namespace
@@ -333,7 +444,7 @@ hipError_t launch_pm(const AttnArgs &a, hipStream_t st) {
   if (a.pt) hipLaunchKernelGGL((attn_kernel<D, PM, true>), dim3(a.n_groups * a.n_splits), dim3(256), 0, st, a);
   else hipLaunchKernelGGL((attn_kernel<D, PM, false>), dim3(a.n_groups * a.n_splits), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_splits == 1) return e;
+  if (e != hipSuccess || a.n_splits == 1 || a.counters) return e;
   const int ncols = std::min(16, a.rows_per_group * a.G);  // valid columns of a group
   hipLaunchKernelGGL((attn_merge_kernel<D, PM>), dim3(a.n_groups * ncols), dim3(D), 0, st, a, ncols);
   return hipGetLastError();

@@ -138,6 +138,9 @@ struct AttnArgs {
   float scale_log2;        // log2(e) / sqrt(d)
   float *part_o;           // [n_groups * n_splits][16][d]
   float *part_ml;          // [n_groups * n_splits][16][2]
+  // arrival counters [n_groups], zero between launches: when set, the last
+  // block of a group to finish merges the group's splits (no merge launch)
+  int32_t *counters;
   // Where the kernel takes each row's position and sequence from:
   // 0: row_pos / row_seq in device memory; 1: pos_arg / seq_arg (one row per
   // group, rows <= 16; no dependent load before the cache reads); 2: a chunk
