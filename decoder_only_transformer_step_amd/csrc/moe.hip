@@ -84,7 +84,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(MoeRouteArgs a
 
 // One block: group table over experts in increasing order, pairs by row.
 // The ids are staged in LDS; counts by LDS atomics; a pair's slot in its
-// expert's group is the number of earlier pairs with the same expert.
+// expert's group follows the number of earlier pairs with the same expert.
 __global__ __launch_bounds__(256) void moe_group_kernel(MoeRouteArgs a) {
   __shared__ int ids_s[GROUP_MAX_PAIRS];
   __shared__ int cnt[256];
@@ -110,13 +110,25 @@ __global__ __launch_bounds__(256) void moe_group_kernel(MoeRouteArgs a) {
     *a.n_groups = ng;
   }
   __syncthreads();
-  for (int p = threadIdx.x; p < P; p += blockDim.x) {
-    const int e = ids_s[p];
-    int rank = 0;
-    for (int q = 0; q < p; ++q) rank += ids_s[q] == e;
-    const int o = start[e] + rank;
-    a.pair_row[o] = p / a.k;
-    a.pair_of[p] = o;
+  // a pair's slot: its expert's start plus the number of earlier pairs of
+  // that expert.  Wave w scans experts w, w + 4, ...: per 64-pair chunk a
+  // ballot marks the expert's pairs, and each marked lane counts the marks
+  // below it (P / 64 ballots per expert instead of P compares per pair)
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE, nw = blockDim.x / WAVE;
+  for (int e = wave; e < E; e += nw) {
+    if (!cnt[e]) continue;
+    int base = start[e];
+    for (int c = 0; c < P; c += WAVE) {
+      const int p = c + lane;
+      const bool hit = p < P && ids_s[p] == e;
+      const unsigned long long m = __ballot(hit);
+      if (hit) {
+        const int o = base + __popcll(m & ((1ull << lane) - 1));
+        a.pair_row[o] = p / a.k;
+        a.pair_of[p] = o;
+      }
+      base += __popcll(m);
+    }
   }
 }
 
@@ -128,6 +140,9 @@ __global__ __launch_bounds__(256) void moe_group_kernel(MoeRouteArgs a) {
 // issued together), the shared-gate dot product joins them, and the first
 // wave then routes exactly as moe_route_kernel does.
 constexpr int RR_THREADS = 1024;
+constexpr int RR_X = 2;  // f32x4 of x per thread: H <= 8192
+constexpr int RR_S = 4;  // 512-element steps of router weights in flight per wave
+static_assert(RR_X * 4 * RR_THREADS >= MOE_ROUTER_MAX_H, "router rows held in registers");
 
 __global__ __launch_bounds__(RR_THREADS) void moe_router_route_kernel(MoeRouteArgs a) {
   extern __shared__ float bsh[];       // b [H], then the logits [E]
@@ -136,50 +151,75 @@ __global__ __launch_bounds__(RR_THREADS) void moe_router_route_kernel(MoeRouteAr
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   float *lg = bsh + H;
   const float *x = a.act_f32 + (int64_t)r * H;
+  // x, gamma and the shared-gate row are loaded together, up front (H <=
+  // RR_X * 4 * RR_THREADS: each thread keeps its elements in registers)
+  f32x4 xv[RR_X], gv[RR_X];
+  float sg[4 * RR_X];
+#pragma unroll
+  for (int i = 0; i < RR_X; ++i) {
+    const int j = min((int)(threadIdx.x + i * RR_THREADS) * 4, H - 4);
+    xv[i] = loadf4(x + j);
+    gv[i] = loadf4(a.gamma + j);
+  }
+#pragma unroll
+  for (int i = 0; i < 4 * RR_X; ++i) {
+    const int j = min((int)threadIdx.x + i * RR_THREADS, H - 1);
+    sg[i] = a.w_sh_gate ? bf16_to_f32(a.w_sh_gate[j]) : 0.f;
+  }
   // RMSNorm in fp32: mean square in fixed order, then the gain
   float ss = 0.f;
-  for (int j = threadIdx.x * 4; j < H; j += RR_THREADS * 4) {
-    const f32x4 v = loadf4(x + j);
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
-  }
+#pragma unroll
+  for (int i = 0; i < RR_X; ++i)
+    if ((int)(threadIdx.x + i * RR_THREADS) * 4 < H)
+      ss += xv[i][0] * xv[i][0] + xv[i][1] * xv[i][1] + xv[i][2] * xv[i][2] + xv[i][3] * xv[i][3];
   ss = block_sum<RR_THREADS / WAVE>(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)H + a.eps);
-  for (int j = threadIdx.x * 4; j < H; j += RR_THREADS * 4) {
-    const f32x4 v = loadf4(x + j), gm = loadf4(a.gamma + j);
-    *reinterpret_cast<f32x4 *>(bsh + j) = f32x4{v[0] * inv * gm[0], v[1] * inv * gm[1], v[2] * inv * gm[2],
-                                                v[3] * inv * gm[3]};
+#pragma unroll
+  for (int i = 0; i < RR_X; ++i) {
+    const int j = (threadIdx.x + i * RR_THREADS) * 4;
+    if (j < H)
+      *reinterpret_cast<f32x4 *>(bsh + j) = f32x4{xv[i][0] * inv * gv[i][0], xv[i][1] * inv * gv[i][1],
+                                                  xv[i][2] * inv * gv[i][2], xv[i][3] * inv * gv[i][3]};
   }
   __syncthreads();
-  // logits: wave w takes experts w + 16 i, four at a time (their loads go
-  // out together); per expert, lane l takes the elements 8 l + 512 s
-  // (H % 8 == 0; lanes past H, and experts past E, read a valid chunk and
-  // drop it)
+  // logits: wave w takes experts w + 16 i, four at a time; per expert, lane
+  // l takes the elements 8 l + 512 s, and the loads of up to RR_S steps of
+  // the four experts go out together (H % 8 == 0; lanes past H, and experts
+  // past E, read a valid chunk and drop it)
   constexpr int NW = RR_THREADS / WAVE, EU = 4;
   const int steps = (H + 511) / 512;
   for (int e0 = wave; e0 < E; e0 += NW * EU) {
     float acc[EU];
 #pragma unroll
     for (int u = 0; u < EU; ++u) acc[u] = 0.f;
-    for (int s = 0; s < steps; ++s) {
-      const int k = s * 512 + lane * 8;
-      const bool ok = k < H;
-      const int kk = ok ? k : 0;
-      u32x4 w[EU];
+    for (int s0 = 0; s0 < steps; s0 += RR_S) {
+      u32x4 w[RR_S][EU];
 #pragma unroll
-      for (int u = 0; u < EU; ++u) w[u] = load16(a.w_router + (int64_t)min(e0 + NW * u, E - 1) * H + kk);
-      const f32x4 b0 = *reinterpret_cast<const f32x4 *>(bsh + kk);
-      const f32x4 b1 = *reinterpret_cast<const f32x4 *>(bsh + kk + 4);
+      for (int t = 0; t < RR_S; ++t) {
+        const int k = (s0 + t) * 512 + lane * 8;
+        const int kk = k < H ? k : 0;
 #pragma unroll
-      for (int u = 0; u < EU; ++u) {
-        float d = bf16_lo(w[u][0]) * b0[0];
-        d = fmaf(bf16_hi(w[u][0]), b0[1], d);
-        d = fmaf(bf16_lo(w[u][1]), b0[2], d);
-        d = fmaf(bf16_hi(w[u][1]), b0[3], d);
-        d = fmaf(bf16_lo(w[u][2]), b1[0], d);
-        d = fmaf(bf16_hi(w[u][2]), b1[1], d);
-        d = fmaf(bf16_lo(w[u][3]), b1[2], d);
-        d = fmaf(bf16_hi(w[u][3]), b1[3], d);
-        acc[u] += ok ? d : 0.f;
+        for (int u = 0; u < EU; ++u) w[t][u] = load16(a.w_router + (int64_t)min(e0 + NW * u, E - 1) * H + kk);
+      }
+#pragma unroll
+      for (int t = 0; t < RR_S; ++t) {
+        const int k = (s0 + t) * 512 + lane * 8;
+        const bool ok = k < H;
+        const int kk = ok ? k : 0;
+        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(bsh + kk);
+        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(bsh + kk + 4);
+#pragma unroll
+        for (int u = 0; u < EU; ++u) {
+          float d = bf16_lo(w[t][u][0]) * b0[0];
+          d = fmaf(bf16_hi(w[t][u][0]), b0[1], d);
+          d = fmaf(bf16_lo(w[t][u][1]), b0[2], d);
+          d = fmaf(bf16_hi(w[t][u][1]), b0[3], d);
+          d = fmaf(bf16_lo(w[t][u][2]), b1[0], d);
+          d = fmaf(bf16_hi(w[t][u][2]), b1[1], d);
+          d = fmaf(bf16_lo(w[t][u][3]), b1[2], d);
+          d = fmaf(bf16_hi(w[t][u][3]), b1[3], d);
+          acc[u] += ok ? d : 0.f;
+        }
       }
     }
 #pragma unroll
@@ -194,8 +234,11 @@ __global__ __launch_bounds__(RR_THREADS) void moe_router_route_kernel(MoeRouteAr
   }
   // shared-expert gate: sigmoid(w_sg . b), fp32 dot in fixed order
   float dot = 0.f;
-  if (a.w_sh_gate)
-    for (int j = threadIdx.x; j < H; j += RR_THREADS) dot += bsh[j] * bf16_to_f32(a.w_sh_gate[j]);
+#pragma unroll
+  for (int i = 0; i < 4 * RR_X; ++i) {
+    const int j = threadIdx.x + i * RR_THREADS;
+    if (j < H) dot += bsh[j] * sg[i];
+  }
   dot = block_sum<RR_THREADS / WAVE>(dot, red);   // (its barriers also publish the logits)
   if (threadIdx.x >= WAVE) return;
   int32_t *ids = a.ids + (int64_t)r * a.k;
