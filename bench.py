@@ -124,23 +124,51 @@ def measure_gemm_capability(shape, rows, stream, ev0, ev1, reps=20):
     del Wt
     C = torch.empty((rows, N), dtype=torch.float32, device="cuda")
     out = {"rows": rows, "N": N, "K": K}
-    for planes in (1, 2):
-        a = A[:planes]
-        diag_gemm_chunk(a, P, C, 1, None, stream.cuda_stream)
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for _ in range(reps):
-            diag_gemm_chunk(a, P, C, 1, None, stream.cuda_stream)
-        ev1.record(stream)
+    for m in sorted({128, rows}):
+        res = {}
+        for planes in (1, 2):
+            a = A[:planes, :m].contiguous()
+            diag_gemm_chunk(a, P, C[:m], 1, None, stream.cuda_stream)
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            for _ in range(reps):
+                diag_gemm_chunk(a, P, C[:m], 1, None, stream.cuda_stream)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            s = ev0.elapsed_time(ev1) * 1e-3 / reps
+            fl = 2.0 * m * N * K
+            res[f"planes{planes}"] = {"us": s * 1e6, "tflops_algorithmic": fl / s / 1e12,
+                                      "mfma_frac_algorithmic": fl / s / 1e12 / MFMA_BF16_PEAK_TFS,
+                                      "mfma_frac_executed": planes * fl / s / 1e12 / MFMA_BF16_PEAK_TFS}
+            log(f"[gpu] gemm {m}x{N}x{K} planes {planes}: {s * 1e6:.1f} us, "
+                f"{fl / s / 1e12:.0f} TFLOP/s algorithmic")
+        if m == rows:
+            out.update(res)
+        out[f"rows{m}"] = res
+    del A, P, C
+    # context only, not part of the path: the vendor library's bf16 GEMM
+    # (torch's linear on this machine, fp32 accumulate, bf16 output) on the same
+    # shapes at the workload's chunk (128 rows) and at `rows` rows
+    import torch.nn.functional as F
+    W = (torch.randn((N, K), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    lib = {}
+    for m in sorted({128, rows}):
+        X = (torch.randn((m, K), device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+        with torch.cuda.stream(stream):
+            F.linear(X, W)
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            for _ in range(reps):
+                F.linear(X, W)
+            ev1.record(stream)
         torch.cuda.synchronize()
         s = ev0.elapsed_time(ev1) * 1e-3 / reps
-        fl = 2.0 * rows * N * K
-        out[f"planes{planes}"] = {"us": s * 1e6, "tflops_algorithmic": fl / s / 1e12,
-                                  "mfma_frac_algorithmic": fl / s / 1e12 / MFMA_BF16_PEAK_TFS,
-                                  "mfma_frac_executed": planes * fl / s / 1e12 / MFMA_BF16_PEAK_TFS}
-        log(f"[gpu] gemm {rows}x{N}x{K} planes {planes}: {s * 1e6:.1f} us, "
-            f"{fl / s / 1e12:.0f} TFLOP/s algorithmic")
-    del A, P, C
+        fl = 2.0 * m * N * K
+        lib[f"rows{m}"] = {"us": s * 1e6, "tflops": fl / s / 1e12, "mfma_frac": fl / s / 1e12 / MFMA_BF16_PEAK_TFS}
+        log(f"[gpu] library bf16 gemm {m}x{N}x{K}: {s * 1e6:.1f} us, {fl / s / 1e12:.0f} TFLOP/s")
+        del X
+    out["library_reference"] = lib
+    del W
     torch.cuda.empty_cache()
     return out
 
