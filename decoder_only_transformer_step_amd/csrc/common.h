@@ -245,6 +245,9 @@ struct GemmArgs {
   // split-K: blockIdx.z = split; partial sums go to Cpart[split][M][np * N]
   float *Cpart;
   int32_t ksplit;
+  // chunk projections of 256+ rows: 1 lets launch_gemm_chunk take the wide
+  // kernel (256 x 256 blocks; the caller sized ksplit for its row blocks)
+  int32_t wide;
   // EPI_ADD with split K: the reduce also writes RMSNorm(new x; norm_gamma)
   // as split bf16 [M][N] at norm_out (lo plane at + norm_lo), if set
   const float *norm_gamma;

@@ -35,6 +35,7 @@ constexpr int CHUNK_MIN_ROWS = 16;   // more rows than this take the chunk proje
 constexpr int CHUNK_BATCH_MIN_ROWS = 8;
 constexpr double CHUNK_BATCH_MIN_BYTES = 40e6;
 constexpr int CHUNK_MAX_SPLIT = 16;
+constexpr int WIDE_MAX_SPLIT = 6;  // largest split-K the wide chunk kernel takes
 constexpr int MAX_CHUNK = 512;     // largest prefill chunk (rows per call)
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -496,13 +497,29 @@ int proj(decoder *D, int node, int epi, GemmArgs g, int max_rows, int *nparts = 
     // chunk kernel: split K so that the blocks (weight tiles x row blocks x
     // splits) fill the compute units about once, with at least two 64-wide k
     // steps per split (fewer, longer blocks measured faster than two rounds)
-    const int nbt = gemm_chunk_tiles(g, epi) * gemm_chunk_mblocks(g.M);
+    // 256+ rows: the wide kernel (256-row blocks) where its split stays at
+    // most WIDE_MAX_SPLIT (measured at 512 rows: gate_up 213 against 230 us,
+    // QKV 78 against 85 with 5 splits; o_proj and down, which need 8 splits
+    // there, were slower: 60.5 and 132 against 49 and 124, from the partials)
+    const int tiles = gemm_chunk_tiles(g, epi);
     const int nsteps = (g.K + 63) / 64;
-    int kc = 1;
-    if (epi != EPI_LOGITS) {
-      kc = std::max(1, D->cus / nbt);
+    auto split_for = [&](int nbt) {
+      int kc = std::max(1, D->cus / nbt);
       kc = std::min(std::min(kc, CHUNK_MAX_SPLIT), std::max(1, nsteps / 2));
       while (kc > 1 && (size_t)kc * g.M * (size_t)npd * ntiles * 16 > D->L.gpart_elems) --kc;
+      return kc;
+    };
+    int kc = 1;
+    g.wide = 0;
+    if (epi != EPI_LOGITS) {
+      const int kw = split_for(tiles * gemm_wide_mblocks(g.M));
+      g.ksplit = kw;
+      if (g.M >= GEMM_WIDE_MIN_ROWS && kw <= WIDE_MAX_SPLIT && gemm_wide_takes(g, epi)) {
+        g.wide = 1;
+        kc = kw;
+      } else {
+        kc = split_for(tiles * gemm_chunk_mblocks(g.M));
+      }
     }
     g.ksplit = kc;
     if (g.ksplit <= 1) g.norm_out = nullptr;
@@ -1604,6 +1621,7 @@ int dec_diag_gemm_chunk(const uint16_t *d_A, int32_t planes, int32_t M, int32_t 
   g.ldc = N;
   g.ksplit = ksplit;
   g.Cpart = d_part;
+  g.wide = 1;
   if (ksplit > 1 && (!d_part || part_elems < (int64_t)ksplit * M * gemm_ntiles(g, EPI_STORE) * 16)) return DEC_E_INVALID;
   if (!gemm_chunk_fits(g, EPI_STORE)) return DEC_E_INVALID;
   return launch_gemm_chunk(g, EPI_STORE, (hipStream_t)stream) == hipSuccess ? DEC_OK : DEC_E_HIP;
@@ -1661,6 +1679,7 @@ int dec_diag_gemm_chunk_noalloc(const uint16_t *d_A, int32_t planes, int32_t M, 
   g.C = d_C;
   g.ldc = N;
   g.ksplit = ksplit;
+  g.wide = 1;
   if (!gemm_chunk_fits(g, EPI_STORE)) return DEC_E_INVALID;
   if (ksplit > 1) {
     // every partial the reduce reads is rewritten by this call's blocks, so

@@ -332,9 +332,14 @@ hipError_t launch_gemm_chunk(const GemmArgs &g, int epi, hipStream_t st) {
   if (!gemm_chunk_fits(g, epi) || g.ksplit < 1 || (epi == EPI_LOGITS && g.ksplit != 1)) return hipErrorInvalidValue;
   const int ntiles16 = gemm_ntiles(g, epi);
   const int units = gemm_chunk_tiles(g, epi) * g.ksplit;
-  const int mblocks = gemm_chunk_mblocks(g.M);
-  const int blocks = (units + CK_XCDS - 1) / CK_XCDS * CK_XCDS * mblocks;
   hipError_t e;
+  if (g.wide && gemm_wide_takes(g, epi)) {
+    e = launch_gemm_wide(g, epi, ntiles16, units, st);
+    if (e != hipSuccess || g.ksplit <= 1) return e;
+    return launch_gemm_reduce(g, epi, ntiles16, st);
+  }
+  const int mblocks = (g.M + CK_ROWS - 1) / CK_ROWS;
+  const int blocks = (units + CK_XCDS - 1) / CK_XCDS * CK_XCDS * mblocks;
   switch (epi) {
     case EPI_STORE: e = launch_epi<EPI_STORE>(g, ntiles16, blocks, mblocks, st); break;
     case EPI_ADD: e = launch_epi<EPI_ADD>(g, ntiles16, blocks, mblocks, st); break;

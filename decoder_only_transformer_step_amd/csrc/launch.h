@@ -33,6 +33,13 @@ hipError_t launch_pack_w32(const uint16_t *W, int64_t rows, int K, uint16_t *P, 
 int gemm_chunk_tiles(const GemmArgs &g, int epi);
 int gemm_chunk_mblocks(int rows);
 hipError_t launch_gemm_chunk(const GemmArgs &g, int epi, hipStream_t st);
+// Chunks of GEMM_WIDE_MIN_ROWS or more rows (not the logits) with g.wide
+// set take the wide kernel inside launch_gemm_chunk: 256 x 256 blocks, both
+// operands in LDS.
+constexpr int GEMM_WIDE_MIN_ROWS = 256;
+bool gemm_wide_takes(const GemmArgs &g, int epi);
+int gemm_wide_mblocks(int rows);
+hipError_t launch_gemm_wide(const GemmArgs &g, int epi, int ntiles16, int units, hipStream_t st);
 // Projection of 2 .. GEMV_ROWS_MAX rows with bf16 weights, each weight row
 // streamed once (verify passes, small decode batches): K split over the waves
 // of a block, the rows' activations in registers (x + gamma: fused RMSNorm;
