@@ -72,6 +72,7 @@ SIGNATURES = {
     "decoder_last_error": (ctypes.c_char_p, [_P]),
     "dec_diag_gemm": (ctypes.c_int, [_P, _I32, _I32, _P, _I32, _P, _P]),
     "dec_diag_gemm_chunk": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, ctypes.c_int64, _P]),
+    "dec_diag_gemm_grouped": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _I32, _P, _I32, _P, _I32, _P, _P]),
     "dec_diag_pack_w32": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "dec_diag_gemm_chunk_noalloc": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _P, _I32, _P]),
     "dec_diag_rmsnorm": (ctypes.c_int, [_P, _P, _I32, _I32, ctypes.c_double, _P, _P]),
@@ -312,6 +313,18 @@ def diag_gemm_chunk(A, Wp, C, ksplit, part, stream):
     _check(lib().dec_diag_gemm_chunk(_ptr(A), planes, M, K, _ptr(Wp), N, _ptr(C), ksplit,
                                      _ptr(part) if part is not None else None, n_part,
                                      ctypes.c_void_p(stream)), None, "dec_diag_gemm_chunk")
+
+
+def diag_gemm_grouped(A, Wp, E, a_rows, groups, max_group_rows, C, stream):
+    """A: bf16 [planes][M][K]; Wp: the stacked expert weights [E * N][K]
+    packed by diag_pack_w32; a_rows int32 [P]; groups int32 [1 + 3 E]
+    (count, expert[E], start[E], count[E]); C fp32 [P][N]."""
+    planes, M, K = A.shape
+    N = Wp.shape[0] // E
+    P = a_rows.numel()
+    _check(lib().dec_diag_gemm_grouped(_ptr(A), planes, M, K, _ptr(Wp), E, N, _ptr(a_rows), P, _ptr(groups),
+                                       max_group_rows, _ptr(C), ctypes.c_void_p(stream)),
+           None, "dec_diag_gemm_grouped")
 
 
 def diag_gemm_chunk_noalloc(A, Wp, C, ksplit, stream):

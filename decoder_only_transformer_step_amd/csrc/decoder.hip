@@ -106,10 +106,12 @@ size_t quant_bytes(const decoder_config_t *c) {
 // Weight matrices that get a packed copy for the chunk projection kernel:
 // only when prefill chunks or decode batches can reach the chunk kernel, and
 // only the shapes the packed tiles cover.  Order within a layer: qkv, o, gate_up /
-// shared gate_up, down / shared down.
+// shared gate_up, down / shared down, then (MoE, prefill chunks only) the
+// stacked expert gate/up and down matrices for the grouped form.
+constexpr int PACK_MATS = 6;
 struct PackSpec {
-  int64_t rows[4];
-  int K[4];
+  int64_t rows[PACK_MATS];
+  int K[PACK_MATS];
 };
 
 PackSpec pack_spec(const decoder_config_t *c) {
@@ -117,9 +119,14 @@ PackSpec pack_spec(const decoder_config_t *c) {
   if (c->max_chunk <= CHUNK_MIN_ROWS && c->max_batch < CHUNK_BATCH_MIN_ROWS) return p;
   const int d = c->head_dim, H = c->hidden, qd = c->n_heads * d, qkvr = (c->n_heads + 2 * c->n_kv_heads) * d;
   const int I = c->n_experts > 0 ? c->shared_inter : c->ffn_inter;
-  const int64_t rows[4] = {qkvr, H, 2 * (int64_t)I, I > 0 ? H : 0};
-  const int K[4] = {H, qd, H, I};
-  for (int i = 0; i < 4; ++i) {
+  // the grouped form needs each expert's slice (and its up half) on a
+  // 32-row tile boundary
+  const int E = c->n_experts, Ie = c->expert_inter;
+  const bool grouped = E > 0 && c->max_chunk > CHUNK_MIN_ROWS && Ie % 32 == 0 && H % 32 == 0;
+  const int64_t rows[PACK_MATS] = {qkvr, H, 2 * (int64_t)I, I > 0 ? H : 0, grouped ? 2 * (int64_t)E * Ie : 0,
+                                   grouped ? (int64_t)E * H : 0};
+  const int K[PACK_MATS] = {H, qd, H, I, H, Ie};
+  for (int i = 0; i < PACK_MATS; ++i) {
     const bool ok = rows[i] > 0 && K[i] > 0 && pack_w32_fits(rows[i], K[i]);
     p.rows[i] = ok ? rows[i] : 0;
     p.K[i] = ok ? K[i] : 0;
@@ -129,7 +136,7 @@ PackSpec pack_spec(const decoder_config_t *c) {
 
 size_t pack_layer_elems(const PackSpec &p) {
   size_t n = 0;
-  for (int i = 0; i < 4; ++i) n += (size_t)p.rows[i] * p.K[i];
+  for (int i = 0; i < PACK_MATS; ++i) n += (size_t)p.rows[i] * p.K[i];
   return n;
 }
 
@@ -265,7 +272,9 @@ struct decoder {
   Layout L;
   std::vector<decoder_layer_weights_t> layers;
   struct Packed {
-    const uint16_t *w[4];  // qkv, o, gate_up (or shared gate_up), down (or shared down); null if not packed
+    // qkv, o, gate_up (or shared gate_up), down (or shared down), expert
+    // gate_up, expert down; null if not packed
+    const uint16_t *w[PACK_MATS];
   };
   std::vector<Packed> packed;
   struct QuantW {
@@ -1025,11 +1034,19 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   g.group_count = mr.group_count;
   g.ksplit = 1;
   if (rows <= 16) g = qcodes(D, g, l, 4);
+  // a prefill chunk: the grouped form of the chunk kernel on the packed
+  // expert weights (32-row blocks of a group's pairs)
+  const bool packed = rows > CHUNK_MIN_ROWS && !g.Wq && D->packed[l].w[4] && D->packed[l].w[5];
   const double exp_wb = g.Wq ? 1.0 : 2.0;  // weight bytes per expert weight streamed
   {
     NodeTimer t(D, DEC_NODE_EXPERTS, exp_bytes * exp_wb * 2.0 / 3.0 + rows * (double)H * 2 + rows * (double)k * Ie * 2,
                 2.0 * rows * k * 2.0 * Ie * H);
-    e = launch_gemm(g, EPI_SWIGLU, grp_rows, slots, st);
+    if (packed) {
+      g.Wp = D->packed[l].w[4];
+      e = launch_gemm_chunk_grouped(g, EPI_SWIGLU, rows, slots, st);
+    } else {
+      e = launch_gemm(g, EPI_SWIGLU, grp_rows, slots, st);
+    }
   }
   if (e != hipSuccess) return hip_fail(D, e, "moe gate_up");
   g.A = D->hexp;
@@ -1048,7 +1065,12 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   {
     NodeTimer t(D, DEC_NODE_EXPERTS, exp_bytes * exp_wb / 3.0 + rows * (double)k * Ie * 2 + rows * (double)k * H * 4,
                 2.0 * rows * k * (double)Ie * H);
-    e = launch_gemm(g, EPI_STORE, grp_rows, slots, st);
+    if (packed) {
+      g.Wp = D->packed[l].w[5];
+      e = launch_gemm_chunk_grouped(g, EPI_STORE, rows, slots, st);
+    } else {
+      e = launch_gemm(g, EPI_STORE, grp_rows, slots, st);
+    }
   }
   if (e != hipSuccess) return hip_fail(D, e, "moe down");
   if (Is > 0) {
@@ -1303,11 +1325,12 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
     D->packed.assign(cfg->n_layers, decoder::Packed{});
     for (int l = 0; l < cfg->n_layers; ++l) {
       const decoder_layer_weights_t &lw = D->layers[l];
-      const uint16_t *src[4] = {
+      const uint16_t *src[PACK_MATS] = {
           (const uint16_t *)lw.w_qkv, (const uint16_t *)lw.w_o,
           (const uint16_t *)(cfg->n_experts > 0 ? lw.w_sh_gate_up : lw.w_gate_up),
-          (const uint16_t *)(cfg->n_experts > 0 ? lw.w_sh_down : lw.w_down)};
-      for (int i = 0; i < 4; ++i) {
+          (const uint16_t *)(cfg->n_experts > 0 ? lw.w_sh_down : lw.w_down),
+          (const uint16_t *)lw.w_exp_gate_up, (const uint16_t *)lw.w_exp_down};
+      for (int i = 0; i < PACK_MATS; ++i) {
         D->packed[l].w[i] = nullptr;
         if (!ps.rows[i] || !src[i]) continue;
         if (launch_pack_w32(src[i], ps.rows[i], ps.K[i], pk, (hipStream_t)stream) != hipSuccess) {
@@ -1625,6 +1648,37 @@ int dec_diag_gemm_chunk(const uint16_t *d_A, int32_t planes, int32_t M, int32_t 
   if (ksplit > 1 && (!d_part || part_elems < (int64_t)ksplit * M * gemm_ntiles(g, EPI_STORE) * 16)) return DEC_E_INVALID;
   if (!gemm_chunk_fits(g, EPI_STORE)) return DEC_E_INVALID;
   return launch_gemm_chunk(g, EPI_STORE, (hipStream_t)stream) == hipSuccess ? DEC_OK : DEC_E_HIP;
+}
+
+int dec_diag_gemm_grouped(const uint16_t *d_A, int32_t planes, int32_t M, int32_t K, const uint16_t *d_Wp,
+                          int32_t E, int32_t N, const int32_t *d_a_rows, int32_t P, const int32_t *d_groups,
+                          int32_t max_group_rows, float *d_C, void *stream) {
+  if (!d_A || !d_Wp || !d_C || !d_a_rows || !d_groups || (planes != 1 && planes != 2) || M < 1 || E < 1 ||
+      N < 32 || N % 32 || K < 16 || K % 16 || P < 1 || max_group_rows < 1 || max_group_rows > P)
+    return DEC_E_INVALID;
+  GemmArgs g{};
+  g.A = d_A;
+  g.a_lo = planes == 2 ? (int64_t)M * K : 0;
+  g.a_rows = d_a_rows;
+  g.lda = K;
+  g.W = d_Wp;
+  g.Wp = d_Wp;
+  g.w_group_stride = (int64_t)N * K;
+  g.M = P;
+  g.N = N;
+  g.K = K;
+  g.np_off = N;
+  g.C = d_C;
+  g.ldc = N;
+  g.ksplit = 1;
+  g.n_groups = d_groups;
+  g.group_expert = d_groups + 1;
+  g.group_start = d_groups + 1 + E;
+  g.group_count = d_groups + 1 + 2 * E;
+  if (!gemm_chunk_grouped_fits(g, EPI_STORE)) return DEC_E_INVALID;
+  return launch_gemm_chunk_grouped(g, EPI_STORE, max_group_rows, std::min(E, P), (hipStream_t)stream) == hipSuccess
+             ? DEC_OK
+             : DEC_E_HIP;
 }
 
 }  // extern "C"

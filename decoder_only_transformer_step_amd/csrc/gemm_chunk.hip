@@ -28,6 +28,13 @@
 //    tiles; partials go to Cpart and gemm_reduce sums them in fixed split
 //    order.  Without a split the epilogue runs straight from the
 //    accumulators.
+//  * Grouped form (MoE experts of a prefill chunk; engine.zig Engine.prefill
+//    batches a chunk's columns by chosen expert, so each chosen expert's
+//    weights are read once): a unit is (group, weight-tile block), the
+//    weights are the expert's slice of a packed copy of the stacked
+//    [E][rows][K] matrix, and a block takes up to 32 of the group's rows,
+//    gathered through a_rows (the token row of each (token, expert) pair).
+//    Blocks past the device-side group count or the group's rows exit.
 #include <algorithm>
 
 #include "common.h"
@@ -140,11 +147,48 @@ __device__ __forceinline__ void mma_step(const u32x4 *src, const u32x4 (&w)[CK_N
   }
 }
 
+// Grouped form: this thread's staging pieces as row pointers (the gather
+// resolved once per block; a row past the block's rows reads the zero page)
+// and their k offsets within a step.
+template <int MT, bool SPLIT>
+struct ARows {
+  const uint16_t *p[AStage<MT, SPLIT>::PER_THREAD];
+  int koff[AStage<MT, SPLIT>::PER_THREAD];
+};
+
+template <int MT, bool SPLIT>
+__device__ __forceinline__ ARows<MT, SPLIT> a_rows_of(const GemmArgs &g, int row0, int rows) {
+  constexpr int PER_PLANE = MT * 256, PIECES = AStage<MT, SPLIT>::PIECES;
+  ARows<MT, SPLIT> ra;
+#pragma unroll
+  for (int i = 0; i < AStage<MT, SPLIT>::PER_THREAD; ++i) {
+    const int e = threadIdx.x + i * CK_WAVES * WAVE;
+    const int plane = e / PER_PLANE, rem = e - plane * PER_PLANE;
+    const int r = rem >> 3;
+    ra.koff[i] = (rem & 7) * 8;
+    const bool ok = (PIECES % (CK_WAVES * WAVE) == 0 || e < PIECES) && r < rows;
+    const int64_t src = ok ? (g.a_rows ? g.a_rows[row0 + r] : row0 + r) : 0;
+    ra.p[i] = ok ? g.A + plane * g.a_lo + src * g.lda + ra.koff[i] : nullptr;
+  }
+  return ra;
+}
+
+template <int MT, bool SPLIT>
+__device__ __forceinline__ void a_load_rows(const ARows<MT, SPLIT> &ra, int k0, int kend,
+                                            u32x4 (&ar)[AStage<MT, SPLIT>::PER_THREAD]) {
+#pragma unroll
+  for (int i = 0; i < AStage<MT, SPLIT>::PER_THREAD; ++i) {
+    const bool ok = ra.p[i] != nullptr && k0 + ra.koff[i] < kend;
+    ar[i] = load16(ok ? static_cast<const void *>(ra.p[i] + k0) : static_cast<const void *>(ck_zero + (threadIdx.x & 63)));
+  }
+}
+
 // Block b -> (unit u = (weight tile, k split), row block mb): the row
 // blocks of one unit are CK_XCDS block ids apart, so they are dispatched to
 // the same XCD at about the same time and the second one finds the weights
-// in that XCD's L2.
-template <int MT, int EPI, bool SPLIT>
+// in that XCD's L2.  GR (grouped): u = (group, weight tile), row blocks of
+// 32 MT rows of the group.
+template <int MT, int EPI, bool SPLIT, bool GR>
 __global__ __launch_bounds__(CK_WAVES * WAVE, 2) void gemm_chunk_kernel(GemmArgs g, int ntiles16, int mblocks) {
   constexpr int NP = paired<EPI>();
   constexpr int LT = CK_NS / NP;  // logical 32-row tiles per wave
@@ -156,13 +200,36 @@ __global__ __launch_bounds__(CK_WAVES * WAVE, 2) void gemm_chunk_kernel(GemmArgs
   const int nbt = (ntiles32 + CK_WAVES * LT - 1) / (CK_WAVES * LT);
   const int u = (blockIdx.x / (CK_XCDS * mblocks)) * CK_XCDS + blockIdx.x % CK_XCDS;
   const int mb = (blockIdx.x / CK_XCDS) % mblocks;
-  if (u >= nbt * g.ksplit) return;
-  const int bt = u % nbt, z = u / nbt;
-  const int row0 = mb * CK_ROWS, rows = min(CK_ROWS, g.M - row0);
+  int bt, z, row0, rows;
+  const uint16_t *Wbase = g.Wp;
+  if constexpr (GR) {
+    // ksplit is 1: u = group * nbt + tile block
+    const int gi = u / nbt;
+    if (gi >= *g.n_groups) return;
+    bt = u - gi * nbt;
+    z = 0;
+    row0 = mb * 32 * MT;
+    rows = min(32 * MT, g.group_count[gi] - row0);
+    if (rows <= 0) return;
+    row0 += g.group_start[gi];
+    Wbase += (int64_t)g.group_expert[gi] * g.w_group_stride;
+  } else {
+    if (u >= nbt * g.ksplit) return;
+    bt = u % nbt;
+    z = u / nbt;
+    row0 = mb * CK_ROWS;
+    rows = min(CK_ROWS, g.M - row0);
+  }
   const int nsteps = (K + CK_STEP - 1) / CK_STEP;
   const int per = (nsteps + g.ksplit - 1) / g.ksplit;
   const int s0 = min(nsteps, z * per), s1 = min(nsteps, s0 + per);
   const uint16_t *abase = g.A + (int64_t)row0 * g.lda;
+  ARows<MT, SPLIT> ra;
+  if constexpr (GR) ra = a_rows_of<MT, SPLIT>(g, row0, rows);
+  auto aload = [&](int k0, int kend, u32x4(&ar)[AStage<MT, SPLIT>::PER_THREAD]) {
+    if constexpr (GR) a_load_rows<MT, SPLIT>(ra, k0, kend, ar);
+    else a_load<MT, SPLIT>(abase, g, rows, k0, kend, ar);
+  };
 
   // this wave's 32-row tiles T (16-row logical tiles 2T, 2T + 1): weight
   // tile p = lt * NP + half, in the packed copy at row tile r0 / 32
@@ -178,7 +245,7 @@ __global__ __launch_bounds__(CK_WAVES * WAVE, 2) void gemm_chunk_kernel(GemmArgs
 #pragma unroll
     for (int h = 0; h < NP; ++h) {
       wv[lt * NP + h] = ok;
-      wp[lt * NP + h] = g.Wp + (ok ? (int64_t)((r0 + h * g.np_off) / 32) * (K / 16) * 512 : 0) + lane * 8;
+      wp[lt * NP + h] = Wbase + (ok ? (int64_t)((r0 + h * g.np_off) / 32) * (K / 16) * 512 : 0) + lane * 8;
     }
   }
   int sw[4];
@@ -197,7 +264,7 @@ __global__ __launch_bounds__(CK_WAVES * WAVE, 2) void gemm_chunk_kernel(GemmArgs
   u32x4 ar[AStage<MT, SPLIT>::PER_THREAD];
   const int kend = min(K, s1 * CK_STEP);
   if (s0 < s1) {
-    a_load<MT, SPLIT>(abase, g, rows, s0 * CK_STEP, kend, ar);
+    aload(s0 * CK_STEP, kend, ar);
     w_load(wp, wv, s0 * CK_STEP, kend, w0);
     a_store<MT, SPLIT>(a_s[0], ar);
   }
@@ -206,12 +273,12 @@ __global__ __launch_bounds__(CK_WAVES * WAVE, 2) void gemm_chunk_kernel(GemmArgs
   // LDS store then leaves the newer weight loads in flight).  Steps at or
   // past s1 read zeros (k >= kend), so an odd step count adds one zero step.
   for (int s = s0; s < s1; s += 2) {
-    a_load<MT, SPLIT>(abase, g, rows, (s + 1) * CK_STEP, kend, ar);
+    aload((s + 1) * CK_STEP, kend, ar);
     w_load(wp, wv, (s + 1) * CK_STEP, kend, w1);
     mma_step<MT, SPLIT>(a_s[0], w0, sw, acc);
     a_store<MT, SPLIT>(a_s[1], ar);
     __syncthreads();
-    a_load<MT, SPLIT>(abase, g, rows, (s + 2) * CK_STEP, kend, ar);
+    aload((s + 2) * CK_STEP, kend, ar);
     w_load(wp, wv, (s + 2) * CK_STEP, kend, w0);
     mma_step<MT, SPLIT>(a_s[1], w1, sw, acc);
     a_store<MT, SPLIT>(a_s[0], ar);
@@ -269,14 +336,14 @@ __global__ __launch_bounds__(CK_WAVES * WAVE, 2) void gemm_chunk_kernel(GemmArgs
   }
 }
 
-template <int MT, int EPI>
+template <int MT, int EPI, bool GR = false>
 hipError_t launch_mt(const GemmArgs &g, int ntiles16, int blocks, int mblocks, hipStream_t st) {
   if (g.a_lo)
-    hipLaunchKernelGGL((gemm_chunk_kernel<MT, EPI, true>), dim3(blocks), dim3(CK_WAVES * WAVE), 0, st, g, ntiles16,
-                       mblocks);
+    hipLaunchKernelGGL((gemm_chunk_kernel<MT, EPI, true, GR>), dim3(blocks), dim3(CK_WAVES * WAVE), 0, st, g,
+                       ntiles16, mblocks);
   else
-    hipLaunchKernelGGL((gemm_chunk_kernel<MT, EPI, false>), dim3(blocks), dim3(CK_WAVES * WAVE), 0, st, g, ntiles16,
-                       mblocks);
+    hipLaunchKernelGGL((gemm_chunk_kernel<MT, EPI, false, GR>), dim3(blocks), dim3(CK_WAVES * WAVE), 0, st, g,
+                       ntiles16, mblocks);
   return hipGetLastError();
 }
 
@@ -349,4 +416,25 @@ hipError_t launch_gemm_chunk(const GemmArgs &g, int epi, hipStream_t st) {
   }
   if (e != hipSuccess || g.ksplit <= 1) return e;
   return launch_gemm_reduce(g, epi, ntiles16, st);
+}
+
+bool gemm_chunk_grouped_fits(const GemmArgs &g, int epi) {
+  // each expert's slice of the stacked weights starts at a 32-row tile; the
+  // SwiGLU up rows follow the expert's N gate rows
+  const int64_t wrows = epi == EPI_SWIGLU ? 2 * (int64_t)g.N : g.N;
+  return (epi == EPI_SWIGLU || epi == EPI_STORE) && g.Wp != nullptr && g.A != nullptr && g.x == nullptr &&
+         g.n_groups != nullptr && g.group_expert != nullptr && g.group_start != nullptr &&
+         g.group_count != nullptr && g.ksplit == 1 && g.N % 32 == 0 && pack_w32_fits(wrows, g.K) &&
+         g.w_group_stride == wrows * g.K && (epi != EPI_SWIGLU || g.np_off == g.N);
+}
+
+hipError_t launch_gemm_chunk_grouped(const GemmArgs &g, int epi, int max_group_rows, int group_slots,
+                                     hipStream_t st) {
+  if (!gemm_chunk_grouped_fits(g, epi) || max_group_rows < 1 || group_slots < 1) return hipErrorInvalidValue;
+  const int ntiles16 = gemm_ntiles(g, epi);
+  const int units = gemm_chunk_tiles(g, epi) * group_slots;
+  const int mblocks = (max_group_rows + 31) / 32;
+  const int blocks = (units + CK_XCDS - 1) / CK_XCDS * CK_XCDS * mblocks;
+  if (epi == EPI_SWIGLU) return launch_mt<1, EPI_SWIGLU, true>(g, ntiles16, blocks, mblocks, st);
+  return launch_mt<1, EPI_STORE, true>(g, ntiles16, blocks, mblocks, st);
 }

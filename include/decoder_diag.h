@@ -43,6 +43,24 @@ int dec_diag_gemm_chunk(const uint16_t *d_A, int32_t planes, int32_t M, int32_t 
                         int32_t N, float *d_C, int32_t ksplit, float *d_part, int64_t part_elems,
                         void *stream);
 
+/* Grouped expert projection with the chunk kernel's grouped form (MoE
+ * prefill; engine.zig Engine.prefill: a chunk's token columns are batched by
+ * chosen expert, so each chosen expert's weights are read once).
+ * C[p][n] = sum_k A[a_rows[p]][k] W_e[n][k] for pair p of group i, e =
+ * expert[i].  A bf16 [planes][M][K] (planes as dec_diag_gemm_chunk);
+ * d_Wp = the stacked expert weights [E][N][K], taken as one [E N][K] matrix
+ * and packed by dec_diag_pack_w32; d_a_rows int32 [P]; C fp32 [P][N].
+ * d_groups (device int32, the layout the MoE router's grouping writes):
+ * [0] = group count G <= min(E, P), then expert[E], start[E], count[E];
+ * group i covers pairs start[i] .. start[i] + count[i] - 1.  The table's
+ * contents are the caller's contract, not checked: every a_rows value < M,
+ * every group inside [0, P), every expert < E, every count <=
+ * max_group_rows (<= P); rows of a longer group are not computed.
+ * N % 32 == 0, K % 16 == 0.  DEC_E_INVALID on bad sizes. */
+int dec_diag_gemm_grouped(const uint16_t *d_A, int32_t planes, int32_t M, int32_t K, const uint16_t *d_Wp,
+                          int32_t E, int32_t N, const int32_t *d_a_rows, int32_t P, const int32_t *d_groups,
+                          int32_t max_group_rows, float *d_C, void *stream);
+
 /* dec_diag_gemm_chunk without the partial-sum workspace, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation).  Same arguments,

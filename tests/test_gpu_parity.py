@@ -75,6 +75,72 @@ def test_chunk_projection_kernel_matches_oracle(M, N, K, ksplit, planes):
     assert np.all(np.abs(got - want) <= 1e-6 * K * scale + 1e-30)
 
 
+def _group_table(routes, E):
+    """(pair_row, groups, max count) for a list of per-token expert lists:
+    pairs ordered by group, groups in the order the experts first appear,
+    the layout the router's grouping writes (count, expert[E], start[E],
+    count[E])."""
+    order = []
+    for r in routes:
+        for e in r:
+            if e not in order:
+                order.append(e)
+    pair_row, expert, start, count = [], [], [], []
+    for e in order:
+        rows = [t for t, r in enumerate(routes) if e in r]
+        expert.append(e)
+        start.append(len(pair_row))
+        count.append(len(rows))
+        pair_row += rows
+    pad = [0] * (E - len(order))
+    groups = [len(order)] + expert + pad + start + pad + count + pad
+    return np.array(pair_row, dtype=np.int32), np.array(groups, dtype=np.int32), max(count)
+
+
+@pytest.mark.parametrize("M,E,k,N,K,planes,skew", [(24, 8, 2, 96, 256, 2, 0), (128, 60, 4, 1408, 2048, 2, 0),
+                                                   (128, 60, 4, 2048, 1408, 2, 0), (100, 6, 2, 64, 688, 1, 1),
+                                                   (40, 5, 3, 32, 16, 2, 2)])
+def test_grouped_projection_kernel_matches_oracle(M, E, k, N, K, planes, skew):
+    """The grouped (MoE expert) form of the chunk kernel: pair p of group i
+    reads token row a_rows[p] and expert i's weights.  Uniform routes (every
+    group inside one 32-row block), a skewed route where one expert takes
+    every token (several 32-row blocks and a ragged tail), groups in a
+    non-sorted expert order, K not a multiple of the 64-wide step."""
+    from decoder_only_transformer_step_amd.binding import diag_gemm_grouped, diag_pack_w32
+    log("gemm_grouped", M, E, k, N, K, planes, skew)
+    rng = np.random.default_rng(7 * M + E)
+    routes = [list(rng.choice(E, size=k, replace=False)) for _ in range(M)]
+    if skew:
+        hot = E - 1
+        routes = [[hot] + [e for e in r if e != hot][:k - 1] for r in routes]
+    pair_row, groups, max_rows = _group_table(routes, E)
+    P = len(pair_row)
+    hi = synth.normal_bf16(M * K, 51 + M, 1.0)
+    lo = synth.normal_bf16(M * K, 53 + M, 2.0 ** -9)
+    A = np.stack([hi, lo])[:planes]
+    W = synth.normal_bf16(E * N * K, 57 + N, 0.02)
+    st = torch.cuda.current_stream().cuda_stream
+    dA = torch.from_numpy(A.view(np.int16)).cuda().view(planes, M, K)
+    dW = torch.from_numpy(W.view(np.int16)).cuda().view(E * N, K)
+    dP = torch.empty_like(dW)
+    diag_pack_w32(dW, dP, st)
+    dC = torch.full((P, N), float("nan"), dtype=torch.float32, device="cuda")
+    diag_gemm_grouped(dA, dP, E, torch.from_numpy(pair_row).cuda(), torch.from_numpy(groups).cuda(), max_rows,
+                      dC, st)
+    torch.cuda.synchronize()
+    got = dC.cpu().numpy().astype(np.float64)
+    a = sum(bits_of(A[p]).astype(np.float64).reshape(M, K) for p in range(planes))
+    a_abs = sum(np.abs(bits_of(A[p]).astype(np.float64).reshape(M, K)) for p in range(planes))
+    n_groups = int(groups[0])
+    for i in range(n_groups):
+        e, s0, c = int(groups[1 + i]), int(groups[1 + E + i]), int(groups[1 + 2 * E + i])
+        We = W[e * N * K:(e + 1) * N * K]
+        rows = pair_row[s0:s0 + c]
+        want = oracle.matmul(We, N, K, a[rows])
+        scale = a_abs[rows] @ np.abs(bits_of(We)).reshape(N, K).T.astype(np.float64)
+        assert np.all(np.abs(got[s0:s0 + c] - want) <= 1e-6 * K * scale + 1e-30), (i, e)
+
+
 def test_rmsnorm_kernel_matches_oracle():
     from decoder_only_transformer_step_amd.binding import diag_rmsnorm
     rows, H = 7, 576
