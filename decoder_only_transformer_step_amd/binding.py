@@ -72,7 +72,7 @@ SIGNATURES = {
     "decoder_last_error": (ctypes.c_char_p, [_P]),
     "dec_diag_gemm": (ctypes.c_int, [_P, _I32, _I32, _P, _I32, _P, _P]),
     "dec_diag_gemm_chunk": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, ctypes.c_int64, _P]),
-    "dec_diag_gemm_grouped": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _I32, _P, _I32, _P, _I32, _P, _P]),
+    "dec_diag_gemm_grouped": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _I32, _P, _I32, _P, _P, _P]),
     "dec_diag_pack_w32": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "dec_diag_gemm_chunk_noalloc": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _P, _I32, _P]),
     "dec_diag_rmsnorm": (ctypes.c_int, [_P, _P, _I32, _I32, ctypes.c_double, _P, _P]),
@@ -315,7 +315,7 @@ def diag_gemm_chunk(A, Wp, C, ksplit, part, stream):
                                      ctypes.c_void_p(stream)), None, "dec_diag_gemm_chunk")
 
 
-def diag_gemm_grouped(A, Wp, E, a_rows, groups, max_group_rows, C, stream):
+def diag_gemm_grouped(A, Wp, E, a_rows, groups, C, stream):
     """A: bf16 [planes][M][K]; Wp: the stacked expert weights [E * N][K]
     packed by diag_pack_w32; a_rows int32 [P]; groups int32 [1 + 3 E]
     (count, expert[E], start[E], count[E]); C fp32 [P][N]."""
@@ -323,7 +323,7 @@ def diag_gemm_grouped(A, Wp, E, a_rows, groups, max_group_rows, C, stream):
     N = Wp.shape[0] // E
     P = a_rows.numel()
     _check(lib().dec_diag_gemm_grouped(_ptr(A), planes, M, K, _ptr(Wp), E, N, _ptr(a_rows), P, _ptr(groups),
-                                       max_group_rows, _ptr(C), ctypes.c_void_p(stream)),
+                                       _ptr(C), ctypes.c_void_p(stream)),
            None, "dec_diag_gemm_grouped")
 
 

@@ -1043,7 +1043,7 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
                 2.0 * rows * k * 2.0 * Ie * H);
     if (packed) {
       g.Wp = D->packed[l].w[4];
-      e = launch_gemm_chunk_grouped(g, EPI_SWIGLU, rows, slots, st);
+      e = launch_gemm_chunk_grouped(g, EPI_SWIGLU, rows * k, slots, st);
     } else {
       e = launch_gemm(g, EPI_SWIGLU, grp_rows, slots, st);
     }
@@ -1067,7 +1067,7 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
                 2.0 * rows * k * (double)Ie * H);
     if (packed) {
       g.Wp = D->packed[l].w[5];
-      e = launch_gemm_chunk_grouped(g, EPI_STORE, rows, slots, st);
+      e = launch_gemm_chunk_grouped(g, EPI_STORE, rows * k, slots, st);
     } else {
       e = launch_gemm(g, EPI_STORE, grp_rows, slots, st);
     }
@@ -1652,9 +1652,9 @@ int dec_diag_gemm_chunk(const uint16_t *d_A, int32_t planes, int32_t M, int32_t 
 
 int dec_diag_gemm_grouped(const uint16_t *d_A, int32_t planes, int32_t M, int32_t K, const uint16_t *d_Wp,
                           int32_t E, int32_t N, const int32_t *d_a_rows, int32_t P, const int32_t *d_groups,
-                          int32_t max_group_rows, float *d_C, void *stream) {
+                          float *d_C, void *stream) {
   if (!d_A || !d_Wp || !d_C || !d_a_rows || !d_groups || (planes != 1 && planes != 2) || M < 1 || E < 1 ||
-      N < 32 || N % 32 || K < 16 || K % 16 || P < 1 || max_group_rows < 1 || max_group_rows > P)
+      N < 32 || N % 32 || K < 16 || K % 16 || P < 1)
     return DEC_E_INVALID;
   GemmArgs g{};
   g.A = d_A;
@@ -1676,7 +1676,7 @@ int dec_diag_gemm_grouped(const uint16_t *d_A, int32_t planes, int32_t M, int32_
   g.group_start = d_groups + 1 + E;
   g.group_count = d_groups + 1 + 2 * E;
   if (!gemm_chunk_grouped_fits(g, EPI_STORE)) return DEC_E_INVALID;
-  return launch_gemm_chunk_grouped(g, EPI_STORE, max_group_rows, std::min(E, P), (hipStream_t)stream) == hipSuccess
+  return launch_gemm_chunk_grouped(g, EPI_STORE, P, std::min(E, P), (hipStream_t)stream) == hipSuccess
              ? DEC_OK
              : DEC_E_HIP;
 }

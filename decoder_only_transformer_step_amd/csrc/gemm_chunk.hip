@@ -30,11 +30,15 @@
 //    accumulators.
 //  * Grouped form (MoE experts of a prefill chunk; engine.zig Engine.prefill
 //    batches a chunk's columns by chosen expert, so each chosen expert's
-//    weights are read once): a unit is (group, weight-tile block), the
-//    weights are the expert's slice of a packed copy of the stacked
-//    [E][rows][K] matrix, and a block takes up to 32 of the group's rows,
-//    gathered through a_rows (the token row of each (token, expert) pair).
-//    Blocks past the device-side group count or the group's rows exit.
+//    weights are read once): the groups' rows are cut into 32-row tiles (in
+//    group order), a block takes one (row tile, weight-tile block) and finds
+//    its group from the device-side group counts; the weights are the
+//    expert's slice of a packed copy of the stacked [E][rows][K] matrix and
+//    the rows are gathered through a_rows (the token row of each (token,
+//    expert) pair).  The grid covers the largest possible tile count, and
+//    only blocks past the actual count exit: a grid of every group times its
+//    largest possible row count, most of whose blocks exit at once, measured
+//    close to twice as slow.
 #include <algorithm>
 
 #include "common.h"
@@ -186,8 +190,8 @@ __device__ __forceinline__ void a_load_rows(const ARows<MT, SPLIT> &ra, int k0, 
 // Block b -> (unit u = (weight tile, k split), row block mb): the row
 // blocks of one unit are CK_XCDS block ids apart, so they are dispatched to
 // the same XCD at about the same time and the second one finds the weights
-// in that XCD's L2.  GR (grouped): u = (group, weight tile), row blocks of
-// 32 MT rows of the group.
+// in that XCD's L2.  GR (grouped, mblocks 1): u = (row tile of 32 MT
+// rows, weight tile).
 template <int MT, int EPI, bool SPLIT, bool GR>
 __global__ __launch_bounds__(CK_WAVES * WAVE, 2) void gemm_chunk_kernel(GemmArgs g, int ntiles16, int mblocks) {
   constexpr int NP = paired<EPI>();
@@ -203,14 +207,46 @@ __global__ __launch_bounds__(CK_WAVES * WAVE, 2) void gemm_chunk_kernel(GemmArgs
   int bt, z, row0, rows;
   const uint16_t *Wbase = g.Wp;
   if constexpr (GR) {
-    // ksplit is 1: u = group * nbt + tile block
-    const int gi = u / nbt;
-    if (gi >= *g.n_groups) return;
-    bt = u - gi * nbt;
+    // ksplit is 1: u = row tile t * nbt + tile block.  Wave 0 finds the
+    // group of row tile t: an inclusive prefix sum of the groups' tile
+    // counts, 64 groups at a time.
+    __shared__ int tile_sel[2];
+    const int t = u / nbt;
+    bt = u - t * nbt;
+    if (wave == 0) {
+      const int ng = *g.n_groups;
+      int base = 0, gsel = -1, tsel = 0;
+      for (int c0 = 0; c0 < ng && gsel < 0; c0 += WAVE) {
+        const int i = c0 + lane;
+        const int cnt = i < ng ? g.group_count[i] : 0;
+        const int nt = (cnt + 32 * MT - 1) / (32 * MT);
+        int incl = nt;
+#pragma unroll
+        for (int o = 1; o < WAVE; o <<= 1) {
+          const int v = __shfl_up(incl, o, WAVE);
+          if (lane >= o) incl += v;
+        }
+        const bool hit = nt > 0 && t >= base + incl - nt && t < base + incl;
+        const unsigned long long m = __ballot(hit);
+        const int src = m ? __ffsll((long long)m) - 1 : 0;
+        const int first = __shfl(incl - nt, src, WAVE);
+        if (m) {
+          gsel = c0 + src;
+          tsel = t - base - first;
+        }
+        base += __shfl(incl, WAVE - 1, WAVE);
+      }
+      if (lane == 0) {
+        tile_sel[0] = gsel;
+        tile_sel[1] = tsel;
+      }
+    }
+    __syncthreads();
+    const int gi = tile_sel[0];
+    if (gi < 0) return;
     z = 0;
-    row0 = mb * 32 * MT;
+    row0 = tile_sel[1] * 32 * MT;
     rows = min(32 * MT, g.group_count[gi] - row0);
-    if (rows <= 0) return;
     row0 += g.group_start[gi];
     Wbase += (int64_t)g.group_expert[gi] * g.w_group_stride;
   } else {
@@ -428,13 +464,13 @@ bool gemm_chunk_grouped_fits(const GemmArgs &g, int epi) {
          g.w_group_stride == wrows * g.K && (epi != EPI_SWIGLU || g.np_off == g.N);
 }
 
-hipError_t launch_gemm_chunk_grouped(const GemmArgs &g, int epi, int max_group_rows, int group_slots,
-                                     hipStream_t st) {
-  if (!gemm_chunk_grouped_fits(g, epi) || max_group_rows < 1 || group_slots < 1) return hipErrorInvalidValue;
+hipError_t launch_gemm_chunk_grouped(const GemmArgs &g, int epi, int pairs, int group_slots, hipStream_t st) {
+  if (!gemm_chunk_grouped_fits(g, epi) || pairs < 1 || group_slots < 1) return hipErrorInvalidValue;
   const int ntiles16 = gemm_ntiles(g, epi);
-  const int units = gemm_chunk_tiles(g, epi) * group_slots;
-  const int mblocks = (max_group_rows + 31) / 32;
-  const int blocks = (units + CK_XCDS - 1) / CK_XCDS * CK_XCDS * mblocks;
-  if (epi == EPI_SWIGLU) return launch_mt<1, EPI_SWIGLU, true>(g, ntiles16, blocks, mblocks, st);
-  return launch_mt<1, EPI_STORE, true>(g, ntiles16, blocks, mblocks, st);
+  // sum over groups of ceil(count / 32) <= (pairs + 31 groups) / 32
+  const int64_t row_tiles = ((int64_t)pairs + 31 * (int64_t)std::min(group_slots, pairs)) / 32;
+  const int64_t blocks = row_tiles * gemm_chunk_tiles(g, epi);
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  if (epi == EPI_SWIGLU) return launch_mt<1, EPI_SWIGLU, true>(g, ntiles16, (int)blocks, 1, st);
+  return launch_mt<1, EPI_STORE, true>(g, ntiles16, (int)blocks, 1, st);
 }

@@ -36,11 +36,11 @@ hipError_t launch_gemm_chunk(const GemmArgs &g, int epi, hipStream_t st);
 // Grouped chunk projection (MoE experts, EPI_SWIGLU or EPI_STORE, no split):
 // g.Wp packs the stacked [E][rows][K] expert weights, g.w_group_stride is
 // one expert's rows x K; rows of group i are group_start[i] ..
-// + group_count[i] (A row through a_rows when set).  max_group_rows bounds
-// any group's rows, group_slots the device-side group count.
+// + group_count[i] (A row through a_rows when set).  pairs: the groups'
+// rows in total (the output rows); group_slots bounds the device-side group
+// count.
 bool gemm_chunk_grouped_fits(const GemmArgs &g, int epi);
-hipError_t launch_gemm_chunk_grouped(const GemmArgs &g, int epi, int max_group_rows, int group_slots,
-                                     hipStream_t st);
+hipError_t launch_gemm_chunk_grouped(const GemmArgs &g, int epi, int pairs, int group_slots, hipStream_t st);
 // Chunks of GEMM_WIDE_MIN_ROWS or more rows (not the logits) with g.wide
 // set take the wide kernel inside launch_gemm_chunk: 256 x 256 blocks, both
 // operands in LDS.

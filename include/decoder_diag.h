@@ -54,12 +54,12 @@ int dec_diag_gemm_chunk(const uint16_t *d_A, int32_t planes, int32_t M, int32_t 
  * [0] = group count G <= min(E, P), then expert[E], start[E], count[E];
  * group i covers pairs start[i] .. start[i] + count[i] - 1.  The table's
  * contents are the caller's contract, not checked: every a_rows value < M,
- * every group inside [0, P), every expert < E, every count <=
- * max_group_rows (<= P); rows of a longer group are not computed.
- * N % 32 == 0, K % 16 == 0.  DEC_E_INVALID on bad sizes. */
+ * the groups' counts positive, summing to at most P, their ranges inside
+ * [0, P), every expert < E.  N % 32 == 0, K % 16 == 0.  DEC_E_INVALID on
+ * bad sizes. */
 int dec_diag_gemm_grouped(const uint16_t *d_A, int32_t planes, int32_t M, int32_t K, const uint16_t *d_Wp,
                           int32_t E, int32_t N, const int32_t *d_a_rows, int32_t P, const int32_t *d_groups,
-                          int32_t max_group_rows, float *d_C, void *stream);
+                          float *d_C, void *stream);
 
 /* dec_diag_gemm_chunk without the partial-sum workspace, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight

@@ -113,7 +113,7 @@ def test_grouped_projection_kernel_matches_oracle(M, E, k, N, K, planes, skew):
     if skew:
         hot = E - 1
         routes = [[hot] + [e for e in r if e != hot][:k - 1] for r in routes]
-    pair_row, groups, max_rows = _group_table(routes, E)
+    pair_row, groups, _ = _group_table(routes, E)
     P = len(pair_row)
     hi = synth.normal_bf16(M * K, 51 + M, 1.0)
     lo = synth.normal_bf16(M * K, 53 + M, 2.0 ** -9)
@@ -125,8 +125,7 @@ def test_grouped_projection_kernel_matches_oracle(M, E, k, N, K, planes, skew):
     dP = torch.empty_like(dW)
     diag_pack_w32(dW, dP, st)
     dC = torch.full((P, N), float("nan"), dtype=torch.float32, device="cuda")
-    diag_gemm_grouped(dA, dP, E, torch.from_numpy(pair_row).cuda(), torch.from_numpy(groups).cuda(), max_rows,
-                      dC, st)
+    diag_gemm_grouped(dA, dP, E, torch.from_numpy(pair_row).cuda(), torch.from_numpy(groups).cuda(), dC, st)
     torch.cuda.synchronize()
     got = dC.cpu().numpy().astype(np.float64)
     a = sum(bits_of(A[p]).astype(np.float64).reshape(M, K) for p in range(planes))
