@@ -114,17 +114,40 @@ struct PackSpec {
   int K[PACK_MATS];
 };
 
+// The grouped expert projection of a prefill chunk streams the routed
+// experts from a packed copy of their stacked weights; when the shared
+// expert's intermediate size is a multiple of an expert's, the shared expert
+// joins that copy as Is / Ie pseudo-experts (pseudo-expert j: gate and up
+// rows j Ie .. (j + 1) Ie, and those columns of the down projection), which
+// every row takes with the shared gate as its weight, and the combine sums
+// their down outputs.  Returns that count, or 0 (the shared expert then runs
+// as its own two chunk projections).
+constexpr int MOE_MAX_SHARED_PARTS = 8;
+
+bool moe_grouped_packed(const decoder_config_t *c) {
+  return c->n_experts > 0 && c->max_chunk > CHUNK_MIN_ROWS && c->expert_inter > 0 && c->expert_inter % 32 == 0 &&
+         c->hidden % 32 == 0;
+}
+
+int moe_shared_parts(const decoder_config_t *c) {
+  if (!moe_grouped_packed(c) || c->shared_inter <= 0 || c->shared_inter % c->expert_inter) return 0;
+  const int s = c->shared_inter / c->expert_inter;
+  return s <= MOE_MAX_SHARED_PARTS ? s : 0;
+}
+
 PackSpec pack_spec(const decoder_config_t *c) {
   PackSpec p{};
   if (c->max_chunk <= CHUNK_MIN_ROWS && c->max_batch < CHUNK_BATCH_MIN_ROWS) return p;
   const int d = c->head_dim, H = c->hidden, qd = c->n_heads * d, qkvr = (c->n_heads + 2 * c->n_kv_heads) * d;
   const int I = c->n_experts > 0 ? c->shared_inter : c->ffn_inter;
   // the grouped form needs each expert's slice (and its up half) on a
-  // 32-row tile boundary
-  const int E = c->n_experts, Ie = c->expert_inter;
-  const bool grouped = E > 0 && c->max_chunk > CHUNK_MIN_ROWS && Ie % 32 == 0 && H % 32 == 0;
-  const int64_t rows[PACK_MATS] = {qkvr, H, 2 * (int64_t)I, I > 0 ? H : 0, grouped ? 2 * (int64_t)E * Ie : 0,
-                                   grouped ? (int64_t)E * H : 0};
+  // 32-row tile boundary; the shared expert's pseudo-experts follow the
+  // routed ones
+  const int Ie = c->expert_inter;
+  const bool grouped = moe_grouped_packed(c);
+  const int64_t ex = (int64_t)c->n_experts + moe_shared_parts(c);
+  const int64_t rows[PACK_MATS] = {qkvr, H, 2 * (int64_t)I, I > 0 ? H : 0, grouped ? 2 * ex * Ie : 0,
+                                   grouped ? ex * H : 0};
   const int K[PACK_MATS] = {H, qd, H, I, H, Ie};
   for (int i = 0; i < PACK_MATS; ++i) {
     const bool ok = rows[i] > 0 && K[i] > 0 && pack_w32_fits(rows[i], K[i]);
@@ -243,17 +266,18 @@ Layout make_layout(const decoder_config_t *c) {
   L.f32_act = take((size_t)H * 4);
   L.f32_hexp = take((size_t)std::max(c->top_k, 1) * std::max(c->expert_inter, 1) * 4);
   if (c->n_experts > 0) {
-    const int E = c->n_experts, k = c->top_k, P = L.R * k;
+    const int E = c->n_experts, k = c->top_k, P = L.R * k, S = moe_shared_parts(c);
+    const size_t PS = (size_t)L.R * (k + S);  // pairs with the shared pseudo-experts'
     L.rlogits = take((size_t)L.R * E * 4);
     L.rids = take((size_t)P * 4);
     L.rids_rec = take((size_t)c->n_layers * P * 4);
     L.rwts = take((size_t)P * 4);
     L.rgate = take((size_t)L.R * 4);
-    L.groups = take((size_t)(1 + 3 * E) * 4);
-    L.pair_row = take((size_t)P * 4);
+    L.groups = take((size_t)(1 + 3 * (E + S)) * 4);
+    L.pair_row = take(PS * 4);
     L.pair_of = take((size_t)P * 4);
-    L.hexp = take((size_t)P * c->expert_inter * 4);
-    L.yexp = take((size_t)P * H * 4);
+    L.hexp = take(PS * c->expert_inter * 4);
+    L.yexp = take(PS * H * 4);
     L.hsh = take((size_t)L.R * std::max(c->shared_inter, 1) * 4);
     L.ysh = take((size_t)L.R * H * 4);
   }
@@ -1006,12 +1030,19 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   mr.wts = D->rwts;
   mr.gate = D->rgate;
   mr.ids_record = D->rids_rec + (size_t)l * rows * k;
+  // a prefill chunk: the grouped form of the chunk kernel on the packed
+  // expert weights (32-row tiles of the groups' pairs), with the shared
+  // expert as S pseudo-experts when it divides into experts
+  const bool packed = rows > CHUNK_MIN_ROWS && D->packed[l].w[4] && D->packed[l].w[5];
+  const int GS = E + moe_shared_parts(&c);  // group table slots
+  const int S = packed ? moe_shared_parts(&c) : 0;
   mr.n_groups = D->groups;
   mr.group_expert = D->groups + 1;
-  mr.group_start = D->groups + 1 + E;
-  mr.group_count = D->groups + 1 + 2 * E;
+  mr.group_start = D->groups + 1 + GS;
+  mr.group_count = D->groups + 1 + 2 * GS;
   mr.pair_row = D->pair_row;
   mr.pair_of = D->pair_of;
+  mr.extra_groups = S;
   {
     NodeTimer t(D, DEC_NODE_ROUTER, E * (double)H * 2 + rows * (double)H * 4 + rows * (double)E * 4,
                 rows * (double)E * H * 2 + rows * (double)E * 8);
@@ -1020,7 +1051,7 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   if (e != hipSuccess) return hip_fail(D, e, "moe_route");
   const int slots = std::min(E, rows * k);
   const int grp_rows = std::min(rows, 32);
-  double exp_bytes = (double)slots * 3.0 * Ie * H;
+  const double exp_bytes = (double)(slots + S) * 3.0 * Ie * H, kp = k + S;
   GemmArgs g = dense_args(D->act, H, W.w_exp_gate_up, rows * k, Ie, H);
   g.a_lo = D->act_lo;
   g.a_rows = D->pair_row;
@@ -1034,16 +1065,13 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   g.group_count = mr.group_count;
   g.ksplit = 1;
   if (rows <= 16) g = qcodes(D, g, l, 4);
-  // a prefill chunk: the grouped form of the chunk kernel on the packed
-  // expert weights (32-row blocks of a group's pairs)
-  const bool packed = rows > CHUNK_MIN_ROWS && !g.Wq && D->packed[l].w[4] && D->packed[l].w[5];
   const double exp_wb = g.Wq ? 1.0 : 2.0;  // weight bytes per expert weight streamed
   {
-    NodeTimer t(D, DEC_NODE_EXPERTS, exp_bytes * exp_wb * 2.0 / 3.0 + rows * (double)H * 2 + rows * (double)k * Ie * 2,
-                2.0 * rows * k * 2.0 * Ie * H);
+    NodeTimer t(D, DEC_NODE_EXPERTS, exp_bytes * exp_wb * 2.0 / 3.0 + rows * (double)H * 2 + rows * kp * Ie * 2,
+                2.0 * rows * kp * 2.0 * Ie * H);
     if (packed) {
       g.Wp = D->packed[l].w[4];
-      e = launch_gemm_chunk_grouped(g, EPI_SWIGLU, rows * k, slots, st);
+      e = launch_gemm_chunk_grouped(g, EPI_SWIGLU, rows * (k + S), slots + S, st);
     } else {
       e = launch_gemm(g, EPI_SWIGLU, grp_rows, slots, st);
     }
@@ -1063,17 +1091,17 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   g.C = D->yexp;
   g.ldc = H;
   {
-    NodeTimer t(D, DEC_NODE_EXPERTS, exp_bytes * exp_wb / 3.0 + rows * (double)k * Ie * 2 + rows * (double)k * H * 4,
-                2.0 * rows * k * (double)Ie * H);
+    NodeTimer t(D, DEC_NODE_EXPERTS, exp_bytes * exp_wb / 3.0 + rows * kp * Ie * 2 + rows * kp * H * 4,
+                2.0 * rows * kp * (double)Ie * H);
     if (packed) {
       g.Wp = D->packed[l].w[5];
-      e = launch_gemm_chunk_grouped(g, EPI_STORE, rows * k, slots, st);
+      e = launch_gemm_chunk_grouped(g, EPI_STORE, rows * (k + S), slots + S, st);
     } else {
       e = launch_gemm(g, EPI_STORE, grp_rows, slots, st);
     }
   }
   if (e != hipSuccess) return hip_fail(D, e, "moe down");
-  if (Is > 0) {
+  if (Is > 0 && S == 0) {
     GemmArgs sg = dense_args(D->act, H, W.w_sh_gate_up, rows, Is, H);
     sg.a_lo = D->act_lo;
     sg.Hout = D->hsh;
@@ -1092,8 +1120,12 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   }
   NodeTimer tcomb(D, DEC_NODE_EXPERTS, rows * (double)H * (8.0 + 4.0 * k + 4.0), rows * (double)H * 2 * (k + 1));
   D->act_norm = nullptr;
-  e = launch_moe_combine(D->x, D->yexp, Is > 0 ? D->ysh : nullptr, D->rwts, D->rgate, D->pair_of, rows,
-                         k, H, st);
+  if (S > 0)  // the shared expert's S partial outputs follow the routed pairs
+    e = launch_moe_combine(D->x, D->yexp, D->yexp + (size_t)rows * k * H, D->rwts, D->rgate, D->pair_of, rows, k,
+                           H, st, S, (int64_t)rows * H);
+  else
+    e = launch_moe_combine(D->x, D->yexp, Is > 0 ? D->ysh : nullptr, D->rwts, D->rgate, D->pair_of, rows, k, H,
+                           st);
   if (e != hipSuccess) return hip_fail(D, e, "moe combine");
   return DEC_OK;
 }
@@ -1247,7 +1279,7 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
   D->act_lo = (int64_t)L.R * cfg->hidden;
   D->attn_lo = D->q_lo = (int64_t)L.R * cfg->n_heads * cfg->head_dim;
   D->h_lo = (int64_t)L.R * std::max(cfg->ffn_inter, 1);
-  D->hexp_lo = (int64_t)L.R * std::max(cfg->top_k, 1) * std::max(cfg->expert_inter, 1);
+  D->hexp_lo = (int64_t)L.R * (std::max(cfg->top_k, 1) + moe_shared_parts(cfg)) * std::max(cfg->expert_inter, 1);
   D->hsh_lo = (int64_t)L.R * std::max(cfg->shared_inter, 1);
   D->f32_attn = carve<float>(D, L.f32_attn);
   D->f32_h = carve<float>(D, L.f32_h);
@@ -1330,10 +1362,33 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
           (const uint16_t *)(cfg->n_experts > 0 ? lw.w_sh_gate_up : lw.w_gate_up),
           (const uint16_t *)(cfg->n_experts > 0 ? lw.w_sh_down : lw.w_down),
           (const uint16_t *)lw.w_exp_gate_up, (const uint16_t *)lw.w_exp_down};
+      const int E = cfg->n_experts, S = moe_shared_parts(cfg), Ie = cfg->expert_inter, Is = cfg->shared_inter;
+      const int H = cfg->hidden;
       for (int i = 0; i < PACK_MATS; ++i) {
         D->packed[l].w[i] = nullptr;
         if (!ps.rows[i] || !src[i]) continue;
-        if (launch_pack_w32(src[i], ps.rows[i], ps.K[i], pk, (hipStream_t)stream) != hipSuccess) {
+        hipError_t pe;
+        if (i < 4) {
+          pe = launch_pack_w32(src[i], ps.rows[i], ps.K[i], pk, (hipStream_t)stream);
+        } else if (i == 4) {
+          // routed experts, then shared pseudo-expert j: its gate rows, its up rows
+          pe = launch_pack_w32(src[i], 2 * (int64_t)E * Ie, H, pk, (hipStream_t)stream);
+          for (int j = 0; j < S && pe == hipSuccess; ++j) {
+            uint16_t *dst = pk + (size_t)(E + j) * 2 * Ie * H;
+            const uint16_t *gsh = (const uint16_t *)lw.w_sh_gate_up;
+            pe = launch_pack_w32(gsh + (size_t)j * Ie * H, Ie, H, dst, (hipStream_t)stream);
+            if (pe == hipSuccess)
+              pe = launch_pack_w32(gsh + ((size_t)Is + (size_t)j * Ie) * H, Ie, H, dst + (size_t)Ie * H,
+                                   (hipStream_t)stream);
+          }
+        } else {
+          // routed experts, then shared pseudo-expert j: columns j Ie .. (j + 1) Ie of the shared down
+          pe = launch_pack_w32(src[i], (int64_t)E * H, Ie, pk, (hipStream_t)stream);
+          for (int j = 0; j < S && pe == hipSuccess; ++j)
+            pe = launch_pack_w32_ld((const uint16_t *)lw.w_sh_down + (size_t)j * Ie, Is, H, Ie,
+                                    pk + (size_t)(E + j) * H * Ie, (hipStream_t)stream);
+        }
+        if (pe != hipSuccess) {
           D->err = "weight packing failed";
           delete D;
           return DEC_E_HIP;

@@ -389,9 +389,11 @@ hipError_t launch_epi(const GemmArgs &g, int ntiles16, int blocks, int mblocks, 
   return launch_mt<2, EPI>(g, ntiles16, blocks, mblocks, st);
 }
 
-// P[((nt * K / 16 + kt) * 64 + l) * 8 + e] = W[32 nt + l % 32][16 kt + 8 (l / 32) + e]:
-// one thread per 16-byte piece; the stores are coalesced.
-__global__ __launch_bounds__(256) void pack_w32_kernel(const uint16_t *W, int64_t pieces, int K, uint16_t *P) {
+// P[((nt * K / 16 + kt) * 64 + l) * 8 + e] = W[32 nt + l % 32][16 kt + 8 (l / 32) + e]
+// (W rows ld elements apart): one thread per 16-byte piece; the stores are
+// coalesced.
+__global__ __launch_bounds__(256) void pack_w32_kernel(const uint16_t *W, int64_t ld, int64_t pieces, int K,
+                                                       uint16_t *P) {
   const int kt16 = K / 16;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < pieces; i += (int64_t)gridDim.x * 256) {
     const int l = (int)(i & 63);
@@ -399,7 +401,7 @@ __global__ __launch_bounds__(256) void pack_w32_kernel(const uint16_t *W, int64_
     const int64_t nt = tile / kt16;
     const int kt = (int)(tile - nt * kt16);
     const int64_t row = 32 * nt + (l & 31);
-    const u32x4 v = load16(W + row * K + 16 * kt + 8 * (l >> 5));
+    const u32x4 v = load16(W + row * ld + 16 * kt + 8 * (l >> 5));
     *reinterpret_cast<u32x4 *>(P + i * 8) = v;
   }
 }
@@ -408,12 +410,16 @@ __global__ __launch_bounds__(256) void pack_w32_kernel(const uint16_t *W, int64_
 
 bool pack_w32_fits(int64_t rows, int K) { return rows > 0 && rows % 32 == 0 && K > 0 && K % 16 == 0; }
 
-hipError_t launch_pack_w32(const uint16_t *W, int64_t rows, int K, uint16_t *P, hipStream_t st) {
-  if (!pack_w32_fits(rows, K)) return hipErrorInvalidValue;
+hipError_t launch_pack_w32_ld(const uint16_t *W, int64_t ld, int64_t rows, int K, uint16_t *P, hipStream_t st) {
+  if (!pack_w32_fits(rows, K) || ld < K || ld % 8) return hipErrorInvalidValue;
   const int64_t pieces = rows * K / 8;
   const int blocks = (int)std::min<int64_t>((pieces + 255) / 256, 65536);
-  hipLaunchKernelGGL(pack_w32_kernel, dim3(blocks), dim3(256), 0, st, W, pieces, K, P);
+  hipLaunchKernelGGL(pack_w32_kernel, dim3(blocks), dim3(256), 0, st, W, ld, pieces, K, P);
   return hipGetLastError();
+}
+
+hipError_t launch_pack_w32(const uint16_t *W, int64_t rows, int K, uint16_t *P, hipStream_t st) {
+  return launch_pack_w32_ld(W, K, rows, K, P, st);
 }
 
 int gemm_chunk_tiles(const GemmArgs &g, int epi) {

@@ -30,6 +30,9 @@ bool gemm_chunk_fits(const GemmArgs &g, int epi);
 // = W[32 nt + l % 32][16 kt + 8 (l / 32) + e] (rows % 32 == 0, K % 16 == 0).
 bool pack_w32_fits(int64_t rows, int K);
 hipError_t launch_pack_w32(const uint16_t *W, int64_t rows, int K, uint16_t *P, hipStream_t st);
+// the same for a [rows][K] slice of a matrix whose rows are ld elements apart
+// (ld % 8 == 0, W 16-byte aligned)
+hipError_t launch_pack_w32_ld(const uint16_t *W, int64_t ld, int64_t rows, int K, uint16_t *P, hipStream_t st);
 int gemm_chunk_tiles(const GemmArgs &g, int epi);
 int gemm_chunk_mblocks(int rows);
 hipError_t launch_gemm_chunk(const GemmArgs &g, int epi, hipStream_t st);
@@ -286,13 +289,17 @@ struct MoeRouteArgs {
   int32_t *n_groups, *group_expert, *group_start, *group_count;
   int32_t *pair_row;       // [rows*k]: token row of sorted pair p
   int32_t *pair_of;        // [rows*k]: sorted pair index of (row, slot)
+  // shared expert as extra_groups pseudo-experts (ids E .. E + extra_groups
+  // - 1, every row): group table entries after the routed groups, pairs
+  // rows*k + j*rows + r (pair_row then holds rows*(k + extra_groups))
+  int32_t extra_groups;
 };
 hipError_t launch_moe_route(const MoeRouteArgs &a, bool group, hipStream_t st);
 // the largest hidden size the fused router (w_router set) keeps in LDS
 constexpr int MOE_ROUTER_MAX_H = 8192;
 
-// x[r][:] += sum_j wts[r][j] * y[pair_of[r*k+j]][:] + gate[r] * ysh[r][:]
-// (pair_of null: y is indexed by r*k+j directly)
+// x[r][:] += sum_j wts[r][j] * y[pair_of[r*k+j]][:] + gate[r] * sum_i ysh[i*sh_stride + r*H][:]
+// over sh_parts shared-expert parts (pair_of null: y is indexed by r*k+j directly)
 hipError_t launch_moe_combine(float *x, const float *y, const float *ysh, const float *wts,
                               const float *gate, const int32_t *pair_of, int rows, int k, int H,
-                              hipStream_t st);
+                              hipStream_t st, int sh_parts = 1, int64_t sh_stride = 0);

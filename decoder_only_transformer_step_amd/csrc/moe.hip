@@ -7,8 +7,11 @@
 //           the shared-expert scale sigmoid(w_sg . b) (1 without a gate).
 //  group:   pairs (row, slot) sorted by expert, then by row: every chosen
 //           expert becomes one group whose weights are streamed once for
-//           all rows that chose it (engine.zig Engine.prefill batching).
-//  combine: x += sum_j w_j y_pair(j) + gate * y_shared, slots in router order.
+//           all rows that chose it (engine.zig Engine.prefill batching);
+//           optionally the shared expert's slices as further groups that
+//           every row joins.
+//  combine: x += sum_j w_j y_pair(j) + gate * y_shared, slots in router
+//           order (y_shared summed over its slices first).
 #include "common.h"
 #include "launch.h"
 
@@ -107,8 +110,15 @@ __global__ __launch_bounds__(256) void moe_group_kernel(MoeRouteArgs a) {
       }
       s += cnt[e];
     }
-    *a.n_groups = ng;
+    // the shared expert's pseudo-experts: every row, after the routed pairs
+    for (int j = 0; j < a.extra_groups; ++j) {
+      a.group_expert[ng + j] = E + j;
+      a.group_start[ng + j] = P + j * a.rows;
+      a.group_count[ng + j] = a.rows;
+    }
+    *a.n_groups = ng + a.extra_groups;
   }
+  for (int q = threadIdx.x; q < a.extra_groups * a.rows; q += blockDim.x) a.pair_row[P + q] = q % a.rows;
   __syncthreads();
   // a pair's slot: its expert's start plus the number of earlier pairs of
   // that expert.  Wave w scans experts w, w + 4, ...: per 64-pair chunk a
@@ -259,7 +269,8 @@ __global__ __launch_bounds__(RR_THREADS) void moe_router_route_kernel(MoeRouteAr
 // x[r][c] += sum_j w_j y[pair(r, j)][c] + gate_r ysh[r][c]; grid (columns / 256, rows)
 __global__ __launch_bounds__(256) void moe_combine_kernel(float *x, const float *y, const float *ysh,
                                                          const float *wts, const float *gate,
-                                                         const int32_t *pair_of, int k, int H) {
+                                                         const int32_t *pair_of, int k, int H, int sh_parts,
+                                                         int64_t sh_stride) {
   const int r = blockIdx.y, c = blockIdx.x * blockDim.x + threadIdx.x;
   float w[8];
   int64_t pr[8];
@@ -275,14 +286,20 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(float *x, const float 
 #pragma unroll
   for (int j = 0; j < 8; ++j)
     if (j < k) acc += w[j] * y[pr[j] * H + c];
-  if (ysh) acc += gs * ysh[(int64_t)r * H + c];
+  if (ysh) {
+    float s = 0.f;
+    for (int i = 0; i < sh_parts; ++i) s += ysh[i * sh_stride + (int64_t)r * H + c];
+    acc += gs * s;
+  }
   x[(int64_t)r * H + c] += acc;
 }
 
 }  // namespace
 
 hipError_t launch_moe_route(const MoeRouteArgs &a, bool group, hipStream_t st) {
-  if (a.E > 256 || a.k > 8 || (group && a.rows * a.k > GROUP_MAX_PAIRS)) return hipErrorInvalidValue;
+  if (a.E > 256 || a.k > 8 || (group && a.rows * a.k > GROUP_MAX_PAIRS) || a.extra_groups < 0 ||
+      a.extra_groups > 8)
+    return hipErrorInvalidValue;
   if (a.w_router) {
     if (!a.act_f32 || !a.gamma || a.H % 8 || a.H > MOE_ROUTER_MAX_H) return hipErrorInvalidValue;
     hipLaunchKernelGGL(moe_router_route_kernel, dim3(a.rows), dim3(RR_THREADS), (size_t)(a.H + a.E) * 4, st, a);
@@ -297,9 +314,9 @@ hipError_t launch_moe_route(const MoeRouteArgs &a, bool group, hipStream_t st) {
 
 hipError_t launch_moe_combine(float *x, const float *y, const float *ysh, const float *wts,
                               const float *gate, const int32_t *pair_of, int rows, int k, int H,
-                              hipStream_t st) {
-  if (k < 1 || k > 8) return hipErrorInvalidValue;
+                              hipStream_t st, int sh_parts, int64_t sh_stride) {
+  if (k < 1 || k > 8 || sh_parts < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(moe_combine_kernel, dim3((H + 255) / 256, rows), dim3(256), 0, st, x, y, ysh, wts, gate,
-                     pair_of, k, H);
+                     pair_of, k, H, sh_parts, sh_stride);
   return hipGetLastError();
 }

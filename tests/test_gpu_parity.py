@@ -323,15 +323,20 @@ def test_8b_shape_batched_decode_of_nine_sequences(wq):
 
 # -------------------------------------------------------------------- MoE --
 
-def small_moe():
+def small_moe(shared_inter=128):
     return Shape("moe-small", hidden=256, n_layers=2, n_heads=4, n_kv_heads=4, head_dim=64, vocab=512,
-                 n_experts=8, top_k=2, expert_inter=96, shared_inter=128, shared_gate=True,
+                 n_experts=8, top_k=2, expert_inter=96, shared_inter=shared_inter, shared_gate=True,
                  qkv_bias=True, rope_base=1e4, max_seq=64, max_chunk=32)
 
 
-def test_moe_small_parity_and_routes():
+@pytest.mark.parametrize("shared_inter", [128, 192])
+def test_moe_small_parity_and_routes(shared_inter):
+    """Prefill of 24 rows (the grouped expert projection) and 4 decode steps.
+    A shared expert of 192 = 2 x 96 rows runs inside the grouped projection
+    as two pseudo-experts that every row takes; one of 128 runs as its own
+    projections."""
     from tests.moe_routes import check_routes_exact, forced
-    shape = small_moe()
+    shape = small_moe(shared_inter)
     W = host_weights(shape)
     ids = [int(t) for t in prompt(shape, 24)]
     m = oracle.Model(shape, W)
