@@ -160,63 +160,71 @@ __device__ __forceinline__ float merge_splits(const AttnArgs &a, int gi, int cc,
   return o * r / L;
 }
 
-// The merge inside attn_kernel: up to two (column, dim) values per thread
-// in one pass, so their loads form a single round trip (chunks of 16 splits
-// bound the registers).  v1 = false: the second value is absent.
-constexpr int MERGE2_CHUNK = 16;
-
-template <int D>
-__device__ __forceinline__ void merge_splits2(const AttnArgs &a, int gi, int c0, int j0, int c1, int j1, bool v1,
-                                              int nact, int h0, int h1, float &out0, float &out1) {
-  const int cb = v1 ? c1 : c0, jb = v1 ? j1 : j0;
-  const float *ml0 = a.part_ml + ((int64_t)gi * a.n_splits * 16 + c0) * 2;
-  const float *ml1 = a.part_ml + ((int64_t)gi * a.n_splits * 16 + cb) * 2;
-  const float *po0 = a.part_o + ((int64_t)gi * a.n_splits * 16 + c0) * D + j0;
-  const float *po1 = a.part_o + ((int64_t)gi * a.n_splits * 16 + cb) * D + jb;
-  float M0 = NEG_SENTINEL, L0 = 0.f, o0 = 0.f, M1 = NEG_SENTINEL, L1 = 0.f, o1 = 0.f;
-  for (int s0 = 0; s0 < nact; s0 += MERGE2_CHUNK) {
-    float m0[MERGE2_CHUNK], l0[MERGE2_CHUNK], x0[MERGE2_CHUNK], m1[MERGE2_CHUNK], l1[MERGE2_CHUNK], x1[MERGE2_CHUNK];
+// The merge inside attn_kernel, run by the group's last block (256
+// threads, up to two (column, dim) values each, at most ATTN_FUSED_MAX_SPLITS
+// splits and 256 (split, column) pairs): one round of relaxed device-scope
+// loads brings every split's O values of the thread into registers and the
+// (m, l) of every (split, column) into LDS; the columns' maxima, rescale
+// factors and denominators are then formed in LDS, and each value is summed
+// in split order.  sc and sl alias LDS the block no longer needs.  FM:
+// the loads per value (nact <= FM; the dispatch below picks 8, 16 or 32, so
+// a merge of a few splits issues a few loads).
+template <int D, int PM, int FM>
+__device__ __forceinline__ void merge_fused(const AttnArgs &a, int gi, int rg, int g, int nact, int ncols,
+                                            float (*sc)[16], float (*sl)[16], float *den) {
+  const int t = threadIdx.x;
+  const int p0 = t, p1 = t + 256;
+  const int c0 = p0 / D, j0 = p0 - c0 * D, c1 = p1 / D, j1 = p1 - c1 * D;
+  const bool v0 = c0 < ncols, v1 = c1 < ncols;
+  const int64_t base = (int64_t)gi * a.n_splits * 16;
+  // (a value past the group's columns reads column 0, dim 0, and is dropped)
+  const float *po0 = a.part_o + (base + (v0 ? c0 : 0)) * D + (v0 ? j0 : 0);
+  const float *po1 = a.part_o + (base + (v1 ? c1 : 0)) * D + (v1 ? j1 : 0);
+  float x0[FM], x1[FM];
 #pragma unroll
-    for (int u = 0; u < MERGE2_CHUNK; ++u) {
-      const int64_t s = min(s0 + u, nact - 1);
-      m0[u] = part_load<true>(ml0 + s * 32);
-      l0[u] = part_load<true>(ml0 + s * 32 + 1);
-      x0[u] = part_load<true>(po0 + s * 16 * D);
-      m1[u] = part_load<true>(ml1 + s * 32);
-      l1[u] = part_load<true>(ml1 + s * 32 + 1);
-      x1[u] = part_load<true>(po1 + s * 16 * D);
-    }
-#pragma unroll
-    for (int u = 0; u < MERGE2_CHUNK; ++u) {
-      m0[u] = s0 + u < nact ? m0[u] : -INFINITY;
-      m1[u] = s0 + u < nact ? m1[u] : -INFINITY;
-    }
-    float cm0 = M0, cm1 = M1;
-#pragma unroll
-    for (int u = 0; u < MERGE2_CHUNK; ++u) {
-      cm0 = fmaxf(cm0, m0[u]);
-      cm1 = fmaxf(cm1, m1[u]);
-    }
-    const float r0 = exp2f(M0 - cm0), r1 = exp2f(M1 - cm1);
-    L0 *= r0;
-    o0 *= r0;
-    L1 *= r1;
-    o1 *= r1;
-#pragma unroll
-    for (int u = 0; u < MERGE2_CHUNK; ++u) {
-      const float sc0 = exp2f(m0[u] - cm0), sc1 = exp2f(m1[u] - cm1);
-      L0 += sc0 * l0[u];
-      o0 += sc0 * x0[u];
-      L1 += sc1 * l1[u];
-      o1 += sc1 * x1[u];
-    }
-    M0 = cm0;
-    M1 = cm1;
+  for (int u = 0; u < FM; ++u) {
+    const int64_t su = min(u, nact - 1);
+    x0[u] = part_load<true>(po0 + su * 16 * D);
+    x1[u] = part_load<true>(po1 + su * 16 * D);
   }
-  const float f0 = attn_sink_fold(a, h0, M0, L0);
-  out0 = o0 * f0 / L0;
-  const float f1 = attn_sink_fold(a, v1 ? h1 : h0, M1, L1);
-  out1 = o1 * f1 / L1;
+  const bool ml_own = t < nact * ncols;
+  const int ms = ml_own ? t / ncols : 0, mc = ml_own ? t - ms * ncols : 0;
+  const float *ml = a.part_ml + (base + ms * 16 + mc) * 2;
+  const float mv = part_load<true>(ml), lv = part_load<true>(ml + 1);
+  if (ml_own) {
+    sc[ms][mc] = mv;
+    sl[ms][mc] = lv;
+  }
+  __syncthreads();
+  if (t < ncols) {
+    float M = NEG_SENTINEL;
+    for (int s = 0; s < nact; ++s) M = fmaxf(M, sc[s][t]);
+    float L = 0.f;
+    for (int s = 0; s < nact; ++s) {
+      const float f = exp2f(sc[s][t] - M);
+      sc[s][t] = f;
+      L += f * sl[s][t];
+    }
+    const float r = attn_sink_fold(a, column<PM>(a, rg, g, t).head, M, L);
+    den[t] = r / L;
+  }
+  __syncthreads();
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int u = 0; u < FM; ++u) {
+    if (u < nact) {
+      o0 += sc[u][v0 ? c0 : 0] * x0[u];
+      o1 += sc[u][v1 ? c1 : 0] * x1[u];
+    }
+  }
+  if (v0) {
+    const Col col = column<PM>(a, rg, g, c0);
+    if (col.valid) store_out(a, ((int64_t)col.row * a.Hq + col.head) * D + j0, o0 * den[c0]);
+  }
+  if (v1) {
+    const Col col = column<PM>(a, rg, g, c1);
+    if (col.valid) store_out(a, ((int64_t)col.row * a.Hq + col.head) * D + j1, o1 * den[c1]);
+  }
 }
 
 template <int D, int PM, bool PG>
@@ -408,17 +416,16 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   __syncthreads();
   if (!last_s) return;
   if (threadIdx.x == 0) __hip_atomic_store(a.counters + gi, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // (the launcher sets counters only when a group has at most 512 values)
+  // (the launcher sets counters only when a group has at most 512 values,
+  // ATTN_FUSED_MAX_SPLITS splits and 256 (split, column) pairs); the
+  // block's own merge is done with lo, which now holds the scale table
+  float(*sc)[16] = reinterpret_cast<float(*)[16]>(&lo[0][0][0]);
+  float(*sl)[16] = sc + ATTN_FUSED_MAX_SPLITS;
   const int ncols = min(16, a.rows_per_group * a.G);
-  const int p0 = threadIdx.x, p1 = threadIdx.x + 256;
-  if (p0 >= ncols * D) return;
-  const int c0 = p0 / D, j0 = p0 - c0 * D, c1 = p1 / D, j1 = p1 - c1 * D;
-  const bool has1 = p1 < ncols * D;
-  const Col col0 = column<PM>(a, rg, g, c0), col1 = column<PM>(a, rg, g, has1 ? c1 : c0);
-  float r0, r1;
-  merge_splits2<D>(a, gi, c0, j0, c1, j1, has1, nact, col0.head, col1.head, r0, r1);
-  if (col0.valid) store_out(a, ((int64_t)col0.row * a.Hq + col0.head) * D + j0, r0);
-  if (has1 && col1.valid) store_out(a, ((int64_t)col1.row * a.Hq + col1.head) * D + j1, r1);
+  static_assert(ATTN_FUSED_MAX_SPLITS == 32, "merge_fused dispatch");
+  if (nact <= 8) merge_fused<D, PM, 8>(a, gi, rg, g, nact, ncols, sc, sl, &lm[0][0]);
+  else if (nact <= 16) merge_fused<D, PM, 16>(a, gi, rg, g, nact, ncols, sc, sl, &lm[0][0]);
+  else merge_fused<D, PM, 32>(a, gi, rg, g, nact, ncols, sc, sl, &lm[0][0]);
 }
 
 // One block per (group, valid column), one thread per dim: combine the

@@ -26,7 +26,6 @@ namespace {
 constexpr int STAGE_RING = 64;     // pinned staging slots (one per call in flight)
 constexpr int ATTN_TARGET_BLOCKS = 1024;
 constexpr int ATTN_MAX_TASKS = 8192;
-constexpr int ATTN_FUSED_MAX_SPLITS = 8;  // attention splits per group merged inside the attention kernel
 constexpr int GEMM_MAX_SPLIT = 8;
 constexpr int CHUNK_MIN_ROWS = 16;   // more rows than this take the chunk projection kernel
 // Batched decode: from this many rows, projections whose weights are at least
@@ -711,12 +710,11 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
   a.kc = kc;
   a.n_splits = ns;
   // the group's last block merges the splits (counters zero again after
-  // every launch) when a group holds at most two values per thread and at
-  // most ATTN_FUSED_MAX_SPLITS splits; otherwise the merge is its own
-  // launch (8B-class decode at 2048+ keys has 17-19 splits per group: the
-  // merge launch measured 14.3 us per layer with the attention, the fused
-  // merge 15.1 us; the MoE decode with 5 splits gains 593.5 -> 606.7 tok/s)
-  if (std::min(16, rows_per_group * a.G) * c.head_dim <= 512 && ns <= ATTN_FUSED_MAX_SPLITS) a.counters = D->attn_cnt;
+  // every launch) when a group holds at most two values per thread, at most
+  // ATTN_FUSED_MAX_SPLITS splits and at most 256 (split, column) pairs;
+  // otherwise the merge is its own launch
+  const int ncols = std::min(16, rows_per_group * a.G);
+  if (ncols * c.head_dim <= 512 && ns <= ATTN_FUSED_MAX_SPLITS && ns * ncols <= 256) a.counters = D->attn_cnt;
   // the chunk kernel shares each key tile among up to 128 query columns; a
   // chunk that fits one column group per kv head (a verify pass of a few
   // drafted rows) takes the decode kernel, whose waves each own a tile

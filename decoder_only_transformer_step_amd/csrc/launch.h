@@ -174,6 +174,8 @@ struct AttnArgs {
 };
 
 constexpr float ATTN_LOG2E = 1.4426950408889634f;
+// splits per group that attn_kernel merges itself (its last block to finish)
+constexpr int ATTN_FUSED_MAX_SPLITS = 32;
 
 // Score of a raw q.k product in log2 units (scaled, soft-capped when set).
 __device__ __forceinline__ float attn_logit2(const AttnArgs &a, float s) {
