@@ -409,11 +409,12 @@ def summarize_mfma(pmc_csv, out, commands):
         groups[(d["name"], d["grid"], d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0))].append(d)
     lines = ["# MFMA work of the prefill chunk projections (rocprofv3 --pmc)", "",
              "Command (from the repository root):", "", "```"] + commands + ["```", "",
-             "`gemm_chunk_kernel<MT, EPI, SPLIT>`: EPI 0 = plain product (the bench's gate_up GEMM "
-             "capability probe), 1 = residual add (o_proj, down), 2 = SwiGLU (gate_up), 3 = QKV. "
-             "One row per GEMM shape (kernel, grid size, MFMA work per dispatch). The model's "
-             "activations enter the MFMAs as two bf16 planes, so their executed flops are twice the "
-             "algorithmic 2 M N K.", "",
+             "`gemm_chunk_kernel<MT, EPI, SPLIT, GR>` (GR: the grouped MoE form) and "
+             "`gemm_wide_kernel<EPI, SPLIT>` (chunks of 256+ rows): EPI 0 = plain product (the bench's "
+             "gate_up GEMM capability probe), 1 = residual add (o_proj, down), 2 = SwiGLU (gate_up), "
+             "3 = QKV. One row per GEMM shape (kernel, grid size, MFMA work per dispatch). The model's "
+             "activations enter the MFMAs as two bf16 planes (SPLIT), so their executed flops are twice "
+             "the algorithmic 2 M N K.", "",
              f"peak: {MFMA_BF16_PEAK_TFS:.0f} TFLOP/s dense bf16", "",
              "| kernel | grid | dispatches | avg us (counter run) | MFMA flops / dispatch | executed TFLOP/s | "
              "% of peak | MFMA-busy cycles / dispatch |",
