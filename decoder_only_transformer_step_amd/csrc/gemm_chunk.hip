@@ -71,6 +71,14 @@ struct AStage {
 
 __device__ __forceinline__ int a_swz(int r32, int g, int s) { return (r32 ^ (2 * (2 * s + g))) + 32 * g; }
 
+// Staging piece -> (row, 16-byte chunk c8 of the row's 128 bytes): each 8
+// consecutive pieces are 4 chunks of two adjacent rows (bits 0-1: c8 % 4,
+// bit 2: row % 2, bit 3: c8 / 4), so the 8 lanes an LDS cycle serves store
+// to 8 different bank groups (one row's 8 chunks would hit only 4 of them
+// under the swizzle).  A wave's global loads still cover 8 whole rows.
+__device__ __forceinline__ int piece_row(int rem) { return ((rem >> 4) << 1) | ((rem >> 2) & 1); }
+__device__ __forceinline__ int piece_c8(int rem) { return (rem & 3) | (((rem >> 3) & 1) << 2); }
+
 // Global -> registers, coalesced: piece e = (plane, row r, 16-byte chunk c8
 // of the step's 128 bytes); rows past `rows` and k past kend read zeros.
 template <int MT, bool SPLIT>
@@ -81,7 +89,7 @@ __device__ __forceinline__ void a_load(const uint16_t *abase, const GemmArgs &g,
   for (int i = 0; i < AStage<MT, SPLIT>::PER_THREAD; ++i) {
     const int e = threadIdx.x + i * CK_WAVES * WAVE;
     const int plane = e / PER_PLANE, rem = e - plane * PER_PLANE;
-    const int r = rem >> 3, k = k0 + (rem & 7) * 8;
+    const int r = piece_row(rem), k = k0 + piece_c8(rem) * 8;
     const bool ok = (PIECES % (CK_WAVES * WAVE) == 0 || e < PIECES) && r < rows && k < kend;
     ar[i] = load16(ok ? static_cast<const void *>(abase + plane * g.a_lo + (int64_t)r * g.lda + k)
                       : static_cast<const void *>(ck_zero + (threadIdx.x & 63)));
@@ -98,7 +106,7 @@ __device__ __forceinline__ void a_store(u32x4 *dst, const u32x4 (&ar)[AStage<MT,
   for (int i = 0; i < AStage<MT, SPLIT>::PER_THREAD; ++i) {
     const int e = threadIdx.x + i * CK_WAVES * WAVE;
     const int plane = e / PER_PLANE, rem = e - plane * PER_PLANE;
-    const int r = rem >> 3, c8 = rem & 7;
+    const int r = piece_row(rem), c8 = piece_c8(rem);
     const int t = r >> 5, s = c8 >> 1, gk = c8 & 1;
     if (PIECES % (CK_WAVES * WAVE) == 0 || e < PIECES)
       dst[((t * 4 + s) * PL + plane) * WAVE + a_swz(r & 31, gk, s)] = ar[i];
@@ -168,8 +176,8 @@ __device__ __forceinline__ ARows<MT, SPLIT> a_rows_of(const GemmArgs &g, int row
   for (int i = 0; i < AStage<MT, SPLIT>::PER_THREAD; ++i) {
     const int e = threadIdx.x + i * CK_WAVES * WAVE;
     const int plane = e / PER_PLANE, rem = e - plane * PER_PLANE;
-    const int r = rem >> 3;
-    ra.koff[i] = (rem & 7) * 8;
+    const int r = piece_row(rem);
+    ra.koff[i] = piece_c8(rem) * 8;
     const bool ok = (PIECES % (CK_WAVES * WAVE) == 0 || e < PIECES) && r < rows;
     const int64_t src = ok ? (g.a_rows ? g.a_rows[row0 + r] : row0 + r) : 0;
     ra.p[i] = ok ? g.A + plane * g.a_lo + src * g.lda + ra.koff[i] : nullptr;
