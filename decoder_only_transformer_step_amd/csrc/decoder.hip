@@ -247,7 +247,8 @@ Layout make_layout(const decoder_config_t *c) {
   L.gout = take((size_t)(c->max_seq + 1) * 4);
   L.part_o = take((size_t)ATTN_MAX_TASKS * 16 * d * 4);
   L.part_ml = take((size_t)ATTN_MAX_TASKS * 16 * 2 * 4);
-  L.attn_cnt = take((size_t)ATTN_MAX_TASKS * 4);  // one arrival counter per attention group
+  // one arrival counter per attention group, then the MoE router's
+  L.attn_cnt = take((size_t)(ATTN_MAX_TASKS + 1) * 4);
   int max_small_n = std::max(qkvr, H);
   if (c->n_experts > 0) max_small_n = std::max(max_small_n, 2 * c->shared_inter);
   L.gpart_elems = (size_t)GEMM_MAX_SPLIT * L.R * 2 * (size_t)max_small_n;
@@ -1041,6 +1042,7 @@ int run_layer(decoder *D, int l, int rows, int rows_per_group, int max_pos, cons
   mr.pair_row = D->pair_row;
   mr.pair_of = D->pair_of;
   mr.extra_groups = S;
+  mr.arrive = D->attn_cnt + ATTN_MAX_TASKS;  // the router's arrival counter
   {
     NodeTimer t(D, DEC_NODE_ROUTER, E * (double)H * 2 + rows * (double)H * 4 + rows * (double)E * 4,
                 rows * (double)E * H * 2 + rows * (double)E * 8);
@@ -1430,7 +1432,7 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
   if (hipMemsetAsync(D->kcache, 0, kvb, D->stream) != hipSuccess ||
       hipMemsetAsync(D->vcache, 0, kvb, D->stream) != hipSuccess ||
       hipMemsetAsync(D->next_token, 0, (size_t)cfg->max_batch * 4, D->stream) != hipSuccess ||
-      hipMemsetAsync(D->attn_cnt, 0, (size_t)ATTN_MAX_TASKS * 4, D->stream) != hipSuccess ||
+      hipMemsetAsync(D->attn_cnt, 0, (size_t)(ATTN_MAX_TASKS + 1) * 4, D->stream) != hipSuccess ||
       hipStreamSynchronize(D->stream) != hipSuccess)
     return cleanup(DEC_E_HIP);
   *out = D;

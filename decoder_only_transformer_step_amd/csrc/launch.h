@@ -295,6 +295,10 @@ struct MoeRouteArgs {
   // - 1, every row): group table entries after the routed groups, pairs
   // rows*k + j*rows + r (pair_row then holds rows*(k + extra_groups))
   int32_t extra_groups;
+  // with w_router and grouping: a zeroed arrival counter; the router launch
+  // then builds the group table itself (its last block), and leaves the
+  // counter zero again
+  int32_t *arrive;
 };
 hipError_t launch_moe_route(const MoeRouteArgs &a, bool group, hipStream_t st);
 // the largest hidden size the fused router (w_router set) keeps in LDS

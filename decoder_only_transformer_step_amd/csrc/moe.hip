@@ -85,30 +85,37 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(MoeRouteArgs a
   }
 }
 
-// One block: group table over experts in increasing order, pairs by row.
-// The ids are staged in LDS; counts by LDS atomics; a pair's slot in its
-// expert's group follows the number of earlier pairs with the same expert.
-__global__ __launch_bounds__(256) void moe_group_kernel(MoeRouteArgs a) {
-  __shared__ int ids_s[GROUP_MAX_PAIRS];
-  __shared__ int cnt[256];
-  __shared__ int start[256];
+// Group table over experts in increasing order, pairs by row, built by one
+// block (any size).  The ids are staged in LDS; counts by LDS atomics; a
+// pair's slot in its expert's group follows the number of earlier pairs with
+// the same expert.  AT: the ids were written by other blocks of the same
+// launch and are read with relaxed device-scope loads.
+struct GroupLds {
+  int ids[GROUP_MAX_PAIRS];
+  int cnt[256];
+  int start[256];
+};
+
+template <bool AT>
+__device__ __forceinline__ void group_pairs(const MoeRouteArgs &a, GroupLds &s) {
   const int E = a.E, P = a.rows * a.k;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
-  for (int p = threadIdx.x; p < P; p += blockDim.x) ids_s[p] = a.ids[p];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) s.cnt[e] = 0;
+  for (int p = threadIdx.x; p < P; p += blockDim.x)
+    s.ids[p] = AT ? __hip_atomic_load(a.ids + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : a.ids[p];
   __syncthreads();
-  for (int p = threadIdx.x; p < P; p += blockDim.x) atomicAdd(&cnt[ids_s[p]], 1);
+  for (int p = threadIdx.x; p < P; p += blockDim.x) atomicAdd(&s.cnt[s.ids[p]], 1);
   __syncthreads();
   if (threadIdx.x == 0) {
-    int s = 0, ng = 0;
+    int st = 0, ng = 0;
     for (int e = 0; e < E; ++e) {
-      start[e] = s;
-      if (cnt[e]) {
+      s.start[e] = st;
+      if (s.cnt[e]) {
         a.group_expert[ng] = e;
-        a.group_start[ng] = s;
-        a.group_count[ng] = cnt[e];
+        a.group_start[ng] = st;
+        a.group_count[ng] = s.cnt[e];
         ++ng;
       }
-      s += cnt[e];
+      st += s.cnt[e];
     }
     // the shared expert's pseudo-experts: every row, after the routed pairs
     for (int j = 0; j < a.extra_groups; ++j) {
@@ -121,16 +128,16 @@ __global__ __launch_bounds__(256) void moe_group_kernel(MoeRouteArgs a) {
   for (int q = threadIdx.x; q < a.extra_groups * a.rows; q += blockDim.x) a.pair_row[P + q] = q % a.rows;
   __syncthreads();
   // a pair's slot: its expert's start plus the number of earlier pairs of
-  // that expert.  Wave w scans experts w, w + 4, ...: per 64-pair chunk a
-  // ballot marks the expert's pairs, and each marked lane counts the marks
+  // that expert.  Wave w scans experts w, w + waves, ...: per 64-pair chunk
+  // a ballot marks the expert's pairs, and each marked lane counts the marks
   // below it (P / 64 ballots per expert instead of P compares per pair)
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE, nw = blockDim.x / WAVE;
   for (int e = wave; e < E; e += nw) {
-    if (!cnt[e]) continue;
-    int base = start[e];
+    if (!s.cnt[e]) continue;
+    int base = s.start[e];
     for (int c = 0; c < P; c += WAVE) {
       const int p = c + lane;
-      const bool hit = p < P && ids_s[p] == e;
+      const bool hit = p < P && s.ids[p] == e;
       const unsigned long long m = __ballot(hit);
       if (hit) {
         const int o = base + __popcll(m & ((1ull << lane) - 1));
@@ -142,13 +149,22 @@ __global__ __launch_bounds__(256) void moe_group_kernel(MoeRouteArgs a) {
   }
 }
 
+__global__ __launch_bounds__(256) void moe_group_kernel(MoeRouteArgs a) {
+  __shared__ GroupLds s;
+  group_pairs<false>(a, s);
+}
+
 // Router and route in one launch (pipeline.rs MoeFfn: router logits of the
 // normed FFN input, softmax over all experts, top-k): one block of 16 waves
 // per row.  b = RMSNorm(x; gamma) goes to LDS in fp32; wave w computes the
 // logits of experts w, w + 16, ... (lane l takes 8 consecutive elements at
 // 8 l + 512 s, one 16-byte weight load each; loads of a wave's experts are
 // issued together), the shared-gate dot product joins them, and the first
-// wave then routes exactly as moe_route_kernel does.
+// wave then routes exactly as moe_route_kernel does.  With a.arrive set the
+// launch also groups the pairs: every block publishes its ids with relaxed
+// device-scope stores, waits for them and counts its arrival; the last
+// block to arrive builds the group table (group_pairs) and resets the
+// counter, so no block waits on another and no grouping launch follows.
 constexpr int RR_THREADS = 1024;
 constexpr int RR_X = 2;  // f32x4 of x per thread: H <= 8192
 constexpr int RR_S = 4;  // 512-element steps of router weights in flight per wave
@@ -250,20 +266,35 @@ __global__ __launch_bounds__(RR_THREADS) void moe_router_route_kernel(MoeRouteAr
     if (j < H) dot += bsh[j] * sg[i];
   }
   dot = block_sum<RR_THREADS / WAVE>(dot, red);   // (its barriers also publish the logits)
-  if (threadIdx.x >= WAVE) return;
-  int32_t *ids = a.ids + (int64_t)r * a.k;
-  float *w = a.wts + (int64_t)r * a.k;
-  float wsel[8], sel;
-  int isel[8];
-  moe_topk(lg, E, a.k, lane, isel, wsel, sel);
-  if (lane == 0) {
-    for (int j = 0; j < a.k; ++j) {
-      ids[j] = isel[j];
-      w[j] = a.renorm ? wsel[j] / sel : wsel[j];
-      if (a.ids_record) a.ids_record[(int64_t)r * a.k + j] = isel[j];
+  if (threadIdx.x < WAVE) {
+    int32_t *ids = a.ids + (int64_t)r * a.k;
+    float *w = a.wts + (int64_t)r * a.k;
+    float wsel[8], sel;
+    int isel[8];
+    moe_topk(lg, E, a.k, lane, isel, wsel, sel);
+    if (lane == 0) {
+      for (int j = 0; j < a.k; ++j) {
+        if (a.arrive) __hip_atomic_store(ids + j, isel[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else ids[j] = isel[j];
+        w[j] = a.renorm ? wsel[j] / sel : wsel[j];
+        if (a.ids_record) a.ids_record[(int64_t)r * a.k + j] = isel[j];
+      }
+      if (a.gate) a.gate[r] = a.w_sh_gate ? 1.0f / (1.0f + expf(-dot)) : 1.0f;
     }
-    if (a.gate) a.gate[r] = a.w_sh_gate ? 1.0f / (1.0f + expf(-dot)) : 1.0f;
   }
+  if (!a.arrive) return;
+  // the ids are complete, then one arrival for the block; the last block
+  // to arrive (counter rows - 1) groups every row's pairs
+  __shared__ int last_s;
+  __shared__ GroupLds gs;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last_s = __hip_atomic_fetch_add(a.arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.rows - 1;
+  __syncthreads();
+  if (!last_s) return;
+  if (threadIdx.x == 0) __hip_atomic_store(a.arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  group_pairs<true>(a, gs);
 }
 
 // x[r][c] += sum_j w_j y[pair(r, j)][c] + gate_r ysh[r][c]; grid (columns / 256, rows)
@@ -300,15 +331,17 @@ hipError_t launch_moe_route(const MoeRouteArgs &a, bool group, hipStream_t st) {
   if (a.E > 256 || a.k > 8 || (group && a.rows * a.k > GROUP_MAX_PAIRS) || a.extra_groups < 0 ||
       a.extra_groups > 8)
     return hipErrorInvalidValue;
-  if (a.w_router) {
-    if (!a.act_f32 || !a.gamma || a.H % 8 || a.H > MOE_ROUTER_MAX_H) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(moe_router_route_kernel, dim3(a.rows), dim3(RR_THREADS), (size_t)(a.H + a.E) * 4, st, a);
+  MoeRouteArgs b = a;
+  if (!group || !a.w_router) b.arrive = nullptr;  // only the one-launch router groups by itself
+  if (b.w_router) {
+    if (!b.act_f32 || !b.gamma || b.H % 8 || b.H > MOE_ROUTER_MAX_H) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(moe_router_route_kernel, dim3(b.rows), dim3(RR_THREADS), (size_t)(b.H + b.E) * 4, st, b);
   } else {
-    hipLaunchKernelGGL(moe_route_kernel, dim3(a.rows), dim3(ROUTE_THREADS), 0, st, a);
+    hipLaunchKernelGGL(moe_route_kernel, dim3(b.rows), dim3(ROUTE_THREADS), 0, st, b);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !group) return e;
-  hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(256), 0, st, a);
+  if (e != hipSuccess || !group || b.arrive) return e;
+  hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(256), 0, st, b);
   return hipGetLastError();
 }
 
