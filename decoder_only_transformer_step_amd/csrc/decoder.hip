@@ -267,7 +267,7 @@ Layout make_layout(const decoder_config_t *c) {
   L.f32_hexp = take((size_t)std::max(c->top_k, 1) * std::max(c->expert_inter, 1) * 4);
   if (c->n_experts > 0) {
     const int E = c->n_experts, k = c->top_k, P = L.R * k, S = moe_shared_parts(c);
-    const size_t PS = (size_t)L.R * (k + S);  // pairs with the shared pseudo-experts'
+    const size_t PS = (size_t)L.R * (k + S);  // pairs, the shared pseudo-experts' included
     L.rlogits = take((size_t)L.R * E * 4);
     L.rids = take((size_t)P * 4);
     L.rids_rec = take((size_t)c->n_layers * P * 4);
