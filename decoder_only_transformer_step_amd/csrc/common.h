@@ -57,6 +57,12 @@ __device__ __forceinline__ u32pair pack_split2(float a, float b) {
 __device__ __forceinline__ u32x4 load16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
+// A 16-byte load marked non-temporal (streamed once: weights of a batch-1
+// projection).  On this part a 352 MB sweep read this way ran at 6.0-6.2
+// TB/s against 5.1-5.2 TB/s with plain loads.
+__device__ __forceinline__ u32x4 load16_nt(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 __device__ __forceinline__ u32x2 load8(const void *p) {
   return *reinterpret_cast<const u32x2 *>(p);
 }

@@ -106,7 +106,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const void *Wv, con
         const bool kv = (step < s1) && (step * 64 + quad * 16 < K);
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-          const u32x4 raw = (kv && nvalid) ? load16(qrow[p] + k) : u32x4{0u, 0u, 0u, 0u};
+          const u32x4 raw = (kv && nvalid) ? load16_nt(qrow[p] + k) : u32x4{0u, 0u, 0u, 0u};
           wf[u][0][p] = i8x8_to_bf16(u32x2{raw[0], raw[1]});
           wf[u][1][p] = i8x8_to_bf16(u32x2{raw[2], raw[3]});
         }
@@ -141,7 +141,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const void *Wv, con
       const int k = step * 32;
       const bool kv = (step < s1) && (k + quad * 8 < K);
 #pragma unroll
-      for (int p = 0; p < NP; ++p) wf[u][p] = (kv && nvalid) ? load16(wrow[p] + k) : u32x4{0u, 0u, 0u, 0u};
+      for (int p = 0; p < NP; ++p) wf[u][p] = (kv && nvalid) ? load16_nt(wrow[p] + k) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll

@@ -107,7 +107,7 @@ __device__ __forceinline__ void load_batch(u32x4 (&v)[UNR][R], const char *const
     const bool ok = st * 64 * EPL + lane * EPL < K;  // false for every lane past the last step
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      v[u][r] = load16(ok ? static_cast<const void *>(wp[r] + st * 1024) : static_cast<const void *>(gv_zero));
+      v[u][r] = load16_nt(ok ? static_cast<const void *>(wp[r] + st * 1024) : static_cast<const void *>(gv_zero));
   }
 }
 

@@ -85,7 +85,7 @@ __device__ __forceinline__ void gr_load(const GemmArgs &g, const int64_t (&off)[
   const int k = s * 512 + lane * 8;
 #pragma unroll
   for (int r = 0; r < RG; ++r)
-    w[r] = load16(off[r] >= 0 && k < g.K ? static_cast<const void *>(g.W + off[r] + k)
+    w[r] = load16_nt(off[r] >= 0 && k < g.K ? static_cast<const void *>(g.W + off[r] + k)
                                           : static_cast<const void *>(gr_zero + lane));
 }
 
