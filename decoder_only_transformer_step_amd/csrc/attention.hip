@@ -227,7 +227,13 @@ __device__ __forceinline__ void merge_fused(const AttnArgs &a, int gi, int rg, i
   }
 }
 
-template <int D, int PM, bool PG>
+// NTK: the K rows are loaded non-temporal (a split of at most one tile per
+// wave reads each K row once, within one wave: 8B decode 314-319 -> 321-322
+// tok/s; the MoE decode's attention, one head per group, 10.56 -> 10.9 us
+// per layer, about 0.5% of its step); with several tiles per wave the hint
+// cost more than it gave (16 x 32 768-key batch 976 -> 943 tok/s), and V,
+// whose 128-byte lines two waves share, stays plain everywhere.
+template <int D, int PM, bool PG, bool NTK = false>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   constexpr int NDT = D / 16;
   __shared__ float lo[4][16][D];
@@ -274,8 +280,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const uint16_t *k_hi = k_lo + 4 * D;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-      ka[ks] = load16(k_lo + ks * 32);
-      kh[ks] = load16(k_hi + ks * 32);
+      ka[ks] = (NTK ? load16_nt : load16)(k_lo + ks * 32);
+      kh[ks] = (NTK ? load16_nt : load16)(k_hi + ks * 32);
     }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) va[dt] = load16(vt + (int64_t)(dt * 16 + c) * a.S + tt + quad * 8);
@@ -449,6 +455,8 @@ namespace {
 template <int D, int PM>
 hipError_t launch_pm(const AttnArgs &a, hipStream_t st) {
   if (a.pt) hipLaunchKernelGGL((attn_kernel<D, PM, true>), dim3(a.n_groups * a.n_splits), dim3(256), 0, st, a);
+  else if (PM == 1 && a.kc <= 128)  // decode, one 32-key tile per wave
+    hipLaunchKernelGGL((attn_kernel<D, PM, false, PM == 1>), dim3(a.n_groups * a.n_splits), dim3(256), 0, st, a);
   else hipLaunchKernelGGL((attn_kernel<D, PM, false>), dim3(a.n_groups * a.n_splits), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1 || a.counters) return e;
