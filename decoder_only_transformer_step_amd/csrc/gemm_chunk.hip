@@ -206,7 +206,7 @@ __device__ __forceinline__ void a_load_rows(const ARows<MT, SPLIT> &ra, int k0, 
 // the same XCD at about the same time and the second one finds the weights
 // in that XCD's L2.  GR (grouped, mblocks 1): u = (row tile of 32 MT
 // rows, weight tile).
-template <int MT, int EPI, bool SPLIT, bool GR>
+template <int MT, int EPI, bool SPLIT, bool GR, bool PIN>
 __global__ __launch_bounds__(CK_WAVES * WAVE, 2) void gemm_chunk_kernel(GemmArgs g, int ntiles16, int mblocks) {
   constexpr int NP = paired<EPI>();
   constexpr int LT = CK_NS / NP;  // logical 32-row tiles per wave
@@ -322,14 +322,29 @@ __global__ __launch_bounds__(CK_WAVES * WAVE, 2) void gemm_chunk_kernel(GemmArgs
   // Two steps per iteration, activation loads first (the wait before their
   // LDS store then leaves the newer weight loads in flight).  Steps at or
   // past s1 read zeros (k >= kend), so an odd step count adds one zero step.
+  // PIN holds that order with scheduling barriers: left to itself the
+  // compiler moved weight loads ahead of activation loads, so the
+  // activation stores also waited for 2-4 of the step's weight loads.  It
+  // pays where few row blocks share a weight tile (128 rows: 8B prefill
+  // 19.25 k -> 19.68 k tok/s on one machine, unchanged on a slower one);
+  // with 8 row blocks (512 rows) the down projection measured 122 -> 125.5
+  // us with it, and the grouped form 1% slower, so those keep the
+  // compiler's order.
+  auto order = [] {
+    if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
+  };
   for (int s = s0; s < s1; s += 2) {
     aload((s + 1) * CK_STEP, kend, ar);
+    order();
     w_load<!GR>(wp, wv, (s + 1) * CK_STEP, kend, w1);
+    order();
     mma_step<MT, SPLIT>(a_s[0], w0, sw, acc);
     a_store<MT, SPLIT>(a_s[1], ar);
     __syncthreads();
     aload((s + 2) * CK_STEP, kend, ar);
+    order();
     w_load<!GR>(wp, wv, (s + 2) * CK_STEP, kend, w0);
+    order();
     mma_step<MT, SPLIT>(a_s[1], w1, sw, acc);
     a_store<MT, SPLIT>(a_s[0], ar);
     __syncthreads();
@@ -386,21 +401,25 @@ __global__ __launch_bounds__(CK_WAVES * WAVE, 2) void gemm_chunk_kernel(GemmArgs
   }
 }
 
-template <int MT, int EPI, bool GR = false>
+template <int MT, int EPI, bool GR, bool PIN>
 hipError_t launch_mt(const GemmArgs &g, int ntiles16, int blocks, int mblocks, hipStream_t st) {
   if (g.a_lo)
-    hipLaunchKernelGGL((gemm_chunk_kernel<MT, EPI, true, GR>), dim3(blocks), dim3(CK_WAVES * WAVE), 0, st, g,
+    hipLaunchKernelGGL((gemm_chunk_kernel<MT, EPI, true, GR, PIN>), dim3(blocks), dim3(CK_WAVES * WAVE), 0, st, g,
                        ntiles16, mblocks);
   else
-    hipLaunchKernelGGL((gemm_chunk_kernel<MT, EPI, false, GR>), dim3(blocks), dim3(CK_WAVES * WAVE), 0, st, g,
+    hipLaunchKernelGGL((gemm_chunk_kernel<MT, EPI, false, GR, PIN>), dim3(blocks), dim3(CK_WAVES * WAVE), 0, st, g,
                        ntiles16, mblocks);
   return hipGetLastError();
 }
 
+// loads in program order up to CK_PIN_MBLOCKS row blocks per weight tile
+constexpr int CK_PIN_MBLOCKS = 2;
+
 template <int EPI>
 hipError_t launch_epi(const GemmArgs &g, int ntiles16, int blocks, int mblocks, hipStream_t st) {
-  if (std::min(g.M, CK_ROWS) <= 32) return launch_mt<1, EPI>(g, ntiles16, blocks, mblocks, st);
-  return launch_mt<2, EPI>(g, ntiles16, blocks, mblocks, st);
+  if (std::min(g.M, CK_ROWS) <= 32) return launch_mt<1, EPI, false, true>(g, ntiles16, blocks, mblocks, st);
+  if (mblocks <= CK_PIN_MBLOCKS) return launch_mt<2, EPI, false, true>(g, ntiles16, blocks, mblocks, st);
+  return launch_mt<2, EPI, false, false>(g, ntiles16, blocks, mblocks, st);
 }
 
 // P[((nt * K / 16 + kt) * 64 + l) * 8 + e] = W[32 nt + l % 32][16 kt + 8 (l / 32) + e]
@@ -491,6 +510,6 @@ hipError_t launch_gemm_chunk_grouped(const GemmArgs &g, int epi, int pairs, int 
   const int64_t row_tiles = ((int64_t)pairs + 31 * (int64_t)std::min(group_slots, pairs)) / 32;
   const int64_t blocks = row_tiles * gemm_chunk_tiles(g, epi);
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  if (epi == EPI_SWIGLU) return launch_mt<1, EPI_SWIGLU, true>(g, ntiles16, (int)blocks, 1, st);
-  return launch_mt<1, EPI_STORE, true>(g, ntiles16, (int)blocks, 1, st);
+  if (epi == EPI_SWIGLU) return launch_mt<1, EPI_SWIGLU, true, false>(g, ntiles16, (int)blocks, 1, st);
+  return launch_mt<1, EPI_STORE, true, false>(g, ntiles16, (int)blocks, 1, st);
 }
