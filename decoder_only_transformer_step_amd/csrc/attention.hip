@@ -81,7 +81,9 @@ __device__ __forceinline__ Col column(const AttnArgs &a, int rg, int g, int c) {
 
 __device__ __forceinline__ void store_out(const AttnArgs &a, int64_t i, float v) {
   if (a.out_f32) {
-    a.out_f32[i] = v;
+    // (read inside the same launch when the output projection is fused)
+    if (a.wo) __hip_atomic_store(a.out_f32 + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else a.out_f32[i] = v;
   } else {
     uint32_t hi, lo;
     split_bf16(v, hi, lo);
@@ -227,18 +229,144 @@ __device__ __forceinline__ void merge_fused(const AttnArgs &a, int gi, int rg, i
   }
 }
 
+// A column group's output is complete: with the output projection fused,
+// every thread's stores complete, then one arrival for the group.
+__device__ __forceinline__ void publish_group(const AttnArgs &a) {
+  if (!a.wo) return;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(a.o_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Fused output projection (batch-1 decode), one block of 4 waves past the
+// attention grid: wave w owns rows (4 b + w) ATTN_O_RPW + r of wo.  The
+// rows' weights (lane l holds k = 8 l + 512 s, as the batch-1 GEMV) and
+// residual values stream into registers while the attention runs; thread 0
+// then waits (a bounded spin) until every column group has arrived, the
+// block stages o (fp32, relaxed device-scope loads) in LDS in the GEMV's
+// layout, and each wave sums its rows with the GEMV's arithmetic order:
+// step by step, 8 FMAs per 16-byte weight load, then the wave reduction,
+// then x + sum, so the result is the separate launch's, bit for bit.  Every
+// block reaches its end: the attention blocks wait on nothing, and they
+// precede the projection blocks in the dispatch order.
+//
+// Measured (8B decode, 136 attention blocks and 256 projection blocks,
+// in-kernel clock): the attention publishes its last group at about 12.4
+// us; the projection blocks see it 1.4 us later, have o in LDS 1.3 us
+// after that and end about 1 us later, against 13 + 8.4 us for the
+// attention and projection launches one after the other.  The weights
+// wait AO_HOLD_TICKS of the 100 MHz clock (1.5 us) before they go out, so
+// that the attention's cache loads, issued first, are not queued behind
+// 33.5 MB of them (8B decode 326 -> 329 tok/s against no wait; 3 us was
+// slower again).
+constexpr int AO_STEPS = ATTN_O_MAX_K / 512;
+constexpr uint32_t AO_SPIN_LIMIT = 1u << 20;
+constexpr uint64_t AO_HOLD_TICKS = 150;
+__device__ u32x4 ao_zero[1];
+
+__device__ __forceinline__ int ao_slot(int k) {  // k: a multiple of 4
+  return ((k >> 9) * 2 + ((k >> 2) & 1)) * 64 + ((k & 511) >> 3);
+}
+
+template <int D>
+__device__ __forceinline__ void o_proj_block(const AttnArgs &a, int b, f32x4 *xs) {
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int K = a.Hq * D, steps = (K + 511) / 512;
+  const int r0 = (b * 4 + wave) * ATTN_O_RPW;
+  int row[ATTN_O_RPW];
+  u32x4 w[ATTN_O_RPW][AO_STEPS];
+  float xr[ATTN_O_RPW];
+#pragma unroll
+  for (int r = 0; r < ATTN_O_RPW; ++r) row[r] = min(r0 + r, a.o_rows - 1);
+  {
+    const uint64_t t_go = wall_clock64() + AO_HOLD_TICKS;
+    while (wall_clock64() < t_go) __builtin_amdgcn_s_sleep(2);
+  }
+#pragma unroll
+  for (int s = 0; s < AO_STEPS; ++s) {
+    const bool ok = s * 512 + lane * 8 < K;
+#pragma unroll
+    for (int r = 0; r < ATTN_O_RPW; ++r)
+      w[r][s] = load16_nt(ok ? static_cast<const void *>(a.wo + (int64_t)row[r] * K + s * 512 + lane * 8)
+                             : static_cast<const void *>(ao_zero));
+  }
+#pragma unroll
+  for (int r = 0; r < ATTN_O_RPW; ++r) xr[r] = a.o_x[row[r]];
+
+  if (threadIdx.x == 0) {
+    for (uint32_t n = 0; n < AO_SPIN_LIMIT; ++n) {
+      const uint32_t seen = __hip_atomic_load(a.o_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((int32_t)(seen - a.o_target) >= 0) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+  // o -> LDS, zero past K (AO_STEPS * 512 elements, 4 per thread and slot)
+  const float *zf = reinterpret_cast<const float *>(ao_zero);
+  float v[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int k = (u * 256 + threadIdx.x) * 4;
+    const float *src = k < K ? a.out_f32 + k : zf;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[u][e] = __hip_atomic_load(const_cast<float *>(src + e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) xs[ao_slot((u * 256 + threadIdx.x) * 4)] = f32x4{v[u][0], v[u][1], v[u][2], v[u][3]};
+  __syncthreads();
+  float acc[ATTN_O_RPW];
+#pragma unroll
+  for (int r = 0; r < ATTN_O_RPW; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int s = 0; s < AO_STEPS; ++s) {
+    if (s < steps) {
+      const f32x4 xa = xs[(s * 2) * 64 + lane], xb = xs[(s * 2 + 1) * 64 + lane];
+#pragma unroll
+      for (int r = 0; r < ATTN_O_RPW; ++r) {
+        const u32x4 q = w[r][s];
+        float t = acc[r];
+        t = fmaf(bf16_lo(q[0]), xa[0], t);
+        t = fmaf(bf16_hi(q[0]), xa[1], t);
+        t = fmaf(bf16_lo(q[1]), xa[2], t);
+        t = fmaf(bf16_hi(q[1]), xa[3], t);
+        t = fmaf(bf16_lo(q[2]), xb[0], t);
+        t = fmaf(bf16_hi(q[2]), xb[1], t);
+        t = fmaf(bf16_lo(q[3]), xb[2], t);
+        t = fmaf(bf16_hi(q[3]), xb[3], t);
+        acc[r] = t;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < ATTN_O_RPW; ++r) acc[r] = wave_sum(acc[r]);
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < ATTN_O_RPW; ++r)
+      if (r0 + r < a.o_rows) a.o_x[row[r]] = xr[r] + acc[r];
+  }
+}
+
 // NTK: the K rows are loaded non-temporal (a split of at most one tile per
 // wave reads each K row once, within one wave: 8B decode 314-319 -> 321-322
 // tok/s; the MoE decode's attention, one head per group, 10.56 -> 10.9 us
 // per layer, about 0.5% of its step); with several tiles per wave the hint
 // cost more than it gave (16 x 32 768-key batch 976 -> 943 tok/s), and V,
 // whose 128-byte lines two waves share, stays plain everywhere.
-template <int D, int PM, bool PG, bool NTK = false>
+// OF: the output projection is fused (blocks past the attention grid).
+template <int D, int PM, bool PG, bool NTK = false, bool OF = false>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   constexpr int NDT = D / 16;
   __shared__ float lo[4][16][D];
   __shared__ float lm[4][16], ll[4][16];
   __shared__ int last_s;
+  if constexpr (OF) {
+    static_assert(64 * D >= AO_STEPS * 512, "o staging fits in lo");
+    if (blockIdx.x >= a.n_groups * a.n_splits) {
+      o_proj_block<D>(a, blockIdx.x - a.n_groups * a.n_splits, reinterpret_cast<f32x4 *>(&lo[0][0][0]));
+      return;
+    }
+  }
 
   const int gi = blockIdx.x / a.n_splits, split = blockIdx.x - gi * a.n_splits;
   const int g = gi % a.Hkv, rg = gi / a.Hkv;
@@ -385,12 +513,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int q = 0; q < NDT; ++q) o[q] += sc * lo[w][cc][jj + 16 * q];
   }
   if (nact == 1) {
-    if (!oc.valid) return;
-    const float r = attn_sink_fold(a, oc.head, M, L);
-    const float inv = r / L;
-    const int64_t ob = ((int64_t)oc.row * a.Hq + oc.head) * D;
+    if (oc.valid) {
+      const float r = attn_sink_fold(a, oc.head, M, L);
+      const float inv = r / L;
+      const int64_t ob = ((int64_t)oc.row * a.Hq + oc.head) * D;
 #pragma unroll
-    for (int q = 0; q < NDT; ++q) store_out(a, ob + jj + 16 * q, o[q] * inv);
+      for (int q = 0; q < NDT; ++q) store_out(a, ob + jj + 16 * q, o[q] * inv);
+    }
+    if (OF) publish_group(a);
     return;
   }
   // several splits: publish this block's partial
@@ -432,6 +562,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   if (nact <= 8) merge_fused<D, PM, 8>(a, gi, rg, g, nact, ncols, sc, sl, &lm[0][0]);
   else if (nact <= 16) merge_fused<D, PM, 16>(a, gi, rg, g, nact, ncols, sc, sl, &lm[0][0]);
   else merge_fused<D, PM, 32>(a, gi, rg, g, nact, ncols, sc, sl, &lm[0][0]);
+  if (OF) publish_group(a);
 }
 
 // One block per (group, valid column), one thread per dim: combine the
@@ -454,10 +585,19 @@ namespace {
 
 template <int D, int PM>
 hipError_t launch_pm(const AttnArgs &a, hipStream_t st) {
-  if (a.pt) hipLaunchKernelGGL((attn_kernel<D, PM, true>), dim3(a.n_groups * a.n_splits), dim3(256), 0, st, a);
+  const int nb = a.n_groups * a.n_splits;
+  if (PM == 1 && a.wo) {  // batch-1 decode with the output projection
+    if (a.pt || !a.counters || !a.out_f32 || a.rows != 1 || (int64_t)a.Hq * D > ATTN_O_MAX_K) return hipErrorInvalidValue;
+    if (a.kc <= 128)
+      hipLaunchKernelGGL((attn_kernel<D, PM, false, PM == 1, PM == 1>), dim3(nb + a.o_blocks), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_kernel<D, PM, false, false, PM == 1>), dim3(nb + a.o_blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  if (a.wo) return hipErrorInvalidValue;
+  if (a.pt) hipLaunchKernelGGL((attn_kernel<D, PM, true>), dim3(nb), dim3(256), 0, st, a);
   else if (PM == 1 && a.kc <= 128)  // decode, one 32-key tile per wave
-    hipLaunchKernelGGL((attn_kernel<D, PM, false, PM == 1>), dim3(a.n_groups * a.n_splits), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((attn_kernel<D, PM, false>), dim3(a.n_groups * a.n_splits), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<D, PM, false, PM == 1>), dim3(nb), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attn_kernel<D, PM, false>), dim3(nb), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1 || a.counters) return e;
   const int ncols = std::min(16, a.rows_per_group * a.G);  // valid columns of a group

@@ -247,8 +247,9 @@ Layout make_layout(const decoder_config_t *c) {
   L.gout = take((size_t)(c->max_seq + 1) * 4);
   L.part_o = take((size_t)ATTN_MAX_TASKS * 16 * d * 4);
   L.part_ml = take((size_t)ATTN_MAX_TASKS * 16 * 2 * 4);
-  // one arrival counter per attention group, then the MoE router's
-  L.attn_cnt = take((size_t)(ATTN_MAX_TASKS + 1) * 4);
+  // one arrival counter per attention group, then the MoE router's, then
+  // the one of the attention's fused output projection
+  L.attn_cnt = take((size_t)(ATTN_MAX_TASKS + 2) * 4);
   int max_small_n = std::max(qkvr, H);
   if (c->n_experts > 0) max_small_n = std::max(max_small_n, 2 * c->shared_inter);
   L.gpart_elems = (size_t)GEMM_MAX_SPLIT * L.R * 2 * (size_t)max_small_n;
@@ -340,6 +341,8 @@ struct decoder {
   int layer_limit = -1;
   bool stop_after_attn = false;  // the last layer run stops after o_proj + residual
   int stop_mid_layer = -1;       // that layer, for the current step (-1: none)
+  bool fuse_o = true;            // batch-1 decode: output projection inside the attention launch
+  uint32_t o_groups = 0;         // groups counted so far by the fused launches' arrival counter
   int last_rows = 0;
   int32_t *pinned = nullptr;
   // paged KV cache: device page table [max_batch][mp] (staged with the rows),
@@ -636,8 +639,11 @@ int norm_into(decoder *D, GemmArgs &g, const float *x, const float *gamma, int r
   return DEC_OK;
 }
 
+// wo (batch-1 decode, bf16 weights): the output projection x += wo . o runs
+// inside the attention launch where the kernel takes it; *o_fused says
+// whether it did (otherwise the caller launches it).
 int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, const int32_t *hpos,
-              float *out_f32 = nullptr) {
+              float *out_f32 = nullptr, const uint16_t *wo = nullptr, bool *o_fused = nullptr) {
   const decoder_config_t &c = D->c;
   const int W = c.sliding_window;
   double kv_rows = 0, qk = 0;
@@ -720,9 +726,26 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
   // chunk that fits one column group per kv head (a verify pass of a few
   // drafted rows) takes the decode kernel, whose waves each own a tile
   const bool chunk_kernel = rows > rows_per_group && attention_chunk_fits(a, c.head_dim);
+  const int qd = c.n_heads * c.head_dim;
+  if (o_fused) *o_fused = false;
+  if (wo && o_fused && D->fuse_o && !chunk_kernel && a.pos_mode == 1 && rows == 1 && out_f32 && a.counters && !a.pt &&
+      qd <= ATTN_O_MAX_K) {
+    const int H = c.hidden;
+    a.wo = wo;
+    a.o_x = D->x;
+    a.o_rows = H;
+    a.o_blocks = (H + 4 * ATTN_O_RPW - 1) / (4 * ATTN_O_RPW);
+    a.o_done = reinterpret_cast<uint32_t *>(D->attn_cnt + ATTN_MAX_TASKS + 1);
+    a.o_target = D->o_groups + (uint32_t)a.n_groups;
+    D->act_norm = nullptr;  // x changes
+    timer.bytes += (double)H * qd * 2 + (double)qd * 4 + (double)H * 8;
+    timer.flops += 2.0 * H * qd;
+    *o_fused = true;
+  }
   hipError_t e = chunk_kernel ? launch_attention_chunk(a, c.head_dim, D->stream)
                               : launch_attention(a, c.head_dim, D->stream);
   if (e != hipSuccess) return hip_fail(D, e, "attention");
+  if (a.wo) D->o_groups = a.o_target;  // the launch's groups count from here on
   return DEC_OK;
 }
 
@@ -846,8 +869,11 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
   q.qkv.Hkv = c.n_kv_heads;
   q.qkv.d = d;
   if (!c.qk_norm && (rc = gemv(D, DEC_NODE_QKV, EPI_QKV, quant(D, q, l, 0)))) return rc;
-  if ((rc = attention(D, l, 1, 1, max_pos, hpos, D->f32_attn))) return rc;
-  if ((rc = gemv(D, DEC_NODE_O, EPI_ADD, quant(D, gemv_args(W.w_o, D->f32_attn, qd, H, D->x), l, 1)))) return rc;
+  bool o_fused = false;
+  if ((rc = attention(D, l, 1, 1, max_pos, hpos, D->f32_attn, D->c.weight_quant ? nullptr : W.w_o, &o_fused)))
+    return rc;
+  if (!o_fused && (rc = gemv(D, DEC_NODE_O, EPI_ADD, quant(D, gemv_args(W.w_o, D->f32_attn, qd, H, D->x), l, 1))))
+    return rc;
   if (l == D->stop_mid_layer) return DEC_OK;
 
   if (c.n_experts == 0) {
@@ -1432,7 +1458,7 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
   if (hipMemsetAsync(D->kcache, 0, kvb, D->stream) != hipSuccess ||
       hipMemsetAsync(D->vcache, 0, kvb, D->stream) != hipSuccess ||
       hipMemsetAsync(D->next_token, 0, (size_t)cfg->max_batch * 4, D->stream) != hipSuccess ||
-      hipMemsetAsync(D->attn_cnt, 0, (size_t)(ATTN_MAX_TASKS + 1) * 4, D->stream) != hipSuccess ||
+      hipMemsetAsync(D->attn_cnt, 0, (size_t)(ATTN_MAX_TASKS + 2) * 4, D->stream) != hipSuccess ||
       hipStreamSynchronize(D->stream) != hipSuccess)
     return cleanup(DEC_E_HIP);
   *out = D;
@@ -1898,6 +1924,12 @@ int decoder_debug_layer_limit(decoder_t *D, int32_t layers) {
 int decoder_debug_stop_after_attention(decoder_t *D, int32_t on) {
   if (check_dec(D) || (on != 0 && on != 1)) return DEC_E_INVALID;
   D->stop_after_attn = on != 0;
+  return DEC_OK;
+}
+
+int decoder_debug_fuse_o_proj(decoder_t *D, int32_t on) {
+  if (check_dec(D) || (on != 0 && on != 1)) return DEC_E_INVALID;
+  D->fuse_o = on != 0;
   return DEC_OK;
 }
 

@@ -171,7 +171,24 @@ struct AttnArgs {
   float softcap;           // 0: off; c > 0: scaled score s -> c tanh(s / c)
   float scale;             // 1 / sqrt(d), for the soft-cap
   const float *sinks;      // [Hq] sink logits of this layer, or null
+  // Batch-1 decode with the output projection fused (wo set; fp32 output,
+  // in-kernel merge): o_blocks blocks past the attention grid each own
+  // 4 ATTN_O_RPW rows of the bf16 matrix wo [o_rows][Hq d] and finish
+  // o_x[n] = o_x[n] + wo[n] . o once every column group has published o.
+  // *o_done counts the groups that have, over every fused launch of the
+  // decoder (it is never reset); this launch's groups are all in once it
+  // reaches o_target (modulo 2^32).
+  const uint16_t *wo;
+  float *o_x;
+  int32_t o_rows, o_blocks;
+  uint32_t *o_done;
+  uint32_t o_target;
 };
+
+// fused output projection: rows per wave, and the widest input it holds
+// (one row of at most ATTN_O_MAX_K bf16 weights per register set)
+constexpr int ATTN_O_RPW = 4;
+constexpr int ATTN_O_MAX_K = 4096;
 
 constexpr float ATTN_LOG2E = 1.4426950408889634f;
 // splits per group that attn_kernel merges itself (its last block to finish)

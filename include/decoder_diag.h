@@ -128,6 +128,13 @@ int decoder_debug_layer_limit(decoder_t *dec, int32_t layers);
  * on = 0 restores full layers.  DEC_E_INVALID for other values. */
 int decoder_debug_stop_after_attention(decoder_t *dec, int32_t on);
 
+/* on = 0: a batch-1 decode step launches each layer's output projection as
+ * its own GEMV after the attention; on = 1 (the default): the attention
+ * launch runs it where the kernel takes it (bf16 weights, fp32 attention
+ * output, the in-kernel split merge).  Both give the same bits; the switch
+ * exists so that tests can compare them.  DEC_E_INVALID for other values. */
+int decoder_debug_fuse_o_proj(decoder_t *dec, int32_t on);
+
 /* Copy the residual stream x (fp32 [rows][H]) left by the last prefill_chunk
  * or decode_step (row i = token i of the chunk, or batch entry i) to d_out. */
 int decoder_debug_read_x(decoder_t *dec, float *d_out, int32_t rows);

@@ -399,6 +399,44 @@ def test_moe_small_multi_chunk_prefill():
         assert_parity(compare_logits(lg[0], want["logits"], f"moe decode {step}"), f"moe decode {step}")
 
 
+@pytest.mark.parametrize("which,P", [("tiny", 16), ("tiny", 300), ("8b2", 130), ("8b2", 301), ("moe", 24)])
+def test_fused_output_projection_same_bits(which, P):
+    """Batch-1 decode runs each layer's output projection (and the residual
+    add) inside the attention launch, its blocks waiting for the column
+    groups' outputs (engine.zig Engine.forward: attention, then the output
+    projection into the residual).  The same steps with the projection as a
+    GEMV launch of its own must give the same bits, and both meet the oracle.
+    Cases: one split per group (the block writes its output) and several
+    (the group's last block merges), head_dim 64 and 128, a MoE layer."""
+    from synth.workloads import C8B
+    from tests.moe_routes import forced
+    shape, chunk = {"tiny": (TINY.with_(name="gqa-tiny-seq512", max_seq=512), 16),
+                    "8b2": (C8B.with_(name="gqa-8b-layers-2", n_layers=2, vocab=1024, max_seq=512), 128),
+                    "moe": (small_moe(), 32)}[which]
+    moe = which == "moe"
+    log("fused o_proj", which, P)
+    W = host_weights(shape)
+    ids = [int(t) for t in prompt(shape, P)]
+    fused, _ = make_decoder(shape, W)
+    plain, _ = make_decoder(shape, W)
+    plain.debug_fuse_o_proj(0)
+    tok = int(np.argmax(run_prefill(fused, ids, chunk)))
+    m = oracle.Model(shape, W)
+    if moe:   # one chunk, on the routes the library took
+        m.forward(ids, 0, force_routes=forced(fused, shape, P))
+    else:
+        m.prefill(ids, chunk)
+    run_prefill(plain, ids, chunk)
+    for i in range(3):
+        lf, af = decode(fused, [0], [tok])
+        kw = {"force_routes": forced(fused, shape, 1)} if moe else {}
+        lp, ap = decode(plain, [0], [tok])
+        assert np.array_equal(lf.view(np.uint32), lp.view(np.uint32)), f"{which} step {i}: fused and separate differ"
+        assert int(af[0]) == int(ap[0])
+        assert_parity(compare_logits(lf[0], m.forward([tok], P + i, **kw)["logits"], f"{which} step {i}"), which)
+        tok = int(af[0])
+
+
 @pytest.mark.parametrize("N,K", [(16, 32), (60, 2048), (100, 688), (777, 4096), (4096, 14336)])
 def test_gemv_kernel_matches_oracle(N, K):
     from decoder_only_transformer_step_amd.binding import diag_gemv
