@@ -453,15 +453,28 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       s1 = mfma16x16x32(as_bf16x8(kh[ks]), as_bf16x8(ql[ks]), s1);
     }
     // lane holds S[key = t0 + 8 quad + i][col c] in s0, key + 4 in s1
+    // (the soft-cap, a uniform kernel argument, has a loop of its own, so
+    // the plain loop is selects with no branches)
     float sv[8];
     float tmax = NEG_SENTINEL;
+    if (a.softcap > 0.f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key0 = t0 + quad * 8 + i, key1 = key0 + 4;
-      sv[i] = (attn_key_ok(a, key0, col.pos) && key0 < k1) ? attn_logit2(a, s0[i]) : -INFINITY;
-      sv[4 + i] = (attn_key_ok(a, key1, col.pos) && key1 < k1) ? attn_logit2(a, s1[i]) : -INFINITY;
-      tmax = fmaxf(tmax, fmaxf(sv[i], sv[4 + i]));
+      for (int i = 0; i < 4; ++i) {
+        const int key0 = t0 + quad * 8 + i, key1 = key0 + 4;
+        sv[i] = (attn_key_ok(a, key0, col.pos) && key0 < k1) ? attn_logit2(a, s0[i]) : -INFINITY;
+        sv[4 + i] = (attn_key_ok(a, key1, col.pos) && key1 < k1) ? attn_logit2(a, s1[i]) : -INFINITY;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key0 = t0 + quad * 8 + i, key1 = key0 + 4;
+        const float v0 = s0[i] * a.scale_log2, v1 = s1[i] * a.scale_log2;
+        sv[i] = (attn_key_ok(a, key0, col.pos) && key0 < k1) ? v0 : -INFINITY;
+        sv[4 + i] = (attn_key_ok(a, key1, col.pos) && key1 < k1) ? v1 : -INFINITY;
+      }
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, fmaxf(sv[i], sv[4 + i]));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, WAVE));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, WAVE));
     const float m_new = fmaxf(m_run, tmax);

@@ -144,19 +144,34 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a, int rpb)
     f32x16 s;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    // the tile's K fragments first, so the LDS reads overlap each other
+    u32x4 ka[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) ka[j] = *reinterpret_cast<const u32x4 *>(cur + (lane & 31) * L::KS + 16 * j + 8 * h);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const u32x4 ka = *reinterpret_cast<const u32x4 *>(cur + (lane & 31) * L::KS + 16 * j + 8 * h);
-      s = mfma32x32x16(as_bf16x8(ka), as_bf16x8(qh[j]), s);
-      s = mfma32x32x16(as_bf16x8(ka), as_bf16x8(ql[j]), s);
+      s = mfma32x32x16(as_bf16x8(ka[j]), as_bf16x8(qh[j]), s);
+      s = mfma32x32x16(as_bf16x8(ka[j]), as_bf16x8(ql[j]), s);
     }
+    // scores in log2 units; the soft-cap (a uniform kernel argument) gets a
+    // loop of its own, so the plain loop is selects with no branches
     float p[16], tmax = AC_NEG;
+    if (a.softcap > 0.f) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = t0 + 8 * (i >> 2) + 4 * h + (i & 3);
-      p[i] = (attn_key_ok(a, key, pos) && key < k1) ? attn_logit2(a, s[i]) : -INFINITY;
-      tmax = fmaxf(tmax, p[i]);
+      for (int i = 0; i < 16; ++i) {
+        const int key = t0 + 8 * (i >> 2) + 4 * h + (i & 3);
+        p[i] = (attn_key_ok(a, key, pos) && key < k1) ? attn_logit2(a, s[i]) : -INFINITY;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = t0 + 8 * (i >> 2) + 4 * h + (i & 3);
+        const float v = s[i] * a.scale_log2;
+        p[i] = (attn_key_ok(a, key, pos) && key < k1) ? v : -INFINITY;
+      }
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, p[i]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, WAVE));
     const float m_new = fmaxf(m_run, tmax);
     const float alpha = exp2f(m_run - m_new);
