@@ -294,9 +294,10 @@ __device__ __forceinline__ void o_proj_block(const AttnArgs &a, int b, f32x4 *xs
   for (int r = 0; r < ATTN_O_RPW; ++r) xr[r] = a.o_x[row[r]];
 
   if (threadIdx.x == 0) {
+    const uint32_t target = *a.o_base + (uint32_t)a.n_groups;
     for (uint32_t n = 0; n < AO_SPIN_LIMIT; ++n) {
       const uint32_t seen = __hip_atomic_load(a.o_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((int32_t)(seen - a.o_target) >= 0) break;
+      if ((int32_t)(seen - target) >= 0) break;
       __builtin_amdgcn_s_sleep(1);
     }
   }
@@ -599,11 +600,11 @@ namespace {
 template <int D, int PM>
 hipError_t launch_pm(const AttnArgs &a, hipStream_t st) {
   const int nb = a.n_groups * a.n_splits;
-  if (PM == 1 && a.wo) {  // batch-1 decode with the output projection
+  if (PM != 2 && a.wo) {  // batch-1 decode with the output projection
     if (a.pt || !a.counters || !a.out_f32 || a.rows != 1 || (int64_t)a.Hq * D > ATTN_O_MAX_K) return hipErrorInvalidValue;
-    if (a.kc <= 128)
-      hipLaunchKernelGGL((attn_kernel<D, PM, false, PM == 1, PM == 1>), dim3(nb + a.o_blocks), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_kernel<D, PM, false, false, PM == 1>), dim3(nb + a.o_blocks), dim3(256), 0, st, a);
+    if (PM == 1 && a.kc <= 128)
+      hipLaunchKernelGGL((attn_kernel<D, PM, false, PM == 1, PM != 2>), dim3(nb + a.o_blocks), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_kernel<D, PM, false, false, PM != 2>), dim3(nb + a.o_blocks), dim3(256), 0, st, a);
     return hipGetLastError();
   }
   if (a.wo) return hipErrorInvalidValue;

@@ -248,8 +248,9 @@ Layout make_layout(const decoder_config_t *c) {
   L.part_o = take((size_t)ATTN_MAX_TASKS * 16 * d * 4);
   L.part_ml = take((size_t)ATTN_MAX_TASKS * 16 * 2 * 4);
   // one arrival counter per attention group, then the MoE router's, then
-  // the one of the attention's fused output projection
-  L.attn_cnt = take((size_t)(ATTN_MAX_TASKS + 2) * 4);
+  // per layer the fused output projection's arrival counter, then per
+  // layer that counter's value at the start of the current step
+  L.attn_cnt = take((size_t)(ATTN_MAX_TASKS + 1 + 2 * c->n_layers) * 4);
   int max_small_n = std::max(qkvr, H);
   if (c->n_experts > 0) max_small_n = std::max(max_small_n, 2 * c->shared_inter);
   L.gpart_elems = (size_t)GEMM_MAX_SPLIT * L.R * 2 * (size_t)max_small_n;
@@ -342,7 +343,6 @@ struct decoder {
   bool stop_after_attn = false;  // the last layer run stops after o_proj + residual
   int stop_mid_layer = -1;       // that layer, for the current step (-1: none)
   bool fuse_o = true;            // batch-1 decode: output projection inside the attention launch
-  uint32_t o_groups = 0;         // groups counted so far by the fused launches' arrival counter
   int last_rows = 0;
   int32_t *pinned = nullptr;
   // paged KV cache: device page table [max_batch][mp] (staged with the rows),
@@ -639,6 +639,10 @@ int norm_into(decoder *D, GemmArgs &g, const float *x, const float *gamma, int r
   return DEC_OK;
 }
 
+// The fused output projection's counters: [n_layers] arrivals, then
+// [n_layers] their values when the current step began.
+uint32_t *o_counters(decoder *D) { return reinterpret_cast<uint32_t *>(D->attn_cnt + ATTN_MAX_TASKS + 1); }
+
 // wo (batch-1 decode, bf16 weights): the output projection x += wo . o runs
 // inside the attention launch where the kernel takes it; *o_fused says
 // whether it did (otherwise the caller launches it).
@@ -728,15 +732,15 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
   const bool chunk_kernel = rows > rows_per_group && attention_chunk_fits(a, c.head_dim);
   const int qd = c.n_heads * c.head_dim;
   if (o_fused) *o_fused = false;
-  if (wo && o_fused && D->fuse_o && !chunk_kernel && a.pos_mode == 1 && rows == 1 && out_f32 && a.counters && !a.pt &&
+  if (wo && o_fused && D->fuse_o && !chunk_kernel && a.pos_mode != 2 && rows == 1 && out_f32 && a.counters && !a.pt &&
       qd <= ATTN_O_MAX_K) {
     const int H = c.hidden;
     a.wo = wo;
     a.o_x = D->x;
     a.o_rows = H;
     a.o_blocks = (H + 4 * ATTN_O_RPW - 1) / (4 * ATTN_O_RPW);
-    a.o_done = reinterpret_cast<uint32_t *>(D->attn_cnt + ATTN_MAX_TASKS + 1);
-    a.o_target = D->o_groups + (uint32_t)a.n_groups;
+    a.o_done = o_counters(D) + layer;
+    a.o_base = o_counters(D) + c.n_layers + layer;
     D->act_norm = nullptr;  // x changes
     timer.bytes += (double)H * qd * 2 + (double)qd * 4 + (double)H * 8;
     timer.flops += 2.0 * H * qd;
@@ -745,7 +749,6 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
   hipError_t e = chunk_kernel ? launch_attention_chunk(a, c.head_dim, D->stream)
                               : launch_attention(a, c.head_dim, D->stream);
   if (e != hipSuccess) return hip_fail(D, e, "attention");
-  if (a.wo) D->o_groups = a.o_target;  // the launch's groups count from here on
   return DEC_OK;
 }
 
@@ -1166,7 +1169,8 @@ int run_step(decoder *D, int rows, int rows_per_group, int max_pos, const int32_
   {
     NodeTimer t(D, DEC_NODE_EMBED, rows * (double)c.hidden * 6, 0);
     D->act_norm = nullptr;
-    e = launch_embed(D->embed, D->ids, D->next_token, D->row_seq, use_next, rows, c.hidden, D->x, st);
+    e = launch_embed(D->embed, D->ids, D->next_token, D->row_seq, use_next, rows, c.hidden, D->x, o_counters(D),
+                     o_counters(D) + c.n_layers, c.n_layers, st);
   }
   if (e != hipSuccess) return hip_fail(D, e, "embed");
   const int nl = D->layer_limit >= 0 ? std::min(D->layer_limit, c.n_layers) : c.n_layers;
@@ -1458,7 +1462,7 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
   if (hipMemsetAsync(D->kcache, 0, kvb, D->stream) != hipSuccess ||
       hipMemsetAsync(D->vcache, 0, kvb, D->stream) != hipSuccess ||
       hipMemsetAsync(D->next_token, 0, (size_t)cfg->max_batch * 4, D->stream) != hipSuccess ||
-      hipMemsetAsync(D->attn_cnt, 0, (size_t)(ATTN_MAX_TASKS + 2) * 4, D->stream) != hipSuccess ||
+      hipMemsetAsync(D->attn_cnt, 0, (size_t)(ATTN_MAX_TASKS + 1 + 2 * cfg->n_layers) * 4, D->stream) != hipSuccess ||
       hipStreamSynchronize(D->stream) != hipSuccess)
     return cleanup(DEC_E_HIP);
   *out = D;

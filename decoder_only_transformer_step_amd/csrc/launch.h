@@ -175,14 +175,16 @@ struct AttnArgs {
   // in-kernel merge): o_blocks blocks past the attention grid each own
   // 4 ATTN_O_RPW rows of the bf16 matrix wo [o_rows][Hq d] and finish
   // o_x[n] = o_x[n] + wo[n] . o once every column group has published o.
-  // *o_done counts the groups that have, over every fused launch of the
-  // decoder (it is never reset); this launch's groups are all in once it
-  // reaches o_target (modulo 2^32).
+  // *o_done counts the groups that have, over every fused launch of this
+  // layer (it is never reset); *o_base is its value when the step began
+  // (copied by the step's embedding launch), so this launch's groups are
+  // all in once it reaches *o_base + n_groups (modulo 2^32).  Both live
+  // in device memory, so a captured graph replays correctly.
   const uint16_t *wo;
   float *o_x;
   int32_t o_rows, o_blocks;
   uint32_t *o_done;
-  uint32_t o_target;
+  const uint32_t *o_base;
 };
 
 // fused output projection: rows per wave, and the widest input it holds
@@ -233,9 +235,11 @@ hipError_t launch_attention_chunk(const AttnArgs &a, int head_dim, hipStream_t s
 
 // ------------------------------------------------------ row-wise kernels --
 // x[r][:] = E[tok(r)][:], tok(r) = next_token[row_seq[r]] if use_next else ids[r]
+// (o_base[i] = o_cnt[i] for i < n_o: the snapshot of the layers' fused
+// output-projection arrival counters that this step's launches count from)
 hipError_t launch_embed(const uint16_t *E, const int32_t *ids, const int32_t *next_token,
                         const int32_t *row_seq, int use_next, int rows, int H, float *x,
-                        hipStream_t st);
+                        const uint32_t *o_cnt, uint32_t *o_base, int n_o, hipStream_t st);
 // out[r] = x[r] * rsqrt(mean(x^2) + eps) * g as split bf16 (lo plane at out + out_lo),
 // or fp32 into out_f32 when it is set
 hipError_t launch_rmsnorm(const float *x, int64_t ldx, const float *g, int rows, int H, float eps,

@@ -407,7 +407,9 @@ def test_fused_output_projection_same_bits(which, P):
     projection into the residual).  The same steps with the projection as a
     GEMV launch of its own must give the same bits, and both meet the oracle.
     Cases: one split per group (the block writes its output) and several
-    (the group's last block merges), head_dim 64 and 128, a MoE layer."""
+    (the group's last block merges), head_dim 64 and 128, a MoE layer, and
+    4 steps replayed from a captured graph, whose launches take their
+    arrival targets from device memory."""
     from synth.workloads import C8B
     from tests.moe_routes import forced
     shape, chunk = {"tiny": (TINY.with_(name="gqa-tiny-seq512", max_seq=512), 16),
@@ -435,6 +437,15 @@ def test_fused_output_projection_same_bits(which, P):
         assert int(af[0]) == int(ap[0])
         assert_parity(compare_logits(lf[0], m.forward([tok], P + i, **kw)["logits"], f"{which} step {i}"), which)
         tok = int(af[0])
+    # greedy steps replayed from a captured graph (positions read from
+    # device memory): the same tokens with and without the fused projection
+    runs = []
+    for d in (fused, plain):
+        t = torch.full((4,), -1, dtype=torch.int32, device="cuda")
+        d.decode_run(0, 4, t)
+        torch.cuda.synchronize()
+        runs.append([int(v) for v in t.cpu().numpy()])
+    assert runs[0] == runs[1], f"{which}: graph-replayed tokens differ {runs}"
 
 
 @pytest.mark.parametrize("N,K", [(16, 32), (60, 2048), (100, 688), (777, 4096), (4096, 14336)])
