@@ -255,6 +255,12 @@ class Decoder:
     def seq_len(self, seq=0):
         return decoder_seq_len(self.handle, seq)
 
+    def set_stream(self, stream):
+        """Launch later calls on `stream` (a torch.cuda.Stream); the library
+        first waits for the work on the old one."""
+        _check(lib().decoder_set_stream(self.handle, ctypes.c_void_p(stream.cuda_stream)), self.handle, "set_stream")
+        self.stream = stream
+
     def debug_layer_limit(self, layers):
         _check(lib().decoder_debug_layer_limit(self.handle, layers), self.handle, "layer_limit")
 

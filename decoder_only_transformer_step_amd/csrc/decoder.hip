@@ -1481,6 +1481,9 @@ void decoder_free(decoder_t *D) {
 
 int decoder_set_stream(decoder_t *D, void *stream) {
   if (!D) return DEC_E_INVALID;
+  // the work already on the old stream finishes first: later calls share
+  // the decoder's buffers and the fused launches' arrival counters with it
+  if ((hipStream_t)stream != D->stream) HIP_TRY(D, hipStreamSynchronize(D->stream), "set_stream");
   D->stream = (hipStream_t)stream;
   return DEC_OK;
 }

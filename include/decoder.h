@@ -263,8 +263,10 @@ int32_t decoder_seq_len(const decoder_t *dec, int32_t seq);
 
 /* Replace the stream all later calls launch on (hipStream_t).  Stream
  * plumbing only; no passage of the pages defines an operation here (their
- * engines run on one queue of their own).  Always DEC_OK for a live
- * decoder; DEC_E_INVALID for NULL. */
+ * engines run on one queue of their own).  When the stream changes, the
+ * call first waits for the work already launched on the old one, so later
+ * calls never overlap it (they share the decoder's buffers).  DEC_OK;
+ * DEC_E_INVALID for NULL; DEC_E_HIP if that wait fails. */
 int decoder_set_stream(decoder_t *dec, void *stream);
 
 /* engine.zig Engine.deinit: release what init made.  Waits for the stream,

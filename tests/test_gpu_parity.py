@@ -448,6 +448,27 @@ def test_fused_output_projection_same_bits(which, P):
     assert runs[0] == runs[1], f"{which}: graph-replayed tokens differ {runs}"
 
 
+def test_stream_switch_keeps_results():
+    """decoder_set_stream between decode steps (plumbing; the engines of the
+    pages run on one queue): the steps launched on the new stream give the
+    same bits as a decoder that stayed on its stream."""
+    shape = TINY
+    W = host_weights(shape)
+    ids = [int(t) for t in prompt(shape, 20)]
+    a, _ = make_decoder(shape, W)
+    b, _ = make_decoder(shape, W)
+    tok = int(np.argmax(run_prefill(a, ids, 16)))
+    run_prefill(b, ids, 16)
+    s2 = torch.cuda.Stream()
+    for i in range(3):
+        la, aa = decode(a, [0], [tok])
+        if i == 1:
+            b.set_stream(s2)
+        lb, _ = decode(b, [0], [tok])
+        assert np.array_equal(la.view(np.uint32), lb.view(np.uint32)), f"step {i}"
+        tok = int(aa[0])
+
+
 @pytest.mark.parametrize("N,K", [(16, 32), (60, 2048), (100, 688), (777, 4096), (4096, 14336)])
 def test_gemv_kernel_matches_oracle(N, K):
     from decoder_only_transformer_step_amd.binding import diag_gemv
