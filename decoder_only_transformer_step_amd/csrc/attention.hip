@@ -601,8 +601,10 @@ template <int D, int PM>
 hipError_t launch_pm(const AttnArgs &a, hipStream_t st) {
   const int nb = a.n_groups * a.n_splits;
   if (PM != 2 && a.wo) {  // batch-1 decode with the output projection
-    if (a.pt || !a.counters || !a.out_f32 || a.rows != 1 || (int64_t)a.Hq * D > ATTN_O_MAX_K) return hipErrorInvalidValue;
-    if (PM == 1 && a.kc <= 128)
+    if (!a.counters || !a.out_f32 || a.rows != 1 || (int64_t)a.Hq * D > ATTN_O_MAX_K) return hipErrorInvalidValue;
+    if (a.pt)
+      hipLaunchKernelGGL((attn_kernel<D, PM, true, false, PM != 2>), dim3(nb + a.o_blocks), dim3(256), 0, st, a);
+    else if (PM == 1 && a.kc <= 128)
       hipLaunchKernelGGL((attn_kernel<D, PM, false, PM == 1, PM != 2>), dim3(nb + a.o_blocks), dim3(256), 0, st, a);
     else hipLaunchKernelGGL((attn_kernel<D, PM, false, false, PM != 2>), dim3(nb + a.o_blocks), dim3(256), 0, st, a);
     return hipGetLastError();

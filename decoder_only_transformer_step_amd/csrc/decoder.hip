@@ -732,7 +732,7 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
   const bool chunk_kernel = rows > rows_per_group && attention_chunk_fits(a, c.head_dim);
   const int qd = c.n_heads * c.head_dim;
   if (o_fused) *o_fused = false;
-  if (wo && o_fused && D->fuse_o && !chunk_kernel && a.pos_mode != 2 && rows == 1 && out_f32 && a.counters && !a.pt &&
+  if (wo && o_fused && D->fuse_o && !chunk_kernel && a.pos_mode != 2 && rows == 1 && out_f32 && a.counters &&
       qd <= ATTN_O_MAX_K) {
     const int H = c.hidden;
     a.wo = wo;
