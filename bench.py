@@ -632,9 +632,12 @@ def main():
     achieved = per_launch_bytes / per_launch_s / 1e9
     qsuf = {1: "_q8", 2: "_q4"}.get(variant.get("weight_quant", 0), "")
     traffic = counter_traffic(f"counters_{dom}_decode_{args.workload}{qsuf}.md")
+    kname = "attn_kernel" if dom == "attn" else "gemv_kernel, batch-1 projection"
+    if dom == "gate_up" and "down" not in wst:  # the dense FFN's two projections in one launch
+        kname = "gemv_ffn_kernel, batch-1 gate/up and down projections"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": f"{dom} ({'gemv_kernel, batch-1 projection' if dom != 'attn' else 'attn_kernel'}, decode)", "bytes_per_launch": per_launch_bytes,
+                "kernel": f"{dom} ({kname}, decode)", "bytes_per_launch": per_launch_bytes,
                 "avg_us": round(per_launch_s * 1e6, 2), "launches": d["launches"],
                 "timing": f"HIP events (no system fence) around every {dom} launch of every {args.sample_every}th "
                           "timed step; an event pair adds about 4.5 us of dispatch latency to the "

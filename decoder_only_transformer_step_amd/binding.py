@@ -85,6 +85,7 @@ SIGNATURES = {
     "decoder_debug_read_x": (ctypes.c_int, [_P, _P, _I32]),
     "decoder_debug_stop_after_attention": (ctypes.c_int, [_P, _I32]),
     "decoder_debug_fuse_o_proj": (ctypes.c_int, [_P, _I32]),
+    "decoder_debug_fuse_ffn": (ctypes.c_int, [_P, _I32]),
     "decoder_debug_read_routes": (ctypes.c_int, [_P, _P, _I32]),
     "decoder_stats_enable": (ctypes.c_int, [_P, _I32]),
     "decoder_stats_read": (ctypes.c_int, [_P, ctypes.POINTER(DecoderStats)]),
@@ -269,6 +270,9 @@ class Decoder:
 
     def debug_fuse_o_proj(self, on):
         _check(lib().decoder_debug_fuse_o_proj(self.handle, int(on)), self.handle, "fuse_o_proj")
+
+    def debug_fuse_ffn(self, on):
+        _check(lib().decoder_debug_fuse_ffn(self.handle, int(on)), self.handle, "fuse_ffn")
 
     def debug_read_x(self, out, rows):
         _check(lib().decoder_debug_read_x(self.handle, _ptr(out), rows), self.handle, "read_x")

@@ -203,6 +203,15 @@ bool config_ok(const decoder_config_t *c) {
   return true;
 }
 
+// Words of the attention counter block: the split-merge counters and the
+// router's, the step snapshots of the fused launches' arrival counters, then
+// those counters, one 128-byte line each.
+int n_sync(const decoder_config_t &c) { return c.n_layers * (1 + GV_NCNT); }
+size_t sync_cnt_off(const decoder_config_t &c) {
+  return align_up((size_t)(ATTN_MAX_TASKS + 1 + n_sync(c)), SYNC_STRIDE);
+}
+size_t attn_cnt_words(const decoder_config_t &c) { return sync_cnt_off(c) + (size_t)n_sync(c) * SYNC_STRIDE; }
+
 Layout make_layout(const decoder_config_t *c) {
   Layout L{};
   const size_t A = 256;
@@ -250,7 +259,7 @@ Layout make_layout(const decoder_config_t *c) {
   // one arrival counter per attention group, then the MoE router's, then
   // per layer the fused output projection's arrival counter, then per
   // layer that counter's value at the start of the current step
-  L.attn_cnt = take((size_t)(ATTN_MAX_TASKS + 1 + 2 * c->n_layers) * 4);
+  L.attn_cnt = take((size_t)attn_cnt_words(*c) * 4);
   int max_small_n = std::max(qkvr, H);
   if (c->n_experts > 0) max_small_n = std::max(max_small_n, 2 * c->shared_inter);
   L.gpart_elems = (size_t)GEMM_MAX_SPLIT * L.R * 2 * (size_t)max_small_n;
@@ -343,6 +352,7 @@ struct decoder {
   bool stop_after_attn = false;  // the last layer run stops after o_proj + residual
   int stop_mid_layer = -1;       // that layer, for the current step (-1: none)
   bool fuse_o = true;            // batch-1 decode: output projection inside the attention launch
+  bool fuse_ffn = true;          // batch-1 decode: gate/up and down projections in one launch
   int last_rows = 0;
   int32_t *pinned = nullptr;
   // paged KV cache: device page table [max_batch][mp] (staged with the rows),
@@ -639,9 +649,12 @@ int norm_into(decoder *D, GemmArgs &g, const float *x, const float *gamma, int r
   return DEC_OK;
 }
 
-// The fused output projection's counters: [n_layers] arrivals, then
-// [n_layers] their values when the current step began.
-uint32_t *o_counters(decoder *D) { return reinterpret_cast<uint32_t *>(D->attn_cnt + ATTN_MAX_TASKS + 1); }
+// The arrival counters of the fused launches (cumulative, never reset),
+// SYNC_STRIDE words apart from sync_cnt_off on: counter l is layer l's
+// output projection's, counters n_layers + GV_NCNT l + i the dense FFN's of
+// layer l; sync_base(D)[j] is counter j's value when the current step began.
+uint32_t *sync_base(decoder *D) { return reinterpret_cast<uint32_t *>(D->attn_cnt + ATTN_MAX_TASKS + 1); }
+uint32_t *sync_cnt(decoder *D) { return reinterpret_cast<uint32_t *>(D->attn_cnt + sync_cnt_off(D->c)); }
 
 // wo (batch-1 decode, bf16 weights): the output projection x += wo . o runs
 // inside the attention launch where the kernel takes it; *o_fused says
@@ -739,8 +752,8 @@ int attention(decoder *D, int layer, int rows, int rows_per_group, int max_pos, 
     a.o_x = D->x;
     a.o_rows = H;
     a.o_blocks = (H + 4 * ATTN_O_RPW - 1) / (4 * ATTN_O_RPW);
-    a.o_done = o_counters(D) + layer;
-    a.o_base = o_counters(D) + c.n_layers + layer;
+    a.o_done = sync_cnt(D) + (int64_t)layer * SYNC_STRIDE;
+    a.o_base = sync_base(D) + layer;
     D->act_norm = nullptr;  // x changes
     timer.bytes += (double)H * qd * 2 + (double)qd * 4 + (double)H * 8;
     timer.flops += 2.0 * H * qd;
@@ -884,8 +897,21 @@ int run_layer_single(decoder *D, int l, int max_pos, const int32_t *hpos) {
     GemvArgs gu = gemv_args(W.w_gate_up, D->x, H, I, D->f32_h);
     gu.gamma = W.ffn_norm;
     gu.eps = eps;
+    const GemvArgs dn = gemv_args(W.w_down, D->f32_h, I, H, D->x);
+    if (D->fuse_ffn && !c.weight_quant && gemv_ffn_fits(gu, dn)) {
+      // one launch: the down blocks wait for the gate/up blocks' arrivals
+      D->act_norm = nullptr;  // x changes
+      NodeTimer timer(D, DEC_NODE_GATE_UP,
+                      2.0 * I * H * 2.0 + H * 4.0 + I * 4.0 + H * I * 2.0 + I * 4.0 + H * 8.0,
+                      2.0 * 2.0 * I * (double)H + 2.0 * H * (double)I);
+      const int j = c.n_layers + GV_NCNT * l;
+      const hipError_t e =
+          launch_gemv_ffn(gu, dn, sync_cnt(D) + (int64_t)j * SYNC_STRIDE, sync_base(D) + j, D->stream);
+      if (e != hipSuccess) return hip_fail(D, e, "fused FFN");
+      return DEC_OK;
+    }
     if ((rc = gemv(D, DEC_NODE_GATE_UP, EPI_SWIGLU, quant(D, gu, l, 2)))) return rc;
-    return gemv(D, DEC_NODE_DOWN, EPI_ADD, quant(D, gemv_args(W.w_down, D->f32_h, I, H, D->x), l, 3));
+    return gemv(D, DEC_NODE_DOWN, EPI_ADD, quant(D, dn, l, 3));
   }
   // MoE FFN for one row: the FFN RMSNorm runs inside the router GEMV and the
   // expert GEMVs (each from x).  The routed gate/up launch routes by itself
@@ -1169,8 +1195,8 @@ int run_step(decoder *D, int rows, int rows_per_group, int max_pos, const int32_
   {
     NodeTimer t(D, DEC_NODE_EMBED, rows * (double)c.hidden * 6, 0);
     D->act_norm = nullptr;
-    e = launch_embed(D->embed, D->ids, D->next_token, D->row_seq, use_next, rows, c.hidden, D->x, o_counters(D),
-                     o_counters(D) + c.n_layers, c.n_layers, st);
+    e = launch_embed(D->embed, D->ids, D->next_token, D->row_seq, use_next, rows, c.hidden, D->x, sync_cnt(D),
+                     sync_base(D), n_sync(c), SYNC_STRIDE, st);
   }
   if (e != hipSuccess) return hip_fail(D, e, "embed");
   const int nl = D->layer_limit >= 0 ? std::min(D->layer_limit, c.n_layers) : c.n_layers;
@@ -1462,7 +1488,7 @@ int decoder_init(const decoder_config_t *cfg, const decoder_weights_t *w, void *
   if (hipMemsetAsync(D->kcache, 0, kvb, D->stream) != hipSuccess ||
       hipMemsetAsync(D->vcache, 0, kvb, D->stream) != hipSuccess ||
       hipMemsetAsync(D->next_token, 0, (size_t)cfg->max_batch * 4, D->stream) != hipSuccess ||
-      hipMemsetAsync(D->attn_cnt, 0, (size_t)(ATTN_MAX_TASKS + 1 + 2 * cfg->n_layers) * 4, D->stream) != hipSuccess ||
+      hipMemsetAsync(D->attn_cnt, 0, (size_t)attn_cnt_words(*cfg) * 4, D->stream) != hipSuccess ||
       hipStreamSynchronize(D->stream) != hipSuccess)
     return cleanup(DEC_E_HIP);
   *out = D;
@@ -1937,6 +1963,12 @@ int decoder_debug_stop_after_attention(decoder_t *D, int32_t on) {
 int decoder_debug_fuse_o_proj(decoder_t *D, int32_t on) {
   if (check_dec(D) || (on != 0 && on != 1)) return DEC_E_INVALID;
   D->fuse_o = on != 0;
+  return DEC_OK;
+}
+
+int decoder_debug_fuse_ffn(decoder_t *D, int32_t on) {
+  if (check_dec(D) || (on != 0 && on != 1)) return DEC_E_INVALID;
+  D->fuse_ffn = on != 0;
   return DEC_OK;
 }
 

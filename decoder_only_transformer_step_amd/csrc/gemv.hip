@@ -283,7 +283,9 @@ __device__ __forceinline__ void item_ptrs(const GemvArgs &g, const char *W, int 
 }
 
 // Epilogue of one item (lane 0 writes).
-template <int EPI>
+// AT: the SwiGLU output goes out with a relaxed device-scope store (read
+// inside the same launch by the down projection's blocks).
+template <int EPI, bool AT = false>
 __device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, int r0, int r1, float v0, float v1,
                                               const ItemPre &pre) {
   if (EPI == EPI_STORE) {
@@ -299,7 +301,11 @@ __device__ __forceinline__ void item_epilogue(const GemvArgs &g, int out_row, in
     acc += pre.b * v0;
     g.C[r0] = pre.a + acc;
   } else if (EPI == EPI_SWIGLU) {
-    g.C[(int64_t)out_row * g.ldc + r0] = silu_f(v0) * v1;
+    if (AT)
+      __hip_atomic_store(g.C + (int64_t)out_row * g.ldc + r0, silu_f(v0) * v1, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    else
+      g.C[(int64_t)out_row * g.ldc + r0] = silu_f(v0) * v1;
   } else if (EPI == EPI_LOGITS) {
     g.C[r0] = v0;
   } else if (EPI == EPI_QKV) {
@@ -385,8 +391,49 @@ __device__ __forceinline__ void publish_route(const GemvArgs &g, const f32x4 *xs
 // wave w of block b items (b IPW + j) WV + w, and loads item j + 1 into the
 // other register buffer while item j is summed, so the activation prologue
 // of a block is paid once for IPW times the weights.
-template <int EPI, int NCH, int WV, int Q, int IPW>
-__global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
+// A launch that runs two projections one after the other (the SwiGLU
+// gate/up, then the down projection of its output): ROLE 1 blocks (the
+// first) store their outputs with relaxed device-scope stores and count
+// their arrival on one of GV_NCNT counters once every store is complete;
+// ROLE 2 blocks issue their first weight chunks, wait (bounded spin) until
+// the counters' sum reaches their snapshots' sum + nb1, then read the
+// activation after their weights (mode 0).  No block
+// waits on a later one: the first part's blocks precede the second's in
+// the dispatch order.
+struct GvSync {
+  uint32_t *cnt;
+  const uint32_t *base;
+  int32_t nb1;
+};
+constexpr uint32_t GV_SPIN_LIMIT = 1u << 20;
+constexpr int GV_AB = 8;               // activation loads in flight per thread
+constexpr int GV_SC1 = 16;             // cache policy bits of a load: sc1
+constexpr int GV_RSRC_W3 = 0x00020000;  // buffer descriptor word 3 (raw dword access)
+
+// Wave 0 polls the GV_NCNT counters, one a lane, until their sum reaches
+// the sum of the snapshots plus nb1 (modulo 2^32).
+__device__ __forceinline__ uint32_t gv_lane_sum(uint32_t v) {
+#pragma unroll
+  for (int o = 1; o < GV_NCNT; o <<= 1) v += (uint32_t)__shfl_xor((int)v, o);
+  return __builtin_amdgcn_readfirstlane(v);  // lane 0's: the same for every lane
+}
+
+__device__ __forceinline__ void gv_wait(const GvSync &sy) {
+  if (threadIdx.x < WAVE) {
+    const int l = threadIdx.x;
+    const uint32_t target = gv_lane_sum(l < GV_NCNT ? sy.base[l] : 0u) + (uint32_t)sy.nb1;
+    for (uint32_t n = 0; n < GV_SPIN_LIMIT; ++n) {
+      const uint32_t seen =
+          l < GV_NCNT ? __hip_atomic_load(sy.cnt + l * SYNC_STRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+      if ((int32_t)(gv_lane_sum(seen) - target) >= 0) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
+template <int EPI, int NCH, int WV, int Q, int IPW, int ROLE>
+__device__ __forceinline__ void gemv_body(const GemvArgs &ga, int bx0, int by, const GvSync &sy) {
   constexpr int NR = gv_rows<EPI>(), CH = gv_ch<Q>() / NR, NT = WV * WAVE, PRN = 32 / WV, PRH = PRN / 2;
   constexpr int SE = 64 * gv_epl<Q>();  // elements per 1 KB step
   extern __shared__ f32x4 xs[];  // activation, fp32 in the layout of xs_slot
@@ -398,7 +445,7 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
   // can follow the grouped slots in one grid: blocks past blocks1 x n_slots
   // run it.  Otherwise blockIdx.y is the slot.
   GemvArgs g = ga;
-  int bx = blockIdx.x, slot = blockIdx.y;
+  int bx = bx0, slot = by;
   if (ga.W2) {
     const int nb1 = ga.blocks1 * ga.n_slots;
     if (bx >= nb1) {
@@ -459,7 +506,8 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
 
   // activation into registers first when it fits.  Mode 1: x and gamma
   // (RMSNorm); 2: fp32 x; 3: bf16 x; 0: read after the weights are issued.
-  const int mode = g.gamma ? (K <= PRH * 4 * NT ? 1 : 0) : xin ? (K <= PRN * 4 * NT ? 2 : 0) : (K <= PRN * 8 * NT ? 3 : 0);
+  const int mode = ROLE == 2 ? 0
+                 : g.gamma ? (K <= PRH * 4 * NT ? 1 : 0) : xin ? (K <= PRN * 4 * NT ? 2 : 0) : (K <= PRN * 8 * NT ? 3 : 0);
   // (addresses picked by pointer selects, loads unconditional: a branch
   // around them would make the merge wait for the data)
   u32x4 pr[PRN];
@@ -484,6 +532,7 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
     load_batch<NR, CH, Q>(buf1, wp, CH, K, lane);
     if (Q == 2) load_exps<NR, EU>(ex1, ep, CH, K, lane);
   }
+  if constexpr (ROLE == 2) gv_wait(sy);
 
   // activation -> LDS (fp32, with the RMSNorm when gamma is set)
   auto put4 = [&](int k, f32x4 v) { xs[xs_slot_t<Q>(k)] = v; };
@@ -530,6 +579,23 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
     for (int k = threadIdx.x * 4; k < K; k += NT * 4) {
       const f32x4 v = loadf4(xin + k), w = loadf4(g.gamma + k);
       put4(k, f32x4{v[0] * inv * w[0], v[1] * inv * w[1], v[2] * inv * w[2], v[3] * inv * w[3]});
+    }
+  } else if (ROLE == 2) {
+    // the first part's outputs of this launch, read at device scope (the
+    // sc1 policy of a device-scope atomic load, 16 bytes a lane; reads past
+    // K return zero), GV_AB loads in flight per thread
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(xin), 0, K * 4, GV_RSRC_W3);
+    for (int k0 = 0; k0 < K; k0 += GV_AB * NT * 4) {
+      u32x4 v[GV_AB];
+#pragma unroll
+      for (int i = 0; i < GV_AB; ++i)
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (k0 + (threadIdx.x + i * NT) * 4) * 4, 0, GV_SC1);
+#pragma unroll
+      for (int i = 0; i < GV_AB; ++i) {
+        const int k = k0 + (threadIdx.x + i * NT) * 4;
+        if (k < K) put4(k, as_f4(v[i]));
+      }
     }
   } else if (xin) {
     for (int k = threadIdx.x * 4; k < K; k += NT * 4) put4(k, loadf4(xin + k));
@@ -614,8 +680,8 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
             bv = bv_s[w];
             bi = bi_s[w];
           }
-        g.part_val[blockIdx.x] = bv;
-        g.part_idx[blockIdx.x] = bi;
+        g.part_val[bx0] = bv;
+        g.part_idx[bx0] = bi;
       }
     }
     return;
@@ -639,7 +705,7 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
   if (NCH != 1) fma_batch<NR, CH, Q, EU>(acc, buf1, ex1, xs, gsum, (c + 1) * CH, steps, lane);
 #pragma unroll
   for (int r = 0; r < NR; ++r) acc[r] = wave_sum(acc[r]) * wsc[r];
-  if (valid && lane == 0) item_epilogue<EPI>(g, out_row, rows[0], rows[NR - 1], acc[0], acc[NR - 1], pre);
+  if (valid && lane == 0) item_epilogue<EPI, ROLE == 1>(g, out_row, rows[0], rows[NR - 1], acc[0], acc[NR - 1], pre);
 
   if (g.route_logits && bx == 0 && slot == 0) publish_route<Q, WV>(g, xs, steps, sred);
 
@@ -658,10 +724,45 @@ __global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
           bv = bv_s[w];
           bi = bi_s[w];
         }
-      g.part_val[blockIdx.x] = bv;
-      g.part_idx[blockIdx.x] = bi;
+      g.part_val[bx0] = bv;
+      g.part_idx[bx0] = bi;
     }
   }
+  if constexpr (ROLE == 1) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(sy.cnt + (bx0 % GV_NCNT) * SYNC_STRIDE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <int EPI, int NCH, int WV, int Q, int IPW>
+__global__ __launch_bounds__(WV * WAVE) void gemv_kernel(GemvArgs ga) {
+  gemv_body<EPI, NCH, WV, Q, IPW, 0>(ga, blockIdx.x, blockIdx.y, GvSync{});
+}
+
+// The SwiGLU gate/up projection and the down projection of its output in
+// one launch: blocks [0, nb1) the first, the rest the second (GvSync).
+template <int NCH1, int NCH2, int WV>
+__global__ __launch_bounds__(WV * WAVE) void gemv_ffn_kernel(GemvArgs gu, GemvArgs dn, GvSync sy) {
+  if ((int)blockIdx.x < sy.nb1) gemv_body<EPI_SWIGLU, NCH1, WV, 0, 1, 1>(gu, blockIdx.x, 0, sy);
+  else gemv_body<EPI_ADD, NCH2, WV, 0, 1, 2>(dn, blockIdx.x - sy.nb1, 0, sy);
+}
+
+template <int WV, int C1>
+void launch_ffn_c2(int c2, dim3 grid, size_t lds, hipStream_t st, const GemvArgs &gu, const GemvArgs &dn,
+                   const GvSync &sy) {
+  if (c2 == 1) hipLaunchKernelGGL((gemv_ffn_kernel<C1, 1, WV>), grid, dim3(WV * WAVE), lds, st, gu, dn, sy);
+  else if (c2 == 2) hipLaunchKernelGGL((gemv_ffn_kernel<C1, 2, WV>), grid, dim3(WV * WAVE), lds, st, gu, dn, sy);
+  else hipLaunchKernelGGL((gemv_ffn_kernel<C1, 0, WV>), grid, dim3(WV * WAVE), lds, st, gu, dn, sy);
+}
+
+template <int WV>
+void launch_ffn_w(int c1, int c2, dim3 grid, size_t lds, hipStream_t st, const GemvArgs &gu, const GemvArgs &dn,
+                  const GvSync &sy) {
+  if (c1 == 1) launch_ffn_c2<WV, 1>(c2, grid, lds, st, gu, dn, sy);
+  else if (c1 == 2) launch_ffn_c2<WV, 2>(c2, grid, lds, st, gu, dn, sy);
+  else launch_ffn_c2<WV, 0>(c2, grid, lds, st, gu, dn, sy);
 }
 
 int device_cus();
@@ -749,6 +850,36 @@ int gemv_waves(int n_items) {
 int gemv_blocks(int n_items) {
   const int wv = gemv_waves(n_items);
   return (n_items + wv - 1) / wv;
+}
+
+// Worth it once the gate/up part fills the chip at least twice over: the
+// down blocks' first weights then stream under its last blocks (8B-class
+// decode, 1792 + 512 blocks: 330 -> 336 tok/s).  A part that fits in one
+// wave of blocks gains nothing to hide the arrival wait under (135M-class,
+// 192 + 72 blocks: 1326 -> 1299 tok/s).
+bool gemv_ffn_fits(const GemvArgs &gu, const GemvArgs &dn) {
+  return gu.W && dn.W && !gu.qbits && !dn.qbits && !gu.Wq && !dn.Wq && !gu.W2 && !dn.W2 && !gu.slot_expert &&
+         !dn.slot_expert && !gu.route_logits && !dn.route_logits && gu.C && dn.a_f32 == gu.C && !dn.gamma &&
+         dn.K == gu.N && gu.n_items == gu.N && dn.C && gemv_blocks(gu.n_items) >= 2 * device_cus();
+}
+
+hipError_t launch_gemv_ffn(const GemvArgs &gu, const GemvArgs &dn, uint32_t *cnt, const uint32_t *base,
+                           hipStream_t st) {
+  if (!gemv_ffn_fits(gu, dn) || !cnt || !base) return hipErrorInvalidValue;
+  // the gate/up part's block shape (its RMSNorm sums over the block's waves)
+  const int wv = gemv_waves(gu.n_items);
+  const GvSync sy{cnt, base, (gu.n_items + wv - 1) / wv};
+  const dim3 grid(sy.nb1 + (dn.n_items + wv - 1) / wv);
+  const size_t lds = std::max(gemv_lds(gu.K, 0), gemv_lds(dn.K, 0));
+  // chunk counts of each part's rows (1 or 2: no refills; else the refill loop)
+  auto nch = [](const GemvArgs &g, int nr) {
+    const int ch = gv_ch<0>() / nr, steps = (g.K + 511) / 512, n = (steps + ch - 1) / ch;
+    return n <= 2 ? n : 0;
+  };
+  const int c1 = nch(gu, 2), c2 = nch(dn, 1);
+  if (wv == 4) launch_ffn_w<4>(c1, c2, grid, lds, st, gu, dn, sy);
+  else launch_ffn_w<8>(c1, c2, grid, lds, st, gu, dn, sy);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv(const GemvArgs &g0, int epi, hipStream_t st, int *blocks) {

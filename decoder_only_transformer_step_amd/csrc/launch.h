@@ -126,6 +126,20 @@ int gemv_blocks(int n_items);
 // `blocks` (optional) receives the grid size, i.e. the number of argmax
 // partials an EPI_LOGITS launch writes
 hipError_t launch_gemv(const GemvArgs &g, int epi, hipStream_t st, int *blocks = nullptr);
+// Arrival counters of the fused launches sit SYNC_STRIDE words apart (one
+// 128-byte line each).  Device-scope atomics on one address are serialised
+// where memory performs them, so a launch whose many blocks arrive together
+// spreads them over GV_NCNT counters.
+constexpr int SYNC_STRIDE = 32;
+constexpr int GV_NCNT = 64;
+// Batch-1 dense FFN in one launch: the SwiGLU gate/up GEMV (gu, output gu.C)
+// and the down GEMV of that output (dn, activation dn.a_f32 == gu.C), the
+// down blocks waiting for the gate/up blocks' arrivals.  Block b of the
+// first part counts on cnt[(b % GV_NCNT) SYNC_STRIDE]; base[i] is counter
+// i's value when the step began (all cumulative).  bf16 weights only.
+bool gemv_ffn_fits(const GemvArgs &gu, const GemvArgs &dn);
+hipError_t launch_gemv_ffn(const GemvArgs &gu, const GemvArgs &dn, uint32_t *cnt, const uint32_t *base,
+                           hipStream_t st);
 
 // idx[r] = argmax over part_val[r][0 .. nparts) (lowest index on ties), and
 // next_token[row_seq[r]] = idx[r] for the last row of each run of rows with
@@ -235,11 +249,11 @@ hipError_t launch_attention_chunk(const AttnArgs &a, int head_dim, hipStream_t s
 
 // ------------------------------------------------------ row-wise kernels --
 // x[r][:] = E[tok(r)][:], tok(r) = next_token[row_seq[r]] if use_next else ids[r]
-// (o_base[i] = o_cnt[i] for i < n_o: the snapshot of the layers' fused
-// output-projection arrival counters that this step's launches count from)
+// (o_base[i] = o_cnt[i * o_stride] for i < n_o: the snapshot of the fused
+// launches' arrival counters that this step's launches count from)
 hipError_t launch_embed(const uint16_t *E, const int32_t *ids, const int32_t *next_token,
                         const int32_t *row_seq, int use_next, int rows, int H, float *x,
-                        const uint32_t *o_cnt, uint32_t *o_base, int n_o, hipStream_t st);
+                        const uint32_t *o_cnt, uint32_t *o_base, int n_o, int o_stride, hipStream_t st);
 // out[r] = x[r] * rsqrt(mean(x^2) + eps) * g as split bf16 (lo plane at out + out_lo),
 // or fp32 into out_f32 when it is set
 hipError_t launch_rmsnorm(const float *x, int64_t ldx, const float *g, int rows, int H, float eps,

@@ -16,11 +16,12 @@ __global__ __launch_bounds__(256) void embed_kernel(const uint16_t *E, const int
                                                     const int32_t *next_token,
                                                     const int32_t *row_seq, int use_next, int H,
                                                     float *x, const uint32_t *o_cnt, uint32_t *o_base,
-                                                    int n_o) {
+                                                    int n_o, int o_stride) {
   const int r = blockIdx.x;
   if (r == 0)
     for (int i = threadIdx.x; i < n_o; i += blockDim.x)
-      o_base[i] = __hip_atomic_load(const_cast<uint32_t *>(o_cnt + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      o_base[i] = __hip_atomic_load(const_cast<uint32_t *>(o_cnt + (int64_t)i * o_stride), __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
   const int tok = use_next ? next_token[row_seq[r]] : ids[r];
   const uint16_t *src = E + (int64_t)tok * H;
   float *dst = x + (int64_t)r * H;
@@ -233,9 +234,9 @@ hipError_t launch_qk_norm_rope(const QkNormArgs &a, hipStream_t st) {
 
 hipError_t launch_embed(const uint16_t *E, const int32_t *ids, const int32_t *next_token,
                         const int32_t *row_seq, int use_next, int rows, int H, float *x,
-                        const uint32_t *o_cnt, uint32_t *o_base, int n_o, hipStream_t st) {
+                        const uint32_t *o_cnt, uint32_t *o_base, int n_o, int o_stride, hipStream_t st) {
   hipLaunchKernelGGL(embed_kernel, dim3(rows), dim3(256), 0, st, E, ids, next_token, row_seq,
-                     use_next, H, x, o_cnt, o_base, n_o);
+                     use_next, H, x, o_cnt, o_base, n_o, o_stride);
   return hipGetLastError();
 }
 

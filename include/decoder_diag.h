@@ -135,6 +135,13 @@ int decoder_debug_stop_after_attention(decoder_t *dec, int32_t on);
  * exists so that tests can compare them.  DEC_E_INVALID for other values. */
 int decoder_debug_fuse_o_proj(decoder_t *dec, int32_t on);
 
+/* on = 0: a batch-1 decode step launches each dense layer's gate/up and down
+ * projections as two GEMVs; on = 1 (the default): one launch runs both, the
+ * down projection's blocks waiting for the gate/up blocks' outputs (bf16
+ * weights).  Both give the same bits; the switch exists so that tests can
+ * compare them.  DEC_E_INVALID for other values. */
+int decoder_debug_fuse_ffn(decoder_t *dec, int32_t on);
+
 /* Copy the residual stream x (fp32 [rows][H]) left by the last prefill_chunk
  * or decode_step (row i = token i of the chunk, or batch entry i) to d_out. */
 int decoder_debug_read_x(decoder_t *dec, float *d_out, int32_t rows);
@@ -154,7 +161,8 @@ enum {
   DEC_NODE_ROPE = 1,     /* bias + RoPE + KV append */
   DEC_NODE_ATTN = 2,     /* attention (+ split merge) */
   DEC_NODE_O = 3,        /* o_proj + residual */
-  DEC_NODE_GATE_UP = 4,  /* dense gate/up projection with the SwiGLU epilogue */
+  DEC_NODE_GATE_UP = 4,  /* dense gate/up projection with the SwiGLU epilogue (batch-1 decode with the
+                            fused FFN launch: also the down projection and residual) */
   DEC_NODE_DOWN = 5,     /* dense down projection + residual */
   DEC_NODE_ROUTER = 6,   /* MoE router logits, top-k and grouping */
   DEC_NODE_EXPERTS = 7,  /* MoE routed + shared experts and the combine */

@@ -404,7 +404,8 @@ def test_fused_output_projection_same_bits(which, P):
     """Batch-1 decode runs each layer's output projection (and the residual
     add) inside the attention launch, its blocks waiting for the column
     groups' outputs (engine.zig Engine.forward: attention, then the output
-    projection into the residual).  The same steps with the projection as a
+    projection into the residual), and a dense layer's gate/up and down
+    projections in one launch.  The same steps with each projection as a
     GEMV launch of its own must give the same bits, and both meet the oracle.
     Cases: one split per group (the block writes its output) and several
     (the group's last block merges), head_dim 64 and 128, a MoE layer, and
@@ -422,6 +423,7 @@ def test_fused_output_projection_same_bits(which, P):
     fused, _ = make_decoder(shape, W)
     plain, _ = make_decoder(shape, W)
     plain.debug_fuse_o_proj(0)
+    plain.debug_fuse_ffn(0)
     tok = int(np.argmax(run_prefill(fused, ids, chunk)))
     m = oracle.Model(shape, W)
     if moe:   # one chunk, on the routes the library took
