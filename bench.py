@@ -633,7 +633,7 @@ def main():
     qsuf = {1: "_q8", 2: "_q4"}.get(variant.get("weight_quant", 0), "")
     traffic = counter_traffic(f"counters_{dom}_decode_{args.workload}{qsuf}.md")
     kname = "attn_kernel" if dom == "attn" else "gemv_kernel, batch-1 projection"
-    if dom == "gate_up" and "down" not in wst:  # the dense FFN's two projections in one launch
+    if dom == "gate_up" and not wst.get("down", {}).get("launches", 0):  # the dense FFN in one launch
         kname = "gemv_ffn_kernel, batch-1 gate/up and down projections"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
