@@ -137,8 +137,9 @@ int decoder_debug_fuse_o_proj(decoder_t *dec, int32_t on);
 
 /* on = 0: a batch-1 decode step launches each dense layer's gate/up and down
  * projections as two GEMVs; on = 1 (the default): one launch runs both, the
- * down projection's blocks waiting for the gate/up blocks' outputs (bf16
- * weights).  Both give the same bits; the switch exists so that tests can
+ * down projection's blocks waiting for the gate/up blocks' outputs, where
+ * it pays (bf16 weights and a gate/up grid of at least two blocks per
+ * compute unit).  Both give the same bits; the switch exists so that tests can
  * compare them.  DEC_E_INVALID for other values. */
 int decoder_debug_fuse_ffn(decoder_t *dec, int32_t on);
 
